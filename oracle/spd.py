@@ -1,0 +1,467 @@
+"""Plain CPU oracle of one Speculative Pipeline Decoding (SPD) draft-and-verify cycle.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  The product path
+(``pipeline_draft_step_amd``) never imports it, and this module imports nothing
+from the product path: the two share no code, constants or tables.
+
+Everything is numpy in float64 (inputs are the bf16- or fp32-valued arrays the
+device sees, widened to float64).  Integer decisions (argmax, sampling, the
+accept test) are exact.  It is written to be read against the pages, not to be
+fast.
+
+Pages cited (by title and section; the text of each page is the authority):
+
+* [SPD]   "Speculative Pipeline Decoding: Higher-Accuracy Drafting with Hidden
+          Latency via Pipeline Parallelism" (arXiv 2605.30852), sections 3.1-3.4
+          and 4 (metrics).  Its display equations were lost in extraction; the
+          readings used below are listed in the design doc.
+* [REV]   The xllm-io paper-review blog post on the same paper, section
+          "核心公式" (core formulas) and "验证与回滚机制" (verification and rollback).
+* [SD]    "Speculative Decoding: How Draft-Model Parallelism Cuts LLM Inference
+          Latency", sections "The four-phase loop", "The acceptance criterion and
+          why it is exact", "Acceptance rate equals 1 minus total variation
+          distance", "Theoretical speedup".
+
+Parity status per function: every function below is pinned by a ``-m "not gpu"``
+test in ``tests/test_oracle_pins.py`` except where its docstring says
+"parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+ZERO_MASK = 0
+CLAMP_MIN = 1
+
+_TWO52 = float(2 ** 52)
+
+
+# --------------------------------------------------------------------------
+# Layout and eligibility  ([SPD] 3.1 Eq. (2), 3.2 Eq. (3) and the partial-fill
+# equation; [REV] core formulas)
+# --------------------------------------------------------------------------
+
+def l_max(k: int, L: int, n: int) -> int:
+    """Deepest target layer available to a token that has completed k of n stages.
+
+    [SPD] 3.2: l_max(k) = min(L, k*L/n).  Stages are whole layers (uniform L/n
+    splits, [SPD] 4 setup), so a non-integral k*L/n is floored.
+    """
+    if not 0 <= k <= n:
+        raise ValueError("depth k must lie in 0..n")
+    return min(L, (k * L) // n)
+
+
+def slot_layers(k: int, L: int, n: int, anchors, mode: int = ZERO_MASK):
+    """Target layer read by each of the m anchor slots at depth k (-1 = empty slot).
+
+    [SPD] 3.2 Eq. (3): a depth-k token consumes every anchor b_j <= l_max(k);
+    the others are left out (ZERO_MASK: their slot of the concatenation is 0).
+    [REV] core formulas, 0<k<n case: the clamped variant reads layer
+    min(b_j, l_max(k)) in every slot (CLAMP_MIN).
+    Both sources give k = 0 its own rule, g^0 = FC(H^0): only slot 0 (b_0 = 0,
+    the embedding) is read.
+    """
+    anchors = [int(b) for b in anchors]
+    if anchors[0] != 0:
+        raise ValueError("the first anchor must be the embedding layer 0")
+    if k == 0:
+        return [0] + [-1] * (len(anchors) - 1)
+    lm = l_max(k, L, n)
+    if mode == ZERO_MASK:
+        return [b if b <= lm else -1 for b in anchors]
+    if mode == CLAMP_MIN:
+        return [min(b, lm) for b in anchors]
+    raise ValueError("unknown anchor mode")
+
+
+def store_layers_for(L: int, n: int, anchors, mode: int = ZERO_MASK):
+    """Sorted list of target layers an anchor store must hold for this mode."""
+    layers = set()
+    for k in range(n + 1):
+        layers.update(l for l in slot_layers(k, L, n, anchors, mode) if l >= 0)
+    return sorted(layers)
+
+
+def depths(t: int, a: int, n: int):
+    """Pipeline depth of positions 0..t-1 when a tokens are in flight.
+
+    [SPD] 3.1 Eq. (2) (a = n) and 3.2's partial-fill layout (a < n): positions
+    before the trailing a are fully processed (k = n); the in-flight tokens form
+    a staircase from the oldest (depth a-1) down to the newest (depth 0, the
+    embedding-only input), the pre-step reading of [SPD] 3.3.
+    """
+    if not 1 <= a <= n or a > t:
+        raise ValueError("need 1 <= a <= min(n, t)")
+    return [n if i < t - a else t - 1 - i for i in range(t)]
+
+
+def cycle_rows(t: int, a: int, n: int):
+    """Rows recomputed by one cycle: the newest fully-processed position plus the
+    a in-flight ones.  Returns (pos0, positions, depths).  Positions before pos0
+    keep the key/value entries computed when they last changed depth."""
+    if t < a + 1:
+        raise ValueError("need at least one fully processed position")
+    dep = depths(t, a, n)
+    pos0 = t - 1 - a
+    pos = list(range(pos0, t))
+    return pos0, pos, [dep[i] for i in pos]
+
+
+# --------------------------------------------------------------------------
+# Feature fusion  ([SPD] 3.2; [REV] core formulas)
+# --------------------------------------------------------------------------
+
+def fuse_features(store, store_layers, pos, depth, gamma, w_fc, *, L, n, anchors,
+                  mode=ZERO_MASK, eps=1e-6, norm_k0=False):
+    """Depth-conditioned feature g_i^k for each requested row.
+
+    store:  [T][S][d]  hidden states H_i^l of every layer listed in store_layers.
+    gamma:  [m*d]      RMSNorm weight of the concatenation.
+    w_fc:   [d][m*d]   FC projection (no bias).
+    For k >= 1: x = Concat over slots (zeros in empty slots), RMS over the filled
+    slots only, u = gamma * x / rms, g = W_fc u.  For k = 0: g = W_fc[:, :d] H^0
+    (no norm, no gamma) unless norm_k0 asks for the uniform rule.
+    """
+    store = np.asarray(store, dtype=np.float64)
+    gamma = np.asarray(gamma, dtype=np.float64)
+    w_fc = np.asarray(w_fc, dtype=np.float64)
+    d = store.shape[2]
+    m = len(anchors)
+    index_of = {l: s for s, l in enumerate(store_layers)}
+    out = np.zeros((len(pos), d))
+    for r, (i, k) in enumerate(zip(pos, depth)):
+        layers = slot_layers(k, L, n, anchors, mode)
+        if k == 0 and not norm_k0:
+            out[r] = w_fc[:, :d] @ store[i, index_of[0]]
+            continue
+        x = np.zeros(m * d)
+        filled = 0
+        for j, l in enumerate(layers):
+            if l >= 0:
+                x[j * d:(j + 1) * d] = store[i, index_of[l]]
+                filled += 1
+        rms = math.sqrt(float(np.dot(x, x)) / (filled * d) + eps)
+        u = gamma * x / rms
+        out[r] = w_fc @ u
+    return out
+
+
+# --------------------------------------------------------------------------
+# Pipeline Draft Module: Qwen3-style decoder ([SPD] 3.1)
+# --------------------------------------------------------------------------
+
+def rms_norm(x, w, eps):
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * w
+
+
+def silu(x):
+    return x / (1.0 + np.exp(-x))
+
+
+def rope(x, positions, theta):
+    """Rotate-half rotary embedding of x [T][H][hd] at the given 0-based positions."""
+    x = np.asarray(x, dtype=np.float64)
+    hd = x.shape[-1]
+    half = hd // 2
+    inv_freq = theta ** (-np.arange(half, dtype=np.float64) * 2.0 / hd)
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * inv_freq[None, :]
+    cos = np.cos(ang)[:, None, :]
+    sin = np.sin(ang)[:, None, :]
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * cos - x2 * sin, x2 * cos + x1 * sin], axis=-1)
+
+
+@dataclass
+class PdmConfig:
+    d: int
+    Hq: int
+    Hkv: int
+    hd: int
+    dff: int
+    eps: float = 1e-6
+    rope_theta: float = 1e6
+
+
+def _split_qkv(qkv, c: PdmConfig):
+    T = qkv.shape[0]
+    nq, nk = c.Hq * c.hd, c.Hkv * c.hd
+    q = qkv[:, :nq].reshape(T, c.Hq, c.hd)
+    k = qkv[:, nq:nq + nk].reshape(T, c.Hkv, c.hd)
+    v = qkv[:, nq + nk:].reshape(T, c.Hkv, c.hd)
+    return q, k, v
+
+
+def _attend(q, k_all, v_all, q_pos, k_pos, c: PdmConfig):
+    """Causal GQA softmax attention: query head h reads key/value head h // (Hq/Hkv)."""
+    group = c.Hq // c.Hkv
+    out = np.zeros((q.shape[0], c.Hq, c.hd))
+    scale = 1.0 / math.sqrt(c.hd)
+    for h in range(c.Hq):
+        kh = k_all[:, h // group, :]
+        vh = v_all[:, h // group, :]
+        s = (q[:, h, :] @ kh.T) * scale
+        s = np.where(np.asarray(k_pos)[None, :] <= np.asarray(q_pos)[:, None], s, -np.inf)
+        s = s - s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p = p / p.sum(axis=1, keepdims=True)
+        out[:, h, :] = p @ vh
+    return out
+
+
+def decoder_layer(h, positions, lw, c: PdmConfig, kv_prefix=None):
+    """One pre-norm decoder layer over rows h [T][d] at `positions`.
+
+    lw: dict of float64 arrays attn_norm [d], wqkv [(Hq+2Hkv)*hd][d] (q heads,
+    then k heads, then v heads), q_norm [hd], k_norm [hd], wo [d][Hq*hd],
+    mlp_norm [d], w_gate_up [2*dff][d] (gate rows, then up rows), w_down [d][dff].
+    kv_prefix: optional (K [P][Hkv][hd], V [P][Hkv][hd], positions [P]) of earlier
+    rows (already normed and rotated).  Returns (h_out, K_rows, V_rows) where
+    K_rows/V_rows are this call's rows' keys/values as they enter attention.
+    """
+    n1 = rms_norm(h, lw["attn_norm"], c.eps)
+    q, k, v = _split_qkv(n1 @ lw["wqkv"].T, c)
+    q = rope(rms_norm(q, lw["q_norm"], c.eps), positions, c.rope_theta)
+    k = rope(rms_norm(k, lw["k_norm"], c.eps), positions, c.rope_theta)
+    if kv_prefix is not None:
+        kp, vp, pp = kv_prefix
+        k_all = np.concatenate([kp, k], axis=0)
+        v_all = np.concatenate([vp, v], axis=0)
+        k_pos = list(pp) + list(positions)
+    else:
+        k_all, v_all, k_pos = k, v, list(positions)
+    att = _attend(q, k_all, v_all, positions, k_pos, c)
+    h = h + att.reshape(h.shape[0], -1) @ lw["wo"].T
+    n2 = rms_norm(h, lw["mlp_norm"], c.eps)
+    gu = n2 @ lw["w_gate_up"].T
+    act = silu(gu[:, :c.dff]) * gu[:, c.dff:]
+    h = h + act @ lw["w_down"].T
+    return h, k, v
+
+
+def pdm_forward(G, layers, final_norm, c: PdmConfig):
+    """Definitional PDM: run f_theta over the whole feature sequence G [t][d]
+    with a causal mask and return the final-normed last row ([SPD] 3.1 Eq. (1):
+    the draft reads the last-position representation).  No token embedding
+    enters: the input rows are the features themselves."""
+    h = np.asarray(G, dtype=np.float64)
+    positions = list(range(h.shape[0]))
+    for lw in layers:
+        h, _, _ = decoder_layer(h, positions, lw, c)
+    return rms_norm(h[-1], final_norm, c.eps)
+
+
+class PdmCache:
+    """Key/value entries per layer for positions 0..len-1 (float64)."""
+
+    def __init__(self, n_layers: int, c: PdmConfig):
+        self.k = [np.zeros((0, c.Hkv, c.hd)) for _ in range(n_layers)]
+        self.v = [np.zeros((0, c.Hkv, c.hd)) for _ in range(n_layers)]
+
+    def length(self) -> int:
+        return self.k[0].shape[0]
+
+    def truncate(self, n: int) -> None:
+        self.k = [x[:n] for x in self.k]
+        self.v = [x[:n] for x in self.v]
+
+
+def pdm_step(g_rows, pos0, cache: PdmCache, layers, final_norm, c: PdmConfig):
+    """Incremental PDM: rows pos0..pos0+M-1 attend to the cached positions
+    < pos0 and causally to each other.  Afterwards the cache holds exactly the
+    positions 0..pos0+M-1 (this call's rows overwrite any older entries at those
+    positions).  Returns (final-normed last row, un-normed output rows [M][d])."""
+    h = np.asarray(g_rows, dtype=np.float64)
+    M = h.shape[0]
+    positions = list(range(pos0, pos0 + M))
+    for li, lw in enumerate(layers):
+        kp, vp = cache.k[li][:pos0], cache.v[li][:pos0]
+        if kp.shape[0] != pos0:
+            raise ValueError("cache does not cover the positions before pos0")
+        h, k, v = decoder_layer(h, positions, lw, c, (kp, vp, range(pos0)))
+        cache.k[li] = np.concatenate([kp, k], axis=0)
+        cache.v[li] = np.concatenate([vp, v], axis=0)
+    return rms_norm(h[-1], final_norm, c.eps), h
+
+
+# --------------------------------------------------------------------------
+# Heads, sampling and verification ([SPD] 3.1, 3.4; [SD] four-phase loop and
+# acceptance criterion)
+# --------------------------------------------------------------------------
+
+def lm_logits(w_lm, h):
+    """logits = W_lm h for a final-normed hidden row h."""
+    return np.asarray(w_lm, dtype=np.float64) @ np.asarray(h, dtype=np.float64)
+
+
+def argmax_first(x):
+    """Greedy choice: the lowest index attaining the maximum; NaN never wins."""
+    x = np.asarray(x, dtype=np.float64)
+    x = np.where(np.isnan(x), -np.inf, x)
+    return int(np.argmax(x))
+
+
+def softmax(logits, temperature):
+    z = np.asarray(logits, dtype=np.float64) / float(temperature)
+    z = z - z.max()
+    e = np.exp(z)
+    return e / e.sum()
+
+
+def prob_weights(p32):
+    """Exact integer weights of an fp32 probability row: floor(p * 2^52).
+    Non-positive and NaN entries weigh 0."""
+    p = np.asarray(p32, dtype=np.float32).astype(np.float64)
+    p = np.where(p > 0, p, 0.0)  # NaN compares false -> 0
+    return np.floor(p * _TWO52).astype(np.uint64)
+
+
+def sample_weights(w, u32):
+    """Inverse-CDF draw from non-negative integer weights with a 32-bit uniform.
+
+    tau = floor(u * S / 2^32); the result is the smallest j whose inclusive
+    prefix sum exceeds tau.  Returns None when every weight is zero.
+    Each j is returned for exactly the u in an interval of length ~w_j*2^32/S.
+    """
+    w = np.asarray(w, dtype=np.uint64)
+    total = int(w.sum(dtype=np.uint64))
+    if total == 0:
+        return None
+    tau = (int(u32) * total) >> 32
+    csum = np.cumsum(w, dtype=np.uint64)
+    return int(np.searchsorted(csum, np.uint64(tau), side="right"))
+
+
+def sample_probs(p32, u32):
+    """Draw from an fp32 probability row (O7 of the design: integer weights)."""
+    j = sample_weights(prob_weights(p32), u32)
+    if j is None:
+        raise ValueError("probability row has no positive entry")
+    return j
+
+
+def accept_test(p_x, q_x, r24):
+    """Exact form of 'accept iff r <= min(1, p(x)/q(x))' with r = (R + 1) / 2^24.
+
+    R is a 24-bit integer, so r is uniform on the lattice (0, 1]: p >= q always
+    accepts and p = 0 never does.  (R+1)*q (25 x 24 bits) fits a double's
+    mantissa exactly, so (R+1)*q <= p*2^24 is decided without rounding.
+    q(x) = 0 accepts.
+    """
+    R1 = float(int(r24) + 1)
+    q = float(np.float32(q_x))
+    p = float(np.float32(p_x))
+    return R1 * q <= p * 16777216.0
+
+
+def residual_weights(p32, q32):
+    """Integer residual max(0, P - Q) of the fp32 rows ([SD] residual p')."""
+    P = prob_weights(p32).astype(object)
+    Q = prob_weights(q32).astype(object)
+    return np.array([max(0, int(a) - int(b)) for a, b in zip(P, Q)], dtype=np.uint64)
+
+
+def verify(p, q, draft, words, *, temperature, bonus):
+    """Speculative-sampling verify of one sequence.
+
+    p:     [gamma+bonus][V] fp32 target probabilities (T>0) or target logits (T=0)
+    q:     [gamma][V]       fp32 draft probabilities (unused at T=0)
+    draft: [gamma]          drafted tokens
+    words: [gamma+1][2]     uint64 random words; word 0 of row j gives the
+                            accept uniform of position j (its top 24 bits),
+                            word 1 gives the resample/bonus uniform (top 32 bits).
+    Returns (n_accept, next_token) with next_token = -1 when none is produced.
+
+    T = 0 ([SPD] 3.4): accept iff the drafted token is the target argmax; on the
+    first mismatch the argmax is the corrected token.
+    T > 0 ([SD] acceptance criterion): accept position j iff
+    r_j <= min(1, p_j(x_j)/q_j(x_j)); at the first rejection j*, the next token
+    is drawn from norm(max(0, p_j* - q_j*)) (from p_j* if that residual is
+    empty); if all gamma are accepted and a bonus row is present, the next
+    token is drawn from p_gamma.
+    """
+    gamma = len(draft)
+    words = np.asarray(words, dtype=np.uint64)
+    for j in range(gamma):
+        x = int(draft[j])
+        if temperature == 0:
+            best = argmax_first(p[j])
+            if x != best:
+                return j, best
+        else:
+            r24 = int(words[j, 0]) >> 40
+            if not accept_test(p[j][x], q[j][x], r24):
+                u = int(words[j, 1]) >> 32
+                t = sample_weights(residual_weights(p[j], q[j]), u)
+                if t is None:
+                    t = sample_probs(p[j], u)
+                return j, t
+    if not bonus:
+        return gamma, -1
+    if temperature == 0:
+        return gamma, argmax_first(p[gamma])
+    return gamma, sample_probs(p[gamma], int(words[gamma, 1]) >> 32)
+
+
+# --------------------------------------------------------------------------
+# Cycle state machine ([SPD] 3.4 streaming verification and rollback; metrics
+# of [SPD] 4 and the acceptance-length formula of [REV])
+# --------------------------------------------------------------------------
+
+@dataclass
+class SeqState:
+    t: int            # sequence length x_1..x_t
+    a: int            # tokens in flight (1..n)
+    commits: int = 0  # N: tokens that exited the last stage
+    cycles: int = 0   # K: executed pipeline steps
+    tokens: list = field(default_factory=list)
+
+
+def transition(st: SeqState, n: int, drafted: int, verified: bool,
+               n_accept: int, next_token: int) -> SeqState:
+    """End-of-cycle update.
+
+    Saturated cycle (a = n): the oldest in-flight token exits and is committed
+    (N += 1) and its successor was verified.  Accept: the new draft enters
+    stage 1 (t += 1, a stays n).  Reject: keep x_1..x_{t-n+1}, discard the n-1
+    younger in-flight tokens and this cycle's draft, append the corrected
+    token at depth 0 (t = t-n+2, a = 1).
+    Partial cycle (a < n): nothing exits or is verified; the draft joins.
+    """
+    st.cycles += 1
+    if verified:
+        if st.a != n:
+            raise ValueError("only a saturated pipeline verifies")
+        st.commits += 1
+        if n_accept == 0:
+            keep = st.t - n + 1
+            del st.tokens[keep:]
+            st.tokens.append(int(next_token))
+            st.t = keep + 1
+            st.a = 1
+            return st
+    st.tokens.append(int(drafted))
+    st.t += 1
+    st.a = min(st.a + 1, n)
+    return st
+
+
+def step_acceptance(st: SeqState) -> float:
+    """alpha = N / K ([SPD] 4 metrics)."""
+    return st.commits / st.cycles
+
+
+def acceptance_length(st: SeqState, n: int) -> float:
+    """L_acc' = (N / K) * n, the zero-draft-cost theoretical speedup ([REV] core
+    formulas; [SPD] 4)."""
+    return step_acceptance(st) * n
+
+
+def expected_speedup(alpha: float, gamma: int, c: float) -> float:
+    """[SD] theoretical speedup (i.i.d. acceptance alpha, cost ratio c)."""
+    return (1.0 - alpha ** (gamma + 1)) / ((1.0 - alpha) * (gamma * c + 1.0))

@@ -1,0 +1,514 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these re-types the oracle's formula: each checks it against a printed
+value (tests/golden), a closed form, a library routine (torch, transformers,
+numpy), an invariant, or exact counting on a small lattice.
+"""
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import spd as O
+
+
+def _golden(golden_dir, name):
+    with open(os.path.join(golden_dir, name)) as f:
+        return json.load(f)
+
+
+# ------------------------------------------------------------------ P1, P2
+
+@pytest.mark.parametrize("n", [4, 8, 16])
+def test_eligible_sets_L32(golden_dir, n):
+    g = _golden(golden_dir, "eligibility_L32.json")
+    want = g["zero_mask_eligible"][str(n)]
+    for k in range(n + 1):
+        got = [l for l in O.slot_layers(k, 32, n, g["anchors"], O.ZERO_MASK) if l >= 0]
+        assert got == want[k], (n, k)
+
+
+def test_eligible_sets_tiny(golden_dir):
+    g = _golden(golden_dir, "eligibility_L32.json")["tiny"]
+    for k in range(g["n"] + 1):
+        got = [l for l in O.slot_layers(k, g["L"], g["n"], g["anchors"]) if l >= 0]
+        assert got == g["zero_mask_eligible"][k]
+
+
+def test_clamp_min_slots(golden_dir):
+    g = _golden(golden_dir, "eligibility_L32.json")
+    for k, want in enumerate(g["clamp_min_slots_n8"]):
+        assert O.slot_layers(k, 32, 8, g["anchors"], O.CLAMP_MIN) == want
+
+
+def test_eligibility_invariants():
+    B = [0, 8, 16, 24, 31]
+    for n in (2, 4, 8, 16, 32):
+        prev = None
+        for k in range(n + 1):
+            s = {l for l in O.slot_layers(k, 32, n, B) if l >= 0}
+            assert 0 in s                           # the embedding is always there
+            if n <= 16:                             # stage depth >= 2: layer 31 needs all stages
+                assert (31 in s) == (k == n)
+            if prev is not None:
+                assert prev <= s                    # features only get richer with depth
+            prev = s
+    assert O.l_max(0, 32, 8) == 0 and O.l_max(8, 32, 8) == 32
+    assert O.l_max(1, 32, 3) == 10                  # floor of 32/3
+
+
+def test_layouts(golden_dir):
+    g = _golden(golden_dir, "layouts.json")
+    for c in g["cases"]:
+        want = eval(c["depths"], {})  # literal list expressions from the fixture
+        assert O.depths(c["t"], c["a"], c["n"]) == want
+    # the partial-fill layout at a = n is Eq. (2)
+    assert O.depths(40, 8, 8) == [8] * 32 + list(range(7, -1, -1))
+    pos0, pos, dep = O.cycle_rows(2048, 8, 8)
+    assert pos0 == 2039 and len(pos) == 9 and dep == [8, 7, 6, 5, 4, 3, 2, 1, 0]
+    pos0, pos, dep = O.cycle_rows(2048, 3, 8)
+    assert pos0 == 2044 and dep == [8, 2, 1, 0]
+
+
+# ------------------------------------------------------------------ P3, P4
+
+def _fuse_setup(rng, d=16, L=8, n=4, anchors=(0, 4, 7), T=12, mode=O.ZERO_MASK):
+    sl = O.store_layers_for(L, n, anchors, mode)
+    store = rng.standard_normal((T, len(sl), d))
+    m = len(anchors)
+    gamma = rng.uniform(0.5, 1.5, m * d)
+    w = rng.standard_normal((d, m * d)) * 0.1
+    return sl, store, gamma, w
+
+
+def test_k0_is_projection_of_embedding():
+    rng = np.random.default_rng(1)
+    d, L, n, B = 16, 8, 4, (0, 4, 7)
+    sl, store, gamma, w = _fuse_setup(rng, d, L, n, B)
+    g = O.fuse_features(store, sl, [5], [0], gamma, w, L=L, n=n, anchors=B)
+    direct = w[:, :d] @ store[5, sl.index(0)]
+    assert np.allclose(g[0], direct, rtol=0, atol=1e-12)
+    store2 = store.copy()
+    store2[5, 1:] += rng.standard_normal(store2[5, 1:].shape)   # deeper layers change
+    g2 = O.fuse_features(store2, sl, [5], [0], gamma, w, L=L, n=n, anchors=B)
+    assert np.array_equal(g, g2)
+    # clamped mode has the same k = 0 rule
+    sl_c, store_c, _, _ = _fuse_setup(np.random.default_rng(1), d, L, n, B, mode=O.CLAMP_MIN)
+    gc = O.fuse_features(store_c, sl_c, [5], [0], gamma, w, L=L, n=n, anchors=B, mode=O.CLAMP_MIN)
+    assert np.allclose(gc[0], w[:, :d] @ store_c[5, sl_c.index(0)], atol=1e-12)
+
+
+def test_full_depth_feature_is_rmsnorm_then_linear():
+    rng = np.random.default_rng(2)
+    d, L, n, B = 16, 8, 4, (0, 4, 7)
+    sl, store, gamma, w = _fuse_setup(rng, d, L, n, B)
+    g = O.fuse_features(store, sl, [3], [n], gamma, w, L=L, n=n, anchors=B)
+    x = torch.tensor(np.concatenate([store[3, sl.index(b)] for b in B]))
+    ref = F.linear(F.rms_norm(x, (x.numel(),), torch.tensor(gamma), eps=1e-6), torch.tensor(w))
+    assert np.allclose(g[0], ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_partial_depth_feature_uses_eligible_anchors_only():
+    """Zero-mask reading: the norm runs over the concatenation of the eligible
+    anchors and the FC sees zeros in the other slots, i.e. only its columns of
+    the eligible slots act."""
+    rng = np.random.default_rng(3)
+    d, L, n, B = 16, 8, 4, (0, 4, 7)
+    sl, store, gamma, w = _fuse_setup(rng, d, L, n, B)
+    g = O.fuse_features(store, sl, [7], [2], gamma, w, L=L, n=n, anchors=B)   # anchors 0, 4
+    x = torch.tensor(np.concatenate([store[7, sl.index(0)], store[7, sl.index(4)]]))
+    ref = F.linear(F.rms_norm(x, (2 * d,), torch.tensor(gamma[:2 * d]), eps=1e-6),
+                   torch.tensor(w[:, :2 * d]))
+    assert np.allclose(g[0], ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_clamped_feature_is_rmsnorm_of_all_slots():
+    rng = np.random.default_rng(4)
+    d, L, n, B = 16, 32, 8, (0, 8, 16, 24, 31)
+    sl, store, gamma, w = _fuse_setup(rng, d, L, n, B, T=4, mode=O.CLAMP_MIN)
+    g = O.fuse_features(store, sl, [1], [3], gamma, w, L=L, n=n, anchors=B, mode=O.CLAMP_MIN)
+    layers = [0, 8, 12, 12, 12]
+    x = torch.tensor(np.concatenate([store[1, sl.index(l)] for l in layers]))
+    ref = F.linear(F.rms_norm(x, (x.numel(),), torch.tensor(gamma), eps=1e-6), torch.tensor(w))
+    assert np.allclose(g[0], ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------ P5-P7, P9
+
+def _qwen3_layer(d, Hq, Hkv, hd, dff, seed):
+    from transformers import Qwen3Config
+    from transformers.models.qwen3 import modeling_qwen3 as mq
+    torch.manual_seed(seed)
+    c = Qwen3Config(hidden_size=d, intermediate_size=dff, num_attention_heads=Hq,
+                    num_key_value_heads=Hkv, head_dim=hd, rms_norm_eps=1e-6, rope_theta=1e6,
+                    attention_bias=False)
+    c._attn_implementation = "eager"
+    layer = mq.Qwen3DecoderLayer(c, 0).double().requires_grad_(False)
+    for p in layer.parameters():
+        p.normal_(0, 0.05)
+    for nm in ("input_layernorm", "post_attention_layernorm"):
+        getattr(layer, nm).weight.uniform_(0.5, 1.5)
+    layer.self_attn.q_norm.weight.uniform_(0.5, 1.5)
+    layer.self_attn.k_norm.weight.uniform_(0.5, 1.5)
+    a, m = layer.self_attn, layer.mlp
+    lw = dict(attn_norm=layer.input_layernorm.weight.numpy(),
+              wqkv=torch.cat([a.q_proj.weight, a.k_proj.weight, a.v_proj.weight]).numpy(),
+              q_norm=a.q_norm.weight.numpy(), k_norm=a.k_norm.weight.numpy(),
+              wo=a.o_proj.weight.numpy(), mlp_norm=layer.post_attention_layernorm.weight.numpy(),
+              w_gate_up=torch.cat([m.gate_proj.weight, m.up_proj.weight]).numpy(),
+              w_down=m.down_proj.weight.numpy())
+    return c, layer, mq.Qwen3RotaryEmbedding(c), lw
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (4, 2), (6, 2)])
+def test_decoder_layer_matches_transformers_qwen3(Hq, Hkv):
+    d, hd, dff, T, p0 = 64, 16, 256, 9, 11
+    c, layer, rot, lw = _qwen3_layer(d, Hq, Hkv, hd, dff, seed=Hq * 10 + Hkv)
+    x = torch.randn(1, T, d, dtype=torch.float64)
+    pos = torch.arange(p0, p0 + T)[None]
+    cos, sin = rot(x, pos)
+    mask = torch.full((T, T), float("-inf"), dtype=torch.float64).triu(1)[None, None]
+    y = layer(x, attention_mask=mask, position_ids=pos, position_embeddings=(cos, sin))
+    y = y[0] if isinstance(y, tuple) else y
+    h, _, _ = O.decoder_layer(x[0].numpy(), list(range(p0, p0 + T)), lw,
+                              O.PdmConfig(d=d, Hq=Hq, Hkv=Hkv, hd=hd, dff=dff))
+    # transformers builds its rotary tables in float32, hence ~1e-7 agreement
+    assert np.abs(h - y[0].numpy()).max() < 1e-6
+
+
+def test_attention_matches_torch_sdpa():
+    rng = np.random.default_rng(5)
+    c = O.PdmConfig(d=0, Hq=6, Hkv=2, hd=8, dff=0)
+    Tq, P = 5, 7
+    q = rng.standard_normal((Tq, 6, 8))
+    k = rng.standard_normal((P + Tq, 2, 8))
+    v = rng.standard_normal((P + Tq, 2, 8))
+    qpos = list(range(P, P + Tq))
+    out = O._attend(q, k, v, qpos, list(range(P + Tq)), c)
+    kk = torch.tensor(k).repeat_interleave(3, dim=1).permute(1, 0, 2)
+    vv = torch.tensor(v).repeat_interleave(3, dim=1).permute(1, 0, 2)
+    qq = torch.tensor(q).permute(1, 0, 2)
+    mask = torch.arange(P + Tq)[None, :] <= torch.tensor(qpos)[:, None]
+    ref = F.scaled_dot_product_attention(qq, kk, vv, attn_mask=mask).permute(1, 0, 2)
+    assert np.allclose(out, ref.numpy(), atol=1e-12)
+
+
+def test_rope_is_a_rotation_with_relative_phase():
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((3, 2, 16))
+    y = rng.standard_normal((3, 2, 16))
+    for pos in ([0, 5, 900], [3, 1000, 4095]):
+        r = O.rope(x, pos, 1e6)
+        assert np.allclose(np.linalg.norm(r, axis=-1), np.linalg.norm(x, axis=-1), atol=1e-12)
+    # <R_m x, R_n y> depends on m - n only
+    a = np.sum(O.rope(x, [10, 10, 10], 1e6) * O.rope(y, [4, 4, 4], 1e6), axis=-1)
+    b = np.sum(O.rope(x, [106, 106, 106], 1e6) * O.rope(y, [100, 100, 100], 1e6), axis=-1)
+    assert np.allclose(a, b, atol=1e-10)
+    assert np.allclose(O.rope(x, [0, 0, 0], 1e6), x)
+    assert not np.allclose(O.rope(x, [1, 1, 1], 1e6), x)
+
+
+def test_silu_and_rmsnorm_match_torch():
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((4, 32)) * 3
+    assert np.allclose(O.silu(x), F.silu(torch.tensor(x)).numpy(), atol=1e-14)
+    w = rng.uniform(0.5, 1.5, 32)
+    assert np.allclose(O.rms_norm(x, w, 1e-6),
+                       F.rms_norm(torch.tensor(x), (32,), torch.tensor(w), eps=1e-6).numpy(),
+                       atol=1e-13)
+
+
+def _random_pdm(rng, c, Ls):
+    def lw():
+        return dict(attn_norm=rng.uniform(0.5, 1.5, c.d),
+                    wqkv=rng.standard_normal(((c.Hq + 2 * c.Hkv) * c.hd, c.d)) * 0.1,
+                    q_norm=rng.uniform(0.5, 1.5, c.hd), k_norm=rng.uniform(0.5, 1.5, c.hd),
+                    wo=rng.standard_normal((c.d, c.Hq * c.hd)) * 0.1,
+                    mlp_norm=rng.uniform(0.5, 1.5, c.d),
+                    w_gate_up=rng.standard_normal((2 * c.dff, c.d)) * 0.1,
+                    w_down=rng.standard_normal((c.d, c.dff)) * 0.1)
+    return [lw() for _ in range(Ls)], rng.uniform(0.5, 1.5, c.d)
+
+
+def test_incremental_pdm_equals_full_recompute():
+    rng = np.random.default_rng(8)
+    c = O.PdmConfig(d=32, Hq=4, Hkv=2, hd=8, dff=64)
+    layers, fnorm = _random_pdm(rng, c, 2)
+    G = rng.standard_normal((20, 32))
+    cache = O.PdmCache(2, c)
+    last, _ = O.pdm_step(G[:14], 0, cache, layers, fnorm, c)        # prefill
+    assert np.allclose(last, O.pdm_forward(G[:14], layers, fnorm, c), atol=1e-12)
+    # cycle: rows 13..19 recomputed with new features (13 reached full depth)
+    G2 = G.copy()
+    G2[13:] = rng.standard_normal((7, 32))
+    last, _ = O.pdm_step(G2[13:], 13, cache, layers, fnorm, c)
+    assert np.allclose(last, O.pdm_forward(G2, layers, fnorm, c), atol=1e-12)
+    assert cache.length() == 20
+    # a stale row in the cache must change the answer (the cache is really read)
+    cache.k[0][5] += 1.0
+    last2, _ = O.pdm_step(G2[13:], 13, cache, layers, fnorm, c)
+    assert not np.allclose(last2, last)
+
+
+# ------------------------------------------------------------------ P8
+
+def test_argmax_first_and_nan():
+    assert O.argmax_first([1.0, 3.0, 3.0, 2.0]) == 1
+    assert O.argmax_first([np.nan, 1.0, 1.0]) == 1
+    assert O.argmax_first([-np.inf, -np.inf]) == 0
+    x = np.random.default_rng(9).standard_normal(1000)
+    assert O.argmax_first(x) == int(np.argmax(x))
+
+
+def test_softmax_matches_torch():
+    x = np.random.default_rng(10).standard_normal(513) * 3
+    for T in (1.0, 0.7):
+        p = O.softmax(x, T)
+        assert abs(p.sum() - 1) < 1e-12
+        assert np.allclose(p, torch.softmax(torch.tensor(x) / T, 0).numpy(), atol=1e-15)
+
+
+# ------------------------------------------------------------------ P11
+
+def test_sampler_interval_boundaries():
+    """Each j owns exactly the u in [ceil(C_{j-1} 2^32 / S), ceil(C_j 2^32 / S)),
+    C_j the inclusive prefix sums: a reading of 'smallest j with prefix > tau'
+    that is off by one in either direction fails at a boundary."""
+    rng = np.random.default_rng(11)
+    for trial in range(20):
+        w = rng.integers(0, 1 << 40, size=7, dtype=np.uint64)
+        w[rng.integers(0, 7)] = 0
+        S = int(w.sum())
+        C = list(itertools.accumulate(int(v) for v in w))
+        prev = 0
+        for j in range(7):
+            lo = prev
+            hi = -((-C[j] << 32) // S)     # ceil(C_j 2^32 / S)
+            if hi > lo:
+                assert O.sample_weights(w, lo) == j
+                assert O.sample_weights(w, hi - 1) == j
+                assert abs((hi - lo) - int(w[j]) * 2 ** 32 / S) <= 1
+            else:
+                assert int(w[j]) == 0 or (hi - lo) == 0
+            prev = max(prev, hi)
+        assert prev == 2 ** 32
+    assert O.sample_weights(np.zeros(4, np.uint64), 123) is None
+
+
+def test_accept_test_counting():
+    """#{R in [0, 2^24): accept} = min(2^24, floor(2^24 p / q)) for r = (R+1)/2^24,
+    checked at the exact boundary (p, q fp32): P(accept) = min(1, p/q) up to the
+    2^-24 lattice, never above it."""
+    rng = np.random.default_rng(12)
+    for _ in range(200):
+        p = float(np.float32(rng.uniform(0, 1)))
+        q = float(np.float32(rng.uniform(1e-3, 1)))
+        cnt = min(2 ** 24, math.floor(Fraction(p) * 2 ** 24 / Fraction(q)))
+        if 0 < cnt < 2 ** 24:
+            assert O.accept_test(p, q, cnt - 1)
+            assert not O.accept_test(p, q, cnt)
+        elif cnt == 2 ** 24:
+            assert O.accept_test(p, q, 2 ** 24 - 1)
+        else:
+            assert not O.accept_test(p, q, 0)
+    assert O.accept_test(0.0, 0.0, 2 ** 24 - 1)      # q(x) = 0 accepts
+    assert not O.accept_test(0.0, 0.5, 0)            # p(x) = 0 never accepts
+    assert O.accept_test(0.5, 0.5, 2 ** 24 - 1)      # p >= q always accepts
+
+
+# ------------------------------------------------------------------ P12, P13
+
+def _exact_output_distribution(p32, q32, residual_fn):
+    """Exact output law of one verify step when x ~ q: sum over drafts x of
+    q(x)[acc(x) 1{x} + (1-acc(x)) res], with acc counted on the 24-bit R lattice
+    and res counted on the 32-bit U lattice through the sampler's intervals."""
+    V = len(p32)
+    out = [Fraction(0)] * V
+    qf = [Fraction(float(v)) for v in q32]
+    qs = sum(qf)
+    res_w = residual_fn(p32, q32)
+    S = int(res_w.sum())
+    if S == 0:
+        res_w = O.prob_weights(p32)
+        S = int(res_w.sum())
+    C = list(itertools.accumulate(int(v) for v in res_w))
+    res = []
+    prev = 0
+    for j in range(V):
+        hi = -((-C[j] << 32) // S)
+        res.append(Fraction(hi - prev, 2 ** 32))
+        prev = hi
+    for x in range(V):
+        if qf[x] == 0:
+            continue
+        px, qx = float(p32[x]), float(q32[x])
+        cnt = min(2 ** 24, math.floor(Fraction(px) * 2 ** 24 / Fraction(qx)))
+        acc = Fraction(cnt, 2 ** 24)
+        w = qf[x] / qs
+        out[x] += w * acc
+        for j in range(V):
+            out[j] += w * (1 - acc) * res[j]
+    return out
+
+
+def _pq(rng, V):
+    p = rng.dirichlet(np.ones(V) * 0.7).astype(np.float32)
+    q = rng.dirichlet(np.ones(V) * 0.7).astype(np.float32)
+    return p, q
+
+
+def test_verify_output_law_is_exactly_p():
+    rng = np.random.default_rng(13)
+    for V in (2, 5, 8):
+        for _ in range(4):
+            p, q = _pq(rng, V)
+            law = _exact_output_distribution(p, q, O.residual_weights)
+            ps = sum(Fraction(float(v)) for v in p)
+            for j in range(V):
+                assert abs(float(law[j]) - float(Fraction(float(p[j])) / ps)) < V * 2.0 ** -22
+
+
+def test_resampling_from_p_instead_of_residual_is_biased():
+    rng = np.random.default_rng(14)
+    p, q = _pq(rng, 6)
+    law = _exact_output_distribution(p, q, lambda a, b: O.prob_weights(a))
+    assert max(abs(float(law[j]) - float(p[j])) for j in range(6)) > 1e-3
+
+
+def test_verify_monte_carlo_law_and_acceptance():
+    """Monte Carlo through oracle.verify itself: chi-square of the output token
+    against p, and the acceptance rate against sum_x min(p, q) = 1 - TVD."""
+    from scipy import stats
+    rng = np.random.default_rng(15)
+    V, N = 6, 60000
+    p, q = _pq(rng, V)
+    bit = np.random.Philox(key=77)
+    words = bit.random_raw(2 * N).astype(np.uint64).reshape(N, 1, 2)
+    words = np.concatenate([words, np.zeros((N, 1, 2), np.uint64)], axis=1)
+    drafts = rng.choice(V, size=N, p=q.astype(np.float64) / q.sum())
+    counts = np.zeros(V)
+    acc = 0
+    for i in range(N):
+        na, nt = O.verify([p], [q], [int(drafts[i])], words[i], temperature=1.0, bonus=False)
+        tok = int(drafts[i]) if na == 1 else nt
+        acc += na
+        counts[tok] += 1
+    pe = p.astype(np.float64) / p.sum()
+    chi = ((counts - N * pe) ** 2 / (N * pe)).sum()
+    assert chi < stats.chi2.ppf(0.999, V - 1)
+    alpha = np.minimum(pe, q / q.sum()).sum()
+    assert abs(acc / N - alpha) < 4 * math.sqrt(alpha * (1 - alpha) / N)
+
+
+def test_all_accept_probability_example(golden_dir):
+    """alpha^K with K = 5, alpha = 0.8 rounds to the 33% printed on the SSD page.
+    Built from five positions whose sum_x min(p, q) is exactly 0.8 and counted
+    exactly through the accept test."""
+    g = _golden(golden_dir, "acceptance_examples.json")["all_accept"]
+    p = np.array([0.5, 0.5, 0.0, 0.0], np.float32)
+    q = np.array([0.5, 0.3, 0.2, 0.0], np.float32)   # sum min = 0.8
+    alpha = Fraction(0)
+    for x in range(4):
+        if q[x] > 0:
+            cnt = min(2 ** 24, math.floor(Fraction(float(p[x])) * 2 ** 24 / Fraction(float(q[x]))))
+            alpha += Fraction(float(q[x])) * Fraction(cnt, 2 ** 24)
+    assert abs(float(alpha) - g["alpha"]) < 1e-6
+    assert round(100 * float(alpha) ** g["K"]) == g["probability_rounded_percent"]
+    # and through the oracle's gamma-form verify (Monte Carlo on 5 i.i.d. positions)
+    rng = np.random.default_rng(16)
+    N, K = 20000, g["K"]
+    words = np.random.Philox(key=5).random_raw(N * (K + 1) * 2).astype(np.uint64).reshape(N, K + 1, 2)
+    drafts = rng.choice(4, size=(N, K), p=q.astype(np.float64))
+    P = [p] * (K + 1)
+    Q = [q] * K
+    full = sum(O.verify(P, Q, list(drafts[i]), words[i], temperature=1.0, bonus=True)[0] == K
+               for i in range(N))
+    a5 = g["alpha"] ** K
+    assert abs(full / N - a5) < 4 * math.sqrt(a5 * (1 - a5) / N)
+
+
+def test_expected_tokens_per_iteration_matches_speedup_formula():
+    """At c = 0 the explainer's speedup is the expected tokens per iteration,
+    sum_{j<=gamma} alpha^j, bounded by gamma + 1."""
+    p = np.array([0.5, 0.5, 0.0, 0.0], np.float32)
+    q = np.array([0.5, 0.3, 0.2, 0.0], np.float32)
+    gamma, N = 4, 20000
+    rng = np.random.default_rng(17)
+    words = np.random.Philox(key=9).random_raw(N * (gamma + 1) * 2).astype(np.uint64)
+    words = words.reshape(N, gamma + 1, 2)
+    drafts = rng.choice(4, size=(N, gamma), p=q.astype(np.float64))
+    tok = [O.verify([p] * (gamma + 1), [q] * gamma, list(drafts[i]), words[i],
+                    temperature=1.0, bonus=True)[0] + 1 for i in range(N)]
+    e = O.expected_speedup(0.8, gamma, 0.0)
+    assert abs(e - sum(0.8 ** j for j in range(gamma + 1))) < 1e-12
+    assert abs(np.mean(tok) - e) < 4 * np.std(tok) / math.sqrt(N)
+    assert O.expected_speedup(0.999999, gamma, 0.0) < gamma + 1
+
+
+def test_greedy_verify():
+    p = np.array([[0.1, 2.0, 2.0, -1.0], [5.0, 0.0, 0.0, 0.0], [0.0, 0.0, 0.0, 9.0]])
+    w = np.zeros((3, 2), np.uint64)
+    assert O.verify(p, None, [1, 0], w, temperature=0, bonus=True) == (2, 3)
+    assert O.verify(p, None, [2, 0], w, temperature=0, bonus=True) == (0, 1)
+    assert O.verify(p, None, [1, 3], w, temperature=0, bonus=False) == (1, 0)
+    assert O.verify(p[:2], None, [1, 0], w, temperature=0, bonus=False) == (2, -1)
+
+
+def test_degenerate_residual_falls_back_to_p():
+    """Rows need not be normalised: with p = 0.3, q = 0.6 everywhere the residual
+    max(0, P - Q) is empty, a high R rejects, and the next token is drawn from p."""
+    p = np.array([0.3, 0.3], np.float32)
+    q = np.array([0.6, 0.6], np.float32)
+    assert O.sample_weights(O.residual_weights(p, q), 5) is None
+    hi_r = np.uint64(0xFFFFFF) << np.uint64(40)
+    for u, want in ((0, 0), ((1 << 31) - 1, 0), (1 << 31, 1), ((1 << 32) - 1, 1)):
+        w = np.array([[hi_r, np.uint64(u) << np.uint64(32)], [0, 0]], np.uint64)
+        assert O.verify([p], [q], [0], w, temperature=1.0, bonus=False) == (0, want)
+    lo_r = np.array([[0, 0], [0, 0]], np.uint64)                  # R = 0 accepts (1*0.6 <= 0.3*2^24)
+    assert O.verify([p], [q], [0], lo_r, temperature=1.0, bonus=False) == (1, -1)
+
+
+# ------------------------------------------------------------------ P14, rollback
+
+def _simulate(n, beta, cycles, seed):
+    rng = np.random.default_rng(seed)
+    st = O.SeqState(t=n + 1, a=1, tokens=list(range(n + 1)))
+    for _ in range(cycles):
+        if st.a == n:
+            ok = rng.random() < beta
+            O.transition(st, n, 0, True, 1 if ok else 0, 1)
+        else:
+            O.transition(st, n, 0, False, 0, -1)
+    return st
+
+
+@pytest.mark.parametrize("n,beta", [(8, 0.8), (16, 0.5), (4, 1.0), (4, 0.0)])
+def test_step_acceptance_closed_form(n, beta):
+    """Each rejection costs n-1 commit-free refill cycles, so under a Bernoulli(beta)
+    verifier N/K -> 1 / (1 + (1-beta)(n-1)); L_acc' = (N/K) n."""
+    st = _simulate(n, beta, 200000, seed=n)
+    want = 1.0 / (1.0 + (1.0 - beta) * (n - 1))
+    assert abs(O.step_acceptance(st) - want) < 0.01
+    assert abs(O.acceptance_length(st, n) - want * n) < 0.01 * n
+
+
+def test_rollback_truncates_to_t_minus_n_plus_1():
+    n = 4
+    st = O.SeqState(t=32, a=4, tokens=list(range(100, 132)))
+    O.transition(st, n, drafted=999, verified=True, n_accept=0, next_token=7)
+    assert st.t == 30 and st.a == 1                         # kept t-n+1 = 29, + corrected
+    assert st.tokens == list(range(100, 129)) + [7]
+    assert st.commits == 1 and st.cycles == 1
+    verified = []
+    for _ in range(n - 1):                                  # refill: no verification
+        verified.append(st.a == n)
+        O.transition(st, n, drafted=5, verified=False, n_accept=0, next_token=-1)
+    assert verified == [False] * (n - 1) and st.a == n
+    O.transition(st, n, drafted=6, verified=True, n_accept=1, next_token=-1)
+    assert st.a == n and st.t == 34 and st.tokens[-1] == 6 and st.commits == 2
