@@ -1,0 +1,239 @@
+"""Benchmark of the SPD draft-and-verify cycle on one MI355X.
+
+A step is one cycle of the headline workload (Qwen3.5-4B-shaped PDM with d = 2560,
+n = 8 stages, L_s = 2 layers, vocabulary 151936, T = 1, context 2048): anchor
+gather + RMSNorm + FC, the PDM step, the draft head with sampling, and -- in
+saturated cycles -- the target head, streaming verify and rollback.  Cycles run
+in independent mode: each cycle's in-flight count comes from a seeded schedule
+(50% saturated, 50% partial fill with a ~ U{1..7}), so no host round trip sits
+inside the timed region.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def algorithmic_bytes(s, a: int) -> dict:
+    """Bytes one cycle must move, by call (weights once, KV read, anchors, rows)."""
+    esz = 2 if s.dtype == 1 else 4
+    d, m, n, V = s.d, s.m, s.n, s.V
+    M = a + 1
+    pos0 = s.ctx - 1 - a
+    depths = [n] + list(range(a - 1, -1, -1))
+    eligible = []
+    for k in depths:
+        if k == 0:
+            eligible.append(1)
+        else:
+            lm = min(s.L, (k * s.L) // n)
+            eligible.append(sum(1 for b in s.anchors if b <= lm))
+    fc = d * m * d * esz + sum(eligible) * d * esz + M * d * 4
+    layer_w = ((s.Hq + 2 * s.Hkv) * s.hd * d + d * s.Hq * s.hd + 2 * s.dff * d + d * s.dff) * esz
+    kv_read = (pos0 + M) * 2 * s.Hkv * s.hd * esz
+    pdm = s.Ls * (layer_w + kv_read) + M * d * 4 * 2
+    head = V * d * esz + d * 4 + V * 4 * (3 if s.temperature > 0 else 1)
+    out = {"fuse": fc, "pdm": pdm, "draft_head": head}
+    if a == n:
+        out["target_head"] = head
+        out["verify"] = 2 * 4 + (2 * V * 4 if s.temperature > 0 else V * 4)
+    return out
+
+
+def cpu_baseline(s, ci, sched, words, qstand_np, x, budget_s=12.0):
+    """The oracle (numpy float64, incremental PDM) on this host, on a time-bounded
+    sample of the same cycles."""
+    from oracle import cycle as OC
+    from oracle import spd as O
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    om = OC.model_from_inputs(ci)
+    k, v = synth.kv_cache(s, ci.T_cap, device=ci.store.device)
+    kk = k.float().cpu().numpy().astype(np.float64)
+    vv = v.float().cpu().numpy().astype(np.float64)
+    t = s.ctx
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        a = sched[done % len(sched)]
+        pos0 = t - 1 - a
+        cache = O.PdmCache(s.Ls, om.pdm)
+        cache.k = [kk[l].transpose(1, 0, 2)[:pos0] for l in range(s.Ls)]
+        cache.v = [vv[l].transpose(2, 0, 1)[:pos0] for l in range(s.Ls)]
+        tokens = list(range(t))
+        tokens[t - s.n + 1] = x
+        st = O.SeqState(t=t, a=a, tokens=tokens)
+        OC.run_cycle(om, st, cache, {}, s.temperature, words[done % len(words)],
+                     q_override=qstand_np)
+        done += 1
+        el = time.perf_counter() - t0
+        if (el >= budget_s and done >= 4) or done >= 200:
+            break
+    return {"value": done / el, "unit": "cycles/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} cycles of the same schedule (numpy float64 oracle, incremental PDM "
+                      f"on a seeded committed cache), {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only (the cycle is a single-GPU "
+              "hot path); --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import pipeline_draft_step_amd as spd
+    from pipeline_draft_step_amd.cycle import DeviceWeights, SpdCycle, SpdModel
+
+    spd.lib()
+    dev = "cuda"
+    s = synth.HEADLINE
+    ci = synth.cycle_inputs(s, device=dev)
+    w = DeviceWeights(store=ci.store, h_final=ci.h_final, fc_norm=ci.fc_norm, w_fc=ci.w_fc,
+                      layers=ci.layers, final_norm=ci.final_norm, w_dlm=ci.w_dlm, w_tlm=ci.w_tlm)
+    model = SpdModel(L=s.L, n=s.n, anchors=s.anchors, d=s.d, Ls=s.Ls, Hq=s.Hq, Hkv=s.Hkv,
+                     hd=s.hd, dff=s.dff, V=s.V, dtype=s.dtype, weights=w, eps=s.eps,
+                     rope_theta=s.rope_theta)
+    cyc = SpdCycle(model, s.temperature, device=dev)
+    t = s.ctx
+    cyc.set_state(t, s.n, list(range(t)))
+    cyc.prefill(t - 1 - s.n)
+
+    total = args.warmup + args.steps
+    sched = synth.cycle_schedule(s, total)
+    words_np = synth.cycle_words(total)
+    words = synth.words_tensor(words_np, dev)
+    qstand = torch.softmax(synth.draft_row_logits(s.V, 3.0, device=dev, seed=8, name="q_standin"), 0)
+    xg = torch.Generator(device=dev)
+    xg.manual_seed(99)
+    x_dev = torch.multinomial(qstand, 1, generator=xg).to(torch.int32)
+    x = int(x_dev.item())
+    torch.cuda.synchronize()
+
+    for c in range(args.warmup):
+        cyc.cycle(t, sched[c], words[c], q_row=qstand, x_ptr=x_dev.data_ptr())
+    torch.cuda.synchronize()
+
+    # timed region: K cycles; events bracket the draft-head call of every cycle
+    head_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        c = args.warmup + i
+        a = sched[c]
+        n = s.n
+        pos0, M = t - 1 - a, a + 1
+        cyc.features(pos0, M, a)
+        cyc.pdm(pos0, M)
+        head_ev[i][0].record()
+        cyc.draft(t, words[c])
+        head_ev[i][1].record()
+        if a == n:
+            cyc.target_and_verify(t, words[c], q_row=qstand, x_ptr=x_dev.data_ptr())
+        cyc.rollback()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = start.elapsed_time(stop)
+    ms_per_step = ms / args.steps
+    cycles_per_s = 1000.0 / ms_per_step
+    head_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in head_ev]))
+
+    timed = sched[args.warmup:]
+    cyc_bytes = [sum(algorithmic_bytes(s, a).values()) for a in timed]
+    mean_bytes = float(np.mean(cyc_bytes))
+    head_bytes = algorithmic_bytes(s, s.n)["draft_head"]
+    achieved = head_bytes / (head_ms * 1e-3) / 1e9
+
+    # per-call breakdown (separate instrumented pass over one saturated and one partial cycle)
+    calls = {}
+    for a in (s.n, 3):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
+        reps = 20
+        acc = np.zeros(6)
+        for r in range(reps):
+            c = r % total
+            pos0, M = t - 1 - a, a + 1
+            ev[0].record()
+            cyc.features(pos0, M, a)
+            ev[1].record()
+            cyc.pdm(pos0, M)
+            ev[2].record()
+            cyc.draft(t, words[c])
+            ev[3].record()
+            if a == s.n:
+                cyc.target_and_verify(t, words[c], q_row=qstand, x_ptr=x_dev.data_ptr())
+            ev[4].record()
+            cyc.rollback()
+            ev[5].record()
+            torch.cuda.synchronize()
+            acc += [ev[i].elapsed_time(ev[i + 1]) for i in range(5)] + [ev[0].elapsed_time(ev[5])]
+        acc = acc / reps * 1000.0
+        calls["saturated" if a == s.n else f"partial_a{a}"] = {
+            "fuse_us": round(acc[0], 1), "pdm_us": round(acc[1], 1),
+            "draft_head_us": round(acc[2], 1), "target_head_verify_us": round(acc[3], 1),
+            "rollback_us": round(acc[4], 1), "cycle_us": round(acc[5], 1),
+            "algorithmic_MB": round(sum(algorithmic_bytes(s, a).values()) / 1e6, 1)}
+
+    result = {
+        "metric": "draft+verify cycles/s + achieved HBM GB/s, d=2560 n=8 vocab 151936, 1 GPU",
+        "value": round(cycles_per_s, 2),
+        "unit": "cycles/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "spd_cycle_qwen35_4b_shape_n8_ls2_t1_mix", "d": s.d, "n": s.n,
+                   "L": s.L, "anchors": list(s.anchors), "Ls": s.Ls, "heads": [s.Hq, s.Hkv, s.hd],
+                   "dff": s.dff, "vocab": s.V, "context": s.ctx, "temperature": s.temperature,
+                   "mix": "50% saturated / 50% partial a~U{1..7}", "batch": 1,
+                   "mode": "independent cycles"},
+        "achieved_hbm_gbs": round(mean_bytes * cycles_per_s / 1e9, 1),
+        "algorithmic_MB_per_cycle": round(mean_bytes / 1e6, 2),
+        "roofline": {"bound": "hbm", "kernel": "spd_lm_head (vocab GEMV + softmax/sample)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_us": round(head_ms * 1000.0, 2),
+                     "algorithmic_bytes_per_launch": int(head_bytes)},
+        "calls": calls,
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(s, ci, timed[:64],
+                                              words_np[args.warmup:], qstand.cpu().numpy(), x,
+                                              budget_s=args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

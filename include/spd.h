@@ -1,0 +1,229 @@
+/*
+ * spd.h -- C ABI of the SPD draft-and-verify cycle for AMD Instinct MI355X (gfx950).
+ *
+ * Speculative Pipeline Decoding ("Speculative Pipeline Decoding: Higher-Accuracy
+ * Drafting with Hidden Latency via Pipeline Parallelism", arXiv 2605.30852) drafts
+ * one token per pipeline cycle from depth-conditioned features of the tokens in
+ * flight, and verifies one in-flight token per cycle.  One cycle on the draft
+ * rank is:
+ *
+ *   spd_fuse_features   anchor gather + RMSNorm + FC  -> features g   (section 3.2)
+ *   spd_pdm_step        L_s-layer Qwen3-style decoder  -> h_last       (section 3.1)
+ *   spd_lm_head         draft head, argmax or sample   -> x_hat, q row (section 3.1, Eq. (1))
+ *   spd_lm_head         target head on the exiting token's last state  (section 3.4)
+ *   spd_verify          greedy match / rejection sampling             (section 3.4)
+ *   spd_rollback        commit, or truncate to t-n+1 and reseed        (section 3.4)
+ *
+ * Conventions shared by every call
+ *  - Pointers marked DEVICE are device pointers owned by the caller; pointers marked
+ *    HOST are read during the call only.  Nothing is retained after return.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Calls enqueue kernels on it
+ *    and return without synchronising; they never allocate or free memory.
+ *  - Argument errors are detected on the host and returned before anything is
+ *    enqueued.  Values held in device memory (tokens, probabilities) are not
+ *    inspected on the host; kernels clamp out-of-range indices so that no access
+ *    leaves the buffers described below.
+ *  - Workspaces: `ws` is a DEVICE buffer of at least spd_workspace_size(...) bytes,
+ *    256-byte aligned.  Its first SPD_WS_COUNTER_BYTES bytes hold arrival counters
+ *    that must be zero before the workspace is first used (allocate it zero-filled);
+ *    every call leaves them zero again.  Calls that share a workspace must not run
+ *    concurrently (use one workspace per stream).
+ *  - dtype SPD_BF16: weights, anchors and the key/value cache are bfloat16 (bit
+ *    pattern in uint16); SPD_F32: all of them are float32.  Features, hidden rows,
+ *    logits and probabilities are always float32.
+ *  - Return value: SPD_OK (0) or a negative status; spd_status_string() names it.
+ */
+#ifndef SPD_H
+#define SPD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  SPD_OK = 0,
+  SPD_E_INVALID = -1,     /* null pointer, bad size or inconsistent arguments */
+  SPD_E_UNSUPPORTED = -2, /* valid but not implemented shape/dtype combination */
+  SPD_E_WORKSPACE = -3,   /* ws_bytes below spd_workspace_size()               */
+  SPD_E_HIP = -4          /* a HIP launch failed; see spd_last_hip_error()      */
+};
+
+enum { SPD_F32 = 0, SPD_BF16 = 1 };
+enum { SPD_ANCHOR_ZERO_MASK = 0, SPD_ANCHOR_CLAMP_MIN = 1 };
+enum { SPD_CALL_FUSE = 0, SPD_CALL_PDM = 1, SPD_CALL_LM_HEAD = 2, SPD_CALL_VERIFY = 3 };
+
+#define SPD_WS_COUNTER_BYTES 65536
+#define SPD_MAX_ANCHORS 8
+#define SPD_MAX_STAGES 32
+
+/* Sizes of the target, the PDM and the heads (section 3.1-3.2, section 4 setup). */
+typedef struct spd_config {
+  int32_t L;           /* target layers                                          */
+  int32_t n;           /* pipeline stages (1..SPD_MAX_STAGES)                    */
+  int32_t m;           /* anchors (1..SPD_MAX_ANCHORS)                           */
+  int32_t d;           /* hidden size of target and PDM                          */
+  int32_t Ls;          /* PDM decoder layers                                     */
+  int32_t Hq, Hkv, hd; /* PDM query heads, key/value heads, head size (16..128)  */
+  int32_t dff;         /* PDM MLP width                                          */
+  int32_t V;           /* vocabulary                                             */
+  int32_t dtype;       /* SPD_F32 or SPD_BF16                                    */
+  int32_t anchor_mode; /* SPD_ANCHOR_ZERO_MASK (default) or SPD_ANCHOR_CLAMP_MIN  */
+  int32_t norm_k0;     /* 0: g^0 = FC(H^0) without norm (default); 1: normalise  */
+  float rms_eps;       /* 1e-6                                                   */
+  float rope_theta;    /* 1e6                                                    */
+} spd_config;
+
+/* One PDM decoder layer (DEVICE pointers, cfg.dtype).  Row-major [rows][cols]. */
+typedef struct spd_layer_weights {
+  const void *attn_norm; /* [d]                                              */
+  const void *wqkv;      /* [(Hq+2*Hkv)*hd][d]: q heads, then k heads, then v  */
+  const void *q_norm;    /* [hd]                                             */
+  const void *k_norm;    /* [hd]                                             */
+  const void *wo;        /* [d][Hq*hd]                                       */
+  const void *mlp_norm;  /* [d]                                              */
+  const void *w_gate_up; /* [2*dff][d]: gate rows, then up rows              */
+  const void *w_down;    /* [d][dff]                                         */
+} spd_layer_weights;
+
+/* Sequence state kept in DEVICE memory by spd_rollback. */
+typedef struct spd_seq_state {
+  int32_t t;       /* sequence length (verified prefix + in-flight tokens) */
+  int32_t a;       /* tokens in flight, 1..n                               */
+  int32_t commits; /* N: tokens that exited the last stage                  */
+  int32_t cycles;  /* K: executed cycles                                    */
+} spd_seq_state;
+
+/* ---------------------------------------------------------------- host helpers */
+
+/* Anchor eligibility (section 3.2, Eq. (3); the review blog's core formulas for the
+ * clamped variant).  l_max(k) = min(L, floor(k*L/n)).  For every depth k in 0..n and
+ * anchor j, writes slot_tab[k*m + j] = index into `store_layers` of the target layer
+ * slot j reads at depth k, or -1 for an empty slot:
+ *   ZERO_MASK: layer b_j if b_j <= l_max(k), else empty;
+ *   CLAMP_MIN: layer min(b_j, l_max(k));
+ *   k = 0 (both modes): slot 0 reads layer 0 (the embedding), the rest are empty.
+ * store_layers (HOST, capacity L+1) receives the sorted distinct layers an anchor
+ * store must hold; *n_store their count.  anchors (HOST [m]) must be strictly
+ * increasing with anchors[0] = 0 and anchors[m-1] <= L.
+ */
+int spd_slot_table(const spd_config *cfg, const int32_t *anchors, int32_t *slot_tab,
+                   int32_t *store_layers, int32_t *n_store);
+
+/* Rows one cycle recomputes (section 3.1 Eq. (2), section 3.2 partial fill, section 3.3
+ * pre-step depths).  With t tokens and a in flight (1 <= a <= n, a < t): M = a+1 rows
+ * at positions pos0 = t-1-a .. t-1; the first is fully processed (depth n) and the
+ * in-flight ones have depths a-1 .. 0.  Writes pos[M], depth[M] (HOST) and returns M,
+ * or SPD_E_INVALID. */
+int spd_layout(int32_t t, int32_t a, int32_t n, int32_t *pos, int32_t *depth);
+
+/* Bytes of workspace a call needs.  call: SPD_CALL_*; rows = M for FUSE and PDM, the
+ * number of head rows for LM_HEAD, B for VERIFY (then gamma and cfg->V are used);
+ * T_cap is the key/value cache capacity of the PDM call (ignored by the others).
+ * Returns 0 for invalid arguments. */
+size_t spd_workspace_size(int32_t call, const spd_config *cfg, int32_t rows, int32_t gamma,
+                          int64_t T_cap);
+
+/* ---------------------------------------------------------------- cycle calls */
+
+/* Depth-conditioned features (section 3.2 Eq. (3); review blog core formulas:
+ * g = FC(norm(Concat(anchors)))).
+ * Rows are positions pos0 .. pos0+M-1; the last `a` of them have depths a-1 .. 0 and
+ * the others depth n (so a = 0 means all rows are fully processed, e.g. prefill).
+ * For a row at position i and depth k:
+ *   k = 0 and !norm_k0: g = W_fc[:, 0:d] . H_i^{layer 0}     (no norm, no gamma)
+ *   otherwise: x = Concat_j (slot_tab[k*m+j] >= 0 ? H_i^{store slot} : 0),
+ *              rms = sqrt(sum(x^2) / (#filled * d) + eps),  g = W_fc (norm_w * x / rms)
+ * hstore  DEVICE [T_cap][S][d]  anchor hidden states, slot s holds store_layers[s]
+ * slot_tab HOST [(n+1)*m]       as written by spd_slot_table (any table of slots < S)
+ * norm_w  DEVICE [m*d]; fc_w DEVICE [d][m*d]; g DEVICE float [M][d] (output).
+ * Requires d % 64 == 0, pos0 >= 0, pos0+M <= T_cap, 0 <= a <= min(n, M).
+ */
+int spd_fuse_features(const spd_config *cfg, const void *hstore, int64_t T_cap, int32_t S,
+                      const int32_t *slot_tab, int32_t pos0, int32_t M, int32_t a,
+                      const void *norm_w, const void *fc_w, float *g,
+                      void *ws, size_t ws_bytes, void *stream);
+
+/* PDM step (section 3.1: f_theta is an Ls-layer decoder with Qwen3-style attention; the
+ * draft reads its last-position output).  Each layer (pre-norm):
+ *   h += W_o . Attn(RoPE(qnorm(W_q n1)), RoPE(knorm(W_k n1)), W_v n1),  n1 = RMSNorm(h)
+ *   h += W_down (silu(W_gate n2) * (W_up n2)),                           n2 = RMSNorm(h)
+ * with GQA (query head h reads kv head h / (Hq/Hkv)), rotate-half RoPE at 0-based
+ * positions, scale 1/sqrt(hd), and a causal mask.  Input rows h = g at positions
+ * pos0 .. pos0+M-1 attend to cached positions < pos0 and to each other.  The call
+ * writes this call's keys/values at positions pos0 .. pos0+M-1 (later cycles treat
+ * positions below their own pos0 as committed).
+ * layers   HOST [Ls]; final_norm DEVICE [d]
+ * k_cache  DEVICE [Ls][Hkv][T_cap][hd]      keys (normed, rotated)
+ * v_cache  DEVICE [Ls][Hkv][hd][T_cap]      values, position-minor
+ * g        DEVICE float [M][d]; h_last DEVICE float [d] = final RMSNorm of row M-1.
+ * Requires d % 64 == 0, hd in {16,32,64,128}, Hq % Hkv == 0, dff % 64 == 0,
+ * T_cap % 8 == 0, pos0 + M <= T_cap.
+ */
+int spd_pdm_step(const spd_config *cfg, const spd_layer_weights *layers, const void *final_norm,
+                 void *k_cache, void *v_cache, int64_t T_cap, const float *g, int32_t pos0,
+                 int32_t M, float *h_last, void *ws, size_t ws_bytes, void *stream);
+
+/* LM head and next-token choice (section 3.1 Eq. (1); section 3.4 target head).
+ * logits[r] = W_lm . h[r] for r < rows (rows <= 16).
+ * temperature == 0: token[r] = lowest index of the maximum logit (NaN never wins);
+ *   probs may be NULL and words is unused.
+ * temperature > 0: probs[r] = softmax(logits[r] / T) (float32) and
+ *   token[r] = inverse-CDF draw from the integer weights w_j = floor(probs_j * 2^52):
+ *   u = words[r] >> 32, tau = floor(u * sum(w) / 2^32), token = smallest j whose
+ *   inclusive prefix sum of w exceeds tau.
+ * w_lm DEVICE [V][d] (cfg.dtype); h DEVICE float [rows][d]; words DEVICE uint64 [rows];
+ * logits, probs DEVICE float [rows][V]; token DEVICE int32 [rows].
+ */
+int spd_lm_head(const spd_config *cfg, const void *w_lm, const float *h, int32_t rows,
+                float temperature, const uint64_t *words, float *logits, float *probs,
+                int32_t *token, void *ws, size_t ws_bytes, void *stream);
+
+/* Verification (section 3.4 streaming verify; the speculative-decoding explainer's
+ * four-phase loop and acceptance criterion).  For each sequence b < B and drafted
+ * positions j = 0 .. gamma-1 in order, until the first rejection:
+ *   T == 0: accept iff draft[b][j] is the argmax of p[b][j] (p holds logits); on a
+ *           mismatch the argmax is the next token.
+ *   T > 0:  R = words[b][j][0] >> 40; accept iff (R+1) * q(x) <= p(x) * 2^24, i.e.
+ *           r <= min(1, p/q) for r = (R+1)/2^24, decided exactly.  On rejection the
+ *           next token is drawn (as in spd_lm_head, with u = words[b][j][1] >> 32)
+ *           from the integer residual max(0, P_i - Q_i), P = floor(p*2^52),
+ *           Q = floor(q*2^52); from P itself if that residual is all zero.
+ * If all gamma drafts are accepted: next = bonus ? draw from p[b][gamma] (argmax at
+ * T == 0; u = words[b][gamma][1] >> 32) : -1.
+ * p DEVICE float [B][gamma+bonus][V]; q DEVICE float [B][gamma][V] (unused at T == 0);
+ * draft DEVICE int32 [B][gamma]; words DEVICE uint64 [B][gamma+1][2];
+ * n_accept, next_token DEVICE int32 [B] (outputs).  SPD streaming verify is
+ * B = 1, gamma = 1, bonus = 0.
+ */
+int spd_verify(int32_t B, int32_t gamma, int32_t V, float temperature, int32_t bonus,
+               const float *p, const float *q, const int32_t *draft, const uint64_t *words,
+               int32_t *n_accept, int32_t *next_token, void *ws, size_t ws_bytes,
+               void *stream);
+
+/* End-of-cycle commit or rollback (section 3.4; review blog, synchronous rollback),
+ * one thread on the device, reading the state the cycle started from:
+ *   a == n (the cycle verified; n_accept[0], next_token[0] are its outcome):
+ *     commits += 1;
+ *     rejected (n_accept[0] == 0): keep x_1..x_{t-n+1}, discard the n-1 younger
+ *       in-flight tokens and this cycle's draft, append next_token[0] at depth 0:
+ *       tokens[t-n+1] = next_token[0]; t = t-n+2; a = 1.
+ *     accepted: tokens[t] = drafted[0]; t += 1 (a stays n).
+ *   a < n: tokens[t] = drafted[0]; t += 1; a += 1.
+ *   cycles += 1 in every case.  Writes at or beyond T_cap are dropped.
+ * st DEVICE; drafted, n_accept, next_token DEVICE int32 [1]; tokens DEVICE int32 [T_cap].
+ */
+int spd_rollback(spd_seq_state *st, int32_t n, const int32_t *drafted, const int32_t *n_accept,
+                 const int32_t *next_token, int32_t *tokens, int64_t T_cap, void *stream);
+
+const char *spd_status_string(int status);
+int spd_last_hip_error(void);
+int spd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPD_H */

@@ -63,9 +63,9 @@ def run_cycle(om: OracleModel, st: O.SeqState, cache: O.PdmCache, ring: dict,
               probs_from=None) -> CycleOut:
     """Run one cycle from state `st` and apply the end-of-cycle transition.
 
-    words: [2, 4] uint64 (one 4-word block for this cycle's verify, one for the
-    draft): words[0,0] accept uniform, words[0,1] resample uniform,
-    words[1,2] draft-sampling uniform (top 32 bits of each).
+    words: [4] uint64 block of this cycle: word 0 accept uniform (top 24 bits),
+    word 1 resample uniform (top 32 bits), word 2 draft-sampling uniform (top 32
+    bits).
     ring: position -> fp32 draft row q of the token drafted at that position.
     q_override: fp32 row to verify against instead of the ring's (independent
     cycles have no ring history).
@@ -86,7 +86,7 @@ def run_cycle(om: OracleModel, st: O.SeqState, cache: O.PdmCache, ring: dict,
         q = O.softmax(dl, temperature).astype(np.float32)
         if probs_from is not None and "q" in probs_from:
             q = probs_from["q"]
-        drafted = O.sample_probs(q, int(words[1, 2]) >> 32)
+        drafted = O.sample_probs(q, int(words[2]) >> 32)
         ring[st.t] = q
     out = CycleOut(pos0=pos0, depths=dep, g=g, h_last=h_last, draft_logits=dl, q=q,
                    drafted=drafted, verified=(st.a == n))
@@ -96,15 +96,16 @@ def run_cycle(om: OracleModel, st: O.SeqState, cache: O.PdmCache, ring: dict,
         tl = O.lm_logits(om.w_tlm, om.h_final[exiting])
         out.target_logits = tl
         x = st.tokens[cand]
+        vwords = np.asarray(words, dtype=np.uint64).reshape(2, 2)
         if temperature == 0:
-            na, nt = O.verify([tl], None, [x], words[:, :2], temperature=0, bonus=False)
+            na, nt = O.verify([tl], None, [x], vwords, temperature=0, bonus=False)
         else:
             p = O.softmax(tl, temperature).astype(np.float32)
             if probs_from is not None and "p" in probs_from:
                 p = probs_from["p"]
             out.p = p
             qrow = q_override if q_override is not None else ring[cand]
-            na, nt = O.verify([p], [qrow], [x], words[:, :2], temperature=temperature,
+            na, nt = O.verify([p], [qrow], [x], vwords, temperature=temperature,
                               bonus=False)
         out.n_accept, out.next_token = na, nt
     O.transition(st, n, drafted, out.verified, out.n_accept, out.next_token)

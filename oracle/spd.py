@@ -361,9 +361,9 @@ def accept_test(p_x, q_x, r24):
 
 def residual_weights(p32, q32):
     """Integer residual max(0, P - Q) of the fp32 rows ([SD] residual p')."""
-    P = prob_weights(p32).astype(object)
-    Q = prob_weights(q32).astype(object)
-    return np.array([max(0, int(a) - int(b)) for a, b in zip(P, Q)], dtype=np.uint64)
+    P = prob_weights(p32)
+    Q = prob_weights(q32)
+    return np.where(P > Q, P - Q, np.uint64(0)).astype(np.uint64)
 
 
 def verify(p, q, draft, words, *, temperature, bonus):

@@ -1,0 +1,472 @@
+// spd_pdm_step: the Pipeline Draft Module, an Ls-layer Qwen3-style decoder
+// ("Speculative Pipeline Decoding", arXiv 2605.30852, section 3.1) run over the
+// M rows a cycle recomputes, attending to the committed key/value cache.
+//
+// Per layer (5 launches + attention combine):
+//   QKV GEMM  : X = RMSNorm(h)*attn_norm staged in LDS (bf16 hi+lo pairs); per head:
+//               q/k RMSNorm, rotate-half RoPE, k/v written to the cache, q kept.
+//   attention : MFMA flash-decode over 64-key chunks, one wave per
+//               (chunk, kv head, query group), GQA rows of a kv head together.
+//   combine   : log-sum-exp merge of the chunk partials.
+//   O GEMM    : h += W_o attn                (epilogue keeps row sums of squares)
+//   gate/up   : X = RMSNorm(h)*mlp_norm; epilogue silu(gate)*up
+//   down GEMM : h += W_down act; the last layer also writes h_last = RMSNorm(h[M-1]).
+#include <math.h>
+
+#include <algorithm>
+
+#include "spd_common.h"
+#include "spd_gemm.h"
+#include "spd_host.h"
+
+namespace spd {
+
+constexpr int ATT_KC = 64;   // keys per chunk
+constexpr int ATT_TPG = 4;   // 16-row query tiles per attention block
+
+// h = g, and per-64-column partial sums of squares of every row
+__global__ __launch_bounds__(64) void rows_init_kernel(const float* g, float* h, float* ss, int M,
+                                                       int d) {
+  const int nb = blockIdx.x, r = blockIdx.y, lane = threadIdx.x;
+  const size_t i = (size_t)r * d + nb * 64 + lane;
+  const float v = g[i];
+  h[i] = v;
+  const float s = wave_sum(v * v);
+  if (lane == 0) ss[(size_t)nb * M + r] = s;
+}
+
+// q/k RMSNorm + RoPE, cache writes.  Block columns cover whole heads (64*NT % hd == 0).
+template <typename WT>
+struct EpiQKV {
+  float* qbuf;  // [M][Hq][hd]
+  WT* kc;       // [Hkv][T_cap][hd]
+  WT* vc;       // [Hkv][hd][T_cap]
+  const WT* qn;
+  const WT* kn;
+  int Hq, Hkv, hd, pos0;
+  int64_t T_cap;
+  float eps, theta;
+  template <int NT, typename Y, typename RM>
+  __device__ void run(const Y& y, int nb, int m0, int Mt, const RM&) const {
+    constexpr int TC = 64 * NT;
+    const int hpb = TC / hd;
+    const int nheads = Hq + 2 * Hkv;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int half = hd >> 1;
+    for (int it = wave; it < Mt * hpb; it += GEMM_WAVES) {
+      const int mm = it / hpb, hl = it - mm * hpb;
+      const int hh = nb * hpb + hl;
+      if (hh >= nheads) continue;
+      const int r = m0 + mm, pos = pos0 + r;
+      const bool e0 = lane < hd, e1 = lane + 64 < hd;
+      float v0 = e0 ? y(mm, hl * hd + lane) : 0.f;
+      float v1 = e1 ? y(mm, hl * hd + lane + 64) : 0.f;
+      if (hh < Hq + Hkv) {
+        const WT* nw = hh < Hq ? qn : kn;
+        const float inv = 1.0f / sqrtf(wave_sum(v0 * v0 + v1 * v1) / (float)hd + eps);
+        v0 = e0 ? v0 * inv * to_f<WT>(nw[lane]) : 0.f;
+        v1 = e1 ? v1 * inv * to_f<WT>(nw[lane + 64]) : 0.f;
+        // rotate-half: element i pairs with i + hd/2 at angle pos * theta^(-2i/hd)
+        if (hd == 128) {
+          double s, c;
+          sincos((double)pos * pow((double)theta, -2.0 * lane / hd), &s, &c);
+          const float x1 = v0, x2 = v1;
+          v0 = x1 * (float)c - x2 * (float)s;
+          v1 = x2 * (float)c + x1 * (float)s;
+        } else {
+          const float other = __shfl_xor(v0, half, WAVE);
+          const int i = lane & (half - 1);
+          double s, c;
+          sincos((double)pos * pow((double)theta, -2.0 * i / hd), &s, &c);
+          v0 = lane < half ? v0 * (float)c - other * (float)s : v0 * (float)c + other * (float)s;
+        }
+      }
+      if (hh < Hq) {
+        float* qp = qbuf + ((size_t)r * Hq + hh) * hd;
+        if (e0) qp[lane] = v0;
+        if (e1) qp[lane + 64] = v1;
+      } else if (hh < Hq + Hkv) {
+        WT* kp = kc + ((size_t)(hh - Hq) * T_cap + pos) * hd;
+        if (e0) kp[lane] = from_f<WT>(v0);
+        if (e1) kp[lane + 64] = from_f<WT>(v1);
+      } else {
+        WT* vp = vc + (size_t)(hh - Hq - Hkv) * hd * T_cap + pos;
+        if (e0) vp[(size_t)lane * T_cap] = from_f<WT>(v0);
+        if (e1) vp[(size_t)(lane + 64) * T_cap] = from_f<WT>(v1);
+      }
+    }
+  }
+};
+
+struct AttnArgs {
+  const float* q;  // [M][Hq][hd]
+  const void* kc;  // [Hkv][T_cap][hd]
+  const void* vc;  // [Hkv][hd][T_cap]
+  float* po;       // [Hkv][QR][nch][hd]
+  float2* pml;     // [Hkv][QR][nch]  (chunk max, chunk sum of exp)
+  int M, Hq, Hkv, pos0, nch;
+  int64_t T_cap;
+  float scale;
+};
+
+// One wave: keys [64c, 64c+64) of kv head h, query tiles of group z.
+template <typename WT, int HD>
+__global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
+  typedef Mfma<WT> F;
+  constexpr int KS = ATT_KC / 16;
+  constexpr int DS = HD / F::KSTEP;
+  constexpr int KT = ATT_KC / F::KSTEP;
+  constexpr int DT = HD / 16;
+  constexpr int KPL = F::KPL;
+  constexpr bool SPLIT = sizeof(WT) == 2;  // q and p as bf16 hi + lo pairs
+  __shared__ __align__(16) WT Ps[16][ATT_KC + 16];
+  __shared__ __align__(16) WT Pl[16][ATT_KC + 16];
+
+  const int c = blockIdx.x, h = blockIdx.y, z = blockIdx.z;
+  const int lane = threadIdx.x, lr = lane & 15, lg = lane >> 4;
+  const int G = a.Hq / a.Hkv, QR = a.M * G;
+  const int nkeys = a.pos0 + a.M;
+  const int key0 = c * ATT_KC;
+  const int qt0 = z * ATT_TPG;
+  const int qt1 = min(qt0 + ATT_TPG, (QR + 15) / 16);
+  if (qt0 >= qt1) return;
+  const int r_last = (min(QR, qt1 * 16) - 1) / G;
+  if (key0 > a.pos0 + r_last) return;  // every row of the group is masked here
+
+  const WT* K = static_cast<const WT*>(a.kc) + (size_t)h * a.T_cap * HD;
+  const WT* Vt = static_cast<const WT*>(a.vc) + (size_t)h * HD * a.T_cap;
+
+  typename F::frag kf[KS][DS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int key = min(key0 + 16 * ks + lr, nkeys - 1);
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) kf[ks][ds] = F::load(K + (size_t)key * HD + ds * F::KSTEP + lg * KPL);
+  }
+  typename F::frag vf[KT][DT];
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+    const int kb = key0 + kt * F::KSTEP + lg * KPL;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const WT* src = Vt + (size_t)(dt * 16 + lr) * a.T_cap + kb;
+      if (kb + KPL <= nkeys) {
+        vf[kt][dt] = F::load(src);
+      } else {
+        float tmp[KPL];
+#pragma unroll
+        for (int e = 0; e < KPL; ++e) tmp[e] = (kb + e < nkeys) ? to_f<WT>(src[e]) : 0.f;
+        vf[kt][dt] = F::pack(tmp);
+      }
+    }
+  }
+
+  for (int qt = qt0; qt < qt1; ++qt) {
+    const int qi = 16 * qt + lr;
+    const bool qv = qi < QR;
+    const float* qp = a.q + ((size_t)(qv ? qi / G : 0) * a.Hq + h * G + (qv ? qi % G : 0)) * HD;
+    typename F::frag qf[DS], ql[DS];
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      float tmp[KPL], rem[KPL];
+#pragma unroll
+      for (int e = 0; e < KPL; ++e) {
+        tmp[e] = qv ? qp[ds * F::KSTEP + lg * KPL + e] * a.scale : 0.f;
+        rem[e] = tmp[e] - to_f<WT>(from_f<WT>(tmp[e]));
+      }
+      qf[ds] = F::pack(tmp);
+      ql[ds] = F::pack(rem);
+    }
+    f32x4 sc[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      sc[ks] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) {
+        sc[ks] = F::mma(qf[ds], kf[ks][ds], sc[ks]);
+        if constexpr (SPLIT) sc[ks] = F::mma(ql[ds], kf[ks][ds], sc[ks]);
+      }
+    }
+    // lane holds S[4*lg + i][16*ks + lr]
+    float mx[4], sm[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int qr = 16 * qt + 4 * lg + i;
+      const int lim = qr < QR ? a.pos0 + qr / G : -1;
+      float m_ = -INFINITY;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int key = key0 + 16 * ks + lr;
+        if (key > lim || key >= nkeys) sc[ks][i] = -INFINITY;
+        m_ = fmaxf(m_, sc[ks][i]);
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) m_ = fmaxf(m_, __shfl_xor(m_, o, WAVE));
+      float s_ = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const float p = sc[ks][i] == -INFINITY ? 0.f : expf(sc[ks][i] - m_);
+        sc[ks][i] = p;
+        s_ += p;
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) s_ += __shfl_xor(s_, o, WAVE);
+      mx[i] = m_;
+      sm[i] = s_;
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const WT hi = from_f<WT>(sc[ks][i]);
+        Ps[4 * lg + i][16 * ks + lr] = hi;
+        if constexpr (SPLIT) Pl[4 * lg + i][16 * ks + lr] = from_f<WT>(sc[ks][i] - to_f<WT>(hi));
+      }
+    __syncthreads();
+    f32x4 o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      const typename F::frag pf = F::load(&Ps[lr][kt * F::KSTEP + lg * KPL]);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] = F::mma(pf, vf[kt][dt], o[dt]);
+      if constexpr (SPLIT) {
+        const typename F::frag pl = F::load(&Pl[lr][kt * F::KSTEP + lg * KPL]);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt] = F::mma(pl, vf[kt][dt], o[dt]);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int qr = 16 * qt + 4 * lg + i;
+      if (qr >= QR) continue;
+      const size_t row = (size_t)h * QR + qr;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) a.po[(row * a.nch + c) * HD + 16 * dt + lr] = o[dt][i];
+      if (lr == 0) a.pml[row * a.nch + c] = make_float2(mx[i], sm[i]);
+    }
+  }
+}
+
+// out[r][head*HD + :] = merge of the chunk partials valid for query row r.
+template <typename AT, int HD>
+__global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a, AT* out) {
+  const int qi = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const int G = a.Hq / a.Hkv, QR = a.M * G;
+  const int r = qi / G, head = h * G + qi % G;
+  const int nvalid = (a.pos0 + r) / ATT_KC + 1;
+  const size_t row = (size_t)h * QR + qi;
+  const float2* ml = a.pml + row * a.nch;
+  float mmax = -INFINITY;
+  for (int c = 0; c < nvalid; ++c) mmax = fmaxf(mmax, ml[c].x);
+  float L = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int c = 0; c < nvalid; ++c) {
+    const float w = expf(ml[c].x - mmax);
+    L += ml[c].y * w;
+    const float* po = a.po + (row * a.nch + c) * HD;
+    if (lane < HD) o0 += po[lane] * w;
+    if (lane + 64 < HD) o1 += po[lane + 64] * w;
+  }
+  AT* op = out + (size_t)r * a.Hq * HD + (size_t)head * HD;
+  if (lane < HD) op[lane] = from_f<AT>(o0 / L);
+  if (lane + 64 < HD) op[lane + 64] = from_f<AT>(o1 / L);
+}
+
+struct PdmPlan {
+  GemmPlan qkv, o, gu, down;
+  int nch, QR;
+  size_t off_h, off_ss, off_q, off_po, off_pml, off_attn, off_act, off_part, total;
+};
+
+static PdmPlan plan_pdm(const spd_config* c, int M, int64_t T_cap) {
+  PdmPlan p;
+  const bool bf = c->dtype == SPD_BF16;
+  const int ks = bf ? Mfma<bf16>::KSTEP : Mfma<float>::KSTEP;
+  const int es = bf ? 2 : 4;
+  p.qkv = plan_gemm((c->Hq + 2 * c->Hkv) * c->hd, c->d, M, ks, es, 2);
+  p.o = plan_gemm(c->d, c->Hq * c->hd, M, ks, es, 1);
+  p.gu = plan_gemm(2 * c->dff, c->d, M, ks, es, 1);
+  p.down = plan_gemm(c->d, c->dff, M, ks, es, 1);
+  p.nch = (int)((T_cap + ATT_KC - 1) / ATT_KC);
+  p.QR = M * (c->Hq / c->Hkv);
+  size_t off = SPD_WS_COUNTER_BYTES;
+  auto take = [&](size_t bytes) { size_t r = off; off = align256(off + bytes); return r; };
+  p.off_h = take((size_t)M * c->d * 4);
+  p.off_ss = take((size_t)(c->d / 64) * M * 4);
+  p.off_q = take((size_t)M * c->Hq * c->hd * 4);
+  p.off_po = take((size_t)c->Hkv * p.QR * p.nch * c->hd * 4);
+  p.off_pml = take((size_t)c->Hkv * p.QR * p.nch * 8);
+  p.off_attn = take((size_t)M * c->Hq * c->hd * 4);
+  p.off_act = take((size_t)M * c->dff * 4);
+  size_t part = 0;
+  const GemmPlan* gps[4] = {&p.qkv, &p.o, &p.gu, &p.down};
+  const size_t Ns[4] = {(size_t)(c->Hq + 2 * c->Hkv) * c->hd, (size_t)c->d, (size_t)2 * c->dff,
+                        (size_t)c->d};
+  for (int i = 0; i < 4; ++i)
+    if (gps[i]->S > 1) part = std::max(part, (size_t)gps[i]->S * M * Ns[i] * 4);
+  p.off_part = take(part);
+  p.total = off;
+  return p;
+}
+
+size_t pdm_workspace(const spd_config* cfg, int M, int64_t T_cap) {
+  return plan_pdm(cfg, M, T_cap).total;
+}
+
+static GemmShape shape_of(const GemmPlan& gp, const void* W, int N, int K, int M, float* part,
+                          unsigned* ctr) {
+  GemmShape g;
+  g.W = W;
+  g.N = N;
+  g.K = K;
+  g.M = M;
+  g.S = gp.S;
+  g.nsteps = gp.nsteps;
+  g.ldx = gp.ldx;
+  g.part = part;
+  g.counters = ctr;
+  g.nblocks = gp.nblocks;
+  return g;
+}
+
+template <typename WT, int HD>
+static int launch_attention(const AttnArgs& aa, int ngroups, float* attn_out, hipStream_t st) {
+  if constexpr (HD % Mfma<WT>::KSTEP != 0) {
+    return SPD_E_UNSUPPORTED;  // head dim below one MFMA k-step of this dtype
+  } else {
+  hipLaunchKernelGGL((attn_partial_kernel<WT, HD>), dim3(aa.nch, aa.Hkv, ngroups), dim3(64), 0, st,
+                     aa);
+  int rc = check_launch();
+  if (rc) return rc;
+  hipLaunchKernelGGL((attn_combine_kernel<float, HD>), dim3(aa.M * (aa.Hq / aa.Hkv), aa.Hkv), dim3(64),
+                     0, st, aa, attn_out);
+  return check_launch();
+  }
+}
+
+template <typename WT>
+static int pdm_impl(const spd_config* c, const spd_layer_weights* layers, const void* final_norm,
+                    void* k_cache, void* v_cache, int64_t T_cap, const float* g, int pos0, int M,
+                    float* h_last, void* ws, hipStream_t st) {
+  const PdmPlan p = plan_pdm(c, M, T_cap);
+  char* w = static_cast<char*>(ws);
+  unsigned* ctr = reinterpret_cast<unsigned*>(w);
+  float* h = reinterpret_cast<float*>(w + p.off_h);
+  float* ss = reinterpret_cast<float*>(w + p.off_ss);
+  float* qb = reinterpret_cast<float*>(w + p.off_q);
+  float* attn = reinterpret_cast<float*>(w + p.off_attn);
+  float* act = reinterpret_cast<float*>(w + p.off_act);
+  float* part = reinterpret_cast<float*>(w + p.off_part);
+  const int d = c->d, hd = c->hd, Hq = c->Hq, Hkv = c->Hkv, dff = c->dff;
+  const int nq = (Hq + 2 * Hkv) * hd;
+
+  hipLaunchKernelGGL(rows_init_kernel, dim3(d / 64, M), dim3(64), 0, st, g, h, ss, M, d);
+  int rc = check_launch();
+  if (rc) return rc;
+  int P = d / 64;  // partial count of ss
+
+  AttnArgs aa;
+  aa.q = qb;
+  aa.po = reinterpret_cast<float*>(w + p.off_po);
+  aa.pml = reinterpret_cast<float2*>(w + p.off_pml);
+  aa.M = M;
+  aa.Hq = Hq;
+  aa.Hkv = Hkv;
+  aa.pos0 = pos0;
+  aa.nch = (pos0 + M + ATT_KC - 1) / ATT_KC;
+  aa.T_cap = T_cap;
+  aa.scale = 1.0f / sqrtf((float)hd);
+  const int ngroups = ((p.QR + 15) / 16 + ATT_TPG - 1) / ATT_TPG;
+
+  for (int l = 0; l < c->Ls; ++l) {
+    const spd_layer_weights& lw = layers[l];
+    WT* kc = static_cast<WT*>(k_cache) + (size_t)l * Hkv * T_cap * hd;
+    WT* vc = static_cast<WT*>(v_cache) + (size_t)l * Hkv * hd * T_cap;
+    // QKV
+    {
+      InNorm<WT> in{h, static_cast<const WT*>(lw.attn_norm), ss, P, M, d, c->rms_eps};
+      EpiQKV<WT> epi{qb, kc, vc, static_cast<const WT*>(lw.q_norm), static_cast<const WT*>(lw.k_norm),
+                     Hq, Hkv, hd, pos0, T_cap, c->rms_eps, c->rope_theta};
+      rc = launch_gemm<WT, 2>(p.qkv, shape_of(p.qkv, lw.wqkv, nq, d, M, part, ctr), in, epi,
+                              RowMapStd{}, st);
+      if (rc) return rc;
+    }
+    // attention
+    aa.kc = kc;
+    aa.vc = vc;
+    switch (hd) {
+      case 16: rc = launch_attention<WT, 16>(aa, ngroups, attn, st); break;
+      case 32: rc = launch_attention<WT, 32>(aa, ngroups, attn, st); break;
+      case 64: rc = launch_attention<WT, 64>(aa, ngroups, attn, st); break;
+      default: rc = launch_attention<WT, 128>(aa, ngroups, attn, st); break;
+    }
+    if (rc) return rc;
+    // O projection + residual
+    {
+      InAct<WT, float> in{attn, Hq * hd};
+      EpiResid<WT> epi{h, ss, d, M, 0, nullptr, nullptr, ctr + CTR_FINAL, p.o.nblocks, c->rms_eps};
+      rc = launch_gemm<WT, 1>(p.o, shape_of(p.o, lw.wo, d, Hq * hd, M, part, ctr), in, epi,
+                              RowMapStd{}, st);
+      if (rc) return rc;
+      P = p.o.nblocks;
+    }
+    // gate/up + silu*mul
+    {
+      InNorm<WT> in{h, static_cast<const WT*>(lw.mlp_norm), ss, P, M, d, c->rms_eps};
+      EpiSilu<float> epi{act, dff};
+      rc = launch_gemm<WT, 1>(p.gu, shape_of(p.gu, lw.w_gate_up, 2 * dff, d, M, part, ctr), in, epi,
+                              RowMapGateUp{dff}, st);
+      if (rc) return rc;
+    }
+    // down + residual (+ final norm of the last row after the last layer)
+    {
+      InAct<WT, float> in{act, dff};
+      const bool last = l == c->Ls - 1;
+      EpiResid<WT> epi{h, ss, d, M, last ? 1 : 0, static_cast<const WT*>(final_norm), h_last,
+                       ctr + CTR_FINAL, p.down.nblocks, c->rms_eps};
+      rc = launch_gemm<WT, 1>(p.down, shape_of(p.down, lw.w_down, d, dff, M, part, ctr), in, epi,
+                              RowMapStd{}, st);
+      if (rc) return rc;
+      P = p.down.nblocks;
+    }
+  }
+  if (c->Ls == 0) return SPD_E_UNSUPPORTED;
+  return SPD_OK;
+}
+
+}  // namespace spd
+
+using namespace spd;
+
+extern "C" int spd_pdm_step(const spd_config* cfg, const spd_layer_weights* layers,
+                            const void* final_norm, void* k_cache, void* v_cache, int64_t T_cap,
+                            const float* g, int32_t pos0, int32_t M, float* h_last, void* ws,
+                            size_t ws_bytes, void* stream) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!layers || !final_norm || !k_cache || !v_cache || !g || !h_last || !ws) return SPD_E_INVALID;
+  if (cfg->Ls < 1 || cfg->Hq < 1 || cfg->Hkv < 1 || cfg->hd < 1 || cfg->dff < 1) return SPD_E_INVALID;
+  if (M < 1 || pos0 < 0 || (int64_t)pos0 + M > T_cap) return SPD_E_INVALID;
+  if (cfg->Hq % cfg->Hkv) return SPD_E_UNSUPPORTED;
+  const int hd = cfg->hd;
+  if (hd != 16 && hd != 32 && hd != 64 && hd != 128) return SPD_E_UNSUPPORTED;
+  if (cfg->d % 64 || cfg->dff % 64 || T_cap % 8) return SPD_E_UNSUPPORTED;
+  if (((int64_t)cfg->Hq * hd) % 32) return SPD_E_UNSUPPORTED;
+  for (int l = 0; l < cfg->Ls; ++l) {
+    const spd_layer_weights& w = layers[l];
+    if (!w.attn_norm || !w.wqkv || !w.q_norm || !w.k_norm || !w.wo || !w.mlp_norm || !w.w_gate_up ||
+        !w.w_down)
+      return SPD_E_INVALID;
+    if (!aligned16(w.wqkv) || !aligned16(w.wo) || !aligned16(w.w_gate_up) || !aligned16(w.w_down))
+      return SPD_E_INVALID;
+  }
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(ws)) return SPD_E_INVALID;
+  if (ws_bytes < pdm_workspace(cfg, M, T_cap)) return SPD_E_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (cfg->dtype == SPD_BF16)
+    return pdm_impl<bf16>(cfg, layers, final_norm, k_cache, v_cache, T_cap, g, pos0, M, h_last, ws,
+                          st);
+  return pdm_impl<float>(cfg, layers, final_norm, k_cache, v_cache, T_cap, g, pos0, M, h_last, ws, st);
+}

@@ -1,0 +1,288 @@
+// spd_verify: speculative-sampling verification of drafted tokens.
+// ("Speculative Pipeline Decoding", arXiv 2605.30852, section 3.4: streaming
+// verification, greedy argmax match at T = 0, standard rejection sampling at T > 0;
+// the speculative-decoding explainer's four-phase loop and acceptance criterion:
+// accept if r <= min(1, p/q), else resample from norm(max(0, p - q)); bonus token
+// from p_{gamma+1} when every draft is accepted.)
+//
+// Grid: (vocabulary chunks, sequences).  Every block first decides the sequence's
+// outcome from the 2*gamma scalars p_j(x_j), q_j(x_j) (cheap, exact), so a fully
+// accepted sequence without bonus costs no row traffic.  Otherwise each block sums
+// the exact integer weights of its chunk of the row to sample from (residual and
+// target weights both, for the empty-residual fallback); the last block of the
+// sequence scans the chunk sums and locates the sample.  Greedy verify reduces
+// (max, first argmax) per chunk for every row instead.
+#include <algorithm>
+
+#include "spd_common.h"
+#include "spd_host.h"
+
+namespace spd {
+
+constexpr int VER_CHUNK = 2048;
+constexpr int VER_THREADS = 256;
+constexpr int VER_MAX_ROWS = 64;  // gamma + bonus limit of the greedy form
+
+struct VerArgs {
+  const float* p;
+  const float* q;
+  const int32_t* draft;
+  const uint64_t* words;
+  int32_t* n_accept;
+  int32_t* next_token;
+  unsigned* counters;
+  void* part;
+  int B, gamma, V, bonus, nchunks;
+};
+
+__device__ uint64_t vblock_scan(uint64_t v, uint64_t* sh) {
+  sh[threadIdx.x] = v;
+  __syncthreads();
+  for (int o = 1; o < VER_THREADS; o <<= 1) {
+    const uint64_t add = (int)threadIdx.x >= o ? sh[threadIdx.x - o] : 0ull;
+    __syncthreads();
+    sh[threadIdx.x] += add;
+    __syncthreads();
+  }
+  return sh[threadIdx.x];
+}
+
+__device__ __forceinline__ uint64_t res_weight(float p, float q) {
+  const uint64_t P = prob_weight(p), Q = prob_weight(q);
+  return P > Q ? P - Q : 0ull;
+}
+
+// T > 0
+__global__ __launch_bounds__(VER_THREADS) void verify_sample_kernel(VerArgs a) {
+  __shared__ uint64_t sh[VER_THREADS];
+  __shared__ int s_j;
+  const int c = blockIdx.x, b = blockIdx.y;
+  const int rowsP = a.gamma + a.bonus;
+  if (threadIdx.x == 0) {
+    int j = 0;
+    for (; j < a.gamma; ++j) {
+      const int x = a.draft[b * a.gamma + j];
+      bool acc = false;
+      if (x >= 0 && x < a.V) {
+        const double px = (double)a.p[((size_t)b * rowsP + j) * a.V + x];
+        const double qx = (double)a.q[((size_t)b * a.gamma + j) * a.V + x];
+        const uint64_t R = a.words[((size_t)b * (a.gamma + 1) + j) * 2] >> 40;
+        acc = (double)(R + 1) * qx <= px * 16777216.0;
+      }
+      if (!acc) break;
+    }
+    s_j = j;
+  }
+  __syncthreads();
+  const int j = s_j;
+  const bool rejected = j < a.gamma;
+  if (!rejected && !a.bonus) {
+    if (c == 0 && threadIdx.x == 0) {
+      a.n_accept[b] = a.gamma;
+      a.next_token[b] = -1;
+    }
+    return;
+  }
+  const float* prow = a.p + ((size_t)b * rowsP + j) * a.V;
+  const float* qrow = rejected ? a.q + ((size_t)b * a.gamma + j) * a.V : nullptr;
+  uint64_t sres = 0, sp = 0;
+  const int base = c * VER_CHUNK;
+  const int end = min(base + VER_CHUNK, a.V);
+  for (int i = base + threadIdx.x; i < end; i += VER_THREADS) {
+    const float pv = prow[i];
+    sp += prob_weight(pv);
+    if (rejected) sres += res_weight(pv, qrow[i]);
+  }
+  sres = wave_sum_u64(sres);
+  sp = wave_sum_u64(sp);
+  __shared__ uint64_t s_w[2][VER_THREADS / 64];
+  if ((threadIdx.x & 63) == 0) {
+    s_w[0][threadIdx.x >> 6] = sres;
+    s_w[1][threadIdx.x >> 6] = sp;
+  }
+  __syncthreads();
+  uint64_t* part = static_cast<uint64_t*>(a.part) + ((size_t)b * a.nchunks + c) * 2;
+  if (threadIdx.x == 0) {
+    uint64_t t0 = 0, t1 = 0;
+    for (int w = 0; w < VER_THREADS / 64; ++w) {
+      t0 += s_w[0][w];
+      t1 += s_w[1][w];
+    }
+    part[0] = t0;
+    part[1] = t1;
+  }
+  unsigned* ctr = a.counters + b;
+  if (!arrive_last(ctr, (unsigned)a.nchunks)) return;
+
+  const uint64_t* pb = static_cast<const uint64_t*>(a.part) + (size_t)b * a.nchunks * 2;
+  // which weights: residual if it has mass, else the target row itself
+  uint64_t tr = 0;
+  for (int k = threadIdx.x; k < a.nchunks; k += VER_THREADS) tr += pb[2 * k];
+  tr = wave_sum_u64(tr);
+  __shared__ uint64_t s_t[VER_THREADS / 64];
+  if ((threadIdx.x & 63) == 0) s_t[threadIdx.x >> 6] = tr;
+  __syncthreads();
+  uint64_t total_res = 0;
+  for (int w = 0; w < VER_THREADS / 64; ++w) total_res += s_t[w];
+  const int which = (rejected && total_res > 0) ? 0 : 1;
+  const uint64_t U = a.words[((size_t)b * (a.gamma + 1) + j) * 2 + 1] >> 32;
+
+  const int per = (a.nchunks + VER_THREADS - 1) / VER_THREADS;
+  uint64_t mine = 0;
+  for (int e = 0; e < per; ++e) {
+    const int k = threadIdx.x * per + e;
+    if (k < a.nchunks) mine += pb[2 * k + which];
+  }
+  const uint64_t incl = vblock_scan(mine, sh);
+  __shared__ uint64_t s_tau, s_off;
+  __shared__ int s_chunk;
+  if (threadIdx.x == VER_THREADS - 1) {
+    s_tau = scale_u32((uint32_t)U, incl);
+    s_chunk = -1;
+  }
+  __syncthreads();
+  const uint64_t tau = s_tau;
+  uint64_t run = incl - mine;
+  if (run <= tau && incl > tau) {
+    for (int e = 0; e < per; ++e) {
+      const int k = threadIdx.x * per + e;
+      if (k >= a.nchunks) break;
+      const uint64_t w = pb[2 * k + which];
+      if (run + w > tau) {
+        s_chunk = k;
+        s_off = run;
+        break;
+      }
+      run += w;
+    }
+  }
+  __syncthreads();
+  int tok = -1;
+  if (s_chunk >= 0) {
+    constexpr int PER = VER_CHUNK / VER_THREADS;
+    const int b0 = s_chunk * VER_CHUNK;
+    uint64_t w[PER];
+    uint64_t tot = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int i = b0 + threadIdx.x * PER + e;
+      uint64_t v = 0;
+      if (i < a.V) v = which == 0 ? res_weight(prow[i], qrow[i]) : prob_weight(prow[i]);
+      w[e] = v;
+      tot += v;
+    }
+    __shared__ int s_found;
+    if (threadIdx.x == 0) s_found = -1;
+    const uint64_t in2 = vblock_scan(tot, sh);
+    uint64_t r2 = s_off + in2 - tot;
+    if (r2 <= tau && s_off + in2 > tau) {
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        r2 += w[e];
+        if (r2 > tau) {
+          s_found = b0 + threadIdx.x * PER + e;
+          break;
+        }
+      }
+    }
+    __syncthreads();
+    tok = s_found;
+  }
+  if (threadIdx.x == 0) {
+    a.n_accept[b] = j;
+    a.next_token[b] = tok < 0 ? 0 : tok;
+  }
+  arrival_reset(ctr);
+}
+
+// T == 0: p holds logits; per chunk (max, first argmax) of every row.
+__global__ __launch_bounds__(VER_THREADS) void verify_greedy_kernel(VerArgs a) {
+  const int c = blockIdx.x, b = blockIdx.y;
+  const int rows = a.gamma + a.bonus;
+  const int base = c * VER_CHUNK;
+  const int end = min(base + VER_CHUNK, a.V);
+  ArgMax* part = static_cast<ArgMax*>(a.part);
+  __shared__ ArgMax s_am[VER_THREADS / 64];
+  for (int j = 0; j < rows; ++j) {
+    const float* prow = a.p + ((size_t)b * rows + j) * a.V;
+    ArgMax am{-INFINITY, ARG_NONE};
+    for (int i = base + threadIdx.x; i < end; i += VER_THREADS) am = argmax_merge(am, ArgMax{prow[i], i});
+    am = wave_argmax(am);
+    if ((threadIdx.x & 63) == 0) s_am[threadIdx.x >> 6] = am;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      ArgMax t = s_am[0];
+      for (int w = 1; w < VER_THREADS / 64; ++w) t = argmax_merge(t, s_am[w]);
+      part[((size_t)b * rows + j) * a.nchunks + c] = t;
+    }
+    __syncthreads();
+  }
+  unsigned* ctr = a.counters + b;
+  if (!arrive_last(ctr, (unsigned)a.nchunks)) return;
+  __shared__ int s_best[VER_MAX_ROWS];
+  for (int j = 0; j < rows; ++j) {
+    const ArgMax* pj = part + ((size_t)b * rows + j) * a.nchunks;
+    ArgMax am{-INFINITY, ARG_NONE};
+    for (int k = threadIdx.x; k < a.nchunks; k += VER_THREADS) am = argmax_merge(am, pj[k]);
+    am = wave_argmax(am);
+    if ((threadIdx.x & 63) == 0) s_am[threadIdx.x >> 6] = am;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      ArgMax t = s_am[0];
+      for (int w = 1; w < VER_THREADS / 64; ++w) t = argmax_merge(t, s_am[w]);
+      s_best[j] = t.i == ARG_NONE ? 0 : t.i;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    int j = 0;
+    while (j < a.gamma && a.draft[b * a.gamma + j] == s_best[j]) ++j;
+    a.n_accept[b] = j;
+    a.next_token[b] = j < a.gamma ? s_best[j] : (a.bonus ? s_best[a.gamma] : -1);
+  }
+  arrival_reset(ctr);
+}
+
+size_t verify_workspace(int B, int gamma, int V) {
+  const size_t nch = (size_t)(V + VER_CHUNK - 1) / VER_CHUNK;
+  const size_t per = std::max((size_t)16, (size_t)(gamma + 1) * sizeof(ArgMax));
+  return align256(SPD_WS_COUNTER_BYTES + (size_t)B * nch * per);
+}
+
+}  // namespace spd
+
+using namespace spd;
+
+extern "C" int spd_verify(int32_t B, int32_t gamma, int32_t V, float temperature, int32_t bonus,
+                          const float* p, const float* q, const int32_t* draft,
+                          const uint64_t* words, int32_t* n_accept, int32_t* next_token, void* ws,
+                          size_t ws_bytes, void* stream) {
+  if (B < 1 || gamma < 0 || V < 1 || (bonus != 0 && bonus != 1)) return SPD_E_INVALID;
+  if (gamma + bonus < 1 || gamma + bonus > VER_MAX_ROWS) return SPD_E_INVALID;
+  if (B >= SPD_WS_COUNTER_BYTES / 4 - 1 || B > 65535) return SPD_E_UNSUPPORTED;
+  if (!(temperature >= 0.f)) return SPD_E_INVALID;
+  if (!p || !n_accept || !next_token || !ws || (gamma > 0 && !draft)) return SPD_E_INVALID;
+  if (temperature > 0.f && (!words || (gamma > 0 && !q))) return SPD_E_INVALID;
+  if (!aligned16(ws)) return SPD_E_INVALID;
+  if (ws_bytes < verify_workspace(B, gamma, V)) return SPD_E_WORKSPACE;
+  VerArgs a;
+  a.p = p;
+  a.q = q;
+  a.draft = draft;
+  a.words = words;
+  a.n_accept = n_accept;
+  a.next_token = next_token;
+  a.counters = static_cast<unsigned*>(ws);
+  a.part = static_cast<char*>(ws) + SPD_WS_COUNTER_BYTES;
+  a.B = B;
+  a.gamma = gamma;
+  a.V = V;
+  a.bonus = bonus;
+  a.nchunks = (V + VER_CHUNK - 1) / VER_CHUNK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (temperature > 0.f)
+    hipLaunchKernelGGL(verify_sample_kernel, dim3(a.nchunks, B), dim3(VER_THREADS), 0, st, a);
+  else
+    hipLaunchKernelGGL(verify_greedy_kernel, dim3(a.nchunks, B), dim3(VER_THREADS), 0, st, a);
+  return check_launch();
+}

@@ -1,0 +1,154 @@
+"""Host driver of one SPD draft-and-verify cycle on the device.
+
+Issues the C-ABI calls in the order a cycle needs them ("Speculative Pipeline
+Decoding", arXiv 2605.30852, sections 3.1-3.4): features of the rows the cycle
+recomputes, the PDM step, the draft head, and -- when the pipeline is saturated
+-- the target head on the exiting token's last-layer state, the streaming verify
+of its successor, and the commit/rollback.  All arithmetic runs in libspd.so;
+this module only allocates buffers and passes pointers.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import (SPD_BF16, SPD_CALL_FUSE, SPD_CALL_LM_HEAD, SPD_CALL_PDM, SPD_CALL_VERIFY,
+               layer_weights, make_config, spd_fuse_features, spd_lm_head, spd_pdm_step,
+               spd_rollback, spd_slot_table, spd_verify, spd_workspace_size)
+
+PREFILL_BLOCK = 256
+
+
+@dataclass
+class DeviceWeights:
+    """Device tensors of the synthetic target states and the PDM/heads."""
+    store: torch.Tensor       # [T_cap][S][d] anchor states (cfg dtype)
+    h_final: torch.Tensor     # [T_cap][d] float32 target last-layer states
+    fc_norm: torch.Tensor
+    w_fc: torch.Tensor
+    layers: list              # dicts with the spd_layer_weights keys
+    final_norm: torch.Tensor
+    w_dlm: torch.Tensor
+    w_tlm: torch.Tensor
+
+
+class SpdModel:
+    def __init__(self, *, L, n, anchors, d, Ls, Hq, Hkv, hd, dff, V, dtype, weights: DeviceWeights,
+                 anchor_mode=0, norm_k0=0, eps=1e-6, rope_theta=1e6):
+        self.cfg = make_config(L=L, n=n, m=len(anchors), d=d, Ls=Ls, Hq=Hq, Hkv=Hkv, hd=hd,
+                               dff=dff, V=V, dtype=dtype, anchor_mode=anchor_mode,
+                               norm_k0=norm_k0, rms_eps=eps, rope_theta=rope_theta)
+        self.anchors = list(anchors)
+        self.slot_tab, self.store_layers = spd_slot_table(self.cfg, self.anchors)
+        self.w = weights
+        self.layer_arr = layer_weights(weights.layers)
+        self.T_cap = weights.store.shape[0]
+        if weights.store.shape[1] != len(self.store_layers):
+            raise ValueError("anchor store does not hold the layers the slot table reads")
+
+
+class SpdCycle:
+    """Buffers of one sequence and the calls of one cycle."""
+
+    def __init__(self, model: SpdModel, temperature: float, device="cuda"):
+        self.m = model
+        c = model.cfg
+        self.T = float(temperature)
+        self.device = device
+        wdt = torch.bfloat16 if c.dtype == SPD_BF16 else torch.float32
+        T_cap = model.T_cap
+        self.g = torch.empty(max(c.n + 1, PREFILL_BLOCK), c.d, device=device)
+        self.h_last = torch.empty(c.d, device=device)
+        self.k_cache = torch.zeros(c.Ls, c.Hkv, T_cap, c.hd, dtype=wdt, device=device)
+        self.v_cache = torch.zeros(c.Ls, c.Hkv, c.hd, T_cap, dtype=wdt, device=device)
+        self.dlogits = torch.empty(c.V, device=device)
+        self.ring = torch.empty(c.n, c.V, device=device)
+        self.dtoken = torch.zeros(1, dtype=torch.int32, device=device)
+        self.tlogits = torch.empty(c.V, device=device)
+        self.p = torch.empty(c.V, device=device)
+        self.ttoken = torch.zeros(1, dtype=torch.int32, device=device)
+        self.n_accept = torch.zeros(1, dtype=torch.int32, device=device)
+        self.next_token = torch.zeros(1, dtype=torch.int32, device=device)
+        self.state = torch.zeros(4, dtype=torch.int32, device=device)
+        self.tokens = torch.zeros(T_cap, dtype=torch.int32, device=device)
+        ws = max(spd_workspace_size(SPD_CALL_FUSE, c, PREFILL_BLOCK),
+                 spd_workspace_size(SPD_CALL_PDM, c, PREFILL_BLOCK, 0, T_cap),
+                 spd_workspace_size(SPD_CALL_FUSE, c, c.n + 1),
+                 spd_workspace_size(SPD_CALL_PDM, c, c.n + 1, 0, T_cap),
+                 spd_workspace_size(SPD_CALL_LM_HEAD, c, 1),
+                 spd_workspace_size(SPD_CALL_VERIFY, c, 1, 1))
+        self.ws = torch.zeros(ws, dtype=torch.uint8, device=device)
+
+    # ---------------------------------------------------------------- pieces
+    def features(self, pos0, M, a, out=None):
+        m = self.m
+        g = self.g if out is None else out
+        spd_fuse_features(m.cfg, m.w.store, m.T_cap, len(m.store_layers), m.slot_tab, pos0, M, a,
+                          m.w.fc_norm, m.w.w_fc, g, self.ws)
+        return g
+
+    def pdm(self, pos0, M, g=None):
+        m = self.m
+        spd_pdm_step(m.cfg, m.layer_arr, m.w.final_norm, self.k_cache, self.v_cache, m.T_cap,
+                     self.g if g is None else g, pos0, M, self.h_last, self.ws)
+        return self.h_last
+
+    def prefill(self, P: int):
+        """Key/value cache of positions 0..P-1, all fully processed (depth n)."""
+        for s in range(0, P, PREFILL_BLOCK):
+            M = min(PREFILL_BLOCK, P - s)
+            self.features(s, M, 0)
+            self.pdm(s, M)
+
+    def draft(self, t, words_block):
+        """Draft head on h_last; at T > 0 the q row goes to ring[t % n]."""
+        m = self.m
+        probs = self.ring[t % m.cfg.n] if self.T > 0 else None
+        w = None if words_block is None else words_block.data_ptr() + 2 * 8
+        spd_lm_head(m.cfg, m.w.w_dlm, self.h_last, 1, self.T, w, self.dlogits, probs, self.dtoken,
+                    self.ws)
+
+    def target_and_verify(self, t, words_block, q_row=None, x_ptr=None):
+        """Target head on the exiting token's state and streaming verify of its successor."""
+        m = self.m
+        n, V = m.cfg.n, m.cfg.V
+        exiting = t - n
+        h = m.w.h_final[exiting]
+        probs = self.p if self.T > 0 else None
+        w = None if words_block is None else words_block.data_ptr() + 2 * 8
+        spd_lm_head(m.cfg, m.w.w_tlm, h, 1, self.T, w, self.tlogits, probs, self.ttoken, self.ws)
+        cand = exiting + 1
+        q = q_row if q_row is not None else self.ring[cand % n]
+        draft = x_ptr if x_ptr is not None else self.tokens.data_ptr() + 4 * cand
+        spd_verify(1, 1, V, self.T, 0, self.p if self.T > 0 else self.tlogits,
+                   q if self.T > 0 else None, draft,
+                   None if words_block is None else words_block, self.n_accept, self.next_token,
+                   self.ws)
+
+    def rollback(self):
+        m = self.m
+        spd_rollback(self.state, m.cfg.n, self.dtoken, self.n_accept, self.next_token,
+                     self.tokens, m.T_cap)
+
+    # ---------------------------------------------------------------- a cycle
+    def cycle(self, t, a, words_block, q_row=None, x_ptr=None):
+        """One cycle at sequence length t with a tokens in flight."""
+        n = self.m.cfg.n
+        pos0, M = t - 1 - a, a + 1
+        self.features(pos0, M, a)
+        self.pdm(pos0, M)
+        self.draft(t, words_block)
+        if a == n:
+            self.target_and_verify(t, words_block, q_row, x_ptr)
+        self.rollback()
+
+    def set_state(self, t, a, tokens=None):
+        self.state.copy_(torch.tensor([t, a, 0, 0], dtype=torch.int32))
+        if tokens is not None:
+            tok = torch.as_tensor(tokens, dtype=torch.int32)
+            self.tokens[:tok.numel()].copy_(tok)
+
+    def read_state(self):
+        t, a, commits, cycles = self.state.tolist()
+        return t, a, commits, cycles

@@ -139,7 +139,7 @@ class CycleInputs:
     shape: SpdShape
     store_layers: list
     store: torch.Tensor          # [T_cap][S][d] anchor hidden states H_i^l
-    h_final: torch.Tensor        # [T_cap][d]   target last-layer states (already final-normed)
+    h_final: torch.Tensor        # [T_cap][d]   float32 target last-layer states (already final-normed)
     fc_norm: torch.Tensor        # [m*d]
     w_fc: torch.Tensor           # [d][m*d]
     layers: list = field(default_factory=list)  # dicts of per-layer tensors
@@ -182,7 +182,7 @@ def cycle_inputs(s: SpdShape, *, device, seed=0, T_cap=None, with_heads=True) ->
     T_cap = int(T_cap or (s.ctx + 64))
     sl = store_layers(s)
     store = normal((T_cap, len(sl), s.d), 1.0, device=device, seed=seed + 1, name="anchors", dtype=dt)
-    h_final = normal((T_cap, s.d), 1.0, device=device, seed=seed + 1, name="h_final", dtype=dt)
+    h_final = normal((T_cap, s.d), 1.0, device=device, seed=seed + 1, name="h_final")
     ci = CycleInputs(
         shape=s, store_layers=sl, store=store, h_final=h_final,
         fc_norm=uniform((s.m * s.d,), 0.5, 1.5, device=device, seed=seed, name="fc_norm", dtype=dt),
@@ -235,3 +235,24 @@ def verify_stress_inputs(v: VerifyShape, *, device, seed=3):
     draft = torch.multinomial(q.reshape(B * G, V), 1, generator=g).reshape(B, G).to(torch.int32)
     words = rand_words(seed, 1, B * (G + 1) * 2).reshape(B, G + 1, 2)
     return p, q, draft.contiguous(), words
+
+
+def kv_cache(s: SpdShape, T_cap: int, *, device, seed=4):
+    """Committed key/value cache contents for a cycle run without prefill:
+    keys [Ls][Hkv][T_cap][hd] (position-major) and values [Ls][Hkv][hd][T_cap]
+    (position-minor), N(0,1) in the storage dtype."""
+    dt = storage_dtype(s.dtype)
+    k = normal((s.Ls, s.Hkv, T_cap, s.hd), 1.0, device=device, seed=seed, name="k_cache", dtype=dt)
+    v = normal((s.Ls, s.Hkv, s.hd, T_cap), 1.0, device=device, seed=seed, name="v_cache", dtype=dt)
+    return k, v
+
+
+def cycle_words(n_cycles: int, seed: int = 2, stream: int = 0) -> np.ndarray:
+    """One 4-word block per cycle: word 0 -> accept uniform, word 1 -> resample
+    uniform, word 2 -> draft-sampling uniform, word 3 -> harness draws."""
+    return rand_words(seed, stream, 4 * n_cycles).reshape(n_cycles, 4)
+
+
+def words_tensor(words: np.ndarray, device) -> torch.Tensor:
+    """uint64 words as an int64 tensor with the same bit patterns."""
+    return torch.from_numpy(np.ascontiguousarray(words).view(np.int64)).to(device)

@@ -1,0 +1,117 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and its host helpers agree with the oracle."""
+import ctypes
+
+import pytest
+
+import synth
+from oracle import spd as O
+from spd_testlib import ensure_built, header_functions
+
+spd = ensure_built()
+
+
+def test_header_symbols_are_exported():
+    names = header_functions()
+    assert len(names) >= 11
+    lib = spd.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(spd.EXPORTED)
+    for n in names:                      # the binding uses the C names
+        if n not in ("spd_status_string", "spd_last_hip_error"):
+            assert hasattr(spd, n), n
+    assert spd.spd_version() == 1
+
+
+def _cfg(s, **kw):
+    base = dict(L=s.L, n=s.n, m=s.m, d=s.d, Ls=s.Ls, Hq=s.Hq, Hkv=s.Hkv, hd=s.hd, dff=s.dff,
+                V=s.V, dtype=s.dtype, anchor_mode=s.anchor_mode, norm_k0=s.norm_k0)
+    base.update(kw)
+    return spd.make_config(**base)
+
+
+@pytest.mark.parametrize("name", sorted(synth.SHAPES))
+@pytest.mark.parametrize("mode", [O.ZERO_MASK, O.CLAMP_MIN])
+def test_slot_table_matches_oracle(name, mode):
+    s = synth.SHAPES[name].with_(anchor_mode=mode)
+    tab, layers = spd.spd_slot_table(_cfg(s), s.anchors)
+    assert layers == O.store_layers_for(s.L, s.n, s.anchors, mode)
+    assert layers == synth.store_layers(s)
+    for k in range(s.n + 1):
+        want = O.slot_layers(k, s.L, s.n, s.anchors, mode)
+        got = [layers[x] if x >= 0 else -1 for x in tab[k * s.m:(k + 1) * s.m]]
+        assert got == want, (k, got, want)
+
+
+def test_slot_table_rejects_bad_anchors():
+    s = synth.TINY
+    with pytest.raises(spd.SpdError):
+        spd.spd_slot_table(_cfg(s), [1, 4, 7])
+    with pytest.raises(spd.SpdError):
+        spd.spd_slot_table(_cfg(s), [0, 7, 4])
+
+
+@pytest.mark.parametrize("t,a,n", [(32, 4, 4), (32, 1, 4), (2048, 8, 8), (2048, 5, 8), (4096, 16, 16)])
+def test_layout_matches_oracle(t, a, n):
+    pos, dep = spd.spd_layout(t, a, n)
+    pos0, opos, odep = O.cycle_rows(t, a, n)
+    assert pos == opos and dep == odep and pos[0] == pos0
+
+
+def test_layout_rejects_bad_arguments():
+    for args in ((5, 0, 4), (5, 5, 4), (4, 4, 4)):
+        with pytest.raises(spd.SpdError):
+            spd.spd_layout(*args)
+
+
+def test_workspace_sizes():
+    s = synth.HEADLINE
+    c = _cfg(s)
+    for call in (spd.SPD_CALL_FUSE, spd.SPD_CALL_PDM, spd.SPD_CALL_LM_HEAD):
+        a = spd.spd_workspace_size(call, c, 9, 0, 2112)
+        b = spd.spd_workspace_size(call, c, 256, 0, 2112) if call != spd.SPD_CALL_LM_HEAD else a
+        assert a >= spd.SPD_WS_COUNTER_BYTES and b >= a
+    assert spd.spd_workspace_size(spd.SPD_CALL_VERIFY, c, 64, 7) > spd.SPD_WS_COUNTER_BYTES
+    assert spd.spd_workspace_size(99, c, 1) == 0
+    assert spd.spd_workspace_size(spd.SPD_CALL_FUSE, c, 0) == 0
+
+
+def test_argument_errors_return_before_any_launch():
+    """Invalid arguments are rejected on the host (no device needed)."""
+    lib = spd.lib()
+    s = synth.TINY
+    c = _cfg(s)
+    tab = (ctypes.c_int32 * ((s.n + 1) * s.m))(*([0] * ((s.n + 1) * s.m)))
+    rc = lib.spd_fuse_features(ctypes.byref(c), None, 64, 3, tab, 0, 5, 4, None, None, None, None,
+                               0, None)
+    assert rc == spd.SPD_E_INVALID
+    fake = 1 << 40   # never dereferenced: the size check fails first
+    rc = lib.spd_fuse_features(ctypes.byref(c), fake, 64, 3, tab, 0, 5, 4, fake, fake, fake, fake,
+                               16, None)
+    assert rc == spd.SPD_E_WORKSPACE
+    rc = lib.spd_fuse_features(ctypes.byref(c), fake, 64, 3, tab, 62, 5, 4, fake, fake, fake, fake,
+                               1 << 30, None)
+    assert rc == spd.SPD_E_INVALID        # pos0 + M > T_cap
+    bad = _cfg(s, hd=48)
+    lw = (spd.spd_layer_weights * 1)()
+    for k, _ in spd.spd_layer_weights._fields_:
+        setattr(lw[0], k, fake)
+    rc = lib.spd_pdm_step(ctypes.byref(bad), lw, fake, fake, fake, 64, fake, 0, 5, fake, fake,
+                          1 << 30, None)
+    assert rc == spd.SPD_E_UNSUPPORTED
+    rc = lib.spd_lm_head(ctypes.byref(c), fake, fake, 17, ctypes.c_float(0.0), None, fake, None,
+                         fake, fake, 1 << 30, None)
+    assert rc == spd.SPD_E_INVALID        # rows > 16
+    rc = lib.spd_lm_head(ctypes.byref(c), fake, fake, 1, ctypes.c_float(1.0), None, fake, None,
+                         fake, fake, 1 << 30, None)
+    assert rc == spd.SPD_E_INVALID        # T > 0 needs probs and words
+    rc = lib.spd_verify(0, 1, 10, ctypes.c_float(1.0), 0, fake, fake, fake, fake, fake, fake, fake,
+                        1 << 30, None)
+    assert rc == spd.SPD_E_INVALID
+    rc = lib.spd_verify(1, 1, 10, ctypes.c_float(1.0), 0, fake, fake, fake, fake, fake, fake, fake,
+                        16, None)
+    assert rc == spd.SPD_E_WORKSPACE
+    rc = lib.spd_rollback(None, 4, fake, fake, fake, fake, 64, None)
+    assert rc == spd.SPD_E_INVALID
+    assert spd.status_string(spd.SPD_E_WORKSPACE) == "workspace too small"

@@ -1,0 +1,411 @@
+"""GPU parity: every C-ABI call against the CPU oracle on the same seeded inputs.
+
+Floating-point outputs (features, PDM rows, logits, probabilities) must agree to
+max|gpu - oracle| / rms(oracle) <= 1e-5 (fp32 path) or 2e-2 (bf16 path).  Token
+decisions, accept counts and rollback state must be bit-exact whenever the
+decision functions are given identical fp32 rows and random words: the oracle's
+decision functions are applied to the rows the GPU produced.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import cycle as OC
+from oracle import spd as O
+from spd_testlib import TOL_BF16, TOL_F32, ensure_built, f64, rel_err, tol_for
+
+pytestmark = pytest.mark.gpu
+
+spd = ensure_built()
+from pipeline_draft_step_amd.cycle import DeviceWeights, SpdCycle, SpdModel  # noqa: E402
+
+DEV = "cuda"
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def device_model(ci):
+    s = ci.shape
+    w = DeviceWeights(store=ci.store, h_final=ci.h_final, fc_norm=ci.fc_norm, w_fc=ci.w_fc,
+                      layers=ci.layers, final_norm=ci.final_norm, w_dlm=ci.w_dlm, w_tlm=ci.w_tlm)
+    return SpdModel(L=s.L, n=s.n, anchors=s.anchors, d=s.d, Ls=s.Ls, Hq=s.Hq, Hkv=s.Hkv, hd=s.hd,
+                    dff=s.dff, V=s.V, dtype=s.dtype, weights=w, anchor_mode=s.anchor_mode,
+                    norm_k0=s.norm_k0, eps=s.eps, rope_theta=s.rope_theta)
+
+
+def row_depths(M, a, n):
+    return [n if r < M - a else M - 1 - r for r in range(M)]
+
+
+SMALL_BF16 = synth.SpdShape("small_bf16", L=32, n=8, anchors=(0, 8, 16, 24, 31), d=256, Ls=2,
+                            Hq=4, Hkv=2, hd=128, dff=512, V=4096, dtype=synth.BF16, ctx=96,
+                            temperature=1.0, lm_std=3.0 / 16)
+SMALL_BF16_H64 = SMALL_BF16.with_(name="small_bf16_hd64", Hq=8, Hkv=2, hd=64, d=192, dff=384)
+
+
+# ------------------------------------------------------------------ features
+
+FUSE_CASES = [
+    ("tiny", synth.TINY, [(32, 4), (32, 1), (32, 3), (28, 0)]),
+    ("small_zero", SMALL_BF16, [(96, 8), (96, 3), (96, 1), (80, 0)]),
+    ("small_clamp", SMALL_BF16.with_(anchor_mode=synth.CLAMP_MIN), [(96, 8), (96, 5)]),
+    ("small_normk0", SMALL_BF16.with_(norm_k0=1), [(96, 8), (96, 2)]),
+    ("headline", synth.HEADLINE, [(2048, 8), (2048, 3), (2048, 1)]),
+    ("9b", synth.SHAPES["qwen35_9b_n16_ls4_t1"], [(4096, 16)]),
+]
+
+
+@pytest.mark.parametrize("name,shape,layouts", FUSE_CASES, ids=[c[0] for c in FUSE_CASES])
+def test_fuse_features(name, shape, layouts):
+    ci = synth.cycle_inputs(shape, device=DEV, with_heads=False)
+    model = device_model(ci)
+    cyc = SpdCycle(model, shape.temperature)
+    om = OC.model_from_inputs(ci, with_heads=False)
+    for (t, a) in layouts:
+        M = a + 1 if a > 0 else t
+        pos0 = t - 1 - a if a > 0 else 0
+        say(name, "fuse", t, a, M)
+        out = torch.empty(M, shape.d, device=DEV)
+        cyc.features(pos0, M, a, out=out)
+        torch.cuda.synchronize()
+        ref = O.fuse_features(om.store, om.store_layers, list(range(pos0, pos0 + M)),
+                              row_depths(M, a, shape.n), om.fc_norm, om.w_fc, L=shape.L, n=shape.n,
+                              anchors=shape.anchors, mode=shape.anchor_mode, eps=shape.eps,
+                              norm_k0=bool(shape.norm_k0))
+        err = rel_err(f64(out), ref)
+        assert err < tol_for(shape.dtype), (t, a, err)
+
+
+# ------------------------------------------------------------------ PDM step
+
+def _oracle_cache_from(k, v, pos0, shape):
+    c = O.PdmCache(shape.Ls, O.PdmConfig(d=shape.d, Hq=shape.Hq, Hkv=shape.Hkv, hd=shape.hd,
+                                         dff=shape.dff))
+    kk = f64(k)  # [Ls][Hkv][T][hd]
+    vv = f64(v)  # [Ls][Hkv][hd][T]
+    c.k = [kk[l].transpose(1, 0, 2)[:pos0].copy() for l in range(shape.Ls)]
+    c.v = [vv[l].transpose(2, 0, 1)[:pos0].copy() for l in range(shape.Ls)]
+    return c
+
+
+def _check_cache_rows(cyc, cache, lo, hi, tol):
+    for l in range(len(cache.k)):
+        gk = f64(cyc.k_cache[l]).transpose(1, 0, 2)[lo:hi]
+        gv = f64(cyc.v_cache[l]).transpose(2, 0, 1)[lo:hi]
+        assert rel_err(gk, cache.k[l][lo:hi]) < tol
+        assert rel_err(gv, cache.v[l][lo:hi]) < tol
+
+
+@pytest.mark.parametrize("shape", [synth.TINY, SMALL_BF16, SMALL_BF16_H64],
+                         ids=["tiny", "small_bf16", "small_bf16_hd64"])
+def test_pdm_prefill_then_cycle(shape):
+    """Prefill through the library, then one saturated and one partial cycle; the
+    oracle runs the same rows incrementally (pinned equal to full recompute)."""
+    ci = synth.cycle_inputs(shape, device=DEV, with_heads=False)
+    model = device_model(ci)
+    cyc = SpdCycle(model, shape.temperature)
+    om = OC.model_from_inputs(ci, with_heads=False)
+    tol = tol_for(shape.dtype)
+    t, n = shape.ctx, shape.n
+    G = synth.normal((t + 2, shape.d), 1.0, device=DEV, seed=9, name="pdm_rows")
+    Gh = f64(G)
+    cache = O.PdmCache(shape.Ls, om.pdm)
+    P = t - 1 - n
+    say(shape.name, "prefill", P)
+    cyc.pdm(0, P, g=G[:P].contiguous())
+    torch.cuda.synchronize()
+    last, _ = O.pdm_step(Gh[:P], 0, cache, om.layers, om.final_norm, om.pdm)
+    assert rel_err(f64(cyc.h_last), last) < tol
+    _check_cache_rows(cyc, cache, 0, P, tol)
+    for (pos0, M) in ((P, n + 1), (P + 1, 3)):
+        say(shape.name, "step", pos0, M)
+        rows = G[pos0:pos0 + M].contiguous()
+        cyc.pdm(pos0, M, g=rows)
+        torch.cuda.synchronize()
+        cache.truncate(pos0)
+        last, _ = O.pdm_step(Gh[pos0:pos0 + M], pos0, cache, om.layers, om.final_norm, om.pdm)
+        assert rel_err(f64(cyc.h_last), last) < tol, (pos0, M)
+        _check_cache_rows(cyc, cache, pos0, pos0 + M, tol)
+
+
+@pytest.mark.parametrize("shape", [synth.HEADLINE, synth.SHAPES["qwen35_4b_n4_ls1_greedy"],
+                                   synth.SHAPES["qwen35_9b_n16_ls4_t1"]],
+                         ids=["headline", "4b_n4", "9b_n16"])
+def test_pdm_full_size_on_synthetic_cache(shape):
+    """Full-size PDM step at context t: the committed cache holds seeded values
+    (an input of the call), the M new rows are checked against the oracle."""
+    ci = synth.cycle_inputs(shape, device=DEV, with_heads=False)
+    model = device_model(ci)
+    cyc = SpdCycle(model, shape.temperature)
+    om = OC.model_from_inputs(ci, with_heads=False)
+    k, v = synth.kv_cache(shape, model.T_cap, device=DEV)
+    t, n = shape.ctx, shape.n
+    for a in (n, 1):
+        cyc.k_cache.copy_(k)       # every step starts from the seeded committed cache
+        cyc.v_cache.copy_(v)
+        pos0, M = t - 1 - a, a + 1
+        say(shape.name, "pdm full", pos0, M)
+        g = synth.normal((M, shape.d), 1.0, device=DEV, seed=10 + a, name="rows")
+        cyc.pdm(pos0, M, g=g)
+        torch.cuda.synchronize()
+        cache = _oracle_cache_from(k, v, pos0, shape)
+        last, _ = O.pdm_step(f64(g), pos0, cache, om.layers, om.final_norm, om.pdm)
+        err = rel_err(f64(cyc.h_last), last)
+        assert err < TOL_BF16, (a, err)
+        _check_cache_rows(cyc, cache, pos0, pos0 + M, TOL_BF16)
+
+
+# ------------------------------------------------------------------ LM head
+
+def _lm_case(V, d, dtype, std, rows, T, seed):
+    wdt = synth.storage_dtype(dtype)
+    W = synth.normal((V, d), std, device=DEV, seed=seed, name="w_lm", dtype=wdt)
+    h = synth.normal((rows, d), 1.0, device=DEV, seed=seed, name="h")
+    cfg = spd.make_config(L=1, n=1, m=1, d=d, Ls=1, Hq=1, Hkv=1, hd=16, dff=64, V=V, dtype=dtype)
+    words = synth.rand_words(seed, 5, rows)
+    wt = synth.words_tensor(words, DEV)
+    logits = torch.empty(rows, V, device=DEV)
+    probs = torch.empty(rows, V, device=DEV)
+    tok = torch.zeros(rows, dtype=torch.int32, device=DEV)
+    ws = torch.zeros(spd.spd_workspace_size(spd.SPD_CALL_LM_HEAD, cfg, rows), dtype=torch.uint8,
+                     device=DEV)
+    spd.spd_lm_head(cfg, W, h, rows, T, wt, logits, probs, tok, ws)
+    torch.cuda.synchronize()
+    return W, h, words, logits, probs, tok, cfg, ws, wt
+
+
+LM_CASES = [
+    ("tiny_t0", 512, 64, 0, 0.02, 1, 0.0),
+    ("tiny_t1", 512, 64, 0, 1.0, 1, 1.0),
+    ("tiny_rows", 512, 64, 0, 1.0, 5, 0.7),
+    ("full_t1", 151936, 2560, 1, 3.0 / np.sqrt(2560), 1, 1.0),
+    ("full_t0", 151936, 2560, 1, 0.02, 1, 0.0),
+    ("full_rows3", 151936, 2560, 1, 3.0 / np.sqrt(2560), 3, 1.0),
+    ("9b_t1", 151936, 4096, 1, 3.0 / np.sqrt(4096), 1, 1.0),
+    ("ragged_v", 151936 - 37, 2560, 1, 3.0 / np.sqrt(2560), 1, 1.0),
+]
+
+
+@pytest.mark.parametrize("name,V,d,dtype,std,rows,T", LM_CASES, ids=[c[0] for c in LM_CASES])
+def test_lm_head(name, V, d, dtype, std, rows, T):
+    say("lm_head", name)
+    W, h, words, logits, probs, tok, *_ = _lm_case(V, d, dtype, std, rows, T, seed=11)
+    Wh, hh = f64(W), f64(h)
+    gl = f64(logits)
+    toks = tok.cpu().numpy()
+    for r in range(rows):
+        ref = O.lm_logits(Wh, hh[r])
+        assert rel_err(gl[r], ref) < tol_for(dtype), r
+        if T == 0:
+            assert toks[r] == O.argmax_first(logits[r].cpu().numpy())
+        else:
+            gp = probs[r].cpu().numpy()
+            pref = O.softmax(logits[r].cpu().numpy().astype(np.float64), T)
+            assert np.max(np.abs(gp - pref)) <= 1e-5 * pref.max()
+            assert toks[r] == O.sample_probs(gp, int(words[r]) >> 32)
+
+
+def test_lm_head_is_deterministic():
+    say("lm_head determinism")
+    W, h, words, logits, probs, tok, cfg, ws, wt = _lm_case(151936, 2560, 1, 3.0 / np.sqrt(2560),
+                                                            1, 1.0, 12)
+    l2 = torch.empty_like(logits)
+    p2 = torch.empty_like(probs)
+    t2 = torch.zeros_like(tok)
+    spd.spd_lm_head(cfg, W, h, 1, 1.0, wt, l2, p2, t2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(l2, logits) and torch.equal(p2, probs) and torch.equal(t2, tok)
+
+
+# ------------------------------------------------------------------ verify
+
+def _verify_gpu(p, q, draft, words, T, bonus):
+    B, G = draft.shape
+    V = p.shape[-1]
+    cfg = spd.make_config(L=1, n=1, m=1, d=64, Ls=1, Hq=1, Hkv=1, hd=16, dff=64, V=V, dtype=0)
+    ws = torch.zeros(spd.spd_workspace_size(spd.SPD_CALL_VERIFY, cfg, B, G), dtype=torch.uint8,
+                     device=DEV)
+    na = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+    nt = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+    spd.spd_verify(B, G, V, T, bonus, p, q, draft, synth.words_tensor(words, DEV), na, nt, ws)
+    torch.cuda.synchronize()
+    return na.cpu().numpy(), nt.cpu().numpy()
+
+
+def test_verify_batched_stress_bitexact():
+    v = synth.VERIFY_STRESS
+    say("verify stress", v.B, v.gamma, v.V)
+    p, q, draft, words = synth.verify_stress_inputs(v, device=DEV)
+    na, nt = _verify_gpu(p, q, draft, words, v.temperature, v.bonus)
+    pc, qc, dc = p.cpu().numpy(), q.cpu().numpy(), draft.cpu().numpy()
+    hist = np.zeros(v.gamma + 1, int)
+    for b in range(v.B):
+        ref = O.verify(pc[b], qc[b], list(dc[b]), words[b], temperature=v.temperature,
+                       bonus=bool(v.bonus))
+        assert (int(na[b]), int(nt[b])) == ref, b
+        hist[ref[0]] += 1
+    assert hist[0] < v.B      # the correlated drafts are accepted at times
+
+
+def test_verify_greedy_gamma_form():
+    say("verify greedy")
+    B, G, V = 16, 7, 151936
+    logits = synth.normal((B, G + 1, V), 3.0, device=DEV, seed=21, name="vg_logits")
+    am = logits.argmax(-1).to(torch.int32)
+    draft = am[:, :G].clone()
+    # sequence b keeps its first b % (G+1) drafts right, then goes wrong
+    for b in range(B):
+        j = b % (G + 1)
+        if j < G:
+            draft[b, j] = (draft[b, j] + 1) % V
+    words = np.zeros((B, G + 1, 2), np.uint64)
+    na, nt = _verify_gpu(logits, None, draft.contiguous(), words, 0.0, 1)
+    lc, dc = logits.cpu().numpy(), draft.cpu().numpy()
+    for b in range(B):
+        ref = O.verify(lc[b], None, list(dc[b]), words[b], temperature=0, bonus=True)
+        assert (int(na[b]), int(nt[b])) == ref
+        assert ref[0] == b % (G + 1)
+
+
+def test_verify_streaming_edge_cases():
+    """B = 1, gamma = 1 as in the SPD cycle: forced accept (p(x) >= q(x)), forced
+    reject (p(x) = 0), empty residual (fallback to p), a ragged vocabulary."""
+    V = 151936 - 5
+    say("verify streaming edge", V)
+    base = torch.softmax(synth.normal((V,), 3.0, device=DEV, seed=30, name="e_p"), 0)
+    qrow = torch.softmax(synth.normal((V,), 3.0, device=DEV, seed=31, name="e_q"), 0)
+    cases = []
+    x = int(torch.argmax(base).item())
+    cases.append((base, qrow, x))                                   # p(x) large: accept likely
+    p0 = base.clone(); p0[17] = 0.0
+    cases.append((p0, qrow, 17))                                    # p(x) = 0: reject
+    cases.append((base * 0.5, base.clone(), x))                     # residual empty at reject
+    rng = np.random.default_rng(5)
+    for (p, q, xx) in cases:
+        for _ in range(3):
+            words = rng.integers(0, 2 ** 64, size=(1, 2, 2), dtype=np.uint64)
+            d = torch.tensor([[xx]], dtype=torch.int32, device=DEV)
+            na, nt = _verify_gpu(p.reshape(1, 1, V).contiguous(), q.reshape(1, 1, V).contiguous(),
+                                 d, words, 1.0, 0)
+            ref = O.verify([p.cpu().numpy()], [q.cpu().numpy()], [xx], words[0], temperature=1.0,
+                           bonus=False)
+            assert (int(na[0]), int(nt[0])) == ref
+
+
+# ------------------------------------------------------------------ rollback
+
+def test_rollback_state_machine():
+    n, T_cap = 4, 64
+    say("rollback")
+    st = torch.zeros(4, dtype=torch.int32, device=DEV)
+    tokens = torch.zeros(T_cap, dtype=torch.int32, device=DEV)
+    d = torch.zeros(1, dtype=torch.int32, device=DEV)
+    na = torch.zeros(1, dtype=torch.int32, device=DEV)
+    nx = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ost = O.SeqState(t=10, a=n, tokens=list(range(100, 110)))
+    st.copy_(torch.tensor([10, n, 0, 0], dtype=torch.int32))
+    tokens[:10] = torch.arange(100, 110, dtype=torch.int32)
+    rng = np.random.default_rng(3)
+    for step in range(60):
+        dv, av, xv = int(rng.integers(0, 1000)), int(rng.random() < 0.5), int(rng.integers(0, 1000))
+        d.fill_(dv); na.fill_(av); nx.fill_(xv)
+        spd.spd_rollback(st, n, d, na, nx, tokens, T_cap)
+        O.transition(ost, n, dv, ost.a == n, av, xv)
+        torch.cuda.synchronize()
+        assert st.tolist() == [ost.t, ost.a, ost.commits, ost.cycles], step
+        assert tokens[:ost.t].tolist() == ost.tokens
+
+
+# ------------------------------------------------------------------ whole cycles
+
+def test_cycle_trajectory_tiny():
+    """A device-state trajectory (greedy) against the oracle: each cycle's
+    features, last hidden row and logits within fp32 tolerance; the decisions the
+    device takes equal the oracle decision functions on the device's rows; the
+    state after every cycle matches the oracle state machine."""
+    s = synth.TINY
+    ci = synth.cycle_inputs(s, device=DEV, T_cap=128)
+    model = device_model(ci)
+    cyc = SpdCycle(model, 0.0)
+    om = OC.model_from_inputs(ci)
+    t0 = s.ctx
+    ost = O.SeqState(t=t0, a=s.n, tokens=list(range(t0)))
+    cyc.set_state(t0, s.n, ost.tokens)
+    cyc.prefill(t0 - 1 - s.n)
+    cache = OC.prefill(om, t0, s.n)
+    wb = synth.cycle_words(48)
+    wdev = synth.words_tensor(wb, DEV)
+    for c in range(48):
+        t, a = ost.t, ost.a
+        say("trajectory cycle", c, t, a)
+        assert cyc.read_state()[:2] == (t, a)
+        cyc.cycle(t, a, wdev[c])
+        torch.cuda.synchronize()
+        out = OC.run_cycle(om, O.SeqState(t=t, a=a, tokens=list(ost.tokens)), cache, {}, 0.0, wb[c])
+        assert rel_err(f64(cyc.h_last), out.h_last) < TOL_F32
+        gl = cyc.dlogits.cpu().numpy()
+        assert rel_err(gl, out.draft_logits) < TOL_F32
+        drafted = O.argmax_first(gl)
+        assert int(cyc.dtoken.item()) == drafted
+        na, nt = -1, -1
+        if a == s.n:
+            tl = cyc.tlogits.cpu().numpy()
+            assert rel_err(tl, out.target_logits) < TOL_F32
+            na, nt = O.verify([tl], None, [ost.tokens[t - s.n + 1]], np.zeros((2, 2), np.uint64),
+                              temperature=0, bonus=False)
+            assert (int(cyc.n_accept.item()), int(cyc.next_token.item())) == (na, nt)
+        O.transition(ost, s.n, drafted, a == s.n, na, nt)
+        tt, aa, cm, cy = cyc.read_state()
+        assert (tt, aa, cm, cy) == (ost.t, ost.a, ost.commits, ost.cycles)
+        assert cyc.tokens[:ost.t].tolist() == ost.tokens
+        cache.truncate(ost.t - 1 - ost.a)
+
+
+def test_cycle_full_headline_sampled():
+    """One saturated and one partial cycle of the headline workload (T = 1) on a
+    seeded committed cache: features, last row, draft/target logits and
+    probabilities within bf16 tolerance; the sampled draft, the verify outcome
+    and the state update bit-exact on the device's rows."""
+    s = synth.HEADLINE
+    ci = synth.cycle_inputs(s, device=DEV)
+    model = device_model(ci)
+    cyc = SpdCycle(model, 1.0)
+    om = OC.model_from_inputs(ci)
+    k, v = synth.kv_cache(s, model.T_cap, device=DEV)
+    t = s.ctx
+    wb = synth.cycle_words(2, seed=7)
+    wdev = synth.words_tensor(wb, DEV)
+    qstand = torch.softmax(synth.draft_row_logits(s.V, 3.0, device=DEV, seed=8, name="q_standin"), 0)
+    xg = torch.Generator(device=DEV)
+    xg.manual_seed(99)
+    x = int(torch.multinomial(qstand, 1, generator=xg).item())
+    for c, a in enumerate((s.n, 3)):
+        say("headline cycle", a)
+        tokens = list(range(t))
+        tokens[t - s.n + 1] = x
+        cyc.k_cache.copy_(k)       # each cycle starts from the seeded committed cache
+        cyc.v_cache.copy_(v)
+        cyc.set_state(t, a, tokens)
+        cyc.cycle(t, a, wdev[c], q_row=qstand)
+        torch.cuda.synchronize()
+        pos0 = t - 1 - a
+        cache = _oracle_cache_from(k, v, pos0, s)
+        st = O.SeqState(t=t, a=a, tokens=list(tokens))
+        gq = cyc.ring[t % s.n].cpu().numpy()
+        gp = cyc.p.cpu().numpy()
+        out = OC.run_cycle(om, st, cache, {}, 1.0, wb[c], q_override=qstand.cpu().numpy(),
+                           probs_from={"q": gq, "p": gp})
+        assert rel_err(f64(cyc.h_last), out.h_last) < TOL_BF16
+        assert rel_err(cyc.dlogits.cpu().numpy(), out.draft_logits) < TOL_BF16
+        assert int(cyc.dtoken.item()) == out.drafted
+        if a == s.n:
+            assert rel_err(cyc.tlogits.cpu().numpy(), out.target_logits) < TOL_BF16
+            assert (int(cyc.n_accept.item()), int(cyc.next_token.item())) == (out.n_accept,
+                                                                             out.next_token)
+        assert cyc.read_state() == (st.t, st.a, st.commits, st.cycles)

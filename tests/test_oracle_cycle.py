@@ -27,7 +27,7 @@ def test_tiny_trajectory_matches_full_recompute():
     st = O.SeqState(t=t0, a=s.n, tokens=list(range(t0)))
     cache = C.prefill(om, st.t, st.a)
     ring = {}
-    words = synth.rand_words(2, 0, 40 * 8).reshape(40, 2, 4)
+    words = synth.cycle_words(40)
     rejects = 0
     for c in range(40):
         before = O.SeqState(t=st.t, a=st.a)
@@ -48,7 +48,7 @@ def test_sampled_cycle_uses_ring_row():
     st = O.SeqState(t=s.ctx, a=1, tokens=list(range(s.ctx)))
     cache = C.prefill(om, st.t, st.a)
     ring = {}
-    words = synth.rand_words(2, 0, 30 * 8).reshape(30, 2, 4)
+    words = synth.cycle_words(30)
     for c in range(30):
         tb, ab = st.t, st.a
         out = C.run_cycle(om, st, cache, ring, 1.0, words[c])
