@@ -143,18 +143,26 @@ def main():
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record()
+    main = torch.cuda.current_stream()
     for i in range(args.steps):
         c = args.warmup + i
         a = sched[c]
-        n = s.n
         pos0, M = t - 1 - a, a + 1
+        sat = a == s.n
+        if sat:  # target head + verify on the side stream (as SpdCycle.cycle does)
+            cyc.ev_fork.record(main)
+            cyc.side.wait_event(cyc.ev_fork)
+            with torch.cuda.stream(cyc.side):
+                cyc.target_and_verify(t, words[c], q_row=qstand, x_ptr=x_dev.data_ptr(),
+                                      ws=cyc.ws_side)
+            cyc.ev_join.record(cyc.side)
         cyc.features(pos0, M, a)
         cyc.pdm(pos0, M)
         head_ev[i][0].record()
         cyc.draft(t, words[c])
         head_ev[i][1].record()
-        if a == n:
-            cyc.target_and_verify(t, words[c], q_row=qstand, x_ptr=x_dev.data_ptr())
+        if sat:
+            main.wait_event(cyc.ev_join)
         cyc.rollback()
     stop.record()
     torch.cuda.synchronize()

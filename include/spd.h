@@ -19,14 +19,14 @@
  *    HOST are read during the call only.  Nothing is retained after return.
  *  - `stream` is a hipStream_t (NULL = the null stream).  Calls enqueue kernels on it
  *    and return without synchronising; they never allocate or free memory.
+ *  - Every device pointer must be 16-byte aligned (torch allocations are).
  *  - Argument errors are detected on the host and returned before anything is
  *    enqueued.  Values held in device memory (tokens, probabilities) are not
  *    inspected on the host; kernels clamp out-of-range indices so that no access
  *    leaves the buffers described below.
  *  - Workspaces: `ws` is a DEVICE buffer of at least spd_workspace_size(...) bytes,
- *    256-byte aligned.  Its first SPD_WS_COUNTER_BYTES bytes hold arrival counters
- *    that must be zero before the workspace is first used (allocate it zero-filled);
- *    every call leaves them zero again.  Calls that share a workspace must not run
+ *    16-byte aligned, holding partial results between the kernels of one call.  It
+ *    needs no initialisation.  Calls that share a workspace must not run
  *    concurrently (use one workspace per stream).
  *  - dtype SPD_BF16: weights, anchors and the key/value cache are bfloat16 (bit
  *    pattern in uint16); SPD_F32: all of them are float32.  Features, hidden rows,
@@ -55,7 +55,6 @@ enum { SPD_F32 = 0, SPD_BF16 = 1 };
 enum { SPD_ANCHOR_ZERO_MASK = 0, SPD_ANCHOR_CLAMP_MIN = 1 };
 enum { SPD_CALL_FUSE = 0, SPD_CALL_PDM = 1, SPD_CALL_LM_HEAD = 2, SPD_CALL_VERIFY = 3 };
 
-#define SPD_WS_COUNTER_BYTES 65536
 #define SPD_MAX_ANCHORS 8
 #define SPD_MAX_STAGES 32
 

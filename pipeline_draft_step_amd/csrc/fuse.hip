@@ -4,7 +4,7 @@
 // at depth k uses every anchor b_j <= l_max(k); the review blog's core formulas
 // give the operator FC(norm(Concat(.))) and g^0 = FC(H^0).
 //
-// One launch of the skinny GEMM.  The input functor gathers the row's eligible
+// The skinny GEMM (plus its finisher when split over K).  The input functor gathers the row's eligible
 // anchor states for its K-slice straight from the anchor store into LDS (empty
 // slots are zeros; gamma is applied; the k = 0 rows read slot 0 only, without
 // gamma) and records the slice's sum of squares.  Because FC is linear,
@@ -35,26 +35,35 @@ struct InAnchor {
   SlotTable tab;
   float* xss;  // [nblocks][S][M] slice sums of squares
   __device__ void stage(const XStage<WT>& xs, int m0, int Mt, int k0, int kw, int nb, int s, int S) const {
+    // wave w stages rows w, w+4, ...: 4 consecutive columns per lane and step
+    // (d % 4 == 0, so a group of 4 never straddles two anchor slots)
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int kv = kw >> 2;
     for (int mm = wave; mm < Mt; mm += GEMM_WAVES) {
       const int r = m0 + mm;
       const int k = depth(r);
       const bool plain = (k == 0) && !norm_k0;
       const size_t base = (size_t)(pos0 + r) * S_store;
       float sq = 0.f;
-      for (int kk = lane; kk < kw; kk += WAVE) {
-        const int col = k0 + kk;
+#pragma unroll 4
+      for (int u = lane; u < kv; u += WAVE) {
+        const int col = k0 + (u << 2);
         const int j = col / d;
         const int c = col - j * d;
         int slot = tab.v[k * m + j];
         if (plain && j != 0) slot = -1;
-        float v = 0.f;
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
         if (slot >= 0 && slot < S_store) {
-          v = to_f<WT>(store[(base + slot) * d + c]);
-          sq += v * v;
-          if (!plain) v *= to_f<WT>(gamma[col]);
+          load4(store + (base + slot) * d + c, v);
+          float gm[4] = {1.f, 1.f, 1.f, 1.f};
+          if (!plain) load4(gamma + col, gm);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            sq += v[i] * v[i];
+            v[i] *= gm[i];
+          }
         }
-        xs.put(mm, kk, v);
+        xs.put4(mm, u << 2, v);
       }
       sq = wave_sum(sq);
       if (lane == 0) xss[((size_t)nb * S + s) * depth.M + r] = sq;
@@ -74,17 +83,20 @@ struct EpiFeature {
   __device__ void run(const Y& y, int nb, int m0, int Mt, const RM&) const {
     constexpr int TC = 64 * NT;
     __shared__ float inv[32];
-    if ((int)threadIdx.x < Mt) {
-      const int r = m0 + threadIdx.x;
+    const int wave = threadIdx.x >> 6;
+    for (int mm = wave; mm < Mt; mm += GEMM_WAVES) {
+      const int r = m0 + mm;
       const int k = depth(r);
-      if (k == 0 && !norm_k0) {
-        inv[threadIdx.x] = 1.f;
-      } else {
-        int filled = 0;
-        for (int j = 0; j < m; ++j) filled += tab.v[k * m + j] >= 0;
-        float t = 0.f;
-        for (int q = 0; q < S; ++q) t += xss[((size_t)nb * S + q) * depth.M + r];
-        inv[threadIdx.x] = filled > 0 ? 1.0f / sqrtf(t / (float)(filled * d) + eps) : 0.f;
+      const float* xp = xss + (size_t)nb * S * depth.M + r;
+      const float t = wave_sum_of(S, [&](int q) { return xp[(size_t)q * depth.M]; });
+      if ((threadIdx.x & 63) == 0) {
+        if (k == 0 && !norm_k0) {
+          inv[mm] = 1.f;
+        } else {
+          int filled = 0;
+          for (int j = 0; j < m; ++j) filled += tab.v[k * m + j] >= 0;
+          inv[mm] = filled > 0 ? 1.0f / sqrtf(t / (float)(filled * d) + eps) : 0.f;
+        }
       }
     }
     __syncthreads();
@@ -106,12 +118,12 @@ static FusePlan plan_fuse(const spd_config* cfg, int M) {
   const bool bf = cfg->dtype == SPD_BF16;
   const int kstep = bf ? Mfma<bf16>::KSTEP : Mfma<float>::KSTEP;
   p.gp = plan_gemm(cfg->d, cfg->m * cfg->d, M, kstep, bf ? 2 : 4, 1);
-  size_t off = SPD_WS_COUNTER_BYTES;
+  size_t off = 0;
   p.off_xss = off;
   off = align256(off + (size_t)p.gp.nblocks * p.gp.S * M * sizeof(float));
   p.off_part = off;
   if (p.gp.S > 1) off = align256(off + (size_t)p.gp.S * M * cfg->d * sizeof(float));
-  p.total = off;
+  p.total = off > 256 ? off : 256;
   return p;
 }
 
@@ -140,7 +152,6 @@ static int fuse_impl(const spd_config* cfg, const void* hstore, int64_t T_cap, i
   gs.nsteps = p.gp.nsteps;
   gs.ldx = p.gp.ldx;
   gs.part = reinterpret_cast<float*>(w + p.off_part);
-  gs.counters = reinterpret_cast<unsigned*>(w);
   gs.nblocks = p.gp.nblocks;
 
   InAnchor<WT> in{static_cast<const WT*>(hstore), static_cast<const WT*>(norm_w), T_cap, S_store,
@@ -165,7 +176,9 @@ extern "C" int spd_fuse_features(const spd_config* cfg, const void* hstore, int6
   if (cfg->d % 64) return SPD_E_UNSUPPORTED;
   for (int i = 0; i < (cfg->n + 1) * cfg->m; ++i)
     if (slot_tab[i] < -1 || slot_tab[i] >= S) return SPD_E_INVALID;
-  if (!aligned16(hstore) || !aligned16(fc_w) || !aligned16(ws)) return SPD_E_INVALID;
+  if (!aligned16(hstore) || !aligned16(fc_w) || !aligned16(norm_w) || !aligned16(g) ||
+      !aligned16(ws))
+    return SPD_E_INVALID;
   if (ws_bytes < fuse_workspace(cfg, M)) return SPD_E_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (cfg->dtype == SPD_BF16)

@@ -10,7 +10,9 @@
 //   combine   : log-sum-exp merge of the chunk partials.
 //   O GEMM    : h += W_o attn                (epilogue keeps row sums of squares)
 //   gate/up   : X = RMSNorm(h)*mlp_norm; epilogue silu(gate)*up
-//   down GEMM : h += W_down act; the last layer also writes h_last = RMSNorm(h[M-1]).
+//   down GEMM : h += W_down act.
+// GEMMs split over K add a small finisher launch that sums the partial tiles and
+// runs the epilogue.  After the last layer, h_last = RMSNorm(h[M-1]) * final_norm.
 #include <math.h>
 
 #include <algorithm>
@@ -22,7 +24,22 @@
 namespace spd {
 
 constexpr int ATT_KC = 64;   // keys per chunk
-constexpr int ATT_TPG = 4;   // 16-row query tiles per attention block
+constexpr int ATT_TPG = 1;   // 16-row query tiles per attention block (one wave each)
+
+// h_last = RMSNorm(h[M-1]) * final_norm, row statistics from P partial sums
+template <typename WT>
+__global__ __launch_bounds__(256) void final_norm_kernel(const float* h, const float* ss, int P, int M,
+                                                         int d, const WT* fnorm, float* h_last,
+                                                         float eps) {
+  __shared__ float s_inv;
+  if (threadIdx.x < 64) {
+    const float t = wave_sum_of(P, [&](int p) { return ss[(size_t)p * M + M - 1]; });
+    if (threadIdx.x == 0) s_inv = 1.0f / sqrtf(t / (float)d + eps);
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < d; c += 256)
+    h_last[c] = h[(size_t)(M - 1) * d + c] * s_inv * to_f<WT>(fnorm[c]);
+}
 
 // h = g, and per-64-column partial sums of squares of every row
 __global__ __launch_bounds__(64) void rows_init_kernel(const float* g, float* h, float* ss, int M,
@@ -260,8 +277,10 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a, AT* out) {
   const size_t row = (size_t)h * QR + qi;
   const float2* ml = a.pml + row * a.nch;
   float mmax = -INFINITY;
+#pragma unroll 8
   for (int c = 0; c < nvalid; ++c) mmax = fmaxf(mmax, ml[c].x);
   float L = 0.f, o0 = 0.f, o1 = 0.f;
+#pragma unroll 8
   for (int c = 0; c < nvalid; ++c) {
     const float w = expf(ml[c].x - mmax);
     L += ml[c].y * w;
@@ -291,7 +310,7 @@ static PdmPlan plan_pdm(const spd_config* c, int M, int64_t T_cap) {
   p.down = plan_gemm(c->d, c->dff, M, ks, es, 1);
   p.nch = (int)((T_cap + ATT_KC - 1) / ATT_KC);
   p.QR = M * (c->Hq / c->Hkv);
-  size_t off = SPD_WS_COUNTER_BYTES;
+  size_t off = 0;
   auto take = [&](size_t bytes) { size_t r = off; off = align256(off + bytes); return r; };
   p.off_h = take((size_t)M * c->d * 4);
   p.off_ss = take((size_t)(c->d / 64) * M * 4);
@@ -315,8 +334,7 @@ size_t pdm_workspace(const spd_config* cfg, int M, int64_t T_cap) {
   return plan_pdm(cfg, M, T_cap).total;
 }
 
-static GemmShape shape_of(const GemmPlan& gp, const void* W, int N, int K, int M, float* part,
-                          unsigned* ctr) {
+static GemmShape shape_of(const GemmPlan& gp, const void* W, int N, int K, int M, float* part) {
   GemmShape g;
   g.W = W;
   g.N = N;
@@ -326,7 +344,6 @@ static GemmShape shape_of(const GemmPlan& gp, const void* W, int N, int K, int M
   g.nsteps = gp.nsteps;
   g.ldx = gp.ldx;
   g.part = part;
-  g.counters = ctr;
   g.nblocks = gp.nblocks;
   return g;
 }
@@ -352,7 +369,6 @@ static int pdm_impl(const spd_config* c, const spd_layer_weights* layers, const 
                     float* h_last, void* ws, hipStream_t st) {
   const PdmPlan p = plan_pdm(c, M, T_cap);
   char* w = static_cast<char*>(ws);
-  unsigned* ctr = reinterpret_cast<unsigned*>(w);
   float* h = reinterpret_cast<float*>(w + p.off_h);
   float* ss = reinterpret_cast<float*>(w + p.off_ss);
   float* qb = reinterpret_cast<float*>(w + p.off_q);
@@ -389,7 +405,7 @@ static int pdm_impl(const spd_config* c, const spd_layer_weights* layers, const 
       InNorm<WT> in{h, static_cast<const WT*>(lw.attn_norm), ss, P, M, d, c->rms_eps};
       EpiQKV<WT> epi{qb, kc, vc, static_cast<const WT*>(lw.q_norm), static_cast<const WT*>(lw.k_norm),
                      Hq, Hkv, hd, pos0, T_cap, c->rms_eps, c->rope_theta};
-      rc = launch_gemm<WT, 2>(p.qkv, shape_of(p.qkv, lw.wqkv, nq, d, M, part, ctr), in, epi,
+      rc = launch_gemm<WT, 2>(p.qkv, shape_of(p.qkv, lw.wqkv, nq, d, M, part), in, epi,
                               RowMapStd{}, st);
       if (rc) return rc;
     }
@@ -406,8 +422,8 @@ static int pdm_impl(const spd_config* c, const spd_layer_weights* layers, const 
     // O projection + residual
     {
       InAct<WT, float> in{attn, Hq * hd};
-      EpiResid<WT> epi{h, ss, d, M, 0, nullptr, nullptr, ctr + CTR_FINAL, p.o.nblocks, c->rms_eps};
-      rc = launch_gemm<WT, 1>(p.o, shape_of(p.o, lw.wo, d, Hq * hd, M, part, ctr), in, epi,
+      EpiResid epi{h, ss, d, M};
+      rc = launch_gemm<WT, 1>(p.o, shape_of(p.o, lw.wo, d, Hq * hd, M, part), in, epi,
                               RowMapStd{}, st);
       if (rc) return rc;
       P = p.o.nblocks;
@@ -415,23 +431,25 @@ static int pdm_impl(const spd_config* c, const spd_layer_weights* layers, const 
     // gate/up + silu*mul
     {
       InNorm<WT> in{h, static_cast<const WT*>(lw.mlp_norm), ss, P, M, d, c->rms_eps};
-      EpiSilu<float> epi{act, dff};
-      rc = launch_gemm<WT, 1>(p.gu, shape_of(p.gu, lw.w_gate_up, 2 * dff, d, M, part, ctr), in, epi,
+      EpiSilu epi{act, dff};
+      rc = launch_gemm<WT, 1>(p.gu, shape_of(p.gu, lw.w_gate_up, 2 * dff, d, M, part), in, epi,
                               RowMapGateUp{dff}, st);
       if (rc) return rc;
     }
-    // down + residual (+ final norm of the last row after the last layer)
+    // down + residual
     {
       InAct<WT, float> in{act, dff};
-      const bool last = l == c->Ls - 1;
-      EpiResid<WT> epi{h, ss, d, M, last ? 1 : 0, static_cast<const WT*>(final_norm), h_last,
-                       ctr + CTR_FINAL, p.down.nblocks, c->rms_eps};
-      rc = launch_gemm<WT, 1>(p.down, shape_of(p.down, lw.w_down, d, dff, M, part, ctr), in, epi,
+      EpiResid epi{h, ss, d, M};
+      rc = launch_gemm<WT, 1>(p.down, shape_of(p.down, lw.w_down, d, dff, M, part), in, epi,
                               RowMapStd{}, st);
       if (rc) return rc;
       P = p.down.nblocks;
     }
   }
+  hipLaunchKernelGGL((final_norm_kernel<WT>), dim3(1), dim3(256), 0, st, h, ss, P, M, d,
+                     static_cast<const WT*>(final_norm), h_last, c->rms_eps);
+  rc = check_launch();
+  if (rc) return rc;
   if (c->Ls == 0) return SPD_E_UNSUPPORTED;
   return SPD_OK;
 }
@@ -459,10 +477,14 @@ extern "C" int spd_pdm_step(const spd_config* cfg, const spd_layer_weights* laye
     if (!w.attn_norm || !w.wqkv || !w.q_norm || !w.k_norm || !w.wo || !w.mlp_norm || !w.w_gate_up ||
         !w.w_down)
       return SPD_E_INVALID;
-    if (!aligned16(w.wqkv) || !aligned16(w.wo) || !aligned16(w.w_gate_up) || !aligned16(w.w_down))
+    if (!aligned16(w.wqkv) || !aligned16(w.wo) || !aligned16(w.w_gate_up) || !aligned16(w.w_down) ||
+        !aligned16(w.attn_norm) || !aligned16(w.mlp_norm) || !aligned16(w.q_norm) ||
+        !aligned16(w.k_norm))
       return SPD_E_INVALID;
   }
-  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(ws)) return SPD_E_INVALID;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(ws) || !aligned16(g) ||
+      !aligned16(final_norm))
+    return SPD_E_INVALID;
   if (ws_bytes < pdm_workspace(cfg, M, T_cap)) return SPD_E_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (cfg->dtype == SPD_BF16)

@@ -120,30 +120,6 @@ __device__ __forceinline__ ArgMax wave_argmax(ArgMax a) {
 }
 constexpr int ARG_NONE = 0x7fffffff;
 
-// ---------------------------------------------------------------------------
-// Last-arriver election.  Every thread of the block calls it after writing its
-// results; it returns true in exactly one block of the `expected` blocks that
-// share `counter`, after all of them have made their writes visible.  The
-// elected block resets the counter when done (arrival_reset).
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned expected) {
-  __shared__ int s_last;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    unsigned old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (old == expected - 1);
-  }
-  __syncthreads();
-  bool last = s_last != 0;
-  if (last) __threadfence();
-  return last;
-}
-__device__ __forceinline__ void arrival_reset(unsigned* counter) {
-  if (threadIdx.x == 0)
-    __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // exact integer weight of an fp32 probability: floor(p * 2^52); <= 0 or NaN -> 0
 __device__ __forceinline__ uint64_t prob_weight(float p) {
   return (p > 0.f) ? (uint64_t)((double)p * 4503599627370496.0) : 0ull;

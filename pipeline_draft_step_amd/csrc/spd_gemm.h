@@ -2,13 +2,16 @@
 // M up to 32 per tile and W streamed from HBM once.
 //
 // Work split: a workgroup (4 waves) owns an N-block of 64*NT weight rows and one
-// K-slice of S equal slices; each wave owns 16*NT rows.  The X slice (rows of
-// the M-tile) is staged in LDS by an input functor `In` that may fuse a gather
-// or a normalisation; W fragments go straight from global memory to the MFMA
-// B operand.  With S > 1 each block writes an fp32 partial tile, and the last
-// block to arrive for an (N-block, M-tile) sums the S partials in fixed order
-// and runs the epilogue functor `Epi`; with S == 1 the tile stays in LDS.
-// Results are therefore deterministic for a given launch shape.
+// of S equal K-slices; each wave owns 16*NT rows.  The X slice (rows of the
+// M-tile) is staged in LDS by an input functor `In` that may fuse a gather or a
+// normalisation; W fragments go straight from global memory to the MFMA B
+// operand, double-buffered so that a full unrolled group of loads is always in
+// flight.  With S == 1 the block runs the epilogue functor `Epi` on its own
+// tile.  With S > 1 it writes an fp32 partial tile and a second, small kernel
+// sums the S partials in fixed order and runs the epilogue: cross-block
+// reductions happen at kernel boundaries only (a device-scope fence per block
+// costs far more than a launch on this multi-die part).  Results are
+// deterministic for a given launch shape.
 #pragma once
 
 #include "spd_common.h"
@@ -22,11 +25,10 @@ constexpr int GEMM_UNROLL = 8;
 struct GemmShape {
   const void* W;
   int N, K, M;
-  int S;             // split-K factor
-  int nsteps;        // K / KSTEP
-  int ldx;           // LDS row pitch of the staged X slice (elements)
-  float* part;       // [S][M][N] partials (S > 1)
-  unsigned* counters;  // [mtiles][nblocks]
+  int S;        // split-K factor
+  int nsteps;   // K / KSTEP
+  int ldx;      // LDS row pitch of the staged X slice (elements)
+  float* part;  // [S][M][N] partials (S > 1)
   int nblocks;
 };
 
@@ -60,16 +62,77 @@ struct XStage {
     hi[m * ldx + k] = h;
     if constexpr (sizeof(WT) == 2) lo[m * ldx + k] = from_f<WT>(v - to_f<WT>(h));
   }
+  // four consecutive k (k % 4 == 0)
+  __device__ __forceinline__ void put4(int m, int k, const float (&v)[4]) const {
+    if constexpr (sizeof(WT) == 2) {
+      bf16 h[4], l[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        h[e] = f2bf(v[e]);
+        l[e] = f2bf(v[e] - bf2f(h[e]));
+      }
+      *reinterpret_cast<uint2*>(hi + m * ldx + k) =
+          make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+      *reinterpret_cast<uint2*>(lo + m * ldx + k) =
+          make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
+    } else {
+      *reinterpret_cast<float4*>(hi + m * ldx + k) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+  }
+};
+
+// four consecutive elements (16-byte aligned for float, 8-byte for bf16)
+__device__ __forceinline__ void load4(const float* p, float (&v)[4]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+}
+__device__ __forceinline__ void load4(const bf16* p, float (&v)[4]) {
+  const uint2 a = *reinterpret_cast<const uint2*>(p);
+  v[0] = bf2f((bf16)(a.x & 0xffff)); v[1] = bf2f((bf16)(a.x >> 16));
+  v[2] = bf2f((bf16)(a.y & 0xffff)); v[3] = bf2f((bf16)(a.y >> 16));
+}
+
+// Sum of n values f(i), i < n, by one wave: lane-strided, then a butterfly (fixed order).
+template <typename F>
+__device__ __forceinline__ float wave_sum_of(int n, const F& f) {
+  const int lane = threadIdx.x & 63;
+  float t = 0.f;
+  for (int i = lane; i < n; i += WAVE) t += f(i);
+  return wave_sum(t);
+}
+
+template <int TC>
+struct TileY {
+  const float (*y)[TC + 1];
+  __device__ __forceinline__ float operator()(int m, int c) const { return y[m][c]; }
+};
+
+template <int NT, typename RowMap>
+struct PartY {
+  const float* part;
+  int M, N, S, m0, nb;
+  RowMap rm;
+  __device__ __forceinline__ float operator()(int m, int c) const {
+    const int row = rm.template row<NT>(nb, c);
+    const float* p = part + (size_t)(m0 + m) * N + row;
+    const size_t stride = (size_t)M * N;
+    float v = 0.f;
+#pragma unroll 8
+    for (int q = 0; q < S; ++q) v += p[q * stride];
+    return v;
+  }
 };
 
 template <typename WT, int MT, int NT, typename In, typename Epi, typename RowMap>
 __global__ __launch_bounds__(GEMM_THREADS) void gemm_skinny_kernel(GemmShape g, In in, Epi epi,
                                                                    RowMap rmap) {
   typedef Mfma<WT> F;
+  typedef typename F::frag frag;
+  constexpr int TR = 16 * MT;  // rows per M-tile
+  constexpr int TC = 64 * NT;  // columns per N-block
+  constexpr bool SPLIT = sizeof(WT) == 2;
+  constexpr int U = GEMM_UNROLL;
   extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int TR = 16 * MT;        // rows per M-tile
-  constexpr int TC = 64 * NT;        // columns per N-block
-  __shared__ float ytile[TR][TC + 1];  // S == 1 result tile
 
   const int S = g.S;
   const int nb = blockIdx.x / S;
@@ -81,23 +144,11 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_skinny_kernel(GemmShape g, 
   const int st1 = (int)((long long)(s + 1) * g.nsteps / S);
   const int k0 = st0 * F::KSTEP;
   const int kw = (st1 - st0) * F::KSTEP;
-
-  constexpr bool SPLIT = sizeof(WT) == 2;
-  WT* xs = reinterpret_cast<WT*>(smem);
-  WT* xs_lo = xs + (size_t)min(TR, g.M) * g.ldx;
-  in.stage(XStage<WT>{xs, xs_lo, g.ldx}, m0, Mt, k0, kw, nb, s, S);
-  __syncthreads();
-
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int lr = lane & 15;
   const int lg = lane >> 4;
-
-  f32x4 acc[MT][NT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t)
-#pragma unroll
-    for (int u = 0; u < NT; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nst = st1 - st0;
 
   // this wave's weight rows: local columns wave*16*NT + 16*u + lr
   const WT* wp[NT];
@@ -108,53 +159,64 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_skinny_kernel(GemmShape g, 
     wv[u] = row < g.N;
     wp[u] = reinterpret_cast<const WT*>(g.W) + (size_t)(wv[u] ? row : 0) * g.K + k0 + lg * F::KPL;
   }
+  // the first group of weight loads goes out before the X slice is staged
+  frag cur[U][NT], nxt[U][NT];
+#pragma unroll
+  for (int i = 0; i < U; ++i)
+#pragma unroll
+    for (int u = 0; u < NT; ++u) cur[i][u] = i < nst ? F::load(wp[u] + i * F::KSTEP) : F::zero();
+
+  WT* xs = reinterpret_cast<WT*>(smem);
+  WT* xs_lo = xs + (size_t)min(TR, g.M) * g.ldx;
+  in.stage(XStage<WT>{xs, xs_lo, g.ldx}, m0, Mt, k0, kw, nb, s, S);
+  __syncthreads();
+
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int u = 0; u < NT; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
   const WT* xp[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) xp[t] = xs + min(16 * t + lr, Mt - 1) * g.ldx + lg * F::KPL;
   const ptrdiff_t lo_off = xs_lo - xs;
 
-  const int nst = st1 - st0;
-  int st = 0;
-  for (; st + GEMM_UNROLL <= nst; st += GEMM_UNROLL) {
-    typename F::frag wf[GEMM_UNROLL][NT];
+  for (int st = 0; st < nst; st += U) {
+    const int nxt0 = st + U;
+    if (nxt0 < nst) {
 #pragma unroll
-    for (int i = 0; i < GEMM_UNROLL; ++i)
+      for (int i = 0; i < U; ++i)
 #pragma unroll
-      for (int u = 0; u < NT; ++u) wf[i][u] = F::load(wp[u] + (st + i) * F::KSTEP);
+        for (int u = 0; u < NT; ++u)
+          nxt[i][u] = nxt0 + i < nst ? F::load(wp[u] + (nxt0 + i) * F::KSTEP) : F::zero();
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < GEMM_UNROLL; ++i) {
+    for (int i = 0; i < U; ++i) {
+      if (st + i < nst) {
 #pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        typename F::frag af = F::load(xp[t] + (st + i) * F::KSTEP);
+        for (int t = 0; t < MT; ++t) {
+          const frag af = F::load(xp[t] + (st + i) * F::KSTEP);
 #pragma unroll
-        for (int u = 0; u < NT; ++u) acc[t][u] = F::mma(af, wf[i][u], acc[t][u]);
-        if constexpr (SPLIT) {
-          typename F::frag al = F::load(xp[t] + lo_off + (st + i) * F::KSTEP);
+          for (int u = 0; u < NT; ++u) acc[t][u] = F::mma(af, cur[i][u], acc[t][u]);
+          if constexpr (SPLIT) {
+            const frag al = F::load(xp[t] + lo_off + (st + i) * F::KSTEP);
 #pragma unroll
-          for (int u = 0; u < NT; ++u) acc[t][u] = F::mma(al, wf[i][u], acc[t][u]);
+            for (int u = 0; u < NT; ++u) acc[t][u] = F::mma(al, cur[i][u], acc[t][u]);
+          }
         }
       }
     }
-  }
-  for (; st < nst; ++st) {
-    typename F::frag wf[NT];
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int u = 0; u < NT; ++u) wf[u] = F::load(wp[u] + st * F::KSTEP);
+    for (int i = 0; i < U; ++i)
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      typename F::frag af = F::load(xp[t] + st * F::KSTEP);
-#pragma unroll
-      for (int u = 0; u < NT; ++u) acc[t][u] = F::mma(af, wf[u], acc[t][u]);
-      if constexpr (SPLIT) {
-        typename F::frag al = F::load(xp[t] + lo_off + st * F::KSTEP);
-#pragma unroll
-        for (int u = 0; u < NT; ++u) acc[t][u] = F::mma(al, wf[u], acc[t][u]);
-      }
-    }
+      for (int u = 0; u < NT; ++u) cur[i][u] = nxt[i][u];
   }
 
-  // write the tile: lane holds D[16t + 4*lg + i][16u + lr] of this wave
+  // lane holds D[16t + 4*lg + i][16u + lr] of this wave
   if (S == 1) {
+    __shared__ float ytile[TR][TC + 1];
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
@@ -162,51 +224,49 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_skinny_kernel(GemmShape g, 
 #pragma unroll
         for (int i = 0; i < 4; ++i) ytile[16 * t + 4 * lg + i][wave * 16 * NT + 16 * u + lr] = acc[t][u][i];
     __syncthreads();
-    struct { const float (*y)[TC + 1]; __device__ float operator()(int m, int c) const { return y[m][c]; } } fy{ytile};
-    epi.template run<NT>(fy, nb, m0, Mt, rmap);
+    epi.template run<NT>(TileY<TC>{ytile}, nb, m0, Mt, rmap);
     return;
   }
 #pragma unroll
   for (int t = 0; t < MT; ++t)
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
-      const int row = rmap.template row<NT>(nb, wave * 16 * NT + 16 * u + lr);
       if (!wv[u]) continue;
+      const int row = rmap.template row<NT>(nb, wave * 16 * NT + 16 * u + lr);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = 16 * t + 4 * lg + i;
         if (m < Mt) g.part[((size_t)s * g.M + m0 + m) * g.N + row] = acc[t][u][i];
       }
     }
-  unsigned* ctr = g.counters + mt * g.nblocks + nb;
-  if (!arrive_last(ctr, (unsigned)S)) return;
-  struct {
-    const float* part; int M, N, S, m0, nb; RowMap rm;
-    __device__ float operator()(int m, int c) const {
-      const int row = rm.template row<NT>(nb, c);
-      float v = 0.f;
-      for (int q = 0; q < S; ++q) v += part[((size_t)q * M + m0 + m) * N + row];
-      return v;
-    }
-  } fp{g.part, g.M, g.N, S, m0, nb, rmap};
-  epi.template run<NT>(fp, nb, m0, Mt, rmap);
-  arrival_reset(ctr);
+}
+
+// Sum of the S partial tiles of one (N-block, M-tile), then the epilogue.
+template <int MT, int NT, typename Epi, typename RowMap>
+__global__ __launch_bounds__(GEMM_THREADS) void gemm_finish_kernel(GemmShape g, Epi epi, RowMap rmap) {
+  const int nb = blockIdx.x, mt = blockIdx.y;
+  const int m0 = mt * 16 * MT;
+  const int Mt = min(16 * MT, g.M - m0);
+  epi.template run<NT>(PartY<NT, RowMap>{g.part, g.M, g.N, g.S, m0, nb, rmap}, nb, m0, Mt, rmap);
 }
 
 // ---------------------------------------------------------------------------
-// Input functors: stage X[m0 .. m0+Mt)[k0 .. k0+kw) into LDS as WT.
+// Input functors: stage X[m0 .. m0+Mt)[k0 .. k0+kw) into LDS.
 // ---------------------------------------------------------------------------
 
-// X given (float or bf16 activations) -> WT
+// X given (float or bf16 activations)
 template <typename WT, typename XT>
 struct InAct {
   const XT* X;
   int K;
   __device__ void stage(const XStage<WT>& xs, int m0, int Mt, int k0, int kw, int, int, int) const {
-    const int tot = Mt * kw;
-    for (int e = threadIdx.x; e < tot; e += GEMM_THREADS) {
-      const int m = e / kw, k = e - m * kw;
-      xs.put(m, k, to_f<XT>(X[(size_t)(m0 + m) * K + k0 + k]));
+    const int kv = kw >> 2;
+#pragma unroll 4
+    for (int e = threadIdx.x; e < Mt * kv; e += GEMM_THREADS) {
+      const int m = e / kv, k = (e - m * kv) << 2;
+      float v[4];
+      load4(X + (size_t)(m0 + m) * K + k0 + k, v);
+      xs.put4(m, k, v);
     }
   }
 };
@@ -218,56 +278,53 @@ struct InNorm {
   const float* H;
   const WT* gamma;
   const float* ss;
-  int P;     // partial count
-  int M;     // rows of H (ss row stride)
+  int P;  // partial count
+  int M;  // rows of H (ss row stride)
   int K;
   float eps;
   __device__ void stage(const XStage<WT>& xs, int m0, int Mt, int k0, int kw, int, int, int) const {
     __shared__ float inv[32];
-    if (threadIdx.x < Mt) {
-      float t = 0.f;
-      for (int p = 0; p < P; ++p) t += ss[(size_t)p * M + m0 + threadIdx.x];
-      inv[threadIdx.x] = 1.0f / sqrtf(t / (float)K + eps);
+    const int wave = threadIdx.x >> 6;
+    for (int m = wave; m < Mt; m += GEMM_WAVES) {
+      const float* sp = ss + m0 + m;
+      const float t = wave_sum_of(P, [&](int p) { return sp[(size_t)p * M]; });
+      if ((threadIdx.x & 63) == 0) inv[m] = 1.0f / sqrtf(t / (float)K + eps);
     }
     __syncthreads();
-    const int tot = Mt * kw;
-    for (int e = threadIdx.x; e < tot; e += GEMM_THREADS) {
-      const int m = e / kw, k = e - m * kw;
-      const float v = H[(size_t)(m0 + m) * K + k0 + k] * inv[m] * to_f<WT>(gamma[k0 + k]);
-      xs.put(m, k, v);
+    const int kv = kw >> 2;
+#pragma unroll 4
+    for (int e = threadIdx.x; e < Mt * kv; e += GEMM_THREADS) {
+      const int m = e / kv, k = (e - m * kv) << 2;
+      float v[4], gm[4];
+      load4(H + (size_t)(m0 + m) * K + k0 + k, v);
+      load4(gamma + k0 + k, gm);
+      const float iv = inv[m];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = v[i] * iv * gm[i];
+      xs.put4(m, k, v);
     }
   }
 };
 
 // ---------------------------------------------------------------------------
-// Epilogue helpers
+// Epilogues
 // ---------------------------------------------------------------------------
 
 // h[row][col] += y; ss_out[nb][row] = sum over the block's columns of h^2.
-// With `final`, the last block of the M-tile holding row M-1 writes
-// h_last = RMSNorm(h[M-1]) * final_norm.
-template <typename WT>
 struct EpiResid {
   float* h;
   float* ss_out;
-  int N;   // = d
+  int N;  // = d
   int M;
-  int final_;
-  const WT* final_norm;
-  float* h_last;
-  unsigned* ctr2;
-  int nblocks;
-  float eps;
   template <int NT, typename Y, typename RM>
   __device__ void run(const Y& y, int nb, int m0, int Mt, const RM&) const {
-    constexpr int TC = 64 * NT;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     for (int m = wave; m < Mt; m += GEMM_WAVES) {
       float sq = 0.f;
 #pragma unroll
       for (int u = 0; u < NT; ++u) {
         const int c = lane + 64 * u;
-        const int col = nb * TC + c;
+        const int col = nb * 64 * NT + c;
         if (col < N) {
           float* hp = h + (size_t)(m0 + m) * N + col;
           const float v = *hp + y(m, c);
@@ -278,25 +335,12 @@ struct EpiResid {
       sq = wave_sum(sq);
       if (lane == 0) ss_out[(size_t)nb * M + m0 + m] = sq;
     }
-    if (!final_ || m0 + Mt != M) return;
-    if (!arrive_last(ctr2, (unsigned)nblocks)) return;
-    __shared__ float s_inv;
-    if (threadIdx.x == 0) {
-      float t = 0.f;
-      for (int p = 0; p < nblocks; ++p) t += ss_out[(size_t)p * M + M - 1];
-      s_inv = 1.0f / sqrtf(t / (float)N + eps);
-    }
-    __syncthreads();
-    for (int c = threadIdx.x; c < N; c += GEMM_THREADS)
-      h_last[c] = h[(size_t)(M - 1) * N + c] * s_inv * to_f<WT>(final_norm[c]);
-    arrival_reset(ctr2);
   }
 };
 
 // act[row][j] = silu(gate_j) * up_j
-template <typename AT>
 struct EpiSilu {
-  AT* act;
+  float* act;
   int dff;
   template <int NT, typename Y, typename RM>
   __device__ void run(const Y& y, int nb, int m0, int Mt, const RM&) const {
@@ -306,23 +350,7 @@ struct EpiSilu {
       const int j = nb * H + c;
       if (j >= dff) continue;
       const float gt = y(m, c), up = y(m, c + H);
-      const float v = gt / (1.0f + expf(-gt)) * up;
-      act[(size_t)(m0 + m) * dff + j] = from_f<AT>(v);
-    }
-  }
-};
-
-// plain store of y (float)
-struct EpiStore {
-  float* Y;
-  int N;
-  template <int NT, typename Yf, typename RM>
-  __device__ void run(const Yf& y, int nb, int m0, int Mt, const RM&) const {
-    constexpr int TC = 64 * NT;
-    for (int e = threadIdx.x; e < Mt * TC; e += GEMM_THREADS) {
-      const int m = e / TC, c = e - m * TC;
-      const int col = nb * TC + c;
-      if (col < N) Y[(size_t)(m0 + m) * N + col] = y(m, c);
+      act[(size_t)(m0 + m) * dff + j] = gt / (1.0f + expf(-gt)) * up;
     }
   }
 };
@@ -338,7 +366,7 @@ struct GemmPlan {
 // Choose split-K so that the grid has about `target` blocks, each with at least
 // `min_steps` k-steps, and the staged slice fits `lds_cap` bytes.
 inline GemmPlan plan_gemm(int N, int K, int M, int kstep, int esize, int NT, int target = 1024,
-                          int min_steps = 4, size_t lds_cap = 40 * 1024) {
+                          int min_steps = 8, size_t lds_cap = 40 * 1024) {
   GemmPlan p;
   p.MT = M > 16 ? 2 : 1;
   p.NT = NT;

@@ -5,13 +5,15 @@
 // accept if r <= min(1, p/q), else resample from norm(max(0, p - q)); bonus token
 // from p_{gamma+1} when every draft is accepted.)
 //
-// Grid: (vocabulary chunks, sequences).  Every block first decides the sequence's
-// outcome from the 2*gamma scalars p_j(x_j), q_j(x_j) (cheap, exact), so a fully
-// accepted sequence without bonus costs no row traffic.  Otherwise each block sums
-// the exact integer weights of its chunk of the row to sample from (residual and
-// target weights both, for the empty-residual fallback); the last block of the
-// sequence scans the chunk sums and locates the sample.  Greedy verify reduces
-// (max, first argmax) per chunk for every row instead.
+// T > 0, launch 1, grid (vocabulary chunks, sequences): every block decides the
+//   sequence's outcome from the 2*gamma scalars p_j(x_j), q_j(x_j) (cheap, exact),
+//   so a fully accepted sequence without bonus reads no rows; otherwise it sums
+//   the exact integer weights of its chunk of the row to sample from (residual
+//   and target weights both, for the empty-residual fallback).
+//   Launch 2, one block per sequence: the same decision, the chunk scan and the
+//   search inside the chosen chunk.
+// T == 0, launch 1: per chunk (max, first argmax) of every row; launch 2: merge
+//   per row and compare with the drafts.
 #include <algorithm>
 
 #include "spd_common.h"
@@ -21,7 +23,7 @@ namespace spd {
 
 constexpr int VER_CHUNK = 2048;
 constexpr int VER_THREADS = 256;
-constexpr int VER_MAX_ROWS = 64;  // gamma + bonus limit of the greedy form
+constexpr int VER_MAX_ROWS = 64;  // gamma + bonus limit
 
 struct VerArgs {
   const float* p;
@@ -30,7 +32,6 @@ struct VerArgs {
   const uint64_t* words;
   int32_t* n_accept;
   int32_t* next_token;
-  unsigned* counters;
   void* part;
   int B, gamma, V, bonus, nchunks;
 };
@@ -44,7 +45,9 @@ __device__ uint64_t vblock_scan(uint64_t v, uint64_t* sh) {
     sh[threadIdx.x] += add;
     __syncthreads();
   }
-  return sh[threadIdx.x];
+  const uint64_t r = sh[threadIdx.x];
+  __syncthreads();
+  return r;
 }
 
 __device__ __forceinline__ uint64_t res_weight(float p, float q) {
@@ -52,43 +55,38 @@ __device__ __forceinline__ uint64_t res_weight(float p, float q) {
   return P > Q ? P - Q : 0ull;
 }
 
-// T > 0
-__global__ __launch_bounds__(VER_THREADS) void verify_sample_kernel(VerArgs a) {
-  __shared__ uint64_t sh[VER_THREADS];
+// first rejected position of sequence b (gamma if all accepted); one thread
+__device__ int first_reject(const VerArgs& a, int b) {
+  const int rowsP = a.gamma + a.bonus;
+  int j = 0;
+  for (; j < a.gamma; ++j) {
+    const int x = a.draft[b * a.gamma + j];
+    bool acc = false;
+    if (x >= 0 && x < a.V) {
+      const double px = (double)a.p[((size_t)b * rowsP + j) * a.V + x];
+      const double qx = (double)a.q[((size_t)b * a.gamma + j) * a.V + x];
+      const uint64_t R = a.words[((size_t)b * (a.gamma + 1) + j) * 2] >> 40;
+      acc = (double)(R + 1) * qx <= px * 16777216.0;
+    }
+    if (!acc) break;
+  }
+  return j;
+}
+
+__global__ __launch_bounds__(VER_THREADS) void verify_sums_kernel(VerArgs a) {
   __shared__ int s_j;
   const int c = blockIdx.x, b = blockIdx.y;
-  const int rowsP = a.gamma + a.bonus;
-  if (threadIdx.x == 0) {
-    int j = 0;
-    for (; j < a.gamma; ++j) {
-      const int x = a.draft[b * a.gamma + j];
-      bool acc = false;
-      if (x >= 0 && x < a.V) {
-        const double px = (double)a.p[((size_t)b * rowsP + j) * a.V + x];
-        const double qx = (double)a.q[((size_t)b * a.gamma + j) * a.V + x];
-        const uint64_t R = a.words[((size_t)b * (a.gamma + 1) + j) * 2] >> 40;
-        acc = (double)(R + 1) * qx <= px * 16777216.0;
-      }
-      if (!acc) break;
-    }
-    s_j = j;
-  }
+  if (threadIdx.x == 0) s_j = first_reject(a, b);
   __syncthreads();
   const int j = s_j;
   const bool rejected = j < a.gamma;
-  if (!rejected && !a.bonus) {
-    if (c == 0 && threadIdx.x == 0) {
-      a.n_accept[b] = a.gamma;
-      a.next_token[b] = -1;
-    }
-    return;
-  }
+  if (!rejected && !a.bonus) return;
+  const int rowsP = a.gamma + a.bonus;
   const float* prow = a.p + ((size_t)b * rowsP + j) * a.V;
   const float* qrow = rejected ? a.q + ((size_t)b * a.gamma + j) * a.V : nullptr;
   uint64_t sres = 0, sp = 0;
-  const int base = c * VER_CHUNK;
-  const int end = min(base + VER_CHUNK, a.V);
-  for (int i = base + threadIdx.x; i < end; i += VER_THREADS) {
+  const int end = min((c + 1) * VER_CHUNK, a.V);
+  for (int i = c * VER_CHUNK + threadIdx.x; i < end; i += VER_THREADS) {
     const float pv = prow[i];
     sp += prob_weight(pv);
     if (rejected) sres += res_weight(pv, qrow[i]);
@@ -101,25 +99,44 @@ __global__ __launch_bounds__(VER_THREADS) void verify_sample_kernel(VerArgs a) {
     s_w[1][threadIdx.x >> 6] = sp;
   }
   __syncthreads();
-  uint64_t* part = static_cast<uint64_t*>(a.part) + ((size_t)b * a.nchunks + c) * 2;
   if (threadIdx.x == 0) {
     uint64_t t0 = 0, t1 = 0;
     for (int w = 0; w < VER_THREADS / 64; ++w) {
       t0 += s_w[0][w];
       t1 += s_w[1][w];
     }
+    uint64_t* part = static_cast<uint64_t*>(a.part) + ((size_t)b * a.nchunks + c) * 2;
     part[0] = t0;
     part[1] = t1;
   }
-  unsigned* ctr = a.counters + b;
-  if (!arrive_last(ctr, (unsigned)a.nchunks)) return;
+}
 
+__global__ __launch_bounds__(VER_THREADS) void verify_locate_kernel(VerArgs a) {
+  __shared__ uint64_t sh[VER_THREADS];
+  __shared__ int s_j;
+  __shared__ uint64_t s_tau, s_off;
+  __shared__ int s_chunk, s_found;
+  __shared__ uint64_t s_t[VER_THREADS / 64];
+  const int b = blockIdx.x;
+  if (threadIdx.x == 0) s_j = first_reject(a, b);
+  __syncthreads();
+  const int j = s_j;
+  const bool rejected = j < a.gamma;
+  if (!rejected && !a.bonus) {
+    if (threadIdx.x == 0) {
+      a.n_accept[b] = a.gamma;
+      a.next_token[b] = -1;
+    }
+    return;
+  }
+  const int rowsP = a.gamma + a.bonus;
+  const float* prow = a.p + ((size_t)b * rowsP + j) * a.V;
+  const float* qrow = rejected ? a.q + ((size_t)b * a.gamma + j) * a.V : nullptr;
   const uint64_t* pb = static_cast<const uint64_t*>(a.part) + (size_t)b * a.nchunks * 2;
-  // which weights: residual if it has mass, else the target row itself
+  // residual if it has mass, else the target row itself
   uint64_t tr = 0;
   for (int k = threadIdx.x; k < a.nchunks; k += VER_THREADS) tr += pb[2 * k];
   tr = wave_sum_u64(tr);
-  __shared__ uint64_t s_t[VER_THREADS / 64];
   if ((threadIdx.x & 63) == 0) s_t[threadIdx.x >> 6] = tr;
   __syncthreads();
   uint64_t total_res = 0;
@@ -134,11 +151,10 @@ __global__ __launch_bounds__(VER_THREADS) void verify_sample_kernel(VerArgs a) {
     if (k < a.nchunks) mine += pb[2 * k + which];
   }
   const uint64_t incl = vblock_scan(mine, sh);
-  __shared__ uint64_t s_tau, s_off;
-  __shared__ int s_chunk;
   if (threadIdx.x == VER_THREADS - 1) {
     s_tau = scale_u32((uint32_t)U, incl);
     s_chunk = -1;
+    s_found = -1;
   }
   __syncthreads();
   const uint64_t tau = s_tau;
@@ -157,7 +173,6 @@ __global__ __launch_bounds__(VER_THREADS) void verify_sample_kernel(VerArgs a) {
     }
   }
   __syncthreads();
-  int tok = -1;
   if (s_chunk >= 0) {
     constexpr int PER = VER_CHUNK / VER_THREADS;
     const int b0 = s_chunk * VER_CHUNK;
@@ -171,8 +186,6 @@ __global__ __launch_bounds__(VER_THREADS) void verify_sample_kernel(VerArgs a) {
       w[e] = v;
       tot += v;
     }
-    __shared__ int s_found;
-    if (threadIdx.x == 0) s_found = -1;
     const uint64_t in2 = vblock_scan(tot, sh);
     uint64_t r2 = s_off + in2 - tot;
     if (r2 <= tau && s_off + in2 > tau) {
@@ -186,27 +199,23 @@ __global__ __launch_bounds__(VER_THREADS) void verify_sample_kernel(VerArgs a) {
       }
     }
     __syncthreads();
-    tok = s_found;
   }
   if (threadIdx.x == 0) {
     a.n_accept[b] = j;
-    a.next_token[b] = tok < 0 ? 0 : tok;
+    a.next_token[b] = s_found < 0 ? 0 : s_found;
   }
-  arrival_reset(ctr);
 }
 
-// T == 0: p holds logits; per chunk (max, first argmax) of every row.
-__global__ __launch_bounds__(VER_THREADS) void verify_greedy_kernel(VerArgs a) {
+__global__ __launch_bounds__(VER_THREADS) void verify_greedy_chunks_kernel(VerArgs a) {
   const int c = blockIdx.x, b = blockIdx.y;
   const int rows = a.gamma + a.bonus;
-  const int base = c * VER_CHUNK;
-  const int end = min(base + VER_CHUNK, a.V);
+  const int end = min((c + 1) * VER_CHUNK, a.V);
   ArgMax* part = static_cast<ArgMax*>(a.part);
   __shared__ ArgMax s_am[VER_THREADS / 64];
   for (int j = 0; j < rows; ++j) {
     const float* prow = a.p + ((size_t)b * rows + j) * a.V;
     ArgMax am{-INFINITY, ARG_NONE};
-    for (int i = base + threadIdx.x; i < end; i += VER_THREADS) am = argmax_merge(am, ArgMax{prow[i], i});
+    for (int i = c * VER_CHUNK + threadIdx.x; i < end; i += VER_THREADS) am = argmax_merge(am, ArgMax{prow[i], i});
     am = wave_argmax(am);
     if ((threadIdx.x & 63) == 0) s_am[threadIdx.x >> 6] = am;
     __syncthreads();
@@ -217,8 +226,13 @@ __global__ __launch_bounds__(VER_THREADS) void verify_greedy_kernel(VerArgs a) {
     }
     __syncthreads();
   }
-  unsigned* ctr = a.counters + b;
-  if (!arrive_last(ctr, (unsigned)a.nchunks)) return;
+}
+
+__global__ __launch_bounds__(VER_THREADS) void verify_greedy_final_kernel(VerArgs a) {
+  const int b = blockIdx.x;
+  const int rows = a.gamma + a.bonus;
+  const ArgMax* part = static_cast<const ArgMax*>(a.part);
+  __shared__ ArgMax s_am[VER_THREADS / 64];
   __shared__ int s_best[VER_MAX_ROWS];
   for (int j = 0; j < rows; ++j) {
     const ArgMax* pj = part + ((size_t)b * rows + j) * a.nchunks;
@@ -240,13 +254,12 @@ __global__ __launch_bounds__(VER_THREADS) void verify_greedy_kernel(VerArgs a) {
     a.n_accept[b] = j;
     a.next_token[b] = j < a.gamma ? s_best[j] : (a.bonus ? s_best[a.gamma] : -1);
   }
-  arrival_reset(ctr);
 }
 
 size_t verify_workspace(int B, int gamma, int V) {
   const size_t nch = (size_t)(V + VER_CHUNK - 1) / VER_CHUNK;
   const size_t per = std::max((size_t)16, (size_t)(gamma + 1) * sizeof(ArgMax));
-  return align256(SPD_WS_COUNTER_BYTES + (size_t)B * nch * per);
+  return align256((size_t)B * nch * per);
 }
 
 }  // namespace spd
@@ -257,9 +270,8 @@ extern "C" int spd_verify(int32_t B, int32_t gamma, int32_t V, float temperature
                           const float* p, const float* q, const int32_t* draft,
                           const uint64_t* words, int32_t* n_accept, int32_t* next_token, void* ws,
                           size_t ws_bytes, void* stream) {
-  if (B < 1 || gamma < 0 || V < 1 || (bonus != 0 && bonus != 1)) return SPD_E_INVALID;
+  if (B < 1 || B > 65535 || gamma < 0 || V < 1 || (bonus != 0 && bonus != 1)) return SPD_E_INVALID;
   if (gamma + bonus < 1 || gamma + bonus > VER_MAX_ROWS) return SPD_E_INVALID;
-  if (B >= SPD_WS_COUNTER_BYTES / 4 - 1 || B > 65535) return SPD_E_UNSUPPORTED;
   if (!(temperature >= 0.f)) return SPD_E_INVALID;
   if (!p || !n_accept || !next_token || !ws || (gamma > 0 && !draft)) return SPD_E_INVALID;
   if (temperature > 0.f && (!words || (gamma > 0 && !q))) return SPD_E_INVALID;
@@ -272,17 +284,23 @@ extern "C" int spd_verify(int32_t B, int32_t gamma, int32_t V, float temperature
   a.words = words;
   a.n_accept = n_accept;
   a.next_token = next_token;
-  a.counters = static_cast<unsigned*>(ws);
-  a.part = static_cast<char*>(ws) + SPD_WS_COUNTER_BYTES;
+  a.part = ws;
   a.B = B;
   a.gamma = gamma;
   a.V = V;
   a.bonus = bonus;
   a.nchunks = (V + VER_CHUNK - 1) / VER_CHUNK;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (temperature > 0.f)
-    hipLaunchKernelGGL(verify_sample_kernel, dim3(a.nchunks, B), dim3(VER_THREADS), 0, st, a);
-  else
-    hipLaunchKernelGGL(verify_greedy_kernel, dim3(a.nchunks, B), dim3(VER_THREADS), 0, st, a);
+  if (temperature > 0.f) {
+    hipLaunchKernelGGL(verify_sums_kernel, dim3(a.nchunks, B), dim3(VER_THREADS), 0, st, a);
+    int rc = check_launch();
+    if (rc) return rc;
+    hipLaunchKernelGGL(verify_locate_kernel, dim3(B), dim3(VER_THREADS), 0, st, a);
+  } else {
+    hipLaunchKernelGGL(verify_greedy_chunks_kernel, dim3(a.nchunks, B), dim3(VER_THREADS), 0, st, a);
+    int rc = check_launch();
+    if (rc) return rc;
+    hipLaunchKernelGGL(verify_greedy_final_kernel, dim3(B), dim3(VER_THREADS), 0, st, a);
+  }
   return check_launch();
 }

@@ -79,6 +79,14 @@ class SpdCycle:
                  spd_workspace_size(SPD_CALL_LM_HEAD, c, 1),
                  spd_workspace_size(SPD_CALL_VERIFY, c, 1, 1))
         self.ws = torch.zeros(ws, dtype=torch.uint8, device=device)
+        # the target head and verify do not depend on this cycle's draft path: they
+        # run on a second stream (default priority) with a workspace of their own
+        self.ws_side = torch.zeros(max(spd_workspace_size(SPD_CALL_LM_HEAD, c, 1),
+                                       spd_workspace_size(SPD_CALL_VERIFY, c, 1, 1)),
+                                   dtype=torch.uint8, device=device)
+        self.side = torch.cuda.Stream(device=device)
+        self.ev_fork = torch.cuda.Event()
+        self.ev_join = torch.cuda.Event()
 
     # ---------------------------------------------------------------- pieces
     def features(self, pos0, M, a, out=None):
@@ -109,22 +117,23 @@ class SpdCycle:
         spd_lm_head(m.cfg, m.w.w_dlm, self.h_last, 1, self.T, w, self.dlogits, probs, self.dtoken,
                     self.ws)
 
-    def target_and_verify(self, t, words_block, q_row=None, x_ptr=None):
+    def target_and_verify(self, t, words_block, q_row=None, x_ptr=None, ws=None):
         """Target head on the exiting token's state and streaming verify of its successor."""
         m = self.m
+        ws = self.ws if ws is None else ws
         n, V = m.cfg.n, m.cfg.V
         exiting = t - n
         h = m.w.h_final[exiting]
         probs = self.p if self.T > 0 else None
         w = None if words_block is None else words_block.data_ptr() + 2 * 8
-        spd_lm_head(m.cfg, m.w.w_tlm, h, 1, self.T, w, self.tlogits, probs, self.ttoken, self.ws)
+        spd_lm_head(m.cfg, m.w.w_tlm, h, 1, self.T, w, self.tlogits, probs, self.ttoken, ws)
         cand = exiting + 1
         q = q_row if q_row is not None else self.ring[cand % n]
         draft = x_ptr if x_ptr is not None else self.tokens.data_ptr() + 4 * cand
         spd_verify(1, 1, V, self.T, 0, self.p if self.T > 0 else self.tlogits,
                    q if self.T > 0 else None, draft,
                    None if words_block is None else words_block, self.n_accept, self.next_token,
-                   self.ws)
+                   ws)
 
     def rollback(self):
         m = self.m
@@ -133,14 +142,23 @@ class SpdCycle:
 
     # ---------------------------------------------------------------- a cycle
     def cycle(self, t, a, words_block, q_row=None, x_ptr=None):
-        """One cycle at sequence length t with a tokens in flight."""
+        """One cycle at sequence length t with a tokens in flight.  In a saturated
+        cycle the target head + verify run on the side stream, concurrently with
+        the features -> PDM -> draft chain; rollback waits for both."""
         n = self.m.cfg.n
         pos0, M = t - 1 - a, a + 1
+        main = torch.cuda.current_stream()
+        if a == n:
+            self.ev_fork.record(main)
+            self.side.wait_event(self.ev_fork)
+            with torch.cuda.stream(self.side):
+                self.target_and_verify(t, words_block, q_row, x_ptr, ws=self.ws_side)
+            self.ev_join.record(self.side)
         self.features(pos0, M, a)
         self.pdm(pos0, M)
         self.draft(t, words_block)
         if a == n:
-            self.target_and_verify(t, words_block, q_row, x_ptr)
+            main.wait_event(self.ev_join)
         self.rollback()
 
     def set_state(self, t, a, tokens=None):
