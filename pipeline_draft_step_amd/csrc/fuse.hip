@@ -79,7 +79,7 @@ struct EpiFeature {
   float eps;
   RowDepth depth;
   SlotTable tab;
-  template <int NT, typename Y, typename RM>
+  template <int MT, int NT, typename Y, typename RM>
   __device__ void run(const Y& y, int nb, int m0, int Mt, const RM&) const {
     constexpr int TC = 64 * NT;
     __shared__ float inv[32];

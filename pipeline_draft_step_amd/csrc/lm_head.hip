@@ -150,7 +150,7 @@ struct EpiLogits {
   BlockStat* stat;  // [nblocks][rows]
   int V, rows;
   float inv_t;
-  template <int NT, typename Y, typename RM>
+  template <int MT, int NT, typename Y, typename RM>
   __device__ void run(const Y& y, int nb, int m0, int Mt, const RM&) const {
     constexpr int TC = 64 * NT;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -198,10 +198,21 @@ __global__ __launch_bounds__(SMX_THREADS) void softmax_chunk_kernel(const BlockS
   float* pr = probs + (size_t)r * V;
   const int base = c * SMX_CHUNK;
   uint64_t part = 0;
-  for (int j = base + threadIdx.x; j < min(base + SMX_CHUNK, V); j += SMX_THREADS) {
-    const float p = expf((lr[j] - s.mx) * inv_t) * inv_sum;
-    pr[j] = p;
-    part += prob_weight(p);
+  constexpr int PER = SMX_CHUNK / SMX_THREADS;
+  float lv[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int j = base + threadIdx.x + SMX_THREADS * e;
+    lv[e] = j < V ? lr[j] : -INFINITY;
+  }
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int j = base + threadIdx.x + SMX_THREADS * e;
+    if (j < V) {
+      const float p = expf((lv[e] - s.mx) * inv_t) * inv_sum;
+      pr[j] = p;
+      part += prob_weight(p);
+    }
   }
   part = wave_sum_u64(part);
   __shared__ uint64_t sh[SMX_THREADS / 64];

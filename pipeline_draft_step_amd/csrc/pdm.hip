@@ -5,8 +5,8 @@
 // Per layer (5 launches + attention combine):
 //   QKV GEMM  : X = RMSNorm(h)*attn_norm staged in LDS (bf16 hi+lo pairs); per head:
 //               q/k RMSNorm, rotate-half RoPE, k/v written to the cache, q kept.
-//   attention : MFMA flash-decode over 64-key chunks, one wave per
-//               (chunk, kv head, query group), GQA rows of a kv head together.
+//   attention : MFMA flash-decode, one block per (256-key chunk, kv head, 16-row
+//               query tile), GQA rows of a kv head together, waves merged in LDS.
 //   combine   : log-sum-exp merge of the chunk partials.
 //   O GEMM    : h += W_o attn                (epilogue keeps row sums of squares)
 //   gate/up   : X = RMSNorm(h)*mlp_norm; epilogue silu(gate)*up
@@ -23,8 +23,9 @@
 
 namespace spd {
 
-constexpr int ATT_KC = 64;   // keys per chunk
-constexpr int ATT_TPG = 1;   // 16-row query tiles per attention block (one wave each)
+constexpr int ATT_SUB = 64;                     // keys per wave
+constexpr int ATT_WAVES = 4;                    // waves per attention block
+constexpr int ATT_KC = ATT_SUB * ATT_WAVES;     // keys per block (one partial per row)
 
 // h_last = RMSNorm(h[M-1]) * final_norm, row statistics from P partial sums
 template <typename WT>
@@ -37,6 +38,7 @@ __global__ __launch_bounds__(256) void final_norm_kernel(const float* h, const f
     if (threadIdx.x == 0) s_inv = 1.0f / sqrtf(t / (float)d + eps);
   }
   __syncthreads();
+#pragma unroll 4
   for (int c = threadIdx.x; c < d; c += 256)
     h_last[c] = h[(size_t)(M - 1) * d + c] * s_inv * to_f<WT>(fnorm[c]);
 }
@@ -63,13 +65,15 @@ struct EpiQKV {
   int Hq, Hkv, hd, pos0;
   int64_t T_cap;
   float eps, theta;
-  template <int NT, typename Y, typename RM>
+  template <int MT, int NT, typename Y, typename RM>
   __device__ void run(const Y& y, int nb, int m0, int Mt, const RM&) const {
     constexpr int TC = 64 * NT;
     const int hpb = TC / hd;
     const int nheads = Hq + 2 * Hkv;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int half = hd >> 1;
+    // rotate-half frequency of this lane's element: theta^(-2i/hd), i = element mod hd/2
+    const double invf = pow((double)theta, -2.0 * (hd == 128 ? lane : (lane & (half - 1))) / hd);
     for (int it = wave; it < Mt * hpb; it += GEMM_WAVES) {
       const int mm = it / hpb, hl = it - mm * hpb;
       const int hh = nb * hpb + hl;
@@ -86,15 +90,14 @@ struct EpiQKV {
         // rotate-half: element i pairs with i + hd/2 at angle pos * theta^(-2i/hd)
         if (hd == 128) {
           double s, c;
-          sincos((double)pos * pow((double)theta, -2.0 * lane / hd), &s, &c);
+          sincos((double)pos * invf, &s, &c);
           const float x1 = v0, x2 = v1;
           v0 = x1 * (float)c - x2 * (float)s;
           v1 = x2 * (float)c + x1 * (float)s;
         } else {
           const float other = __shfl_xor(v0, half, WAVE);
-          const int i = lane & (half - 1);
           double s, c;
-          sincos((double)pos * pow((double)theta, -2.0 * i / hd), &s, &c);
+          sincos((double)pos * invf, &s, &c);
           v0 = lane < half ? v0 * (float)c - other * (float)s : v0 * (float)c + other * (float)s;
         }
       }
@@ -126,41 +129,43 @@ struct AttnArgs {
   float scale;
 };
 
-// One wave: keys [64c, 64c+64) of kv head h, query tiles of group z.
+// One block: kv head h (blockIdx.y), keys [256c, 256c+256) (blockIdx.x), one
+// 16-row tile of the head's GQA query rows (blockIdx.z).  Wave w owns 64 keys:
+// S = Q K^T and O = P V on MFMA (Q and P as bf16 hi + lo pairs), softmax over its
+// keys; the four waves are merged in LDS (log-sum-exp) into one partial per row.
 template <typename WT, int HD>
-__global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   typedef Mfma<WT> F;
-  constexpr int KS = ATT_KC / 16;
+  typedef typename F::frag frag;
+  constexpr int KS = ATT_SUB / 16;
   constexpr int DS = HD / F::KSTEP;
-  constexpr int KT = ATT_KC / F::KSTEP;
+  constexpr int KT = ATT_SUB / F::KSTEP;
   constexpr int DT = HD / 16;
   constexpr int KPL = F::KPL;
-  constexpr bool SPLIT = sizeof(WT) == 2;  // q and p as bf16 hi + lo pairs
-  __shared__ __align__(16) WT Ps[16][ATT_KC + 16];
-  __shared__ __align__(16) WT Pl[16][ATT_KC + 16];
+  constexpr bool SPLIT = sizeof(WT) == 2;
+  constexpr int NP = SPLIT ? 2 : 1;
+  __shared__ __align__(16) WT Ps[ATT_WAVES][NP][16][ATT_SUB + 16];
+  __shared__ float Ob[ATT_WAVES][16][HD + 4];
+  __shared__ float2 Ml[ATT_WAVES][16];
 
-  const int c = blockIdx.x, h = blockIdx.y, z = blockIdx.z;
-  const int lane = threadIdx.x, lr = lane & 15, lg = lane >> 4;
+  const int c = blockIdx.x, h = blockIdx.y, qt = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int G = a.Hq / a.Hkv, QR = a.M * G;
   const int nkeys = a.pos0 + a.M;
-  const int key0 = c * ATT_KC;
-  const int qt0 = z * ATT_TPG;
-  const int qt1 = min(qt0 + ATT_TPG, (QR + 15) / 16);
-  if (qt0 >= qt1) return;
-  const int r_last = (min(QR, qt1 * 16) - 1) / G;
-  if (key0 > a.pos0 + r_last) return;  // every row of the group is masked here
+  const int r_last = (min(QR, 16 * qt + 16) - 1) / G;
+  if (c * ATT_KC > a.pos0 + r_last) return;  // every row of the tile is masked here
+  const int key0 = c * ATT_KC + wave * ATT_SUB;
 
   const WT* K = static_cast<const WT*>(a.kc) + (size_t)h * a.T_cap * HD;
   const WT* Vt = static_cast<const WT*>(a.vc) + (size_t)h * HD * a.T_cap;
-
-  typename F::frag kf[KS][DS];
+  frag kf[KS][DS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const int key = min(key0 + 16 * ks + lr, nkeys - 1);
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) kf[ks][ds] = F::load(K + (size_t)key * HD + ds * F::KSTEP + lg * KPL);
   }
-  typename F::frag vf[KT][DT];
+  frag vf[KT][DT];
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt) {
     const int kb = key0 + kt * F::KSTEP + lg * KPL;
@@ -177,92 +182,118 @@ __global__ __launch_bounds__(64) void attn_partial_kernel(AttnArgs a) {
       }
     }
   }
-
-  for (int qt = qt0; qt < qt1; ++qt) {
-    const int qi = 16 * qt + lr;
-    const bool qv = qi < QR;
-    const float* qp = a.q + ((size_t)(qv ? qi / G : 0) * a.Hq + h * G + (qv ? qi % G : 0)) * HD;
-    typename F::frag qf[DS], ql[DS];
+  // Q fragments (A operand): row = query index 16*qt + lr, pre-scaled by 1/sqrt(hd)
+  const int qi = 16 * qt + lr;
+  const bool qv = qi < QR;
+  const float* qp = a.q + ((size_t)(qv ? qi / G : 0) * a.Hq + h * G + (qv ? qi % G : 0)) * HD;
+  frag qf[DS], ql[DS];
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds) {
+    float tmp[KPL], rem[KPL];
+#pragma unroll
+    for (int e = 0; e < KPL; ++e) {
+      tmp[e] = qv ? qp[ds * F::KSTEP + lg * KPL + e] * a.scale : 0.f;
+      rem[e] = tmp[e] - to_f<WT>(from_f<WT>(tmp[e]));
+    }
+    qf[ds] = F::pack(tmp);
+    ql[ds] = F::pack(rem);
+  }
+  f32x4 sc[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    sc[ks] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
-      float tmp[KPL], rem[KPL];
-#pragma unroll
-      for (int e = 0; e < KPL; ++e) {
-        tmp[e] = qv ? qp[ds * F::KSTEP + lg * KPL + e] * a.scale : 0.f;
-        rem[e] = tmp[e] - to_f<WT>(from_f<WT>(tmp[e]));
-      }
-      qf[ds] = F::pack(tmp);
-      ql[ds] = F::pack(rem);
+      sc[ks] = F::mma(qf[ds], kf[ks][ds], sc[ks]);
+      if constexpr (SPLIT) sc[ks] = F::mma(ql[ds], kf[ks][ds], sc[ks]);
     }
-    f32x4 sc[KS];
+  }
+  // lane holds S[4*lg + i][16*ks + lr] of this wave's keys
+  float mx[4], sm[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int qr = 16 * qt + 4 * lg + i;
+    const int lim = qr < QR ? a.pos0 + qr / G : -1;
+    float m_ = -INFINITY;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      sc[ks] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
-        sc[ks] = F::mma(qf[ds], kf[ks][ds], sc[ks]);
-        if constexpr (SPLIT) sc[ks] = F::mma(ql[ds], kf[ks][ds], sc[ks]);
-      }
+      const int key = key0 + 16 * ks + lr;
+      if (key > lim || key >= nkeys) sc[ks][i] = -INFINITY;
+      m_ = fmaxf(m_, sc[ks][i]);
     }
-    // lane holds S[4*lg + i][16*ks + lr]
-    float mx[4], sm[4];
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) m_ = fmaxf(m_, __shfl_xor(m_, o, WAVE));
+    float s_ = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const float p = sc[ks][i] == -INFINITY ? 0.f : expf(sc[ks][i] - m_);
+      sc[ks][i] = p;
+      s_ += p;
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) s_ += __shfl_xor(s_, o, WAVE);
+    mx[i] = m_;
+    sm[i] = s_;
+  }
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int qr = 16 * qt + 4 * lg + i;
-      const int lim = qr < QR ? a.pos0 + qr / G : -1;
-      float m_ = -INFINITY;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int key = key0 + 16 * ks + lr;
-        if (key > lim || key >= nkeys) sc[ks][i] = -INFINITY;
-        m_ = fmaxf(m_, sc[ks][i]);
-      }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) m_ = fmaxf(m_, __shfl_xor(m_, o, WAVE));
-      float s_ = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const float p = sc[ks][i] == -INFINITY ? 0.f : expf(sc[ks][i] - m_);
-        sc[ks][i] = p;
-        s_ += p;
-      }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) s_ += __shfl_xor(s_, o, WAVE);
-      mx[i] = m_;
-      sm[i] = s_;
+      const WT hi = from_f<WT>(sc[ks][i]);
+      Ps[wave][0][4 * lg + i][16 * ks + lr] = hi;
+      if constexpr (SPLIT) Ps[wave][NP - 1][4 * lg + i][16 * ks + lr] = from_f<WT>(sc[ks][i] - to_f<WT>(hi));
     }
+  if (lr == 0) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int i = 0; i < 4; ++i) Ml[wave][4 * lg + i] = make_float2(mx[i], sm[i]);
+  }
+  __syncthreads();
+  f32x4 o[DT];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const WT hi = from_f<WT>(sc[ks][i]);
-        Ps[4 * lg + i][16 * ks + lr] = hi;
-        if constexpr (SPLIT) Pl[4 * lg + i][16 * ks + lr] = from_f<WT>(sc[ks][i] - to_f<WT>(hi));
-      }
-    __syncthreads();
-    f32x4 o[DT];
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kt = 0; kt < KT; ++kt) {
+    const frag pf = F::load(&Ps[wave][0][lr][kt * F::KSTEP + lg * KPL]);
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-      const typename F::frag pf = F::load(&Ps[lr][kt * F::KSTEP + lg * KPL]);
+    for (int dt = 0; dt < DT; ++dt) o[dt] = F::mma(pf, vf[kt][dt], o[dt]);
+    if constexpr (SPLIT) {
+      const frag pl = F::load(&Ps[wave][NP - 1][lr][kt * F::KSTEP + lg * KPL]);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt] = F::mma(pf, vf[kt][dt], o[dt]);
-      if constexpr (SPLIT) {
-        const typename F::frag pl = F::load(&Pl[lr][kt * F::KSTEP + lg * KPL]);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[dt] = F::mma(pl, vf[kt][dt], o[dt]);
-      }
+      for (int dt = 0; dt < DT; ++dt) o[dt] = F::mma(pl, vf[kt][dt], o[dt]);
     }
-    __syncthreads();
+  }
+  // merge the four waves: rescale to the block maximum of each row
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int qr = 16 * qt + 4 * lg + i;
-      if (qr >= QR) continue;
-      const size_t row = (size_t)h * QR + qr;
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * lg + i;
+    float mb = -INFINITY;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) a.po[(row * a.nch + c) * HD + 16 * dt + lr] = o[dt][i];
-      if (lr == 0) a.pml[row * a.nch + c] = make_float2(mx[i], sm[i]);
+    for (int w = 0; w < ATT_WAVES; ++w) mb = fmaxf(mb, Ml[w][row].x);
+    const float f = mx[i] == -INFINITY ? 0.f : expf(mx[i] - mb);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) Ob[wave][row][16 * dt + lr] = o[dt][i] * f;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < 16 * HD; e += 256) {
+    const int row = e / HD, dim = e - row * HD;
+    const int qr = 16 * qt + row;
+    if (qr >= QR) continue;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < ATT_WAVES; ++w) v += Ob[w][row][dim];
+    a.po[(((size_t)h * QR + qr) * a.nch + c) * HD + dim] = v;
+  }
+  if (threadIdx.x < 16) {
+    const int row = threadIdx.x, qr = 16 * qt + row;
+    if (qr < QR) {
+      float mb = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < ATT_WAVES; ++w) mb = fmaxf(mb, Ml[w][row].x);
+      float L = 0.f;
+#pragma unroll
+      for (int w = 0; w < ATT_WAVES; ++w)
+        if (Ml[w][row].x > -INFINITY) L += Ml[w][row].y * expf(Ml[w][row].x - mb);
+      a.pml[((size_t)h * QR + qr) * a.nch + c] = make_float2(mb, L);
     }
   }
 }
@@ -353,7 +384,7 @@ static int launch_attention(const AttnArgs& aa, int ngroups, float* attn_out, hi
   if constexpr (HD % Mfma<WT>::KSTEP != 0) {
     return SPD_E_UNSUPPORTED;  // head dim below one MFMA k-step of this dtype
   } else {
-  hipLaunchKernelGGL((attn_partial_kernel<WT, HD>), dim3(aa.nch, aa.Hkv, ngroups), dim3(64), 0, st,
+  hipLaunchKernelGGL((attn_partial_kernel<WT, HD>), dim3(aa.nch, aa.Hkv, ngroups), dim3(256), 0, st,
                      aa);
   int rc = check_launch();
   if (rc) return rc;
@@ -394,7 +425,7 @@ static int pdm_impl(const spd_config* c, const spd_layer_weights* layers, const 
   aa.nch = (pos0 + M + ATT_KC - 1) / ATT_KC;
   aa.T_cap = T_cap;
   aa.scale = 1.0f / sqrtf((float)hd);
-  const int ngroups = ((p.QR + 15) / 16 + ATT_TPG - 1) / ATT_TPG;
+  const int ngroups = (p.QR + 15) / 16;  // query tiles
 
   for (int l = 0; l < c->Ls; ++l) {
     const spd_layer_weights& lw = layers[l];

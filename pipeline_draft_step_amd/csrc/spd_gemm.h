@@ -18,9 +18,19 @@
 
 namespace spd {
 
+#ifndef SPD_GEMM_UNROLL
+#define SPD_GEMM_UNROLL 8     // k-steps of weight loads in flight per wave (double-buffered)
+#endif
+#ifndef SPD_GEMM_TARGET
+#define SPD_GEMM_TARGET 1024  // blocks a split-K launch aims for
+#endif
+#ifndef SPD_GEMM_MIN_STEPS
+#define SPD_GEMM_MIN_STEPS 8  // minimum k-steps per split
+#endif
+
 constexpr int GEMM_THREADS = 256;
 constexpr int GEMM_WAVES = 4;
-constexpr int GEMM_UNROLL = 8;
+constexpr int GEMM_UNROLL = SPD_GEMM_UNROLL;
 
 struct GemmShape {
   const void* W;
@@ -105,22 +115,6 @@ template <int TC>
 struct TileY {
   const float (*y)[TC + 1];
   __device__ __forceinline__ float operator()(int m, int c) const { return y[m][c]; }
-};
-
-template <int NT, typename RowMap>
-struct PartY {
-  const float* part;
-  int M, N, S, m0, nb;
-  RowMap rm;
-  __device__ __forceinline__ float operator()(int m, int c) const {
-    const int row = rm.template row<NT>(nb, c);
-    const float* p = part + (size_t)(m0 + m) * N + row;
-    const size_t stride = (size_t)M * N;
-    float v = 0.f;
-#pragma unroll 8
-    for (int q = 0; q < S; ++q) v += p[q * stride];
-    return v;
-  }
 };
 
 template <typename WT, int MT, int NT, typename In, typename Epi, typename RowMap>
@@ -224,7 +218,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_skinny_kernel(GemmShape g, 
 #pragma unroll
         for (int i = 0; i < 4; ++i) ytile[16 * t + 4 * lg + i][wave * 16 * NT + 16 * u + lr] = acc[t][u][i];
     __syncthreads();
-    epi.template run<NT>(TileY<TC>{ytile}, nb, m0, Mt, rmap);
+    epi.template run<MT, NT>(TileY<TC>{ytile}, nb, m0, Mt, rmap);
     return;
   }
 #pragma unroll
@@ -241,13 +235,44 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_skinny_kernel(GemmShape g, 
     }
 }
 
-// Sum of the S partial tiles of one (N-block, M-tile), then the epilogue.
+// Sum of the S partial tiles of one (N-block, M-tile) into LDS (fixed order over
+// the splits, all loads of a split in flight together), then the epilogue.
 template <int MT, int NT, typename Epi, typename RowMap>
 __global__ __launch_bounds__(GEMM_THREADS) void gemm_finish_kernel(GemmShape g, Epi epi, RowMap rmap) {
+  constexpr int TR = 16 * MT, TC = 64 * NT;
+  constexpr int PER = TR * TC / GEMM_THREADS;  // tile entries per thread
+  __shared__ float ytile[TR][TC + 1];
   const int nb = blockIdx.x, mt = blockIdx.y;
-  const int m0 = mt * 16 * MT;
-  const int Mt = min(16 * MT, g.M - m0);
-  epi.template run<NT>(PartY<NT, RowMap>{g.part, g.M, g.N, g.S, m0, nb, rmap}, nb, m0, Mt, rmap);
+  const int m0 = mt * TR;
+  const int Mt = min(TR, g.M - m0);
+  const float* ptr[PER];
+  bool ok[PER];
+  float acc[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int e = threadIdx.x + GEMM_THREADS * j;
+    const int m = e / TC, c = e - m * TC;
+    const int row = rmap.template row<NT>(nb, c);
+    ok[j] = m < Mt && row < g.N;
+    ptr[j] = g.part + (size_t)(m0 + (ok[j] ? m : 0)) * g.N + (ok[j] ? row : 0);
+    acc[j] = 0.f;
+  }
+  const size_t stride = (size_t)g.M * g.N;
+#pragma unroll 2
+  for (int q = 0; q < g.S; ++q) {
+    float v[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) v[j] = ok[j] ? ptr[j][q * stride] : 0.f;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) acc[j] += v[j];
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int e = threadIdx.x + GEMM_THREADS * j;
+    ytile[e / TC][e % TC] = acc[j];
+  }
+  __syncthreads();
+  epi.template run<MT, NT>(TileY<TC>{ytile}, nb, m0, Mt, rmap);
 }
 
 // ---------------------------------------------------------------------------
@@ -316,19 +341,32 @@ struct EpiResid {
   float* ss_out;
   int N;  // = d
   int M;
-  template <int NT, typename Y, typename RM>
+  template <int MT, int NT, typename Y, typename RM>
   __device__ void run(const Y& y, int nb, int m0, int Mt, const RM&) const {
+    constexpr int R = 4 * MT;  // rows per wave at most
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    for (int m = wave; m < Mt; m += GEMM_WAVES) {
+    float hv[R][NT];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int m = wave + GEMM_WAVES * r;
+#pragma unroll
+      for (int u = 0; u < NT; ++u) {
+        const int col = nb * 64 * NT + lane + 64 * u;
+        hv[r][u] = (m < Mt && col < N) ? h[(size_t)(m0 + m) * N + col] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int m = wave + GEMM_WAVES * r;
+      if (m >= Mt) break;
       float sq = 0.f;
 #pragma unroll
       for (int u = 0; u < NT; ++u) {
         const int c = lane + 64 * u;
         const int col = nb * 64 * NT + c;
         if (col < N) {
-          float* hp = h + (size_t)(m0 + m) * N + col;
-          const float v = *hp + y(m, c);
-          *hp = v;
+          const float v = hv[r][u] + y(m, c);
+          h[(size_t)(m0 + m) * N + col] = v;
           sq += v * v;
         }
       }
@@ -342,7 +380,7 @@ struct EpiResid {
 struct EpiSilu {
   float* act;
   int dff;
-  template <int NT, typename Y, typename RM>
+  template <int MT, int NT, typename Y, typename RM>
   __device__ void run(const Y& y, int nb, int m0, int Mt, const RM&) const {
     constexpr int H = 32 * NT;
     for (int e = threadIdx.x; e < Mt * H; e += GEMM_THREADS) {

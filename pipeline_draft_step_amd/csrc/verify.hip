@@ -85,11 +85,18 @@ __global__ __launch_bounds__(VER_THREADS) void verify_sums_kernel(VerArgs a) {
   const float* prow = a.p + ((size_t)b * rowsP + j) * a.V;
   const float* qrow = rejected ? a.q + ((size_t)b * a.gamma + j) * a.V : nullptr;
   uint64_t sres = 0, sp = 0;
-  const int end = min((c + 1) * VER_CHUNK, a.V);
-  for (int i = c * VER_CHUNK + threadIdx.x; i < end; i += VER_THREADS) {
-    const float pv = prow[i];
-    sp += prob_weight(pv);
-    if (rejected) sres += res_weight(pv, qrow[i]);
+  constexpr int PER = VER_CHUNK / VER_THREADS;
+  float pv[PER], qv[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int i = c * VER_CHUNK + threadIdx.x + VER_THREADS * e;
+    pv[e] = i < a.V ? prow[i] : 0.f;
+    qv[e] = (rejected && i < a.V) ? qrow[i] : 0.f;
+  }
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    sp += prob_weight(pv[e]);
+    if (rejected) sres += res_weight(pv[e], qv[e]);
   }
   sres = wave_sum_u64(sres);
   sp = wave_sum_u64(sp);
@@ -215,6 +222,7 @@ __global__ __launch_bounds__(VER_THREADS) void verify_greedy_chunks_kernel(VerAr
   for (int j = 0; j < rows; ++j) {
     const float* prow = a.p + ((size_t)b * rows + j) * a.V;
     ArgMax am{-INFINITY, ARG_NONE};
+#pragma unroll 8
     for (int i = c * VER_CHUNK + threadIdx.x; i < end; i += VER_THREADS) am = argmax_merge(am, ArgMax{prow[i], i});
     am = wave_argmax(am);
     if ((threadIdx.x & 63) == 0) s_am[threadIdx.x >> 6] = am;
