@@ -25,9 +25,11 @@
  *    inspected on the host; kernels clamp out-of-range indices so that no access
  *    leaves the buffers described below.
  *  - Workspaces: `ws` is a DEVICE buffer of at least spd_workspace_size(...) bytes,
- *    16-byte aligned, holding partial results between the kernels of one call.  It
- *    needs no initialisation.  Calls that share a workspace must not run
- *    concurrently (use one workspace per stream).
+ *    16-byte aligned, holding partial results of one call.  Its first
+ *    SPD_WS_COUNTER_BYTES bytes are arrival counters that must be zero before the
+ *    workspace is first used (allocate it zero-filled); every completed call leaves
+ *    them zero again.  Calls that share a workspace must not run concurrently (use
+ *    one workspace per stream).
  *  - dtype SPD_BF16: weights, anchors and the key/value cache are bfloat16 (bit
  *    pattern in uint16); SPD_F32: all of them are float32.  Features, hidden rows,
  *    logits and probabilities are always float32.
@@ -55,6 +57,7 @@ enum { SPD_F32 = 0, SPD_BF16 = 1 };
 enum { SPD_ANCHOR_ZERO_MASK = 0, SPD_ANCHOR_CLAMP_MIN = 1 };
 enum { SPD_CALL_FUSE = 0, SPD_CALL_PDM = 1, SPD_CALL_LM_HEAD = 2, SPD_CALL_VERIFY = 3 };
 
+#define SPD_WS_COUNTER_BYTES 65536
 #define SPD_MAX_ANCHORS 8
 #define SPD_MAX_STAGES 32
 

@@ -17,6 +17,7 @@ SPD_OK, SPD_E_INVALID, SPD_E_UNSUPPORTED, SPD_E_WORKSPACE, SPD_E_HIP = 0, -1, -2
 SPD_F32, SPD_BF16 = 0, 1
 SPD_ANCHOR_ZERO_MASK, SPD_ANCHOR_CLAMP_MIN = 0, 1
 SPD_CALL_FUSE, SPD_CALL_PDM, SPD_CALL_LM_HEAD, SPD_CALL_VERIFY = 0, 1, 2, 3
+SPD_WS_COUNTER_BYTES = 65536
 SPD_MAX_ANCHORS = 8
 SPD_MAX_STAGES = 32
 

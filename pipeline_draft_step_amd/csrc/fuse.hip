@@ -4,7 +4,7 @@
 // at depth k uses every anchor b_j <= l_max(k); the review blog's core formulas
 // give the operator FC(norm(Concat(.))) and g^0 = FC(H^0).
 //
-// The skinny GEMM (plus its finisher when split over K).  The input functor gathers the row's eligible
+// One launch of the skinny GEMM.  The input functor gathers the row's eligible
 // anchor states for its K-slice straight from the anchor store into LDS (empty
 // slots are zeros; gamma is applied; the k = 0 rows read slot 0 only, without
 // gamma) and records the slice's sum of squares.  Because FC is linear,
@@ -35,38 +35,54 @@ struct InAnchor {
   SlotTable tab;
   float* xss;  // [nblocks][S][M] slice sums of squares
   __device__ void stage(const XStage<WT>& xs, int m0, int Mt, int k0, int kw, int nb, int s, int S) const {
-    // wave w stages rows w, w+4, ...: 4 consecutive columns per lane and step
-    // (d % 4 == 0, so a group of 4 never straddles two anchor slots)
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // StageIdx layout (d % 4 == 0, so a group of 4 never straddles two anchor slots)
     const int kv = kw >> 2;
-    for (int mm = wave; mm < Mt; mm += GEMM_WAVES) {
-      const int r = m0 + mm;
-      const int k = depth(r);
-      const bool plain = (k == 0) && !norm_k0;
-      const size_t base = (size_t)(pos0 + r) * S_store;
-      float sq = 0.f;
-#pragma unroll 4
-      for (int u = lane; u < kv; u += WAVE) {
-        const int col = k0 + (u << 2);
-        const int j = col / d;
-        const int c = col - j * d;
-        int slot = tab.v[k * m + j];
-        if (plain && j != 0) slot = -1;
-        float v[4] = {0.f, 0.f, 0.f, 0.f};
-        if (slot >= 0 && slot < S_store) {
-          load4(store + (base + slot) * d + c, v);
-          float gm[4] = {1.f, 1.f, 1.f, 1.f};
-          if (!plain) load4(gamma + col, gm);
+    const StageIdx ix(Mt, kv);
+    float sq[STAGE_ROWS];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            sq += v[i] * v[i];
-            v[i] *= gm[i];
-          }
-        }
-        xs.put4(mm, u << 2, v);
+    for (int j = 0; j < STAGE_ROWS; ++j) sq[j] = 0.f;
+    for (int b0 = 0; b0 < ix.n; b0 += STAGE_BATCH) {
+      float4 v[STAGE_BATCH], gm[STAGE_BATCH];
+#pragma unroll
+      for (int i = 0; i < STAGE_BATCH; ++i) {
+        int j, mm, u;
+        ix.at(b0 + i, j, mm, u);
+        // unconditional loads from clamped addresses, masked afterwards (a
+        // conditional load becomes a branch whose join waits for every load)
+        const bool ok = b0 + i < ix.n && u < kv;
+        const int r = m0 + (ok ? mm : 0);
+        const int k = depth(r);
+        const bool plain = (k == 0) && !norm_k0;
+        const int col = k0 + (ok ? 4 * u : 0);
+        const int a = col / d;
+        const int c = col - a * d;
+        int slot = tab.v[k * m + a];
+        if (plain && a != 0) slot = -1;
+        const bool use = ok && slot >= 0 && slot < S_store;
+        const float4 x = ldg4(store + ((size_t)(pos0 + r) * S_store + (use ? slot : 0)) * d + c);
+        const float4 gg = ldg4(gamma + col);
+        v[i] = use ? x : make_float4(0.f, 0.f, 0.f, 0.f);
+        gm[i] = (use && !plain) ? gg : make_float4(1.f, 1.f, 1.f, 1.f);
       }
-      sq = wave_sum(sq);
-      if (lane == 0) xss[((size_t)nb * S + s) * depth.M + r] = sq;
+#pragma unroll
+      for (int i = 0; i < STAGE_BATCH; ++i) {
+        int j, mm, u;
+        ix.at(b0 + i, j, mm, u);
+        if (b0 + i < ix.n && u < kv) {
+          const float q = v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
+#pragma unroll
+          for (int t = 0; t < STAGE_ROWS; ++t)
+            if (t == j) sq[t] += q;
+          const float x[4] = {v[i].x * gm[i].x, v[i].y * gm[i].y, v[i].z * gm[i].z, v[i].w * gm[i].w};
+          xs.put4(mm, 4 * u, x);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < STAGE_ROWS; ++j) {
+      const int mm = ix.wave + GEMM_WAVES * j;
+      const float t = wave_sum(sq[j]);
+      if (mm < Mt && ix.lane == 0) st_coh(xss + ((size_t)nb * S + s) * depth.M + m0 + mm, t);
     }
   }
 };
@@ -88,7 +104,7 @@ struct EpiFeature {
       const int r = m0 + mm;
       const int k = depth(r);
       const float* xp = xss + (size_t)nb * S * depth.M + r;
-      const float t = wave_sum_of(S, [&](int q) { return xp[(size_t)q * depth.M]; });
+      const float t = wave_sum_of(S, [&](int q) { return ld_coh(xp + (size_t)q * depth.M); });
       if ((threadIdx.x & 63) == 0) {
         if (k == 0 && !norm_k0) {
           inv[mm] = 1.f;
@@ -118,7 +134,7 @@ static FusePlan plan_fuse(const spd_config* cfg, int M) {
   const bool bf = cfg->dtype == SPD_BF16;
   const int kstep = bf ? Mfma<bf16>::KSTEP : Mfma<float>::KSTEP;
   p.gp = plan_gemm(cfg->d, cfg->m * cfg->d, M, kstep, bf ? 2 : 4, 1);
-  size_t off = 0;
+  size_t off = SPD_WS_COUNTER_BYTES;
   p.off_xss = off;
   off = align256(off + (size_t)p.gp.nblocks * p.gp.S * M * sizeof(float));
   p.off_part = off;
@@ -153,6 +169,7 @@ static int fuse_impl(const spd_config* cfg, const void* hstore, int64_t T_cap, i
   gs.ldx = p.gp.ldx;
   gs.part = reinterpret_cast<float*>(w + p.off_part);
   gs.nblocks = p.gp.nblocks;
+  gs.counters = reinterpret_cast<unsigned*>(w);
 
   InAnchor<WT> in{static_cast<const WT*>(hstore), static_cast<const WT*>(norm_w), T_cap, S_store,
                   d, m, pos0, cfg->norm_k0, dep, tab, xss};

@@ -340,12 +340,12 @@ static LmPlan plan_lm(const spd_config* c, int rows) {
                    /*target=*/1, /*min_steps=*/1 << 30);
   p.nstat = p.dot ? (c->V + 4 * DOT_ROWS - 1) / (4 * DOT_ROWS) : p.gp.nblocks;
   p.nchunks = (c->V + SMX_CHUNK - 1) / SMX_CHUNK;
-  size_t off = 0;
+  size_t off = SPD_WS_COUNTER_BYTES;
   auto take = [&](size_t b) { size_t r = off; off = align256(off + b); return r; };
   p.off_part = take(!p.dot && p.gp.S > 1 ? (size_t)p.gp.S * rows * c->V * 4 : 0);
   p.off_stat = take((size_t)p.nstat * rows * sizeof(BlockStat));
   p.off_csum = take((size_t)rows * p.nchunks * 8);
-  p.total = std::max(off, (size_t)256);
+  p.total = off;
   return p;
 }
 

@@ -6,13 +6,13 @@
 //   QKV GEMM  : X = RMSNorm(h)*attn_norm staged in LDS (bf16 hi+lo pairs); per head:
 //               q/k RMSNorm, rotate-half RoPE, k/v written to the cache, q kept.
 //   attention : MFMA flash-decode, one block per (256-key chunk, kv head, 16-row
-//               query tile), GQA rows of a kv head together, waves merged in LDS.
-//   combine   : log-sum-exp merge of the chunk partials.
+//               query tile), GQA rows of a kv head together, waves merged in LDS;
+//               the last chunk block of a (kv head, tile) merges the chunk partials.
 //   O GEMM    : h += W_o attn                (epilogue keeps row sums of squares)
 //   gate/up   : X = RMSNorm(h)*mlp_norm; epilogue silu(gate)*up
 //   down GEMM : h += W_down act.
-// GEMMs split over K add a small finisher launch that sums the partial tiles and
-// runs the epilogue.  After the last layer, h_last = RMSNorm(h[M-1]) * final_norm.
+// GEMMs split over K reduce their partial tiles in the last block of each tile;
+// after the last layer the down epilogue also writes h_last = RMSNorm(h[M-1]) * final_norm.
 #include <math.h>
 
 #include <algorithm>
@@ -26,22 +26,7 @@ namespace spd {
 constexpr int ATT_SUB = 64;                     // keys per wave
 constexpr int ATT_WAVES = 4;                    // waves per attention block
 constexpr int ATT_KC = ATT_SUB * ATT_WAVES;     // keys per block (one partial per row)
-
-// h_last = RMSNorm(h[M-1]) * final_norm, row statistics from P partial sums
-template <typename WT>
-__global__ __launch_bounds__(256) void final_norm_kernel(const float* h, const float* ss, int P, int M,
-                                                         int d, const WT* fnorm, float* h_last,
-                                                         float eps) {
-  __shared__ float s_inv;
-  if (threadIdx.x < 64) {
-    const float t = wave_sum_of(P, [&](int p) { return ss[(size_t)p * M + M - 1]; });
-    if (threadIdx.x == 0) s_inv = 1.0f / sqrtf(t / (float)d + eps);
-  }
-  __syncthreads();
-#pragma unroll 4
-  for (int c = threadIdx.x; c < d; c += 256)
-    h_last[c] = h[(size_t)(M - 1) * d + c] * s_inv * to_f<WT>(fnorm[c]);
-}
+constexpr int ATT_MAXCH = 128;                  // chunks per row: context up to 32768
 
 // h = g, and per-64-column partial sums of squares of every row
 __global__ __launch_bounds__(64) void rows_init_kernel(const float* g, float* h, float* ss, int M,
@@ -124,7 +109,9 @@ struct AttnArgs {
   const void* vc;  // [Hkv][hd][T_cap]
   float* po;       // [Hkv][QR][nch][hd]
   float2* pml;     // [Hkv][QR][nch]  (chunk max, chunk sum of exp)
-  int M, Hq, Hkv, pos0, nch;
+  float* out;      // [M][Hq*hd] attention output
+  unsigned* counters;  // [Hkv][nqt]
+  int M, Hq, Hkv, pos0, nch, nqt;
   int64_t T_cap;
   float scale;
 };
@@ -154,6 +141,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   const int nkeys = a.pos0 + a.M;
   const int r_last = (min(QR, 16 * qt + 16) - 1) / G;
   if (c * ATT_KC > a.pos0 + r_last) return;  // every row of the tile is masked here
+  SPD_MARK(0);
   const int key0 = c * ATT_KC + wave * ATT_SUB;
 
   const WT* K = static_cast<const WT*>(a.kc) + (size_t)h * a.T_cap * HD;
@@ -182,6 +170,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
       }
     }
   }
+  SPD_MARK(1);
   // Q fragments (A operand): row = query index 16*qt + lr, pre-scaled by 1/sqrt(hd)
   const int qi = 16 * qt + lr;
   const bool qv = qi < QR;
@@ -208,6 +197,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
       if constexpr (SPLIT) sc[ks] = F::mma(ql[ds], kf[ks][ds], sc[ks]);
     }
   }
+  SPD_MARK(2);
   // lane holds S[4*lg + i][16*ks + lr] of this wave's keys
   float mx[4], sm[4];
 #pragma unroll
@@ -221,8 +211,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
       if (key > lim || key >= nkeys) sc[ks][i] = -INFINITY;
       m_ = fmaxf(m_, sc[ks][i]);
     }
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) m_ = fmaxf(m_, __shfl_xor(m_, o, WAVE));
+m_ = row16_max(m_);
     float s_ = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -230,8 +219,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
       sc[ks][i] = p;
       s_ += p;
     }
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) s_ += __shfl_xor(s_, o, WAVE);
+s_ = row16_sum(s_);
     mx[i] = m_;
     sm[i] = s_;
   }
@@ -262,6 +250,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
       for (int dt = 0; dt < DT; ++dt) o[dt] = F::mma(pl, vf[kt][dt], o[dt]);
     }
   }
+  SPD_MARK(3);
   // merge the four waves: rescale to the block maximum of each row
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -281,7 +270,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     float v = 0.f;
 #pragma unroll
     for (int w = 0; w < ATT_WAVES; ++w) v += Ob[w][row][dim];
-    a.po[(((size_t)h * QR + qr) * a.nch + c) * HD + dim] = v;
+    st_coh(a.po + (((size_t)h * QR + qr) * a.nch + c) * HD + dim, v);
   }
   if (threadIdx.x < 16) {
     const int row = threadIdx.x, qr = 16 * qt + row;
@@ -293,35 +282,79 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
       for (int w = 0; w < ATT_WAVES; ++w)
         if (Ml[w][row].x > -INFINITY) L += Ml[w][row].y * expf(Ml[w][row].x - mb);
-      a.pml[((size_t)h * QR + qr) * a.nch + c] = make_float2(mb, L);
+      float* ml = reinterpret_cast<float*>(a.pml + ((size_t)h * QR + qr) * a.nch + c);
+      st_coh(ml, mb);
+      st_coh(ml + 1, L);
     }
   }
-}
-
-// out[r][head*HD + :] = merge of the chunk partials valid for query row r.
-template <typename AT, int HD>
-__global__ __launch_bounds__(64) void attn_combine_kernel(AttnArgs a, AT* out) {
-  const int qi = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
-  const int G = a.Hq / a.Hkv, QR = a.M * G;
-  const int r = qi / G, head = h * G + qi % G;
-  const int nvalid = (a.pos0 + r) / ATT_KC + 1;
-  const size_t row = (size_t)h * QR + qi;
-  const float2* ml = a.pml + row * a.nch;
-  float mmax = -INFINITY;
-#pragma unroll 8
-  for (int c = 0; c < nvalid; ++c) mmax = fmaxf(mmax, ml[c].x);
-  float L = 0.f, o0 = 0.f, o1 = 0.f;
-#pragma unroll 8
-  for (int c = 0; c < nvalid; ++c) {
-    const float w = expf(ml[c].x - mmax);
-    L += ml[c].y * w;
-    const float* po = a.po + (row * a.nch + c) * HD;
-    if (lane < HD) o0 += po[lane] * w;
-    if (lane + 64 < HD) o1 += po[lane + 64] * w;
+  // the last chunk block of (kv head, query tile) merges the chunk partials of its rows
+  const int nchunk_tile = min(a.nch, (a.pos0 + r_last) / ATT_KC + 1);
+  SPD_MARK(4);
+  if (!arrive_last(a.counters + h * a.nqt + qt, (unsigned)nchunk_tile)) {
+    SPD_MARK(5);
+    return;
   }
-  AT* op = out + (size_t)r * a.Hq * HD + (size_t)head * HD;
-  if (lane < HD) op[lane] = from_f<AT>(o0 / L);
-  if (lane + 64 < HD) op[lane + 64] = from_f<AT>(o1 / L);
+  SPD_MARK(5);
+  // chunk weights exp(m_c - max) of each row: 16 threads per row, chunks strided
+  __shared__ float s_w[16][ATT_MAXCH];
+  __shared__ float s_L[16];
+  {
+    constexpr int CPT = ATT_MAXCH / 16;  // chunks per thread at most
+    const int row = threadIdx.x >> 4, j = threadIdx.x & 15;
+    const int qr = 16 * qt + row;
+    const int nv = qr < QR ? (a.pos0 + qr / G) / ATT_KC + 1 : 0;
+    const uint64_t* ml = reinterpret_cast<const uint64_t*>(a.pml + ((size_t)h * QR + (qr < QR ? qr : 0)) * a.nch);
+    float2 v[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int cc = j + 16 * i;
+      v[i] = cc < nv ? __builtin_bit_cast(float2, ld_coh_u64(ml + cc)) : make_float2(-INFINITY, 0.f);
+    }
+    float mmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) mmax = fmaxf(mmax, v[i].x);
+mmax = row16_max(mmax);
+    float L = 0.f;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int cc = j + 16 * i;
+      const float wgt = cc < nv ? expf(v[i].x - mmax) : 0.f;
+      s_w[row][cc] = wgt;
+      L += v[i].y * wgt;
+    }
+L = row16_sum(L);
+    if (j == 0) s_L[row] = L;
+  }
+  __syncthreads();
+  // output: each thread owns 4 consecutive dims of a row; 8 chunk partials in flight
+  constexpr int D4 = HD / 4;
+  for (int e = threadIdx.x; e < 16 * D4; e += 256) {
+    const int row = e / D4, dim = (e - row * D4) * 4;
+    const int qr = 16 * qt + row;
+    if (qr >= QR) continue;
+    const int r = qr / G;
+    const int nv = (a.pos0 + r) / ATT_KC + 1;
+    const uint32_t base = (uint32_t)(((((size_t)h * QR + qr) * a.nch) * HD + dim) * 4);
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int c0 = 0; c0 < nv; c0 += 8) {
+      float4 pv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        pv[i] = c0 + i < nv ? ld_coh4(a.po, base + (uint32_t)((c0 + i) * HD * 4)) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float wgt = c0 + i < nv ? s_w[row][c0 + i] : 0.f;
+        o.x += pv[i].x * wgt;
+        o.y += pv[i].y * wgt;
+        o.z += pv[i].z * wgt;
+        o.w += pv[i].w * wgt;
+      }
+    }
+    const float il = 1.0f / s_L[row];
+    float* dst = a.out + (size_t)r * a.Hq * HD + (size_t)(h * G + qr % G) * HD + dim;
+    *reinterpret_cast<float4*>(dst) = make_float4(o.x * il, o.y * il, o.z * il, o.w * il);
+  }
+  SPD_MARK(6);
 }
 
 struct PdmPlan {
@@ -337,11 +370,11 @@ static PdmPlan plan_pdm(const spd_config* c, int M, int64_t T_cap) {
   const int es = bf ? 2 : 4;
   p.qkv = plan_gemm((c->Hq + 2 * c->Hkv) * c->hd, c->d, M, ks, es, 2);
   p.o = plan_gemm(c->d, c->Hq * c->hd, M, ks, es, 1);
-  p.gu = plan_gemm(2 * c->dff, c->d, M, ks, es, 1);
+  p.gu = plan_gemm(2 * c->dff, c->d, M, ks, es, 2);
   p.down = plan_gemm(c->d, c->dff, M, ks, es, 1);
   p.nch = (int)((T_cap + ATT_KC - 1) / ATT_KC);
   p.QR = M * (c->Hq / c->Hkv);
-  size_t off = 0;
+  size_t off = SPD_WS_COUNTER_BYTES;
   auto take = [&](size_t bytes) { size_t r = off; off = align256(off + bytes); return r; };
   p.off_h = take((size_t)M * c->d * 4);
   p.off_ss = take((size_t)(c->d / 64) * M * 4);
@@ -365,7 +398,8 @@ size_t pdm_workspace(const spd_config* cfg, int M, int64_t T_cap) {
   return plan_pdm(cfg, M, T_cap).total;
 }
 
-static GemmShape shape_of(const GemmPlan& gp, const void* W, int N, int K, int M, float* part) {
+static GemmShape shape_of(const GemmPlan& gp, const void* W, int N, int K, int M, float* part,
+                          unsigned* ctr) {
   GemmShape g;
   g.W = W;
   g.N = N;
@@ -376,21 +410,18 @@ static GemmShape shape_of(const GemmPlan& gp, const void* W, int N, int K, int M
   g.ldx = gp.ldx;
   g.part = part;
   g.nblocks = gp.nblocks;
+  g.counters = ctr;
   return g;
 }
 
 template <typename WT, int HD>
-static int launch_attention(const AttnArgs& aa, int ngroups, float* attn_out, hipStream_t st) {
+static int launch_attention(const AttnArgs& aa, hipStream_t st) {
   if constexpr (HD % Mfma<WT>::KSTEP != 0) {
     return SPD_E_UNSUPPORTED;  // head dim below one MFMA k-step of this dtype
   } else {
-  hipLaunchKernelGGL((attn_partial_kernel<WT, HD>), dim3(aa.nch, aa.Hkv, ngroups), dim3(256), 0, st,
-                     aa);
-  int rc = check_launch();
-  if (rc) return rc;
-  hipLaunchKernelGGL((attn_combine_kernel<float, HD>), dim3(aa.M * (aa.Hq / aa.Hkv), aa.Hkv), dim3(64),
-                     0, st, aa, attn_out);
-  return check_launch();
+    hipLaunchKernelGGL((attn_partial_kernel<WT, HD>), dim3(aa.nch, aa.Hkv, aa.nqt), dim3(256), 0, st,
+                       aa);
+    return check_launch();
   }
 }
 
@@ -406,6 +437,7 @@ static int pdm_impl(const spd_config* c, const spd_layer_weights* layers, const 
   float* attn = reinterpret_cast<float*>(w + p.off_attn);
   float* act = reinterpret_cast<float*>(w + p.off_act);
   float* part = reinterpret_cast<float*>(w + p.off_part);
+  unsigned* ctr = reinterpret_cast<unsigned*>(w);
   const int d = c->d, hd = c->hd, Hq = c->Hq, Hkv = c->Hkv, dff = c->dff;
   const int nq = (Hq + 2 * Hkv) * hd;
 
@@ -423,9 +455,11 @@ static int pdm_impl(const spd_config* c, const spd_layer_weights* layers, const 
   aa.Hkv = Hkv;
   aa.pos0 = pos0;
   aa.nch = (pos0 + M + ATT_KC - 1) / ATT_KC;
+  aa.out = attn;
+  aa.counters = ctr;
+  aa.nqt = (p.QR + 15) / 16;
   aa.T_cap = T_cap;
   aa.scale = 1.0f / sqrtf((float)hd);
-  const int ngroups = (p.QR + 15) / 16;  // query tiles
 
   for (int l = 0; l < c->Ls; ++l) {
     const spd_layer_weights& lw = layers[l];
@@ -436,7 +470,7 @@ static int pdm_impl(const spd_config* c, const spd_layer_weights* layers, const 
       InNorm<WT> in{h, static_cast<const WT*>(lw.attn_norm), ss, P, M, d, c->rms_eps};
       EpiQKV<WT> epi{qb, kc, vc, static_cast<const WT*>(lw.q_norm), static_cast<const WT*>(lw.k_norm),
                      Hq, Hkv, hd, pos0, T_cap, c->rms_eps, c->rope_theta};
-      rc = launch_gemm<WT, 2>(p.qkv, shape_of(p.qkv, lw.wqkv, nq, d, M, part), in, epi,
+      rc = launch_gemm<WT, 2>(p.qkv, shape_of(p.qkv, lw.wqkv, nq, d, M, part, ctr), in, epi,
                               RowMapStd{}, st);
       if (rc) return rc;
     }
@@ -444,17 +478,17 @@ static int pdm_impl(const spd_config* c, const spd_layer_weights* layers, const 
     aa.kc = kc;
     aa.vc = vc;
     switch (hd) {
-      case 16: rc = launch_attention<WT, 16>(aa, ngroups, attn, st); break;
-      case 32: rc = launch_attention<WT, 32>(aa, ngroups, attn, st); break;
-      case 64: rc = launch_attention<WT, 64>(aa, ngroups, attn, st); break;
-      default: rc = launch_attention<WT, 128>(aa, ngroups, attn, st); break;
+      case 16: rc = launch_attention<WT, 16>(aa, st); break;
+      case 32: rc = launch_attention<WT, 32>(aa, st); break;
+      case 64: rc = launch_attention<WT, 64>(aa, st); break;
+      default: rc = launch_attention<WT, 128>(aa, st); break;
     }
     if (rc) return rc;
     // O projection + residual
     {
       InAct<WT, float> in{attn, Hq * hd};
-      EpiResid epi{h, ss, d, M};
-      rc = launch_gemm<WT, 1>(p.o, shape_of(p.o, lw.wo, d, Hq * hd, M, part), in, epi,
+      EpiResid<WT> epi{h, ss, d, M, 0, nullptr, nullptr, ctr + CTR_FINAL, p.o.nblocks, c->rms_eps};
+      rc = launch_gemm<WT, 1>(p.o, shape_of(p.o, lw.wo, d, Hq * hd, M, part, ctr), in, epi,
                               RowMapStd{}, st);
       if (rc) return rc;
       P = p.o.nblocks;
@@ -463,24 +497,22 @@ static int pdm_impl(const spd_config* c, const spd_layer_weights* layers, const 
     {
       InNorm<WT> in{h, static_cast<const WT*>(lw.mlp_norm), ss, P, M, d, c->rms_eps};
       EpiSilu epi{act, dff};
-      rc = launch_gemm<WT, 1>(p.gu, shape_of(p.gu, lw.w_gate_up, 2 * dff, d, M, part), in, epi,
+      rc = launch_gemm<WT, 2>(p.gu, shape_of(p.gu, lw.w_gate_up, 2 * dff, d, M, part, ctr), in, epi,
                               RowMapGateUp{dff}, st);
       if (rc) return rc;
     }
-    // down + residual
+    // down + residual; after the last layer its epilogue also writes h_last
     {
       InAct<WT, float> in{act, dff};
-      EpiResid epi{h, ss, d, M};
-      rc = launch_gemm<WT, 1>(p.down, shape_of(p.down, lw.w_down, d, dff, M, part), in, epi,
+      const bool last = l == c->Ls - 1;
+      EpiResid<WT> epi{h, ss, d, M, last ? 1 : 0, static_cast<const WT*>(final_norm), h_last,
+                       ctr + CTR_FINAL, p.down.nblocks, c->rms_eps};
+      rc = launch_gemm<WT, 1>(p.down, shape_of(p.down, lw.w_down, d, dff, M, part, ctr), in, epi,
                               RowMapStd{}, st);
       if (rc) return rc;
       P = p.down.nblocks;
     }
   }
-  hipLaunchKernelGGL((final_norm_kernel<WT>), dim3(1), dim3(256), 0, st, h, ss, P, M, d,
-                     static_cast<const WT*>(final_norm), h_last, c->rms_eps);
-  rc = check_launch();
-  if (rc) return rc;
   if (c->Ls == 0) return SPD_E_UNSUPPORTED;
   return SPD_OK;
 }
@@ -502,6 +534,11 @@ extern "C" int spd_pdm_step(const spd_config* cfg, const spd_layer_weights* laye
   const int hd = cfg->hd;
   if (hd != 16 && hd != 32 && hd != 64 && hd != 128) return SPD_E_UNSUPPORTED;
   if (cfg->d % 64 || cfg->dff % 64 || T_cap % 8) return SPD_E_UNSUPPORTED;
+  if (((int64_t)pos0 + M + ATT_KC - 1) / ATT_KC > ATT_MAXCH) return SPD_E_UNSUPPORTED;
+  {
+    const int G = cfg->Hq / cfg->Hkv;
+    if ((int64_t)cfg->Hkv * ((M * G + 15) / 16) >= CTR_FINAL) return SPD_E_UNSUPPORTED;
+  }
   if (((int64_t)cfg->Hq * hd) % 32) return SPD_E_UNSUPPORTED;
   for (int l = 0; l < cfg->Ls; ++l) {
     const spd_layer_weights& w = layers[l];

@@ -7,6 +7,28 @@
 
 #include "../../include/spd.h"
 
+// Optional per-block timeline hook for profiling builds: SPD_MARK(i) stores the
+// device real-time clock (100 MHz) for event i of the calling block into slot
+// [dispatch packet mod 64][block][i] of a buffer that the profiling harness
+// defines, plus the packet address of each dispatch.  Compiles to nothing otherwise.
+#ifdef SPD_TRACE
+extern __device__ unsigned long long spd_trace_buf[];
+extern __device__ unsigned spd_trace_tag[];
+#define SPD_MARK(i)                                                                  \
+  do {                                                                               \
+    if (threadIdx.x == 0) {                                                          \
+      const uintptr_t d_ = (uintptr_t)__builtin_amdgcn_dispatch_ptr();               \
+      const unsigned r_ = (unsigned)(d_ >> 6) & 63u;                                 \
+      const unsigned b_ = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z); \
+      if (b_ < 4096u)                                                                \
+        spd_trace_buf[((size_t)r_ * 4096u + b_) * 8u + (i)] = __builtin_amdgcn_s_memrealtime(); \
+      if (b_ == 0u) spd_trace_tag[r_] = (unsigned)d_ | 1u;                           \
+    }                                                                                \
+  } while (0)
+#else
+#define SPD_MARK(i) ((void)0)
+#endif
+
 namespace spd {
 
 typedef uint16_t bf16;  // bfloat16 bit pattern
@@ -18,12 +40,14 @@ constexpr int WAVE = 64;
 __device__ __forceinline__ float bf2f(bf16 v) { return __uint_as_float((uint32_t)v << 16); }
 
 // float -> bfloat16, round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ bf16 f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16)(u >> 16);
+// fp32 -> bf16, round to nearest even (the hardware v_cvt_pk_bf16_f32)
+typedef float spd_f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 spd_bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+  const spd_f32x2 f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, spd_bf16x2));
 }
+__device__ __forceinline__ bf16 f2bf(float f) { return (bf16)(pack2_bf16(f, 0.f) & 0xffffu); }
 
 template <typename T> __device__ __forceinline__ float to_f(T v);
 template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
@@ -59,7 +83,7 @@ template <> struct Mfma<bf16> {
   static __device__ __forceinline__ frag pack(const float* v) {
     uint32_t w[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f2bf(v[2 * i]) | ((uint32_t)f2bf(v[2 * i + 1]) << 16);
+    for (int i = 0; i < 4; ++i) w[i] = pack2_bf16(v[2 * i], v[2 * i + 1]);
     return make_uint4(w[0], w[1], w[2], w[3]);
   }
 };
@@ -77,26 +101,64 @@ template <> struct Mfma<float> {
 };
 
 // ---------------------------------------------------------------------------
-// Wave reductions (xor butterflies; every lane ends with the result)
+// Wave reductions.  Within each row of 16 lanes: DPP butterflies (quad_perm,
+// half-mirror, mirror), which stay in the VALU; the four row results are then
+// combined from readlane values.  Every lane ends with the same result, and the
+// summation order is fixed.  Callers run them with the whole wave active.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, dpp_u32<CTRL>(__builtin_bit_cast(uint32_t, v)));
+}
+constexpr int DPP_QUAD_1032 = 0xb1;  // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_2301 = 0x4e;  // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141;
+constexpr int DPP_MIRROR = 0x140;
+
+// sum / max over each row of 16 lanes, result in every lane of the row
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<DPP_QUAD_1032>(v);
+  v += dpp_f32<DPP_QUAD_2301>(v);
+  v += dpp_f32<DPP_HALF_MIRROR>(v);
+  v += dpp_f32<DPP_MIRROR>(v);
   return v;
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f32<DPP_QUAD_1032>(v));
+  v = fmaxf(v, dpp_f32<DPP_QUAD_2301>(v));
+  v = fmaxf(v, dpp_f32<DPP_HALF_MIRROR>(v));
+  v = fmaxf(v, dpp_f32<DPP_MIRROR>(v));
+  return v;
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
-  return v;
+  v = row16_max(v);
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  return ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)v);
+}
+__device__ __forceinline__ uint64_t lane_u64(uint64_t v, int l) {
+  return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), l) << 32) |
+         (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
 }
 __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint32_t lo = __shfl_xor((uint32_t)v, o, WAVE);
-    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, WAVE);
-    v += ((uint64_t)hi << 32) | lo;
-  }
-  return v;
+  v += dpp_u64<DPP_QUAD_1032>(v);
+  v += dpp_u64<DPP_QUAD_2301>(v);
+  v += dpp_u64<DPP_HALF_MIRROR>(v);
+  v += dpp_u64<DPP_MIRROR>(v);
+  return lane_u64(v, 0) + lane_u64(v, 16) + lane_u64(v, 32) + lane_u64(v, 48);
 }
 
 // (value, index) maximum with the lowest index winning ties; NaN never wins.
@@ -119,6 +181,94 @@ __device__ __forceinline__ ArgMax wave_argmax(ArgMax a) {
   return a;
 }
 constexpr int ARG_NONE = 0x7fffffff;
+
+// ---------------------------------------------------------------------------
+// Cross-block hand-off without fences.  On this part an agent-scope fence is a
+// whole-L2 writeback + invalidate, which stalls every streaming wave on the
+// die.  Data that another block of the same launch will read is therefore
+// written and read with agent-scope relaxed atomics, which compile to plain
+// vector loads/stores carrying the device-coherence bit (sc1): they bypass the
+// die-local caches without flushing them.  A block that wrote such data waits
+// for its stores to complete (s_waitcnt) before bumping an arrival counter; the
+// block that sees the final count reads everyone's data with sc1 loads.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void st_coh(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coh(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh_u64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_coh_u64(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh_i32(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_coh_i32(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// 16-byte coherent load of base + byte offset `off` (base must be the same for the
+// whole wave: it becomes a buffer descriptor; `off` < 2^31).  buffer_load_dwordx4
+// with the device-coherence bit.
+__device__ __forceinline__ float4 ld_coh4(const void* base, uint32_t off) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16));
+}
+__device__ __forceinline__ void st_coh4(float* p, float4 v) {
+  uint64_t* q = reinterpret_cast<uint64_t*>(p);
+  st_coh_u64(q, __builtin_bit_cast(uint64_t, make_float2(v.x, v.y)));
+  st_coh_u64(q + 1, __builtin_bit_cast(uint64_t, make_float2(v.z, v.w)));
+}
+
+// Every thread of the block calls this after its st_coh stores.  Returns true in
+// exactly one of the `expected` blocks sharing `counter`, after all of them have
+// arrived; that block resets the counter to zero for the next use.
+__device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned expected) {
+  __shared__ int s_last;
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned old =
+        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = old == expected - 1;
+    if (s_last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  return s_last != 0;
+}
+
+// Two-level form for thousands of arrivals: blocks of group g = id % ngroups
+// count on their own counter (counters 64 bytes apart); the last of each group
+// counts on the top counter.  counters: [ngroups + 1] x 16 words.
+__device__ __forceinline__ bool arrive_last2(unsigned* counters, unsigned id, unsigned total,
+                                             unsigned ngroups) {
+  __shared__ int s_last;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (ngroups > total) ngroups = total;
+    const unsigned g = id % ngroups;
+    const unsigned gsize = total / ngroups + (g < total % ngroups ? 1u : 0u);
+    unsigned* gc = counters + 16 * g;
+    unsigned* top = counters + 16 * ngroups;
+    int last = 0;
+    if (__hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gsize - 1) {
+      __hip_atomic_store(gc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ngroups - 1) {
+        __hip_atomic_store(top, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = 1;
+      }
+    }
+    s_last = last;
+  }
+  __syncthreads();
+  return s_last != 0;
+}
 
 // exact integer weight of an fp32 probability: floor(p * 2^52); <= 0 or NaN -> 0
 __device__ __forceinline__ uint64_t prob_weight(float p) {

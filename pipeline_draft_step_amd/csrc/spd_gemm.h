@@ -4,33 +4,38 @@
 // Work split: a workgroup (4 waves) owns an N-block of 64*NT weight rows and one
 // of S equal K-slices; each wave owns 16*NT rows.  The X slice (rows of the
 // M-tile) is staged in LDS by an input functor `In` that may fuse a gather or a
-// normalisation; W fragments go straight from global memory to the MFMA B
-// operand, double-buffered so that a full unrolled group of loads is always in
-// flight.  With S == 1 the block runs the epilogue functor `Epi` on its own
-// tile.  With S > 1 it writes an fp32 partial tile and a second, small kernel
-// sums the S partials in fixed order and runs the epilogue: cross-block
-// reductions happen at kernel boundaries only (a device-scope fence per block
-// costs far more than a launch on this multi-die part).  Results are
-// deterministic for a given launch shape.
+// normalisation.  bf16 W is read in groups of 8 k-steps as 4-row x 256-byte
+// load instructions (the pattern HBM streams fastest) and reordered into MFMA B
+// fragments through a small wave-private LDS buffer; fp32 W goes straight from
+// global memory to the MFMA operand.  Either way the next group's loads are in
+// flight while the current one is multiplied.  With S == 1 the block runs the epilogue functor `Epi` on its own
+// tile.  With S > 1 every block writes an fp32 partial tile with coherent (sc1)
+// stores and counts itself in; the last of the S blocks of an (N-block, M-tile)
+// sums the partials in fixed split order and runs the epilogue (no fences, see
+// spd_common.h).  Results are deterministic for a given launch shape.
 #pragma once
+
+#include <algorithm>
+#include <type_traits>
 
 #include "spd_common.h"
 
 namespace spd {
 
 #ifndef SPD_GEMM_UNROLL
-#define SPD_GEMM_UNROLL 8     // k-steps of weight loads in flight per wave (double-buffered)
-#endif
-#ifndef SPD_GEMM_TARGET
-#define SPD_GEMM_TARGET 1024  // blocks a split-K launch aims for
-#endif
-#ifndef SPD_GEMM_MIN_STEPS
-#define SPD_GEMM_MIN_STEPS 8  // minimum k-steps per split
+#define SPD_GEMM_UNROLL 8  // fp32 weights: k-steps of loads in flight per wave (double-buffered)
 #endif
 
 constexpr int GEMM_THREADS = 256;
 constexpr int GEMM_WAVES = 4;
 constexpr int GEMM_UNROLL = SPD_GEMM_UNROLL;
+// bf16 weight groups: 8 k-steps (512 bytes of each row) per group, fetched as 8
+// load instructions that each cover 4 rows x 256 contiguous bytes.  Four of them
+// at a time pass through a wave-private LDS buffer (1 KB + 64 B pad each, which
+// makes the fragment reads bank-conflict free) to reach the MFMA B layout.
+constexpr int WG_STEPS = 8;
+constexpr int TB_STRIDE = 1024 + 64;
+constexpr int TB_WAVE = 4 * TB_STRIDE;
 
 struct GemmShape {
   const void* W;
@@ -40,6 +45,9 @@ struct GemmShape {
   int ldx;      // LDS row pitch of the staged X slice (elements)
   float* part;  // [S][M][N] partials (S > 1)
   int nblocks;
+  unsigned* counters;  // [mtiles][nblocks] arrival counters (S > 1), zero between uses
+  int x_bytes;         // dynamic LDS: staged X slice (hi + lo), aliased by the
+  int ytile_bytes;     // fp32 result tile; the transpose buffers follow both
 };
 
 // Row of W that local column c (0 .. 64*NT-1) of N-block nb maps to.
@@ -75,16 +83,11 @@ struct XStage {
   // four consecutive k (k % 4 == 0)
   __device__ __forceinline__ void put4(int m, int k, const float (&v)[4]) const {
     if constexpr (sizeof(WT) == 2) {
-      bf16 h[4], l[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        h[e] = f2bf(v[e]);
-        l[e] = f2bf(v[e] - bf2f(h[e]));
-      }
-      *reinterpret_cast<uint2*>(hi + m * ldx + k) =
-          make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
-      *reinterpret_cast<uint2*>(lo + m * ldx + k) =
-          make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
+      const uint32_t h0 = pack2_bf16(v[0], v[1]), h1 = pack2_bf16(v[2], v[3]);
+      const uint32_t l0 = pack2_bf16(v[0] - __uint_as_float(h0 << 16), v[1] - __uint_as_float(h0 & 0xffff0000u));
+      const uint32_t l1 = pack2_bf16(v[2] - __uint_as_float(h1 << 16), v[3] - __uint_as_float(h1 & 0xffff0000u));
+      *reinterpret_cast<uint2*>(hi + m * ldx + k) = make_uint2(h0, h1);
+      *reinterpret_cast<uint2*>(lo + m * ldx + k) = make_uint2(l0, l1);
     } else {
       *reinterpret_cast<float4*>(hi + m * ldx + k) = make_float4(v[0], v[1], v[2], v[3]);
     }
@@ -143,28 +146,11 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_skinny_kernel(GemmShape g, 
   const int lr = lane & 15;
   const int lg = lane >> 4;
   const int nst = st1 - st0;
-
-  // this wave's weight rows: local columns wave*16*NT + 16*u + lr
-  const WT* wp[NT];
-  bool wv[NT];
-#pragma unroll
-  for (int u = 0; u < NT; ++u) {
-    const int row = rmap.template row<NT>(nb, wave * 16 * NT + 16 * u + lr);
-    wv[u] = row < g.N;
-    wp[u] = reinterpret_cast<const WT*>(g.W) + (size_t)(wv[u] ? row : 0) * g.K + k0 + lg * F::KPL;
-  }
-  // the first group of weight loads goes out before the X slice is staged
-  frag cur[U][NT], nxt[U][NT];
-#pragma unroll
-  for (int i = 0; i < U; ++i)
-#pragma unroll
-    for (int u = 0; u < NT; ++u) cur[i][u] = i < nst ? F::load(wp[u] + i * F::KSTEP) : F::zero();
+  SPD_MARK(0);
 
   WT* xs = reinterpret_cast<WT*>(smem);
-  WT* xs_lo = xs + (size_t)min(TR, g.M) * g.ldx;
-  in.stage(XStage<WT>{xs, xs_lo, g.ldx}, m0, Mt, k0, kw, nb, s, S);
-  __syncthreads();
-
+  const int xrows = min(TR, g.M);
+  WT* xs_lo = xs + (size_t)xrows * g.ldx;
   f32x4 acc[MT][NT];
 #pragma unroll
   for (int t = 0; t < MT; ++t)
@@ -175,42 +161,148 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_skinny_kernel(GemmShape g, 
   for (int t = 0; t < MT; ++t) xp[t] = xs + min(16 * t + lr, Mt - 1) * g.ldx + lg * F::KPL;
   const ptrdiff_t lo_off = xs_lo - xs;
 
-  for (int st = 0; st < nst; st += U) {
-    const int nxt0 = st + U;
-    if (nxt0 < nst) {
+  if constexpr (SPLIT) {
+    // rows of load instruction i (q = i % 4): local rows 16u + 4q + lane % 4; this
+    // lane's 16 bytes sit at element 8 * (lane / 4) of the instruction's 128-element span
+    const WT* wq[NT][4];
 #pragma unroll
-      for (int i = 0; i < U; ++i)
+    for (int u = 0; u < NT; ++u)
 #pragma unroll
-        for (int u = 0; u < NT; ++u)
-          nxt[i][u] = nxt0 + i < nst ? F::load(wp[u] + (nxt0 + i) * F::KSTEP) : F::zero();
-    }
-    __builtin_amdgcn_sched_barrier(0);
+      for (int q = 0; q < 4; ++q) {
+        const int row = rmap.template row<NT>(nb, wave * 16 * NT + 16 * u + 4 * q + (lane & 3));
+        wq[u][q] = reinterpret_cast<const WT*>(g.W) + (size_t)(row < g.N ? row : 0) * g.K;
+      }
+    const int ksub = lane >> 4;          // k-step of this lane's chunk inside a half group
+    const int loff = k0 + 8 * (lane >> 2);  // this lane's element offset in the row
+    // X is staged before the first weight loads go out: a wave's loads complete in
+    // issue order, so staging behind a weight group would wait for all of it.
+    SPD_MARK(1);
+    in.stage(XStage<WT>{xs, xs_lo, g.ldx}, m0, Mt, k0, kw, nb, s, S);
+    SPD_MARK(7);
+    // Two register buffers with fixed roles (A: even groups, B: odd groups), so
+    // that consuming one never waits for the loads of the other.  Loads are
+    // unconditional (a conditional load becomes a branch whose join waits for
+    // every outstanding load): chunks past the slice read the first element of
+    // the row instead; they only feed k-steps that are never multiplied, and rows
+    // past N (clamped to row 0) only feed columns that are never stored.
+    frag bufA[NT][WG_STEPS], bufB[NT][WG_STEPS];
+    auto issue = [&](frag (&d)[NT][WG_STEPS], int st) {
 #pragma unroll
-    for (int i = 0; i < U; ++i) {
-      if (st + i < nst) {
+      for (int u = 0; u < NT; ++u)
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-          const frag af = F::load(xp[t] + (st + i) * F::KSTEP);
+        for (int i = 0; i < WG_STEPS; ++i) {
+          const int h = i >> 2, q = i & 3;
+          d[u][i] = F::load(wq[u][q] + (st + 4 * h + ksub < nst ? loff + st * F::KSTEP + 128 * h : 0));
+        }
+    };
+    issue(bufA, 0);
+    __syncthreads();
+    SPD_MARK(2);
+    unsigned char* tb = reinterpret_cast<unsigned char*>(xs_lo + (size_t)xrows * g.ldx) +
+                        (size_t)(max(g.ytile_bytes - g.x_bytes, 0)) + wave * TB_WAVE;
+    const int rdb = (lr >> 2) * TB_STRIDE + 16 * ((lr & 3) + 4 * lg);
+    // multiply one group; FULL: all WG_STEPS k-steps are inside the slice
+    auto consume = [&](const frag (&c)[NT][WG_STEPS], int st, auto full) {
+      constexpr bool FULL = decltype(full)::value;
 #pragma unroll
-          for (int u = 0; u < NT; ++u) acc[t][u] = F::mma(af, cur[i][u], acc[t][u]);
-          if constexpr (SPLIT) {
-            const frag al = F::load(xp[t] + lo_off + (st + i) * F::KSTEP);
+      for (int u = 0; u < NT; ++u)
 #pragma unroll
-            for (int u = 0; u < NT; ++u) acc[t][u] = F::mma(al, cur[i][u], acc[t][u]);
+        for (int h = 0; h < 2; ++h) {
+          if (!FULL && st + 4 * h >= nst) continue;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<frag*>(tb + j * TB_STRIDE + 16 * lane) = c[u][4 * h + j];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int ks = st + 4 * h + j;
+            if (FULL || ks < nst) {
+              const frag b = *reinterpret_cast<const frag*>(tb + rdb + 256 * j);
+#pragma unroll
+              for (int t = 0; t < MT; ++t) {
+                const frag af = F::load(xp[t] + ks * F::KSTEP);
+                const frag al = F::load(xp[t] + lo_off + ks * F::KSTEP);
+                acc[t][u] = F::mma(af, b, acc[t][u]);
+                acc[t][u] = F::mma(al, b, acc[t][u]);
+              }
+            }
           }
         }
-      }
+    };
+    // Main loop over pairs of full groups with unconditional issues, so that every
+    // path into a wait has the same loads outstanding (the wait counts are taken
+    // over all paths); the last one or two groups follow outside the loop.
+    const int ng = (nst + WG_STEPS - 1) / WG_STEPS;
+    int gi = 0;
+    for (; gi + 2 < ng; gi += 2) {
+      issue(bufB, (gi + 1) * WG_STEPS);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(bufA, gi * WG_STEPS, std::true_type{});
+      __builtin_amdgcn_sched_barrier(0);
+      issue(bufA, (gi + 2) * WG_STEPS);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(bufB, (gi + 1) * WG_STEPS, std::true_type{});
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
+    if (gi + 1 < ng) {
+      issue(bufB, (gi + 1) * WG_STEPS);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(bufA, gi * WG_STEPS, std::true_type{});
+      __builtin_amdgcn_sched_barrier(0);
+      consume(bufB, (gi + 1) * WG_STEPS, std::false_type{});
+    } else if (gi < ng) {
+      consume(bufA, gi * WG_STEPS, std::false_type{});
+    }
+  } else {
+    // fp32 weights: fragments straight from global memory in the MFMA layout
+    const WT* wp[NT];
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+      const int row = rmap.template row<NT>(nb, wave * 16 * NT + 16 * u + lr);
+      wp[u] = reinterpret_cast<const WT*>(g.W) + (size_t)(row < g.N ? row : 0) * g.K + k0 + lg * F::KPL;
+    }
+    frag cur[U][NT], nxt[U][NT];
 #pragma unroll
     for (int i = 0; i < U; ++i)
 #pragma unroll
-      for (int u = 0; u < NT; ++u) cur[i][u] = nxt[i][u];
+      for (int u = 0; u < NT; ++u) cur[i][u] = F::load(wp[u] + (i < nst ? i * F::KSTEP : 0));
+    SPD_MARK(1);
+    in.stage(XStage<WT>{xs, xs_lo, g.ldx}, m0, Mt, k0, kw, nb, s, S);
+    __syncthreads();
+    SPD_MARK(2);
+    for (int st = 0; st < nst; st += U) {
+      const int nxt0 = st + U;
+      if (nxt0 < nst) {
+#pragma unroll
+        for (int i = 0; i < U; ++i)
+#pragma unroll
+          for (int u = 0; u < NT; ++u)
+            nxt[i][u] = F::load(wp[u] + (nxt0 + i < nst ? (nxt0 + i) * F::KSTEP : 0));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        if (st + i < nst) {
+#pragma unroll
+          for (int t = 0; t < MT; ++t) {
+            const frag af = F::load(xp[t] + (st + i) * F::KSTEP);
+#pragma unroll
+            for (int u = 0; u < NT; ++u) acc[t][u] = F::mma(af, cur[i][u], acc[t][u]);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < U; ++i)
+#pragma unroll
+        for (int u = 0; u < NT; ++u) cur[i][u] = nxt[i][u];
+    }
   }
 
+  SPD_MARK(3);
   // lane holds D[16t + 4*lg + i][16u + lr] of this wave
+  float (*ytile)[TC + 1] = reinterpret_cast<float (*)[TC + 1]>(smem);  // aliases the X slice
   if (S == 1) {
-    __shared__ float ytile[TR][TC + 1];
+    __syncthreads();  // every wave is done reading X
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
@@ -218,86 +310,148 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_skinny_kernel(GemmShape g, 
 #pragma unroll
         for (int i = 0; i < 4; ++i) ytile[16 * t + 4 * lg + i][wave * 16 * NT + 16 * u + lr] = acc[t][u][i];
     __syncthreads();
+    SPD_MARK(5);
     epi.template run<MT, NT>(TileY<TC>{ytile}, nb, m0, Mt, rmap);
+    SPD_MARK(6);
     return;
   }
 #pragma unroll
   for (int t = 0; t < MT; ++t)
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
-      if (!wv[u]) continue;
       const int row = rmap.template row<NT>(nb, wave * 16 * NT + 16 * u + lr);
+      if (row >= g.N) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = 16 * t + 4 * lg + i;
-        if (m < Mt) g.part[((size_t)s * g.M + m0 + m) * g.N + row] = acc[t][u][i];
+        if (m < Mt) st_coh(g.part + ((size_t)s * g.M + m0 + m) * g.N + row, acc[t][u][i]);
       }
     }
-}
-
-// Sum of the S partial tiles of one (N-block, M-tile) into LDS (fixed order over
-// the splits, all loads of a split in flight together), then the epilogue.
-template <int MT, int NT, typename Epi, typename RowMap>
-__global__ __launch_bounds__(GEMM_THREADS) void gemm_finish_kernel(GemmShape g, Epi epi, RowMap rmap) {
-  constexpr int TR = 16 * MT, TC = 64 * NT;
-  constexpr int PER = TR * TC / GEMM_THREADS;  // tile entries per thread
-  __shared__ float ytile[TR][TC + 1];
-  const int nb = blockIdx.x, mt = blockIdx.y;
-  const int m0 = mt * TR;
-  const int Mt = min(TR, g.M - m0);
-  const float* ptr[PER];
-  bool ok[PER];
-  float acc[PER];
+  if (!arrive_last(g.counters + mt * g.nblocks + nb, (unsigned)S)) {
+    SPD_MARK(4);
+    return;
+  }
+  SPD_MARK(4);
+  // last block of this tile: sum the S partials (fixed order) into LDS.  Each
+  // thread owns 4 consecutive columns of PER4 rows; 16 partial loads of every
+  // element are in flight at once.
+  constexpr int C4 = TC / 4;
+  constexpr int PER4 = TR * C4 / GEMM_THREADS;
+  uint32_t off[PER4];
+  bool ok[PER4];
+  float4 sum[PER4];
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
+  for (int j = 0; j < PER4; ++j) {
     const int e = threadIdx.x + GEMM_THREADS * j;
-    const int m = e / TC, c = e - m * TC;
+    const int m = e / C4, c = (e - m * C4) * 4;
     const int row = rmap.template row<NT>(nb, c);
     ok[j] = m < Mt && row < g.N;
-    ptr[j] = g.part + (size_t)(m0 + (ok[j] ? m : 0)) * g.N + (ok[j] ? row : 0);
-    acc[j] = 0.f;
+    off[j] = (uint32_t)(((size_t)(m0 + (ok[j] ? m : 0)) * g.N + (ok[j] ? row : 0)) * 4);
+    sum[j] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  const size_t stride = (size_t)g.M * g.N;
-#pragma unroll 2
-  for (int q = 0; q < g.S; ++q) {
-    float v[PER];
+  const uint32_t stride = (uint32_t)((size_t)g.M * g.N * 4);
+  constexpr int QB = 16 / PER4 > 0 ? 16 / PER4 : 1;
+  for (int q0 = 0; q0 < S; q0 += QB) {
+    float4 v[QB][PER4];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) v[j] = ok[j] ? ptr[j][q * stride] : 0.f;
+    for (int q = 0; q < QB; ++q)
 #pragma unroll
-    for (int j = 0; j < PER; ++j) acc[j] += v[j];
+      for (int j = 0; j < PER4; ++j)
+        v[q][j] = (q0 + q < S && ok[j]) ? ld_coh4(g.part, off[j] + (uint32_t)(q0 + q) * stride)
+                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int q = 0; q < QB; ++q)
+#pragma unroll
+      for (int j = 0; j < PER4; ++j) {
+        sum[j].x += v[q][j].x;
+        sum[j].y += v[q][j].y;
+        sum[j].z += v[q][j].z;
+        sum[j].w += v[q][j].w;
+      }
   }
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
+  for (int j = 0; j < PER4; ++j) {
     const int e = threadIdx.x + GEMM_THREADS * j;
-    ytile[e / TC][e % TC] = acc[j];
+    const int m = e / C4, c = (e - m * C4) * 4;
+    ytile[m][c] = sum[j].x;
+    ytile[m][c + 1] = sum[j].y;
+    ytile[m][c + 2] = sum[j].z;
+    ytile[m][c + 3] = sum[j].w;
   }
   __syncthreads();
+  SPD_MARK(5);
   epi.template run<MT, NT>(TileY<TC>{ytile}, nb, m0, Mt, rmap);
+  SPD_MARK(6);
 }
 
 // ---------------------------------------------------------------------------
 // Input functors: stage X[m0 .. m0+Mt)[k0 .. k0+kw) into LDS.
 // ---------------------------------------------------------------------------
 
-// X given (float or bf16 activations)
+// Staging layout shared by the input functors: wave w stages rows w, w + 4, ...
+// of the M-tile (at most STAGE_ROWS), lane l the 4-column groups l, l + 64, ... of
+// each of them.  A lane's items are handled in batches of STAGE_BATCH whose loads
+// are all issued before any result is used: with HBM saturated by the weight
+// stream every dependent round trip costs microseconds.
+constexpr int STAGE_BATCH = 12;
+constexpr int STAGE_ROWS = 8;
+
+struct StageIdx {
+  int wave, lane, per_row, n;
+  __device__ __forceinline__ StageIdx(int Mt, int kv) {
+    wave = threadIdx.x >> 6;
+    lane = threadIdx.x & 63;
+    per_row = (kv + WAVE - 1) / WAVE;
+    const int nr = (Mt - wave + GEMM_WAVES - 1) / GEMM_WAVES;
+    n = nr > 0 ? nr * per_row : 0;
+  }
+  // item -> (row slot j of this wave, tile row mm, column group u)
+  __device__ __forceinline__ void at(int it, int& j, int& mm, int& u) const {
+    j = it / per_row;
+    mm = wave + GEMM_WAVES * j;
+    u = lane + WAVE * (it - j * per_row);
+  }
+};
+
+__device__ __forceinline__ float4 ldg4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 ldg4(const bf16* p) {
+  const uint2 a = *reinterpret_cast<const uint2*>(p);
+  return make_float4(bf2f((bf16)(a.x & 0xffff)), bf2f((bf16)(a.x >> 16)), bf2f((bf16)(a.y & 0xffff)),
+                     bf2f((bf16)(a.y >> 16)));
+}
+
+// X given (float activations)
 template <typename WT, typename XT>
 struct InAct {
   const XT* X;
   int K;
   __device__ void stage(const XStage<WT>& xs, int m0, int Mt, int k0, int kw, int, int, int) const {
     const int kv = kw >> 2;
-#pragma unroll 4
-    for (int e = threadIdx.x; e < Mt * kv; e += GEMM_THREADS) {
-      const int m = e / kv, k = (e - m * kv) << 2;
-      float v[4];
-      load4(X + (size_t)(m0 + m) * K + k0 + k, v);
-      xs.put4(m, k, v);
+    const StageIdx ix(Mt, kv);
+    for (int b0 = 0; b0 < ix.n; b0 += STAGE_BATCH) {
+      float4 v[STAGE_BATCH];
+#pragma unroll
+      for (int i = 0; i < STAGE_BATCH; ++i) {
+        int j, mm, u;
+        ix.at(b0 + i, j, mm, u);
+        const bool ok = b0 + i < ix.n && u < kv;
+        v[i] = ldg4(X + (ok ? (size_t)(m0 + mm) * K + k0 + 4 * u : (size_t)m0 * K + k0));
+      }
+#pragma unroll
+      for (int i = 0; i < STAGE_BATCH; ++i) {
+        int j, mm, u;
+        ix.at(b0 + i, j, mm, u);
+        if (b0 + i < ix.n && u < kv) {
+          const float t[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+          xs.put4(mm, 4 * u, t);
+        }
+      }
     }
   }
 };
 
 // X = RMSNorm(H) * gamma, with the row statistics summed from per-block
-// partial sums of squares ss[p][row] written by the producer of H.
+// partial sums of squares ss[p][row] (P <= 128 partials) written by the producer of H.
 template <typename WT>
 struct InNorm {
   const float* H;
@@ -308,25 +462,52 @@ struct InNorm {
   int K;
   float eps;
   __device__ void stage(const XStage<WT>& xs, int m0, int Mt, int k0, int kw, int, int, int) const {
-    __shared__ float inv[32];
-    const int wave = threadIdx.x >> 6;
-    for (int m = wave; m < Mt; m += GEMM_WAVES) {
-      const float* sp = ss + m0 + m;
-      const float t = wave_sum_of(P, [&](int p) { return sp[(size_t)p * M]; });
-      if ((threadIdx.x & 63) == 0) inv[m] = 1.0f / sqrtf(t / (float)K + eps);
-    }
-    __syncthreads();
     const int kv = kw >> 2;
-#pragma unroll 4
-    for (int e = threadIdx.x; e < Mt * kv; e += GEMM_THREADS) {
-      const int m = e / kv, k = (e - m * kv) << 2;
-      float v[4], gm[4];
-      load4(H + (size_t)(m0 + m) * K + k0 + k, v);
-      load4(gamma + k0 + k, gm);
-      const float iv = inv[m];
+    const StageIdx ix(Mt, kv);
+    float sp[STAGE_ROWS][2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = v[i] * iv * gm[i];
-      xs.put4(m, k, v);
+    for (int j = 0; j < STAGE_ROWS; ++j) {
+      const int mm = ix.wave + GEMM_WAVES * j;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int p = ix.lane + WAVE * h;
+        const bool ok = mm < Mt && p < P;
+        const float t = ss[ok ? (size_t)p * M + m0 + mm : (size_t)m0];
+        sp[j][h] = ok ? t : 0.f;
+      }
+    }
+    // row scales go through LDS: a register array indexed by the (wave-uniform) row
+    // slot would be placed in scratch, whose loads wait for every outstanding load
+    __shared__ float s_inv[GEMM_WAVES][STAGE_ROWS];
+    for (int b0 = 0; b0 < ix.n; b0 += STAGE_BATCH) {
+      float4 v[STAGE_BATCH], gm[STAGE_BATCH];
+#pragma unroll
+      for (int i = 0; i < STAGE_BATCH; ++i) {
+        int j, mm, u;
+        ix.at(b0 + i, j, mm, u);
+        const bool ok = b0 + i < ix.n && u < kv;
+        v[i] = ldg4(H + (ok ? (size_t)(m0 + mm) * K + k0 + 4 * u : (size_t)m0 * K + k0));
+        gm[i] = ldg4(gamma + k0 + (ok ? 4 * u : 0));
+      }
+      if (b0 == 0) {
+#pragma unroll
+        for (int j = 0; j < STAGE_ROWS; ++j) {
+          const float t = 1.0f / sqrtf(wave_sum(sp[j][0] + sp[j][1]) / (float)K + eps);
+          if (ix.lane == 0) s_inv[ix.wave][j] = t;
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
+#pragma unroll
+      for (int i = 0; i < STAGE_BATCH; ++i) {
+        int j, mm, u;
+        ix.at(b0 + i, j, mm, u);
+        if (b0 + i < ix.n && u < kv) {
+          const float iv = s_inv[ix.wave][j];
+          const float t[4] = {v[i].x * iv * gm[i].x, v[i].y * iv * gm[i].y, v[i].z * iv * gm[i].z,
+                              v[i].w * iv * gm[i].w};
+          xs.put4(mm, 4 * u, t);
+        }
+      }
     }
   }
 };
@@ -336,11 +517,21 @@ struct InNorm {
 // ---------------------------------------------------------------------------
 
 // h[row][col] += y; ss_out[nb][row] = sum over the block's columns of h^2.
+// With `final_`, the epilogue blocks of the M-tile holding row M-1 count in and
+// the last one writes h_last = RMSNorm(h[M-1]) * final_norm (h and the sums are
+// stored coherently so that block can read them).
+template <typename WT>
 struct EpiResid {
   float* h;
   float* ss_out;
   int N;  // = d
   int M;
+  int final_;
+  const WT* final_norm;
+  float* h_last;
+  unsigned* ctr_final;
+  int nblocks;
+  float eps;
   template <int MT, int NT, typename Y, typename RM>
   __device__ void run(const Y& y, int nb, int m0, int Mt, const RM&) const {
     constexpr int R = 4 * MT;  // rows per wave at most
@@ -352,7 +543,7 @@ struct EpiResid {
 #pragma unroll
       for (int u = 0; u < NT; ++u) {
         const int col = nb * 64 * NT + lane + 64 * u;
-        hv[r][u] = (m < Mt && col < N) ? h[(size_t)(m0 + m) * N + col] : 0.f;
+        hv[r][u] = h[(m < Mt && col < N) ? (size_t)(m0 + m) * N + col : (size_t)m0 * N];
       }
     }
 #pragma unroll
@@ -366,13 +557,26 @@ struct EpiResid {
         const int col = nb * 64 * NT + c;
         if (col < N) {
           const float v = hv[r][u] + y(m, c);
-          h[(size_t)(m0 + m) * N + col] = v;
+          st_coh(h + (size_t)(m0 + m) * N + col, v);
           sq += v * v;
         }
       }
       sq = wave_sum(sq);
-      if (lane == 0) ss_out[(size_t)nb * M + m0 + m] = sq;
+      if (lane == 0) st_coh(ss_out + (size_t)nb * M + m0 + m, sq);
     }
+    if (!final_ || m0 + Mt != M) return;
+    if (!arrive_last(ctr_final, (unsigned)nblocks)) return;
+    __shared__ float s_inv;
+    if (threadIdx.x < 64) {
+      float t = 0.f;
+      for (int p = threadIdx.x; p < nblocks; p += 64) t += ld_coh(ss_out + (size_t)p * M + M - 1);
+      t = wave_sum(t);
+      if (threadIdx.x == 0) s_inv = 1.0f / sqrtf(t / (float)N + eps);
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int c = threadIdx.x; c < N; c += GEMM_THREADS)
+      h_last[c] = ld_coh(h + (size_t)(M - 1) * N + c) * s_inv * to_f<WT>(final_norm[c]);
   }
 };
 
@@ -397,33 +601,37 @@ struct EpiSilu {
 // Host-side launch planning
 // ---------------------------------------------------------------------------
 struct GemmPlan {
-  int MT, NT, S, nblocks, mtiles, nsteps, ldx;
+  int MT, NT, S, nblocks, mtiles, nsteps, ldx, x_bytes, ytile_bytes;
   size_t lds_bytes;
 };
 
-// Choose split-K so that the grid has about `target` blocks, each with at least
-// `min_steps` k-steps, and the staged slice fits `lds_cap` bytes.
-inline GemmPlan plan_gemm(int N, int K, int M, int kstep, int esize, int NT, int target = 1024,
-                          int min_steps = 8, size_t lds_cap = 40 * 1024) {
+// Choose split-K so that the grid has at most `target` blocks (or one split), each
+// with at least `min_steps` k-steps, and the block's dynamic LDS fits `lds_cap`.
+inline GemmPlan plan_gemm(int N, int K, int M, int kstep, int esize, int NT, int target = 512,
+                          int min_steps = 8, size_t lds_cap = 62 * 1024) {
   GemmPlan p;
   p.MT = M > 16 ? 2 : 1;
   p.NT = NT;
   p.nblocks = (N + 64 * NT - 1) / (64 * NT);
   p.mtiles = (M + 16 * p.MT - 1) / (16 * p.MT);
   p.nsteps = K / kstep;
-  int S = (target + p.nblocks * p.mtiles - 1) / (p.nblocks * p.mtiles);
+  int S = target / (p.nblocks * p.mtiles);  // the grid stays within `target` blocks
   int smax = p.nsteps / min_steps;
   if (smax < 1) smax = 1;
   if (S > smax) S = smax;
   if (S < 1) S = 1;
   const int rows = M < 16 * p.MT ? M : 16 * p.MT;  // rows actually staged
+  p.ytile_bytes = 16 * p.MT * (64 * NT + 1) * 4;
+  const size_t tb = esize == 2 ? (size_t)GEMM_WAVES * TB_WAVE : 0;
   for (;;) {
     const int steps = (p.nsteps + S - 1) / S;
     const int ldx = steps * kstep + 16 / esize * 2;  // +32 bytes of padding
-    const size_t lds = (size_t)rows * ldx * esize * (esize == 2 ? 2 : 1);  // bf16: hi + lo
+    const size_t xb = (size_t)rows * ldx * esize * (esize == 2 ? 2 : 1);  // bf16: hi + lo
+    const size_t lds = std::max(xb, (size_t)p.ytile_bytes) + tb;
     if (lds <= lds_cap || S >= p.nsteps) {
       p.S = S;
       p.ldx = ldx;
+      p.x_bytes = (int)xb;
       p.lds_bytes = lds;
       break;
     }

@@ -35,25 +35,23 @@ inline int check_config(const spd_config* c) {
   return SPD_OK;
 }
 
+constexpr int CTR_FINAL = SPD_WS_COUNTER_BYTES / 4 - 16;  // counter of a second-level arrival
+
 template <typename WT, int NT, typename In, typename Epi, typename RM>
 int launch_gemm(const GemmPlan& p, const GemmShape& g, const In& in, const Epi& epi, const RM& rm,
                 hipStream_t st) {
+  if ((size_t)p.mtiles * p.nblocks >= (size_t)CTR_FINAL) return SPD_E_UNSUPPORTED;
+  if ((size_t)p.S * g.M * g.N * 4 >= ((size_t)1 << 31)) return SPD_E_UNSUPPORTED;  // 32-bit offsets
+  GemmShape gs = g;
+  gs.x_bytes = p.x_bytes;
+  gs.ytile_bytes = p.ytile_bytes;
   dim3 grid(p.nblocks * p.S, p.mtiles);
   if (p.MT == 1)
     hipLaunchKernelGGL((gemm_skinny_kernel<WT, 1, NT, In, Epi, RM>), grid, dim3(GEMM_THREADS),
-                       p.lds_bytes, st, g, in, epi, rm);
+                       p.lds_bytes, st, gs, in, epi, rm);
   else
     hipLaunchKernelGGL((gemm_skinny_kernel<WT, 2, NT, In, Epi, RM>), grid, dim3(GEMM_THREADS),
-                       p.lds_bytes, st, g, in, epi, rm);
-  int rc = check_launch();
-  if (rc || p.S == 1) return rc;
-  dim3 fgrid(p.nblocks, p.mtiles);
-  if (p.MT == 1)
-    hipLaunchKernelGGL((gemm_finish_kernel<1, NT, Epi, RM>), fgrid, dim3(GEMM_THREADS), 0, st, g, epi,
-                       rm);
-  else
-    hipLaunchKernelGGL((gemm_finish_kernel<2, NT, Epi, RM>), fgrid, dim3(GEMM_THREADS), 0, st, g, epi,
-                       rm);
+                       p.lds_bytes, st, gs, in, epi, rm);
   return check_launch();
 }
 

@@ -267,7 +267,7 @@ __global__ __launch_bounds__(VER_THREADS) void verify_greedy_final_kernel(VerArg
 size_t verify_workspace(int B, int gamma, int V) {
   const size_t nch = (size_t)(V + VER_CHUNK - 1) / VER_CHUNK;
   const size_t per = std::max((size_t)16, (size_t)(gamma + 1) * sizeof(ArgMax));
-  return align256((size_t)B * nch * per);
+  return SPD_WS_COUNTER_BYTES + align256((size_t)B * nch * per);
 }
 
 }  // namespace spd
@@ -292,7 +292,7 @@ extern "C" int spd_verify(int32_t B, int32_t gamma, int32_t V, float temperature
   a.words = words;
   a.n_accept = n_accept;
   a.next_token = next_token;
-  a.part = ws;
+  a.part = static_cast<char*>(ws) + SPD_WS_COUNTER_BYTES;
   a.B = B;
   a.gamma = gamma;
   a.V = V;
