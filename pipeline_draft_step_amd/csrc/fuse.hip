@@ -159,7 +159,7 @@ static int fuse_impl(const spd_config* cfg, const void* hstore, int64_t T_cap, i
   char* w = static_cast<char*>(ws);
   float* xss = reinterpret_cast<float*>(w + p.off_xss);
 
-  GemmShape gs;
+  GemmShape gs{};
   gs.W = fc_w;
   gs.N = d;
   gs.K = m * d;

@@ -380,7 +380,7 @@ static int lm_impl(const spd_config* c, const void* w_lm, const float* h, int ro
     }
     rc = check_launch();
   } else {
-    GemmShape g;
+    GemmShape g{};
     g.W = w_lm;
     g.N = c->V;
     g.K = c->d;

@@ -28,13 +28,17 @@ constexpr int ATT_WAVES = 4;                    // waves per attention block
 constexpr int ATT_KC = ATT_SUB * ATT_WAVES;     // keys per block (one partial per row)
 constexpr int ATT_MAXCH = 128;                  // chunks per row: context up to 32768
 
-// h = g, and per-64-column partial sums of squares of every row
+// h = g, per-64-column partial sums of squares of every row, and the first QKV
+// GEMM's input g * attn_norm as an XSplit (its RMSNorm row scale comes from ss)
+template <typename WT>
 __global__ __launch_bounds__(64) void rows_init_kernel(const float* g, float* h, float* ss, int M,
-                                                       int d) {
+                                                       int d, XSplit<WT> xo, const WT* gamma) {
   const int nb = blockIdx.x, r = blockIdx.y, lane = threadIdx.x;
-  const size_t i = (size_t)r * d + nb * 64 + lane;
+  const int col = nb * 64 + lane;
+  const size_t i = (size_t)r * d + col;
   const float v = g[i];
   h[i] = v;
+  xo.put1(r, col, v * to_f<WT>(gamma[col]));
   const float s = wave_sum(v * v);
   if (lane == 0) ss[(size_t)nb * M + r] = s;
 }
@@ -109,7 +113,9 @@ struct AttnArgs {
   const void* vc;  // [Hkv][hd][T_cap]
   float* po;       // [Hkv][QR][nch][hd]
   float2* pml;     // [Hkv][QR][nch]  (chunk max, chunk sum of exp)
-  float* out;      // [M][Hq*hd] attention output
+  void* xh;        // attention output [M][Hq*hd] as the O projection's XSplit input
+  void* xl;
+  int xld;         // row stride of xh / xl (elements)
   unsigned* counters;  // [Hkv][nqt]
   int M, Hq, Hkv, pos0, nch, nqt;
   int64_t T_cap;
@@ -308,7 +314,8 @@ s_ = row16_sum(s_);
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int cc = j + 16 * i;
-      v[i] = cc < nv ? __builtin_bit_cast(float2, ld_coh_u64(ml + cc)) : make_float2(-INFINITY, 0.f);
+      const float2 t = __builtin_bit_cast(float2, ld_coh_u64(ml + (cc < nv ? cc : 0)));
+      v[i] = cc < nv ? t : make_float2(-INFINITY, 0.f);
     }
     float mmax = -INFINITY;
 #pragma unroll
@@ -340,7 +347,7 @@ L = row16_sum(L);
       float4 pv[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        pv[i] = c0 + i < nv ? ld_coh4(a.po, base + (uint32_t)((c0 + i) * HD * 4)) : make_float4(0.f, 0.f, 0.f, 0.f);
+        pv[i] = ld_coh4(a.po, base + (uint32_t)((c0 + i < nv ? c0 + i : 0) * HD * 4));
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float wgt = c0 + i < nv ? s_w[row][c0 + i] : 0.f;
@@ -351,8 +358,8 @@ L = row16_sum(L);
       }
     }
     const float il = 1.0f / s_L[row];
-    float* dst = a.out + (size_t)r * a.Hq * HD + (size_t)(h * G + qr % G) * HD + dim;
-    *reinterpret_cast<float4*>(dst) = make_float4(o.x * il, o.y * il, o.z * il, o.w * il);
+    const XSplit<WT> xo{static_cast<WT*>(a.xh), static_cast<WT*>(a.xl), a.xld};
+    xo.put4(r, (h * G + qr % G) * HD + dim, make_float4(o.x * il, o.y * il, o.z * il, o.w * il));
   }
   SPD_MARK(6);
 }
@@ -360,7 +367,8 @@ L = row16_sum(L);
 struct PdmPlan {
   GemmPlan qkv, o, gu, down;
   int nch, QR;
-  size_t off_h, off_ss, off_q, off_po, off_pml, off_attn, off_act, off_part, total;
+  size_t off_h, off_ss, off_q, off_po, off_pml, off_x0h, off_x0l, off_x1h, off_x1l, off_part, total;
+  int ld1;  // row stride of the second XSplit buffer
 };
 
 static PdmPlan plan_pdm(const spd_config* c, int M, int64_t T_cap) {
@@ -381,8 +389,12 @@ static PdmPlan plan_pdm(const spd_config* c, int M, int64_t T_cap) {
   p.off_q = take((size_t)M * c->Hq * c->hd * 4);
   p.off_po = take((size_t)c->Hkv * p.QR * p.nch * c->hd * 4);
   p.off_pml = take((size_t)c->Hkv * p.QR * p.nch * 8);
-  p.off_attn = take((size_t)M * c->Hq * c->hd * 4);
-  p.off_act = take((size_t)M * c->dff * 4);
+  // XSplit GEMM inputs: x0 feeds QKV and gate/up (width d), x1 feeds O and down
+  p.ld1 = std::max(c->Hq * c->hd, c->dff);
+  p.off_x0h = take((size_t)M * c->d * es);
+  p.off_x0l = take((size_t)M * c->d * es);
+  p.off_x1h = take((size_t)M * p.ld1 * es);
+  p.off_x1l = take((size_t)M * p.ld1 * es);
   size_t part = 0;
   const GemmPlan* gps[4] = {&p.qkv, &p.o, &p.gu, &p.down};
   const size_t Ns[4] = {(size_t)(c->Hq + 2 * c->Hkv) * c->hd, (size_t)c->d, (size_t)2 * c->dff,
@@ -399,8 +411,13 @@ size_t pdm_workspace(const spd_config* cfg, int M, int64_t T_cap) {
 }
 
 static GemmShape shape_of(const GemmPlan& gp, const void* W, int N, int K, int M, float* part,
-                          unsigned* ctr) {
-  GemmShape g;
+                          unsigned* ctr, const float* rs_ss = nullptr, int rs_P = 0, float eps = 0.f) {
+  GemmShape g{};
+  g.rs_ss = rs_ss;
+  g.rs_P = rs_P;
+  g.rs_M = M;
+  g.rs_K = K;
+  g.rs_eps = eps;
   g.W = W;
   g.N = N;
   g.K = K;
@@ -434,14 +451,17 @@ static int pdm_impl(const spd_config* c, const spd_layer_weights* layers, const 
   float* h = reinterpret_cast<float*>(w + p.off_h);
   float* ss = reinterpret_cast<float*>(w + p.off_ss);
   float* qb = reinterpret_cast<float*>(w + p.off_q);
-  float* attn = reinterpret_cast<float*>(w + p.off_attn);
-  float* act = reinterpret_cast<float*>(w + p.off_act);
   float* part = reinterpret_cast<float*>(w + p.off_part);
   unsigned* ctr = reinterpret_cast<unsigned*>(w);
   const int d = c->d, hd = c->hd, Hq = c->Hq, Hkv = c->Hkv, dff = c->dff;
   const int nq = (Hq + 2 * Hkv) * hd;
+  // XSplit buffers: x0 = input of QKV and gate/up, x1 = input of O and down
+  const XSplit<WT> x0{reinterpret_cast<WT*>(w + p.off_x0h), reinterpret_cast<WT*>(w + p.off_x0l), d};
+  const XSplit<WT> x1{reinterpret_cast<WT*>(w + p.off_x1h), reinterpret_cast<WT*>(w + p.off_x1l), p.ld1};
+  const XSplit<WT> none{nullptr, nullptr, 0};
 
-  hipLaunchKernelGGL(rows_init_kernel, dim3(d / 64, M), dim3(64), 0, st, g, h, ss, M, d);
+  hipLaunchKernelGGL((rows_init_kernel<WT>), dim3(d / 64, M), dim3(64), 0, st, g, h, ss, M, d, x0,
+                     static_cast<const WT*>(layers[0].attn_norm));
   int rc = check_launch();
   if (rc) return rc;
   int P = d / 64;  // partial count of ss
@@ -455,7 +475,9 @@ static int pdm_impl(const spd_config* c, const spd_layer_weights* layers, const 
   aa.Hkv = Hkv;
   aa.pos0 = pos0;
   aa.nch = (pos0 + M + ATT_KC - 1) / ATT_KC;
-  aa.out = attn;
+  aa.xh = x1.hi;
+  aa.xl = x1.lo;
+  aa.xld = p.ld1;
   aa.counters = ctr;
   aa.nqt = (p.QR + 15) / 16;
   aa.T_cap = T_cap;
@@ -465,16 +487,16 @@ static int pdm_impl(const spd_config* c, const spd_layer_weights* layers, const 
     const spd_layer_weights& lw = layers[l];
     WT* kc = static_cast<WT*>(k_cache) + (size_t)l * Hkv * T_cap * hd;
     WT* vc = static_cast<WT*>(v_cache) + (size_t)l * Hkv * hd * T_cap;
-    // QKV
+    // QKV: x0 = h * attn_norm, row scale = 1 / rms(h)
     {
-      InNorm<WT> in{h, static_cast<const WT*>(lw.attn_norm), ss, P, M, d, c->rms_eps};
+      InSplit<WT> in{x0.hi, x0.lo, d};
       EpiQKV<WT> epi{qb, kc, vc, static_cast<const WT*>(lw.q_norm), static_cast<const WT*>(lw.k_norm),
                      Hq, Hkv, hd, pos0, T_cap, c->rms_eps, c->rope_theta};
-      rc = launch_gemm<WT, 2>(p.qkv, shape_of(p.qkv, lw.wqkv, nq, d, M, part, ctr), in, epi,
-                              RowMapStd{}, st);
+      rc = launch_gemm<WT, 2>(p.qkv, shape_of(p.qkv, lw.wqkv, nq, d, M, part, ctr, ss, P, c->rms_eps),
+                              in, epi, RowMapStd{}, st);
       if (rc) return rc;
     }
-    // attention
+    // attention -> x1
     aa.kc = kc;
     aa.vc = vc;
     switch (hd) {
@@ -484,29 +506,32 @@ static int pdm_impl(const spd_config* c, const spd_layer_weights* layers, const 
       default: rc = launch_attention<WT, 128>(aa, st); break;
     }
     if (rc) return rc;
-    // O projection + residual
+    // O projection + residual; x0 = h * mlp_norm
     {
-      InAct<WT, float> in{attn, Hq * hd};
-      EpiResid<WT> epi{h, ss, d, M, 0, nullptr, nullptr, ctr + CTR_FINAL, p.o.nblocks, c->rms_eps};
+      InSplit<WT> in{x1.hi, x1.lo, p.ld1};
+      EpiResid<WT> epi{h, ss, d, M, 0, nullptr, nullptr, ctr + CTR_FINAL, p.o.nblocks, c->rms_eps,
+                       x0, static_cast<const WT*>(lw.mlp_norm)};
       rc = launch_gemm<WT, 1>(p.o, shape_of(p.o, lw.wo, d, Hq * hd, M, part, ctr), in, epi,
                               RowMapStd{}, st);
       if (rc) return rc;
       P = p.o.nblocks;
     }
-    // gate/up + silu*mul
+    // gate/up + silu*mul -> x1; row scale = 1 / rms(h)
     {
-      InNorm<WT> in{h, static_cast<const WT*>(lw.mlp_norm), ss, P, M, d, c->rms_eps};
-      EpiSilu epi{act, dff};
-      rc = launch_gemm<WT, 2>(p.gu, shape_of(p.gu, lw.w_gate_up, 2 * dff, d, M, part, ctr), in, epi,
-                              RowMapGateUp{dff}, st);
+      InSplit<WT> in{x0.hi, x0.lo, d};
+      EpiSilu<WT> epi{x1, dff};
+      rc = launch_gemm<WT, 2>(p.gu, shape_of(p.gu, lw.w_gate_up, 2 * dff, d, M, part, ctr, ss, P,
+                                             c->rms_eps),
+                              in, epi, RowMapGateUp{dff}, st);
       if (rc) return rc;
     }
-    // down + residual; after the last layer its epilogue also writes h_last
+    // down + residual; x0 = h * next attn_norm; after the last layer h_last
     {
-      InAct<WT, float> in{act, dff};
+      InSplit<WT> in{x1.hi, x1.lo, p.ld1};
       const bool last = l == c->Ls - 1;
       EpiResid<WT> epi{h, ss, d, M, last ? 1 : 0, static_cast<const WT*>(final_norm), h_last,
-                       ctr + CTR_FINAL, p.down.nblocks, c->rms_eps};
+                       ctr + CTR_FINAL, p.down.nblocks, c->rms_eps, last ? none : x0,
+                       last ? nullptr : static_cast<const WT*>(layers[l + 1].attn_norm)};
       rc = launch_gemm<WT, 1>(p.down, shape_of(p.down, lw.w_down, d, dff, M, part, ctr), in, epi,
                               RowMapStd{}, st);
       if (rc) return rc;
@@ -534,6 +559,7 @@ extern "C" int spd_pdm_step(const spd_config* cfg, const spd_layer_weights* laye
   const int hd = cfg->hd;
   if (hd != 16 && hd != 32 && hd != 64 && hd != 128) return SPD_E_UNSUPPORTED;
   if (cfg->d % 64 || cfg->dff % 64 || T_cap % 8) return SPD_E_UNSUPPORTED;
+  if (cfg->d > 8192) return SPD_E_UNSUPPORTED;  // row statistics come in <= 128 partial sums
   if (((int64_t)pos0 + M + ATT_KC - 1) / ATT_KC > ATT_MAXCH) return SPD_E_UNSUPPORTED;
   {
     const int G = cfg->Hq / cfg->Hkv;

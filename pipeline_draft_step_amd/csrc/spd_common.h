@@ -41,6 +41,7 @@ __device__ __forceinline__ float bf2f(bf16 v) { return __uint_as_float((uint32_t
 
 // float -> bfloat16, round to nearest even; NaN stays a quiet NaN.
 // fp32 -> bf16, round to nearest even (the hardware v_cvt_pk_bf16_f32)
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float spd_f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 spd_bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {

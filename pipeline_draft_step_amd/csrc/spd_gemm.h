@@ -48,6 +48,11 @@ struct GemmShape {
   unsigned* counters;  // [mtiles][nblocks] arrival counters (S > 1), zero between uses
   int x_bytes;         // dynamic LDS: staged X slice (hi + lo), aliased by the
   int ytile_bytes;     // fp32 result tile; the transpose buffers follow both
+  // optional per-row scale of the product: 1 / sqrt(sum_p rs_ss[p][row] / rs_K + rs_eps)
+  // (the RMSNorm of an input whose gamma the producer has already applied)
+  const float* rs_ss;  // [rs_P][rs_M] partial sums of squares, or nullptr (scale 1)
+  int rs_P, rs_M, rs_K;
+  float rs_eps;
 };
 
 // Row of W that local column c (0 .. 64*NT-1) of N-block nb maps to.
@@ -114,6 +119,49 @@ __device__ __forceinline__ float wave_sum_of(int n, const F& f) {
   return wave_sum(t);
 }
 
+// Stagers with kTwoPhase issue their loads (load) before the first weight group
+// and write LDS (store) afterwards; the others stage in one call.
+template <typename T, typename = void>
+struct TwoPhase : std::false_type {};
+template <typename T>
+struct TwoPhase<T, std::void_t<decltype(T::kTwoPhase)>> : std::bool_constant<T::kTwoPhase> {};
+
+// Row scales of the tile (see GemmShape::rs_ss): wave w owns rows w, w + 4, ...
+// (RW = 4 * MT of them); the partial sums are loaded first (load) and reduced
+// into s_rs (finish).
+template <int RW>
+struct RowScale {
+  float p[RW][2];
+  __device__ __forceinline__ void load(const GemmShape& g, int m0, int Mt) {
+    if (!g.rs_ss) return;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < RW; ++j) {
+      const int mm = wave + GEMM_WAVES * j;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int q = lane + WAVE * h;
+        const bool ok = mm < Mt && q < g.rs_P;
+        p[j][h] = g.rs_ss[ok ? (size_t)q * g.rs_M + m0 + mm : (size_t)m0];  // masked in finish
+      }
+    }
+  }
+  __device__ __forceinline__ void finish(const GemmShape& g, int Mt, float* s_rs) const {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < RW; ++j) {
+      const int mm = wave + GEMM_WAVES * j;
+      float v = 1.f;
+      if (g.rs_ss) {
+        const float a = (mm < Mt && lane < g.rs_P) ? p[j][0] : 0.f;
+        const float b = (mm < Mt && lane + WAVE < g.rs_P) ? p[j][1] : 0.f;
+        v = 1.0f / sqrtf(wave_sum(a + b) / (float)g.rs_K + g.rs_eps);
+      }
+      if (lane == 0) s_rs[mm] = v;
+    }
+  }
+};
+
 template <int TC>
 struct TileY {
   const float (*y)[TC + 1];
@@ -130,6 +178,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_skinny_kernel(GemmShape g, 
   constexpr bool SPLIT = sizeof(WT) == 2;
   constexpr int U = GEMM_UNROLL;
   extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ float s_rs[32];  // row scales of the tile
 
   const int S = g.S;
   const int nb = blockIdx.x / S;
@@ -174,11 +223,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_skinny_kernel(GemmShape g, 
       }
     const int ksub = lane >> 4;          // k-step of this lane's chunk inside a half group
     const int loff = k0 + 8 * (lane >> 2);  // this lane's element offset in the row
-    // X is staged before the first weight loads go out: a wave's loads complete in
-    // issue order, so staging behind a weight group would wait for all of it.
     SPD_MARK(1);
-    in.stage(XStage<WT>{xs, xs_lo, g.ldx}, m0, Mt, k0, kw, nb, s, S);
-    SPD_MARK(7);
     // Two register buffers with fixed roles (A: even groups, B: odd groups), so
     // that consuming one never waits for the loads of the other.  Loads are
     // unconditional (a conditional load becomes a branch whose join waits for
@@ -195,7 +240,55 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_skinny_kernel(GemmShape g, 
           d[u][i] = F::load(wq[u][q] + (st + 4 * h + ksub < nst ? loff + st * F::KSTEP + 128 * h : 0));
         }
     };
-    issue(bufA, 0);
+    // A wave's loads complete in issue order: the row-scale and X-slice loads go
+    // out before the first weight group, so waiting for them never waits for it.
+    RowScale<4 * MT> rsc;
+    rsc.load(g, m0, Mt);
+    const XStage<WT> xst{xs, xs_lo, g.ldx};
+    if constexpr (TwoPhase<In>::value) {
+      constexpr int SB = In::SB, CH = In::CH;
+      // round 0; program order is pinned: X loads, first weight group, LDS writes
+      // (native vectors: HIP's uint4 struct is copied with memcpy, which keeps the
+      // array out of registers)
+      {
+        u32x4 rh[SB], rl[SB];
+#pragma unroll
+        for (int i = 0; i < SB; ++i) {
+          int m, c;
+          bool ok;
+          In::chunk(0, i, Mt, kw, m, c, ok);
+          const size_t off = (size_t)(m0 + m) * in.K + k0 + c * CH;
+          rh[i] = *reinterpret_cast<const u32x4*>(in.hi + off);
+          rl[i] = *reinterpret_cast<const u32x4*>(in.lo + off);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        issue(bufA, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < SB; ++i) {
+          int m, c;
+          bool ok;
+          In::chunk(0, i, Mt, kw, m, c, ok);
+          if (ok) {
+            *reinterpret_cast<u32x4*>(xst.hi + m * xst.ldx + c * CH) = rh[i];
+            *reinterpret_cast<u32x4*>(xst.lo + m * xst.ldx + c * CH) = rl[i];
+          }
+        }
+      }
+      // further rounds (slices larger than one round), one chunk at a time
+      const int nch = kw / CH, n = Mt * nch;
+      for (int e = SB * GEMM_THREADS + threadIdx.x; e < n; e += GEMM_THREADS) {
+        const int m = e / nch, c = e - m * nch;
+        const size_t off = (size_t)(m0 + m) * in.K + k0 + c * CH;
+        *reinterpret_cast<uint4*>(xst.hi + m * xst.ldx + c * CH) = *reinterpret_cast<const uint4*>(in.hi + off);
+        *reinterpret_cast<uint4*>(xst.lo + m * xst.ldx + c * CH) = *reinterpret_cast<const uint4*>(in.lo + off);
+      }
+    } else {
+      in.stage(xst, m0, Mt, k0, kw, nb, s, S);
+      issue(bufA, 0);
+    }
+    rsc.finish(g, Mt, s_rs);
+    SPD_MARK(7);
     __syncthreads();
     SPD_MARK(2);
     unsigned char* tb = reinterpret_cast<unsigned char*>(xs_lo + (size_t)xrows * g.ldx) +
@@ -266,7 +359,21 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_skinny_kernel(GemmShape g, 
 #pragma unroll
       for (int u = 0; u < NT; ++u) cur[i][u] = F::load(wp[u] + (i < nst ? i * F::KSTEP : 0));
     SPD_MARK(1);
-    in.stage(XStage<WT>{xs, xs_lo, g.ldx}, m0, Mt, k0, kw, nb, s, S);
+    RowScale<4 * MT> rsc;
+    rsc.load(g, m0, Mt);
+    const XStage<WT> xst{xs, xs_lo, g.ldx};
+    if constexpr (TwoPhase<In>::value) {
+      constexpr int CH = In::CH;
+      const int nch = kw / CH, n = Mt * nch;
+      for (int e = threadIdx.x; e < n; e += GEMM_THREADS) {
+        const int m = e / nch, c = e - m * nch;
+        *reinterpret_cast<uint4*>(xst.hi + m * xst.ldx + c * CH) =
+            *reinterpret_cast<const uint4*>(in.hi + (size_t)(m0 + m) * in.K + k0 + c * CH);
+      }
+    } else {
+      in.stage(xst, m0, Mt, k0, kw, nb, s, S);
+    }
+    rsc.finish(g, Mt, s_rs);
     __syncthreads();
     SPD_MARK(2);
     for (int st = 0; st < nst; st += U) {
@@ -308,7 +415,8 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_skinny_kernel(GemmShape g, 
 #pragma unroll
       for (int u = 0; u < NT; ++u)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ytile[16 * t + 4 * lg + i][wave * 16 * NT + 16 * u + lr] = acc[t][u][i];
+        for (int i = 0; i < 4; ++i)
+          ytile[16 * t + 4 * lg + i][wave * 16 * NT + 16 * u + lr] = acc[t][u][i] * s_rs[16 * t + 4 * lg + i];
     __syncthreads();
     SPD_MARK(5);
     epi.template run<MT, NT>(TileY<TC>{ytile}, nb, m0, Mt, rmap);
@@ -373,10 +481,11 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_skinny_kernel(GemmShape g, 
   for (int j = 0; j < PER4; ++j) {
     const int e = threadIdx.x + GEMM_THREADS * j;
     const int m = e / C4, c = (e - m * C4) * 4;
-    ytile[m][c] = sum[j].x;
-    ytile[m][c + 1] = sum[j].y;
-    ytile[m][c + 2] = sum[j].z;
-    ytile[m][c + 3] = sum[j].w;
+    const float sc = s_rs[m];
+    ytile[m][c] = sum[j].x * sc;
+    ytile[m][c + 1] = sum[j].y * sc;
+    ytile[m][c + 2] = sum[j].z * sc;
+    ytile[m][c + 3] = sum[j].w * sc;
   }
   __syncthreads();
   SPD_MARK(5);
@@ -420,6 +529,59 @@ __device__ __forceinline__ float4 ldg4(const bf16* p) {
                      bf2f((bf16)(a.y >> 16)));
 }
 
+// Activations handed from one GEMM to the next are stored ready to stage: for
+// bf16 weights as two bf16 arrays, hi = bf16(x) and lo = bf16(x - hi), which give
+// the MFMA about 16 mantissa bits of x; for fp32 weights as one fp32 array.
+template <typename WT>
+struct XSplit {
+  WT* hi;
+  WT* lo;
+  int ld;  // row stride (elements)
+  __device__ __forceinline__ void put1(int m, int k, float v) const {
+    if constexpr (sizeof(WT) == 2) {
+      const uint32_t h = pack2_bf16(v, 0.f);
+      hi[(size_t)m * ld + k] = (WT)(h & 0xffffu);
+      lo[(size_t)m * ld + k] = (WT)(pack2_bf16(v - __uint_as_float(h << 16), 0.f) & 0xffffu);
+    } else {
+      hi[(size_t)m * ld + k] = v;
+    }
+  }
+  __device__ __forceinline__ void put4(int m, int k, float4 v) const {
+    if constexpr (sizeof(WT) == 2) {
+      const uint32_t h0 = pack2_bf16(v.x, v.y), h1 = pack2_bf16(v.z, v.w);
+      const uint32_t l0 = pack2_bf16(v.x - __uint_as_float(h0 << 16), v.y - __uint_as_float(h0 & 0xffff0000u));
+      const uint32_t l1 = pack2_bf16(v.z - __uint_as_float(h1 << 16), v.w - __uint_as_float(h1 & 0xffff0000u));
+      *reinterpret_cast<uint2*>(hi + (size_t)m * ld + k) = make_uint2(h0, h1);
+      *reinterpret_cast<uint2*>(lo + (size_t)m * ld + k) = make_uint2(l0, l1);
+    } else {
+      *reinterpret_cast<float4*>(hi + (size_t)m * ld + k) = v;
+    }
+  }
+};
+
+// X given as an XSplit pair: staging is a copy of 16-byte chunks.  The kernel
+// issues the first round of chunk loads before the first weight group and writes
+// them to LDS afterwards (chunk() gives the addresses); further rounds follow.
+template <typename WT>
+struct InSplit {
+  const WT* hi;
+  const WT* lo;
+  int K;  // row stride (elements)
+  static constexpr bool kTwoPhase = true;
+  static constexpr int CH = 16 / (int)sizeof(WT);  // elements per chunk
+  static constexpr int SB = 4;                     // chunks per thread in the first round
+  // chunk i of round r of this thread: tile row m, chunk column c (clamped to a
+  // valid chunk when !ok, so that the load can be unconditional)
+  static __device__ __forceinline__ void chunk(int r, int i, int Mt, int kw, int& m, int& c, bool& ok) {
+    const int nch = kw / CH, n = Mt * nch;
+    const int e = (r * SB + i) * GEMM_THREADS + threadIdx.x;
+    ok = e < n;
+    const int ec = ok ? e : 0;
+    m = ec / nch;
+    c = ec - m * nch;
+  }
+};
+
 // X given (float activations)
 template <typename WT, typename XT>
 struct InAct {
@@ -450,73 +612,13 @@ struct InAct {
   }
 };
 
-// X = RMSNorm(H) * gamma, with the row statistics summed from per-block
-// partial sums of squares ss[p][row] (P <= 128 partials) written by the producer of H.
-template <typename WT>
-struct InNorm {
-  const float* H;
-  const WT* gamma;
-  const float* ss;
-  int P;  // partial count
-  int M;  // rows of H (ss row stride)
-  int K;
-  float eps;
-  __device__ void stage(const XStage<WT>& xs, int m0, int Mt, int k0, int kw, int, int, int) const {
-    const int kv = kw >> 2;
-    const StageIdx ix(Mt, kv);
-    float sp[STAGE_ROWS][2];
-#pragma unroll
-    for (int j = 0; j < STAGE_ROWS; ++j) {
-      const int mm = ix.wave + GEMM_WAVES * j;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int p = ix.lane + WAVE * h;
-        const bool ok = mm < Mt && p < P;
-        const float t = ss[ok ? (size_t)p * M + m0 + mm : (size_t)m0];
-        sp[j][h] = ok ? t : 0.f;
-      }
-    }
-    // row scales go through LDS: a register array indexed by the (wave-uniform) row
-    // slot would be placed in scratch, whose loads wait for every outstanding load
-    __shared__ float s_inv[GEMM_WAVES][STAGE_ROWS];
-    for (int b0 = 0; b0 < ix.n; b0 += STAGE_BATCH) {
-      float4 v[STAGE_BATCH], gm[STAGE_BATCH];
-#pragma unroll
-      for (int i = 0; i < STAGE_BATCH; ++i) {
-        int j, mm, u;
-        ix.at(b0 + i, j, mm, u);
-        const bool ok = b0 + i < ix.n && u < kv;
-        v[i] = ldg4(H + (ok ? (size_t)(m0 + mm) * K + k0 + 4 * u : (size_t)m0 * K + k0));
-        gm[i] = ldg4(gamma + k0 + (ok ? 4 * u : 0));
-      }
-      if (b0 == 0) {
-#pragma unroll
-        for (int j = 0; j < STAGE_ROWS; ++j) {
-          const float t = 1.0f / sqrtf(wave_sum(sp[j][0] + sp[j][1]) / (float)K + eps);
-          if (ix.lane == 0) s_inv[ix.wave][j] = t;
-        }
-        __builtin_amdgcn_wave_barrier();
-      }
-#pragma unroll
-      for (int i = 0; i < STAGE_BATCH; ++i) {
-        int j, mm, u;
-        ix.at(b0 + i, j, mm, u);
-        if (b0 + i < ix.n && u < kv) {
-          const float iv = s_inv[ix.wave][j];
-          const float t[4] = {v[i].x * iv * gm[i].x, v[i].y * iv * gm[i].y, v[i].z * iv * gm[i].z,
-                              v[i].w * iv * gm[i].w};
-          xs.put4(mm, 4 * u, t);
-        }
-      }
-    }
-  }
-};
-
 // ---------------------------------------------------------------------------
 // Epilogues
 // ---------------------------------------------------------------------------
 
-// h[row][col] += y; ss_out[nb][row] = sum over the block's columns of h^2.
+// h[row][col] += y; ss_out[nb][row] = sum over the block's columns of h^2; and,
+// when xo.hi is set, the next GEMM's input h * gnext as an XSplit (its RMSNorm
+// row scale is applied to that GEMM's product from ss_out).
 // With `final_`, the epilogue blocks of the M-tile holding row M-1 count in and
 // the last one writes h_last = RMSNorm(h[M-1]) * final_norm (h and the sums are
 // stored coherently so that block can read them).
@@ -532,6 +634,8 @@ struct EpiResid {
   unsigned* ctr_final;
   int nblocks;
   float eps;
+  XSplit<WT> xo;
+  const WT* gnext;
   template <int MT, int NT, typename Y, typename RM>
   __device__ void run(const Y& y, int nb, int m0, int Mt, const RM&) const {
     constexpr int R = 4 * MT;  // rows per wave at most
@@ -559,6 +663,7 @@ struct EpiResid {
           const float v = hv[r][u] + y(m, c);
           st_coh(h + (size_t)(m0 + m) * N + col, v);
           sq += v * v;
+          if (xo.hi) xo.put1(m0 + m, col, v * to_f<WT>(gnext[col]));
         }
       }
       sq = wave_sum(sq);
@@ -580,9 +685,10 @@ struct EpiResid {
   }
 };
 
-// act[row][j] = silu(gate_j) * up_j
+// act[row][j] = silu(gate_j) * up_j, written as the down projection's XSplit input
+template <typename WT>
 struct EpiSilu {
-  float* act;
+  XSplit<WT> out;
   int dff;
   template <int MT, int NT, typename Y, typename RM>
   __device__ void run(const Y& y, int nb, int m0, int Mt, const RM&) const {
@@ -592,7 +698,7 @@ struct EpiSilu {
       const int j = nb * H + c;
       if (j >= dff) continue;
       const float gt = y(m, c), up = y(m, c + H);
-      act[(size_t)(m0 + m) * dff + j] = gt / (1.0f + expf(-gt)) * up;
+      out.put1(m0 + m, j, gt / (1.0f + expf(-gt)) * up);
     }
   }
 };
