@@ -4,20 +4,22 @@
 // at depth k uses every anchor b_j <= l_max(k); the review blog's core formulas
 // give the operator FC(norm(Concat(.))) and g^0 = FC(H^0).
 //
-// One launch of the skinny GEMM.  The input functor gathers the row's eligible
-// anchor states for its K-slice straight from the anchor store into LDS (empty
-// slots are zeros; gamma is applied; the k = 0 rows read slot 0 only, without
-// gamma) and records the slice's sum of squares.  Because FC is linear,
-// W (gamma * x / rms) = (W (gamma * x)) / rms, so the epilogue divides the
-// reduced product by the row's rms once the slice sums are known.
+// Two launches.  The gather kernel reads each row's eligible anchor states from
+// the anchor store (empty slots are zeros; the k = 0 rows read slot 0 only,
+// without gamma), writes gamma * x as the FC's pre-split bf16 hi/lo input and,
+// in the last block of each row, the row's 1/rms over its filled slots.  The
+// skinny GEMM then streams W_fc; because FC is linear,
+// W (gamma * x / rms) = (W (gamma * x)) / rms, the row scale is applied to the
+// product tile.
 #include "spd_common.h"
 #include "spd_gemm.h"
 #include "spd_host.h"
 
 namespace spd {
 
+constexpr int TABN = (SPD_MAX_STAGES + 1) * SPD_MAX_ANCHORS;
 struct SlotTable {
-  int8_t v[(SPD_MAX_STAGES + 1) * SPD_MAX_ANCHORS];
+  int8_t v[TABN];
 };
 
 struct RowDepth {
@@ -25,121 +27,130 @@ struct RowDepth {
   __device__ __forceinline__ int operator()(int r) const { return r < M - a ? n : M - 1 - r; }
 };
 
-template <typename WT>
-struct InAnchor {
-  const WT* store;
-  const WT* gamma;
-  int64_t T_cap;
-  int S_store, d, m, pos0, norm_k0;
-  RowDepth depth;
-  SlotTable tab;
-  float* xss;  // [nblocks][S][M] slice sums of squares
-  __device__ void stage(const XStage<WT>& xs, int m0, int Mt, int k0, int kw, int nb, int s, int S) const {
-    // StageIdx layout (d % 4 == 0, so a group of 4 never straddles two anchor slots)
-    const int kv = kw >> 2;
-    const StageIdx ix(Mt, kv);
-    float sq[STAGE_ROWS];
-#pragma unroll
-    for (int j = 0; j < STAGE_ROWS; ++j) sq[j] = 0.f;
-    for (int b0 = 0; b0 < ix.n; b0 += STAGE_BATCH) {
-      float4 v[STAGE_BATCH], gm[STAGE_BATCH];
-#pragma unroll
-      for (int i = 0; i < STAGE_BATCH; ++i) {
-        int j, mm, u;
-        ix.at(b0 + i, j, mm, u);
-        // unconditional loads from clamped addresses, masked afterwards (a
-        // conditional load becomes a branch whose join waits for every load)
-        const bool ok = b0 + i < ix.n && u < kv;
-        const int r = m0 + (ok ? mm : 0);
-        const int k = depth(r);
-        const bool plain = (k == 0) && !norm_k0;
-        const int col = k0 + (ok ? 4 * u : 0);
-        const int a = col / d;
-        const int c = col - a * d;
-        int slot = tab.v[k * m + a];
-        if (plain && a != 0) slot = -1;
-        const bool use = ok && slot >= 0 && slot < S_store;
-        const float4 x = ldg4(store + ((size_t)(pos0 + r) * S_store + (use ? slot : 0)) * d + c);
-        const float4 gg = ldg4(gamma + col);
-        v[i] = use ? x : make_float4(0.f, 0.f, 0.f, 0.f);
-        gm[i] = (use && !plain) ? gg : make_float4(1.f, 1.f, 1.f, 1.f);
-      }
-#pragma unroll
-      for (int i = 0; i < STAGE_BATCH; ++i) {
-        int j, mm, u;
-        ix.at(b0 + i, j, mm, u);
-        if (b0 + i < ix.n && u < kv) {
-          const float q = v[i].x * v[i].x + v[i].y * v[i].y + v[i].z * v[i].z + v[i].w * v[i].w;
-#pragma unroll
-          for (int t = 0; t < STAGE_ROWS; ++t)
-            if (t == j) sq[t] += q;
-          const float x[4] = {v[i].x * gm[i].x, v[i].y * gm[i].y, v[i].z * gm[i].z, v[i].w * gm[i].w};
-          xs.put4(mm, 4 * u, x);
-        }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < STAGE_ROWS; ++j) {
-      const int mm = ix.wave + GEMM_WAVES * j;
-      const float t = wave_sum(sq[j]);
-      if (mm < Mt && ix.lane == 0) st_coh(xss + ((size_t)nb * S + s) * depth.M + m0 + mm, t);
-    }
-  }
-};
+constexpr int GATHER_COLS = 8 * 256;  // columns per gather block (8 per thread)
 
 template <typename WT>
-struct EpiFeature {
-  float* g;
-  const float* xss;
-  int d, m, S, norm_k0;
+struct GatherArgs {
+  const WT* store;  // [T_cap][S_store][d]
+  const WT* gamma;  // [m*d]
+  XSplit<WT> xo;    // [M][m*d]
+  float* part;      // [ncb][M] partial sums of squares
+  float* inv;       // [M] row scale
+  unsigned* counters;
+  int S_store, d, m, pos0, norm_k0, ncb;
   float eps;
   RowDepth depth;
   SlotTable tab;
+};
+
+// Block (column block cb, row r); each thread owns 8 consecutive columns, which
+// never straddle two anchors (d % 64 == 0).
+template <typename WT>
+__global__ __launch_bounds__(256) void feature_gather_kernel(GatherArgs<WT> f) {
+  __shared__ int8_t s_tab[TABN];
+  __shared__ float s_red[4];
+  SPD_MARK(0);
+  if (threadIdx.x == 0) {
+    // the table is copied with constant indices: a dynamically indexed kernel
+    // argument would be copied to scratch memory
+    int* dst = reinterpret_cast<int*>(s_tab);
+    const int* src = reinterpret_cast<const int*>(f.tab.v);
+#pragma unroll
+    for (int i = 0; i < TABN / 4; ++i) dst[i] = src[i];
+  }
+  __syncthreads();
+  const int cb = blockIdx.x, r = blockIdx.y;
+  const int k = f.depth(r);
+  const bool plain = (k == 0) && !f.norm_k0;
+  const int K = f.m * f.d;
+  const int col = cb * GATHER_COLS + 8 * threadIdx.x;
+  const bool inb = col < K;
+  const int a = inb ? col / f.d : 0;
+  const int c = inb ? col - a * f.d : 0;
+  int slot = s_tab[k * f.m + a];
+  if (plain && a != 0) slot = -1;
+  const bool use = inb && slot >= 0 && slot < f.S_store;
+  // unconditional loads from clamped addresses, masked afterwards
+  const WT* src = f.store + ((size_t)(f.pos0 + r) * f.S_store + (use ? slot : 0)) * f.d + c;
+  const WT* gp = f.gamma + (inb ? col : 0);
+  float x[8], gm[8];
+  {
+    const float4 x0 = ldg4(src), x1 = ldg4(src + 4);
+    const float4 g0 = ldg4(gp), g1 = ldg4(gp + 4);
+    const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[e] = use ? xv[e] : 0.f;
+      gm[e] = plain ? 1.f : gv[e];
+    }
+  }
+  float sq = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sq += x[e] * x[e];
+  if (inb) {
+    f.xo.put4(r, col, make_float4(x[0] * gm[0], x[1] * gm[1], x[2] * gm[2], x[3] * gm[3]));
+    f.xo.put4(r, col + 4, make_float4(x[4] * gm[4], x[5] * gm[5], x[6] * gm[6], x[7] * gm[7]));
+  }
+  SPD_MARK(1);
+  sq = wave_sum(sq);
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = sq;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    st_coh(f.part + (size_t)cb * gridDim.y + r, (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]));
+  SPD_MARK(4);
+  if (!arrive_last(f.counters + r, (unsigned)f.ncb)) return;
+  SPD_MARK(5);
+  if (threadIdx.x < 64) {
+    float t = 0.f;
+    for (int q = threadIdx.x; q < f.ncb; q += 64) t += ld_coh(f.part + (size_t)q * gridDim.y + r);
+    t = wave_sum(t);
+    if (threadIdx.x == 0) {
+      int filled = 0;
+#pragma unroll
+      for (int j = 0; j < SPD_MAX_ANCHORS; ++j) filled += (j < f.m && s_tab[k * f.m + j] >= 0) ? 1 : 0;
+      f.inv[r] = plain ? 1.f : (filled > 0 ? 1.0f / sqrtf(t / (float)(filled * f.d) + f.eps) : 0.f);
+    }
+  }
+}
+
+// g[row][col] = y (the row scale is already applied to the tile)
+struct EpiRows {
+  float* g;
+  int N;
   template <int MT, int NT, typename Y, typename RM>
   __device__ void run(const Y& y, int nb, int m0, int Mt, const RM&) const {
     constexpr int TC = 64 * NT;
-    __shared__ float inv[32];
-    const int wave = threadIdx.x >> 6;
-    for (int mm = wave; mm < Mt; mm += GEMM_WAVES) {
-      const int r = m0 + mm;
-      const int k = depth(r);
-      const float* xp = xss + (size_t)nb * S * depth.M + r;
-      const float t = wave_sum_of(S, [&](int q) { return ld_coh(xp + (size_t)q * depth.M); });
-      if ((threadIdx.x & 63) == 0) {
-        if (k == 0 && !norm_k0) {
-          inv[mm] = 1.f;
-        } else {
-          int filled = 0;
-          for (int j = 0; j < m; ++j) filled += tab.v[k * m + j] >= 0;
-          inv[mm] = filled > 0 ? 1.0f / sqrtf(t / (float)(filled * d) + eps) : 0.f;
-        }
-      }
-    }
-    __syncthreads();
     for (int e = threadIdx.x; e < Mt * TC; e += GEMM_THREADS) {
       const int mm = e / TC, c = e - mm * TC;
       const int col = nb * TC + c;
-      if (col < d) g[(size_t)(m0 + mm) * d + col] = y(mm, c) * inv[mm];
+      if (col < N) g[(size_t)(m0 + mm) * N + col] = y(mm, c);
     }
   }
 };
 
 struct FusePlan {
   GemmPlan gp;
-  size_t off_xss, off_part, total;
+  int ncb;
+  size_t off_part, off_inv, off_xh, off_xl, off_gpart, total;
 };
 
 static FusePlan plan_fuse(const spd_config* cfg, int M) {
   FusePlan p;
   const bool bf = cfg->dtype == SPD_BF16;
   const int kstep = bf ? Mfma<bf16>::KSTEP : Mfma<float>::KSTEP;
-  p.gp = plan_gemm(cfg->d, cfg->m * cfg->d, M, kstep, bf ? 2 : 4, 1);
+  const int es = bf ? 2 : 4;
+  const size_t K = (size_t)cfg->m * cfg->d;
+  p.gp = plan_gemm(cfg->d, (int)K, M, kstep, es, 1);
+  p.ncb = (int)((K + GATHER_COLS - 1) / GATHER_COLS);
   size_t off = SPD_WS_COUNTER_BYTES;
-  p.off_xss = off;
-  off = align256(off + (size_t)p.gp.nblocks * p.gp.S * M * sizeof(float));
-  p.off_part = off;
-  if (p.gp.S > 1) off = align256(off + (size_t)p.gp.S * M * cfg->d * sizeof(float));
-  p.total = off > 256 ? off : 256;
+  auto take = [&](size_t b) { size_t r = off; off = align256(off + b); return r; };
+  p.off_part = take((size_t)p.ncb * M * 4);
+  p.off_inv = take((size_t)M * 4);
+  p.off_xh = take((size_t)M * K * es);
+  p.off_xl = take(bf ? (size_t)M * K * es : 0);
+  p.off_gpart = take(p.gp.S > 1 ? (size_t)p.gp.S * M * cfg->d * 4 : 0);
+  p.total = off;
   return p;
 }
 
@@ -149,15 +160,31 @@ template <typename WT>
 static int fuse_impl(const spd_config* cfg, const void* hstore, int64_t T_cap, int S_store,
                      const int32_t* slot_tab, int pos0, int M, int a, const void* norm_w,
                      const void* fc_w, float* g, void* ws, hipStream_t st) {
+  (void)T_cap;
   FusePlan p = plan_fuse(cfg, M);
   const int d = cfg->d, m = cfg->m, n = cfg->n;
-  SlotTable tab;
-  for (int i = 0; i < (SPD_MAX_STAGES + 1) * SPD_MAX_ANCHORS; ++i) tab.v[i] = -1;
-  for (int k = 0; k <= n; ++k)
-    for (int j = 0; j < m; ++j) tab.v[k * m + j] = (int8_t)slot_tab[k * m + j];
-  RowDepth dep{M, a, n};
   char* w = static_cast<char*>(ws);
-  float* xss = reinterpret_cast<float*>(w + p.off_xss);
+  GatherArgs<WT> ga;
+  for (int i = 0; i < TABN; ++i) ga.tab.v[i] = -1;
+  for (int k = 0; k <= n; ++k)
+    for (int j = 0; j < m; ++j) ga.tab.v[k * m + j] = (int8_t)slot_tab[k * m + j];
+  ga.store = static_cast<const WT*>(hstore);
+  ga.gamma = static_cast<const WT*>(norm_w);
+  ga.xo = XSplit<WT>{reinterpret_cast<WT*>(w + p.off_xh), reinterpret_cast<WT*>(w + p.off_xl), m * d};
+  ga.part = reinterpret_cast<float*>(w + p.off_part);
+  ga.inv = reinterpret_cast<float*>(w + p.off_inv);
+  ga.counters = reinterpret_cast<unsigned*>(w);
+  ga.S_store = S_store;
+  ga.d = d;
+  ga.m = m;
+  ga.pos0 = pos0;
+  ga.norm_k0 = cfg->norm_k0;
+  ga.ncb = p.ncb;
+  ga.eps = cfg->rms_eps;
+  ga.depth = RowDepth{M, a, n};
+  hipLaunchKernelGGL((feature_gather_kernel<WT>), dim3(p.ncb, M), dim3(256), 0, st, ga);
+  int rc = check_launch();
+  if (rc) return rc;
 
   GemmShape gs{};
   gs.W = fc_w;
@@ -167,14 +194,12 @@ static int fuse_impl(const spd_config* cfg, const void* hstore, int64_t T_cap, i
   gs.S = p.gp.S;
   gs.nsteps = p.gp.nsteps;
   gs.ldx = p.gp.ldx;
-  gs.part = reinterpret_cast<float*>(w + p.off_part);
+  gs.part = reinterpret_cast<float*>(w + p.off_gpart);
   gs.nblocks = p.gp.nblocks;
   gs.counters = reinterpret_cast<unsigned*>(w);
-
-  InAnchor<WT> in{static_cast<const WT*>(hstore), static_cast<const WT*>(norm_w), T_cap, S_store,
-                  d, m, pos0, cfg->norm_k0, dep, tab, xss};
-  EpiFeature<WT> epi{g, xss, d, m, p.gp.S, cfg->norm_k0, cfg->rms_eps, dep, tab};
-  return launch_gemm<WT, 1>(p.gp, gs, in, epi, RowMapStd{}, st);
+  gs.rs_inv = ga.inv;
+  InSplit<WT, RS_INV> in{ga.xo.hi, ga.xo.lo, m * d};
+  return launch_gemm<WT, 1>(p.gp, gs, in, EpiRows{g, d}, RowMapStd{}, st);
 }
 
 }  // namespace spd
@@ -190,6 +215,7 @@ extern "C" int spd_fuse_features(const spd_config* cfg, const void* hstore, int6
   if (!hstore || !slot_tab || !norm_w || !fc_w || !g || !ws) return SPD_E_INVALID;
   if (M < 1 || pos0 < 0 || T_cap < 1 || (int64_t)pos0 + M > T_cap || S < 1) return SPD_E_INVALID;
   if (a < 0 || a > cfg->n || a > M) return SPD_E_INVALID;
+  if (M >= CTR_FINAL) return SPD_E_UNSUPPORTED;  // one arrival counter per row
   if (cfg->d % 64) return SPD_E_UNSUPPORTED;
   for (int i = 0; i < (cfg->n + 1) * cfg->m; ++i)
     if (slot_tab[i] < -1 || slot_tab[i] >= S) return SPD_E_INVALID;

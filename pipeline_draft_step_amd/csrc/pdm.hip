@@ -23,10 +23,10 @@
 
 namespace spd {
 
-constexpr int ATT_SUB = 64;                     // keys per wave
+constexpr int ATT_SUB = 32;                     // keys per wave
 constexpr int ATT_WAVES = 4;                    // waves per attention block
 constexpr int ATT_KC = ATT_SUB * ATT_WAVES;     // keys per block (one partial per row)
-constexpr int ATT_MAXCH = 128;                  // chunks per row: context up to 32768
+constexpr int ATT_MAXCH = 256;                  // chunks per row: context up to 32768
 
 // h = g, per-64-column partial sums of squares of every row, and the first QKV
 // GEMM's input g * attn_norm as an XSplit (its RMSNorm row scale comes from ss)
@@ -152,6 +152,17 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
 
   const WT* K = static_cast<const WT*>(a.kc) + (size_t)h * a.T_cap * HD;
   const WT* Vt = static_cast<const WT*>(a.vc) + (size_t)h * HD * a.T_cap;
+  // All loads are unconditional (a conditional load becomes a branch whose join
+  // waits for every outstanding load) and issued in the order they are needed:
+  // Q, K, then V.  Q row = query index 16*qt + lr (clamped; rows past QR are zeroed).
+  const int qi = 16 * qt + lr;
+  const bool qv = qi < QR;
+  const float* qp = a.q + ((size_t)(qv ? qi / G : 0) * a.Hq + h * G + (qv ? qi % G : 0)) * HD;
+  float qraw[DS][KPL];
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+    for (int e = 0; e < KPL; ++e) qraw[ds][e] = qp[ds * F::KSTEP + lg * KPL + e];
   frag kf[KS][DS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
@@ -159,35 +170,27 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) kf[ks][ds] = F::load(K + (size_t)key * HD + ds * F::KSTEP + lg * KPL);
   }
+  // V: this lane's KPL keys start at kb; kb + KPL <= T_cap whenever kb < nkeys (both
+  // multiples of KPL), so the clamp only moves fully masked fragments
   frag vf[KT][DT];
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt) {
     const int kb = key0 + kt * F::KSTEP + lg * KPL;
+    const int kbc = min(kb, (int)a.T_cap - KPL);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const WT* src = Vt + (size_t)(dt * 16 + lr) * a.T_cap + kb;
-      if (kb + KPL <= nkeys) {
-        vf[kt][dt] = F::load(src);
-      } else {
-        float tmp[KPL];
-#pragma unroll
-        for (int e = 0; e < KPL; ++e) tmp[e] = (kb + e < nkeys) ? to_f<WT>(src[e]) : 0.f;
-        vf[kt][dt] = F::pack(tmp);
-      }
-    }
+    for (int dt = 0; dt < DT; ++dt) vf[kt][dt] = F::load(Vt + (size_t)(dt * 16 + lr) * a.T_cap + kbc);
   }
+  __builtin_amdgcn_sched_barrier(0);  // keep V in flight with Q and K
   SPD_MARK(1);
-  // Q fragments (A operand): row = query index 16*qt + lr, pre-scaled by 1/sqrt(hd)
-  const int qi = 16 * qt + lr;
-  const bool qv = qi < QR;
-  const float* qp = a.q + ((size_t)(qv ? qi / G : 0) * a.Hq + h * G + (qv ? qi % G : 0)) * HD;
+  // Q fragments (A operand), pre-scaled by 1/sqrt(hd), as hi + lo pairs
   frag qf[DS], ql[DS];
+  const float qs = qv ? a.scale : 0.f;  // clamped rows (finite values) become zero
 #pragma unroll
   for (int ds = 0; ds < DS; ++ds) {
     float tmp[KPL], rem[KPL];
 #pragma unroll
     for (int e = 0; e < KPL; ++e) {
-      tmp[e] = qv ? qp[ds * F::KSTEP + lg * KPL + e] * a.scale : 0.f;
+      tmp[e] = qraw[ds][e] * qs;  // used unconditionally: no load is sunk into a branch
       rem[e] = tmp[e] - to_f<WT>(from_f<WT>(tmp[e]));
     }
     qf[ds] = F::pack(tmp);
@@ -242,6 +245,14 @@ s_ = row16_sum(s_);
     for (int i = 0; i < 4; ++i) Ml[wave][4 * lg + i] = make_float2(mx[i], sm[i]);
   }
   __syncthreads();
+  // zero the V elements of keys >= nkeys (their P is 0, but the cache past the
+  // committed rows may hold anything)
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+    const int kb = key0 + kt * F::KSTEP + lg * KPL;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) vf[kt][dt] = F::mask_from(vf[kt][dt], nkeys - kb);
+  }
   f32x4 o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -489,7 +500,7 @@ static int pdm_impl(const spd_config* c, const spd_layer_weights* layers, const 
     WT* vc = static_cast<WT*>(v_cache) + (size_t)l * Hkv * hd * T_cap;
     // QKV: x0 = h * attn_norm, row scale = 1 / rms(h)
     {
-      InSplit<WT> in{x0.hi, x0.lo, d};
+      InSplit<WT, RS_SS> in{x0.hi, x0.lo, d};
       EpiQKV<WT> epi{qb, kc, vc, static_cast<const WT*>(lw.q_norm), static_cast<const WT*>(lw.k_norm),
                      Hq, Hkv, hd, pos0, T_cap, c->rms_eps, c->rope_theta};
       rc = launch_gemm<WT, 2>(p.qkv, shape_of(p.qkv, lw.wqkv, nq, d, M, part, ctr, ss, P, c->rms_eps),
@@ -518,7 +529,7 @@ static int pdm_impl(const spd_config* c, const spd_layer_weights* layers, const 
     }
     // gate/up + silu*mul -> x1; row scale = 1 / rms(h)
     {
-      InSplit<WT> in{x0.hi, x0.lo, d};
+      InSplit<WT, RS_SS> in{x0.hi, x0.lo, d};
       EpiSilu<WT> epi{x1, dff};
       rc = launch_gemm<WT, 2>(p.gu, shape_of(p.gu, lw.w_gate_up, 2 * dff, d, M, part, ctr, ss, P,
                                              c->rms_eps),

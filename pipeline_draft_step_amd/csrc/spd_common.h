@@ -80,6 +80,14 @@ template <> struct Mfma<bf16> {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, a),
                                                    __builtin_bit_cast(bf16x8_v, b), c, 0, 0, 0);
   }
+  // keep the first `n` of the 8 elements (n <= 0: none), zero the rest
+  static __device__ __forceinline__ frag mask_from(frag f, int n) {
+    const uint32_t m0 = n >= 2 ? 0xffffffffu : (n == 1 ? 0xffffu : 0u);
+    const uint32_t m1 = n >= 4 ? 0xffffffffu : (n == 3 ? 0xffffu : 0u);
+    const uint32_t m2 = n >= 6 ? 0xffffffffu : (n == 5 ? 0xffffu : 0u);
+    const uint32_t m3 = n >= 8 ? 0xffffffffu : (n == 7 ? 0xffffu : 0u);
+    return make_uint4(f.x & m0, f.y & m1, f.z & m2, f.w & m3);
+  }
   // pack 8 floats (rounded to bf16) into one fragment
   static __device__ __forceinline__ frag pack(const float* v) {
     uint32_t w[4];
@@ -99,6 +107,7 @@ template <> struct Mfma<float> {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
   }
   static __device__ __forceinline__ frag pack(const float* v) { return v[0]; }
+  static __device__ __forceinline__ frag mask_from(frag f, int n) { return n >= 1 ? f : 0.f; }
 };
 
 // ---------------------------------------------------------------------------

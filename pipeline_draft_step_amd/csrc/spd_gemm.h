@@ -50,9 +50,11 @@ struct GemmShape {
   int ytile_bytes;     // fp32 result tile; the transpose buffers follow both
   // optional per-row scale of the product: 1 / sqrt(sum_p rs_ss[p][row] / rs_K + rs_eps)
   // (the RMSNorm of an input whose gamma the producer has already applied)
-  const float* rs_ss;  // [rs_P][rs_M] partial sums of squares, or nullptr (scale 1)
+  const float* rs_ss;  // [rs_P][rs_M] partial sums of squares
   int rs_P, rs_M, rs_K;
   float rs_eps;
+  const float* rs_inv;  // or the row scales themselves [M]
+  // (which one applies is fixed by the input functor, see RowScaleOf)
 };
 
 // Row of W that local column c (0 .. 64*NT-1) of N-block nb maps to.
@@ -129,20 +131,32 @@ struct TwoPhase<T, std::void_t<decltype(T::kTwoPhase)>> : std::bool_constant<T::
 // Row scales of the tile (see GemmShape::rs_ss): wave w owns rows w, w + 4, ...
 // (RW = 4 * MT of them); the partial sums are loaded first (load) and reduced
 // into s_rs (finish).
-template <int RW>
+// Row-scale mode, a compile-time property of the input functor (kRowScale):
+// none, from partial sums of squares (rs_ss), or given per row (rs_inv).
+enum { RS_NONE = 0, RS_SS = 1, RS_INV = 2 };
+template <typename T, typename = void>
+struct RowScaleOf : std::integral_constant<int, RS_NONE> {};
+template <typename T>
+struct RowScaleOf<T, std::void_t<decltype(T::kRowScale)>> : std::integral_constant<int, T::kRowScale> {};
+
+template <int RW, int RS>
 struct RowScale {
   float p[RW][2];
   __device__ __forceinline__ void load(const GemmShape& g, int m0, int Mt) {
-    if (!g.rs_ss) return;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if constexpr (RS == RS_INV) {
 #pragma unroll
-    for (int j = 0; j < RW; ++j) {
-      const int mm = wave + GEMM_WAVES * j;
+      for (int j = 0; j < RW; ++j) p[j][0] = g.rs_inv[m0 + min(wave + GEMM_WAVES * j, Mt - 1)];
+    } else if constexpr (RS == RS_SS) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int q = lane + WAVE * h;
-        const bool ok = mm < Mt && q < g.rs_P;
-        p[j][h] = g.rs_ss[ok ? (size_t)q * g.rs_M + m0 + mm : (size_t)m0];  // masked in finish
+      for (int j = 0; j < RW; ++j) {
+        const int mm = wave + GEMM_WAVES * j;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int c = lane + WAVE * h;
+          const bool ok = mm < Mt && c < g.rs_P;
+          p[j][h] = g.rs_ss[ok ? (size_t)c * g.rs_M + m0 + mm : (size_t)m0];  // masked in finish
+        }
       }
     }
   }
@@ -152,7 +166,9 @@ struct RowScale {
     for (int j = 0; j < RW; ++j) {
       const int mm = wave + GEMM_WAVES * j;
       float v = 1.f;
-      if (g.rs_ss) {
+      if constexpr (RS == RS_INV) {
+        v = p[j][0];
+      } else if constexpr (RS == RS_SS) {
         const float a = (mm < Mt && lane < g.rs_P) ? p[j][0] : 0.f;
         const float b = (mm < Mt && lane + WAVE < g.rs_P) ? p[j][1] : 0.f;
         v = 1.0f / sqrtf(wave_sum(a + b) / (float)g.rs_K + g.rs_eps);
@@ -242,7 +258,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_skinny_kernel(GemmShape g, 
     };
     // A wave's loads complete in issue order: the row-scale and X-slice loads go
     // out before the first weight group, so waiting for them never waits for it.
-    RowScale<4 * MT> rsc;
+    RowScale<4 * MT, RowScaleOf<In>::value> rsc;
     rsc.load(g, m0, Mt);
     const XStage<WT> xst{xs, xs_lo, g.ldx};
     if constexpr (TwoPhase<In>::value) {
@@ -359,7 +375,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_skinny_kernel(GemmShape g, 
 #pragma unroll
       for (int u = 0; u < NT; ++u) cur[i][u] = F::load(wp[u] + (i < nst ? i * F::KSTEP : 0));
     SPD_MARK(1);
-    RowScale<4 * MT> rsc;
+    RowScale<4 * MT, RowScaleOf<In>::value> rsc;
     rsc.load(g, m0, Mt);
     const XStage<WT> xst{xs, xs_lo, g.ldx};
     if constexpr (TwoPhase<In>::value) {
@@ -562,12 +578,13 @@ struct XSplit {
 // X given as an XSplit pair: staging is a copy of 16-byte chunks.  The kernel
 // issues the first round of chunk loads before the first weight group and writes
 // them to LDS afterwards (chunk() gives the addresses); further rounds follow.
-template <typename WT>
+template <typename WT, int RS = RS_NONE>
 struct InSplit {
   const WT* hi;
   const WT* lo;
   int K;  // row stride (elements)
   static constexpr bool kTwoPhase = true;
+  static constexpr int kRowScale = RS;
   static constexpr int CH = 16 / (int)sizeof(WT);  // elements per chunk
   static constexpr int SB = 4;                     // chunks per thread in the first round
   // chunk i of round r of this thread: tile row m, chunk column c (clamped to a
