@@ -7,15 +7,15 @@
 //   rows == 1, bf16, d % 512 == 0: a VALU kernel; each wave owns 8 vocabulary
 //     rows, reads every row as 1 KB contiguous loads (lane l: bytes 16l..16l+15
 //     of each 1 KB piece) and accumulates v_dot2_f32_bf16 products against h held
-//     in registers as a bf16 hi + lo pair; a butterfly reduction finishes a row.
+//     in registers as a bf16 hi + lo pair; a reduction finishes a row.
 //   otherwise: the MFMA skinny GEMM.
 //   Both write the logits and, per block, (max, first argmax, sum exp((l-max)/T)).
-// T == 0, launch 2: one block per row merges the block statistics -> greedy token.
-// T > 0, launch 2: per 2048-entry chunk, each block merges the statistics (fixed
-//   order, so every block gets the same (max, sum)), writes p = exp((l-max)/T)/sum
-//   and sums the exact integer weights floor(p*2^52) of its chunk;
-//   launch 3: one block per row scans the chunk sums, finds the chunk holding
-//   tau = floor(u*S/2^32) and the first index inside it whose prefix exceeds tau.
+//   The last block to finish merges the block statistics in a fixed order into
+//   the row's (max, argmax, sum); at T == 0 it writes the greedy token.
+// T > 0, launch 2: per 2048-entry chunk, p = exp((l-max)/T)/sum and the sum of
+//   the exact integer weights floor(p*2^52) of the chunk; the last chunk block
+//   of a row scans the chunk sums, finds the chunk holding tau = floor(u*S/2^32)
+//   and the first index inside it whose prefix exceeds tau.
 #include <algorithm>
 
 #include "spd_common.h"
@@ -41,7 +41,7 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2_v, b), c, false);
 }
 
-// per-wave statistics of `cnt` logits held one per lane (lanes >= cnt hold -inf)
+// per-wave statistics of logits held one per lane (lanes without one hold -inf)
 __device__ __forceinline__ BlockStat lane_stats(float v, int idx, float inv_t) {
   ArgMax am = wave_argmax(ArgMax{v, idx});
   float se = 0.f;
@@ -67,21 +67,75 @@ __device__ __forceinline__ BlockStat stat_merge(BlockStat a, BlockStat b, float 
   return r;
 }
 
-// Merge n block statistics in a fixed order: thread-strided, then a tree.
-__device__ BlockStat block_merge_stats(const BlockStat* st, int stride, int n, float inv_t) {
-  __shared__ BlockStat sh[SMX_THREADS];
+__device__ __forceinline__ void st_stat(BlockStat* p, BlockStat s) {
+  float* q = reinterpret_cast<float*>(p);
+  st_coh(q, s.mx);
+  st_coh_i32(reinterpret_cast<int*>(q + 1), s.arg);
+  st_coh(q + 2, s.se);
+}
+__device__ __forceinline__ BlockStat ld_stat(const BlockStat* p) {
+  const float* q = reinterpret_cast<const float*>(p);
+  return BlockStat{ld_coh(q), ld_coh_i32(reinterpret_cast<const int*>(q + 1)), ld_coh(q + 2)};
+}
+
+// Block-wide merge of the n statistics st[b * stride], b < n, in a fixed order:
+// thread-strided runs (every load of a round issued first), then a butterfly
+// within each wave, then the four waves in order.  Every thread gets the result.
+template <bool COH>
+__device__ BlockStat merge_stats(const BlockStat* st, int stride, int n, float inv_t) {
+  __shared__ BlockStat s_ws[SMX_THREADS / 64];
+  constexpr int PB = 8;
   BlockStat a{-INFINITY, ARG_NONE, 0.f};
-#pragma unroll 8
-  for (int b = threadIdx.x; b < n; b += SMX_THREADS) a = stat_merge(a, st[(size_t)b * stride], inv_t);
-  sh[threadIdx.x] = a;
-  __syncthreads();
-  for (int w = SMX_THREADS / 2; w > 0; w >>= 1) {
-    if ((int)threadIdx.x < w) sh[threadIdx.x] = stat_merge(sh[threadIdx.x], sh[threadIdx.x + w], inv_t);
-    __syncthreads();
+  for (int b0 = 0; b0 < n; b0 += PB * SMX_THREADS) {
+    BlockStat v[PB];
+#pragma unroll
+    for (int i = 0; i < PB; ++i) {
+      const int b = b0 + threadIdx.x + SMX_THREADS * i;
+      const BlockStat* q = st + (size_t)(b < n ? b : 0) * stride;
+      v[i] = COH ? ld_stat(q) : *q;
+    }
+#pragma unroll
+    for (int i = 0; i < PB; ++i)
+      if (b0 + (int)threadIdx.x + SMX_THREADS * i < n) a = stat_merge(a, v[i], inv_t);
   }
-  const BlockStat r = sh[0];
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const BlockStat b{__shfl_xor(a.mx, o, WAVE), __shfl_xor(a.arg, o, WAVE), __shfl_xor(a.se, o, WAVE)};
+    // lower lane index first, so that both partners compute the same value
+    a = (threadIdx.x & o) ? stat_merge(b, a, inv_t) : stat_merge(a, b, inv_t);
+  }
+  if ((threadIdx.x & 63) == 0) s_ws[threadIdx.x >> 6] = a;
+  __syncthreads();
+  BlockStat r = s_ws[0];
+#pragma unroll
+  for (int w = 1; w < SMX_THREADS / 64; ++w) r = stat_merge(r, s_ws[w], inv_t);
   __syncthreads();
   return r;
+}
+
+// Where the merged statistics of each row go.
+struct HeadFinish {
+  unsigned* counters;  // arrival counters (two-level, 17 x 16 words)
+  BlockStat* gstat;    // [rows] merged statistics
+  int32_t* token;      // [rows], written when greedy (T == 0)
+  int greedy;
+};
+
+__device__ void finish_row(const BlockStat* st, int stride, int n, int r, float inv_t,
+                           const HeadFinish& f) {
+  const BlockStat g = merge_stats<true>(st, stride, n, inv_t);
+  if (threadIdx.x == 0) {
+    f.gstat[r] = g;
+    if (f.greedy) f.token[r] = g.arg == ARG_NONE ? 0 : g.arg;
+  }
+}
+
+// T == 0 after the VALU GEMV: one block per row merges the block statistics.
+__global__ __launch_bounds__(SMX_THREADS) void greedy_kernel(const BlockStat* stat, int nstat,
+                                                             int rows, int32_t* token) {
+  const int r = blockIdx.x;
+  const BlockStat g = merge_stats<false>(stat + r, rows, nstat, 0.f);
+  if (threadIdx.x == 0) token[r] = g.arg == ARG_NONE ? 0 : g.arg;
 }
 
 // VALU GEMV for one hidden row: J = d / 512 loads of 1 KB per vocabulary row.
@@ -150,6 +204,8 @@ struct EpiLogits {
   BlockStat* stat;  // [nblocks][rows]
   int V, rows;
   float inv_t;
+  int nblocks;
+  HeadFinish f;
   template <int MT, int NT, typename Y, typename RM>
   __device__ void run(const Y& y, int nb, int m0, int Mt, const RM&) const {
     constexpr int TC = 64 * NT;
@@ -175,152 +231,218 @@ struct EpiLogits {
           if (v[u] > -INFINITY) se += expf((v[u] - am.v) * inv_t);
         se = wave_sum(se);
       }
-      if (lane == 0) stat[(size_t)nb * rows + m0 + m] = BlockStat{am.v, am.i, se};
+      if (lane == 0) st_stat(stat + (size_t)nb * rows + m0 + m, BlockStat{am.v, am.i, se});
     }
+    // every N-block runs this epilogue once (the tile covers all rows)
+    if (!arrive_last2(f.counters, nb, nblocks, 16)) return;
+    for (int r = 0; r < rows; ++r) finish_row(stat + r, rows, nblocks, r, inv_t, f);
   }
 };
 
-__global__ __launch_bounds__(SMX_THREADS) void lm_argmax_kernel(const BlockStat* stat, int nstat,
-                                                                int rows, int32_t* token) {
-  const int r = blockIdx.x;
-  const BlockStat s = block_merge_stats(stat + r, rows, nstat, 0.f);
-  if (threadIdx.x == 0) token[r] = s.arg == ARG_NONE ? 0 : s.arg;
+// inclusive prefix sum over the lanes of a wave (lane order)
+__device__ __forceinline__ uint64_t wave_scan_u64(uint64_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < WAVE; o <<= 1) {
+    const uint32_t lo = __shfl_up((uint32_t)v, o, WAVE), hi = __shfl_up((uint32_t)(v >> 32), o, WAVE);
+    if (lane >= o) v += ((uint64_t)hi << 32) | lo;
+  }
+  return v;
 }
 
-__global__ __launch_bounds__(SMX_THREADS) void softmax_chunk_kernel(const BlockStat* stat, int nstat,
-                                                                    int rows, const float* logits,
-                                                                    float* probs, uint64_t* csum,
-                                                                    int V, int nchunks, float inv_t) {
+// Row statistics at T > 0 from the GEMV's block statistics: M = max mx_b, then
+// S = sum_b se_b exp((mx_b - M)/T), each in a fixed order (thread runs, DPP
+// within waves, waves in order); every thread gets the result.  Up to
+// 20 * 256 statistics stay in registers between the two passes.
+__device__ void stats_max_sum(const BlockStat* st, int stride, int n, float inv_t, float& M, float& S) {
+  __shared__ float s_r[SMX_THREADS / 64];
+  constexpr int PB = 20;
+  const int wave = threadIdx.x >> 6;
+  const bool one_round = n <= PB * SMX_THREADS;
+  float m[PB], e[PB];
+  float mx = -INFINITY;
+  for (int b0 = 0; b0 < n; b0 += PB * SMX_THREADS) {
+#pragma unroll
+    for (int i = 0; i < PB; ++i) {
+      const int b = b0 + threadIdx.x + SMX_THREADS * i;
+      const BlockStat q = st[(size_t)(b < n ? b : 0) * stride];
+      const bool ok = b < n;
+      m[i] = ok ? q.mx : -INFINITY;
+      e[i] = ok ? q.se : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < PB; ++i) mx = fmaxf(mx, m[i]);
+  }
+  mx = wave_max(mx);
+  if ((threadIdx.x & 63) == 0) s_r[wave] = mx;
+  __syncthreads();
+  M = fmaxf(fmaxf(s_r[0], s_r[1]), fmaxf(s_r[2], s_r[3]));
+  __syncthreads();
+  float sum = 0.f;
+  if (one_round) {
+#pragma unroll
+    for (int i = 0; i < PB; ++i)
+      if (m[i] > -INFINITY) sum += e[i] * expf((m[i] - M) * inv_t);
+  } else {
+    for (int b0 = 0; b0 < n; b0 += PB * SMX_THREADS) {
+#pragma unroll
+      for (int i = 0; i < PB; ++i) {
+        const int b = b0 + threadIdx.x + SMX_THREADS * i;
+        const BlockStat q = st[(size_t)(b < n ? b : 0) * stride];
+        const bool ok = b < n;
+        m[i] = ok ? q.mx : -INFINITY;
+        e[i] = ok ? q.se : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < PB; ++i)
+        if (m[i] > -INFINITY) sum += e[i] * expf((m[i] - M) * inv_t);
+    }
+  }
+  sum = wave_sum(sum);
+  if ((threadIdx.x & 63) == 0) s_r[wave] = sum;
+  __syncthreads();
+  S = (s_r[0] + s_r[1]) + (s_r[2] + s_r[3]);
+  __syncthreads();
+}
+
+constexpr int SMX_MAXCH = 4 * WAVE;  // chunks one wave scans (vocabulary <= 524288)
+
+// T > 0: one block per (2048-entry chunk, row).  Probabilities and chunk weight
+// sums are stored coherently; the last chunk block of the row samples: wave 0
+// scans the chunk sums and finds the chunk holding tau, then the block scans the
+// weights of that chunk (8 consecutive entries per thread).
+// The row statistics are either derived here from the GEMV's nstat block
+// statistics (every block in the same fixed order, so all agree) or, when
+// nstat == 0, read from gstat.
+__global__ __launch_bounds__(SMX_THREADS) void softmax_sample_kernel(
+    const BlockStat* stat, int nstat, int rows, const BlockStat* gstat, const float* logits,
+    float* probs, uint64_t* csum, unsigned* counters, const uint64_t* words, int V, int nchunks,
+    float inv_t, int32_t* token) {
+  __shared__ uint64_t s_w[SMX_THREADS / 64];
+  __shared__ uint64_t s_tau, s_off;
+  __shared__ int s_cc, s_tok;
   const int c = blockIdx.x, r = blockIdx.y;
-  const BlockStat s = block_merge_stats(stat + r, rows, nstat, inv_t);
-  const float inv_sum = 1.0f / s.se;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  SPD_MARK(0);
+  float M, S;
+  if (nstat > 0) {
+    stats_max_sum(stat + r, rows, nstat, inv_t, M, S);
+  } else {
+    M = gstat[r].mx;
+    S = gstat[r].se;
+  }
+  SPD_MARK(1);
+  const float inv_sum = 1.0f / S;
   const float* lr = logits + (size_t)r * V;
   float* pr = probs + (size_t)r * V;
   const int base = c * SMX_CHUNK;
-  uint64_t part = 0;
   constexpr int PER = SMX_CHUNK / SMX_THREADS;
   float lv[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     const int j = base + threadIdx.x + SMX_THREADS * e;
-    lv[e] = j < V ? lr[j] : -INFINITY;
+    lv[e] = lr[j < V ? j : 0];
   }
+  uint64_t part = 0;
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     const int j = base + threadIdx.x + SMX_THREADS * e;
     if (j < V) {
-      const float p = expf((lv[e] - s.mx) * inv_t) * inv_sum;
-      pr[j] = p;
+      const float p = expf((lv[e] - M) * inv_t) * inv_sum;
+      st_coh(pr + j, p);
       part += prob_weight(p);
     }
   }
   part = wave_sum_u64(part);
-  __shared__ uint64_t sh[SMX_THREADS / 64];
-  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = part;
+  if (lane == 0) s_w[wave] = part;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint64_t t = 0;
-    for (int w = 0; w < SMX_THREADS / 64; ++w) t += sh[w];
-    csum[(size_t)r * nchunks + c] = t;
+  if (threadIdx.x == 0)
+    st_coh_u64(csum + (size_t)r * nchunks + c, (s_w[0] + s_w[1]) + (s_w[2] + s_w[3]));
+  SPD_MARK(2);
+  if (!arrive_last(counters + r, (unsigned)nchunks)) {
+    SPD_MARK(3);
+    return;
   }
-}
-
-// Inclusive scan of one uint64 per thread across the block (fixed order).
-__device__ uint64_t block_scan_u64(uint64_t v, uint64_t* sh) {
-  sh[threadIdx.x] = v;
-  __syncthreads();
-  for (int o = 1; o < SMX_THREADS; o <<= 1) {
-    const uint64_t add = (int)threadIdx.x >= o ? sh[threadIdx.x - o] : 0ull;
-    __syncthreads();
-    sh[threadIdx.x] += add;
-    __syncthreads();
+  SPD_MARK(3);
+  const uint64_t* cs = csum + (size_t)r * nchunks;
+  if (wave == 0) {
+    // lane l holds chunks 4l .. 4l+3
+    uint64_t cw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = 4 * lane + i;
+      const uint64_t t = ld_coh_u64(cs + (k < nchunks ? k : 0));
+      cw[i] = k < nchunks ? t : 0ull;
+    }
+    const uint64_t tot = (cw[0] + cw[1]) + (cw[2] + cw[3]);
+    const uint64_t incl = wave_scan_u64(tot);
+    const uint64_t Sw = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(incl >> 32), 63) << 32) |
+                        (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)incl, 63);
+    const uint64_t tau = scale_u32((uint32_t)(words[r] >> 32), Sw);
+    uint64_t run = incl - tot;
+    if (lane == 0) {
+      s_tau = tau;
+      s_cc = -1;
+    }
+    if (run <= tau && tau < incl) {  // exactly one lane (none when the total is 0)
+      int cc = -1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (cc < 0 && tau < run + cw[i]) {
+          cc = 4 * lane + i;
+        } else if (cc < 0) {
+          run += cw[i];
+        }
+      }
+      s_cc = cc;
+      s_off = run;
+    }
   }
-  const uint64_t r = sh[threadIdx.x];
   __syncthreads();
-  return r;
-}
-
-// Smallest index j of [0, n) whose inclusive prefix of wfun(j), started at
-// `offset`, exceeds tau; -1 if none.  Indices are split into contiguous runs of
-// `per` per thread, so the scan over thread totals keeps index order.
-template <typename WF>
-__device__ int block_locate(const WF& wfun, int n, uint64_t offset, uint64_t tau, uint64_t* sh) {
-  __shared__ int s_found;
-  const int per = (n + SMX_THREADS - 1) / SMX_THREADS;
-  if (threadIdx.x == 0) s_found = -1;
+  const int cc = s_cc;
+  if (cc < 0) {
+    if (threadIdx.x == 0) token[r] = 0;
+    return;
+  }
+  // weights of chunk cc: thread t owns entries 8t .. 8t+7
+  const int b0 = cc * SMX_CHUNK;
+  const int n = min(SMX_CHUNK, V - b0);
+  uint64_t w[PER];
+  {
+    float pv[PER];  // clamped indices: the last chunk may be partial
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int j = (int)threadIdx.x * PER + e;
+      pv[e] = ld_coh(pr + b0 + (j < n ? j : 0));
+    }
+#pragma unroll
+    for (int e = 0; e < PER; ++e) w[e] = (int)threadIdx.x * PER + e < n ? prob_weight(pv[e]) : 0ull;
+  }
   uint64_t tot = 0;
-  for (int e = 0; e < per; ++e) {
-    const int j = threadIdx.x * per + e;
-    if (j < n) tot += wfun(j);
-  }
-  const uint64_t incl = block_scan_u64(tot, sh);
-  uint64_t run = offset + incl - tot;
-  if (run <= tau && offset + incl > tau) {  // exactly one thread owns tau
-    for (int e = 0; e < per; ++e) {
-      const int j = threadIdx.x * per + e;
-      if (j >= n) break;
-      run += wfun(j);
-      if (run > tau) {
-        s_found = j;
-        break;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) tot += w[e];
+  const uint64_t winc = wave_scan_u64(tot);
+  if (lane == 63) s_w[wave] = winc;
+  if (threadIdx.x == 0) s_tok = -1;
+  __syncthreads();
+  uint64_t before = s_off;
+  for (int q = 0; q < wave; ++q) before += s_w[q];
+  uint64_t run = before + winc - tot;
+  const uint64_t tau = s_tau;
+  if (run <= tau && tau < run + tot) {
+    int found = -1;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      if (found < 0) {
+        run += w[e];
+        if (run > tau) found = (int)threadIdx.x * PER + e;
       }
     }
+    s_tok = b0 + found;
   }
   __syncthreads();
-  return s_found;
-}
-
-struct ChunkSum {
-  const uint64_t* c;
-  __device__ uint64_t operator()(int j) const { return c[j]; }
-};
-struct ProbWeight {
-  const float* p;
-  __device__ uint64_t operator()(int j) const { return prob_weight(p[j]); }
-};
-
-__global__ __launch_bounds__(SMX_THREADS) void sample_locate_kernel(const float* probs,
-                                                                    const uint64_t* csum,
-                                                                    const uint64_t* words, int V,
-                                                                    int nchunks, int32_t* token) {
-  __shared__ uint64_t sh[SMX_THREADS];
-  __shared__ uint64_t s_tau;
-  const int r = blockIdx.x;
-  const uint64_t* cs = csum + (size_t)r * nchunks;
-  uint64_t mine = 0;
-  for (int k = threadIdx.x; k < nchunks; k += SMX_THREADS) mine += cs[k];
-  mine = wave_sum_u64(mine);
-  __shared__ uint64_t s_w[SMX_THREADS / 64];
-  if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = mine;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint64_t S = 0;
-    for (int w = 0; w < SMX_THREADS / 64; ++w) S += s_w[w];
-    s_tau = scale_u32((uint32_t)(words[r] >> 32), S);
-  }
-  __syncthreads();
-  const uint64_t tau = s_tau;
-  const int c = block_locate(ChunkSum{cs}, nchunks, 0, tau, sh);
-  int tok = 0;
-  if (c >= 0) {
-    uint64_t off = 0;  // weight before chunk c (same fixed-order sum as the scan)
-    __shared__ uint64_t s_off;
-    uint64_t part = 0;
-    for (int k = threadIdx.x; k < c; k += SMX_THREADS) part += cs[k];
-    part = wave_sum_u64(part);
-    if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = part;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      for (int w = 0; w < SMX_THREADS / 64; ++w) off += s_w[w];
-      s_off = off;
-    }
-    __syncthreads();
-    const int b0 = c * SMX_CHUNK;
-    const int j = block_locate(ProbWeight{probs + (size_t)r * V + b0}, min(SMX_CHUNK, V - b0), s_off,
-                               tau, sh);
-    tok = j < 0 ? 0 : b0 + j;
-  }
-  if (threadIdx.x == 0) token[r] = tok;
+  if (threadIdx.x == 0) token[r] = s_tok < 0 ? 0 : s_tok;
+  SPD_MARK(4);
 }
 
 struct LmPlan {
@@ -328,7 +450,7 @@ struct LmPlan {
   int J;
   GemmPlan gp;
   int nstat, nchunks;
-  size_t off_part, off_stat, off_csum, total;
+  size_t off_part, off_stat, off_gstat, off_csum, total;
 };
 
 static LmPlan plan_lm(const spd_config* c, int rows) {
@@ -338,12 +460,13 @@ static LmPlan plan_lm(const spd_config* c, int rows) {
   p.J = c->d / 512;
   p.gp = plan_gemm(c->V, c->d, rows, bf ? Mfma<bf16>::KSTEP : Mfma<float>::KSTEP, bf ? 2 : 4, 2,
                    /*target=*/1, /*min_steps=*/1 << 30);
-  p.nstat = p.dot ? (c->V + 4 * DOT_ROWS - 1) / (4 * DOT_ROWS) : p.gp.nblocks;
+    p.nstat = p.dot ? (c->V + 4 * DOT_ROWS - 1) / (4 * DOT_ROWS) : p.gp.nblocks;
   p.nchunks = (c->V + SMX_CHUNK - 1) / SMX_CHUNK;
   size_t off = SPD_WS_COUNTER_BYTES;
   auto take = [&](size_t b) { size_t r = off; off = align256(off + b); return r; };
   p.off_part = take(!p.dot && p.gp.S > 1 ? (size_t)p.gp.S * rows * c->V * 4 : 0);
   p.off_stat = take((size_t)p.nstat * rows * sizeof(BlockStat));
+  p.off_gstat = take((size_t)rows * sizeof(BlockStat));
   p.off_csum = take((size_t)rows * p.nchunks * 8);
   p.total = off;
   return p;
@@ -365,7 +488,9 @@ static int lm_impl(const spd_config* c, const void* w_lm, const float* h, int ro
   const LmPlan p = plan_lm(c, rows);
   char* w = static_cast<char*>(ws);
   BlockStat* stat = reinterpret_cast<BlockStat*>(w + p.off_stat);
+  unsigned* ctr = reinterpret_cast<unsigned*>(w);
   const float inv_t = T > 0.f ? 1.0f / T : 0.f;
+  const HeadFinish f{ctr + CTR_HEAD, reinterpret_cast<BlockStat*>(w + p.off_gstat), token, T > 0.f ? 0 : 1};
   int rc;
   if (p.dot) {
     switch (p.J) {
@@ -379,6 +504,11 @@ static int lm_impl(const spd_config* c, const void* w_lm, const float* h, int ro
       default: launch_dot<8>(p.nstat, st, w_lm, h, c->V, inv_t, logits, stat); break;
     }
     rc = check_launch();
+    if (rc) return rc;
+    if (T <= 0.f) {
+      hipLaunchKernelGGL(greedy_kernel, dim3(rows), dim3(SMX_THREADS), 0, st, stat, p.nstat, rows, token);
+      return check_launch();
+    }
   } else {
     GemmShape g{};
     g.W = w_lm;
@@ -390,22 +520,15 @@ static int lm_impl(const spd_config* c, const void* w_lm, const float* h, int ro
     g.ldx = p.gp.ldx;
     g.part = reinterpret_cast<float*>(w + p.off_part);
     g.nblocks = p.gp.nblocks;
-    EpiLogits epi{logits, stat, c->V, rows, inv_t};
+    g.counters = ctr;
+    EpiLogits epi{logits, stat, c->V, rows, inv_t, p.gp.nblocks, f};
     rc = launch_gemm<WT, 2>(p.gp, g, InAct<WT, float>{h, c->d}, epi, RowMapStd{}, st);
+    if (rc || T <= 0.f) return rc;
   }
-  if (rc) return rc;
-  if (T <= 0.f) {
-    hipLaunchKernelGGL(lm_argmax_kernel, dim3(rows), dim3(SMX_THREADS), 0, st, stat, p.nstat, rows,
-                       token);
-    return check_launch();
-  }
-  uint64_t* csum = reinterpret_cast<uint64_t*>(w + p.off_csum);
-  hipLaunchKernelGGL(softmax_chunk_kernel, dim3(p.nchunks, rows), dim3(SMX_THREADS), 0, st, stat,
-                     p.nstat, rows, logits, probs, csum, c->V, p.nchunks, inv_t);
-  rc = check_launch();
-  if (rc) return rc;
-  hipLaunchKernelGGL(sample_locate_kernel, dim3(rows), dim3(SMX_THREADS), 0, st, probs, csum, words,
-                     c->V, p.nchunks, token);
+  hipLaunchKernelGGL(softmax_sample_kernel, dim3(p.nchunks, rows), dim3(SMX_THREADS), 0, st, stat,
+                     p.dot ? p.nstat : 0, rows, f.gstat, logits, probs,
+                     reinterpret_cast<uint64_t*>(w + p.off_csum), ctr + CTR_HEAD + 512, words, c->V,
+                     p.nchunks, inv_t, token);
   return check_launch();
 }
 
@@ -424,6 +547,7 @@ extern "C" int spd_lm_head(const spd_config* cfg, const void* w_lm, const float*
   if (temperature > 0.f && (!probs || !words)) return SPD_E_INVALID;
   if (cfg->d % 64) return SPD_E_UNSUPPORTED;
   if ((int64_t)cfg->V * cfg->d > ((int64_t)1 << 40)) return SPD_E_UNSUPPORTED;
+  if (temperature > 0.f && cfg->V > SMX_MAXCH * SMX_CHUNK) return SPD_E_UNSUPPORTED;
   if (!aligned16(w_lm) || !aligned16(h) || !aligned16(ws)) return SPD_E_INVALID;
   if (ws_bytes < lm_head_workspace(cfg, rows)) return SPD_E_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);

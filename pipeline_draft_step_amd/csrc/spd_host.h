@@ -36,11 +36,12 @@ inline int check_config(const spd_config* c) {
 }
 
 constexpr int CTR_FINAL = SPD_WS_COUNTER_BYTES / 4 - 16;  // counter of a second-level arrival
+constexpr int CTR_HEAD = CTR_FINAL - 1024;  // vocabulary-head counters [CTR_HEAD, CTR_FINAL)
 
 template <typename WT, int NT, typename In, typename Epi, typename RM>
 int launch_gemm(const GemmPlan& p, const GemmShape& g, const In& in, const Epi& epi, const RM& rm,
                 hipStream_t st) {
-  if ((size_t)p.mtiles * p.nblocks >= (size_t)CTR_FINAL) return SPD_E_UNSUPPORTED;
+  if ((size_t)p.mtiles * p.nblocks >= (size_t)CTR_HEAD) return SPD_E_UNSUPPORTED;
   if ((size_t)p.S * g.M * g.N * 4 >= ((size_t)1 << 31)) return SPD_E_UNSUPPORTED;  // 32-bit offsets
   GemmShape gs = g;
   gs.x_bytes = p.x_bytes;
