@@ -30,10 +30,18 @@ constexpr int ATT_MAXCH = 256;                  // chunks per row: context up to
 
 // h = g, per-64-column partial sums of squares of every row, and the first QKV
 // GEMM's input g * attn_norm as an XSplit (its RMSNorm row scale comes from ss)
+// Blocks with nb == 0 also write the rotate-half RoPE table of the row's
+// position, rope[r][i] = (cos, sin)(pos * theta^(-2i/hd)), i < hd/2, in fp64.
 template <typename WT>
 __global__ __launch_bounds__(64) void rows_init_kernel(const float* g, float* h, float* ss, int M,
-                                                       int d, XSplit<WT> xo, const WT* gamma) {
+                                                       int d, XSplit<WT> xo, const WT* gamma,
+                                                       float2* rope, int pos0, int hd, float theta) {
   const int nb = blockIdx.x, r = blockIdx.y, lane = threadIdx.x;
+  if (nb == 0 && lane < hd / 2) {
+    double sn, cs;
+    sincos((double)(pos0 + r) * pow((double)theta, -2.0 * lane / hd), &sn, &cs);
+    rope[(size_t)r * (hd / 2) + lane] = make_float2((float)cs, (float)sn);
+  }
   const int col = nb * 64 + lane;
   const size_t i = (size_t)r * d + col;
   const float v = g[i];
@@ -51,9 +59,10 @@ struct EpiQKV {
   WT* vc;       // [Hkv][hd][T_cap]
   const WT* qn;
   const WT* kn;
+  const float2* rope;  // [M][hd/2] (cos, sin) of each row's position
   int Hq, Hkv, hd, pos0;
   int64_t T_cap;
-  float eps, theta;
+  float eps;
   template <int MT, int NT, typename Y, typename RM>
   __device__ void run(const Y& y, int nb, int m0, int Mt, const RM&) const {
     constexpr int TC = 64 * NT;
@@ -61,8 +70,8 @@ struct EpiQKV {
     const int nheads = Hq + 2 * Hkv;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int half = hd >> 1;
-    // rotate-half frequency of this lane's element: theta^(-2i/hd), i = element mod hd/2
-    const double invf = pow((double)theta, -2.0 * (hd == 128 ? lane : (lane & (half - 1))) / hd);
+    const int fi = hd == 128 ? lane : (lane & (half - 1));  // frequency index of this lane
+    const int l0 = min(lane, hd - 1), l1 = min(lane + 64, hd - 1);  // clamped: loads stay unconditional
     for (int it = wave; it < Mt * hpb; it += GEMM_WAVES) {
       const int mm = it / hpb, hl = it - mm * hpb;
       const int hh = nb * hpb + hl;
@@ -73,21 +82,19 @@ struct EpiQKV {
       float v1 = e1 ? y(mm, hl * hd + lane + 64) : 0.f;
       if (hh < Hq + Hkv) {
         const WT* nw = hh < Hq ? qn : kn;
+        const float w0 = to_f<WT>(nw[l0]), w1 = to_f<WT>(nw[l1]);
+        const float2 cs = rope[(size_t)r * half + fi];
         const float inv = 1.0f / sqrtf(wave_sum(v0 * v0 + v1 * v1) / (float)hd + eps);
-        v0 = e0 ? v0 * inv * to_f<WT>(nw[lane]) : 0.f;
-        v1 = e1 ? v1 * inv * to_f<WT>(nw[lane + 64]) : 0.f;
+        v0 = e0 ? v0 * inv * w0 : 0.f;
+        v1 = e1 ? v1 * inv * w1 : 0.f;
         // rotate-half: element i pairs with i + hd/2 at angle pos * theta^(-2i/hd)
         if (hd == 128) {
-          double s, c;
-          sincos((double)pos * invf, &s, &c);
           const float x1 = v0, x2 = v1;
-          v0 = x1 * (float)c - x2 * (float)s;
-          v1 = x2 * (float)c + x1 * (float)s;
+          v0 = x1 * cs.x - x2 * cs.y;
+          v1 = x2 * cs.x + x1 * cs.y;
         } else {
           const float other = __shfl_xor(v0, half, WAVE);
-          double s, c;
-          sincos((double)pos * invf, &s, &c);
-          v0 = lane < half ? v0 * (float)c - other * (float)s : v0 * (float)c + other * (float)s;
+          v0 = lane < half ? v0 * cs.x - other * cs.y : v0 * cs.x + other * cs.y;
         }
       }
       if (hh < Hq) {
@@ -378,7 +385,7 @@ L = row16_sum(L);
 struct PdmPlan {
   GemmPlan qkv, o, gu, down;
   int nch, QR;
-  size_t off_h, off_ss, off_q, off_po, off_pml, off_x0h, off_x0l, off_x1h, off_x1l, off_part, total;
+  size_t off_h, off_ss, off_q, off_rope, off_po, off_pml, off_x0h, off_x0l, off_x1h, off_x1l, off_part, total;
   int ld1;  // row stride of the second XSplit buffer
 };
 
@@ -398,6 +405,7 @@ static PdmPlan plan_pdm(const spd_config* c, int M, int64_t T_cap) {
   p.off_h = take((size_t)M * c->d * 4);
   p.off_ss = take((size_t)(c->d / 64) * M * 4);
   p.off_q = take((size_t)M * c->Hq * c->hd * 4);
+  p.off_rope = take((size_t)M * (c->hd / 2) * 8);
   p.off_po = take((size_t)c->Hkv * p.QR * p.nch * c->hd * 4);
   p.off_pml = take((size_t)c->Hkv * p.QR * p.nch * 8);
   // XSplit GEMM inputs: x0 feeds QKV and gate/up (width d), x1 feeds O and down
@@ -471,8 +479,9 @@ static int pdm_impl(const spd_config* c, const spd_layer_weights* layers, const 
   const XSplit<WT> x1{reinterpret_cast<WT*>(w + p.off_x1h), reinterpret_cast<WT*>(w + p.off_x1l), p.ld1};
   const XSplit<WT> none{nullptr, nullptr, 0};
 
+  float2* rope = reinterpret_cast<float2*>(w + p.off_rope);
   hipLaunchKernelGGL((rows_init_kernel<WT>), dim3(d / 64, M), dim3(64), 0, st, g, h, ss, M, d, x0,
-                     static_cast<const WT*>(layers[0].attn_norm));
+                     static_cast<const WT*>(layers[0].attn_norm), rope, pos0, hd, c->rope_theta);
   int rc = check_launch();
   if (rc) return rc;
   int P = d / 64;  // partial count of ss
@@ -502,7 +511,7 @@ static int pdm_impl(const spd_config* c, const spd_layer_weights* layers, const 
     {
       InSplit<WT, RS_SS> in{x0.hi, x0.lo, d};
       EpiQKV<WT> epi{qb, kc, vc, static_cast<const WT*>(lw.q_norm), static_cast<const WT*>(lw.k_norm),
-                     Hq, Hkv, hd, pos0, T_cap, c->rms_eps, c->rope_theta};
+                     rope, Hq, Hkv, hd, pos0, T_cap, c->rms_eps};
       rc = launch_gemm<WT, 2>(p.qkv, shape_of(p.qkv, lw.wqkv, nq, d, M, part, ctr, ss, P, c->rms_eps),
                               in, epi, RowMapStd{}, st);
       if (rc) return rc;
