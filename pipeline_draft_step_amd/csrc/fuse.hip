@@ -6,13 +6,16 @@
 //
 // Two launches.  The gather kernel reads each row's eligible anchor states from
 // the anchor store (empty slots are zeros; the k = 0 rows read slot 0 only,
-// without gamma), writes gamma * x as the FC's pre-split bf16 hi/lo input and,
-// in the last block of each row, the row's 1/rms over its filled slots.  The
-// skinny GEMM then streams W_fc; because FC is linear,
-// W (gamma * x / rms) = (W (gamma * x)) / rms, the row scale is applied to the
-// product tile.
+// without gamma), writes gamma * x as the FC's input and, in the last block of
+// each row, the row's 1/rms over its filled slots.  Because FC is linear,
+// W (gamma * x / rms) = (W (gamma * x)) / rms, so the row scale is applied to
+// the product tile.  Decode-sized calls stream W_fc through the skinny GEMM,
+// which takes the input pre-split into bf16 hi/lo parts (fp32-accurate
+// activations); prefill-sized calls in bf16 run the MFMA-tiled large-M GEMM,
+// which takes the bf16-rounded input as a plain bf16 operand.
 #include "spd_common.h"
 #include "spd_gemm.h"
+#include "spd_gemm_big.h"
 #include "spd_host.h"
 
 namespace spd {
@@ -45,7 +48,7 @@ struct GatherArgs {
 
 // Block (column block cb, row r); each thread owns 8 consecutive columns, which
 // never straddle two anchors (d % 64 == 0).
-template <typename WT>
+template <typename WT, bool HI_ONLY>
 __global__ __launch_bounds__(256) void feature_gather_kernel(GatherArgs<WT> f) {
   __shared__ int8_t s_tab[TABN];
   __shared__ float s_red[4];
@@ -89,8 +92,15 @@ __global__ __launch_bounds__(256) void feature_gather_kernel(GatherArgs<WT> f) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) sq += x[e] * x[e];
   if (inb) {
-    f.xo.put4(r, col, make_float4(x[0] * gm[0], x[1] * gm[1], x[2] * gm[2], x[3] * gm[3]));
-    f.xo.put4(r, col + 4, make_float4(x[4] * gm[4], x[5] * gm[5], x[6] * gm[6], x[7] * gm[7]));
+    const float4 lo4 = make_float4(x[0] * gm[0], x[1] * gm[1], x[2] * gm[2], x[3] * gm[3]);
+    const float4 hi4 = make_float4(x[4] * gm[4], x[5] * gm[5], x[6] * gm[6], x[7] * gm[7]);
+    if constexpr (HI_ONLY) {
+      f.xo.put4_hi(r, col, lo4);
+      f.xo.put4_hi(r, col + 4, hi4);
+    } else {
+      f.xo.put4(r, col, lo4);
+      f.xo.put4(r, col + 4, hi4);
+    }
   }
   SPD_MARK(1);
   sq = wave_sum(sq);
@@ -129,8 +139,36 @@ struct EpiRows {
   }
 };
 
+// Large-M path: bf16 only, for prefill-sized M, when the K range splits into
+// whole 64-wide stages.  KS splits K so that the tiles times KS fill the GPU.
+constexpr int FUSE_BIG_MIN_M = 256;
+constexpr int FUSE_BIG_TARGET_BLOCKS = 256;
+
+struct BigPlan {
+  bool use;
+  int mtiles, ntiles, KS, kstages;
+};
+
+static BigPlan plan_big(const spd_config* cfg, int M) {
+  BigPlan b{};
+  const int K = cfg->m * cfg->d, N = cfg->d;
+  if (cfg->dtype != SPD_BF16 || M < FUSE_BIG_MIN_M || K % BG_BK) return b;
+  b.mtiles = (M + BG_BM - 1) / BG_BM;
+  b.ntiles = (N + BG_BN - 1) / BG_BN;
+  const int stages = K / BG_BK;
+  if (stages < BG_SLOTS) return b;
+  b.KS = 1;
+  while (b.KS < BG_MAX_KS && b.mtiles * b.ntiles * b.KS * 2 <= FUSE_BIG_TARGET_BLOCKS &&
+         stages % (b.KS * 2) == 0 && stages / (b.KS * 2) >= BG_SLOTS)
+    b.KS *= 2;
+  b.kstages = stages / b.KS;
+  b.use = true;
+  return b;
+}
+
 struct FusePlan {
   GemmPlan gp;
+  BigPlan big;
   int ncb;
   size_t off_part, off_inv, off_xh, off_xl, off_gpart, total;
 };
@@ -141,6 +179,7 @@ static FusePlan plan_fuse(const spd_config* cfg, int M) {
   const int kstep = bf ? Mfma<bf16>::KSTEP : Mfma<float>::KSTEP;
   const int es = bf ? 2 : 4;
   const size_t K = (size_t)cfg->m * cfg->d;
+  p.big = plan_big(cfg, M);
   p.gp = plan_gemm(cfg->d, (int)K, M, kstep, es, 1);
   p.ncb = (int)((K + GATHER_COLS - 1) / GATHER_COLS);
   size_t off = SPD_WS_COUNTER_BYTES;
@@ -148,8 +187,13 @@ static FusePlan plan_fuse(const spd_config* cfg, int M) {
   p.off_part = take((size_t)p.ncb * M * 4);
   p.off_inv = take((size_t)M * 4);
   p.off_xh = take((size_t)M * K * es);
-  p.off_xl = take(bf ? (size_t)M * K * es : 0);
-  p.off_gpart = take(p.gp.S > 1 ? (size_t)p.gp.S * M * cfg->d * 4 : 0);
+  if (p.big.use) {
+    p.off_xl = take(0);
+    p.off_gpart = take(p.big.KS > 1 ? (size_t)p.big.mtiles * p.big.ntiles * p.big.KS * BG_PART_FLOATS * 4 : 0);
+  } else {
+    p.off_xl = take(bf ? (size_t)M * K * es : 0);
+    p.off_gpart = take(p.gp.S > 1 ? (size_t)p.gp.S * M * cfg->d * 4 : 0);
+  }
   p.total = off;
   return p;
 }
@@ -182,7 +226,36 @@ static int fuse_impl(const spd_config* cfg, const void* hstore, int64_t T_cap, i
   ga.ncb = p.ncb;
   ga.eps = cfg->rms_eps;
   ga.depth = RowDepth{M, a, n};
-  hipLaunchKernelGGL((feature_gather_kernel<WT>), dim3(p.ncb, M), dim3(256), 0, st, ga);
+  if (p.big.use) {
+    if constexpr (sizeof(WT) == 2) {
+      hipLaunchKernelGGL((feature_gather_kernel<WT, true>), dim3(p.ncb, M), dim3(256), 0, st, ga);
+      int rc = check_launch();
+      if (rc) return rc;
+      // the gather's row counters are back at zero when it ends, so the GEMM
+      // reuses the start of the counter region for its tile counters
+      BigGemm bgm{};
+      bgm.A = reinterpret_cast<const bf16*>(ga.xo.hi);
+      bgm.B = static_cast<const bf16*>(fc_w);
+      bgm.C = g;
+      bgm.rs = ga.inv;
+      bgm.part = reinterpret_cast<float*>(w + p.off_gpart);
+      bgm.counters = reinterpret_cast<unsigned*>(w);
+      bgm.M = M;
+      bgm.N = d;
+      bgm.K = m * d;
+      bgm.lda = m * d;
+      bgm.ldb = m * d;
+      bgm.ldc = d;
+      bgm.mtiles = p.big.mtiles;
+      bgm.ntiles = p.big.ntiles;
+      bgm.KS = p.big.KS;
+      bgm.kstages = p.big.kstages;
+      hipLaunchKernelGGL(gemm_big_kernel, dim3(p.big.mtiles * p.big.ntiles * p.big.KS), dim3(BG_THREADS), 0,
+                         st, bgm);
+      return check_launch();
+    }
+  }
+  hipLaunchKernelGGL((feature_gather_kernel<WT, false>), dim3(p.ncb, M), dim3(256), 0, st, ga);
   int rc = check_launch();
   if (rc) return rc;
 
@@ -215,7 +288,7 @@ extern "C" int spd_fuse_features(const spd_config* cfg, const void* hstore, int6
   if (!hstore || !slot_tab || !norm_w || !fc_w || !g || !ws) return SPD_E_INVALID;
   if (M < 1 || pos0 < 0 || T_cap < 1 || (int64_t)pos0 + M > T_cap || S < 1) return SPD_E_INVALID;
   if (a < 0 || a > cfg->n || a > M) return SPD_E_INVALID;
-  if (M >= CTR_FINAL) return SPD_E_UNSUPPORTED;  // one arrival counter per row
+  if (M >= CTR_FINAL) return SPD_E_UNSUPPORTED;  // one arrival counter per row (and per GEMM tile)
   if (cfg->d % 64) return SPD_E_UNSUPPORTED;
   for (int i = 0; i < (cfg->n + 1) * cfg->m; ++i)
     if (slot_tab[i] < -1 || slot_tab[i] >= S) return SPD_E_INVALID;

@@ -235,6 +235,13 @@ __device__ __forceinline__ void st_coh4(float* p, float4 v) {
   st_coh_u64(q + 1, __builtin_bit_cast(uint64_t, make_float2(v.z, v.w)));
 }
 
+// 16-byte coherent store at byte offset `off` from a wave-uniform base (one
+// buffer_store_dwordx4 with the same cache policy as the st_coh stores)
+__device__ __forceinline__ void st_coh4b(void* base, uint32_t off, float4 v) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 16);
+}
+
 // Every thread of the block calls this after its st_coh stores.  Returns true in
 // exactly one of the `expected` blocks sharing `counter`, after all of them have
 // arrived; that block resets the counter to zero for the next use.

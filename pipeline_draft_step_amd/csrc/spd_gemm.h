@@ -562,6 +562,14 @@ struct XSplit {
       hi[(size_t)m * ld + k] = v;
     }
   }
+  // the rounded value only (for consumers that take bf16 operands as they are)
+  __device__ __forceinline__ void put4_hi(int m, int k, float4 v) const {
+    if constexpr (sizeof(WT) == 2) {
+      *reinterpret_cast<uint2*>(hi + (size_t)m * ld + k) = make_uint2(pack2_bf16(v.x, v.y), pack2_bf16(v.z, v.w));
+    } else {
+      *reinterpret_cast<float4*>(hi + (size_t)m * ld + k) = v;
+    }
+  }
   __device__ __forceinline__ void put4(int m, int k, float4 v) const {
     if constexpr (sizeof(WT) == 2) {
       const uint32_t h0 = pack2_bf16(v.x, v.y), h1 = pack2_bf16(v.z, v.w);

@@ -1,0 +1,254 @@
+// Large-M GEMM for prefill-sized products: C[M][N] = rs[m] * (A[M][K] . B[N][K]^T),
+// A and B bf16 with K contiguous (A = activations, B = weights), C fp32.
+//
+// Block tile 256 x 160, eight waves, two per SIMD: wave v owns rows
+// 64 (v % 4) .. +63 and columns 80 (v / 4) .. +79 as 4 x 5 tiles of the
+// 16x16x32 bf16 MFMA (80 accumulator registers).  With two waves on each SIMD
+// one wave's LDS reads and load issue overlap the other's MFMAs.  K advances in
+// 64-wide stages through a ring of three LDS buffers filled with direct
+// global->LDS loads (global_load_lds_dwordx4: lane l of an instruction lands at
+// LDS offset 16 l) two stages ahead; each wave spreads its share of a stage's
+// loads through its MFMAs.  A tile row is 128 bytes held as eight 16-byte
+// chunks in the order chunk ^ (row & 7) ^ ((row >> 3) & 1), which keeps the
+// fragment reads free of bank conflicts.
+//
+// Large tiles halve the bytes each CU pulls through its load path per flop, and
+// the K range is split KS ways to still give every CU a block: the KS blocks of
+// one tile write fp32 partial tiles, and the last one to arrive adds them in
+// the fixed order 0 .. KS-1 and writes C.  Blocks are dealt to the XCDs round
+// robin (block b runs on XCD b mod 8); block ids are remapped so that each XCD
+// holds all KS parts of its tiles and a compact patch of tiles, which keeps the
+// partials and the shared operand rows in that XCD's L2.
+#pragma once
+
+#include "spd_common.h"
+
+namespace spd {
+
+constexpr int BG_BM = 256, BG_BN = 160, BG_BK = 64;
+constexpr int BG_THREADS = 512;
+constexpr int BG_SLOTS = 3;
+constexpr int BG_ROW = BG_BK * 2;                 // bytes per tile row and stage
+constexpr int BG_A_BYTES = BG_BM * BG_ROW;        // 32 KB
+constexpr int BG_B_BYTES = BG_BN * BG_ROW;        // 20 KB
+constexpr int BG_STAGE_BYTES = BG_A_BYTES + BG_B_BYTES;
+constexpr int BG_A_GROUPS = BG_A_BYTES / 1024;    // 1 KB load groups of a stage
+constexpr int BG_GROUPS = BG_STAGE_BYTES / 1024;  // 52
+constexpr int BG_WAVES = BG_THREADS / 64;
+constexpr int BG_LOADS = (BG_GROUPS + BG_WAVES - 1) / BG_WAVES;  // per wave and stage: 7
+constexpr int BG_MFMAS = 2 * 4 * 5;                              // per wave and stage
+constexpr int BG_FRAGS = 20;                      // 16x16 accumulator tiles per wave
+constexpr int BG_PART_FLOATS = BG_BM * BG_BN;     // one partial tile
+constexpr int BG_MAX_KS = 4;
+static_assert(BG_SLOTS * BG_STAGE_BYTES <= 160 * 1024, "LDS ring");
+
+struct BigGemm {
+  const bf16* A;       // [M][lda]
+  const bf16* B;       // [N][ldb]
+  float* C;            // [M][ldc]
+  const float* rs;     // [M] row scales, or nullptr
+  float* part;         // [tiles][KS][BG_PART_FLOATS] when KS > 1
+  unsigned* counters;  // [tiles], zero on entry, left zero
+  int M, N, K, lda, ldb, ldc;
+  int mtiles, ntiles, KS;
+  int kstages;  // 64-wide K stages per block (K / (64 KS))
+};
+
+typedef f32x4 BgAccT;
+
+typedef void __attribute__((address_space(3))) * lds_ptr_t;
+
+__device__ __forceinline__ int bg_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// Wave v issues its share of the loads of K stage `st` into the stage buffer
+// `base`: 1 KB groups (8 tile rows) v, v + 8, ...; the 52 groups do not split
+// evenly, so waves 4 .. 7 repeat one of their own groups (same bytes to the
+// same place) instead of taking a branch.
+__device__ __forceinline__ void bg_issue(const BigGemm& g, unsigned char* base, int st, int m0, int n0,
+                                         int v, int lane) {
+  const int k0 = st * BG_BK;
+  const int rin = lane >> 3, pc = lane & 7;  // row within the group, physical chunk
+#pragma unroll
+  for (int i = 0; i < BG_LOADS; ++i) {
+    int q = v + BG_WAVES * i;
+    if (i == BG_LOADS - 1) q = q < BG_GROUPS ? q : v;
+    const bool isA = q < BG_A_GROUPS;
+    const int r = 8 * (isA ? q : q - BG_A_GROUPS) + rin;  // tile row
+    const int c = pc ^ bg_swz(r);
+    const bf16* src = isA ? g.A + (size_t)min(m0 + r, g.M - 1) * g.lda
+                          : g.B + (size_t)min(n0 + r, g.N - 1) * g.ldb;
+    __builtin_amdgcn_global_load_lds((const void*)(src + k0 + 8 * c), (lds_ptr_t)(base + q * 1024), 16, 0, 0);
+  }
+}
+
+// s_waitcnt vmcnt(N), other counters left alone (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void bg_wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+}
+
+// The MFMAs of one stage for wave (wm, wn).  16x16x32 operand layout: lane l
+// supplies row l % 16 and k = 8 (l / 16) .. +7 of the 32-wide k step; the B
+// tile is stored [n][k], so both operands are read the same way.
+__device__ __forceinline__ void bg_compute(const unsigned char* sa, BgAccT (&acc)[BG_FRAGS], int wm, int wn,
+                                           int lane) {
+  const unsigned char* sb = sa + BG_A_BYTES;
+  const int lr = lane & 15, lq = lane >> 4;
+#pragma unroll
+  for (int kk = 0; kk < BG_BK / 32; ++kk) {
+    const int c = 4 * kk + lq;  // logical 16-byte chunk
+    u32x4 af[4], bfr[5];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wm * 64 + i * 16 + lr;
+      af[i] = *reinterpret_cast<const u32x4*>(sa + r * BG_ROW + 16 * (c ^ bg_swz(r)));
+    }
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+      const int r = wn * 80 + j * 16 + lr;
+      bfr[j] = *reinterpret_cast<const u32x4*>(sb + r * BG_ROW + 16 * (c ^ bg_swz(r)));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 5; ++j)
+        acc[i * 5 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, af[i]),
+                                                                 __builtin_bit_cast(bf16x8_v, bfr[j]),
+                                                                 acc[i * 5 + j], 0, 0, 0);
+  }
+}
+
+// One K stage held in ring slot `cur`; `nxt` (the slot of stage s - 1, free
+// once every wave has passed the barrier) receives stage s + 2.  The loads are
+// unconditional (past the end they re-read the last stage into the free slot),
+// so the whole step is one scheduling region and the wait counts never change;
+// the group barriers spread the wave's loads through its MFMAs.
+#define BG_STEP(cur, nxt)                                                           \
+  do {                                                                              \
+    bg_wait_vm<BG_LOADS>();                                                         \
+    __builtin_amdgcn_s_barrier();                                                   \
+    bg_issue(g, nxt, kbeg + min(s + BG_SLOTS - 1, ns - 1), m0, n0, wave, lane);     \
+    bg_compute(cur, acc, wm, wn, lane);                                             \
+    _Pragma("unroll") for (int r_ = 0; r_ < BG_LOADS - 1; ++r_) {                   \
+      __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);                            \
+      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                            \
+    }                                                                               \
+    __builtin_amdgcn_sched_group_barrier(0x008, BG_MFMAS - 6 * (BG_LOADS - 1), 0);  \
+    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                              \
+    ++s;                                                                            \
+  } while (0)
+
+__global__ __launch_bounds__(BG_THREADS) void gemm_big_kernel(BigGemm g) {
+  // one array per ring slot: separate objects let the compiler tell the
+  // direct-to-LDS writes of later stages from the reads of the current one
+  __shared__ __align__(1024) unsigned char s0[BG_STAGE_BYTES];
+  __shared__ __align__(1024) unsigned char s1[BG_STAGE_BYTES];
+  __shared__ __align__(1024) unsigned char s2[BG_STAGE_BYTES];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave & 3, wn = wave >> 2;
+
+  const int KS = g.KS;
+  const int T = g.mtiles * g.ntiles * KS;
+  const int b = blockIdx.x;
+  const int tb = (T % 8 == 0) ? (b % 8) * (T / 8) + b / 8 : b;
+  const int kh = tb % KS, u = tb / KS;
+  constexpr int GM = 4;  // M-tiles per group: a run of consecutive u covers GM x (run / GM) tiles
+  const int grp = u / (GM * g.ntiles), first_m = grp * GM;
+  const int gsz = min(g.mtiles - first_m, GM);
+  const int tin = u - grp * GM * g.ntiles;
+  const int mt = first_m + tin % gsz, nt = tin / gsz;
+  const int m0 = mt * BG_BM, n0 = nt * BG_BN;
+  const int ns = g.kstages, kbeg = kh * ns;  // the host guarantees ns >= BG_SLOTS
+
+  bg_issue(g, s0, kbeg, m0, n0, wave, lane);
+  bg_issue(g, s1, kbeg + 1, m0, n0, wave, lane);
+
+  BgAccT acc[BG_FRAGS];
+#pragma unroll
+  for (int f = 0; f < BG_FRAGS; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  int s = 0;
+  while (s + BG_SLOTS <= ns) {
+    BG_STEP(s0, s2);
+    BG_STEP(s1, s0);
+    BG_STEP(s2, s1);
+  }
+  if (s < ns) BG_STEP(s0, s2);
+  if (s < ns) BG_STEP(s1, s0);
+  // the surplus loads of the last steps must land before the block's LDS is released
+  bg_wait_vm<0>();
+
+  // accumulator register e of tile (i, j): row 64 wm + 16 i + 4 (lane / 16) + e,
+  // column 80 wn + 16 j + lane % 16
+  const int lr = lane & 15, lq = lane >> 4;
+  if (KS > 1) {
+    // partial tile as [wave][f][lane][e]: every store is 1 KB contiguous
+    float* mine = g.part + ((size_t)u * KS + kh) * BG_PART_FLOATS + (size_t)wave * (BG_FRAGS * 256);
+#pragma unroll
+    for (int f = 0; f < BG_FRAGS; ++f)
+      st_coh4b(mine, (uint32_t)((f * 256 + lane * 4) * 4), make_float4(acc[f][0], acc[f][1], acc[f][2], acc[f][3]));
+    if (!arrive_last(g.counters + u, (unsigned)KS)) return;
+    // the sum runs over the parts in the order 0 .. KS-1 whichever block is
+    // last; with two parts a + b == b + a, so the own part stays in registers
+    const float* base = g.part + (size_t)u * KS * BG_PART_FLOATS + (size_t)wave * (BG_FRAGS * 256);
+    if (KS > 2) {
+#pragma unroll
+      for (int f = 0; f < BG_FRAGS; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int p = 0; p < KS; ++p) {
+      if (KS == 2 && p == kh) continue;
+      const float* src = base + (size_t)p * BG_PART_FLOATS;
+      float4 v[BG_FRAGS];
+#pragma unroll
+      for (int f = 0; f < BG_FRAGS; ++f) v[f] = ld_coh4(src, (uint32_t)((f * 256 + lane * 4) * 4));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int f = 0; f < BG_FRAGS; ++f) {
+        acc[f][0] += v[f].x;
+        acc[f][1] += v[f].y;
+        acc[f][2] += v[f].z;
+        acc[f][3] += v[f].w;
+      }
+    }
+  }
+  // the 16 row scales of this lane, loaded together before any store
+  float rsv[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = m0 + wm * 64 + 16 * i + 4 * lq + e;
+      rsv[i][e] = g.rs ? g.rs[min(row, g.M - 1)] : 1.f;
+    }
+  const bool full = m0 + BG_BM <= g.M && n0 + BG_BN <= g.N;
+  if (full) {
+    // no bounds checks: one straight run of stores
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float* crow = g.C + (size_t)(m0 + wm * 64 + 16 * i + 4 * lq + e) * g.ldc + n0 + wn * 80 + lr;
+#pragma unroll
+        for (int j = 0; j < 5; ++j) crow[16 * j] = acc[i * 5 + j][e] * rsv[i][e];
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = m0 + wm * 64 + 16 * i + 4 * lq + e;
+        if (row < g.M) {
+#pragma unroll
+          for (int j = 0; j < 5; ++j) {
+            const int col = n0 + wn * 80 + 16 * j + lr;
+            if (col < g.N) g.C[(size_t)row * g.ldc + col] = acc[i * 5 + j][e] * rsv[i][e];
+          }
+        }
+      }
+  }
+}
+
+#undef BG_STEP
+
+}  // namespace spd

@@ -17,7 +17,8 @@ from . import (SPD_BF16, SPD_CALL_FUSE, SPD_CALL_LM_HEAD, SPD_CALL_PDM, SPD_CALL
                layer_weights, make_config, spd_fuse_features, spd_lm_head, spd_pdm_step,
                spd_rollback, spd_slot_table, spd_verify, spd_workspace_size)
 
-PREFILL_BLOCK = 256
+PREFILL_BLOCK = 256   # rows per PDM prefill call
+FEATURE_BLOCK = 2048  # rows per prefill feature call (one large-M FC GEMM)
 
 
 @dataclass
@@ -59,6 +60,7 @@ class SpdCycle:
         wdt = torch.bfloat16 if c.dtype == SPD_BF16 else torch.float32
         T_cap = model.T_cap
         self.g = torch.empty(max(c.n + 1, PREFILL_BLOCK), c.d, device=device)
+        self.g_pre = torch.empty(min(FEATURE_BLOCK, T_cap), c.d, device=device)
         self.h_last = torch.empty(c.d, device=device)
         self.k_cache = torch.zeros(c.Ls, c.Hkv, T_cap, c.hd, dtype=wdt, device=device)
         self.v_cache = torch.zeros(c.Ls, c.Hkv, c.hd, T_cap, dtype=wdt, device=device)
@@ -72,7 +74,8 @@ class SpdCycle:
         self.next_token = torch.zeros(1, dtype=torch.int32, device=device)
         self.state = torch.zeros(4, dtype=torch.int32, device=device)
         self.tokens = torch.zeros(T_cap, dtype=torch.int32, device=device)
-        ws = max(spd_workspace_size(SPD_CALL_FUSE, c, PREFILL_BLOCK),
+        ws = max(spd_workspace_size(SPD_CALL_FUSE, c, min(FEATURE_BLOCK, T_cap)),
+                 spd_workspace_size(SPD_CALL_FUSE, c, PREFILL_BLOCK),
                  spd_workspace_size(SPD_CALL_PDM, c, PREFILL_BLOCK, 0, T_cap),
                  spd_workspace_size(SPD_CALL_FUSE, c, c.n + 1),
                  spd_workspace_size(SPD_CALL_PDM, c, c.n + 1, 0, T_cap),
@@ -103,11 +106,14 @@ class SpdCycle:
         return self.h_last
 
     def prefill(self, P: int):
-        """Key/value cache of positions 0..P-1, all fully processed (depth n)."""
-        for s in range(0, P, PREFILL_BLOCK):
-            M = min(PREFILL_BLOCK, P - s)
-            self.features(s, M, 0)
-            self.pdm(s, M)
+        """Key/value cache of positions 0..P-1, all fully processed (depth n): the
+        features of up to FEATURE_BLOCK rows in one call, then the PDM in blocks."""
+        for s in range(0, P, FEATURE_BLOCK):
+            Mf = min(FEATURE_BLOCK, P - s)
+            self.features(s, Mf, 0, out=self.g_pre)
+            for b in range(0, Mf, PREFILL_BLOCK):
+                M = min(PREFILL_BLOCK, Mf - b)
+                self.pdm(s + b, M, g=self.g_pre[b:b + M])
 
     def draft(self, t, words_block):
         """Draft head on h_last; at T > 0 the q row goes to ring[t % n]."""

@@ -82,6 +82,46 @@ def test_fuse_features(name, shape, layouts):
         assert err < tol_for(shape.dtype), (t, a, err)
 
 
+PREFILL_FUSE_CASES = [
+    # (name, shape, M, rows checked: None = all)
+    ("small_prefill", SMALL_BF16.with_(ctx=320), 300, None),
+    ("small_prefill_h64", SMALL_BF16_H64.with_(ctx=600), 520, None),
+    ("headline_prefill", synth.HEADLINE, 2048, 48),
+    ("headline_prefill_ragged", synth.HEADLINE, 2039, 24),
+]
+
+
+@pytest.mark.parametrize("name,shape,M,nsample", PREFILL_FUSE_CASES,
+                         ids=[c[0] for c in PREFILL_FUSE_CASES])
+def test_fuse_features_prefill(name, shape, M, nsample):
+    """Prefill-sized calls (every row at depth n) take the MFMA-tiled large-M GEMM:
+    split-K partial tiles, ragged M and N tiles.  The full headline product is
+    checked on sampled rows (tile edges included), which the oracle computes one
+    by one."""
+    ci = synth.cycle_inputs(shape, device=DEV, with_heads=False)
+    model = device_model(ci)
+    cyc = SpdCycle(model, shape.temperature)
+    om = OC.model_from_inputs(ci, with_heads=False)
+    say(name, "prefill fuse", M)
+    out = torch.full((M, shape.d), float("nan"), device=DEV)
+    for rep in range(2):  # the second call reuses the arrival counters the first left at zero
+        cyc.features(0, M, 0, out=out)
+    torch.cuda.synchronize()
+    if nsample is None:
+        rows = list(range(M))
+    else:
+        rng = np.random.default_rng(5)
+        edges = [0, 1, 255, 256, 511, 512, M // 2, M - 2, M - 1]
+        rows = sorted(set(edges) | set(int(x) for x in rng.choice(M, nsample, replace=False)))
+    ref = O.fuse_features(om.store, om.store_layers, rows, [shape.n] * len(rows), om.fc_norm,
+                          om.w_fc, L=shape.L, n=shape.n, anchors=shape.anchors,
+                          mode=shape.anchor_mode, eps=shape.eps, norm_k0=bool(shape.norm_k0))
+    got = f64(out)[rows]
+    assert np.isfinite(got).all()
+    err = rel_err(got, ref)
+    assert err < tol_for(shape.dtype), (M, err)
+
+
 # ------------------------------------------------------------------ PDM step
 
 def _oracle_cache_from(k, v, pos0, shape):
