@@ -11,6 +11,7 @@ inside the timed region.  Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -23,6 +24,28 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "spd_lm_head_traffic_headline.md")
+
+
+def measured_traffic():
+    """HBM bytes per spd_lm_head launch from the committed counter summary (two
+    rocprofv3 passes, FETCH_SIZE and WRITE_SIZE, scaled by a known-size copy), or
+    None when the summary is missing or the kernel sources changed since."""
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+        blob = text.split("```json", 1)[1].split("```", 1)[0]
+        rec = json.loads(blob)
+        h = hashlib.sha256()
+        for f in rec["sources"]:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        if h.hexdigest() != rec["source_sha256"]:
+            return None
+        return int(rec["traffic_bytes_per_launch"])
+    except (OSError, IndexError, KeyError, ValueError):
+        return None
 
 
 def algorithmic_bytes(s, a: int) -> dict:
@@ -96,6 +119,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="end with a plain 256 MiB device-to-device copy, the known-size "
+                         "reference that scales the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only (the cycle is a single-GPU "
@@ -208,6 +234,28 @@ def main():
             "rollback_us": round(acc[4], 1), "cycle_us": round(acc[5], 1),
             "algorithmic_MB": round(sum(algorithmic_bytes(s, a).values()) / 1e6, 1)}
 
+    # prefill feature call (every row at depth n): the anchor gather plus the
+    # MFMA-tiled large-M FC GEMM, timed as a whole on the launch stream
+    Mp = min(2048, cyc.g_pre.shape[0])
+    m_anch = len(s.anchors)
+    for _ in range(3):
+        cyc.features(0, Mp, 0, out=cyc.g_pre)
+    pe0, pe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    reps = 20
+    pe0.record()
+    for _ in range(reps):
+        cyc.features(0, Mp, 0, out=cyc.g_pre)
+    pe1.record()
+    torch.cuda.synchronize()
+    pre_us = pe0.elapsed_time(pe1) / reps * 1000.0
+    pre_flops = 2.0 * Mp * s.d * (m_anch * s.d)
+    pre_tflops = pre_flops / (pre_us * 1e-6) / 1e12
+    prefill_fc = {"M": Mp, "N": s.d, "K": m_anch * s.d, "call_us": round(pre_us, 2),
+                  "includes": "anchor gather + RMS scale + FC GEMM (one spd_fuse_features call)",
+                  "achieved_tflops": round(pre_tflops, 1), "bound": "mfma",
+                  "peak_tflops": BF16_PEAK_TFLOPS, "frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4)}
+
     result = {
         "metric": "draft+verify cycles/s + achieved HBM GB/s, d=2560 n=8 vocab 151936, 1 GPU",
         "value": round(cycles_per_s, 2),
@@ -230,16 +278,23 @@ def main():
         "algorithmic_MB_per_cycle": round(mean_bytes / 1e6, 2),
         "roofline": {"bound": "hbm", "kernel": "spd_lm_head (vocab GEMV + softmax/sample)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "avg_us": round(head_ms * 1000.0, 2),
                      "algorithmic_bytes_per_launch": int(head_bytes)},
         "calls": calls,
+        "prefill_fc": prefill_fc,
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(s, ci, timed[:64],
                                               words_np[args.warmup:], qstand.cpu().numpy(), x,
                                               budget_s=args.cpu_budget)
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
     print(json.dumps(result), flush=True)
 
 
