@@ -165,7 +165,11 @@ __global__ __launch_bounds__(256) void lmh_dot_kernel(const bf16* __restrict__ W
   for (int r = 0; r < DOT_ROWS; ++r) {
     const int row = min(row0 + r, V - 1);
 #pragma unroll
-    for (int j = 0; j < J; ++j) w[r][j] = *reinterpret_cast<const uint4*>(W + (size_t)row * K + 512 * j + 8 * lane);
+    for (int j = 0; j < J; ++j) {
+      // the head is read once per call: nontemporal loads stream it past the caches
+      w[r][j] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+                                             reinterpret_cast<const u32x4*>(W + (size_t)row * K + 512 * j + 8 * lane)));
+    }
   }
   float mine = -INFINITY;  // lane r < DOT_ROWS ends with row r's logit
 #pragma unroll
