@@ -139,13 +139,15 @@ __global__ __launch_bounds__(SMX_THREADS) void greedy_kernel(const BlockStat* st
 }
 
 // VALU GEMV for one hidden row: J = d / 512 loads of 1 KB per vocabulary row.
+// A row group is 4 waves x DOT_ROWS rows; block b takes groups b, b + grid, ...
+// and writes one statistics record per group.
 template <int J>
 __global__ __launch_bounds__(256) void lmh_dot_kernel(const bf16* __restrict__ W, const float* __restrict__ h,
                                                       int V, float inv_t, float* __restrict__ logits,
                                                       BlockStat* __restrict__ stat) {
   constexpr int K = 512 * J;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int row0 = (blockIdx.x * 4 + wave) * DOT_ROWS;
+  const int ngroups = (V + 4 * DOT_ROWS - 1) / (4 * DOT_ROWS);
   // lane's slice of h: k = 512 j + 8 lane + e, as bf16 hi and lo pairs
   uint32_t hh[J][4], hl[J][4];
 #pragma unroll
@@ -160,45 +162,49 @@ __global__ __launch_bounds__(256) void lmh_dot_kernel(const bf16* __restrict__ W
       hl[j][e] = (uint32_t)f2bf(x[2 * e] - bf2f(h0)) | ((uint32_t)f2bf(x[2 * e + 1] - bf2f(h1)) << 16);
     }
   }
-  uint4 w[DOT_ROWS][J];
+  __shared__ BlockStat ws[4];
+  for (int grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
+    const int row0 = (grp * 4 + wave) * DOT_ROWS;
+    uint4 w[DOT_ROWS][J];
 #pragma unroll
-  for (int r = 0; r < DOT_ROWS; ++r) {
-    const int row = min(row0 + r, V - 1);
+    for (int r = 0; r < DOT_ROWS; ++r) {
+      const int row = min(row0 + r, V - 1);
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      // the head is read once per call: nontemporal loads stream it past the caches
-      w[r][j] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
-                                             reinterpret_cast<const u32x4*>(W + (size_t)row * K + 512 * j + 8 * lane)));
-    }
-  }
-  float mine = -INFINITY;  // lane r < DOT_ROWS ends with row r's logit
-#pragma unroll
-  for (int r = 0; r < DOT_ROWS; ++r) {
-    float s = 0.f;
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const uint32_t* a = reinterpret_cast<const uint32_t*>(&w[r][j]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        s = dot2(a[e], hh[j][e], s);
-        s = dot2(a[e], hl[j][e], s);
+      for (int j = 0; j < J; ++j) {
+        // the head is read once per call: nontemporal loads stream it past the caches
+        w[r][j] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+                                               reinterpret_cast<const u32x4*>(W + (size_t)row * K + 512 * j + 8 * lane)));
       }
     }
-    s = wave_sum(s);
-    if (lane == r) mine = s;
-  }
-  const int row = row0 + lane;
-  const bool valid = lane < DOT_ROWS && row < V;
-  if (valid) logits[row] = mine;
-  // block statistics over the block's 4 * DOT_ROWS logits
-  __shared__ BlockStat ws[4];
-  const BlockStat bs = lane_stats(valid ? mine : -INFINITY, valid ? row : ARG_NONE, inv_t);
-  if (lane == 0) ws[wave] = bs;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    BlockStat a = ws[0];
-    for (int q = 1; q < 4; ++q) a = stat_merge(a, ws[q], inv_t);
-    stat[blockIdx.x] = a;
+    float mine = -INFINITY;  // lane r < DOT_ROWS ends with row r's logit
+#pragma unroll
+    for (int r = 0; r < DOT_ROWS; ++r) {
+      float s = 0.f;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const uint32_t* a = reinterpret_cast<const uint32_t*>(&w[r][j]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s = dot2(a[e], hh[j][e], s);
+          s = dot2(a[e], hl[j][e], s);
+        }
+      }
+      s = wave_sum(s);
+      if (lane == r) mine = s;
+    }
+    const int row = row0 + lane;
+    const bool valid = lane < DOT_ROWS && row < V;
+    if (valid) logits[row] = mine;
+    // statistics over the group's 4 * DOT_ROWS logits
+    const BlockStat bs = lane_stats(valid ? mine : -INFINITY, valid ? row : ARG_NONE, inv_t);
+    if (lane == 0) ws[wave] = bs;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      BlockStat a = ws[0];
+      for (int q = 1; q < 4; ++q) a = stat_merge(a, ws[q], inv_t);
+      stat[grp] = a;
+    }
+    __syncthreads();  // ws is rewritten by the next group
   }
 }
 
