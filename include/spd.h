@@ -55,6 +55,12 @@ enum {
 
 enum { SPD_F32 = 0, SPD_BF16 = 1 };
 enum { SPD_ANCHOR_ZERO_MASK = 0, SPD_ANCHOR_CLAMP_MIN = 1 };
+/* Feature schedules (section 3.3 and 4.5; PPSD in section 2): which depth's features
+ * a row at staircase depth k uses.  PRE_STEP (the method's own): depth k.  POST_STEP:
+ * depth min(n, k+1), every in-flight position one stage deeper (the newest token uses
+ * g^1 instead of g^0).  FIRST_STAGE: depth min(k, 1), nothing deeper than the first
+ * stage (PPSD's features). */
+enum { SPD_SCHEDULE_PRE_STEP = 0, SPD_SCHEDULE_POST_STEP = 1, SPD_SCHEDULE_FIRST_STAGE = 2 };
 enum { SPD_CALL_FUSE = 0, SPD_CALL_PDM = 1, SPD_CALL_LM_HEAD = 2, SPD_CALL_VERIFY = 3 };
 
 #define SPD_WS_COUNTER_BYTES 65536
@@ -76,6 +82,7 @@ typedef struct spd_config {
   int32_t norm_k0;     /* 0: g^0 = FC(H^0) without norm (default); 1: normalise  */
   float rms_eps;       /* 1e-6                                                   */
   float rope_theta;    /* 1e6                                                    */
+  int32_t feature_schedule; /* SPD_SCHEDULE_PRE_STEP (default), _POST_STEP, _FIRST_STAGE */
 } spd_config;
 
 /* One PDM decoder layer (DEVICE pointers, cfg.dtype).  Row-major [rows][cols]. */
@@ -101,15 +108,17 @@ typedef struct spd_seq_state {
 /* ---------------------------------------------------------------- host helpers */
 
 /* Anchor eligibility (section 3.2, Eq. (3); the review blog's core formulas for the
- * clamped variant).  l_max(k) = min(L, floor(k*L/n)).  For every depth k in 0..n and
- * anchor j, writes slot_tab[k*m + j] = index into `store_layers` of the target layer
- * slot j reads at depth k, or -1 for an empty slot:
- *   ZERO_MASK: layer b_j if b_j <= l_max(k), else empty;
- *   CLAMP_MIN: layer min(b_j, l_max(k));
- *   k = 0 (both modes): slot 0 reads layer 0 (the embedding), the rest are empty.
+ * clamped variant).  l_max(k) = min(L, floor(k*L/n)).  For every staircase depth k in
+ * 0..n and anchor j, writes slot_tab[k*m + j] = index into `store_layers` of the
+ * target layer slot j reads, or -1 for an empty slot.  With e = the feature depth of
+ * k under cfg->feature_schedule (k, min(n, k+1) or min(k, 1)):
+ *   ZERO_MASK: layer b_j if b_j <= l_max(e), else empty;
+ *   CLAMP_MIN: layer min(b_j, l_max(e));
+ *   e = 0 (both modes): slot 0 reads layer 0 (the embedding), the rest are empty.
  * store_layers (HOST, capacity L+1) receives the sorted distinct layers an anchor
- * store must hold; *n_store their count.  anchors (HOST [m]) must be strictly
- * increasing with anchors[0] = 0 and anchors[m-1] <= L.
+ * store must hold for the anchor mode (every schedule reads a subset of them);
+ * *n_store their count.  anchors (HOST [m]) must be strictly increasing with
+ * anchors[0] = 0 and anchors[m-1] <= L.
  */
 int spd_slot_table(const spd_config *cfg, const int32_t *anchors, int32_t *slot_tab,
                    int32_t *store_layers, int32_t *n_store);
@@ -135,9 +144,11 @@ size_t spd_workspace_size(int32_t call, const spd_config *cfg, int32_t rows, int
  * Rows are positions pos0 .. pos0+M-1; the last `a` of them have depths a-1 .. 0 and
  * the others depth n (so a = 0 means all rows are fully processed, e.g. prefill).
  * For a row at position i and depth k:
- *   k = 0 and !norm_k0: g = W_fc[:, 0:d] . H_i^{layer 0}     (no norm, no gamma)
+ *   k = 0, !norm_k0 and not POST_STEP: g = W_fc[:, 0:d] . H_i^{layer 0}  (no norm, no gamma)
  *   otherwise: x = Concat_j (slot_tab[k*m+j] >= 0 ? H_i^{store slot} : 0),
  *              rms = sqrt(sum(x^2) / (#filled * d) + eps),  g = W_fc (norm_w * x / rms)
+ * (under SPD_SCHEDULE_POST_STEP the depth-0 row uses depth-1 features, normalised).
+ * The large-M path (bf16, M >= 256) feeds the product the bf16-rounded norm_w * x.
  * hstore  DEVICE [T_cap][S][d]  anchor hidden states, slot s holds store_layers[s]
  * slot_tab HOST [(n+1)*m]       as written by spd_slot_table (any table of slots < S)
  * norm_w  DEVICE [m*d]; fc_w DEVICE [d][m*d]; g DEVICE float [M][d] (output).

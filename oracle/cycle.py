@@ -40,6 +40,7 @@ class OracleModel:
     w_dlm: np.ndarray
     w_tlm: np.ndarray
     pdm: O.PdmConfig
+    schedule: int = O.PRE_STEP
 
 
 @dataclass
@@ -76,7 +77,7 @@ def run_cycle(om: OracleModel, st: O.SeqState, cache: O.PdmCache, ring: dict,
     pos0, pos, dep = O.cycle_rows(st.t, st.a, n)
     g = O.fuse_features(om.store, om.store_layers, pos, dep, om.fc_norm, om.w_fc,
                         L=om.L, n=n, anchors=om.anchors, mode=om.mode, eps=om.eps,
-                        norm_k0=om.norm_k0)
+                        norm_k0=om.norm_k0, schedule=om.schedule)
     h_last, _ = O.pdm_step(g, pos0, cache, om.layers, om.final_norm, om.pdm)
     dl = O.lm_logits(om.w_dlm, h_last)
     if temperature == 0:
@@ -119,7 +120,7 @@ def prefill(om: OracleModel, t: int, a: int):
     if P > 0:
         g = O.fuse_features(om.store, om.store_layers, list(range(P)), [om.n] * P,
                             om.fc_norm, om.w_fc, L=om.L, n=om.n, anchors=om.anchors,
-                            mode=om.mode, eps=om.eps, norm_k0=om.norm_k0)
+                            mode=om.mode, eps=om.eps, norm_k0=om.norm_k0, schedule=om.schedule)
         O.pdm_step(g, 0, cache, om.layers, om.final_norm, om.pdm)
     return cache
 
@@ -142,4 +143,5 @@ def model_from_inputs(ci, with_heads=True) -> OracleModel:
         w_dlm=_f64(ci.w_dlm) if with_heads else None,
         w_tlm=_f64(ci.w_tlm) if with_heads else None,
         pdm=O.PdmConfig(d=s.d, Hq=s.Hq, Hkv=s.Hkv, hd=s.hd, dff=s.dff, eps=s.eps,
-                        rope_theta=s.rope_theta))
+                        rope_theta=s.rope_theta),
+        schedule=s.feature_schedule)

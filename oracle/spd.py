@@ -37,6 +37,11 @@ import numpy as np
 ZERO_MASK = 0
 CLAMP_MIN = 1
 
+# feature schedules ([SPD] 3.3 and 4.5; [SPD] 2 for PPSD)
+PRE_STEP = 0     # the pages' choice: features present before the current pipeline forward
+POST_STEP = 1    # features after the forward: every in-flight position one stage deeper
+FIRST_STAGE = 2  # PPSD's features: nothing deeper than the first stage (l <= L/n)
+
 _TWO52 = float(2 ** 52)
 
 
@@ -79,8 +84,31 @@ def slot_layers(k: int, L: int, n: int, anchors, mode: int = ZERO_MASK):
     raise ValueError("unknown anchor mode")
 
 
+def feature_depth(k: int, n: int, schedule: int = PRE_STEP) -> int:
+    """Depth whose features a row uses when the staircase puts it at depth k.
+
+    [SPD] 3.3: the pre-step schedule conditions on the intermediates present
+    before the current pipeline forward; relative to a post-step schedule every
+    in-flight position is one stage shallower (its example: the newest token
+    uses g^0 instead of g^1), so post-step = min(n, k + 1).  The verified prefix
+    (k = n) is the same in both.  [SPD] 2: PPSD uses only first-stage features,
+    read here as depth min(k, 1): the embedding alone for a token that has not
+    entered a stage yet, the first stage's output (l <= L/n) for all others.
+    """
+    if not 0 <= k <= n:
+        raise ValueError("depth k must lie in 0..n")
+    if schedule == PRE_STEP:
+        return k
+    if schedule == POST_STEP:
+        return min(n, k + 1)
+    if schedule == FIRST_STAGE:
+        return min(k, 1)
+    raise ValueError("unknown feature schedule")
+
+
 def store_layers_for(L: int, n: int, anchors, mode: int = ZERO_MASK):
-    """Sorted list of target layers an anchor store must hold for this mode."""
+    """Sorted list of target layers an anchor store must hold for this mode (every
+    feature schedule reads a subset of them)."""
     layers = set()
     for k in range(n + 1):
         layers.update(l for l in slot_layers(k, L, n, anchors, mode) if l >= 0)
@@ -117,7 +145,7 @@ def cycle_rows(t: int, a: int, n: int):
 # --------------------------------------------------------------------------
 
 def fuse_features(store, store_layers, pos, depth, gamma, w_fc, *, L, n, anchors,
-                  mode=ZERO_MASK, eps=1e-6, norm_k0=False):
+                  mode=ZERO_MASK, eps=1e-6, norm_k0=False, schedule=PRE_STEP):
     """Depth-conditioned feature g_i^k for each requested row.
 
     store:  [T][S][d]  hidden states H_i^l of every layer listed in store_layers.
@@ -125,7 +153,10 @@ def fuse_features(store, store_layers, pos, depth, gamma, w_fc, *, L, n, anchors
     w_fc:   [d][m*d]   FC projection (no bias).
     For k >= 1: x = Concat over slots (zeros in empty slots), RMS over the filled
     slots only, u = gamma * x / rms, g = W_fc u.  For k = 0: g = W_fc[:, :d] H^0
-    (no norm, no gamma) unless norm_k0 asks for the uniform rule.
+    (no norm, no gamma) unless norm_k0 asks for the uniform rule.  `depth` is
+    the staircase depth; the feature schedule maps it to the depth whose
+    features the row uses (feature_depth), and the k = 0 rule applies when that
+    depth is 0.
     """
     store = np.asarray(store, dtype=np.float64)
     gamma = np.asarray(gamma, dtype=np.float64)
@@ -134,7 +165,8 @@ def fuse_features(store, store_layers, pos, depth, gamma, w_fc, *, L, n, anchors
     m = len(anchors)
     index_of = {l: s for s, l in enumerate(store_layers)}
     out = np.zeros((len(pos), d))
-    for r, (i, k) in enumerate(zip(pos, depth)):
+    for r, (i, k_row) in enumerate(zip(pos, depth)):
+        k = feature_depth(k_row, n, schedule)
         layers = slot_layers(k, L, n, anchors, mode)
         if k == 0 and not norm_k0:
             out[r] = w_fc[:, :d] @ store[i, index_of[0]]

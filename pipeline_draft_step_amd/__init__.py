@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libspd.so")
 SPD_OK, SPD_E_INVALID, SPD_E_UNSUPPORTED, SPD_E_WORKSPACE, SPD_E_HIP = 0, -1, -2, -3, -4
 SPD_F32, SPD_BF16 = 0, 1
 SPD_ANCHOR_ZERO_MASK, SPD_ANCHOR_CLAMP_MIN = 0, 1
+SPD_SCHEDULE_PRE_STEP, SPD_SCHEDULE_POST_STEP, SPD_SCHEDULE_FIRST_STAGE = 0, 1, 2
 SPD_CALL_FUSE, SPD_CALL_PDM, SPD_CALL_LM_HEAD, SPD_CALL_VERIFY = 0, 1, 2, 3
 SPD_WS_COUNTER_BYTES = 65536
 SPD_MAX_ANCHORS = 8
@@ -32,7 +33,8 @@ class spd_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("L", "n", "m", "d", "Ls", "Hq", "Hkv", "hd", "dff", "V", "dtype",
                  "anchor_mode", "norm_k0")] + [("rms_eps", ctypes.c_float),
-                                               ("rope_theta", ctypes.c_float)]
+                                               ("rope_theta", ctypes.c_float),
+                                               ("feature_schedule", ctypes.c_int32)]
 
 
 class spd_layer_weights(ctypes.Structure):
@@ -123,9 +125,9 @@ def _i32_array(values):
 
 
 def make_config(*, L, n, m, d, Ls, Hq, Hkv, hd, dff, V, dtype, anchor_mode=0, norm_k0=0,
-                rms_eps=1e-6, rope_theta=1e6) -> spd_config:
+                rms_eps=1e-6, rope_theta=1e6, feature_schedule=0) -> spd_config:
     return spd_config(L, n, m, d, Ls, Hq, Hkv, hd, dff, V, dtype, anchor_mode, norm_k0,
-                      rms_eps, rope_theta)
+                      rms_eps, rope_theta, feature_schedule)
 
 
 # ----------------------------------------------------------------- host helpers

@@ -52,7 +52,7 @@ extern "C" int spd_slot_table(const spd_config* cfg, const int32_t* anchors, int
   for (int j = 1; j < m; ++j)
     if (anchors[j] <= anchors[j - 1]) return SPD_E_INVALID;
   if (anchors[m - 1] > L) return SPD_E_INVALID;
-  // layer read by (k, j), -1 when the slot is empty
+  // layer read by (depth k, slot j) for depths 0..n, -1 when the slot is empty
   int layer[SPD_MAX_STAGES + 1][SPD_MAX_ANCHORS];
   for (int k = 0; k <= n; ++k) {
     const int lmax = (int)(((int64_t)k * L) / n) < L ? (int)(((int64_t)k * L) / n) : L;
@@ -66,7 +66,7 @@ extern "C" int spd_slot_table(const spd_config* cfg, const int32_t* anchors, int
       }
     }
   }
-  // distinct layers, sorted
+  // distinct layers of the anchor mode, sorted
   char used[4097];
   if (L > 4096) return SPD_E_UNSUPPORTED;
   memset(used, 0, sizeof(used));
@@ -83,8 +83,13 @@ extern "C" int spd_slot_table(const spd_config* cfg, const int32_t* anchors, int
     }
   }
   *n_store = S;
-  for (int k = 0; k <= n; ++k)
-    for (int j = 0; j < m; ++j) slot_tab[k * m + j] = layer[k][j] >= 0 ? index[layer[k][j]] : -1;
+  // the row at staircase depth k reads the features of depth e(k)
+  for (int k = 0; k <= n; ++k) {
+    const int e = cfg->feature_schedule == SPD_SCHEDULE_POST_STEP    ? (k + 1 < n ? k + 1 : n)
+                  : cfg->feature_schedule == SPD_SCHEDULE_FIRST_STAGE ? (k < 1 ? k : 1)
+                                                                      : k;
+    for (int j = 0; j < m; ++j) slot_tab[k * m + j] = layer[e][j] >= 0 ? index[layer[e][j]] : -1;
+  }
   return SPD_OK;
 }
 

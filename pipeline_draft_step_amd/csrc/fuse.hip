@@ -222,7 +222,9 @@ static int fuse_impl(const spd_config* cfg, const void* hstore, int64_t T_cap, i
   ga.d = d;
   ga.m = m;
   ga.pos0 = pos0;
-  ga.norm_k0 = cfg->norm_k0;
+  // under the post-step schedule the staircase's depth-0 row uses depth-1 features,
+  // which are normalised like every depth >= 1 row
+  ga.norm_k0 = cfg->norm_k0 || cfg->feature_schedule == SPD_SCHEDULE_POST_STEP;
   ga.ncb = p.ncb;
   ga.eps = cfg->rms_eps;
   ga.depth = RowDepth{M, a, n};

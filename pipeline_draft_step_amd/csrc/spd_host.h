@@ -32,6 +32,8 @@ inline int check_config(const spd_config* c) {
   if (c->anchor_mode != SPD_ANCHOR_ZERO_MASK && c->anchor_mode != SPD_ANCHOR_CLAMP_MIN)
     return SPD_E_INVALID;
   if (!(c->rms_eps >= 0.f)) return SPD_E_INVALID;
+  if (c->feature_schedule < SPD_SCHEDULE_PRE_STEP || c->feature_schedule > SPD_SCHEDULE_FIRST_STAGE)
+    return SPD_E_INVALID;
   return SPD_OK;
 }
 

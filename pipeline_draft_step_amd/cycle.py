@@ -36,10 +36,11 @@ class DeviceWeights:
 
 class SpdModel:
     def __init__(self, *, L, n, anchors, d, Ls, Hq, Hkv, hd, dff, V, dtype, weights: DeviceWeights,
-                 anchor_mode=0, norm_k0=0, eps=1e-6, rope_theta=1e6):
+                 anchor_mode=0, norm_k0=0, eps=1e-6, rope_theta=1e6, feature_schedule=0):
         self.cfg = make_config(L=L, n=n, m=len(anchors), d=d, Ls=Ls, Hq=Hq, Hkv=Hkv, hd=hd,
                                dff=dff, V=V, dtype=dtype, anchor_mode=anchor_mode,
-                               norm_k0=norm_k0, rms_eps=eps, rope_theta=rope_theta)
+                               norm_k0=norm_k0, rms_eps=eps, rope_theta=rope_theta,
+                               feature_schedule=feature_schedule)
         self.anchors = list(anchors)
         self.slot_tab, self.store_layers = spd_slot_table(self.cfg, self.anchors)
         self.w = weights

@@ -49,6 +49,7 @@ class SpdShape:
     mix: bool = False       # 50% saturated / 50% partial-fill cycles
     anchor_mode: int = ZERO_MASK
     norm_k0: int = 0
+    feature_schedule: int = 0  # 0 pre-step, 1 post-step, 2 first-stage only
     eps: float = 1e-6
     rope_theta: float = 1e6
 

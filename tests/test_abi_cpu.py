@@ -44,6 +44,25 @@ def test_slot_table_matches_oracle(name, mode):
         assert got == want, (k, got, want)
 
 
+@pytest.mark.parametrize("name", ["tiny_fp32_n4", "qwen35_4b_n8_ls2_t1_mix", "qwen35_9b_n16_ls4_t1"])
+@pytest.mark.parametrize("mode", [O.ZERO_MASK, O.CLAMP_MIN])
+@pytest.mark.parametrize("schedule", [O.POST_STEP, O.FIRST_STAGE])
+def test_slot_table_schedules_match_oracle(name, mode, schedule):
+    s = synth.SHAPES[name].with_(anchor_mode=mode)
+    tab, layers = spd.spd_slot_table(_cfg(s, feature_schedule=schedule), s.anchors)
+    assert layers == O.store_layers_for(s.L, s.n, s.anchors, mode)   # same store for every schedule
+    for k in range(s.n + 1):
+        want = O.slot_layers(O.feature_depth(k, s.n, schedule), s.L, s.n, s.anchors, mode)
+        got = [layers[x] if x >= 0 else -1 for x in tab[k * s.m:(k + 1) * s.m]]
+        assert got == want, (k, got, want)
+
+
+def test_config_rejects_unknown_schedule():
+    s = synth.TINY
+    with pytest.raises(spd.SpdError):
+        spd.spd_slot_table(_cfg(s, feature_schedule=3), s.anchors)
+
+
 def test_slot_table_rejects_bad_anchors():
     s = synth.TINY
     with pytest.raises(spd.SpdError):

@@ -36,7 +36,8 @@ def device_model(ci):
                       layers=ci.layers, final_norm=ci.final_norm, w_dlm=ci.w_dlm, w_tlm=ci.w_tlm)
     return SpdModel(L=s.L, n=s.n, anchors=s.anchors, d=s.d, Ls=s.Ls, Hq=s.Hq, Hkv=s.Hkv, hd=s.hd,
                     dff=s.dff, V=s.V, dtype=s.dtype, weights=w, anchor_mode=s.anchor_mode,
-                    norm_k0=s.norm_k0, eps=s.eps, rope_theta=s.rope_theta)
+                    norm_k0=s.norm_k0, eps=s.eps, rope_theta=s.rope_theta,
+                    feature_schedule=s.feature_schedule)
 
 
 def row_depths(M, a, n):
@@ -56,6 +57,13 @@ FUSE_CASES = [
     ("small_zero", SMALL_BF16, [(96, 8), (96, 3), (96, 1), (80, 0)]),
     ("small_clamp", SMALL_BF16.with_(anchor_mode=synth.CLAMP_MIN), [(96, 8), (96, 5)]),
     ("small_normk0", SMALL_BF16.with_(norm_k0=1), [(96, 8), (96, 2)]),
+    # feature-schedule variants (slot-table switches, no kernel change)
+    ("small_post_step", SMALL_BF16.with_(feature_schedule=1), [(96, 8), (96, 3), (96, 1)]),
+    ("small_first_stage", SMALL_BF16.with_(feature_schedule=2), [(96, 8), (96, 3), (80, 0)]),
+    ("small_first_stage_clamp", SMALL_BF16.with_(feature_schedule=2, anchor_mode=synth.CLAMP_MIN),
+     [(96, 8), (96, 4)]),
+    ("tiny_post_step", synth.TINY.with_(feature_schedule=1), [(32, 4), (32, 2)]),
+    ("headline_post_step", synth.HEADLINE.with_(feature_schedule=1), [(2048, 8), (2048, 3)]),
     ("headline", synth.HEADLINE, [(2048, 8), (2048, 3), (2048, 1)]),
     ("9b", synth.SHAPES["qwen35_9b_n16_ls4_t1"], [(4096, 16)]),
 ]
@@ -77,7 +85,7 @@ def test_fuse_features(name, shape, layouts):
         ref = O.fuse_features(om.store, om.store_layers, list(range(pos0, pos0 + M)),
                               row_depths(M, a, shape.n), om.fc_norm, om.w_fc, L=shape.L, n=shape.n,
                               anchors=shape.anchors, mode=shape.anchor_mode, eps=shape.eps,
-                              norm_k0=bool(shape.norm_k0))
+                              norm_k0=bool(shape.norm_k0), schedule=shape.feature_schedule)
         err = rel_err(f64(out), ref)
         assert err < tol_for(shape.dtype), (t, a, err)
 
@@ -364,12 +372,14 @@ def test_rollback_state_machine():
 
 # ------------------------------------------------------------------ whole cycles
 
-def test_cycle_trajectory_tiny():
+@pytest.mark.parametrize("schedule", [0, 1, 2], ids=["pre_step", "post_step", "first_stage"])
+def test_cycle_trajectory_tiny(schedule):
     """A device-state trajectory (greedy) against the oracle: each cycle's
     features, last hidden row and logits within fp32 tolerance; the decisions the
     device takes equal the oracle decision functions on the device's rows; the
-    state after every cycle matches the oracle state machine."""
-    s = synth.TINY
+    state after every cycle matches the oracle state machine.  Run under each
+    feature schedule (the prefill and every cycle's features follow it)."""
+    s = synth.TINY.with_(feature_schedule=schedule)
     ci = synth.cycle_inputs(s, device=DEV, T_cap=128)
     model = device_model(ci)
     cyc = SpdCycle(model, 0.0)

@@ -63,6 +63,85 @@ def test_eligibility_invariants():
     assert O.l_max(1, 32, 3) == 10                  # floor of 32/3
 
 
+@pytest.mark.parametrize("n", [4, 8])
+def test_post_step_eligible_sets(golden_dir, n):
+    g = _golden(golden_dir, "feature_schedules_L32.json")
+    want = g["post_step_zero_mask"][str(n)]
+    for k in range(n + 1):
+        e = O.feature_depth(k, n, O.POST_STEP)
+        got = [l for l in O.slot_layers(e, 32, n, g["anchors"], O.ZERO_MASK) if l >= 0]
+        assert got == want[k], (n, k)
+
+
+@pytest.mark.parametrize("n", [4, 8, 16])
+def test_first_stage_eligible_sets(golden_dir, n):
+    g = _golden(golden_dir, "feature_schedules_L32.json")
+    want = g["first_stage_zero_mask"][str(n)]
+    for k in range(n + 1):
+        e = O.feature_depth(k, n, O.FIRST_STAGE)
+        got = [l for l in O.slot_layers(e, 32, n, g["anchors"], O.ZERO_MASK) if l >= 0]
+        assert got == want[k], (n, k)
+        assert max(got) <= 32 // n            # nothing deeper than the first stage
+
+
+def test_first_stage_clamp_min_slots(golden_dir):
+    g = _golden(golden_dir, "feature_schedules_L32.json")
+    for k, want in enumerate(g["first_stage_clamp_min_slots_n8"]):
+        assert O.slot_layers(O.feature_depth(k, 8, O.FIRST_STAGE), 32, 8, g["anchors"],
+                             O.CLAMP_MIN) == want
+
+
+def test_schedule_invariants():
+    for n in (2, 4, 8, 16):
+        for k in range(n + 1):
+            assert O.feature_depth(k, n, O.PRE_STEP) == k
+            post = O.feature_depth(k, n, O.POST_STEP)
+            assert post == (k + 1 if k < n else n)     # one stage deeper, prefix unchanged
+            assert O.feature_depth(k, n, O.FIRST_STAGE) <= 1
+    with pytest.raises(ValueError):
+        O.feature_depth(0, 8, 7)
+
+
+def test_post_step_newest_row_is_normalised_depth1_feature():
+    """[SPD] 3.3's example: post-step gives the newest token g^1, not g^0.  The
+    staircase row at depth 0 must then equal the pre-step feature of a depth-1
+    row (RMSNorm over the eligible concat, then FC) and differ from FC(H^0)."""
+    rng = np.random.default_rng(11)
+    d, L, n, B = 16, 8, 4, (0, 4, 7)
+    sl, store, gamma, w = _fuse_setup(rng, d, L, n, B)
+    g_post = O.fuse_features(store, sl, [6], [0], gamma, w, L=L, n=n, anchors=B,
+                             schedule=O.POST_STEP)
+    # depth 1 at L = 8, n = 4 reaches layer 2: only the embedding anchor is eligible
+    x = torch.tensor(store[6, sl.index(0)])
+    ref = F.linear(F.rms_norm(x, (d,), torch.tensor(gamma[:d]), eps=1e-6), torch.tensor(w[:, :d]))
+    assert np.allclose(g_post[0], ref.numpy(), rtol=1e-12, atol=1e-12)
+    g_pre = O.fuse_features(store, sl, [6], [0], gamma, w, L=L, n=n, anchors=B)
+    assert not np.allclose(g_pre[0], g_post[0])
+    # the depth-1 row under post-step reads depth 2 (layers 0 and 4)
+    g1 = O.fuse_features(store, sl, [6], [1], gamma, w, L=L, n=n, anchors=B, schedule=O.POST_STEP)
+    x2 = torch.tensor(np.concatenate([store[6, sl.index(0)], store[6, sl.index(4)]]))
+    ref2 = F.linear(F.rms_norm(x2, (2 * d,), torch.tensor(gamma[:2 * d]), eps=1e-6),
+                    torch.tensor(w[:, :2 * d]))
+    assert np.allclose(g1[0], ref2.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_first_stage_prefix_row_uses_first_stage_only():
+    """PPSD's features: a fully processed row (k = n) reads nothing deeper than
+    layer L/n, and deeper layers of the store do not change it."""
+    rng = np.random.default_rng(12)
+    d, L, n, B = 16, 8, 2, (0, 4, 7)
+    sl, store, gamma, w = _fuse_setup(rng, d, L, n, B)
+    g = O.fuse_features(store, sl, [3], [n], gamma, w, L=L, n=n, anchors=B, schedule=O.FIRST_STAGE)
+    x = torch.tensor(np.concatenate([store[3, sl.index(0)], store[3, sl.index(4)]]))   # L/n = 4
+    ref = F.linear(F.rms_norm(x, (2 * d,), torch.tensor(gamma[:2 * d]), eps=1e-6),
+                   torch.tensor(w[:, :2 * d]))
+    assert np.allclose(g[0], ref.numpy(), rtol=1e-12, atol=1e-12)
+    store2 = store.copy()
+    store2[3, sl.index(7)] += 1.0
+    g2 = O.fuse_features(store2, sl, [3], [n], gamma, w, L=L, n=n, anchors=B, schedule=O.FIRST_STAGE)
+    assert np.array_equal(g, g2)
+
+
 def test_layouts(golden_dir):
     g = _golden(golden_dir, "layouts.json")
     for c in g["cases"]:
