@@ -140,30 +140,12 @@ struct EpiRows {
 };
 
 // Large-M path: bf16 only, for prefill-sized M, when the K range splits into
-// whole 64-wide stages.  KS splits K so that the tiles times KS fill the GPU.
+// whole 64-wide stages.
 constexpr int FUSE_BIG_MIN_M = 256;
-constexpr int FUSE_BIG_TARGET_BLOCKS = 256;
-
-struct BigPlan {
-  bool use;
-  int mtiles, ntiles, KS, kstages;
-};
 
 static BigPlan plan_big(const spd_config* cfg, int M) {
-  BigPlan b{};
-  const int K = cfg->m * cfg->d, N = cfg->d;
-  if (cfg->dtype != SPD_BF16 || M < FUSE_BIG_MIN_M || K % BG_BK) return b;
-  b.mtiles = (M + BG_BM - 1) / BG_BM;
-  b.ntiles = (N + BG_BN - 1) / BG_BN;
-  const int stages = K / BG_BK;
-  if (stages < BG_SLOTS) return b;
-  b.KS = 1;
-  while (b.KS < BG_MAX_KS && b.mtiles * b.ntiles * b.KS * 2 <= FUSE_BIG_TARGET_BLOCKS &&
-         stages % (b.KS * 2) == 0 && stages / (b.KS * 2) >= BG_SLOTS)
-    b.KS *= 2;
-  b.kstages = stages / b.KS;
-  b.use = true;
-  return b;
+  if (cfg->dtype != SPD_BF16 || M < FUSE_BIG_MIN_M) return BigPlan{};
+  return plan_big_gemm(M, cfg->d, cfg->m * cfg->d);
 }
 
 struct FusePlan {
@@ -189,7 +171,7 @@ static FusePlan plan_fuse(const spd_config* cfg, int M) {
   p.off_xh = take((size_t)M * K * es);
   if (p.big.use) {
     p.off_xl = take(0);
-    p.off_gpart = take(p.big.KS > 1 ? (size_t)p.big.mtiles * p.big.ntiles * p.big.KS * BG_PART_FLOATS * 4 : 0);
+    p.off_gpart = take(p.big.part_bytes);
   } else {
     p.off_xl = take(bf ? (size_t)M * K * es : 0);
     p.off_gpart = take(p.gp.S > 1 ? (size_t)p.gp.S * M * cfg->d * 4 : 0);
@@ -235,25 +217,9 @@ static int fuse_impl(const spd_config* cfg, const void* hstore, int64_t T_cap, i
       if (rc) return rc;
       // the gather's row counters are back at zero when it ends, so the GEMM
       // reuses the start of the counter region for its tile counters
-      BigGemm bgm{};
-      bgm.A = reinterpret_cast<const bf16*>(ga.xo.hi);
-      bgm.B = static_cast<const bf16*>(fc_w);
-      bgm.C = g;
-      bgm.rs = ga.inv;
-      bgm.part = reinterpret_cast<float*>(w + p.off_gpart);
-      bgm.counters = reinterpret_cast<unsigned*>(w);
-      bgm.M = M;
-      bgm.N = d;
-      bgm.K = m * d;
-      bgm.lda = m * d;
-      bgm.ldb = m * d;
-      bgm.ldc = d;
-      bgm.mtiles = p.big.mtiles;
-      bgm.ntiles = p.big.ntiles;
-      bgm.KS = p.big.KS;
-      bgm.kstages = p.big.kstages;
-      hipLaunchKernelGGL(gemm_big_kernel, dim3(p.big.mtiles * p.big.ntiles * p.big.KS), dim3(BG_THREADS), 0,
-                         st, bgm);
+      launch_big_gemm(p.big, reinterpret_cast<const bf16*>(ga.xo.hi), m * d, static_cast<const bf16*>(fc_w), g,
+                      d, ga.inv, M, d, m * d, reinterpret_cast<float*>(w + p.off_gpart),
+                      reinterpret_cast<unsigned*>(w), st);
       return check_launch();
     }
   }

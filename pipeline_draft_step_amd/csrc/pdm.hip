@@ -19,6 +19,7 @@
 
 #include "spd_common.h"
 #include "spd_gemm.h"
+#include "spd_gemm_big.h"
 #include "spd_host.h"
 
 namespace spd {
@@ -382,11 +383,330 @@ L = row16_sum(L);
   SPD_MARK(6);
 }
 
+// ---------------------------------------------------------------------------
+// Prefill-sized steps (bf16, M >= 256, hd = 128): the four products of a layer
+// run on the large-M MFMA GEMM with bf16-rounded activations and write fp32
+// rows; the row kernels below apply what the decode path's GEMM epilogues do.
+// ---------------------------------------------------------------------------
+constexpr int PDM_BIG_MIN_M = 256;
+
+// block sum of a value every thread holds (256 threads)
+__device__ __forceinline__ float block_sum256(float v) {
+  __shared__ float s_part[4];
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
+}
+
+// four values as bf16 hi parts at p and the lo parts (v - hi) at p + K
+__device__ __forceinline__ void put4_hilo(bf16* p, int K, float4 v) {
+  const uint32_t h0 = pack2_bf16(v.x, v.y), h1 = pack2_bf16(v.z, v.w);
+  const uint32_t l0 = pack2_bf16(v.x - __uint_as_float(h0 << 16), v.y - __uint_as_float(h0 & 0xffff0000u));
+  const uint32_t l1 = pack2_bf16(v.z - __uint_as_float(h1 << 16), v.w - __uint_as_float(h1 & 0xffff0000u));
+  *reinterpret_cast<uint2*>(p) = make_uint2(h0, h1);
+  *reinterpret_cast<uint2*>(p + K) = make_uint2(l0, l1);
+}
+
+// h = g, the row's 1/rms, the first QKV input g * attn_norm as a [hi | lo] row
+// of 2d bf16 values, and the rotate-half RoPE table of the row's position
+// (fp64 angles)
+template <typename WT>
+__global__ __launch_bounds__(256) void big_rows_init_kernel(const float* g, float* h, float* rs, WT* xa,
+                                                            const WT* gamma, float2* rope, int d, int pos0,
+                                                            int hd, float theta, float eps) {
+  const int r = blockIdx.x;
+  if (threadIdx.x < hd / 2) {
+    double sn, cs;
+    sincos((double)(pos0 + r) * pow((double)theta, -2.0 * threadIdx.x / hd), &sn, &cs);
+    rope[(size_t)r * (hd / 2) + threadIdx.x] = make_float2((float)cs, (float)sn);
+  }
+  float sq = 0.f;
+  for (int c = 4 * threadIdx.x; c < d; c += 4 * 256) {
+    const size_t i = (size_t)r * d + c;
+    const float4 v = *reinterpret_cast<const float4*>(g + i);
+    *reinterpret_cast<float4*>(h + i) = v;
+    sq += (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
+    put4_hilo(xa + (size_t)r * 2 * d + c, d,
+              make_float4(v.x * to_f<WT>(gamma[c]), v.y * to_f<WT>(gamma[c + 1]), v.z * to_f<WT>(gamma[c + 2]),
+                          v.w * to_f<WT>(gamma[c + 3])));
+  }
+  const float t = block_sum256(sq);
+  if (threadIdx.x == 0) rs[r] = 1.0f / sqrtf(t / (float)d + eps);
+}
+
+// q and k heads of one row: per-head RMSNorm with q_norm / k_norm, rotate-half
+// RoPE (element i pairs with i + 64), q to the attention buffer, k to the cache.
+template <typename WT>
+__global__ __launch_bounds__(64) void qk_post_kernel(const float* C, int ldc, float* qbuf, WT* kc, const WT* qn,
+                                                     const WT* kn, const float2* rope, int Hq, int pos0,
+                                                     int64_t T_cap, float eps) {
+  const int hh = blockIdx.x, r = blockIdx.y, lane = threadIdx.x;
+  const float* y = C + (size_t)r * ldc + hh * 128;
+  float v0 = y[lane], v1 = y[lane + 64];
+  const WT* nw = hh < Hq ? qn : kn;
+  const float inv = 1.0f / sqrtf(wave_sum(v0 * v0 + v1 * v1) / 128.f + eps);
+  v0 *= inv * to_f<WT>(nw[lane]);
+  v1 *= inv * to_f<WT>(nw[lane + 64]);
+  const float2 cs = rope[(size_t)r * 64 + lane];
+  const float x1 = v0, x2 = v1;
+  v0 = x1 * cs.x - x2 * cs.y;
+  v1 = x2 * cs.x + x1 * cs.y;
+  if (hh < Hq) {
+    float* qp = qbuf + ((size_t)r * Hq + hh) * 128;
+    qp[lane] = v0;
+    qp[lane + 64] = v1;
+  } else {
+    WT* kp = kc + ((size_t)(hh - Hq) * T_cap + pos0 + r) * 128;
+    kp[lane] = from_f<WT>(v0);
+    kp[lane + 64] = from_f<WT>(v1);
+  }
+}
+
+// v heads into the position-minor cache [Hkv][hd][T_cap]: a block writes 64
+// consecutive positions of every dimension of one head.
+template <typename WT>
+__global__ __launch_bounds__(256) void v_post_kernel(const float* C, int ldc, WT* vc, int col0, int pos0,
+                                                     int64_t T_cap, int M) {
+  const int vh = blockIdx.x, r = blockIdx.y * 64 + (threadIdx.x & 63);
+  if (r >= M) return;
+  const float* y = C + (size_t)r * ldc + col0 + vh * 128;
+  WT* vp = vc + (size_t)vh * 128 * T_cap + pos0 + r;
+  for (int dim = threadIdx.x >> 6; dim < 128; dim += 4) vp[(size_t)dim * T_cap] = from_f<WT>(y[dim]);
+}
+
+// h += y, the row's 1/rms, the next GEMM's input h * gnext as a [hi | lo] row
+// when gnext is given; with final_norm, the final-normed last row into h_last
+template <typename WT>
+__global__ __launch_bounds__(256) void resid_post_kernel(const float* C, int ldc, float* h, float* rs, WT* xa,
+                                                         const WT* gnext, int d, float eps, const WT* final_norm,
+                                                         float* h_last, int M) {
+  const int r = blockIdx.x;
+  float sq = 0.f;
+  for (int c = 4 * threadIdx.x; c < d; c += 4 * 256) {
+    const size_t i = (size_t)r * d + c;
+    float4 v = *reinterpret_cast<const float4*>(h + i);
+    const float4 y = *reinterpret_cast<const float4*>(C + (size_t)r * ldc + c);
+    v.x += y.x;
+    v.y += y.y;
+    v.z += y.z;
+    v.w += y.w;
+    *reinterpret_cast<float4*>(h + i) = v;
+    sq += (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
+    if (gnext)
+      put4_hilo(xa + (size_t)r * 2 * d + c, d,
+                make_float4(v.x * to_f<WT>(gnext[c]), v.y * to_f<WT>(gnext[c + 1]), v.z * to_f<WT>(gnext[c + 2]),
+                            v.w * to_f<WT>(gnext[c + 3])));
+  }
+  const float t = block_sum256(sq);
+  const float inv = 1.0f / sqrtf(t / (float)d + eps);
+  if (threadIdx.x == 0) rs[r] = inv;
+  if (final_norm && r == M - 1) {
+    for (int c = threadIdx.x; c < d; c += 256) h_last[c] = h[(size_t)r * d + c] * inv * to_f<WT>(final_norm[c]);
+  }
+}
+
+// act[r][j] = silu(gate_j) * up_j (gate columns first, then up) as a [hi | lo]
+// row of 2 dff bf16 values
+template <typename WT>
+__global__ __launch_bounds__(256) void swiglu_post_kernel(const float* C, int ldc, WT* xb, int dff) {
+  const int r = blockIdx.y, j = 4 * (blockIdx.x * 256 + threadIdx.x);
+  if (j >= dff) return;
+  const float4 gt = *reinterpret_cast<const float4*>(C + (size_t)r * ldc + j);
+  const float4 up = *reinterpret_cast<const float4*>(C + (size_t)r * ldc + dff + j);
+  auto act = [](float gv, float uv) { return gv / (1.0f + expf(-gv)) * uv; };
+  put4_hilo(xb + (size_t)r * 2 * dff + j, dff,
+            make_float4(act(gt.x, up.x), act(gt.y, up.y), act(gt.z, up.z), act(gt.w, up.w)));
+}
+
+// Causal attention for prefill-sized steps (bf16, hd = 128), flash style: a block
+// owns 64 of a kv head's GQA query rows (query index qi = row * G + head in the
+// group, as in the decode kernel) and walks the keys in blocks of 64 up to its
+// causal limit.  Per key block the K tile (key-major) and the V tile (from the
+// position-minor cache, dimension-major) are staged in LDS; each wave computes
+// S = Q K^T for its 16 rows on MFMA (Q and P as bf16 hi + lo pairs), keeps a
+// running maximum and sum per row, and accumulates O += P V.  The output is
+// written once, as the O projection's [hi | lo] input rows: no partials.
+constexpr int FA_KB = 64;               // keys per step
+constexpr int FA_ROWS = 64;             // query rows per block (16 per wave)
+constexpr int FA_KSTR = 128 + 8;        // padded LDS row strides (bf16 elements)
+constexpr int FA_VSTR = FA_KB + 8;
+
+struct FlashArgs {
+  const float* q;  // [M][Hq][128]
+  const bf16* kc;  // [Hkv][T_cap][128] of this layer
+  const bf16* vc;  // [Hkv][128][T_cap]
+  bf16* xh;        // output hi parts, row stride xld
+  bf16* xl;        // output lo parts
+  int xld;
+  int M, Hq, Hkv, pos0, nqt;
+  int64_t T_cap;
+  float scale;
+};
+
+__global__ __launch_bounds__(256) void attn_flash_kernel(FlashArgs a) {
+  typedef Mfma<bf16> F;
+  typedef F::frag frag;
+  __shared__ __align__(16) bf16 Ks[FA_KB * FA_KSTR];
+  __shared__ __align__(16) bf16 Vs[128 * FA_VSTR];
+  __shared__ __align__(16) bf16 Ps[4][2][16 * FA_VSTR];
+  const int h = blockIdx.y;
+  const int qt = a.nqt - 1 - blockIdx.x;  // the longest (latest) tiles start first
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int G = a.Hq / a.Hkv, QR = a.M * G;
+  const int nkeys = a.pos0 + a.M;
+  const int r_last = (min(QR, FA_ROWS * qt + FA_ROWS) - 1) / G;  // last position of the tile
+  const int nkb = (a.pos0 + r_last) / FA_KB + 1;
+  const bf16* K = a.kc + (size_t)h * a.T_cap * 128;
+  const bf16* Vt = a.vc + (size_t)h * 128 * a.T_cap;
+
+  // Q fragments of this lane's row (A operand), pre-scaled, as hi + lo pairs
+  const int qi = FA_ROWS * qt + 16 * wave + lr;
+  const bool qv = qi < QR;
+  const float* qp = a.q + ((size_t)(qv ? qi / G : 0) * a.Hq + h * G + (qv ? qi % G : 0)) * 128;
+  frag qf[4], ql[4];
+  {
+    const float qs = qv ? a.scale : 0.f;
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) {
+      const float4 x0 = *reinterpret_cast<const float4*>(qp + ds * 32 + lg * 8);
+      const float4 x1 = *reinterpret_cast<const float4*>(qp + ds * 32 + lg * 8 + 4);
+      float tmp[8] = {x0.x * qs, x0.y * qs, x0.z * qs, x0.w * qs, x1.x * qs, x1.y * qs, x1.z * qs, x1.w * qs};
+      float rem[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) rem[e] = tmp[e] - to_f<bf16>(from_f<bf16>(tmp[e]));
+      qf[ds] = F::pack(tmp);
+      ql[ds] = F::pack(rem);
+    }
+  }
+  // causal limit of the 4 rows this lane's accumulators hold (rows 4 lg + i of the wave)
+  int lim[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = FA_ROWS * qt + 16 * wave + 4 * lg + i;
+    lim[i] = a.pos0 + (r < QR ? r / G : 0);
+  }
+  float mrow[4], lrow[4];
+  f32x4 o[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    mrow[i] = -INFINITY;
+    lrow[i] = 0.f;
+  }
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int key0 = kb * FA_KB;
+    __syncthreads();  // the previous tiles are consumed
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      const int idx = pass * 256 + threadIdx.x;
+      // K: row = key, 16 chunks of 8 dims; keys past the cache end read its last row
+      const int kr = idx >> 4, kc = idx & 15;
+      const int key = min(key0 + kr, (int)a.T_cap - 1);
+      *reinterpret_cast<uint4*>(Ks + kr * FA_KSTR + kc * 8) =
+          *reinterpret_cast<const uint4*>(K + (size_t)key * 128 + kc * 8);
+      // V: row = dimension, 8 chunks of 8 keys; keys past the last written one are zeroed
+      const int vr = idx >> 3, vcn = idx & 7;
+      const int kk = key0 + vcn * 8;
+      uint4 v = *reinterpret_cast<const uint4*>(Vt + (size_t)vr * a.T_cap + min(kk, (int)a.T_cap - 8));
+      v = F::mask_from(v, nkeys - kk);
+      *reinterpret_cast<uint4*>(Vs + vr * FA_VSTR + vcn * 8) = v;
+    }
+    __syncthreads();
+    // S = Q K^T: lane holds S[4 lg + i][16 ks + lr]
+    f32x4 sc[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      sc[ks] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds) {
+        const frag kf = *reinterpret_cast<const frag*>(Ks + (16 * ks + lr) * FA_KSTR + ds * 32 + lg * 8);
+        sc[ks] = F::mma(qf[ds], kf, sc[ks]);
+        sc[ks] = F::mma(ql[ds], kf, sc[ks]);
+      }
+    }
+    // online softmax per row
+    float scl[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int key = key0 + 16 * ks + lr;
+        if (key > lim[i]) sc[ks][i] = -INFINITY;
+        mx = fmaxf(mx, sc[ks][i]);
+      }
+      mx = row16_max(mx);
+      const float mnew = fmaxf(mrow[i], mx);  // finite: key 0 is inside every row's limit
+      scl[i] = expf(mrow[i] - mnew);
+      float sm = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const float pv = sc[ks][i] == -INFINITY ? 0.f : expf(sc[ks][i] - mnew);
+        sc[ks][i] = pv;
+        sm += pv;
+      }
+      sm = row16_sum(sm);
+      lrow[i] = lrow[i] * scl[i] + sm;
+      mrow[i] = mnew;
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[dt][i] *= scl[i];
+    // P (16 rows x 64 keys) as hi and lo parts through the wave's LDS buffers
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16 hi = from_f<bf16>(sc[ks][i]);
+        Ps[wave][0][(4 * lg + i) * FA_VSTR + 16 * ks + lr] = hi;
+        Ps[wave][1][(4 * lg + i) * FA_VSTR + 16 * ks + lr] = from_f<bf16>(sc[ks][i] - to_f<bf16>(hi));
+      }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's P writes are done
+    __builtin_amdgcn_wave_barrier();
+    // O += P V
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const frag ph = *reinterpret_cast<const frag*>(&Ps[wave][0][lr * FA_VSTR + kt * 32 + lg * 8]);
+      const frag pl = *reinterpret_cast<const frag*>(&Ps[wave][1][lr * FA_VSTR + kt * 32 + lg * 8]);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const frag vf = *reinterpret_cast<const frag*>(Vs + (16 * dt + lr) * FA_VSTR + kt * 32 + lg * 8);
+        o[dt] = F::mma(ph, vf, o[dt]);
+        o[dt] = F::mma(pl, vf, o[dt]);
+      }
+    }
+  }
+  // O / l as [hi | lo] parts; lane holds O[4 lg + i][16 dt + lr]
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = FA_ROWS * qt + 16 * wave + 4 * lg + i;
+    if (r >= QR) continue;
+    const float inv = 1.0f / lrow[i];
+    const size_t base = (size_t)(r / G) * a.xld + (size_t)(h * G + r % G) * 128 + lr;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const float v = o[dt][i] * inv;
+      const bf16 hi = from_f<bf16>(v);
+      a.xh[base + 16 * dt] = hi;
+      a.xl[base + 16 * dt] = from_f<bf16>(v - to_f<bf16>(hi));
+    }
+  }
+}
+
 struct PdmPlan {
   GemmPlan qkv, o, gu, down;
   int nch, QR;
   size_t off_h, off_ss, off_q, off_rope, off_po, off_pml, off_x0h, off_x0l, off_x1h, off_x1l, off_part, total;
   int ld1;  // row stride of the second XSplit buffer
+  // large-M path
+  bool big;
+  BigPlan bqkv, bo, bgu, bdown;
+  size_t off_C, off_rs, off_bpart, off_xa, off_xb;
 };
 
 static PdmPlan plan_pdm(const spd_config* c, int M, int64_t T_cap) {
@@ -421,6 +741,25 @@ static PdmPlan plan_pdm(const spd_config* c, int M, int64_t T_cap) {
   for (int i = 0; i < 4; ++i)
     if (gps[i]->S > 1) part = std::max(part, (size_t)gps[i]->S * M * Ns[i] * 4);
   p.off_part = take(part);
+  p.big = bf && M >= PDM_BIG_MIN_M && c->hd == 128;
+  if (p.big) {
+    // activations enter as [hi | lo] rows: every product runs over 2K columns
+    const int nq = (c->Hq + 2 * c->Hkv) * c->hd;
+    p.bqkv = plan_big_gemm(M, nq, 2 * c->d);
+    p.bo = plan_big_gemm(M, c->d, 2 * c->Hq * c->hd);
+    p.bgu = plan_big_gemm(M, 2 * c->dff, 2 * c->d);
+    p.bdown = plan_big_gemm(M, c->d, 2 * c->dff);
+    p.big = p.bqkv.use && p.bo.use && p.bgu.use && p.bdown.use;
+  }
+  if (p.big) {
+    const int nq = (c->Hq + 2 * c->Hkv) * c->hd;
+    p.off_C = take((size_t)M * std::max(std::max(nq, c->d), 2 * c->dff) * 4);
+    p.off_rs = take((size_t)M * 4);
+    p.off_xa = take((size_t)M * 2 * c->d * 2);
+    p.off_xb = take((size_t)M * 2 * p.ld1 * 2);
+    p.off_bpart = take(std::max(std::max(p.bqkv.part_bytes, p.bo.part_bytes),
+                                std::max(p.bgu.part_bytes, p.bdown.part_bytes)));
+  }
   p.total = off;
   return p;
 }
@@ -461,6 +800,82 @@ static int launch_attention(const AttnArgs& aa, hipStream_t st) {
   }
 }
 
+// Large-M step.  Buffers: x0 hi = bf16 input of QKV and gate/up (d wide), x1 hi/lo =
+// attention output (the GEMM reads the hi part) and SwiGLU activations, C = one
+// GEMM's fp32 output, rs = the row scales 1/rms(h).
+static int pdm_big(const spd_config* c, const spd_layer_weights* layers, const void* final_norm, void* k_cache,
+                   void* v_cache, int64_t T_cap, const float* g, int pos0, int M, float* h_last, char* w,
+                   const PdmPlan& p, AttnArgs aa, hipStream_t st) {
+  typedef bf16 WT;
+  const int d = c->d, hd = c->hd, Hq = c->Hq, Hkv = c->Hkv, dff = c->dff;
+  const int nq = (Hq + 2 * Hkv) * hd;
+  float* h = reinterpret_cast<float*>(w + p.off_h);
+  float* qb = reinterpret_cast<float*>(w + p.off_q);
+  float* C = reinterpret_cast<float*>(w + p.off_C);
+  float* rs = reinterpret_cast<float*>(w + p.off_rs);
+  float* bpart = reinterpret_cast<float*>(w + p.off_bpart);
+  unsigned* ctr = reinterpret_cast<unsigned*>(w);
+  WT* xa = reinterpret_cast<WT*>(w + p.off_xa);  // [M][2d]: QKV and gate/up input
+  WT* xb = reinterpret_cast<WT*>(w + p.off_xb);  // [M][2 K]: O (K = Hq hd) and down (K = dff) input
+  const int ko = Hq * hd;
+  float2* rope = reinterpret_cast<float2*>(w + p.off_rope);
+  hipLaunchKernelGGL((big_rows_init_kernel<WT>), dim3(M), dim3(256), 0, st, g, h, rs, xa,
+                     static_cast<const WT*>(layers[0].attn_norm), rope, d, pos0, hd, c->rope_theta, c->rms_eps);
+  int rc = check_launch();
+  if (rc) return rc;
+  for (int l = 0; l < c->Ls; ++l) {
+    const spd_layer_weights& lw = layers[l];
+    WT* kc = static_cast<WT*>(k_cache) + (size_t)l * Hkv * T_cap * hd;
+    WT* vc = static_cast<WT*>(v_cache) + (size_t)l * Hkv * hd * T_cap;
+    launch_big_gemm(p.bqkv, xa, 2 * d, static_cast<const WT*>(lw.wqkv), C, nq, rs, M, nq, 2 * d, bpart, ctr, st,
+                    d);
+    hipLaunchKernelGGL((qk_post_kernel<WT>), dim3(Hq + Hkv, M), dim3(64), 0, st, C, nq, qb, kc,
+                       static_cast<const WT*>(lw.q_norm), static_cast<const WT*>(lw.k_norm), rope, Hq, pos0,
+                       T_cap, c->rms_eps);
+    hipLaunchKernelGGL((v_post_kernel<WT>), dim3(Hkv, (M + 63) / 64), dim3(256), 0, st, C, nq, vc,
+                       (Hq + Hkv) * hd, pos0, T_cap, M);
+    rc = check_launch();
+    if (rc) return rc;
+    {
+      FlashArgs fa;
+      fa.q = qb;
+      fa.kc = kc;
+      fa.vc = vc;
+      fa.xh = xb;  // the attention output as [hi | lo] rows of 2 Hq hd
+      fa.xl = xb + ko;
+      fa.xld = 2 * ko;
+      fa.M = M;
+      fa.Hq = Hq;
+      fa.Hkv = Hkv;
+      fa.pos0 = pos0;
+      fa.nqt = (M * (Hq / Hkv) + FA_ROWS - 1) / FA_ROWS;
+      fa.T_cap = T_cap;
+      fa.scale = aa.scale;
+      hipLaunchKernelGGL(attn_flash_kernel, dim3(fa.nqt, Hkv), dim3(256), 0, st, fa);
+      rc = check_launch();
+      if (rc) return rc;
+    }
+    launch_big_gemm(p.bo, xb, 2 * ko, static_cast<const WT*>(lw.wo), C, d, nullptr, M, d, 2 * ko, bpart, ctr, st,
+                    ko);
+    hipLaunchKernelGGL((resid_post_kernel<WT>), dim3(M), dim3(256), 0, st, C, d, h, rs, xa,
+                       static_cast<const WT*>(lw.mlp_norm), d, c->rms_eps, static_cast<const WT*>(nullptr),
+                       static_cast<float*>(nullptr), M);
+    launch_big_gemm(p.bgu, xa, 2 * d, static_cast<const WT*>(lw.w_gate_up), C, 2 * dff, rs, M, 2 * dff, 2 * d,
+                    bpart, ctr, st, d);
+    hipLaunchKernelGGL((swiglu_post_kernel<WT>), dim3((dff / 4 + 255) / 256, M), dim3(256), 0, st, C, 2 * dff,
+                       xb, dff);
+    launch_big_gemm(p.bdown, xb, 2 * dff, static_cast<const WT*>(lw.w_down), C, d, nullptr, M, d, 2 * dff, bpart,
+                    ctr, st, dff);
+    const bool last = l == c->Ls - 1;
+    hipLaunchKernelGGL((resid_post_kernel<WT>), dim3(M), dim3(256), 0, st, C, d, h, rs, last ? nullptr : xa,
+                       last ? nullptr : static_cast<const WT*>(layers[l + 1].attn_norm), d, c->rms_eps,
+                       last ? static_cast<const WT*>(final_norm) : nullptr, h_last, M);
+    rc = check_launch();
+    if (rc) return rc;
+  }
+  return SPD_OK;
+}
+
 template <typename WT>
 static int pdm_impl(const spd_config* c, const spd_layer_weights* layers, const void* final_norm,
                     void* k_cache, void* v_cache, int64_t T_cap, const float* g, int pos0, int M,
@@ -480,12 +895,7 @@ static int pdm_impl(const spd_config* c, const spd_layer_weights* layers, const 
   const XSplit<WT> none{nullptr, nullptr, 0};
 
   float2* rope = reinterpret_cast<float2*>(w + p.off_rope);
-  hipLaunchKernelGGL((rows_init_kernel<WT>), dim3(d / 64, M), dim3(64), 0, st, g, h, ss, M, d, x0,
-                     static_cast<const WT*>(layers[0].attn_norm), rope, pos0, hd, c->rope_theta);
-  int rc = check_launch();
-  if (rc) return rc;
-  int P = d / 64;  // partial count of ss
-
+  int rc;
   AttnArgs aa;
   aa.q = qb;
   aa.po = reinterpret_cast<float*>(w + p.off_po);
@@ -503,6 +913,14 @@ static int pdm_impl(const spd_config* c, const spd_layer_weights* layers, const 
   aa.T_cap = T_cap;
   aa.scale = 1.0f / sqrtf((float)hd);
 
+  if constexpr (sizeof(WT) == 2) {
+    if (p.big) return pdm_big(c, layers, final_norm, k_cache, v_cache, T_cap, g, pos0, M, h_last, w, p, aa, st);
+  }
+  hipLaunchKernelGGL((rows_init_kernel<WT>), dim3(d / 64, M), dim3(64), 0, st, g, h, ss, M, d, x0,
+                     static_cast<const WT*>(layers[0].attn_norm), rope, pos0, hd, c->rope_theta);
+  rc = check_launch();
+  if (rc) return rc;
+  int P = d / 64;  // partial count of ss
   for (int l = 0; l < c->Ls; ++l) {
     const spd_layer_weights& lw = layers[l];
     WT* kc = static_cast<WT*>(k_cache) + (size_t)l * Hkv * T_cap * hd;

@@ -50,6 +50,7 @@ struct BigGemm {
   float* part;         // [tiles][KS][BG_PART_FLOATS] when KS > 1
   unsigned* counters;  // [tiles], zero on entry, left zero
   int M, N, K, lda, ldb, ldc;
+  int kb;  // B's K: for K = 2 kb, A's row is [hi | lo] and B's columns repeat
   int mtiles, ntiles, KS;
   int kstages;  // 64-wide K stages per block (K / (64 KS))
 };
@@ -67,6 +68,7 @@ __device__ __forceinline__ int bg_swz(int r) { return r & 7; }
 __device__ __forceinline__ void bg_issue(const BigGemm& g, unsigned char* base, int st, int m0, int n0,
                                          int v, int lane) {
   const int k0 = st * BG_BK;
+  const int kB = k0 < g.kb ? k0 : k0 - g.kb;  // B column of the stage (K <= 2 kb, kb % 64 == 0)
   const int rin = lane >> 3, pc = lane & 7;  // row within the group, physical chunk
 #pragma unroll
   for (int i = 0; i < BG_LOADS; ++i) {
@@ -75,9 +77,9 @@ __device__ __forceinline__ void bg_issue(const BigGemm& g, unsigned char* base, 
     const bool isA = q < BG_A_GROUPS;
     const int r = 8 * (isA ? q : q - BG_A_GROUPS) + rin;  // tile row
     const int c = pc ^ bg_swz(r);
-    const bf16* src = isA ? g.A + (size_t)min(m0 + r, g.M - 1) * g.lda
-                          : g.B + (size_t)min(n0 + r, g.N - 1) * g.ldb;
-    __builtin_amdgcn_global_load_lds((const void*)(src + k0 + 8 * c), (lds_ptr_t)(base + q * 1024), 16, 0, 0);
+    const bf16* src = isA ? g.A + (size_t)min(m0 + r, g.M - 1) * g.lda + k0
+                          : g.B + (size_t)min(n0 + r, g.N - 1) * g.ldb + kB;
+    __builtin_amdgcn_global_load_lds((const void*)(src + 8 * c), (lds_ptr_t)(base + q * 1024), 16, 0, 0);
   }
 }
 
@@ -139,7 +141,8 @@ __device__ __forceinline__ void bg_compute(const unsigned char* sa, BgAccT (&acc
     ++s;                                                                            \
   } while (0)
 
-__global__ __launch_bounds__(BG_THREADS) void gemm_big_kernel(BigGemm g) {
+// internal linkage: every translation unit that launches it holds its own copy
+static __global__ __launch_bounds__(BG_THREADS) void gemm_big_kernel(BigGemm g) {
   // one array per ring slot: separate objects let the compiler tell the
   // direct-to-LDS writes of later stages from the reads of the current one
   __shared__ __align__(1024) unsigned char s0[BG_STAGE_BYTES];
@@ -250,5 +253,62 @@ __global__ __launch_bounds__(BG_THREADS) void gemm_big_kernel(BigGemm g) {
 }
 
 #undef BG_STEP
+
+// ---------------------------------------------------------------------------
+// Host-side planning: KS splits K so that the tiles times KS fill the GPU
+// (each part keeps at least BG_SLOTS stages of 64).
+// ---------------------------------------------------------------------------
+constexpr int BG_TARGET_BLOCKS = 256;
+
+struct BigPlan {
+  bool use;
+  int mtiles, ntiles, KS, kstages;
+  size_t part_bytes;  // partial tiles when KS > 1
+};
+
+inline BigPlan plan_big_gemm(int M, int N, int K) {
+  BigPlan b{};
+  if (M < 1 || N < 1 || K % BG_BK) return b;
+  b.mtiles = (M + BG_BM - 1) / BG_BM;
+  b.ntiles = (N + BG_BN - 1) / BG_BN;
+  const int stages = K / BG_BK;
+  if (stages < BG_SLOTS) return b;
+  b.KS = 1;
+  while (b.KS < BG_MAX_KS && b.mtiles * b.ntiles * b.KS * 2 <= BG_TARGET_BLOCKS && stages % (b.KS * 2) == 0 &&
+         stages / (b.KS * 2) >= BG_SLOTS)
+    b.KS *= 2;
+  b.kstages = stages / b.KS;
+  b.part_bytes = b.KS > 1 ? (size_t)b.mtiles * b.ntiles * b.KS * BG_PART_FLOATS * 4 : 0;
+  b.use = true;
+  return b;
+}
+
+// C[M][ldc] = rs[m] * (A[M][lda] . B[N][kb]^T) over K columns of A; K = kb, or
+// K = 2 kb with A's rows holding [hi | lo] bf16 parts of an fp32 activation (the
+// product then carries the activation to about fp32 accuracy).  counters: at
+// least mtiles * ntiles zero words, left zero.
+inline void launch_big_gemm(const BigPlan& p, const bf16* A, int lda, const bf16* B, float* C, int ldc,
+                            const float* rs, int M, int N, int K, float* part, unsigned* counters,
+                            hipStream_t st, int kb = 0) {
+  BigGemm g{};
+  g.A = A;
+  g.B = B;
+  g.C = C;
+  g.rs = rs;
+  g.part = part;
+  g.counters = counters;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.lda = lda;
+  g.kb = kb > 0 ? kb : K;
+  g.ldb = g.kb;
+  g.ldc = ldc;
+  g.mtiles = p.mtiles;
+  g.ntiles = p.ntiles;
+  g.KS = p.KS;
+  g.kstages = p.kstages;
+  hipLaunchKernelGGL(gemm_big_kernel, dim3(p.mtiles * p.ntiles * p.KS), dim3(BG_THREADS), 0, st, g);
+}
 
 }  // namespace spd

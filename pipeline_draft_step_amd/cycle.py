@@ -75,8 +75,13 @@ class SpdCycle:
         self.next_token = torch.zeros(1, dtype=torch.int32, device=device)
         self.state = torch.zeros(4, dtype=torch.int32, device=device)
         self.tokens = torch.zeros(T_cap, dtype=torch.int32, device=device)
+        # prefill runs the PDM over whole feature blocks when its large-M path
+        # applies (bf16, head size 128), else in PREFILL_BLOCK rows
+        self.pdm_block = (min(FEATURE_BLOCK, T_cap) if c.dtype == SPD_BF16 and c.hd == 128
+                          else PREFILL_BLOCK)
         ws = max(spd_workspace_size(SPD_CALL_FUSE, c, min(FEATURE_BLOCK, T_cap)),
                  spd_workspace_size(SPD_CALL_FUSE, c, PREFILL_BLOCK),
+                 spd_workspace_size(SPD_CALL_PDM, c, self.pdm_block, 0, T_cap),
                  spd_workspace_size(SPD_CALL_PDM, c, PREFILL_BLOCK, 0, T_cap),
                  spd_workspace_size(SPD_CALL_FUSE, c, c.n + 1),
                  spd_workspace_size(SPD_CALL_PDM, c, c.n + 1, 0, T_cap),
@@ -112,8 +117,8 @@ class SpdCycle:
         for s in range(0, P, FEATURE_BLOCK):
             Mf = min(FEATURE_BLOCK, P - s)
             self.features(s, Mf, 0, out=self.g_pre)
-            for b in range(0, Mf, PREFILL_BLOCK):
-                M = min(PREFILL_BLOCK, Mf - b)
+            for b in range(0, Mf, self.pdm_block):
+                M = min(self.pdm_block, Mf - b)
                 self.pdm(s + b, M, g=self.g_pre[b:b + M])
 
     def draft(self, t, words_block):

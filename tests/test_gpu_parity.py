@@ -150,11 +150,17 @@ def _check_cache_rows(cyc, cache, lo, hi, tol):
         assert rel_err(gv, cache.v[l][lo:hi]) < tol
 
 
-@pytest.mark.parametrize("shape", [synth.TINY, SMALL_BF16, SMALL_BF16_H64],
-                         ids=["tiny", "small_bf16", "small_bf16_hd64"])
+@pytest.mark.parametrize("shape", [synth.TINY, SMALL_BF16, SMALL_BF16_H64, SMALL_BF16.with_(ctx=320),
+                                   synth.HEADLINE],
+                         ids=["tiny", "small_bf16", "small_bf16_hd64", "small_bf16_large_m",
+                              "headline_large_m"])
 def test_pdm_prefill_then_cycle(shape):
     """Prefill through the library, then one saturated and one partial cycle; the
-    oracle runs the same rows incrementally (pinned equal to full recompute)."""
+    oracle runs the same rows incrementally (pinned equal to full recompute).
+    Prefills of 256 rows or more in bf16 with head size 128 take the large-M
+    path (MFMA-tiled GEMMs with bf16 activations, row kernels for the
+    epilogues): 311 rows at d = 256 and the headline's 2039 rows at d = 2560,
+    every cache row and the final row checked."""
     ci = synth.cycle_inputs(shape, device=DEV, with_heads=False)
     model = device_model(ci)
     cyc = SpdCycle(model, shape.temperature)
