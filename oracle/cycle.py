@@ -41,6 +41,8 @@ class OracleModel:
     w_tlm: np.ndarray
     pdm: O.PdmConfig
     schedule: int = O.PRE_STEP
+    top_k: int = 0           # sampling filters of both heads (T > 0)
+    top_p: float = 1.0
 
 
 @dataclass
@@ -84,7 +86,7 @@ def run_cycle(om: OracleModel, st: O.SeqState, cache: O.PdmCache, ring: dict,
         q = None
         drafted = O.argmax_first(dl)
     else:
-        q = O.softmax(dl, temperature).astype(np.float32)
+        q = O.filtered_softmax(dl, temperature, om.top_k, om.top_p).astype(np.float32)
         if probs_from is not None and "q" in probs_from:
             q = probs_from["q"]
         drafted = O.sample_probs(q, int(words[2]) >> 32)
@@ -101,7 +103,7 @@ def run_cycle(om: OracleModel, st: O.SeqState, cache: O.PdmCache, ring: dict,
         if temperature == 0:
             na, nt = O.verify([tl], None, [x], vwords, temperature=0, bonus=False)
         else:
-            p = O.softmax(tl, temperature).astype(np.float32)
+            p = O.filtered_softmax(tl, temperature, om.top_k, om.top_p).astype(np.float32)
             if probs_from is not None and "p" in probs_from:
                 p = probs_from["p"]
             out.p = p
@@ -144,4 +146,4 @@ def model_from_inputs(ci, with_heads=True) -> OracleModel:
         w_tlm=_f64(ci.w_tlm) if with_heads else None,
         pdm=O.PdmConfig(d=s.d, Hq=s.Hq, Hkv=s.Hkv, hd=s.hd, dff=s.dff, eps=s.eps,
                         rope_theta=s.rope_theta),
-        schedule=s.feature_schedule)
+        schedule=s.feature_schedule, top_k=s.top_k, top_p=s.top_p)

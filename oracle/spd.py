@@ -345,6 +345,52 @@ def softmax(logits, temperature):
     return e / e.sum()
 
 
+def top_k_set(logits, k):
+    """Ascending indices of the top-k filter's support ([SPD] 4, evaluation
+    setting: sampling runs use top-k = 50).
+
+    The k largest logits, a total order on (value descending, index ascending),
+    NaN below every number; -0 and +0 are equal values.  k <= 0 or k >= V keeps
+    every index.
+    """
+    x = np.asarray(logits, dtype=np.float64)
+    V = len(x)
+    if k <= 0 or k >= V:
+        return np.arange(V)
+    nan = np.isnan(x)
+    key = np.where(nan, 0.0, x)
+    order = np.lexsort((np.arange(V), -key, nan))   # last key is the primary one
+    return np.sort(order[:k])
+
+
+def filtered_softmax(logits, temperature, top_k=0, top_p=1.0):
+    """Sampling distribution after the top-k and top-p filters, zero outside
+    the kept set ([SPD] 4 evaluation setting: T = 1, top-k = 50, top-p = 1.0).
+
+    top-k: softmax(logits / T) restricted to top_k_set(logits, top_k) and
+    renormalised (top_k = 0: no filter).
+    top-p (nucleus, applied after top-k, only when top_k >= 1 and 0 < top_p < 1):
+    order the kept tokens by probability (descending; probability is increasing
+    in the logit, so this is the logit order, equal logits by ascending index),
+    keep the shortest prefix whose mass reaches top_p, renormalise over it.
+    """
+    x = np.asarray(logits, dtype=np.float64)
+    keep = top_k_set(x, top_k)
+    z = x[keep] / float(temperature)
+    e = np.exp(z - z.max())
+    pk = e / e.sum()
+    if top_k >= 1 and 0.0 < top_p < 1.0:
+        order = np.lexsort((keep, -x[keep]))         # logit desc, index asc
+        before = np.concatenate(([0.0], np.cumsum(pk[order])[:-1]))
+        m = int(np.count_nonzero(before < top_p))    # prefix mass before a kept token < top_p
+        sub = np.sort(order[:m])
+        keep, e = keep[sub], e[sub]
+        pk = e / e.sum()
+    p = np.zeros(len(x))
+    p[keep] = pk
+    return p
+
+
 def prob_weights(p32):
     """Exact integer weights of an fp32 probability row: floor(p * 2^52).
     Non-positive and NaN entries weigh 0."""

@@ -50,6 +50,8 @@ class SpdShape:
     anchor_mode: int = ZERO_MASK
     norm_k0: int = 0
     feature_schedule: int = 0  # 0 pre-step, 1 post-step, 2 first-stage only
+    top_k: int = 0             # sampling filters at T > 0 (0 / 1.0: off)
+    top_p: float = 1.0
     eps: float = 1e-6
     rope_theta: float = 1e6
 

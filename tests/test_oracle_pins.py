@@ -353,6 +353,126 @@ def test_softmax_matches_torch():
         assert np.allclose(p, torch.softmax(torch.tensor(x) / T, 0).numpy(), atol=1e-15)
 
 
+# ------------------------------------------------------------------ top-k / top-p filters
+
+def _brute_top_k(x, k):
+    """i is kept iff fewer than k entries precede it in the order value descending,
+    equal values by ascending index, NaN after every number (rank counting)."""
+    V = len(x)
+
+    def precedes(j, i):
+        a, b = x[j], x[i]
+        if math.isnan(a):
+            return math.isnan(b) and j < i
+        if math.isnan(b):
+            return True
+        return a > b or (a == b and j < i)
+
+    return [i for i in range(V) if sum(precedes(j, i) for j in range(V)) < k]
+
+
+def test_top_k_set_brute_force_with_ties():
+    rng = np.random.default_rng(20)
+    for trial in range(60):
+        V = int(rng.integers(1, 20))
+        x = rng.integers(-3, 4, size=V).astype(np.float64)     # many equal values
+        if trial % 4 == 0:
+            x[rng.integers(0, V)] = np.nan
+        if trial % 5 == 0:
+            x[rng.integers(0, V)] = -0.0
+        for k in range(-1, V + 2):
+            want = list(range(V)) if k <= 0 or k >= V else _brute_top_k(list(x), k)
+            assert list(O.top_k_set(x, k)) == want, (x, k)
+
+
+def test_top_k_set_matches_torch_topk_on_distinct_values():
+    x = np.random.default_rng(21).standard_normal(4096) * 3
+    for k in (1, 50, 257, 4095):
+        ref = np.sort(torch.topk(torch.tensor(x), k).indices.numpy())
+        assert np.array_equal(O.top_k_set(x, k), ref)
+
+
+def test_top_k_softmax_is_masked_torch_softmax():
+    """top-k alone: softmax of the logits with every other entry set to -inf."""
+    x = np.random.default_rng(22).standard_normal(1000) * 3
+    for T in (1.0, 0.6):
+        for k in (0, 1, 50, 999, 1000):
+            xt = torch.tensor(x)
+            if 0 < k < len(x):
+                idx = torch.topk(xt, k).indices
+                masked = torch.full_like(xt, -math.inf)
+                masked[idx] = xt[idx]
+            else:
+                masked = xt
+            ref = torch.softmax(masked / T, 0).numpy()
+            got = O.filtered_softmax(x, T, k)
+            assert np.allclose(got, ref, rtol=0, atol=1e-15)
+            assert np.count_nonzero(got) == (k if 0 < k < len(x) else len(x))
+    one = O.filtered_softmax(x, 1.0, 1)
+    assert one[O.argmax_first(x)] == 1.0 and one.sum() == 1.0
+
+
+def test_top_p_worked_example():
+    """p = (0.4, 0.3, 0.2, 0.1): the nucleus for 0.65 is the first two tokens (0.7
+    >= 0.65 > 0.4), for 0.75 the first three; top_p = 1 keeps everything."""
+    x = np.log([0.1, 0.4, 0.2, 0.3])
+    got = O.filtered_softmax(x, 1.0, 4, 0.65)
+    assert np.allclose(got, [0, 4 / 7, 0, 3 / 7], atol=1e-15)
+    got = O.filtered_softmax(x, 1.0, 4, 0.75)
+    assert np.allclose(got, [0, 4 / 9, 2 / 9, 3 / 9], atol=1e-15)
+    assert np.allclose(O.filtered_softmax(x, 1.0, 4, 1.0), [0.1, 0.4, 0.2, 0.3], atol=1e-15)
+    assert np.allclose(O.filtered_softmax(x, 1.0, 3, 1e-9), [0, 1, 0, 0], atol=0)
+    # top_k = 0 leaves top_p off
+    assert np.allclose(O.filtered_softmax(x, 1.0, 0, 0.5), [0.1, 0.4, 0.2, 0.3], atol=1e-15)
+
+
+def test_top_p_matches_ascending_cumulative_removal():
+    """A second formulation of the nucleus: sort ascending, drop the tokens whose
+    cumulative mass is <= 1 - top_p, always keep the most probable one."""
+    rng = np.random.default_rng(23)
+    for trial in range(30):
+        V = 600
+        x = rng.standard_normal(V) * 2.5
+        k = int(rng.choice([5, 50, 200, 600]))
+        top_p = float(rng.choice([0.2, 0.5, 0.9, 0.97]))
+        T = float(rng.choice([1.0, 0.7]))
+        xt = torch.tensor(x) / T
+        if k < V:
+            idx = torch.topk(xt, k).indices
+            masked = torch.full_like(xt, -math.inf)
+            masked[idx] = xt[idx]
+        else:
+            masked = xt
+        probs = torch.softmax(masked, 0)
+        sp, si = torch.sort(probs)
+        remove = torch.cumsum(sp, 0) <= 1 - top_p
+        remove[-1] = False
+        masked2 = masked.clone()
+        masked2[si[remove]] = -math.inf
+        ref = torch.softmax(masked2, 0).numpy()
+        got = O.filtered_softmax(x, T, k, top_p)
+        assert np.allclose(got, ref, rtol=0, atol=1e-14), (trial, k, top_p)
+
+
+def test_verify_law_is_exactly_filtered_p():
+    """Verification with top-k/top-p filtered p and q (zeros outside their sets,
+    supports that differ) still outputs exactly p."""
+    rng = np.random.default_rng(24)
+    for V, k, tp in ((6, 3, 1.0), (8, 4, 0.8), (7, 7, 0.6)):
+        for _ in range(3):
+            lp = rng.standard_normal(V) * 2
+            lq = lp + rng.standard_normal(V)
+            p = O.filtered_softmax(lp, 1.0, k, tp).astype(np.float32)
+            q = O.filtered_softmax(lq, 1.0, k, tp).astype(np.float32)
+            law = _exact_output_distribution(p, q, O.residual_weights)
+            ps = sum(Fraction(float(v)) for v in p)
+            for j in range(V):
+                want = Fraction(float(p[j])) / ps
+                assert abs(float(law[j]) - float(want)) < V * 2.0 ** -22
+                if p[j] == 0:
+                    assert law[j] == 0
+
+
 # ------------------------------------------------------------------ P11
 
 def test_sampler_interval_boundaries():
