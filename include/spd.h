@@ -66,6 +66,7 @@ enum { SPD_CALL_FUSE = 0, SPD_CALL_PDM = 1, SPD_CALL_LM_HEAD = 2, SPD_CALL_VERIF
 #define SPD_WS_COUNTER_BYTES 65536
 #define SPD_MAX_ANCHORS 8
 #define SPD_MAX_STAGES 32
+#define SPD_TOP_K_MAX 256
 
 /* Sizes of the target, the PDM and the heads (section 3.1-3.2, section 4 setup). */
 typedef struct spd_config {
@@ -83,6 +84,10 @@ typedef struct spd_config {
   float rms_eps;       /* 1e-6                                                   */
   float rope_theta;    /* 1e6                                                    */
   int32_t feature_schedule; /* SPD_SCHEDULE_PRE_STEP (default), _POST_STEP, _FIRST_STAGE */
+  int32_t top_k;       /* sampling filter of spd_lm_head at T > 0: 0 = off, else   */
+                       /* 1..SPD_TOP_K_MAX (section 4 evaluation setting: 50)      */
+  float top_p;         /* nucleus mass, used when top_k >= 1 and 0 < top_p < 1;   */
+                       /* 0 and 1 = off (section 4 evaluation setting: 1.0)        */
 } spd_config;
 
 /* One PDM decoder layer (DEVICE pointers, cfg.dtype).  Row-major [rows][cols]. */
@@ -187,6 +192,12 @@ int spd_pdm_step(const spd_config *cfg, const spd_layer_weights *layers, const v
  *   token[r] = inverse-CDF draw from the integer weights w_j = floor(probs_j * 2^52):
  *   u = words[r] >> 32, tau = floor(u * sum(w) / 2^32), token = smallest j whose
  *   inclusive prefix sum of w exceeds tau.
+ *   With cfg.top_k >= 1 (section 4 evaluation setting: T = 1, top-k = 50, top-p = 1)
+ *   the softmax is taken over the cfg.top_k largest logits only (equal logits rank by
+ *   ascending index, NaN last) and probs is 0 elsewhere; with 0 < cfg.top_p < 1 it is
+ *   further restricted to the shortest run of those, in descending logit order, whose
+ *   top-k probability (computed in float64) reaches top_p, and renormalised.  The draw
+ *   is the same inverse CDF over the filtered probs.
  * w_lm DEVICE [V][d] (cfg.dtype); h DEVICE float [rows][d]; words DEVICE uint64 [rows];
  * logits, probs DEVICE float [rows][V]; token DEVICE int32 [rows].
  */
@@ -233,6 +244,7 @@ int spd_rollback(spd_seq_state *st, int32_t n, const int32_t *drafted, const int
 
 const char *spd_status_string(int status);
 int spd_last_hip_error(void);
+/* Version of this interface: 2 (spd_config gained top_k and top_p). */
 int spd_version(void);
 
 #ifdef __cplusplus

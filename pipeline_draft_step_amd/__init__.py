@@ -21,6 +21,7 @@ SPD_CALL_FUSE, SPD_CALL_PDM, SPD_CALL_LM_HEAD, SPD_CALL_VERIFY = 0, 1, 2, 3
 SPD_WS_COUNTER_BYTES = 65536
 SPD_MAX_ANCHORS = 8
 SPD_MAX_STAGES = 32
+SPD_TOP_K_MAX = 256
 
 EXPORTED = (
     "spd_slot_table", "spd_layout", "spd_workspace_size", "spd_fuse_features",
@@ -34,7 +35,9 @@ class spd_config(ctypes.Structure):
                 ("L", "n", "m", "d", "Ls", "Hq", "Hkv", "hd", "dff", "V", "dtype",
                  "anchor_mode", "norm_k0")] + [("rms_eps", ctypes.c_float),
                                                ("rope_theta", ctypes.c_float),
-                                               ("feature_schedule", ctypes.c_int32)]
+                                               ("feature_schedule", ctypes.c_int32),
+                                               ("top_k", ctypes.c_int32),
+                                               ("top_p", ctypes.c_float)]
 
 
 class spd_layer_weights(ctypes.Structure):
@@ -125,9 +128,10 @@ def _i32_array(values):
 
 
 def make_config(*, L, n, m, d, Ls, Hq, Hkv, hd, dff, V, dtype, anchor_mode=0, norm_k0=0,
-                rms_eps=1e-6, rope_theta=1e6, feature_schedule=0) -> spd_config:
+                rms_eps=1e-6, rope_theta=1e6, feature_schedule=0, top_k=0,
+                top_p=1.0) -> spd_config:
     return spd_config(L, n, m, d, Ls, Hq, Hkv, hd, dff, V, dtype, anchor_mode, norm_k0,
-                      rms_eps, rope_theta, feature_schedule)
+                      rms_eps, rope_theta, feature_schedule, top_k, top_p)
 
 
 # ----------------------------------------------------------------- host helpers

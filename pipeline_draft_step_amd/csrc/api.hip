@@ -143,4 +143,4 @@ extern "C" const char* spd_status_string(int status) {
 
 extern "C" int spd_last_hip_error(void) { return last_hip_error_ref(); }
 
-extern "C" int spd_version(void) { return 1; }
+extern "C" int spd_version(void) { return 2; }

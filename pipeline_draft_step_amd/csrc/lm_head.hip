@@ -455,12 +455,284 @@ __global__ __launch_bounds__(SMX_THREADS) void softmax_sample_kernel(
   SPD_MARK(4);
 }
 
+// ---------------------------------------------------------------- top-k / top-p sampling
+//
+// Sampling filters of the evaluation setting of "Speculative Pipeline Decoding"
+// (section 4: T = 1 with top-k = 50 and top-p = 1.0).  One kernel, grid
+// (chunks, rows): every block selects its chunk's k largest logits with a radix
+// selection in LDS, hands them over as candidates and zeroes the rest of its
+// probability range; the last block to arrive selects the k largest of all
+// candidates, applies the nucleus cut, writes their probabilities and draws the
+// token with the same exact integer inverse CDF as the unfiltered path.  Every
+// probability entry is written by exactly one block.
+
+constexpr int TOPK_BINS = 2048;        // 11-bit digits
+constexpr int TOPK_KMAX = SPD_TOP_K_MAX;
+constexpr int TOPK_BATCH = 16;         // candidate keys per thread and load batch
+static_assert(TOPK_KMAX <= SMX_THREADS, "one set member per thread in the last block");
+
+// 64-bit selection key: the logit's order-preserving bit pattern above the
+// complemented index, so keys are distinct and a larger key means a larger value,
+// equal values ranking by ascending index.  NaN maps below every number and -0 onto
+// +0.  A real key has bit 31 set (indices are below 2^31); 0 means "no item".
+__device__ __forceinline__ uint64_t topk_key(float x, int j) {
+  const uint32_t b = x == 0.f ? 0u : __float_as_uint(x);
+  const uint32_t o = x != x ? 0u : ((b & 0x80000000u) ? ~b : (b | 0x80000000u));
+  return ((uint64_t)o << 32) | (uint32_t)~(uint32_t)j;
+}
+__device__ __forceinline__ float topk_value(uint64_t key) {
+  const uint32_t o = (uint32_t)(key >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+__device__ __forceinline__ int topk_index(uint64_t key) { return (int)~(uint32_t)key; }
+
+struct SelShared {
+  unsigned hist[TOPK_BINS];
+  unsigned wtot[SMX_THREADS / 64];
+  unsigned digit, need, exact;
+};
+
+// The k-th largest of the non-zero keys the block visits (exactly k of them are
+// >= the result).  Needs more than k non-zero keys.  Most significant digit first,
+// 11 bits at a time; a pass histograms the keys that share the digits fixed so far
+// and fixes the digit whose bucket holds the k-th key.  It stops once that bucket
+// holds exactly the keys still needed: all of them are selected, so the bucket's
+// lowest key value (digits below zero) is a valid threshold.  With distinct keys
+// this happens at the latest on the last digit.  visit(f) calls f(key) for every
+// key of every thread; all threads call this function.
+template <class Visit>
+__device__ uint64_t select_kth(const Visit& visit, unsigned k, SelShared& s) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  constexpr int BPT = TOPK_BINS / SMX_THREADS;  // bins owned by a thread in the search
+  uint64_t prefix = 0;
+  unsigned need = k;
+  int hi = 64;  // bits >= hi are fixed
+  while (hi > 0) {
+    const int bits = hi > 11 ? 11 : hi;
+    const int shift = hi - bits;
+    for (int b = t; b < TOPK_BINS; b += SMX_THREADS) s.hist[b] = 0u;
+    __syncthreads();
+    const uint64_t hmask = hi == 64 ? 0ull : ~0ull << hi;
+    const unsigned dmask = (1u << bits) - 1u;
+    visit([&](uint64_t key) {
+      if (key != 0ull && (key & hmask) == prefix)
+        atomicAdd(&s.hist[(unsigned)(key >> shift) & dmask], 1u);
+    });
+    __syncthreads();
+    unsigned c[BPT], sum = 0;
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      c[i] = s.hist[BPT * t + i];
+      sum += c[i];
+    }
+    int incl = (int)sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    if (lane == 63) s.wtot[wave] = (unsigned)incl;
+    __syncthreads();
+    // keys in higher bins: the later lanes of this wave, then the later waves
+    unsigned above = (unsigned)(__shfl(incl, 63, 64) - incl);
+    for (int w = wave + 1; w < SMX_THREADS / 64; ++w) above += s.wtot[w];
+    if (above < need && need <= above + sum) {  // exactly one thread
+      for (int i = BPT - 1; i >= 0; --i) {
+        if (above + c[i] >= need) {
+          s.digit = (unsigned)(BPT * t + i);
+          s.need = need - above;
+          s.exact = c[i] == need - above;
+          break;
+        }
+        above += c[i];
+      }
+    }
+    __syncthreads();
+    prefix |= (uint64_t)s.digit << shift;
+    need = s.need;
+    hi = shift;
+    const bool done = s.exact != 0u;
+    __syncthreads();  // s is reused by the next pass or the caller
+    if (done) break;
+  }
+  return prefix;
+}
+
+__device__ __forceinline__ float block_sum_f32(float v, float* red) {
+  v = wave_sum(v);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  v = (red[0] + red[1]) + (red[2] + red[3]);
+  __syncthreads();
+  return v;
+}
+
+// exclusive prefix sum over the threads of the block, in thread order; *total gets the sum
+__device__ __forceinline__ double block_excl_scan_f64(double v, double* red, double* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  double incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) red[wave] = incl;
+  __syncthreads();
+  double before = 0.0;
+  for (int w = 0; w < wave; ++w) before += red[w];
+  *total = (red[0] + red[1]) + (red[2] + red[3]);
+  __syncthreads();
+  return before + incl - v;
+}
+
+__global__ __launch_bounds__(SMX_THREADS) void topk_sample_kernel(
+    const float* logits, float* probs, uint64_t* cand, unsigned* counters, const uint64_t* words,
+    int V, int nchunks, int k, float T, float top_p, int32_t* token) {
+  __shared__ SelShared s;
+  __shared__ unsigned s_cnt;
+  __shared__ uint64_t s_sel[TOPK_KMAX];   // the selected keys, in arrival order
+  __shared__ uint64_t s_ord[TOPK_KMAX];   // ... in descending key order
+  __shared__ int s_irank[TOPK_KMAX];      // index rank of s_ord[i]
+  __shared__ uint64_t s_w[TOPK_KMAX];     // integer weights in ascending index order
+  __shared__ int s_idx[TOPK_KMAX];        // vocabulary index in ascending index order
+  __shared__ float s_rf[SMX_THREADS / 64];
+  __shared__ double s_rd[SMX_THREADS / 64];
+  __shared__ uint64_t s_ru[SMX_THREADS / 64];
+  const int c = blockIdx.x, r = blockIdx.y, t = threadIdx.x;
+  const int wave = t >> 6, lane = t & 63;
+  const int cs = k < SMX_CHUNK ? k : SMX_CHUNK;  // candidate slots per chunk
+  const float* lr = logits + (size_t)r * V;
+  float* pr = probs + (size_t)r * V;
+  uint64_t* cr = cand + (size_t)r * nchunks * cs;
+  const int base = c * SMX_CHUNK;
+  const int n = min(SMX_CHUNK, V - base);
+  constexpr int PER = SMX_CHUNK / SMX_THREADS;
+  uint64_t key[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int j = base + t + SMX_THREADS * e;
+    const float x = lr[j < V ? j : 0];
+    key[e] = j < V ? topk_key(x, j) : 0ull;
+  }
+  uint64_t th = 1ull;  // every real key is >= 1
+  if (n > k)
+    th = select_kth(
+        [&](auto f) {
+#pragma unroll
+          for (int e = 0; e < PER; ++e) f(key[e]);
+        },
+        (unsigned)k, s);
+  if (t == 0) s_cnt = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    if (key[e] == 0ull) continue;
+    if (key[e] >= th) {
+      const unsigned slot = atomicAdd(&s_cnt, 1u);  // < min(k, n) <= cs
+      if (slot < (unsigned)cs) st_coh_u64(cr + (size_t)c * cs + slot, key[e]);
+    } else {
+      pr[base + t + SMX_THREADS * e] = 0.f;
+    }
+  }
+  if (!arrive_last(counters + r, (unsigned)nchunks)) return;
+
+  // ---- last block: the k largest of all candidates
+  const int ncand = (nchunks - 1) * cs + min(k, V - (nchunks - 1) * SMX_CHUNK);
+  int kk = min(k, V);
+  auto visit_cand = [&](auto f) {
+    for (int b0 = 0; b0 < ncand; b0 += SMX_THREADS * TOPK_BATCH) {
+      uint64_t kv[TOPK_BATCH];
+#pragma unroll
+      for (int e = 0; e < TOPK_BATCH; ++e) {
+        const int i = b0 + t + SMX_THREADS * e;
+        const uint64_t v = ld_coh_u64(cr + (i < ncand ? i : 0));
+        kv[e] = i < ncand ? v : 0ull;
+      }
+#pragma unroll
+      for (int e = 0; e < TOPK_BATCH; ++e) f(kv[e]);
+    }
+  };
+  uint64_t th2 = 1ull;
+  if (ncand > kk) th2 = select_kth(visit_cand, (unsigned)kk, s);
+  if (t == 0) s_cnt = 0u;
+  __syncthreads();
+  visit_cand([&](uint64_t key2) {
+    if (key2 == 0ull) return;
+    if (key2 >= th2) {
+      const unsigned slot = atomicAdd(&s_cnt, 1u);  // exactly kk keys pass
+      if (slot < (unsigned)TOPK_KMAX) s_sel[slot] = key2;
+    } else if ((unsigned)topk_index(key2) < (unsigned)V) {
+      pr[topk_index(key2)] = 0.f;
+    }
+  });
+  __syncthreads();
+  kk = min(kk, (int)s_cnt);  // equal unless the candidates were inconsistent
+  // ranks of each member by key (descending) and by index (ascending)
+  if (t < kk) {
+    const uint64_t mine = s_sel[t];
+    const int mi = topk_index(mine);
+    int rk = 0, ri = 0;
+    for (int q = 0; q < kk; ++q) {
+      const uint64_t o = s_sel[q];
+      rk += o > mine;
+      ri += topk_index(o) < mi;
+    }
+    s_ord[rk] = mine;
+    s_irank[rk] = ri;
+  }
+  __syncthreads();
+  // thread t < kk now owns the member of key rank t
+  const bool member = t < kk;
+  const uint64_t my = member ? s_ord[t] : 0ull;
+  const float v = member ? topk_value(my) : 0.f;
+  const float vmax = topk_value(s_ord[0]);
+  bool keep = member;
+  if (top_p > 0.f && top_p < 1.f) {
+    // nucleus: keep the members whose preceding top-k mass (descending order) is below
+    // top_p; the mass is taken in float64
+    const double z0 = (double)vmax / (double)T;
+    const double e64 = member ? exp((double)v / (double)T - z0) : 0.0;
+    double S64, S2;
+    block_excl_scan_f64(e64, s_rd, &S64);
+    const double p64 = member ? e64 / S64 : 0.0;
+    const double before = block_excl_scan_f64(p64, s_rd, &S2);
+    keep = member && before < (double)top_p;
+  }
+  const float inv_t = 1.0f / T;
+  const float e32 = keep ? expf((v - vmax) * inv_t) : 0.f;
+  const float Z = block_sum_f32(e32, s_rf);
+  const float p = keep ? e32 * (1.0f / Z) : 0.f;
+  if (member) {
+    const int ix = topk_index(my);
+    if ((unsigned)ix < (unsigned)V) st_coh(pr + ix, p);
+    s_w[s_irank[t]] = prob_weight(p);
+    s_idx[s_irank[t]] = ix;
+  }
+  __syncthreads();
+  // inverse CDF in ascending index order
+  const uint64_t w = member ? s_w[t] : 0ull;
+  const uint64_t winc = wave_scan_u64(w);
+  if (lane == 63) s_ru[wave] = winc;
+  __syncthreads();
+  uint64_t before = 0;
+  for (int q = 0; q < wave; ++q) before += s_ru[q];
+  const uint64_t Sw = (s_ru[0] + s_ru[1]) + (s_ru[2] + s_ru[3]);
+  const uint64_t tau = scale_u32((uint32_t)(words[r] >> 32), Sw);
+  const uint64_t lo = before + winc - w;
+  if (Sw == 0ull) {
+    if (t == 0) token[r] = 0;
+  } else if (member && lo <= tau && tau < lo + w) {
+    token[r] = s_idx[t];
+  }
+}
+
 struct LmPlan {
   bool dot;
   int J;
   GemmPlan gp;
   int nstat, nchunks;
-  size_t off_part, off_stat, off_gstat, off_csum, total;
+  size_t off_part, off_stat, off_gstat, off_csum, off_cand, total;
 };
 
 static LmPlan plan_lm(const spd_config* c, int rows) {
@@ -478,6 +750,7 @@ static LmPlan plan_lm(const spd_config* c, int rows) {
   p.off_stat = take((size_t)p.nstat * rows * sizeof(BlockStat));
   p.off_gstat = take((size_t)rows * sizeof(BlockStat));
   p.off_csum = take((size_t)rows * p.nchunks * 8);
+  p.off_cand = take(c->top_k > 0 ? (size_t)rows * p.nchunks * std::min(c->top_k, SMX_CHUNK) * 8 : 0);
   p.total = off;
   return p;
 }
@@ -534,6 +807,12 @@ static int lm_impl(const spd_config* c, const void* w_lm, const float* h, int ro
     EpiLogits epi{logits, stat, c->V, rows, inv_t, p.gp.nblocks, f};
     rc = launch_gemm<WT, 2>(p.gp, g, InAct<WT, float>{h, c->d}, epi, RowMapStd{}, st);
     if (rc || T <= 0.f) return rc;
+  }
+  if (c->top_k > 0) {
+    hipLaunchKernelGGL(topk_sample_kernel, dim3(p.nchunks, rows), dim3(SMX_THREADS), 0, st, logits,
+                       probs, reinterpret_cast<uint64_t*>(w + p.off_cand), ctr + CTR_HEAD + 512,
+                       words, c->V, p.nchunks, c->top_k, T, c->top_p, token);
+    return check_launch();
   }
   hipLaunchKernelGGL(softmax_sample_kernel, dim3(p.nchunks, rows), dim3(SMX_THREADS), 0, st, stat,
                      p.dot ? p.nstat : 0, rows, f.gstat, logits, probs,

@@ -34,6 +34,8 @@ inline int check_config(const spd_config* c) {
   if (!(c->rms_eps >= 0.f)) return SPD_E_INVALID;
   if (c->feature_schedule < SPD_SCHEDULE_PRE_STEP || c->feature_schedule > SPD_SCHEDULE_FIRST_STAGE)
     return SPD_E_INVALID;
+  if (c->top_k < 0 || c->top_k > SPD_TOP_K_MAX || !(c->top_p >= 0.f && c->top_p <= 1.f))
+    return SPD_E_INVALID;
   return SPD_OK;
 }
 

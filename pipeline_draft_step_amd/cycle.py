@@ -36,11 +36,12 @@ class DeviceWeights:
 
 class SpdModel:
     def __init__(self, *, L, n, anchors, d, Ls, Hq, Hkv, hd, dff, V, dtype, weights: DeviceWeights,
-                 anchor_mode=0, norm_k0=0, eps=1e-6, rope_theta=1e6, feature_schedule=0):
+                 anchor_mode=0, norm_k0=0, eps=1e-6, rope_theta=1e6, feature_schedule=0,
+                 top_k=0, top_p=1.0):
         self.cfg = make_config(L=L, n=n, m=len(anchors), d=d, Ls=Ls, Hq=Hq, Hkv=Hkv, hd=hd,
                                dff=dff, V=V, dtype=dtype, anchor_mode=anchor_mode,
                                norm_k0=norm_k0, rms_eps=eps, rope_theta=rope_theta,
-                               feature_schedule=feature_schedule)
+                               feature_schedule=feature_schedule, top_k=top_k, top_p=top_p)
         self.anchors = list(anchors)
         self.slot_tab, self.store_layers = spd_slot_table(self.cfg, self.anchors)
         self.w = weights

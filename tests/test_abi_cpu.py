@@ -21,7 +21,7 @@ def test_header_symbols_are_exported():
     for n in names:                      # the binding uses the C names
         if n not in ("spd_status_string", "spd_last_hip_error"):
             assert hasattr(spd, n), n
-    assert spd.spd_version() == 1
+    assert spd.spd_version() == 2
 
 
 def _cfg(s, **kw):
@@ -61,6 +61,22 @@ def test_config_rejects_unknown_schedule():
     s = synth.TINY
     with pytest.raises(spd.SpdError):
         spd.spd_slot_table(_cfg(s, feature_schedule=3), s.anchors)
+
+
+@pytest.mark.parametrize("top_k,top_p", [(-1, 1.0), (spd.SPD_TOP_K_MAX + 1, 1.0), (50, 1.5),
+                                         (50, -0.1), (50, float("nan"))])
+def test_config_rejects_bad_sampling_filters(top_k, top_p):
+    s = synth.TINY
+    with pytest.raises(spd.SpdError):
+        spd.spd_slot_table(_cfg(s, top_k=top_k, top_p=top_p), s.anchors)
+
+
+def test_lm_head_workspace_holds_top_k_candidates():
+    s = synth.HEADLINE
+    base = spd.spd_workspace_size(spd.SPD_CALL_LM_HEAD, _cfg(s), 1)
+    for k in (1, 50, spd.SPD_TOP_K_MAX):
+        ws = spd.spd_workspace_size(spd.SPD_CALL_LM_HEAD, _cfg(s, top_k=k), 1)
+        assert ws >= base + (-(-s.V // 2048)) * k * 8
 
 
 def test_slot_table_rejects_bad_anchors():

@@ -37,7 +37,7 @@ def device_model(ci):
     return SpdModel(L=s.L, n=s.n, anchors=s.anchors, d=s.d, Ls=s.Ls, Hq=s.Hq, Hkv=s.Hkv, hd=s.hd,
                     dff=s.dff, V=s.V, dtype=s.dtype, weights=w, anchor_mode=s.anchor_mode,
                     norm_k0=s.norm_k0, eps=s.eps, rope_theta=s.rope_theta,
-                    feature_schedule=s.feature_schedule)
+                    feature_schedule=s.feature_schedule, top_k=s.top_k, top_p=s.top_p)
 
 
 def row_depths(M, a, n):
@@ -277,6 +277,89 @@ def test_lm_head_is_deterministic():
     assert torch.equal(l2, logits) and torch.equal(p2, probs) and torch.equal(t2, tok)
 
 
+# ------------------------------------------------------------------ top-k / top-p sampling
+
+def _run_lm(W, h, V, d, dtype, rows, T, seed, top_k, top_p):
+    cfg = spd.make_config(L=1, n=1, m=1, d=d, Ls=1, Hq=1, Hkv=1, hd=16, dff=64, V=V, dtype=dtype,
+                          top_k=top_k, top_p=top_p)
+    words = synth.rand_words(seed, 5, rows)
+    wt = synth.words_tensor(words, DEV)
+    logits = torch.empty(rows, V, device=DEV)
+    probs = torch.full((rows, V), -1.0, device=DEV)     # every entry must be written
+    tok = torch.full((rows,), -7, dtype=torch.int32, device=DEV)
+    ws = torch.zeros(spd.spd_workspace_size(spd.SPD_CALL_LM_HEAD, cfg, rows), dtype=torch.uint8,
+                     device=DEV)
+    spd.spd_lm_head(cfg, W, h, rows, T, wt, logits, probs, tok, ws)
+    torch.cuda.synchronize()
+    return words, logits, probs, tok
+
+
+def _check_filtered(words, logits, probs, tok, T, top_k, top_p):
+    """The kept set is exact (the oracle's filters applied to the device's fp32
+    logits), the probabilities are within fp32 rounding of the oracle's, and the
+    token is the oracle's draw from the device's probability row."""
+    toks = tok.cpu().numpy()
+    for r in range(logits.shape[0]):
+        lg = logits[r].cpu().numpy().astype(np.float64)
+        gp = probs[r].cpu().numpy()
+        ref = O.filtered_softmax(lg, T, top_k, top_p)
+        assert np.array_equal(np.flatnonzero(gp), np.flatnonzero(ref)), r
+        assert np.max(np.abs(gp - ref)) <= 2e-6 * ref.max(), r
+        assert abs(float(gp.astype(np.float64).sum()) - 1.0) < 1e-5
+        assert toks[r] == O.sample_probs(gp, int(words[r]) >> 32), r
+
+
+TOPK_CASES = [
+    # name, V, d, dtype, std, rows, T, top_k, top_p
+    ("full_k50", 151936, 2560, 1, 3.0 / np.sqrt(2560), 1, 1.0, 50, 1.0),
+    ("full_k50_p09", 151936, 2560, 1, 3.0 / np.sqrt(2560), 1, 1.0, 50, 0.9),
+    ("full_k256", 151936, 2560, 1, 3.0 / np.sqrt(2560), 1, 1.0, 256, 1.0),
+    ("full_k256_p05", 151936, 2560, 1, 3.0 / np.sqrt(2560), 1, 0.7, 256, 0.5),
+    ("full_k1", 151936, 2560, 1, 3.0 / np.sqrt(2560), 1, 1.0, 1, 1.0),
+    ("ragged_k50", 151936 - 37, 2560, 1, 3.0 / np.sqrt(2560), 1, 1.0, 50, 1.0),
+    ("rows3_k50", 151936, 2560, 1, 3.0 / np.sqrt(2560), 3, 1.0, 50, 0.95),
+    ("9b_k50", 151936, 4096, 1, 3.0 / np.sqrt(4096), 1, 1.0, 50, 1.0),
+    ("small_three_chunks", 5000, 64, 0, 1.0, 2, 0.7, 100, 0.8),
+    ("k_above_v", 200, 64, 0, 1.0, 1, 1.0, 256, 1.0),
+    ("k_equals_v", 256, 64, 0, 1.0, 1, 1.0, 256, 0.3),
+    ("k_in_last_chunk_only", 2049, 64, 0, 1.0, 1, 1.0, 2, 1.0),
+]
+
+
+@pytest.mark.parametrize("name,V,d,dtype,std,rows,T,top_k,top_p", TOPK_CASES,
+                         ids=[c[0] for c in TOPK_CASES])
+def test_lm_head_top_k_top_p(name, V, d, dtype, std, rows, T, top_k, top_p):
+    say("lm_head filters", name)
+    wdt = synth.storage_dtype(dtype)
+    W = synth.normal((V, d), std, device=DEV, seed=31, name="w_lm", dtype=wdt)
+    h = synth.normal((rows, d), 1.0, device=DEV, seed=31, name="h")
+    words, logits, probs, tok = _run_lm(W, h, V, d, dtype, rows, T, 31, top_k, top_p)
+    Wh, hh = f64(W), f64(h)
+    for r in range(rows):
+        assert rel_err(f64(logits[r]), O.lm_logits(Wh, hh[r])) < tol_for(dtype), r
+    _check_filtered(words, logits, probs, tok, T, top_k, top_p)
+
+
+@pytest.mark.parametrize("V,top_k", [(5000, 50), (151936, 50), (151936, 256)])
+def test_lm_head_top_k_ties_break_by_index(V, top_k):
+    """Integer-valued logits (small integer weights, 0/1 hidden rows: every sum is
+    exact in any order) with thousands of equal values: the kept set takes the
+    lowest indices among the equal logits at the cut; the result is repeatable."""
+    say("lm_head ties", V, top_k)
+    d = 64
+    gen = torch.Generator().manual_seed(41)
+    W = torch.randint(-2, 3, (V, d), generator=gen).float().to(DEV)
+    h = torch.randint(0, 2, (1, d), generator=gen).float().to(DEV)
+    words, logits, probs, tok = _run_lm(W, h, V, d, 0, 1, 1.0, 41, top_k, 1.0)
+    lg = logits[0].cpu().numpy().astype(np.float64)
+    assert np.array_equal(lg, np.round(lg))
+    cut = np.sort(lg)[::-1][top_k - 1]
+    assert np.count_nonzero(lg == cut) > 1            # the cut falls inside a run of ties
+    _check_filtered(words, logits, probs, tok, 1.0, top_k, 1.0)
+    _, l2, p2, t2 = _run_lm(W, h, V, d, 0, 1, 1.0, 41, top_k, 1.0)
+    assert torch.equal(p2, probs) and torch.equal(t2, tok)
+
+
 # ------------------------------------------------------------------ verify
 
 def _verify_gpu(p, q, draft, words, T, bonus):
@@ -423,12 +506,15 @@ def test_cycle_trajectory_tiny(schedule):
         cache.truncate(ost.t - 1 - ost.a)
 
 
-def test_cycle_full_headline_sampled():
+@pytest.mark.parametrize("top_k,top_p", [(0, 1.0), (50, 1.0), (50, 0.9)],
+                         ids=["full_softmax", "top_k50", "top_k50_p09"])
+def test_cycle_full_headline_sampled(top_k, top_p):
     """One saturated and one partial cycle of the headline workload (T = 1) on a
     seeded committed cache: features, last row, draft/target logits and
     probabilities within bf16 tolerance; the sampled draft, the verify outcome
-    and the state update bit-exact on the device's rows."""
-    s = synth.HEADLINE
+    and the state update bit-exact on the device's rows.  With the sampling
+    filters on, the draft and target rows keep exactly the oracle's sets."""
+    s = synth.HEADLINE.with_(top_k=top_k, top_p=top_p)
     ci = synth.cycle_inputs(s, device=DEV)
     model = device_model(ci)
     cyc = SpdCycle(model, 1.0)
@@ -460,8 +546,16 @@ def test_cycle_full_headline_sampled():
         assert rel_err(f64(cyc.h_last), out.h_last) < TOL_BF16
         assert rel_err(cyc.dlogits.cpu().numpy(), out.draft_logits) < TOL_BF16
         assert int(cyc.dtoken.item()) == out.drafted
+        dl = cyc.dlogits.cpu().numpy().astype(np.float64)
+        dref = O.filtered_softmax(dl, 1.0, top_k, top_p)
+        assert np.array_equal(np.flatnonzero(gq), np.flatnonzero(dref))
+        assert np.max(np.abs(gq - dref)) <= 2e-6 * dref.max()
         if a == s.n:
             assert rel_err(cyc.tlogits.cpu().numpy(), out.target_logits) < TOL_BF16
+            tl = cyc.tlogits.cpu().numpy().astype(np.float64)
+            tref = O.filtered_softmax(tl, 1.0, top_k, top_p)
+            assert np.array_equal(np.flatnonzero(gp), np.flatnonzero(tref))
+            assert np.max(np.abs(gp - tref)) <= 2e-6 * tref.max()
             assert (int(cyc.n_accept.item()), int(cyc.next_token.item())) == (out.n_accept,
                                                                              out.next_token)
         assert cyc.read_state() == (st.t, st.a, st.commits, st.cycles)
