@@ -158,45 +158,48 @@ def main():
     x = int(x_dev.item())
     torch.cuda.synchronize()
 
-    for c in range(args.warmup):
-        cyc.cycle(t, sched[c], words[c], q_row=qstand, x_ptr=x_dev.data_ptr())
-    torch.cuda.synchronize()
-
-    # timed region: K cycles; events bracket the draft-head call of every cycle
-    head_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    start.record()
     main = torch.cuda.current_stream()
-    for i in range(args.steps):
-        c = args.warmup + i
-        a = sched[c]
-        pos0, M = t - 1 - a, a + 1
-        sat = a == s.n
-        if sat:  # target head + verify on the side stream (as SpdCycle.cycle does)
-            cyc.ev_fork.record(main)
-            cyc.side.wait_event(cyc.ev_fork)
-            with torch.cuda.stream(cyc.side):
-                cyc.target_and_verify(t, words[c], q_row=qstand, x_ptr=x_dev.data_ptr(),
-                                      ws=cyc.ws_side)
-            cyc.ev_join.record(cyc.side)
-        cyc.features(pos0, M, a)
-        cyc.pdm(pos0, M)
-        head_ev[i][0].record()
-        cyc.draft(t, words[c])
-        head_ev[i][1].record()
-        if sat:
-            main.wait_event(cyc.ev_join)
-        cyc.rollback()
-    stop.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms = start.elapsed_time(stop)
-    ms_per_step = ms / args.steps
+
+    def run_cycles(cyc, steps):
+        """warmup + `steps` timed cycles; returns (ms per cycle, mean draft-head ms, wall s)"""
+        for c in range(args.warmup):
+            cyc.cycle(t, sched[c], words[c], q_row=qstand, x_ptr=x_dev.data_ptr())
+        torch.cuda.synchronize()
+        # timed region: K cycles; events bracket the draft-head call of every cycle
+        head_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(steps)]
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        start.record()
+        for i in range(steps):
+            c = args.warmup + i
+            a = sched[c]
+            pos0, M = t - 1 - a, a + 1
+            sat = a == s.n
+            if sat:  # target head + verify on the side stream (as SpdCycle.cycle does)
+                cyc.ev_fork.record(main)
+                cyc.side.wait_event(cyc.ev_fork)
+                with torch.cuda.stream(cyc.side):
+                    cyc.target_and_verify(t, words[c], q_row=qstand, x_ptr=x_dev.data_ptr(),
+                                          ws=cyc.ws_side, background=True)
+                cyc.ev_join.record(cyc.side)
+            cyc.features(pos0, M, a)
+            cyc.pdm(pos0, M)
+            head_ev[i][0].record()
+            cyc.draft(t, words[c])
+            head_ev[i][1].record()
+            if sat:
+                main.wait_event(cyc.ev_join)
+            cyc.rollback()
+        stop.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        head = float(np.mean([e0.elapsed_time(e1) for e0, e1 in head_ev]))
+        return start.elapsed_time(stop) / steps, head, wall
+
+    ms_per_step, head_ms, wall = run_cycles(cyc, args.steps)
     cycles_per_s = 1000.0 / ms_per_step
-    head_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in head_ev]))
 
     timed = sched[args.warmup:]
     cyc_bytes = [sum(algorithmic_bytes(s, a).values()) for a in timed]
@@ -270,6 +273,20 @@ def main():
     prefill = {"rows": P, "us": round(pf0.elapsed_time(pf1) / 3 * 1000.0, 1),
                "includes": "spd_fuse_features + spd_pdm_step over the prefix, large-M MFMA path"}
 
+    # the pages' sampling setting (T = 1, top-k = 50, top-p = 1.0) on both heads: the
+    # same cycles through a second model whose heads filter
+    model_k = SpdModel(L=s.L, n=s.n, anchors=s.anchors, d=s.d, Ls=s.Ls, Hq=s.Hq, Hkv=s.Hkv,
+                       hd=s.hd, dff=s.dff, V=s.V, dtype=s.dtype, weights=w, eps=s.eps,
+                       rope_theta=s.rope_theta, top_k=50, top_p=1.0)
+    cyc_k = SpdCycle(model_k, s.temperature, device=dev)
+    cyc_k.set_state(t, s.n, list(range(t)))
+    cyc_k.prefill(t - 1 - s.n)
+    ms_k, head_k, _ = run_cycles(cyc_k, max(args.steps // 2, 1))
+    top_k50 = {"top_k": 50, "top_p": 1.0, "cycles_per_s": round(1000.0 / ms_k, 2),
+               "ms_per_step": round(ms_k, 4), "draft_head_us": round(head_k * 1000.0, 2),
+               "draft_head_us_unfiltered": round(head_ms * 1000.0, 2)}
+    del cyc_k, model_k
+
     result = {
         "metric": "draft+verify cycles/s + achieved HBM GB/s, d=2560 n=8 vocab 151936, 1 GPU",
         "value": round(cycles_per_s, 2),
@@ -298,6 +315,7 @@ def main():
         "calls": calls,
         "prefill_fc": prefill_fc,
         "prefill": prefill,
+        "sampling_top_k50": top_k50,
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_cpu_baseline:

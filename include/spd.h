@@ -88,6 +88,9 @@ typedef struct spd_config {
                        /* 1..SPD_TOP_K_MAX (section 4 evaluation setting: 50)      */
   float top_p;         /* nucleus mass, used when top_k >= 1 and 0 < top_p < 1;   */
                        /* 0 and 1 = off (section 4 evaluation setting: 1.0)        */
+  int32_t head_workgroups; /* spd_lm_head's vocabulary GEMV (bf16, one row): 0 = one */
+                       /* workgroup per 32 rows; else at most this many, each looping */
+                       /* over row groups (a head streaming beside other work)     */
 } spd_config;
 
 /* One PDM decoder layer (DEVICE pointers, cfg.dtype).  Row-major [rows][cols]. */
@@ -244,7 +247,7 @@ int spd_rollback(spd_seq_state *st, int32_t n, const int32_t *drafted, const int
 
 const char *spd_status_string(int status);
 int spd_last_hip_error(void);
-/* Version of this interface: 2 (spd_config gained top_k and top_p). */
+/* Version of this interface: 2 (spd_config gained top_k, top_p and head_workgroups). */
 int spd_version(void);
 
 #ifdef __cplusplus

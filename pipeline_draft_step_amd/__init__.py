@@ -37,7 +37,8 @@ class spd_config(ctypes.Structure):
                                                ("rope_theta", ctypes.c_float),
                                                ("feature_schedule", ctypes.c_int32),
                                                ("top_k", ctypes.c_int32),
-                                               ("top_p", ctypes.c_float)]
+                                               ("top_p", ctypes.c_float),
+                                               ("head_workgroups", ctypes.c_int32)]
 
 
 class spd_layer_weights(ctypes.Structure):
@@ -129,9 +130,9 @@ def _i32_array(values):
 
 def make_config(*, L, n, m, d, Ls, Hq, Hkv, hd, dff, V, dtype, anchor_mode=0, norm_k0=0,
                 rms_eps=1e-6, rope_theta=1e6, feature_schedule=0, top_k=0,
-                top_p=1.0) -> spd_config:
+                top_p=1.0, head_workgroups=0) -> spd_config:
     return spd_config(L, n, m, d, Ls, Hq, Hkv, hd, dff, V, dtype, anchor_mode, norm_k0,
-                      rms_eps, rope_theta, feature_schedule, top_k, top_p)
+                      rms_eps, rope_theta, feature_schedule, top_k, top_p, head_workgroups)
 
 
 # ----------------------------------------------------------------- host helpers

@@ -608,6 +608,7 @@ __global__ __launch_bounds__(SMX_THREADS) void topk_sample_kernel(
   const int base = c * SMX_CHUNK;
   const int n = min(SMX_CHUNK, V - base);
   constexpr int PER = SMX_CHUNK / SMX_THREADS;
+  SPD_MARK(0);
   uint64_t key[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
@@ -615,6 +616,7 @@ __global__ __launch_bounds__(SMX_THREADS) void topk_sample_kernel(
     const float x = lr[j < V ? j : 0];
     key[e] = j < V ? topk_key(x, j) : 0ull;
   }
+  SPD_MARK(1);
   uint64_t th = 1ull;  // every real key is >= 1
   if (n > k)
     th = select_kth(
@@ -623,6 +625,7 @@ __global__ __launch_bounds__(SMX_THREADS) void topk_sample_kernel(
           for (int e = 0; e < PER; ++e) f(key[e]);
         },
         (unsigned)k, s);
+  SPD_MARK(2);
   if (t == 0) s_cnt = 0u;
   __syncthreads();
 #pragma unroll
@@ -635,7 +638,9 @@ __global__ __launch_bounds__(SMX_THREADS) void topk_sample_kernel(
       pr[base + t + SMX_THREADS * e] = 0.f;
     }
   }
+  SPD_MARK(3);
   if (!arrive_last(counters + r, (unsigned)nchunks)) return;
+  SPD_MARK(4);
 
   // ---- last block: the k largest of all candidates
   const int ncand = (nchunks - 1) * cs + min(k, V - (nchunks - 1) * SMX_CHUNK);
@@ -655,6 +660,7 @@ __global__ __launch_bounds__(SMX_THREADS) void topk_sample_kernel(
   };
   uint64_t th2 = 1ull;
   if (ncand > kk) th2 = select_kth(visit_cand, (unsigned)kk, s);
+  SPD_MARK(5);
   if (t == 0) s_cnt = 0u;
   __syncthreads();
   visit_cand([&](uint64_t key2) {
@@ -710,6 +716,7 @@ __global__ __launch_bounds__(SMX_THREADS) void topk_sample_kernel(
     s_idx[s_irank[t]] = ix;
   }
   __syncthreads();
+  SPD_MARK(6);
   // inverse CDF in ascending index order
   const uint64_t w = member ? s_w[t] : 0ull;
   const uint64_t winc = wave_scan_u64(w);
@@ -725,6 +732,7 @@ __global__ __launch_bounds__(SMX_THREADS) void topk_sample_kernel(
   } else if (member && lo <= tau && tau < lo + w) {
     token[r] = s_idx[t];
   }
+  SPD_MARK(7);
 }
 
 struct LmPlan {
@@ -776,15 +784,16 @@ static int lm_impl(const spd_config* c, const void* w_lm, const float* h, int ro
   const HeadFinish f{ctr + CTR_HEAD, reinterpret_cast<BlockStat*>(w + p.off_gstat), token, T > 0.f ? 0 : 1};
   int rc;
   if (p.dot) {
+    const int nblk = c->head_workgroups > 0 ? std::min(p.nstat, c->head_workgroups) : p.nstat;
     switch (p.J) {
-      case 1: launch_dot<1>(p.nstat, st, w_lm, h, c->V, inv_t, logits, stat); break;
-      case 2: launch_dot<2>(p.nstat, st, w_lm, h, c->V, inv_t, logits, stat); break;
-      case 3: launch_dot<3>(p.nstat, st, w_lm, h, c->V, inv_t, logits, stat); break;
-      case 4: launch_dot<4>(p.nstat, st, w_lm, h, c->V, inv_t, logits, stat); break;
-      case 5: launch_dot<5>(p.nstat, st, w_lm, h, c->V, inv_t, logits, stat); break;
-      case 6: launch_dot<6>(p.nstat, st, w_lm, h, c->V, inv_t, logits, stat); break;
-      case 7: launch_dot<7>(p.nstat, st, w_lm, h, c->V, inv_t, logits, stat); break;
-      default: launch_dot<8>(p.nstat, st, w_lm, h, c->V, inv_t, logits, stat); break;
+      case 1: launch_dot<1>(nblk, st, w_lm, h, c->V, inv_t, logits, stat); break;
+      case 2: launch_dot<2>(nblk, st, w_lm, h, c->V, inv_t, logits, stat); break;
+      case 3: launch_dot<3>(nblk, st, w_lm, h, c->V, inv_t, logits, stat); break;
+      case 4: launch_dot<4>(nblk, st, w_lm, h, c->V, inv_t, logits, stat); break;
+      case 5: launch_dot<5>(nblk, st, w_lm, h, c->V, inv_t, logits, stat); break;
+      case 6: launch_dot<6>(nblk, st, w_lm, h, c->V, inv_t, logits, stat); break;
+      case 7: launch_dot<7>(nblk, st, w_lm, h, c->V, inv_t, logits, stat); break;
+      default: launch_dot<8>(nblk, st, w_lm, h, c->V, inv_t, logits, stat); break;
     }
     rc = check_launch();
     if (rc) return rc;

@@ -36,6 +36,7 @@ inline int check_config(const spd_config* c) {
     return SPD_E_INVALID;
   if (c->top_k < 0 || c->top_k > SPD_TOP_K_MAX || !(c->top_p >= 0.f && c->top_p <= 1.f))
     return SPD_E_INVALID;
+  if (c->head_workgroups < 0) return SPD_E_INVALID;
   return SPD_OK;
 }
 

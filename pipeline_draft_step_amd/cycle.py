@@ -14,8 +14,8 @@ from dataclasses import dataclass
 import torch
 
 from . import (SPD_BF16, SPD_CALL_FUSE, SPD_CALL_LM_HEAD, SPD_CALL_PDM, SPD_CALL_VERIFY,
-               layer_weights, make_config, spd_fuse_features, spd_lm_head, spd_pdm_step,
-               spd_rollback, spd_slot_table, spd_verify, spd_workspace_size)
+               layer_weights, make_config, spd_config, spd_fuse_features, spd_lm_head,
+               spd_pdm_step, spd_rollback, spd_slot_table, spd_verify, spd_workspace_size)
 
 PREFILL_BLOCK = 256   # rows per PDM prefill call
 FEATURE_BLOCK = 2048  # rows per prefill feature call (one large-M FC GEMM)
@@ -95,6 +95,10 @@ class SpdCycle:
                                        spd_workspace_size(SPD_CALL_VERIFY, c, 1, 1)),
                                    dtype=torch.uint8, device=device)
         self.side = torch.cuda.Stream(device=device)
+        # the side stream's head streams beside the latency-bound feature/PDM chain:
+        # one workgroup per compute unit leaves the chain's kernels room to run
+        self.cfg_bg = spd_config.from_buffer_copy(c)
+        self.cfg_bg.head_workgroups = torch.cuda.get_device_properties(device).multi_processor_count
         self.ev_fork = torch.cuda.Event()
         self.ev_join = torch.cuda.Event()
 
@@ -130,16 +134,19 @@ class SpdCycle:
         spd_lm_head(m.cfg, m.w.w_dlm, self.h_last, 1, self.T, w, self.dlogits, probs, self.dtoken,
                     self.ws)
 
-    def target_and_verify(self, t, words_block, q_row=None, x_ptr=None, ws=None):
-        """Target head on the exiting token's state and streaming verify of its successor."""
+    def target_and_verify(self, t, words_block, q_row=None, x_ptr=None, ws=None,
+                          background=False):
+        """Target head on the exiting token's state and streaming verify of its successor.
+        background: the head runs beside the draft chain (one workgroup per CU)."""
         m = self.m
+        cfg = self.cfg_bg if background else m.cfg
         ws = self.ws if ws is None else ws
         n, V = m.cfg.n, m.cfg.V
         exiting = t - n
         h = m.w.h_final[exiting]
         probs = self.p if self.T > 0 else None
         w = None if words_block is None else words_block.data_ptr() + 2 * 8
-        spd_lm_head(m.cfg, m.w.w_tlm, h, 1, self.T, w, self.tlogits, probs, self.ttoken, ws)
+        spd_lm_head(cfg, m.w.w_tlm, h, 1, self.T, w, self.tlogits, probs, self.ttoken, ws)
         cand = exiting + 1
         q = q_row if q_row is not None else self.ring[cand % n]
         draft = x_ptr if x_ptr is not None else self.tokens.data_ptr() + 4 * cand
@@ -165,7 +172,8 @@ class SpdCycle:
             self.ev_fork.record(main)
             self.side.wait_event(self.ev_fork)
             with torch.cuda.stream(self.side):
-                self.target_and_verify(t, words_block, q_row, x_ptr, ws=self.ws_side)
+                self.target_and_verify(t, words_block, q_row, x_ptr, ws=self.ws_side,
+                                       background=True)
             self.ev_join.record(self.side)
         self.features(pos0, M, a)
         self.pdm(pos0, M)

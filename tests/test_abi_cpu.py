@@ -71,6 +71,12 @@ def test_config_rejects_bad_sampling_filters(top_k, top_p):
         spd.spd_slot_table(_cfg(s, top_k=top_k, top_p=top_p), s.anchors)
 
 
+def test_config_rejects_negative_head_workgroups():
+    s = synth.TINY
+    with pytest.raises(spd.SpdError):
+        spd.spd_slot_table(_cfg(s, head_workgroups=-1), s.anchors)
+
+
 def test_lm_head_workspace_holds_top_k_candidates():
     s = synth.HEADLINE
     base = spd.spd_workspace_size(spd.SPD_CALL_LM_HEAD, _cfg(s), 1)

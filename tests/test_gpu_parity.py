@@ -277,6 +277,22 @@ def test_lm_head_is_deterministic():
     assert torch.equal(l2, logits) and torch.equal(p2, probs) and torch.equal(t2, tok)
 
 
+@pytest.mark.parametrize("workgroups", [1, 7, 256, 5000])
+def test_lm_head_workgroup_cap_is_bitwise_neutral(workgroups):
+    """A capped vocabulary GEMV (each workgroup loops over row groups) gives the
+    same logits, probabilities and token, bit for bit."""
+    say("lm_head workgroups", workgroups)
+    W, h, words, logits, probs, tok, cfg, ws, wt = _lm_case(151936, 2560, 1, 3.0 / np.sqrt(2560),
+                                                            1, 1.0, 13)
+    cfg.head_workgroups = workgroups
+    l2 = torch.empty_like(logits)
+    p2 = torch.empty_like(probs)
+    t2 = torch.zeros_like(tok)
+    spd.spd_lm_head(cfg, W, h, 1, 1.0, wt, l2, p2, t2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(l2, logits) and torch.equal(p2, probs) and torch.equal(t2, tok)
+
+
 # ------------------------------------------------------------------ top-k / top-p sampling
 
 def _run_lm(W, h, V, d, dtype, rows, T, seed, top_k, top_p):
