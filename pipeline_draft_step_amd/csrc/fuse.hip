@@ -6,8 +6,9 @@
 //
 // Two launches.  The gather kernel reads each row's eligible anchor states from
 // the anchor store (empty slots are zeros; the k = 0 rows read slot 0 only,
-// without gamma), writes gamma * x as the FC's input and, in the last block of
-// each row, the row's 1/rms over its filled slots.  Because FC is linear,
+// without gamma), writes gamma * x as the FC's input and the row's 1/rms over its
+// filled slots (decode-sized calls split a row over several blocks and finish
+// the sum in the last one; prefill-sized calls take one block per row).  Because FC is linear,
 // W (gamma * x / rms) = (W (gamma * x)) / rms, so the row scale is applied to
 // the product tile.  Decode-sized calls stream W_fc through the skinny GEMM,
 // which takes the input pre-split into bf16 hi/lo parts (fp32-accurate
@@ -48,7 +49,7 @@ struct GatherArgs {
 
 // Block (column block cb, row r); each thread owns 8 consecutive columns, which
 // never straddle two anchors (d % 64 == 0).
-template <typename WT, bool HI_ONLY>
+template <typename WT>
 __global__ __launch_bounds__(256) void feature_gather_kernel(GatherArgs<WT> f) {
   __shared__ int8_t s_tab[TABN];
   __shared__ float s_red[4];
@@ -94,13 +95,8 @@ __global__ __launch_bounds__(256) void feature_gather_kernel(GatherArgs<WT> f) {
   if (inb) {
     const float4 lo4 = make_float4(x[0] * gm[0], x[1] * gm[1], x[2] * gm[2], x[3] * gm[3]);
     const float4 hi4 = make_float4(x[4] * gm[4], x[5] * gm[5], x[6] * gm[6], x[7] * gm[7]);
-    if constexpr (HI_ONLY) {
-      f.xo.put4_hi(r, col, lo4);
-      f.xo.put4_hi(r, col + 4, hi4);
-    } else {
-      f.xo.put4(r, col, lo4);
-      f.xo.put4(r, col + 4, hi4);
-    }
+    f.xo.put4(r, col, lo4);
+    f.xo.put4(r, col + 4, hi4);
   }
   SPD_MARK(1);
   sq = wave_sum(sq);
@@ -121,6 +117,80 @@ __global__ __launch_bounds__(256) void feature_gather_kernel(GatherArgs<WT> f) {
       for (int j = 0; j < SPD_MAX_ANCHORS; ++j) filled += (j < f.m && s_tab[k * f.m + j] >= 0) ? 1 : 0;
       f.inv[r] = plain ? 1.f : (filled > 0 ? 1.0f / sqrtf(t / (float)(filled * f.d) + f.eps) : 0.f);
     }
+  }
+}
+
+// Large-M form of the gather (bf16-rounded input only): one block per row, so the
+// row's sum of squares is a block reduction and no partial sums or arrival
+// counters are needed.  Columns are taken in batches of GR_BATCH x 2048 whose
+// loads are all issued before any of them is used.
+constexpr int GR_BATCH = 4;
+
+template <typename WT>
+__global__ __launch_bounds__(256) void feature_gather_rows_kernel(GatherArgs<WT> f) {
+  __shared__ int8_t s_tab[TABN];
+  __shared__ float s_red[4];
+  if (threadIdx.x == 0) {
+    int* dst = reinterpret_cast<int*>(s_tab);
+    const int* src = reinterpret_cast<const int*>(f.tab.v);
+#pragma unroll
+    for (int i = 0; i < TABN / 4; ++i) dst[i] = src[i];
+  }
+  __syncthreads();
+  const int r = blockIdx.x;
+  const int k = f.depth(r);
+  const bool plain = (k == 0) && !f.norm_k0;
+  const int K = f.m * f.d;
+  const size_t row = (size_t)(f.pos0 + r) * f.S_store;
+  float sq = 0.f;
+  for (int base = 0; base < K; base += GR_BATCH * GATHER_COLS) {
+    float4 xv[GR_BATCH][2], gv[GR_BATCH][2];
+    bool use[GR_BATCH];
+#pragma unroll
+    for (int b = 0; b < GR_BATCH; ++b) {
+      const int col = base + b * GATHER_COLS + 8 * threadIdx.x;
+      const bool inb = col < K;
+      const int a = inb ? col / f.d : 0;
+      const int c = inb ? col - a * f.d : 0;
+      int slot = s_tab[k * f.m + a];
+      if (plain && a != 0) slot = -1;
+      use[b] = inb && slot >= 0 && slot < f.S_store;
+      const WT* src = f.store + (row + (use[b] ? slot : 0)) * f.d + c;
+      const WT* gp = f.gamma + (inb ? col : 0);
+      xv[b][0] = ldg4(src);
+      xv[b][1] = ldg4(src + 4);
+      gv[b][0] = ldg4(gp);
+      gv[b][1] = ldg4(gp + 4);
+    }
+#pragma unroll
+    for (int b = 0; b < GR_BATCH; ++b) {
+      const int col = base + b * GATHER_COLS + 8 * threadIdx.x;
+      const float x[8] = {xv[b][0].x, xv[b][0].y, xv[b][0].z, xv[b][0].w,
+                          xv[b][1].x, xv[b][1].y, xv[b][1].z, xv[b][1].w};
+      const float g[8] = {gv[b][0].x, gv[b][0].y, gv[b][0].z, gv[b][0].w,
+                          gv[b][1].x, gv[b][1].y, gv[b][1].z, gv[b][1].w};
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float xe = use[b] ? x[e] : 0.f;
+        sq += xe * xe;
+        y[e] = xe * (plain ? 1.f : g[e]);
+      }
+      if (col < K) {
+        f.xo.put4_hi(r, col, make_float4(y[0], y[1], y[2], y[3]));
+        f.xo.put4_hi(r, col + 4, make_float4(y[4], y[5], y[6], y[7]));
+      }
+    }
+  }
+  sq = wave_sum(sq);
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = sq;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float t = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
+    int filled = 0;
+#pragma unroll
+    for (int j = 0; j < SPD_MAX_ANCHORS; ++j) filled += (j < f.m && s_tab[k * f.m + j] >= 0) ? 1 : 0;
+    f.inv[r] = plain ? 1.f : (filled > 0 ? 1.0f / sqrtf(t / (float)(filled * f.d) + f.eps) : 0.f);
   }
 }
 
@@ -212,7 +282,7 @@ static int fuse_impl(const spd_config* cfg, const void* hstore, int64_t T_cap, i
   ga.depth = RowDepth{M, a, n};
   if (p.big.use) {
     if constexpr (sizeof(WT) == 2) {
-      hipLaunchKernelGGL((feature_gather_kernel<WT, true>), dim3(p.ncb, M), dim3(256), 0, st, ga);
+      hipLaunchKernelGGL((feature_gather_rows_kernel<WT>), dim3(M), dim3(256), 0, st, ga);
       int rc = check_launch();
       if (rc) return rc;
       // the gather's row counters are back at zero when it ends, so the GEMM
@@ -223,7 +293,7 @@ static int fuse_impl(const spd_config* cfg, const void* hstore, int64_t T_cap, i
       return check_launch();
     }
   }
-  hipLaunchKernelGGL((feature_gather_kernel<WT, false>), dim3(p.ncb, M), dim3(256), 0, st, ga);
+  hipLaunchKernelGGL((feature_gather_kernel<WT>), dim3(p.ncb, M), dim3(256), 0, st, ga);
   int rc = check_launch();
   if (rc) return rc;
 
