@@ -229,16 +229,19 @@ def _split_qkv(qkv, c: PdmConfig):
     return q, k, v
 
 
-def _attend(q, k_all, v_all, q_pos, k_pos, c: PdmConfig):
-    """Causal GQA softmax attention: query head h reads key/value head h // (Hq/Hkv)."""
+def _attend(q, k_all, v_all, q_pos, k_pos, c: PdmConfig, allowed=None):
+    """GQA softmax attention: query head h reads key/value head h // (Hq/Hkv).
+    Causal by position unless `allowed` [queries][keys] gives the mask."""
     group = c.Hq // c.Hkv
     out = np.zeros((q.shape[0], c.Hq, c.hd))
     scale = 1.0 / math.sqrt(c.hd)
+    if allowed is None:
+        allowed = np.asarray(k_pos)[None, :] <= np.asarray(q_pos)[:, None]
     for h in range(c.Hq):
         kh = k_all[:, h // group, :]
         vh = v_all[:, h // group, :]
         s = (q[:, h, :] @ kh.T) * scale
-        s = np.where(np.asarray(k_pos)[None, :] <= np.asarray(q_pos)[:, None], s, -np.inf)
+        s = np.where(allowed, s, -np.inf)
         s = s - s.max(axis=1, keepdims=True)
         p = np.exp(s)
         p = p / p.sum(axis=1, keepdims=True)
@@ -246,15 +249,17 @@ def _attend(q, k_all, v_all, q_pos, k_pos, c: PdmConfig):
     return out
 
 
-def decoder_layer(h, positions, lw, c: PdmConfig, kv_prefix=None):
+def decoder_layer(h, positions, lw, c: PdmConfig, kv_prefix=None, allowed=None):
     """One pre-norm decoder layer over rows h [T][d] at `positions`.
 
     lw: dict of float64 arrays attn_norm [d], wqkv [(Hq+2Hkv)*hd][d] (q heads,
     then k heads, then v heads), q_norm [hd], k_norm [hd], wo [d][Hq*hd],
     mlp_norm [d], w_gate_up [2*dff][d] (gate rows, then up rows), w_down [d][dff].
     kv_prefix: optional (K [P][Hkv][hd], V [P][Hkv][hd], positions [P]) of earlier
-    rows (already normed and rotated).  Returns (h_out, K_rows, V_rows) where
-    K_rows/V_rows are this call's rows' keys/values as they enter attention.
+    rows (already normed and rotated).  allowed: optional attention mask [rows]
+    [prefix + rows] (default: causal by position).  Returns (h_out, K_rows,
+    V_rows) where K_rows/V_rows are this call's rows' keys/values as they enter
+    attention.
     """
     n1 = rms_norm(h, lw["attn_norm"], c.eps)
     q, k, v = _split_qkv(n1 @ lw["wqkv"].T, c)
@@ -267,7 +272,7 @@ def decoder_layer(h, positions, lw, c: PdmConfig, kv_prefix=None):
         k_pos = list(pp) + list(positions)
     else:
         k_all, v_all, k_pos = k, v, list(positions)
-    att = _attend(q, k_all, v_all, positions, k_pos, c)
+    att = _attend(q, k_all, v_all, positions, k_pos, c, allowed)
     h = h + att.reshape(h.shape[0], -1) @ lw["wo"].T
     n2 = rms_norm(h, lw["mlp_norm"], c.eps)
     gu = n2 @ lw["w_gate_up"].T
@@ -319,6 +324,97 @@ def pdm_step(g_rows, pos0, cache: PdmCache, layers, final_norm, c: PdmConfig):
         cache.k[li] = np.concatenate([kp, k], axis=0)
         cache.v[li] = np.concatenate([vp, v], axis=0)
     return rms_norm(h[-1], final_norm, c.eps), h
+
+
+# --------------------------------------------------------------------------
+# Draft trees ([SPD] 4, draft-tree paragraph, and Appendix B: width-W trees raise
+# acceptance; [REV] draft-tree paragraphs).  The pages measure trees only in
+# theory and leave branched KV caches and tree attention masks open; the
+# readings below are this oracle's and are listed in the design doc.
+# --------------------------------------------------------------------------
+
+def tree_levels(anc):
+    """Level of every node of a draft tree given by ancestor masks.
+
+    Rows are the nodes in topological order.  Bit j of anc[i] is set iff node j
+    is node i or one of its ancestors; node 0 is the root (anc[0] = 1).  Every
+    other node's parent p is its highest ancestor below it, and
+    anc[i] = anc[p] | 2^i.  Returns the number of proper ancestors of each node.
+    """
+    anc = [int(x) for x in anc]
+    if not anc or anc[0] != 1:
+        raise ValueError("node 0 must be the root, with mask 1")
+    for i in range(1, len(anc)):
+        a = anc[i]
+        if not (a >> i) & 1 or a >> (i + 1):
+            raise ValueError("a node's mask holds itself and only earlier nodes")
+        rest = a & ~(1 << i)
+        if rest == 0 or anc[rest.bit_length() - 1] != rest:
+            raise ValueError("a node's mask is its parent's mask plus itself")
+    return [bin(x).count("1") - 1 for x in anc]
+
+
+def tree_rows(anc, a: int, n: int, pos0: int):
+    """Anchor-store rows, pipeline depths and positions of a draft tree's nodes.
+
+    Node i reads store row pos0 + i (the target states of its own branch) and
+    sits at position pos0 + level(i).  The root (level 0) is the newest fully
+    processed token (depth n); level l = 1..a holds in-flight tokens at depth
+    a - l, the tree form of [SPD] 3.1 Eq. (2) and 3.3 (pre-step depths).
+    """
+    lv = tree_levels(anc)
+    if not 1 <= a <= n or max(lv) > a:
+        raise ValueError("need 1 <= a <= n and no level deeper than a")
+    rows = [pos0 + i for i in range(len(anc))]
+    depth = [n if l == 0 else a - l for l in lv]
+    pos = [pos0 + l for l in lv]
+    return rows, depth, pos
+
+
+def pdm_step_tree(g_rows, pos0, cache: PdmCache, layers, final_norm, c: PdmConfig, anc):
+    """Tree-masked incremental PDM.  Node i sits at position pos0 + level(i) and
+    attends to the cached positions < pos0 and to the nodes on its own root
+    path (anc[i]); its key/value entries occupy cache slot pos0 + i (a branched
+    cache: siblings share a position but not a slot).  Afterwards the cache holds
+    slots 0..pos0+M-1.  Returns (final-normed rows [M][d], un-normed rows)."""
+    h = np.asarray(g_rows, dtype=np.float64)
+    M = h.shape[0]
+    lv = tree_levels(anc)
+    if len(lv) != M:
+        raise ValueError("one mask per row")
+    positions = [pos0 + l for l in lv]
+    allowed = np.array([[True] * pos0 + [bool((int(anc[i]) >> j) & 1) for j in range(M)]
+                        for i in range(M)])
+    for li, lw in enumerate(layers):
+        kp, vp = cache.k[li][:pos0], cache.v[li][:pos0]
+        if kp.shape[0] != pos0:
+            raise ValueError("cache does not cover the positions before pos0")
+        h, k, v = decoder_layer(h, positions, lw, c, (kp, vp, range(pos0)), allowed=allowed)
+        cache.k[li] = np.concatenate([kp, k], axis=0)
+        cache.v[li] = np.concatenate([vp, v], axis=0)
+    return rms_norm(h, final_norm, c.eps), h
+
+
+def top_k_list(logits, k):
+    """The k largest logits' indices in descending order (equal values by
+    ascending index, NaN last): the W children a greedy draft tree gives a
+    node (EAGLE-style top-k expansion, [SPD] 4 draft-tree paragraph)."""
+    x = np.asarray(logits, dtype=np.float64)
+    nan = np.isnan(x)
+    order = np.lexsort((np.arange(len(x)), -np.where(nan, 0.0, x), nan))
+    return [int(i) for i in order[:max(int(k), 1)]]
+
+
+def verify_siblings(p_logits, cand):
+    """Greedy verification of sibling candidates for one position ([SPD] 3.4 at
+    T = 0 applied to a tree level): the sibling equal to the target argmax is
+    accepted.  Returns (index of the accepted sibling, -1) or, when none
+    matches, (-1, the argmax as the corrected token)."""
+    best = argmax_first(p_logits)
+    for i, x in enumerate(cand):
+        if int(x) == best:
+            return i, -1
+    return -1, best
 
 
 # --------------------------------------------------------------------------

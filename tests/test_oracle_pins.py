@@ -335,6 +335,105 @@ def test_incremental_pdm_equals_full_recompute():
     assert not np.allclose(last2, last)
 
 
+# ------------------------------------------------------------------ draft trees
+
+def _tree_masks(parents):
+    """Ancestor masks from a parent list (parents[0] = -1)."""
+    anc = []
+    for i, p in enumerate(parents):
+        anc.append((1 << i) | (anc[p] if p >= 0 else 0))
+    return anc
+
+
+def test_tree_levels_and_rejects_bad_masks():
+    anc = _tree_masks([-1, 0, 0, 1, 2, 2, 3])
+    assert anc == [1, 3, 5, 11, 21, 37, 75]
+    assert O.tree_levels(anc) == [0, 1, 1, 2, 2, 2, 3]
+    chain = _tree_masks([-1, 0, 1, 2])
+    assert O.tree_levels(chain) == [0, 1, 2, 3]
+    for bad in ([3], [1, 2], [1, 3, 7 | 16], [1, 3, 6], [1, 3, 5, 14]):
+        with pytest.raises(ValueError):
+            O.tree_levels(bad)
+
+
+def test_tree_rows_of_a_chain_are_the_cycle_layout():
+    for n, a in ((8, 8), (8, 3), (4, 1)):
+        t = 40
+        pos0, pos, dep = O.cycle_rows(t, a, n)
+        rows, depth, tpos = O.tree_rows(_tree_masks([-1] + list(range(a))), a, n, pos0)
+        assert rows == pos and tpos == pos and depth == dep
+
+
+def test_tree_rows_branches_share_positions():
+    anc = _tree_masks([-1, 0, 0, 0, 0, 1, 1, 2])
+    rows, depth, pos = O.tree_rows(anc, 3, 8, 100)
+    assert rows == list(range(100, 108))
+    assert pos == [100, 101, 101, 101, 101, 102, 102, 102]
+    assert depth == [8, 2, 2, 2, 2, 1, 1, 1]
+
+
+def test_tree_pdm_rows_equal_the_full_forward_of_their_root_paths():
+    """Every node's final-normed row equals the definitional causal forward over
+    the committed prefix followed by the node's own root path; siblings do not
+    see each other."""
+    rng = np.random.default_rng(25)
+    c = O.PdmConfig(d=32, Hq=4, Hkv=2, hd=8, dff=64)
+    layers, fnorm = _random_pdm(rng, c, 2)
+    P = 9
+    prefix = rng.standard_normal((P, 32))
+    cache = O.PdmCache(2, c)
+    O.pdm_step(prefix, 0, cache, layers, fnorm, c)
+    parents = [-1, 0, 0, 0, 1, 1, 2, 4]
+    anc = _tree_masks(parents)
+    G = rng.standard_normal((len(parents), 32))
+    rows, _ = O.pdm_step_tree(G, P, cache, layers, fnorm, c, anc)
+    assert cache.length() == P + len(parents)
+    for i in range(len(parents)):
+        path = [j for j in range(len(parents)) if (anc[i] >> j) & 1]
+        ref = O.pdm_forward(np.concatenate([prefix, G[path]]), layers, fnorm, c)
+        assert np.allclose(rows[i], ref, atol=1e-12), i
+
+
+def test_tree_pdm_of_a_chain_is_the_causal_step():
+    rng = np.random.default_rng(26)
+    c = O.PdmConfig(d=32, Hq=4, Hkv=4, hd=8, dff=64)
+    layers, fnorm = _random_pdm(rng, c, 1)
+    prefix = rng.standard_normal((6, 32))
+    G = rng.standard_normal((5, 32))
+    c1, c2 = O.PdmCache(1, c), O.PdmCache(1, c)
+    O.pdm_step(prefix, 0, c1, layers, fnorm, c)
+    O.pdm_step(prefix, 0, c2, layers, fnorm, c)
+    last, _ = O.pdm_step(G, 6, c1, layers, fnorm, c)
+    rows, _ = O.pdm_step_tree(G, 6, c2, layers, fnorm, c, _tree_masks([-1, 0, 1, 2, 3]))
+    assert np.allclose(rows[-1], last, atol=1e-13)
+    assert np.allclose(c1.k[0], c2.k[0], atol=1e-13) and np.allclose(c1.v[0], c2.v[0], atol=1e-13)
+
+
+def test_top_k_list_order():
+    x = np.random.default_rng(27).standard_normal(3000) * 3
+    for k in (1, 4, 50):
+        assert O.top_k_list(x, k) == torch.topk(torch.tensor(x), k, sorted=True).indices.tolist()
+    ties = np.array([2.0, 5.0, 5.0, np.nan, 1.0, 5.0, 2.0])
+    assert O.top_k_list(ties, 5) == [1, 2, 5, 0, 6]
+    assert O.top_k_list(ties, 7) == [1, 2, 5, 0, 6, 4, 3]
+    assert O.top_k_list(ties, 1) == [O.argmax_first(ties)]
+
+
+def test_verify_siblings_greedy():
+    p = np.array([0.1, 3.0, 2.0, 3.0, -1.0])
+    assert O.verify_siblings(p, [2, 1, 3]) == (1, -1)     # argmax is index 1 (first of the ties)
+    assert O.verify_siblings(p, [3, 2]) == (-1, 1)        # an equal value is not the argmax
+    assert O.verify_siblings(p, [1]) == (0, -1)
+    rng = np.random.default_rng(28)
+    for _ in range(50):        # one sibling: the streaming greedy verify
+        row = rng.standard_normal(64)
+        x = int(rng.integers(0, 64)) if rng.random() < 0.5 else O.argmax_first(row)
+        na, nt = O.verify([row], None, [x], np.zeros((2, 2), np.uint64), temperature=0,
+                          bonus=False)
+        acc, nxt = O.verify_siblings(row, [x])
+        assert (acc == 0) == (na == 1) and (nxt if acc < 0 else -1) == nt
+
+
 # ------------------------------------------------------------------ P8
 
 def test_argmax_first_and_nan():
