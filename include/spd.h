@@ -67,6 +67,7 @@ enum { SPD_CALL_FUSE = 0, SPD_CALL_PDM = 1, SPD_CALL_LM_HEAD = 2, SPD_CALL_VERIF
 #define SPD_MAX_ANCHORS 8
 #define SPD_MAX_STAGES 32
 #define SPD_TOP_K_MAX 256
+#define SPD_TREE_MAX_NODES 64
 
 /* Sizes of the target, the PDM and the heads (section 3.1-3.2, section 4 setup). */
 typedef struct spd_config {
@@ -190,7 +191,10 @@ int spd_pdm_step(const spd_config *cfg, const spd_layer_weights *layers, const v
 /* LM head and next-token choice (section 3.1 Eq. (1); section 3.4 target head).
  * logits[r] = W_lm . h[r] for r < rows (rows <= 16).
  * temperature == 0: token[r] = lowest index of the maximum logit (NaN never wins);
- *   probs may be NULL and words is unused.
+ *   probs may be NULL and words is unused.  With cfg.top_k >= 2 (the children of a
+ *   greedy draft-tree node) token is [rows][top_k] instead: the indices of the top_k
+ *   largest logits in descending order (equal logits by ascending index, NaN last),
+ *   -1 past the vocabulary.
  * temperature > 0: probs[r] = softmax(logits[r] / T) (float32) and
  *   token[r] = inverse-CDF draw from the integer weights w_j = floor(probs_j * 2^52):
  *   u = words[r] >> 32, tau = floor(u * sum(w) / 2^32), token = smallest j whose
@@ -244,6 +248,49 @@ int spd_verify(int32_t B, int32_t gamma, int32_t V, float temperature, int32_t b
  */
 int spd_rollback(spd_seq_state *st, int32_t n, const int32_t *drafted, const int32_t *n_accept,
                  const int32_t *next_token, int32_t *tokens, int64_t T_cap, void *stream);
+
+/* ---------------------------------------------------------------- draft trees */
+
+/* Width-W draft trees (section 4, draft-tree paragraph, and Appendix B: trees raise
+ * acceptance; the pages measure them in theory only and leave branched key/value
+ * caches and tree attention masks open).  A tree's M <= SPD_TREE_MAX_NODES nodes are
+ * rows in topological order; anc DEVICE uint64 [M]: bit j of anc[i] is set iff node
+ * j is node i or one of its ancestors.  Node 0 is the root, the newest fully
+ * processed token (anc[0] = 1); every other node's mask is its parent's plus its own
+ * bit.  level(i) = popcount(anc[i]) - 1.  Node i reads anchor-store row pos0 + i
+ * (its own branch's target states), sits at position pos0 + level(i) and keeps its
+ * keys/values in cache slot pos0 + i.  The masks are read on the device and not
+ * validated; a malformed mask changes results but no access leaves the buffers. */
+
+/* spd_fuse_features over a tree: node i has depth n at level 0 and a - level(i)
+ * below it (the in-flight levels 1..a); otherwise as spd_fuse_features.
+ * Requires 1 <= a <= n, M <= SPD_TREE_MAX_NODES; anc 8-byte aligned. */
+int spd_fuse_features_tree(const spd_config *cfg, const void *hstore, int64_t T_cap, int32_t S,
+                           const int32_t *slot_tab, int32_t pos0, int32_t M, int32_t a,
+                           const uint64_t *anc, const void *norm_w, const void *fc_w, float *g,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/* spd_pdm_step over a tree: node i attends to the cached positions < pos0 and to the
+ * nodes on its own root path, with RoPE at position pos0 + level(i); its keys/values
+ * go to slot pos0 + i.  h_out DEVICE float [n_out][d] receives the final-normed rows
+ * M - n_out .. M - 1 (the deepest level's nodes when they come last), 1 <= n_out <= M.
+ * Workspace as spd_pdm_step. */
+int spd_pdm_step_tree(const spd_config *cfg, const spd_layer_weights *layers,
+                      const void *final_norm, void *k_cache, void *v_cache, int64_t T_cap,
+                      const float *g, int32_t pos0, int32_t M, const uint64_t *anc, int32_t n_out,
+                      float *h_out, void *ws, size_t ws_bytes, void *stream);
+
+/* Greedy verification of sibling candidates (section 3.4 at T = 0, applied to a tree
+ * level whose nodes share one parent).  For each sequence b < B: best = argmax of the
+ * target logits p[b] (lowest index on ties); accepted[b] = the first i < W with
+ * cand[b][i] == best, or -1; next_token[b] = best when none is accepted, else -1.
+ * p DEVICE float [B][V]; cand DEVICE int32 [B][W]; accepted, next_token DEVICE int32
+ * [B].  ws >= spd_workspace_size(SPD_CALL_VERIFY, cfg with this V, B, 0, 0).
+ * The W candidates of a greedy tree node come from spd_lm_head at T = 0 with
+ * cfg.top_k = W. */
+int spd_verify_siblings(int32_t B, int32_t W, int32_t V, const float *p, const int32_t *cand,
+                        int32_t *accepted, int32_t *next_token, void *ws, size_t ws_bytes,
+                        void *stream);
 
 const char *spd_status_string(int status);
 int spd_last_hip_error(void);

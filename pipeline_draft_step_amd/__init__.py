@@ -22,11 +22,13 @@ SPD_WS_COUNTER_BYTES = 65536
 SPD_MAX_ANCHORS = 8
 SPD_MAX_STAGES = 32
 SPD_TOP_K_MAX = 256
+SPD_TREE_MAX_NODES = 64
 
 EXPORTED = (
     "spd_slot_table", "spd_layout", "spd_workspace_size", "spd_fuse_features",
     "spd_pdm_step", "spd_lm_head", "spd_verify", "spd_rollback", "spd_status_string",
-    "spd_last_hip_error", "spd_version",
+    "spd_last_hip_error", "spd_version", "spd_fuse_features_tree", "spd_pdm_step_tree",
+    "spd_verify_siblings",
 )
 
 
@@ -85,6 +87,11 @@ def lib():
         L.spd_lm_head.argtypes = [cfgp, _P, _P, _I32, _F, _P, _P, _P, _P, _P, _SZ, _P]
         L.spd_verify.argtypes = [_I32, _I32, _I32, _F, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
         L.spd_rollback.argtypes = [_P, _I32, _P, _P, _P, _P, _I64, _P]
+        L.spd_fuse_features_tree.argtypes = [cfgp, _P, _I64, _I32, i32p, _I32, _I32, _I32, _P, _P,
+                                             _P, _P, _P, _SZ, _P]
+        L.spd_pdm_step_tree.argtypes = [cfgp, ctypes.POINTER(spd_layer_weights), _P, _P, _P, _I64,
+                                        _P, _I32, _I32, _P, _I32, _P, _P, _SZ, _P]
+        L.spd_verify_siblings.argtypes = [_I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]
         L.spd_status_string.argtypes = [ctypes.c_int]
         L.spd_status_string.restype = ctypes.c_char_p
         L.spd_last_hip_error.restype = ctypes.c_int
@@ -206,6 +213,31 @@ def spd_rollback(st, n, drafted, n_accept, next_token, tokens, T_cap, stream=Non
     _check("spd_rollback", lib().spd_rollback(
         _ptr(st), n, _ptr(drafted), _ptr(n_accept), _ptr(next_token), _ptr(tokens), T_cap,
         _stream(stream)))
+
+
+# ----------------------------------------------------------------- draft trees
+
+def spd_fuse_features_tree(cfg, hstore, T_cap, S, slot_tab, pos0, M, a, anc, norm_w, fc_w, g, ws,
+                           stream=None):
+    _check("spd_fuse_features_tree", lib().spd_fuse_features_tree(
+        ctypes.byref(cfg), _ptr(hstore), T_cap, S, _i32_array(slot_tab), pos0, M, a, _ptr(anc),
+        _ptr(norm_w), _ptr(fc_w), _ptr(g), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream)))
+
+
+def spd_pdm_step_tree(cfg, layers, final_norm, k_cache, v_cache, T_cap, g, pos0, M, anc, n_out,
+                      h_out, ws, stream=None):
+    arr = layers if isinstance(layers, ctypes.Array) else layer_weights(layers)
+    _check("spd_pdm_step_tree", lib().spd_pdm_step_tree(
+        ctypes.byref(cfg), arr, _ptr(final_norm), _ptr(k_cache), _ptr(v_cache), T_cap,
+        _ptr(g), pos0, M, _ptr(anc), n_out, _ptr(h_out), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream)))
+
+
+def spd_verify_siblings(B, W, V, p, cand, accepted, next_token, ws, stream=None):
+    _check("spd_verify_siblings", lib().spd_verify_siblings(
+        B, W, V, _ptr(p), _ptr(cand), _ptr(accepted), _ptr(next_token), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def spd_version() -> int:

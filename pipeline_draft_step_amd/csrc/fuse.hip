@@ -26,9 +26,19 @@ struct SlotTable {
   int8_t v[TABN];
 };
 
+// Pipeline depth of row r.  Chain (anc == null): the newest fully processed row(s)
+// at depth n, then the a in-flight rows at a-1 .. 0.  Draft tree: node r at level
+// l = popcount(anc[r]) - 1 has depth n at the root and a - l below it.
 struct RowDepth {
   int M, a, n;
-  __device__ __forceinline__ int operator()(int r) const { return r < M - a ? n : M - 1 - r; }
+  const uint64_t* anc;
+  __device__ __forceinline__ int operator()(int r) const {
+    if (anc) {
+      const int lv = __popcll(anc[r]) - 1;
+      return lv <= 0 ? n : max(a - lv, 0);
+    }
+    return r < M - a ? n : M - 1 - r;
+  }
 };
 
 constexpr int GATHER_COLS = 8 * 256;  // columns per gather block (8 per thread)
@@ -254,8 +264,8 @@ size_t fuse_workspace(const spd_config* cfg, int M) { return plan_fuse(cfg, M).t
 
 template <typename WT>
 static int fuse_impl(const spd_config* cfg, const void* hstore, int64_t T_cap, int S_store,
-                     const int32_t* slot_tab, int pos0, int M, int a, const void* norm_w,
-                     const void* fc_w, float* g, void* ws, hipStream_t st) {
+                     const int32_t* slot_tab, int pos0, int M, int a, const uint64_t* anc,
+                     const void* norm_w, const void* fc_w, float* g, void* ws, hipStream_t st) {
   (void)T_cap;
   FusePlan p = plan_fuse(cfg, M);
   const int d = cfg->d, m = cfg->m, n = cfg->n;
@@ -279,8 +289,8 @@ static int fuse_impl(const spd_config* cfg, const void* hstore, int64_t T_cap, i
   ga.norm_k0 = cfg->norm_k0 || cfg->feature_schedule == SPD_SCHEDULE_POST_STEP;
   ga.ncb = p.ncb;
   ga.eps = cfg->rms_eps;
-  ga.depth = RowDepth{M, a, n};
-  if (p.big.use) {
+  ga.depth = RowDepth{M, a, n, anc};
+  if (p.big.use && !anc) {
     if constexpr (sizeof(WT) == 2) {
       hipLaunchKernelGGL((feature_gather_rows_kernel<WT>), dim3(M), dim3(256), 0, st, ga);
       int rc = check_launch();
@@ -317,10 +327,10 @@ static int fuse_impl(const spd_config* cfg, const void* hstore, int64_t T_cap, i
 
 using namespace spd;
 
-extern "C" int spd_fuse_features(const spd_config* cfg, const void* hstore, int64_t T_cap,
-                                 int32_t S, const int32_t* slot_tab, int32_t pos0, int32_t M,
-                                 int32_t a, const void* norm_w, const void* fc_w, float* g,
-                                 void* ws, size_t ws_bytes, void* stream) {
+static int fuse_entry(const spd_config* cfg, const void* hstore, int64_t T_cap, int32_t S,
+                      const int32_t* slot_tab, int32_t pos0, int32_t M, int32_t a,
+                      const uint64_t* anc, const void* norm_w, const void* fc_w, float* g,
+                      void* ws, size_t ws_bytes, void* stream) {
   int rc = check_config(cfg);
   if (rc) return rc;
   if (!hstore || !slot_tab || !norm_w || !fc_w || !g || !ws) return SPD_E_INVALID;
@@ -336,6 +346,24 @@ extern "C" int spd_fuse_features(const spd_config* cfg, const void* hstore, int6
   if (ws_bytes < fuse_workspace(cfg, M)) return SPD_E_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (cfg->dtype == SPD_BF16)
-    return fuse_impl<bf16>(cfg, hstore, T_cap, S, slot_tab, pos0, M, a, norm_w, fc_w, g, ws, st);
-  return fuse_impl<float>(cfg, hstore, T_cap, S, slot_tab, pos0, M, a, norm_w, fc_w, g, ws, st);
+    return fuse_impl<bf16>(cfg, hstore, T_cap, S, slot_tab, pos0, M, a, anc, norm_w, fc_w, g, ws, st);
+  return fuse_impl<float>(cfg, hstore, T_cap, S, slot_tab, pos0, M, a, anc, norm_w, fc_w, g, ws, st);
+}
+
+extern "C" int spd_fuse_features(const spd_config* cfg, const void* hstore, int64_t T_cap,
+                                 int32_t S, const int32_t* slot_tab, int32_t pos0, int32_t M,
+                                 int32_t a, const void* norm_w, const void* fc_w, float* g,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  return fuse_entry(cfg, hstore, T_cap, S, slot_tab, pos0, M, a, nullptr, norm_w, fc_w, g, ws,
+                    ws_bytes, stream);
+}
+
+extern "C" int spd_fuse_features_tree(const spd_config* cfg, const void* hstore, int64_t T_cap,
+                                      int32_t S, const int32_t* slot_tab, int32_t pos0, int32_t M,
+                                      int32_t a, const uint64_t* anc, const void* norm_w,
+                                      const void* fc_w, float* g, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  if (!anc || ((uintptr_t)anc & 7) || M > SPD_TREE_MAX_NODES || a < 1) return SPD_E_INVALID;
+  return fuse_entry(cfg, hstore, T_cap, S, slot_tab, pos0, M, a, anc, norm_w, fc_w, g, ws,
+                    ws_bytes, stream);
 }

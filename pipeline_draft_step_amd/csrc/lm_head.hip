@@ -628,13 +628,14 @@ __global__ __launch_bounds__(SMX_THREADS) void topk_sample_kernel(
   SPD_MARK(2);
   if (t == 0) s_cnt = 0u;
   __syncthreads();
+  const bool list_only = probs == nullptr;  // T = 0: the ordered top-k list, no probabilities
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     if (key[e] == 0ull) continue;
     if (key[e] >= th) {
       const unsigned slot = atomicAdd(&s_cnt, 1u);  // < min(k, n) <= cs
       if (slot < (unsigned)cs) st_coh_u64(cr + (size_t)c * cs + slot, key[e]);
-    } else {
+    } else if (!list_only) {
       pr[base + t + SMX_THREADS * e] = 0.f;
     }
   }
@@ -668,7 +669,7 @@ __global__ __launch_bounds__(SMX_THREADS) void topk_sample_kernel(
     if (key2 >= th2) {
       const unsigned slot = atomicAdd(&s_cnt, 1u);  // exactly kk keys pass
       if (slot < (unsigned)TOPK_KMAX) s_sel[slot] = key2;
-    } else if ((unsigned)topk_index(key2) < (unsigned)V) {
+    } else if (!list_only && (unsigned)topk_index(key2) < (unsigned)V) {
       pr[topk_index(key2)] = 0.f;
     }
   });
@@ -688,6 +689,10 @@ __global__ __launch_bounds__(SMX_THREADS) void topk_sample_kernel(
     s_irank[rk] = ri;
   }
   __syncthreads();
+  if (list_only) {  // token[r][i] = i-th largest logit's index, -1 past the vocabulary
+    if (t < k) token[(size_t)r * k + t] = t < kk ? topk_index(s_ord[t]) : -1;
+    return;
+  }
   // thread t < kk now owns the member of key rank t
   const bool member = t < kk;
   const uint64_t my = member ? s_ord[t] : 0ull;
@@ -781,7 +786,9 @@ static int lm_impl(const spd_config* c, const void* w_lm, const float* h, int ro
   BlockStat* stat = reinterpret_cast<BlockStat*>(w + p.off_stat);
   unsigned* ctr = reinterpret_cast<unsigned*>(w);
   const float inv_t = T > 0.f ? 1.0f / T : 0.f;
-  const HeadFinish f{ctr + CTR_HEAD, reinterpret_cast<BlockStat*>(w + p.off_gstat), token, T > 0.f ? 0 : 1};
+  const bool topk_list = T <= 0.f && c->top_k >= 2;  // greedy draft-tree children
+  const HeadFinish f{ctr + CTR_HEAD, reinterpret_cast<BlockStat*>(w + p.off_gstat), token,
+                     (T > 0.f || topk_list) ? 0 : 1};
   int rc;
   if (p.dot) {
     const int nblk = c->head_workgroups > 0 ? std::min(p.nstat, c->head_workgroups) : p.nstat;
@@ -797,7 +804,7 @@ static int lm_impl(const spd_config* c, const void* w_lm, const float* h, int ro
     }
     rc = check_launch();
     if (rc) return rc;
-    if (T <= 0.f) {
+    if (T <= 0.f && !topk_list) {
       hipLaunchKernelGGL(greedy_kernel, dim3(rows), dim3(SMX_THREADS), 0, st, stat, p.nstat, rows, token);
       return check_launch();
     }
@@ -815,12 +822,12 @@ static int lm_impl(const spd_config* c, const void* w_lm, const float* h, int ro
     g.counters = ctr;
     EpiLogits epi{logits, stat, c->V, rows, inv_t, p.gp.nblocks, f};
     rc = launch_gemm<WT, 2>(p.gp, g, InAct<WT, float>{h, c->d}, epi, RowMapStd{}, st);
-    if (rc || T <= 0.f) return rc;
+    if (rc || (T <= 0.f && !topk_list)) return rc;
   }
   if (c->top_k > 0) {
     hipLaunchKernelGGL(topk_sample_kernel, dim3(p.nchunks, rows), dim3(SMX_THREADS), 0, st, logits,
-                       probs, reinterpret_cast<uint64_t*>(w + p.off_cand), ctr + CTR_HEAD + 512,
-                       words, c->V, p.nchunks, c->top_k, T, c->top_p, token);
+                       topk_list ? nullptr : probs, reinterpret_cast<uint64_t*>(w + p.off_cand),
+                       ctr + CTR_HEAD + 512, words, c->V, p.nchunks, c->top_k, T, c->top_p, token);
     return check_launch();
   }
   hipLaunchKernelGGL(softmax_sample_kernel, dim3(p.nchunks, rows), dim3(SMX_THREADS), 0, st, stat,

@@ -36,11 +36,14 @@ constexpr int ATT_MAXCH = 256;                  // chunks per row: context up to
 template <typename WT>
 __global__ __launch_bounds__(64) void rows_init_kernel(const float* g, float* h, float* ss, int M,
                                                        int d, XSplit<WT> xo, const WT* gamma,
-                                                       float2* rope, int pos0, int hd, float theta) {
+                                                       float2* rope, int pos0, int hd, float theta,
+                                                       const uint64_t* anc) {
   const int nb = blockIdx.x, r = blockIdx.y, lane = threadIdx.x;
   if (nb == 0 && lane < hd / 2) {
+    // a draft-tree node sits at its level (number of proper ancestors), a chain row at r
+    const int off = anc ? max(__popcll(anc[r]) - 1, 0) : r;
     double sn, cs;
-    sincos((double)(pos0 + r) * pow((double)theta, -2.0 * lane / hd), &sn, &cs);
+    sincos((double)(pos0 + off) * pow((double)theta, -2.0 * lane / hd), &sn, &cs);
     rope[(size_t)r * (hd / 2) + lane] = make_float2((float)cs, (float)sn);
   }
   const int col = nb * 64 + lane;
@@ -125,6 +128,7 @@ struct AttnArgs {
   void* xl;
   int xld;         // row stride of xh / xl (elements)
   unsigned* counters;  // [Hkv][nqt]
+  const uint64_t* anc;  // draft-tree ancestor masks [M], or null for causal rows
   int M, Hq, Hkv, pos0, nch, nqt;
   int64_t T_cap;
   float scale;
@@ -217,6 +221,12 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   SPD_MARK(2);
   // lane holds S[4*lg + i][16*ks + lr] of this wave's keys
   float mx[4], sm[4];
+  // draft tree: a row reads the new keys of its own root path only
+  uint64_t am[4] = {~0ull, ~0ull, ~0ull, ~0ull};
+  if (a.anc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) am[i] = a.anc[min(16 * qt + 4 * lg + i, QR - 1) / G];
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int qr = 16 * qt + 4 * lg + i;
@@ -225,7 +235,10 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int key = key0 + 16 * ks + lr;
-      if (key > lim || key >= nkeys) sc[ks][i] = -INFINITY;
+      // key <= lim keeps the shift below the row index (< 64 for tree rows)
+      const bool off_path =
+          a.anc && key >= a.pos0 && key <= lim && !((am[i] >> ((key - a.pos0) & 63)) & 1ull);
+      if (key > lim || key >= nkeys || off_path) sc[ks][i] = -INFINITY;
       m_ = fmaxf(m_, sc[ks][i]);
     }
 m_ = row16_max(m_);
@@ -879,7 +892,7 @@ static int pdm_big(const spd_config* c, const spd_layer_weights* layers, const v
 template <typename WT>
 static int pdm_impl(const spd_config* c, const spd_layer_weights* layers, const void* final_norm,
                     void* k_cache, void* v_cache, int64_t T_cap, const float* g, int pos0, int M,
-                    float* h_last, void* ws, hipStream_t st) {
+                    const uint64_t* anc, int n_out, float* h_last, void* ws, hipStream_t st) {
   const PdmPlan p = plan_pdm(c, M, T_cap);
   char* w = static_cast<char*>(ws);
   float* h = reinterpret_cast<float*>(w + p.off_h);
@@ -912,12 +925,13 @@ static int pdm_impl(const spd_config* c, const spd_layer_weights* layers, const 
   aa.nqt = (p.QR + 15) / 16;
   aa.T_cap = T_cap;
   aa.scale = 1.0f / sqrtf((float)hd);
+  aa.anc = anc;
 
   if constexpr (sizeof(WT) == 2) {
-    if (p.big) return pdm_big(c, layers, final_norm, k_cache, v_cache, T_cap, g, pos0, M, h_last, w, p, aa, st);
+    if (p.big && !anc) return pdm_big(c, layers, final_norm, k_cache, v_cache, T_cap, g, pos0, M, h_last, w, p, aa, st);
   }
   hipLaunchKernelGGL((rows_init_kernel<WT>), dim3(d / 64, M), dim3(64), 0, st, g, h, ss, M, d, x0,
-                     static_cast<const WT*>(layers[0].attn_norm), rope, pos0, hd, c->rope_theta);
+                     static_cast<const WT*>(layers[0].attn_norm), rope, pos0, hd, c->rope_theta, anc);
   rc = check_launch();
   if (rc) return rc;
   int P = d / 64;  // partial count of ss
@@ -969,7 +983,7 @@ static int pdm_impl(const spd_config* c, const spd_layer_weights* layers, const 
       const bool last = l == c->Ls - 1;
       EpiResid<WT> epi{h, ss, d, M, last ? 1 : 0, static_cast<const WT*>(final_norm), h_last,
                        ctr + CTR_FINAL, p.down.nblocks, c->rms_eps, last ? none : x0,
-                       last ? nullptr : static_cast<const WT*>(layers[l + 1].attn_norm)};
+                       last ? nullptr : static_cast<const WT*>(layers[l + 1].attn_norm), n_out};
       rc = launch_gemm<WT, 1>(p.down, shape_of(p.down, lw.w_down, d, dff, M, part, ctr), in, epi,
                               RowMapStd{}, st);
       if (rc) return rc;
@@ -984,10 +998,10 @@ static int pdm_impl(const spd_config* c, const spd_layer_weights* layers, const 
 
 using namespace spd;
 
-extern "C" int spd_pdm_step(const spd_config* cfg, const spd_layer_weights* layers,
-                            const void* final_norm, void* k_cache, void* v_cache, int64_t T_cap,
-                            const float* g, int32_t pos0, int32_t M, float* h_last, void* ws,
-                            size_t ws_bytes, void* stream) {
+static int pdm_entry(const spd_config* cfg, const spd_layer_weights* layers, const void* final_norm,
+                     void* k_cache, void* v_cache, int64_t T_cap, const float* g, int32_t pos0,
+                     int32_t M, const uint64_t* anc, int32_t n_out, float* h_last, void* ws,
+                     size_t ws_bytes, void* stream) {
   int rc = check_config(cfg);
   if (rc) return rc;
   if (!layers || !final_norm || !k_cache || !v_cache || !g || !h_last || !ws) return SPD_E_INVALID;
@@ -1020,7 +1034,27 @@ extern "C" int spd_pdm_step(const spd_config* cfg, const spd_layer_weights* laye
   if (ws_bytes < pdm_workspace(cfg, M, T_cap)) return SPD_E_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (cfg->dtype == SPD_BF16)
-    return pdm_impl<bf16>(cfg, layers, final_norm, k_cache, v_cache, T_cap, g, pos0, M, h_last, ws,
-                          st);
-  return pdm_impl<float>(cfg, layers, final_norm, k_cache, v_cache, T_cap, g, pos0, M, h_last, ws, st);
+    return pdm_impl<bf16>(cfg, layers, final_norm, k_cache, v_cache, T_cap, g, pos0, M, anc, n_out,
+                          h_last, ws, st);
+  return pdm_impl<float>(cfg, layers, final_norm, k_cache, v_cache, T_cap, g, pos0, M, anc, n_out,
+                         h_last, ws, st);
+}
+
+extern "C" int spd_pdm_step(const spd_config* cfg, const spd_layer_weights* layers,
+                            const void* final_norm, void* k_cache, void* v_cache, int64_t T_cap,
+                            const float* g, int32_t pos0, int32_t M, float* h_last, void* ws,
+                            size_t ws_bytes, void* stream) {
+  return pdm_entry(cfg, layers, final_norm, k_cache, v_cache, T_cap, g, pos0, M, nullptr, 1, h_last,
+                   ws, ws_bytes, stream);
+}
+
+extern "C" int spd_pdm_step_tree(const spd_config* cfg, const spd_layer_weights* layers,
+                                 const void* final_norm, void* k_cache, void* v_cache,
+                                 int64_t T_cap, const float* g, int32_t pos0, int32_t M,
+                                 const uint64_t* anc, int32_t n_out, float* h_out, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  if (!anc || ((uintptr_t)anc & 7) || M > SPD_TREE_MAX_NODES || n_out < 1 || n_out > M)
+    return SPD_E_INVALID;
+  return pdm_entry(cfg, layers, final_norm, k_cache, v_cache, T_cap, g, pos0, M, anc, n_out, h_out,
+                   ws, ws_bytes, stream);
 }

@@ -661,6 +661,7 @@ struct EpiResid {
   float eps;
   XSplit<WT> xo;
   const WT* gnext;
+  int n_out;  // final_: rows M - n_out .. M - 1 are final-normed into h_last [n_out][N]
   template <int MT, int NT, typename Y, typename RM>
   __device__ void run(const Y& y, int nb, int m0, int Mt, const RM&) const {
     constexpr int R = 4 * MT;  // rows per wave at most
@@ -694,19 +695,25 @@ struct EpiResid {
       sq = wave_sum(sq);
       if (lane == 0) st_coh(ss_out + (size_t)nb * M + m0 + m, sq);
     }
-    if (!final_ || m0 + Mt != M) return;
-    if (!arrive_last(ctr_final, (unsigned)nblocks)) return;
+    if (!final_) return;
+    // every tile of every row block arrives; the last one normalises the output rows
+    const int mtiles = (M + 16 * MT - 1) / (16 * MT);
+    if (!arrive_last(ctr_final, (unsigned)(nblocks * mtiles))) return;
     __shared__ float s_inv;
-    if (threadIdx.x < 64) {
-      float t = 0.f;
-      for (int p = threadIdx.x; p < nblocks; p += 64) t += ld_coh(ss_out + (size_t)p * M + M - 1);
-      t = wave_sum(t);
-      if (threadIdx.x == 0) s_inv = 1.0f / sqrtf(t / (float)N + eps);
-    }
-    __syncthreads();
+    for (int o = 0; o < n_out; ++o) {
+      const int row = M - n_out + o;
+      if (threadIdx.x < 64) {
+        float t = 0.f;
+        for (int p = threadIdx.x; p < nblocks; p += 64) t += ld_coh(ss_out + (size_t)p * M + row);
+        t = wave_sum(t);
+        if (threadIdx.x == 0) s_inv = 1.0f / sqrtf(t / (float)N + eps);
+      }
+      __syncthreads();
 #pragma unroll 4
-    for (int c = threadIdx.x; c < N; c += GEMM_THREADS)
-      h_last[c] = ld_coh(h + (size_t)(M - 1) * N + c) * s_inv * to_f<WT>(final_norm[c]);
+      for (int c = threadIdx.x; c < N; c += GEMM_THREADS)
+        h_last[(size_t)o * N + c] = ld_coh(h + (size_t)row * N + c) * s_inv * to_f<WT>(final_norm[c]);
+      __syncthreads();
+    }
   }
 };
 

@@ -34,6 +34,7 @@ struct VerArgs {
   int32_t* next_token;
   void* part;
   int B, gamma, V, bonus, nchunks;
+  int W;  // sibling candidates per sequence (greedy sibling verification)
 };
 
 __device__ uint64_t vblock_scan(uint64_t v, uint64_t* sh) {
@@ -264,6 +265,30 @@ __global__ __launch_bounds__(VER_THREADS) void verify_greedy_final_kernel(VerArg
   }
 }
 
+// Greedy verification of W sibling candidates of one position per sequence (a draft
+// tree's oldest level): draft[b][i], i < W, is accepted when it equals the target
+// argmax of row b; the first such i is reported.  Row argmax from the chunk pass.
+__global__ __launch_bounds__(VER_THREADS) void verify_siblings_final_kernel(VerArgs a) {
+  const int b = blockIdx.x;
+  const ArgMax* pj = static_cast<const ArgMax*>(a.part) + (size_t)b * a.nchunks;
+  __shared__ ArgMax s_am[VER_THREADS / 64];
+  ArgMax am{-INFINITY, ARG_NONE};
+  for (int k = threadIdx.x; k < a.nchunks; k += VER_THREADS) am = argmax_merge(am, pj[k]);
+  am = wave_argmax(am);
+  if ((threadIdx.x & 63) == 0) s_am[threadIdx.x >> 6] = am;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    ArgMax t = s_am[0];
+    for (int w = 1; w < VER_THREADS / 64; ++w) t = argmax_merge(t, s_am[w]);
+    const int best = t.i == ARG_NONE ? 0 : t.i;
+    int acc = -1;
+    for (int i = 0; i < a.W && acc < 0; ++i)
+      if (a.draft[(size_t)b * a.W + i] == best) acc = i;
+    a.n_accept[b] = acc;
+    a.next_token[b] = acc < 0 ? best : -1;
+  }
+}
+
 size_t verify_workspace(int B, int gamma, int V) {
   const size_t nch = (size_t)(V + VER_CHUNK - 1) / VER_CHUNK;
   const size_t per = std::max((size_t)16, (size_t)(gamma + 1) * sizeof(ArgMax));
@@ -310,5 +335,31 @@ extern "C" int spd_verify(int32_t B, int32_t gamma, int32_t V, float temperature
     if (rc) return rc;
     hipLaunchKernelGGL(verify_greedy_final_kernel, dim3(B), dim3(VER_THREADS), 0, st, a);
   }
+  return check_launch();
+}
+
+extern "C" int spd_verify_siblings(int32_t B, int32_t W, int32_t V, const float* p,
+                                   const int32_t* cand, int32_t* accepted, int32_t* next_token,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  if (B < 1 || B > 65535 || W < 1 || W > SPD_TREE_MAX_NODES || V < 1) return SPD_E_INVALID;
+  if (!p || !cand || !accepted || !next_token || !ws || !aligned16(ws)) return SPD_E_INVALID;
+  if (ws_bytes < verify_workspace(B, 0, V)) return SPD_E_WORKSPACE;
+  VerArgs a{};
+  a.p = p;
+  a.draft = cand;
+  a.n_accept = accepted;
+  a.next_token = next_token;
+  a.part = static_cast<char*>(ws) + SPD_WS_COUNTER_BYTES;
+  a.B = B;
+  a.gamma = 0;  // the chunk pass reads one target row per sequence
+  a.bonus = 1;
+  a.V = V;
+  a.nchunks = (V + VER_CHUNK - 1) / VER_CHUNK;
+  a.W = W;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(verify_greedy_chunks_kernel, dim3(a.nchunks, B), dim3(VER_THREADS), 0, st, a);
+  int rc = check_launch();
+  if (rc) return rc;
+  hipLaunchKernelGGL(verify_siblings_final_kernel, dim3(B), dim3(VER_THREADS), 0, st, a);
   return check_launch();
 }

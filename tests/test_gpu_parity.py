@@ -376,6 +376,176 @@ def test_lm_head_top_k_ties_break_by_index(V, top_k):
     assert torch.equal(p2, probs) and torch.equal(t2, tok)
 
 
+# ------------------------------------------------------------------ draft trees
+
+def _width_tree(W, a):
+    """Parents of a width-W tree with a levels below the root: level 1 holds W
+    children of the root, every deeper level W nodes whose parents are the first
+    nodes of the level above (two children each), as a top-W expansion keeps the
+    likeliest paths."""
+    parents, prev = [-1], [0]
+    for lvl in range(a):
+        cur = []
+        for i in range(W):
+            parents.append(0 if lvl == 0 else prev[min(i // 2, len(prev) - 1)])
+            cur.append(len(parents) - 1)
+        prev = cur
+    return parents
+
+
+def _masks(parents):
+    anc = []
+    for i, p in enumerate(parents):
+        anc.append((1 << i) | (anc[p] if p >= 0 else 0))
+    return anc
+
+
+def _anc_tensor(anc):
+    return torch.from_numpy(np.array(anc, dtype=np.uint64).view(np.int64)).to(DEV)
+
+
+TREE_CASES = [
+    # name, shape, W, a, pos0 (None: the cycle's, ctx - 1 - n)
+    ("small_w4_a3", SMALL_BF16, 4, 3, None),
+    ("small_w4_a3_short_prefix", SMALL_BF16, 4, 3, 3),
+    ("small_w2_a8", SMALL_BF16, 2, 8, None),
+    ("tiny_w3_a3", synth.TINY, 3, 3, None),
+    ("tiny_w4_a4_no_prefix", synth.TINY, 4, 4, 0),
+    ("headline_w4_a7", synth.HEADLINE, 4, 7, None),
+    ("headline_w4_a8_two_row_tiles", synth.HEADLINE, 4, 8, None),
+]
+
+
+@pytest.mark.parametrize("name,shape,W,a,pos0", TREE_CASES, ids=[c[0] for c in TREE_CASES])
+def test_tree_features_and_pdm_step(name, shape, W, a, pos0):
+    """Features of every tree node (depth n at the root, a - level below) and the
+    tree-masked PDM step on a seeded committed cache: the deepest level's final
+    rows and every node's cache slot against the oracle.  The short-prefix cases
+    make the tree's own keys dominate attention, so a wrong mask or position
+    cannot hide inside the tolerance."""
+    ci = synth.cycle_inputs(shape, device=DEV, with_heads=False)
+    model = device_model(ci)
+    cyc = SpdCycle(model, shape.temperature)
+    om = OC.model_from_inputs(ci, with_heads=False)
+    anc = _width_tree(W, a)
+    anc = _masks(anc)
+    M = len(anc)
+    if pos0 is None:
+        pos0 = shape.ctx - 1 - shape.n
+    assert pos0 + M <= model.T_cap
+    say(name, "tree", M, pos0)
+    dev_anc = _anc_tensor(anc)
+    ws = torch.zeros(max(spd.spd_workspace_size(spd.SPD_CALL_FUSE, model.cfg, M),
+                         spd.spd_workspace_size(spd.SPD_CALL_PDM, model.cfg, M, 0, model.T_cap)),
+                     dtype=torch.uint8, device=DEV)
+    g = torch.empty(M, shape.d, device=DEV)
+    spd.spd_fuse_features_tree(model.cfg, model.w.store, model.T_cap, len(model.store_layers),
+                               model.slot_tab, pos0, M, a, dev_anc, model.w.fc_norm, model.w.w_fc, g,
+                               ws)
+    torch.cuda.synchronize()
+    rows, depth, _ = O.tree_rows(anc, a, shape.n, pos0)
+    ref = O.fuse_features(om.store, om.store_layers, rows, depth, om.fc_norm, om.w_fc, L=shape.L,
+                          n=shape.n, anchors=shape.anchors, mode=shape.anchor_mode, eps=shape.eps,
+                          norm_k0=bool(shape.norm_k0), schedule=shape.feature_schedule)
+    assert rel_err(f64(g), ref) < tol_for(shape.dtype)
+
+    k, v = synth.kv_cache(shape, model.T_cap, device=DEV)
+    cyc.k_cache.copy_(k)
+    cyc.v_cache.copy_(v)
+    gin = synth.normal((M, shape.d), 1.0, device=DEV, seed=77, name="tree_rows")
+    n_out = W
+    h_out = torch.empty(n_out, shape.d, device=DEV)
+    spd.spd_pdm_step_tree(model.cfg, model.layer_arr, model.w.final_norm, cyc.k_cache, cyc.v_cache,
+                          model.T_cap, gin, pos0, M, dev_anc, n_out, h_out, ws)
+    torch.cuda.synchronize()
+    cache = _oracle_cache_from(k, v, pos0, shape)
+    ref_rows, _ = O.pdm_step_tree(f64(gin), pos0, cache, om.layers, om.final_norm, om.pdm, anc)
+    tol = tol_for(shape.dtype)
+    for o in range(n_out):
+        assert rel_err(f64(h_out[o]), ref_rows[M - n_out + o]) < tol, o
+    _check_cache_rows(cyc, cache, pos0, pos0 + M, tol)
+
+
+def test_tree_pdm_chain_matches_causal_step():
+    """A chain given as tree masks is the ordinary step, bit for bit."""
+    shape = SMALL_BF16
+    ci = synth.cycle_inputs(shape, device=DEV, with_heads=False)
+    model = device_model(ci)
+    cyc = SpdCycle(model, shape.temperature)
+    k, v = synth.kv_cache(shape, model.T_cap, device=DEV)
+    M, pos0 = 9, shape.ctx - 9
+    g = synth.normal((M, shape.d), 1.0, device=DEV, seed=78, name="chain_rows")
+    anc = _anc_tensor(_masks([-1] + list(range(M - 1))))
+    ws = torch.zeros(spd.spd_workspace_size(spd.SPD_CALL_PDM, model.cfg, M, 0, model.T_cap),
+                     dtype=torch.uint8, device=DEV)
+    outs = []
+    for tree in (False, True):
+        cyc.k_cache.copy_(k)
+        cyc.v_cache.copy_(v)
+        h = torch.empty(1, shape.d, device=DEV)
+        if tree:
+            spd.spd_pdm_step_tree(model.cfg, model.layer_arr, model.w.final_norm, cyc.k_cache,
+                                  cyc.v_cache, model.T_cap, g, pos0, M, anc, 1, h, ws)
+        else:
+            spd.spd_pdm_step(model.cfg, model.layer_arr, model.w.final_norm, cyc.k_cache,
+                             cyc.v_cache, model.T_cap, g, pos0, M, h, ws)
+        torch.cuda.synchronize()
+        outs.append((h.clone(), cyc.k_cache.clone(), cyc.v_cache.clone()))
+    for x, y in zip(*outs):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("rows,V,d,dtype,W", [(1, 151936, 2560, 1, 4), (4, 151936, 2560, 1, 4),
+                                              (1, 5000, 64, 0, 8), (2, 300, 64, 0, 256)])
+def test_lm_head_top_w_children(rows, V, d, dtype, W):
+    """T = 0 with top_k = W: the ordered W largest logits of each row (the
+    children of a greedy tree node), -1 past the vocabulary."""
+    say("lm_head top-W", rows, V, W)
+    wdt = synth.storage_dtype(dtype)
+    Wt = synth.normal((V, d), 0.02 if dtype else 1.0, device=DEV, seed=51, name="w_lm", dtype=wdt)
+    h = synth.normal((rows, d), 1.0, device=DEV, seed=51, name="h")
+    cfg = spd.make_config(L=1, n=1, m=1, d=d, Ls=1, Hq=1, Hkv=1, hd=16, dff=64, V=V, dtype=dtype,
+                          top_k=W)
+    logits = torch.empty(rows, V, device=DEV)
+    tok = torch.full((rows, W), -7, dtype=torch.int32, device=DEV)
+    ws = torch.zeros(spd.spd_workspace_size(spd.SPD_CALL_LM_HEAD, cfg, rows), dtype=torch.uint8,
+                     device=DEV)
+    spd.spd_lm_head(cfg, Wt, h, rows, 0.0, None, logits, None, tok, ws)
+    torch.cuda.synchronize()
+    got = tok.cpu().numpy()
+    for r in range(rows):
+        want = O.top_k_list(logits[r].cpu().numpy().astype(np.float64), min(W, V))
+        want += [-1] * (W - len(want))
+        assert got[r].tolist() == want, r
+
+
+def test_verify_siblings_greedy():
+    B, W, V = 40, 4, 151936
+    say("verify siblings", B, W)
+    logits = synth.normal((B, V), 3.0, device=DEV, seed=61, name="sib_logits")
+    best = logits.argmax(-1).to(torch.int32).cpu().numpy()
+    gen = np.random.default_rng(61)
+    cand = gen.integers(0, V, size=(B, W)).astype(np.int32)
+    for b in range(B):
+        j = b % (W + 1)                 # W: no sibling matches
+        cand[b][cand[b] == best[b]] = (best[b] + 1) % V
+        if j < W:
+            cand[b][j] = best[b]
+    cand_d = torch.from_numpy(cand).to(DEV)
+    cfg = spd.make_config(L=1, n=1, m=1, d=64, Ls=1, Hq=1, Hkv=1, hd=16, dff=64, V=V, dtype=0)
+    ws = torch.zeros(spd.spd_workspace_size(spd.SPD_CALL_VERIFY, cfg, B, 0), dtype=torch.uint8,
+                     device=DEV)
+    acc = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+    nxt = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+    spd.spd_verify_siblings(B, W, V, logits, cand_d, acc, nxt, ws)
+    torch.cuda.synchronize()
+    lc = logits.cpu().numpy()
+    for b in range(B):
+        ref = O.verify_siblings(lc[b], cand[b])
+        assert (int(acc[b]), int(nxt[b])) == ref, b
+        assert ref[0] == (b % (W + 1) if b % (W + 1) < W else -1)
+
+
 # ------------------------------------------------------------------ verify
 
 def _verify_gpu(p, q, draft, words, T, bonus):
