@@ -287,6 +287,67 @@ def main():
                "draft_head_us_unfiltered": round(head_ms * 1000.0, 2)}
     del cyc_k, model_k
 
+    # greedy width-4 draft tree at the saturated depth: features and PDM over the
+    # 29 tree nodes (root + 7 levels of 4), the top-4 children of the 4 deepest
+    # nodes, greedy verification of the 4 oldest siblings
+    W_tree, a_tree = 4, s.n - 1
+    parents, prev = [-1], [0]
+    for lvl in range(a_tree):
+        cur = []
+        for i in range(W_tree):
+            parents.append(0 if lvl == 0 else prev[min(i // 2, len(prev) - 1)])
+            cur.append(len(parents) - 1)
+        prev = cur
+    anc = []
+    for i, par in enumerate(parents):
+        anc.append((1 << i) | (anc[par] if par >= 0 else 0))
+    Mt = len(anc)
+    anc_d = torch.tensor(anc, dtype=torch.int64, device=dev)
+    cfg_t = spd.spd_config.from_buffer_copy(model.cfg)
+    cfg_t.top_k = W_tree
+    ws_t = torch.zeros(max(spd.spd_workspace_size(spd.SPD_CALL_FUSE, cfg_t, Mt),
+                           spd.spd_workspace_size(spd.SPD_CALL_PDM, cfg_t, Mt, 0, model.T_cap),
+                           spd.spd_workspace_size(spd.SPD_CALL_LM_HEAD, cfg_t, W_tree),
+                           spd.spd_workspace_size(spd.SPD_CALL_VERIFY, cfg_t, 1, 0)),
+                       dtype=torch.uint8, device=dev)
+    g_t = torch.empty(Mt, s.d, device=dev)
+    h_t = torch.empty(W_tree, s.d, device=dev)
+    lg_t = torch.empty(W_tree, s.V, device=dev)
+    kids = torch.empty(W_tree, W_tree, dtype=torch.int32, device=dev)
+    acc_t = torch.empty(1, dtype=torch.int32, device=dev)
+    nxt_t = torch.empty(1, dtype=torch.int32, device=dev)
+    pos0_t = t - 1 - s.n
+
+    def tree_step(ev=None):
+        rec = (lambda i: ev[i].record()) if ev else (lambda i: None)
+        rec(0)
+        spd.spd_fuse_features_tree(cfg_t, w.store, model.T_cap, len(model.store_layers),
+                                   model.slot_tab, pos0_t, Mt, a_tree, anc_d, w.fc_norm, w.w_fc,
+                                   g_t, ws_t)
+        rec(1)
+        spd.spd_pdm_step_tree(cfg_t, model.layer_arr, w.final_norm, cyc.k_cache, cyc.v_cache,
+                              model.T_cap, g_t, pos0_t, Mt, anc_d, W_tree, h_t, ws_t)
+        rec(2)
+        spd.spd_lm_head(cfg_t, w.w_dlm, h_t, W_tree, 0.0, None, lg_t, None, kids, ws_t)
+        rec(3)
+        spd.spd_verify_siblings(1, W_tree, s.V, cyc.tlogits, kids, acc_t, nxt_t, ws_t)
+        rec(4)
+
+    for _ in range(5):
+        tree_step()
+    tacc = np.zeros(4)
+    reps = 20
+    for _ in range(reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        tree_step(ev)
+        torch.cuda.synchronize()
+        tacc += [ev[i].elapsed_time(ev[i + 1]) for i in range(4)]
+    tacc = tacc / reps * 1000.0
+    tree = {"width": W_tree, "levels": a_tree, "nodes": Mt, "fuse_us": round(tacc[0], 1),
+            "pdm_us": round(tacc[1], 1), "draft_head_top4_x4rows_us": round(tacc[2], 1),
+            "verify_siblings_us": round(tacc[3], 1), "step_us": round(float(tacc.sum()), 1),
+            "note": "calls in sequence, each timed alone (the chain cycle's calls: see calls)"}
+
     result = {
         "metric": "draft+verify cycles/s + achieved HBM GB/s, d=2560 n=8 vocab 151936, 1 GPU",
         "value": round(cycles_per_s, 2),
@@ -316,6 +377,7 @@ def main():
         "prefill_fc": prefill_fc,
         "prefill": prefill,
         "sampling_top_k50": top_k50,
+        "draft_tree_w4": tree,
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_cpu_baseline:
