@@ -417,6 +417,50 @@ def verify_siblings(p_logits, cand):
     return -1, best
 
 
+def sibling_weights(p32):
+    """floor(p * 2^51) of an fp32 probability row as Python integers (entries
+    that are not positive, NaN included, weigh 0)."""
+    p = np.asarray(p32, dtype=np.float32).astype(np.float64)
+    p = np.where(p > 0, p, 0.0)
+    return [int(v) for v in np.floor(p * 2.0 ** 51)]
+
+
+def verify_siblings_sampled(p32, q32, cand, words):
+    """Stochastic verification of W sibling candidates drawn independently from q
+    (the multi-round form of [SD]'s acceptance criterion, as in SpecInfer's
+    multi-candidate speculative sampling): round i tests candidate x_i against the
+    current target p_i with r <= min(1, p_i(x)/q(x)); a rejection replaces the
+    target by the normalised residual max(0, p_i - q); after W rejections the token
+    is drawn from the last residual.  The output is distributed as p.
+
+    Integer form, exact on both sides: A = floor(p 2^51), B = floor(q 2^51),
+    p_i = A/sum(A), q = B/sum(B).  Round i accepts x_i iff
+    (R_i + 1) B(x_i) sum(A) <= 2^24 A(x_i) sum(B) with R_i = words[i][0] >> 40
+    (a candidate outside the vocabulary is rejected).  On rejection
+    D = max(0, A sum(B) - B sum(A)) and A = D >> s, s = max(0, bitlength(sum D) - 52),
+    which keeps sum(A) below 2^52.  After W rejections the token is the inverse-CDF
+    draw from A with u = words[W][1] >> 32 (from floor(p 2^51) if A sums to 0).
+    Returns (index of the accepted candidate, -1) or (-1, drawn token).
+    """
+    A = sibling_weights(p32)
+    B = sibling_weights(q32)
+    SB = sum(B)
+    V = len(A)
+    for i, x in enumerate(cand):
+        SA = sum(A)
+        x = int(x)
+        R1 = (int(words[i][0]) >> 40) + 1
+        if 0 <= x < V and R1 * B[x] * SA <= (1 << 24) * A[x] * SB:
+            return i, -1
+        D = [max(0, a * SB - b * SA) for a, b in zip(A, B)]
+        s = max(0, sum(D).bit_length() - 52)
+        A = [d >> s for d in D]
+    if sum(A) == 0:
+        A = sibling_weights(p32)
+    t = sample_weights(np.array(A, dtype=np.uint64), int(words[len(cand)][1]) >> 32)
+    return -1, 0 if t is None else t
+
+
 # --------------------------------------------------------------------------
 # Heads, sampling and verification ([SPD] 3.1, 3.4; [SD] four-phase loop and
 # acceptance criterion)

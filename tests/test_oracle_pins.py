@@ -434,6 +434,110 @@ def test_verify_siblings_greedy():
         assert (acc == 0) == (na == 1) and (nxt if acc < 0 else -1) == nt
 
 
+def _accept_threshold(run, lo=0, hi=1 << 24):
+    """Number of R values in [lo, hi) for which run(R) accepts, acceptance being
+    monotone (accepts exactly for R below a threshold): binary search."""
+    if not run(lo):
+        return 0
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        if run(mid):
+            lo = mid
+        else:
+            hi = mid
+    return hi
+
+
+def _sibling_law(p, q, W):
+    """Exact output law of verify_siblings_sampled with W candidates drawn
+    independently from the integer q, computed by calling the oracle as a black
+    box: per candidate tuple and round, the accepted share of the 2^24 R lattice
+    (binary search on the monotone accept region); after W rejections, the share of
+    the 2^32 u lattice each token takes (binary search on the monotone inverse CDF)."""
+    V = len(p)
+    B = O.sibling_weights(q)
+    SB = sum(B)
+    law = [Fraction(0)] * V
+    rej_all = 1 << 24                   # R that rejects whenever rejection is possible
+    for tup in itertools.product(range(V), repeat=W):
+        wq = Fraction(1)
+        for x in tup:
+            wq *= Fraction(B[x], SB)
+        if wq == 0:
+            continue
+        reach = Fraction(1)
+        for i in range(W):
+            def run(R, i=i):
+                words = np.zeros((W + 1, 2), np.uint64)
+                for k in range(i):
+                    words[k][0] = np.uint64((rej_all - 1) << 40)
+                words[i][0] = np.uint64(R << 40)
+                acc, _ = O.verify_siblings_sampled(p, q, tup, words)
+                return acc == i
+            n_acc = _accept_threshold(run)
+            law[tup[i]] += wq * reach * Fraction(n_acc, 1 << 24)
+            reach *= Fraction((1 << 24) - n_acc, 1 << 24)
+            if reach == 0:
+                break
+        if reach == 0:
+            continue
+
+        def draw(u):
+            words = np.zeros((W + 1, 2), np.uint64)
+            for k in range(W):
+                words[k][0] = np.uint64((rej_all - 1) << 40)
+            words[W][1] = np.uint64(u << 32)
+            return O.verify_siblings_sampled(p, q, tup, words)[1]
+        start = 0
+        while start < (1 << 32):
+            tok = draw(start)
+            lo, hi = start, 1 << 32         # last u with the same token: binary search
+            while hi - lo > 1:
+                mid = (lo + hi) // 2
+                if draw(mid) == tok:
+                    lo = mid
+                else:
+                    hi = mid
+            law[tok] += wq * reach * Fraction(hi - start, 1 << 32)
+            start = hi
+    return law
+
+
+@pytest.mark.parametrize("V,W", [(4, 1), (4, 2), (5, 3)])
+def test_sampled_sibling_verify_output_law_is_exactly_p(V, W):
+    """Multi-candidate speculative sampling with W independent draws from q
+    outputs exactly p (up to the 2^-24 / 2^-32 lattices): checked on small
+    vocabularies, including rows with zeros (filtered p and q of different
+    supports)."""
+    rng = np.random.default_rng(29 + V * 10 + W)
+    cases = [(rng.dirichlet(np.ones(V) * 0.7).astype(np.float32),
+              rng.dirichlet(np.ones(V) * 0.7).astype(np.float32))]
+    lp = rng.standard_normal(V) * 2
+    cases.append((O.filtered_softmax(lp, 1.0, V - 1).astype(np.float32),
+                  O.filtered_softmax(lp + rng.standard_normal(V), 1.0, V - 1).astype(np.float32)))
+    for p, q in cases:
+        law = _sibling_law(p, q, W)
+        A = O.sibling_weights(p)
+        assert abs(float(sum(law)) - 1.0) < 1e-12
+        for j in range(V):
+            assert abs(float(law[j]) - A[j] / sum(A)) < (W + 1) * V * 2.0 ** -22, (j, W)
+
+
+def test_sampled_sibling_verify_cases():
+    p = np.array([0.5, 0.25, 0.25, 0.0], np.float32)
+    q = np.array([0.25, 0.25, 0.25, 0.25], np.float32)
+    w = np.zeros((3, 2), np.uint64)
+    # p >= q at a token always accepts; p = 0 never does
+    assert O.verify_siblings_sampled(p, q, [0, 1], w) == (0, -1)
+    w[0][0] = np.uint64(((1 << 24) - 1) << 40)
+    assert O.verify_siblings_sampled(p, q, [3, 0], w) == (1, -1)
+    # two rejections at token 3: the residual after round 1 is max(0, p - q) = (1/4, 0, 0, 0)
+    w[1][0] = np.uint64(((1 << 24) - 1) << 40)
+    assert O.verify_siblings_sampled(p, q, [3, 3], w) == (-1, 0)
+    # out-of-vocabulary candidates are rejected
+    assert O.verify_siblings_sampled(p, q, [7, -1], w)[0] == -1
+
+
 # ------------------------------------------------------------------ P8
 
 def test_argmax_first_and_nan():
