@@ -330,7 +330,8 @@ def main():
         rec(2)
         spd.spd_lm_head(cfg_t, w.w_dlm, h_t, W_tree, 0.0, None, lg_t, None, kids, ws_t)
         rec(3)
-        spd.spd_verify_siblings(1, W_tree, s.V, cyc.tlogits, kids, acc_t, nxt_t, ws_t)
+        spd.spd_verify_siblings(1, W_tree, s.V, 0.0, cyc.tlogits, None, kids, None, acc_t, nxt_t,
+                                ws_t)
         rec(4)
 
     for _ in range(5):
@@ -343,9 +344,24 @@ def main():
         torch.cuda.synchronize()
         tacc += [ev[i].elapsed_time(ev[i + 1]) for i in range(4)]
     tacc = tacc / reps * 1000.0
+    # T = 1 sibling verification, worst case: every round rejects (W passes pairs over V)
+    rej = np.zeros((W_tree + 1, 2), np.uint64)
+    rej[:W_tree, 0] = np.uint64(((1 << 24) - 1) << 40)
+    rej_d = synth.words_tensor(rej, dev)
+    qrow = cyc.ring[0:1]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    spd.spd_verify_siblings(1, W_tree, s.V, 1.0, cyc.p, qrow, kids, rej_d, acc_t, nxt_t, ws_t)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        spd.spd_verify_siblings(1, W_tree, s.V, 1.0, cyc.p, qrow, kids, rej_d, acc_t, nxt_t, ws_t)
+    e1.record()
+    torch.cuda.synchronize()
+    sib_t1_us = e0.elapsed_time(e1) / reps * 1000.0
     tree = {"width": W_tree, "levels": a_tree, "nodes": Mt, "fuse_us": round(tacc[0], 1),
             "pdm_us": round(tacc[1], 1), "draft_head_top4_x4rows_us": round(tacc[2], 1),
             "verify_siblings_us": round(tacc[3], 1), "step_us": round(float(tacc.sum()), 1),
+            "verify_siblings_t1_all_rejected_us": round(sib_t1_us, 1),
             "note": "calls in sequence, each timed alone (the chain cycle's calls: see calls)"}
 
     result = {

@@ -280,15 +280,27 @@ int spd_pdm_step_tree(const spd_config *cfg, const spd_layer_weights *layers,
                       const float *g, int32_t pos0, int32_t M, const uint64_t *anc, int32_t n_out,
                       float *h_out, void *ws, size_t ws_bytes, void *stream);
 
-/* Greedy verification of sibling candidates (section 3.4 at T = 0, applied to a tree
- * level whose nodes share one parent).  For each sequence b < B: best = argmax of the
- * target logits p[b] (lowest index on ties); accepted[b] = the first i < W with
- * cand[b][i] == best, or -1; next_token[b] = best when none is accepted, else -1.
- * p DEVICE float [B][V]; cand DEVICE int32 [B][W]; accepted, next_token DEVICE int32
- * [B].  ws >= spd_workspace_size(SPD_CALL_VERIFY, cfg with this V, B, 0, 0).
- * The W candidates of a greedy tree node come from spd_lm_head at T = 0 with
- * cfg.top_k = W. */
-int spd_verify_siblings(int32_t B, int32_t W, int32_t V, const float *p, const int32_t *cand,
+/* Verification of sibling candidates: W candidates for one position per sequence (a
+ * draft-tree level whose nodes share one parent).  Returns accepted[b] = index of the
+ * accepted candidate, or -1 with next_token[b] = the token that replaces them (else -1).
+ * temperature == 0 (section 3.4, greedy): p DEVICE float [B][V] holds target logits;
+ *   best = argmax (lowest index on ties); the first i with cand[b][i] == best is
+ *   accepted, else next_token = best.  q and words are unused.
+ * temperature > 0 (multi-round form of the speculative-decoding explainer's acceptance
+ *   criterion; the candidates must be independent draws from q): p, q DEVICE float
+ *   [B][V] probability rows (sums near 1), words DEVICE uint64 [B][W+1][2].  With
+ *   A = floor(p 2^51), B = floor(q 2^51) (integers): round i accepts cand[b][i] = x iff
+ *   (R_i + 1) B(x) sum(A) <= 2^24 A(x) sum(B), R_i = words[b][i][0] >> 40 (x outside the
+ *   vocabulary is rejected); on rejection A <- max(0, A sum(B) - B sum(A)) >> s with
+ *   s = max(0, bitlength of its sum - 52), the residual max(0, p_i - q) as the next
+ *   target.  After W rejections next_token is the inverse-CDF draw from A with
+ *   u = words[b][W][1] >> 32 (from floor(p 2^51) if A is empty).  The output token is
+ *   distributed as p.  One block per sequence; cost grows with W^2 passes over V.
+ * cand DEVICE int32 [B][W] (W <= SPD_TREE_MAX_NODES); accepted, next_token DEVICE int32
+ * [B].  ws >= spd_workspace_size(SPD_CALL_VERIFY, cfg with this V, B, 0, 0).  The W
+ * candidates of a greedy tree node come from spd_lm_head at T = 0 with cfg.top_k = W. */
+int spd_verify_siblings(int32_t B, int32_t W, int32_t V, float temperature, const float *p,
+                        const float *q, const int32_t *cand, const uint64_t *words,
                         int32_t *accepted, int32_t *next_token, void *ws, size_t ws_bytes,
                         void *stream);
 

@@ -91,7 +91,8 @@ def lib():
                                              _P, _P, _P, _SZ, _P]
         L.spd_pdm_step_tree.argtypes = [cfgp, ctypes.POINTER(spd_layer_weights), _P, _P, _P, _I64,
                                         _P, _I32, _I32, _P, _I32, _P, _P, _SZ, _P]
-        L.spd_verify_siblings.argtypes = [_I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]
+        L.spd_verify_siblings.argtypes = [_I32, _I32, _I32, _F, _P, _P, _P, _P, _P, _P, _P, _SZ,
+                                          _P]
         L.spd_status_string.argtypes = [ctypes.c_int]
         L.spd_status_string.restype = ctypes.c_char_p
         L.spd_last_hip_error.restype = ctypes.c_int
@@ -234,10 +235,11 @@ def spd_pdm_step_tree(cfg, layers, final_norm, k_cache, v_cache, T_cap, g, pos0,
         _stream(stream)))
 
 
-def spd_verify_siblings(B, W, V, p, cand, accepted, next_token, ws, stream=None):
+def spd_verify_siblings(B, W, V, temperature, p, q, cand, words, accepted, next_token, ws,
+                        stream=None):
     _check("spd_verify_siblings", lib().spd_verify_siblings(
-        B, W, V, _ptr(p), _ptr(cand), _ptr(accepted), _ptr(next_token), _ptr(ws),
-        ws.numel() * ws.element_size(), _stream(stream)))
+        B, W, V, float(temperature), _ptr(p), _ptr(q), _ptr(cand), _ptr(words), _ptr(accepted),
+        _ptr(next_token), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def spd_version() -> int:

@@ -289,6 +289,146 @@ __global__ __launch_bounds__(VER_THREADS) void verify_siblings_final_kernel(VerA
   }
 }
 
+// Stochastic verification of W sibling candidates drawn independently from q
+// (multi-round rejection: each rejection makes the normalised residual max(0, p_i - q)
+// the next round's target; after W rejections the token is drawn from the last
+// residual).  Exact integer form: A = floor(p 2^51), B = floor(q 2^51); round i
+// accepts x_i iff (R_i + 1) B(x_i) sum(A) <= 2^24 A(x_i) sum(B); on rejection
+// A <- max(0, A sum(B) - B sum(A)) >> s with s = max(0, bitlength(sum) - 52), which keeps
+// sum(A) < 2^52 and every product below 2^128.  A row's round-i weight is recomputed
+// from (p_j, q_j) and the per-round scalars, so nothing but scalars is stored.
+// One block per sequence.
+constexpr int SIB_THREADS = 1024;
+constexpr int SIB_WAVES = SIB_THREADS / 64;
+typedef unsigned __int128 u128;
+
+__device__ __forceinline__ uint64_t sib_weight(float p) {  // floor(p * 2^51), 0 unless p > 0
+  return (p > 0.f) ? (uint64_t)((double)p * 2251799813685248.0) : 0ull;
+}
+__device__ __forceinline__ u128 sib_resid(uint64_t a, uint64_t b, uint64_t SA, uint64_t SB) {
+  const u128 x = (u128)a * SB, y = (u128)b * SA;
+  return x > y ? x - y : (u128)0;
+}
+// round-`rounds` weight of an entry with first-round weights (a, b)
+__device__ __forceinline__ uint64_t sib_chain(uint64_t a, uint64_t b, int rounds, const uint64_t* hSA,
+                                              const int* hS, uint64_t SB) {
+  for (int k = 0; k < rounds; ++k) a = (uint64_t)(sib_resid(a, b, hSA[k], SB) >> hS[k]);
+  return a;
+}
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, m, 64), hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+// block sum of a 128-bit value (exact, any order); every thread gets the result
+__device__ u128 sib_block_sum(u128 v, u128* red) {
+  uint64_t lo = (uint64_t)v, hi = (uint64_t)(v >> 64);
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const uint64_t olo = shfl_xor_u64(lo, m), ohi = shfl_xor_u64(hi, m);
+    const uint64_t nlo = lo + olo;
+    hi = hi + ohi + (nlo < lo ? 1ull : 0ull);
+    lo = nlo;
+  }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = ((u128)hi << 64) | lo;
+  __syncthreads();
+  u128 t = 0;
+  for (int w = 0; w < SIB_WAVES; ++w) t += red[w];
+  __syncthreads();
+  return t;
+}
+
+__global__ __launch_bounds__(SIB_THREADS) void verify_siblings_sampled_kernel(VerArgs a) {
+  __shared__ u128 s_red[SIB_WAVES];
+  __shared__ uint64_t s_hSA[SPD_TREE_MAX_NODES];
+  __shared__ int s_hS[SPD_TREE_MAX_NODES];
+  __shared__ int s_acc;
+  __shared__ uint64_t s_wt[SIB_WAVES];
+  __shared__ int s_tok;
+  const int b = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const float* prow = a.p + (size_t)b * a.V;
+  const float* qrow = a.q + (size_t)b * a.V;
+  const uint64_t* wd = a.words + (size_t)b * (a.W + 1) * 2;
+  u128 sa = 0, sb = 0;
+  for (int j = t; j < a.V; j += SIB_THREADS) {
+    sa += sib_weight(prow[j]);
+    sb += sib_weight(qrow[j]);
+  }
+  const uint64_t SA0 = (uint64_t)sib_block_sum(sa, s_red);
+  const uint64_t SB = (uint64_t)sib_block_sum(sb, s_red);
+  uint64_t SA = SA0;
+  for (int i = 0; i < a.W; ++i) {
+    if (t == 0) {
+      const int x = a.draft[(size_t)b * a.W + i];
+      int acc = 0;
+      if (x >= 0 && x < a.V) {
+        const uint64_t bx = sib_weight(qrow[x]);
+        const uint64_t ax = sib_chain(sib_weight(prow[x]), bx, i, s_hSA, s_hS, SB);
+        const uint64_t R1 = (wd[2 * i] >> 40) + 1;
+        acc = (u128)R1 * bx * SA <= ((u128)ax * SB) << 24;
+      }
+      s_acc = acc;
+      s_hSA[i] = SA;
+    }
+    __syncthreads();
+    if (s_acc) {
+      if (t == 0) {
+        a.n_accept[b] = i;
+        a.next_token[b] = -1;
+      }
+      return;
+    }
+    // residual of round i: its 128-bit total fixes the shift, then the new total
+    u128 dsum = 0;
+    for (int j = t; j < a.V; j += SIB_THREADS) {
+      const uint64_t bj = sib_weight(qrow[j]);
+      const uint64_t aj = sib_chain(sib_weight(prow[j]), bj, i, s_hSA, s_hS, SB);
+      dsum += sib_resid(aj, bj, SA, SB);
+    }
+    const u128 D = sib_block_sum(dsum, s_red);
+    const uint64_t dhi = (uint64_t)(D >> 64), dlo = (uint64_t)D;
+    const int bits = dhi ? 128 - __builtin_clzll(dhi) : (dlo ? 64 - __builtin_clzll(dlo) : 0);
+    if (t == 0) s_hS[i] = bits > 52 ? bits - 52 : 0;
+    __syncthreads();
+    u128 asum = 0;
+    for (int j = t; j < a.V; j += SIB_THREADS)
+      asum += sib_chain(sib_weight(prow[j]), sib_weight(qrow[j]), i + 1, s_hSA, s_hS, SB);
+    SA = (uint64_t)sib_block_sum(asum, s_red);
+  }
+  // every candidate rejected: inverse-CDF draw from the last residual (from p if empty)
+  const int rounds = SA > 0 ? a.W : 0;
+  const uint64_t S = SA > 0 ? SA : SA0;
+  const uint64_t tau = scale_u32((uint32_t)(wd[2 * a.W + 1] >> 32), S);
+  if (t == 0) s_tok = -1;
+  uint64_t before = 0;
+  for (int base = 0; base < a.V; base += SIB_THREADS) {
+    const int j = base + t;
+    const uint64_t w = j < a.V ? sib_chain(sib_weight(prow[j]), sib_weight(qrow[j]), rounds, s_hSA, s_hS, SB)
+                               : 0ull;
+    uint64_t incl = w;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t lo = __shfl_up((uint32_t)incl, o, 64), hi = __shfl_up((uint32_t)(incl >> 32), o, 64);
+      if (lane >= o) incl += ((uint64_t)hi << 32) | lo;
+    }
+    if (lane == 63) s_wt[wave] = incl;
+    __syncthreads();
+    uint64_t off = before, tile = 0;
+    for (int w2 = 0; w2 < SIB_WAVES; ++w2) {
+      if (w2 < wave) off += s_wt[w2];
+      tile += s_wt[w2];
+    }
+    if (w > 0 && off + incl - w <= tau && tau < off + incl) s_tok = j;
+    __syncthreads();
+    if (s_tok >= 0) break;
+    before += tile;
+  }
+  if (t == 0) {
+    a.n_accept[b] = -1;
+    a.next_token[b] = s_tok >= 0 ? s_tok : 0;
+  }
+}
+
 size_t verify_workspace(int B, int gamma, int V) {
   const size_t nch = (size_t)(V + VER_CHUNK - 1) / VER_CHUNK;
   const size_t per = std::max((size_t)16, (size_t)(gamma + 1) * sizeof(ArgMax));
@@ -338,25 +478,34 @@ extern "C" int spd_verify(int32_t B, int32_t gamma, int32_t V, float temperature
   return check_launch();
 }
 
-extern "C" int spd_verify_siblings(int32_t B, int32_t W, int32_t V, const float* p,
-                                   const int32_t* cand, int32_t* accepted, int32_t* next_token,
+extern "C" int spd_verify_siblings(int32_t B, int32_t W, int32_t V, float temperature,
+                                   const float* p, const float* q, const int32_t* cand,
+                                   const uint64_t* words, int32_t* accepted, int32_t* next_token,
                                    void* ws, size_t ws_bytes, void* stream) {
   if (B < 1 || B > 65535 || W < 1 || W > SPD_TREE_MAX_NODES || V < 1) return SPD_E_INVALID;
+  if (!(temperature >= 0.f)) return SPD_E_INVALID;
   if (!p || !cand || !accepted || !next_token || !ws || !aligned16(ws)) return SPD_E_INVALID;
+  if (temperature > 0.f && (!q || !words)) return SPD_E_INVALID;
   if (ws_bytes < verify_workspace(B, 0, V)) return SPD_E_WORKSPACE;
   VerArgs a{};
   a.p = p;
+  a.q = q;
   a.draft = cand;
+  a.words = words;
   a.n_accept = accepted;
   a.next_token = next_token;
   a.part = static_cast<char*>(ws) + SPD_WS_COUNTER_BYTES;
   a.B = B;
-  a.gamma = 0;  // the chunk pass reads one target row per sequence
+  a.gamma = 0;  // the greedy chunk pass reads one target row per sequence
   a.bonus = 1;
   a.V = V;
   a.nchunks = (V + VER_CHUNK - 1) / VER_CHUNK;
   a.W = W;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (temperature > 0.f) {
+    hipLaunchKernelGGL(verify_siblings_sampled_kernel, dim3(B), dim3(SIB_THREADS), 0, st, a);
+    return check_launch();
+  }
   hipLaunchKernelGGL(verify_greedy_chunks_kernel, dim3(a.nchunks, B), dim3(VER_THREADS), 0, st, a);
   int rc = check_launch();
   if (rc) return rc;

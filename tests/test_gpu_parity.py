@@ -537,13 +537,53 @@ def test_verify_siblings_greedy():
                      device=DEV)
     acc = torch.full((B,), -7, dtype=torch.int32, device=DEV)
     nxt = torch.full((B,), -7, dtype=torch.int32, device=DEV)
-    spd.spd_verify_siblings(B, W, V, logits, cand_d, acc, nxt, ws)
+    spd.spd_verify_siblings(B, W, V, 0.0, logits, None, cand_d, None, acc, nxt, ws)
     torch.cuda.synchronize()
     lc = logits.cpu().numpy()
     for b in range(B):
         ref = O.verify_siblings(lc[b], cand[b])
         assert (int(acc[b]), int(nxt[b])) == ref, b
         assert ref[0] == (b % (W + 1) if b % (W + 1) < W else -1)
+
+
+@pytest.mark.parametrize("B,W,V,top_k", [(6, 4, 151936, 0), (4, 4, 151936, 50), (48, 3, 5000, 0),
+                                         (24, 8, 700, 20)])
+def test_verify_siblings_sampled(B, W, V, top_k):
+    """T = 1: W independent draws from q per sequence, multi-round rejection; the
+    accepted index or the replacement token equal the oracle's on the device's rows
+    and words, bit for bit.  Half the sequences get R words that force the early
+    rounds to reject, so the residual rounds and the final draw are exercised."""
+    say("verify siblings sampled", B, W, V, top_k)
+    lp = synth.normal((B, V), 3.0, device=DEV, seed=62, name="sib_p")
+    lq = lp + synth.normal((B, V), 1.0, device=DEV, seed=63, name="sib_q")
+    if top_k:
+        def filt(x):
+            th = torch.topk(x, top_k, dim=-1).values[:, -1:]
+            return torch.where(x >= th, x, torch.full_like(x, -float("inf")))
+        lp, lq = filt(lp), filt(lq)
+    p = torch.softmax(lp, -1).contiguous()
+    q = torch.softmax(lq, -1).contiguous()
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(64)
+    cand = torch.multinomial(q, W, replacement=True, generator=gen).to(torch.int32).contiguous()
+    words = synth.rand_words(65, 5, B * (W + 1) * 2).reshape(B, W + 1, 2)
+    for b in range(0, B, 2):
+        for i in range(min(W - 1, 2)):
+            words[b, i, 0] = np.uint64(((1 << 24) - 1) << 40)
+    cfg = spd.make_config(L=1, n=1, m=1, d=64, Ls=1, Hq=1, Hkv=1, hd=16, dff=64, V=V, dtype=0)
+    ws = torch.zeros(spd.spd_workspace_size(spd.SPD_CALL_VERIFY, cfg, B, 0), dtype=torch.uint8,
+                     device=DEV)
+    acc = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+    nxt = torch.full((B,), -7, dtype=torch.int32, device=DEV)
+    spd.spd_verify_siblings(B, W, V, 1.0, p, q, cand, synth.words_tensor(words, DEV), acc, nxt, ws)
+    torch.cuda.synchronize()
+    pc, qc, cc = p.cpu().numpy(), q.cpu().numpy(), cand.cpu().numpy()
+    hist = {"accepted": 0, "replaced": 0}
+    for b in range(B):
+        ref = O.verify_siblings_sampled(pc[b], qc[b], cc[b], words[b])
+        assert (int(acc[b]), int(nxt[b])) == ref, b
+        hist["accepted" if ref[0] >= 0 else "replaced"] += 1
+    assert hist["replaced"] > 0 or B < 8
 
 
 # ------------------------------------------------------------------ verify
