@@ -365,33 +365,58 @@ L = row16_sum(L);
     if (j == 0) s_L[row] = L;
   }
   __syncthreads();
-  // output: each thread owns 4 consecutive dims of a row; 8 chunk partials in flight
+  // output: a thread owns NI items of 4 consecutive dims of a row; the partials of up
+  // to CB chunks of all its items are in flight together (one round trip for
+  // contexts up to CB * ATT_KC keys)
   constexpr int D4 = HD / 4;
-  for (int e = threadIdx.x; e < 16 * D4; e += 256) {
+  constexpr int NI = (16 * D4 + 255) / 256;
+  constexpr int CB = 16;
+  int rowv[NI], nvv[NI], dimv[NI], qrv[NI];
+  uint32_t basev[NI];
+  int nvmax = 0;
+#pragma unroll
+  for (int ii = 0; ii < NI; ++ii) {
+    const int e = threadIdx.x + 256 * ii;
     const int row = e / D4, dim = (e - row * D4) * 4;
     const int qr = 16 * qt + row;
-    if (qr >= QR) continue;
-    const int r = qr / G;
-    const int nv = (a.pos0 + r) / ATT_KC + 1;
-    const uint32_t base = (uint32_t)(((((size_t)h * QR + qr) * a.nch) * HD + dim) * 4);
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int c0 = 0; c0 < nv; c0 += 8) {
-      float4 pv[8];
+    const bool ok = e < 16 * D4 && qr < QR;
+    const int qc = ok ? qr : 16 * qt;  // a valid row of the tile for the unused items
+    rowv[ii] = ok ? row : 0;
+    dimv[ii] = ok ? dim : 0;
+    qrv[ii] = ok ? qr : -1;
+    nvv[ii] = ok ? (a.pos0 + qr / G) / ATT_KC + 1 : 0;
+    basev[ii] = (uint32_t)(((((size_t)h * QR + qc) * a.nch) * HD + (ok ? dim : 0)) * 4);
+    nvmax = max(nvmax, nvv[ii]);
+  }
+  float4 acc[NI];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        pv[i] = ld_coh4(a.po, base + (uint32_t)((c0 + i < nv ? c0 + i : 0) * HD * 4));
+  for (int ii = 0; ii < NI; ++ii) acc[ii] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c0 = 0; c0 < nvmax; c0 += CB) {
+    float4 pv[NI][CB];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float wgt = c0 + i < nv ? s_w[row][c0 + i] : 0.f;
-        o.x += pv[i].x * wgt;
-        o.y += pv[i].y * wgt;
-        o.z += pv[i].z * wgt;
-        o.w += pv[i].w * wgt;
+    for (int ii = 0; ii < NI; ++ii)
+#pragma unroll
+      for (int i = 0; i < CB; ++i)
+        pv[ii][i] = ld_coh4(a.po, basev[ii] + (uint32_t)((c0 + i < nvv[ii] ? c0 + i : 0) * HD * 4));
+#pragma unroll
+    for (int ii = 0; ii < NI; ++ii)
+#pragma unroll
+      for (int i = 0; i < CB; ++i) {
+        const float wgt = c0 + i < nvv[ii] ? s_w[rowv[ii]][c0 + i] : 0.f;
+        acc[ii].x += pv[ii][i].x * wgt;
+        acc[ii].y += pv[ii][i].y * wgt;
+        acc[ii].z += pv[ii][i].z * wgt;
+        acc[ii].w += pv[ii][i].w * wgt;
       }
-    }
-    const float il = 1.0f / s_L[row];
-    const XSplit<WT> xo{static_cast<WT*>(a.xh), static_cast<WT*>(a.xl), a.xld};
-    xo.put4(r, (h * G + qr % G) * HD + dim, make_float4(o.x * il, o.y * il, o.z * il, o.w * il));
+  }
+  const XSplit<WT> xo{static_cast<WT*>(a.xh), static_cast<WT*>(a.xl), a.xld};
+#pragma unroll
+  for (int ii = 0; ii < NI; ++ii) {
+    const int qr = qrv[ii];
+    if (qr < 0) continue;
+    const float il = 1.0f / s_L[rowv[ii]];
+    xo.put4(qr / G, (h * G + qr % G) * HD + dimv[ii],
+            make_float4(acc[ii].x * il, acc[ii].y * il, acc[ii].z * il, acc[ii].w * il));
   }
   SPD_MARK(6);
 }
