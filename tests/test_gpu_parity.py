@@ -243,6 +243,12 @@ LM_CASES = [
     ("full_rows3", 151936, 2560, 1, 3.0 / np.sqrt(2560), 3, 1.0),
     ("9b_t1", 151936, 4096, 1, 3.0 / np.sqrt(4096), 1, 1.0),
     ("ragged_v", 151936 - 37, 2560, 1, 3.0 / np.sqrt(2560), 1, 1.0),
+    # several hidden rows share one pass over the head (skinny MFMA GEMM path)
+    ("full_rows2", 151936, 2560, 1, 3.0 / np.sqrt(2560), 2, 1.0),
+    ("full_rows4_t0", 151936, 2560, 1, 0.02, 4, 0.0),
+    ("9b_rows3", 151936, 4096, 1, 3.0 / np.sqrt(4096), 3, 0.8),
+    ("9b_rows4", 151936, 4096, 1, 3.0 / np.sqrt(4096), 4, 1.0),
+    ("ragged_rows4", 151936 - 37, 2560, 1, 3.0 / np.sqrt(2560), 4, 1.0),
 ]
 
 
