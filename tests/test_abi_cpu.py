@@ -156,3 +156,35 @@ def test_argument_errors_return_before_any_launch():
     rc = lib.spd_rollback(None, 4, fake, fake, fake, fake, 64, None)
     assert rc == spd.SPD_E_INVALID
     assert spd.status_string(spd.SPD_E_WORKSPACE) == "workspace too small"
+
+
+def test_tree_and_sibling_argument_errors():
+    """The draft-tree calls reject bad masks pointers, node counts, output counts and
+    candidate counts on the host."""
+    lib = spd.lib()
+    s = synth.TINY
+    c = _cfg(s)
+    tab = (ctypes.c_int32 * ((s.n + 1) * s.m))(*([0] * ((s.n + 1) * s.m)))
+    fake = 1 << 40
+    for anc, M, a in ((None, 5, 2), (fake + 4, 5, 2), (fake, spd.SPD_TREE_MAX_NODES + 1, 2),
+                      (fake, 5, 0)):
+        rc = lib.spd_fuse_features_tree(ctypes.byref(c), fake, 256, 3, tab, 0, M, a, anc, fake,
+                                        fake, fake, fake, 1 << 30, None)
+        assert rc == spd.SPD_E_INVALID, (anc, M, a)
+    lw = (spd.spd_layer_weights * 1)()
+    for k, _ in spd.spd_layer_weights._fields_:
+        setattr(lw[0], k, fake)
+    for anc, M, n_out in ((None, 5, 1), (fake + 2, 5, 1), (fake, 65, 1), (fake, 5, 0), (fake, 5, 6)):
+        rc = lib.spd_pdm_step_tree(ctypes.byref(c), lw, fake, fake, fake, 256, fake, 0, M, anc,
+                                   n_out, fake, fake, 1 << 30, None)
+        assert rc == spd.SPD_E_INVALID, (anc, M, n_out)
+    for B, W, T, q, words in ((0, 4, 0.0, None, None), (1, 0, 0.0, None, None),
+                              (1, spd.SPD_TREE_MAX_NODES + 1, 0.0, None, None),
+                              (1, 4, 1.0, None, fake), (1, 4, 1.0, fake, None),
+                              (1, 4, -1.0, fake, fake)):
+        rc = lib.spd_verify_siblings(B, W, 100, ctypes.c_float(T), fake, q, fake, words, fake,
+                                     fake, fake, 1 << 30, None)
+        assert rc == spd.SPD_E_INVALID, (B, W, T)
+    rc = lib.spd_verify_siblings(1, 4, 100, ctypes.c_float(0.0), fake, None, fake, None, fake,
+                                 fake, fake, 16, None)
+    assert rc == spd.SPD_E_WORKSPACE
