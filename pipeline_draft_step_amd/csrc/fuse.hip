@@ -242,7 +242,7 @@ static FusePlan plan_fuse(const spd_config* cfg, int M) {
   const int es = bf ? 2 : 4;
   const size_t K = (size_t)cfg->m * cfg->d;
   p.big = plan_big(cfg, M);
-  p.gp = plan_gemm(cfg->d, (int)K, M, kstep, es, 1);
+  p.gp = plan_gemm(cfg->d, (int)K, M, kstep, es, 1, 256);  // about one block per CU (measured)
   p.ncb = (int)((K + GATHER_COLS - 1) / GATHER_COLS);
   size_t off = SPD_WS_COUNTER_BYTES;
   auto take = [&](size_t b) { size_t r = off; off = align256(off + b); return r; };

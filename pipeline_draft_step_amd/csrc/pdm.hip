@@ -752,10 +752,12 @@ static PdmPlan plan_pdm(const spd_config* c, int M, int64_t T_cap) {
   const bool bf = c->dtype == SPD_BF16;
   const int ks = bf ? Mfma<bf16>::KSTEP : Mfma<float>::KSTEP;
   const int es = bf ? 2 : 4;
-  p.qkv = plan_gemm((c->Hq + 2 * c->Hkv) * c->hd, c->d, M, ks, es, 2);
-  p.o = plan_gemm(c->d, c->Hq * c->hd, M, ks, es, 1);
-  p.gu = plan_gemm(2 * c->dff, c->d, M, ks, es, 2);
-  p.down = plan_gemm(c->d, c->dff, M, ks, es, 1);
+  // grid targets measured at the 2560-wide shape: about one block per CU for the
+  // products over the hidden size, two for the down projection (rows of dff)
+  p.qkv = plan_gemm((c->Hq + 2 * c->Hkv) * c->hd, c->d, M, ks, es, 2, 256);
+  p.o = plan_gemm(c->d, c->Hq * c->hd, M, ks, es, 1, 256);
+  p.gu = plan_gemm(2 * c->dff, c->d, M, ks, es, 2, 256);
+  p.down = plan_gemm(c->d, c->dff, M, ks, es, 1, 512);
   p.nch = (int)((T_cap + ATT_KC - 1) / ATT_KC);
   p.QR = M * (c->Hq / c->Hkv);
   size_t off = SPD_WS_COUNTER_BYTES;
