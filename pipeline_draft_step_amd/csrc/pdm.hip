@@ -241,7 +241,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
       if (key > lim || key >= nkeys || off_path) sc[ks][i] = -INFINITY;
       m_ = fmaxf(m_, sc[ks][i]);
     }
-m_ = row16_max(m_);
+    m_ = row16_max(m_);
     float s_ = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -249,7 +249,7 @@ m_ = row16_max(m_);
       sc[ks][i] = p;
       s_ += p;
     }
-s_ = row16_sum(s_);
+    s_ = row16_sum(s_);
     mx[i] = m_;
     sm[i] = s_;
   }
@@ -352,7 +352,7 @@ s_ = row16_sum(s_);
     float mmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) mmax = fmaxf(mmax, v[i].x);
-mmax = row16_max(mmax);
+    mmax = row16_max(mmax);
     float L = 0.f;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
@@ -361,7 +361,7 @@ mmax = row16_max(mmax);
       s_w[row][cc] = wgt;
       L += v[i].y * wgt;
     }
-L = row16_sum(L);
+    L = row16_sum(L);
     if (j == 0) s_L[row] = L;
   }
   __syncthreads();
