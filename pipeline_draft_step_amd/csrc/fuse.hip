@@ -63,6 +63,7 @@ template <typename WT>
 __global__ __launch_bounds__(256) void feature_gather_kernel(GatherArgs<WT> f) {
   __shared__ int8_t s_tab[TABN];
   __shared__ float s_red[4];
+  __builtin_amdgcn_s_setprio(3);  // decode chain first on a shared SIMD (as in the GEMMs)
   SPD_MARK(0);
   if (threadIdx.x == 0) {
     // the table is copied with constant indices: a dynamically indexed kernel

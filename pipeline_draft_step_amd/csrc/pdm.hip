@@ -38,6 +38,7 @@ __global__ __launch_bounds__(64) void rows_init_kernel(const float* g, float* h,
                                                        int d, XSplit<WT> xo, const WT* gamma,
                                                        float2* rope, int pos0, int hd, float theta,
                                                        const uint64_t* anc) {
+  __builtin_amdgcn_s_setprio(3);  // decode chain first on a shared SIMD (as in the GEMMs)
   const int nb = blockIdx.x, r = blockIdx.y, lane = threadIdx.x;
   if (nb == 0 && lane < hd / 2) {
     // a draft-tree node sits at its level (number of proper ancestors), a chain row at r
@@ -153,6 +154,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   __shared__ float Ob[ATT_WAVES][16][HD + 4];
   __shared__ float2 Ml[ATT_WAVES][16];
 
+  __builtin_amdgcn_s_setprio(3);  // decode chain first on a shared SIMD (as in the GEMMs)
   const int c = blockIdx.x, h = blockIdx.y, qt = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int G = a.Hq / a.Hkv, QR = a.M * G;

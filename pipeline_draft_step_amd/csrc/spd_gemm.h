@@ -196,6 +196,9 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_skinny_kernel(GemmShape g, 
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ float s_rs[32];  // row scales of the tile
 
+  // the decode chain is latency-bound and shares the chip with a head streaming on
+  // another stream: its waves issue first on a shared SIMD
+  __builtin_amdgcn_s_setprio(3);
   const int S = g.S;
   const int nb = blockIdx.x / S;
   const int s = blockIdx.x - nb * S;
