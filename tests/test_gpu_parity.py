@@ -419,6 +419,7 @@ TREE_CASES = [
     ("tiny_w4_a4_no_prefix", synth.TINY, 4, 4, 0),
     ("headline_w4_a7", synth.HEADLINE, 4, 7, None),
     ("headline_w4_a8_two_row_tiles", synth.HEADLINE, 4, 8, None),
+    ("small_w9_a7_max_nodes", SMALL_BF16, 9, 7, None),          # 64 nodes: the mask limit
 ]
 
 
