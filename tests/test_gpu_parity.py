@@ -739,6 +739,66 @@ def test_cycle_trajectory_tiny(schedule):
         cache.truncate(ost.t - 1 - ost.a)
 
 
+@pytest.mark.parametrize("top_k,top_p", [(0, 1.0), (50, 1.0), (20, 0.8)],
+                         ids=["full_softmax", "top_k50", "top_k20_p08"])
+def test_cycle_trajectory_tiny_sampled(top_k, top_p):
+    """A T = 1 device-state trajectory with rejections and rollbacks: every draft is
+    the oracle's draw from the device's (filtered) q row, every verification the
+    oracle's decision on the device's p and ring q rows, the kept sets are the
+    oracle's filters of the device's logits, and the state matches the oracle state
+    machine after every cycle."""
+    s = synth.TINY.with_(top_k=top_k, top_p=top_p)
+    ci = synth.cycle_inputs(s, device=DEV, T_cap=128)
+    model = device_model(ci)
+    cyc = SpdCycle(model, 1.0)
+    om = OC.model_from_inputs(ci)
+    t0 = s.ctx
+    ost = O.SeqState(t=t0, a=s.n, tokens=list(range(t0)))
+    cyc.set_state(t0, s.n, ost.tokens)
+    cyc.prefill(t0 - 1 - s.n)
+    cache = OC.prefill(om, t0, s.n)
+    # q rows of the tokens already in flight (drafted before the trajectory starts)
+    seed_logits = synth.normal((s.n, s.V), 3.0, device="cpu", seed=91, name="ring_seed")
+    for r in range(s.n):
+        row = O.filtered_softmax(seed_logits[r].double().numpy(), 1.0, top_k, top_p)
+        cyc.ring[r].copy_(torch.from_numpy(row.astype(np.float32)))
+    wb = synth.cycle_words(40, seed=17)
+    wdev = synth.words_tensor(wb, DEV)
+    verified = rejected = 0
+    for c in range(40):
+        t, a = ost.t, ost.a
+        say("sampled trajectory cycle", c, t, a)
+        cand = t - s.n + 1
+        q_cand = cyc.ring[cand % s.n].cpu().numpy().copy() if a == s.n else None
+        cyc.cycle(t, a, wdev[c])
+        torch.cuda.synchronize()
+        gq = cyc.ring[t % s.n].cpu().numpy()
+        gp = cyc.p.cpu().numpy() if a == s.n else None
+        probs_from = {"q": gq} if gp is None else {"q": gq, "p": gp}
+        out = OC.run_cycle(om, O.SeqState(t=t, a=a, tokens=list(ost.tokens)), cache, {}, 1.0, wb[c],
+                           q_override=q_cand, probs_from=probs_from)
+        assert rel_err(f64(cyc.h_last), out.h_last) < TOL_F32
+        dl = cyc.dlogits.cpu().numpy()
+        assert rel_err(dl, out.draft_logits) < TOL_F32
+        dref = O.filtered_softmax(dl.astype(np.float64), 1.0, top_k, top_p)
+        assert np.array_equal(np.flatnonzero(gq), np.flatnonzero(dref))
+        assert int(cyc.dtoken.item()) == out.drafted
+        if a == s.n:
+            verified += 1
+            rejected += out.n_accept == 0
+            tl = cyc.tlogits.cpu().numpy()
+            assert rel_err(tl, out.target_logits) < TOL_F32
+            tref = O.filtered_softmax(tl.astype(np.float64), 1.0, top_k, top_p)
+            assert np.array_equal(np.flatnonzero(gp), np.flatnonzero(tref))
+            assert (int(cyc.n_accept.item()), int(cyc.next_token.item())) == (out.n_accept,
+                                                                             out.next_token)
+        O.transition(ost, s.n, out.drafted, a == s.n, out.n_accept, out.next_token)
+        assert cyc.read_state() == (ost.t, ost.a, ost.commits, ost.cycles)
+        assert cyc.tokens[:ost.t].tolist() == ost.tokens
+        cache.truncate(ost.t - 1 - ost.a)
+    assert verified >= 5 and rejected >= 1      # rollbacks are exercised
+
+
 @pytest.mark.parametrize("top_k,top_p", [(0, 1.0), (50, 1.0), (50, 0.9)],
                          ids=["full_softmax", "top_k50", "top_k50_p09"])
 def test_cycle_full_headline_sampled(top_k, top_p):
