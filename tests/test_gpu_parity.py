@@ -215,6 +215,29 @@ def test_pdm_full_size_on_synthetic_cache(shape):
         _check_cache_rows(cyc, cache, pos0, pos0 + M, TOL_BF16)
 
 
+def test_cycle_calls_are_deterministic():
+    """The same feature call and PDM step twice (same inputs, same cache) give the
+    same rows, cache entries and last row bit for bit: every cross-block sum runs
+    in a fixed order whichever block arrives last."""
+    s = synth.HEADLINE
+    ci = synth.cycle_inputs(s, device=DEV, with_heads=False)
+    model = device_model(ci)
+    cyc = SpdCycle(model, s.temperature)
+    k, v = synth.kv_cache(s, model.T_cap, device=DEV)
+    a = s.n
+    pos0, M = s.ctx - 1 - a, a + 1
+    outs = []
+    for _ in range(2):
+        cyc.k_cache.copy_(k)
+        cyc.v_cache.copy_(v)
+        g = cyc.features(pos0, M, a).clone()
+        cyc.pdm(pos0, M)
+        torch.cuda.synchronize()
+        outs.append((g, cyc.h_last.clone(), cyc.k_cache.clone(), cyc.v_cache.clone()))
+    for x, y in zip(*outs):
+        assert torch.equal(x, y)
+
+
 # ------------------------------------------------------------------ LM head
 
 def _lm_case(V, d, dtype, std, rows, T, seed):
