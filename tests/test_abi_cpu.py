@@ -188,3 +188,36 @@ def test_tree_and_sibling_argument_errors():
     rc = lib.spd_verify_siblings(1, 4, 100, ctypes.c_float(0.0), fake, None, fake, None, fake,
                                  fake, fake, 16, None)
     assert rc == spd.SPD_E_WORKSPACE
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """No fallback: without libspd.so every binding raises instead of computing."""
+    monkeypatch.setattr(spd, "_lib", None)
+    monkeypatch.setattr(spd, "LIB_PATH", spd.LIB_PATH + ".absent")
+    with pytest.raises(RuntimeError, match="missing"):
+        spd.lib()
+    with pytest.raises(RuntimeError, match="missing"):
+        spd.spd_layout(32, 4, 4)
+    with pytest.raises(RuntimeError, match="missing"):
+        spd.spd_slot_table(_cfg(synth.TINY), synth.TINY.anchors)
+
+
+def test_product_package_never_reaches_the_oracle():
+    """The package and bench's timed path import nothing from oracle/ (only the
+    tests, smoke() and the CPU-baseline leg may)."""
+    import ast
+    import os
+    pkg = os.path.dirname(spd.__file__)
+    for root, _, files in os.walk(pkg):
+        for f in files:
+            if not f.endswith(".py"):
+                continue
+            tree = ast.parse(open(os.path.join(root, f)).read())
+            for node in ast.walk(tree):
+                names = []
+                if isinstance(node, ast.Import):
+                    names = [a.name for a in node.names]
+                elif isinstance(node, ast.ImportFrom):
+                    names = [node.module or ""]
+                for n in names:
+                    assert not n.split(".")[0] == "oracle", (f, n)
