@@ -14,8 +14,8 @@ Pages cited (by title and section; the text of each page is the authority):
 
 * [SPD]   "Speculative Pipeline Decoding: Higher-Accuracy Drafting with Hidden
           Latency via Pipeline Parallelism" (arXiv 2605.30852), sections 3.1-3.4
-          and 4 (metrics).  Its display equations were lost in extraction; the
-          readings used below are listed in the design doc.
+          and 4 (metrics).  Its display equations were lost in extraction; each
+          function below states the reading of the prose it takes.
 * [REV]   The xllm-io paper-review blog post on the same paper, section
           "核心公式" (core formulas) and "验证与回滚机制" (verification and rollback).
 * [SD]    "Speculative Decoding: How Draft-Model Parallelism Cuts LLM Inference
@@ -330,7 +330,9 @@ def pdm_step(g_rows, pos0, cache: PdmCache, layers, final_norm, c: PdmConfig):
 # Draft trees ([SPD] 4, draft-tree paragraph, and Appendix B: width-W trees raise
 # acceptance; [REV] draft-tree paragraphs).  The pages measure trees only in
 # theory and leave branched KV caches and tree attention masks open; the
-# readings below are this oracle's and are listed in the design doc.
+# readings below are this oracle's own: the tree is the staircase with branches
+# (level l holds in-flight tokens at depth a - l), each node keeps its own
+# key/value slot, and a node attends to the committed prefix and its root path.
 # --------------------------------------------------------------------------
 
 def tree_levels(anc):
