@@ -86,6 +86,8 @@ def cpu_baseline(s, ci, sched, words, qstand_np, x, budget_s=12.0):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
+    if ci.store_layers != O.store_layers_for(s.L, s.n, s.anchors, s.anchor_mode):
+        raise RuntimeError("anchor store layers differ between the library and the oracle")
     om = OC.model_from_inputs(ci)
     k, v = synth.kv_cache(s, ci.T_cap, device=ci.store.device)
     kk = k.float().cpu().numpy().astype(np.float64)
@@ -137,7 +139,9 @@ def main():
     spd.lib()
     dev = "cuda"
     s = synth.HEADLINE
-    ci = synth.cycle_inputs(s, device=dev)
+    cfg0 = spd.make_config(L=s.L, n=s.n, m=s.m, d=s.d, Ls=s.Ls, Hq=s.Hq, Hkv=s.Hkv, hd=s.hd, dff=s.dff,
+                           V=s.V, dtype=s.dtype, anchor_mode=s.anchor_mode, norm_k0=s.norm_k0)
+    ci = synth.cycle_inputs(s, spd.spd_slot_table(cfg0, list(s.anchors))[1], device=dev)
     w = DeviceWeights(store=ci.store, h_final=ci.h_final, fc_norm=ci.fc_norm, w_fc=ci.w_fc,
                       layers=ci.layers, final_norm=ci.final_norm, w_dlm=ci.w_dlm, w_tlm=ci.w_tlm)
     model = SpdModel(L=s.L, n=s.n, anchors=s.anchors, d=s.d, Ls=s.Ls, Hq=s.Hq, Hkv=s.Hkv,

@@ -168,22 +168,14 @@ def layer_weights(s: SpdShape, li: int, *, device, seed):
     }
 
 
-def store_layers(s: SpdShape):
-    """Target layers the anchor store holds: the anchors themselves, plus, in the
-    clamped mode, every stage boundary a clamped slot can read."""
-    if s.anchor_mode == ZERO_MASK:
-        return list(s.anchors)
-    layers = set(s.anchors)
-    for k in range(1, s.n + 1):
-        lm = min(s.L, (k * s.L) // s.n)
-        layers.update(min(b, lm) for b in s.anchors)
-    return sorted(layers)
-
-
-def cycle_inputs(s: SpdShape, *, device, seed=0, T_cap=None, with_heads=True) -> CycleInputs:
+def cycle_inputs(s: SpdShape, store_layers, *, device, seed=0, T_cap=None, with_heads=True) -> CycleInputs:
+    """Seeded weights and target states of shape `s`.  `store_layers` lists the
+    target layers the anchor store holds, in slot order; it is the caller's (the
+    oracle's or the library's slot table), so that this module does none of the
+    method's arithmetic."""
     dt = storage_dtype(s.dtype)
     T_cap = int(T_cap or (s.ctx + 64))
-    sl = store_layers(s)
+    sl = [int(x) for x in store_layers]
     store = normal((T_cap, len(sl), s.d), 1.0, device=device, seed=seed + 1, name="anchors", dtype=dt)
     h_final = normal((T_cap, s.d), 1.0, device=device, seed=seed + 1, name="h_final")
     ci = CycleInputs(

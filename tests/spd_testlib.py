@@ -18,6 +18,14 @@ def header_functions():
     return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(spd_\w+)\s*\(", src, flags=re.M)))
 
 
+def make_inputs(shape, **kw):
+    """synth.cycle_inputs with the anchor store's layers taken from the oracle."""
+    import synth
+    from oracle import spd as O
+    return synth.cycle_inputs(shape, O.store_layers_for(shape.L, shape.n, shape.anchors, shape.anchor_mode),
+                              **kw)
+
+
 def ensure_built():
     import pipeline_draft_step_amd as spd
     if not os.path.exists(spd.LIB_PATH):

@@ -15,7 +15,7 @@ import torch
 import synth
 from oracle import cycle as OC
 from oracle import spd as O
-from spd_testlib import TOL_BF16, TOL_F32, ensure_built, f64, rel_err, tol_for
+from spd_testlib import TOL_BF16, TOL_F32, ensure_built, f64, make_inputs, rel_err, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -71,7 +71,7 @@ FUSE_CASES = [
 
 @pytest.mark.parametrize("name,shape,layouts", FUSE_CASES, ids=[c[0] for c in FUSE_CASES])
 def test_fuse_features(name, shape, layouts):
-    ci = synth.cycle_inputs(shape, device=DEV, with_heads=False)
+    ci = make_inputs(shape, device=DEV, with_heads=False)
     model = device_model(ci)
     cyc = SpdCycle(model, shape.temperature)
     om = OC.model_from_inputs(ci, with_heads=False)
@@ -106,7 +106,7 @@ def test_fuse_features_prefill(name, shape, M, nsample):
     split-K partial tiles, ragged M and N tiles.  The full headline product is
     checked on sampled rows (tile edges included), which the oracle computes one
     by one."""
-    ci = synth.cycle_inputs(shape, device=DEV, with_heads=False)
+    ci = make_inputs(shape, device=DEV, with_heads=False)
     model = device_model(ci)
     cyc = SpdCycle(model, shape.temperature)
     om = OC.model_from_inputs(ci, with_heads=False)
@@ -161,7 +161,7 @@ def test_pdm_prefill_then_cycle(shape):
     path (MFMA-tiled GEMMs with bf16 activations, row kernels for the
     epilogues): 311 rows at d = 256 and the headline's 2039 rows at d = 2560,
     every cache row and the final row checked."""
-    ci = synth.cycle_inputs(shape, device=DEV, with_heads=False)
+    ci = make_inputs(shape, device=DEV, with_heads=False)
     model = device_model(ci)
     cyc = SpdCycle(model, shape.temperature)
     om = OC.model_from_inputs(ci, with_heads=False)
@@ -194,7 +194,7 @@ def test_pdm_prefill_then_cycle(shape):
 def test_pdm_full_size_on_synthetic_cache(shape):
     """Full-size PDM step at context t: the committed cache holds seeded values
     (an input of the call), the M new rows are checked against the oracle."""
-    ci = synth.cycle_inputs(shape, device=DEV, with_heads=False)
+    ci = make_inputs(shape, device=DEV, with_heads=False)
     model = device_model(ci)
     cyc = SpdCycle(model, shape.temperature)
     om = OC.model_from_inputs(ci, with_heads=False)
@@ -220,7 +220,7 @@ def test_cycle_calls_are_deterministic():
     same rows, cache entries and last row bit for bit: every cross-block sum runs
     in a fixed order whichever block arrives last."""
     s = synth.HEADLINE
-    ci = synth.cycle_inputs(s, device=DEV, with_heads=False)
+    ci = make_inputs(s, device=DEV, with_heads=False)
     model = device_model(ci)
     cyc = SpdCycle(model, s.temperature)
     k, v = synth.kv_cache(s, model.T_cap, device=DEV)
@@ -453,7 +453,7 @@ def test_tree_features_and_pdm_step(name, shape, W, a, pos0):
     rows and every node's cache slot against the oracle.  The short-prefix cases
     make the tree's own keys dominate attention, so a wrong mask or position
     cannot hide inside the tolerance."""
-    ci = synth.cycle_inputs(shape, device=DEV, with_heads=False)
+    ci = make_inputs(shape, device=DEV, with_heads=False)
     model = device_model(ci)
     cyc = SpdCycle(model, shape.temperature)
     om = OC.model_from_inputs(ci, with_heads=False)
@@ -499,7 +499,7 @@ def test_tree_features_and_pdm_step(name, shape, W, a, pos0):
 def test_tree_pdm_chain_matches_causal_step():
     """A chain given as tree masks is the ordinary step, bit for bit."""
     shape = SMALL_BF16
-    ci = synth.cycle_inputs(shape, device=DEV, with_heads=False)
+    ci = make_inputs(shape, device=DEV, with_heads=False)
     model = device_model(ci)
     cyc = SpdCycle(model, shape.temperature)
     k, v = synth.kv_cache(shape, model.T_cap, device=DEV)
@@ -725,7 +725,7 @@ def test_cycle_trajectory_tiny(schedule):
     state after every cycle matches the oracle state machine.  Run under each
     feature schedule (the prefill and every cycle's features follow it)."""
     s = synth.TINY.with_(feature_schedule=schedule)
-    ci = synth.cycle_inputs(s, device=DEV, T_cap=128)
+    ci = make_inputs(s, device=DEV, T_cap=128)
     model = device_model(ci)
     cyc = SpdCycle(model, 0.0)
     om = OC.model_from_inputs(ci)
@@ -771,7 +771,7 @@ def test_cycle_trajectory_tiny_sampled(top_k, top_p):
     oracle's filters of the device's logits, and the state matches the oracle state
     machine after every cycle."""
     s = synth.TINY.with_(top_k=top_k, top_p=top_p)
-    ci = synth.cycle_inputs(s, device=DEV, T_cap=128)
+    ci = make_inputs(s, device=DEV, T_cap=128)
     model = device_model(ci)
     cyc = SpdCycle(model, 1.0)
     om = OC.model_from_inputs(ci)
@@ -831,7 +831,7 @@ def test_cycle_full_headline_sampled(top_k, top_p):
     and the state update bit-exact on the device's rows.  With the sampling
     filters on, the draft and target rows keep exactly the oracle's sets."""
     s = synth.HEADLINE.with_(top_k=top_k, top_p=top_p)
-    ci = synth.cycle_inputs(s, device=DEV)
+    ci = make_inputs(s, device=DEV)
     model = device_model(ci)
     cyc = SpdCycle(model, 1.0)
     om = OC.model_from_inputs(ci)

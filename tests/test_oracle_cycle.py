@@ -7,6 +7,7 @@ import numpy as np
 import synth
 from oracle import cycle as C
 from oracle import spd as O
+from spd_testlib import make_inputs
 
 
 def _full_recompute_draft(om, st_before):
@@ -21,7 +22,7 @@ def _full_recompute_draft(om, st_before):
 
 def test_tiny_trajectory_matches_full_recompute():
     s = synth.TINY
-    ci = synth.cycle_inputs(s, device="cpu", seed=0, T_cap=96)
+    ci = make_inputs(s, device="cpu", seed=0, T_cap=96)
     om = C.model_from_inputs(ci)
     t0 = s.ctx
     st = O.SeqState(t=t0, a=s.n, tokens=list(range(t0)))
@@ -43,7 +44,7 @@ def test_tiny_trajectory_matches_full_recompute():
 
 def test_sampled_cycle_uses_ring_row():
     s = synth.TINY.with_(temperature=1.0)
-    ci = synth.cycle_inputs(s, device="cpu", seed=1, T_cap=96)
+    ci = make_inputs(s, device="cpu", seed=1, T_cap=96)
     om = C.model_from_inputs(ci)
     st = O.SeqState(t=s.ctx, a=1, tokens=list(range(s.ctx)))
     cache = C.prefill(om, st.t, st.a)
