@@ -215,6 +215,27 @@ def test_pdm_full_size_on_synthetic_cache(shape):
         _check_cache_rows(cyc, cache, pos0, pos0 + M, TOL_BF16)
 
 
+@pytest.mark.parametrize("shape", [synth.TINY, SMALL_BF16, synth.HEADLINE],
+                         ids=["tiny", "small_bf16", "headline"])
+def test_pdm_step_with_empty_committed_prefix(shape):
+    """The first cycle of a sequence: pos0 = 0, so nothing is committed and the M
+    rows attend only to each other (M = 1: a row attending to itself alone)."""
+    ci = make_inputs(shape, device=DEV, with_heads=False)
+    model = device_model(ci)
+    cyc = SpdCycle(model, shape.temperature)
+    om = OC.model_from_inputs(ci, with_heads=False)
+    tol = tol_for(shape.dtype)
+    for M in (1, shape.n + 1):
+        say(shape.name, "pdm empty prefix", M)
+        g = synth.normal((M, shape.d), 1.0, device=DEV, seed=20 + M, name="rows0")
+        cyc.pdm(0, M, g=g)
+        torch.cuda.synchronize()
+        cache = O.PdmCache(shape.Ls, om.pdm)
+        last, _ = O.pdm_step(f64(g), 0, cache, om.layers, om.final_norm, om.pdm)
+        assert rel_err(f64(cyc.h_last), last) < tol, M
+        _check_cache_rows(cyc, cache, 0, M, tol)
+
+
 def test_cycle_calls_are_deterministic():
     """The same feature call and PDM step twice (same inputs, same cache) give the
     same rows, cache entries and last row bit for bit: every cross-block sum runs
@@ -272,6 +293,9 @@ LM_CASES = [
     ("9b_rows3", 151936, 4096, 1, 3.0 / np.sqrt(4096), 3, 0.8),
     ("9b_rows4", 151936, 4096, 1, 3.0 / np.sqrt(4096), 4, 1.0),
     ("ragged_rows4", 151936 - 37, 2560, 1, 3.0 / np.sqrt(2560), 4, 1.0),
+    # the most rows one call takes (16: one full MFMA row tile)
+    ("tiny_rows16_t0", 512, 64, 0, 0.02, 16, 0.0),
+    ("full_rows16_t1", 151936, 2560, 1, 3.0 / np.sqrt(2560), 16, 1.0),
 ]
 
 
