@@ -296,6 +296,9 @@ LM_CASES = [
     # the most rows one call takes (16: one full MFMA row tile)
     ("tiny_rows16_t0", 512, 64, 0, 0.02, 16, 0.0),
     ("full_rows16_t1", 151936, 2560, 1, 3.0 / np.sqrt(2560), 16, 1.0),
+    # near one-hot and near flat distributions
+    ("full_t_low", 151936, 2560, 1, 3.0 / np.sqrt(2560), 1, 0.05),
+    ("full_t_high", 151936, 2560, 1, 3.0 / np.sqrt(2560), 2, 20.0),
 ]
 
 
