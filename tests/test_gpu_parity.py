@@ -52,9 +52,10 @@ SMALL_BF16_H64 = SMALL_BF16.with_(name="small_bf16_hd64", Hq=8, Hkv=2, hd=64, d=
 
 # ------------------------------------------------------------------ features
 
+# (t, a) layouts; t = a + 1 is a sequence's first cycle (pos0 = 0), a = 0 a prefill of t rows
 FUSE_CASES = [
-    ("tiny", synth.TINY, [(32, 4), (32, 1), (32, 3), (28, 0)]),
-    ("small_zero", SMALL_BF16, [(96, 8), (96, 3), (96, 1), (80, 0)]),
+    ("tiny", synth.TINY, [(32, 4), (32, 1), (32, 3), (28, 0), (5, 4), (2, 1), (1, 0)]),
+    ("small_zero", SMALL_BF16, [(96, 8), (96, 3), (96, 1), (80, 0), (9, 8)]),
     ("small_clamp", SMALL_BF16.with_(anchor_mode=synth.CLAMP_MIN), [(96, 8), (96, 5)]),
     ("small_normk0", SMALL_BF16.with_(norm_k0=1), [(96, 8), (96, 2)]),
     # feature-schedule variants (slot-table switches, no kernel change)
@@ -64,7 +65,7 @@ FUSE_CASES = [
      [(96, 8), (96, 4)]),
     ("tiny_post_step", synth.TINY.with_(feature_schedule=1), [(32, 4), (32, 2)]),
     ("headline_post_step", synth.HEADLINE.with_(feature_schedule=1), [(2048, 8), (2048, 3)]),
-    ("headline", synth.HEADLINE, [(2048, 8), (2048, 3), (2048, 1)]),
+    ("headline", synth.HEADLINE, [(2048, 8), (2048, 3), (2048, 1), (9, 8), (2, 1)]),
     ("9b", synth.SHAPES["qwen35_9b_n16_ls4_t1"], [(4096, 16)]),
 ]
 
