@@ -161,7 +161,8 @@ size_t spd_workspace_size(int32_t call, const spd_config *cfg, int32_t rows, int
  * hstore  DEVICE [T_cap][S][d]  anchor hidden states, slot s holds store_layers[s]
  * slot_tab HOST [(n+1)*m]       as written by spd_slot_table (any table of slots < S)
  * norm_w  DEVICE [m*d]; fc_w DEVICE [d][m*d]; g DEVICE float [M][d] (output).
- * Requires d % 64 == 0, pos0 >= 0, pos0+M <= T_cap, 0 <= a <= min(n, M).
+ * Requires d % 64 == 0, pos0 >= 0, pos0+M <= T_cap, 0 <= a <= min(n, M); SPD_E_UNSUPPORTED
+ * when d % 64 != 0 or m*d > 262144.
  */
 int spd_fuse_features(const spd_config *cfg, const void *hstore, int64_t T_cap, int32_t S,
                       const int32_t *slot_tab, int32_t pos0, int32_t M, int32_t a,

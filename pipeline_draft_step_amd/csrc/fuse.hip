@@ -113,21 +113,15 @@ __global__ __launch_bounds__(256) void feature_gather_kernel(GatherArgs<WT> f) {
   sq = wave_sum(sq);
   if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = sq;
   __syncthreads();
-  if (threadIdx.x == 0)
-    st_coh(f.part + (size_t)cb * gridDim.y + r, (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]));
-  SPD_MARK(4);
-  if (!arrive_last(f.counters + r, (unsigned)f.ncb)) return;
-  SPD_MARK(5);
-  if (threadIdx.x < 64) {
-    float t = 0.f;
-    for (int q = threadIdx.x; q < f.ncb; q += 64) t += ld_coh(f.part + (size_t)q * gridDim.y + r);
-    t = wave_sum(t);
-    if (threadIdx.x == 0) {
-      int filled = 0;
+  if (threadIdx.x == 0) {
+    // this block's share of the row's mean square over the eligible slots; the
+    // product kernel adds the ncb shares (a row without norm leaves -1 in share 0)
+    int filled = 0;
 #pragma unroll
-      for (int j = 0; j < SPD_MAX_ANCHORS; ++j) filled += (j < f.m && s_tab[k * f.m + j] >= 0) ? 1 : 0;
-      f.inv[r] = plain ? 1.f : (filled > 0 ? 1.0f / sqrtf(t / (float)(filled * f.d) + f.eps) : 0.f);
-    }
+    for (int j = 0; j < SPD_MAX_ANCHORS; ++j) filled += (j < f.m && s_tab[k * f.m + j] >= 0) ? 1 : 0;
+    const float blk = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
+    f.part[(size_t)cb * gridDim.y + r] =
+        plain ? (cb == 0 ? -1.f : 0.f) : (filled > 0 ? blk / (float)(filled * f.d) : 0.f);
   }
 }
 
@@ -319,8 +313,12 @@ static int fuse_impl(const spd_config* cfg, const void* hstore, int64_t T_cap, i
   gs.part = reinterpret_cast<float*>(w + p.off_gpart);
   gs.nblocks = p.gp.nblocks;
   gs.counters = reinterpret_cast<unsigned*>(w);
-  gs.rs_inv = ga.inv;
-  InSplit<WT, RS_INV> in{ga.xo.hi, ga.xo.lo, m * d};
+  gs.rs_ss = ga.part;
+  gs.rs_P = p.ncb;
+  gs.rs_M = M;
+  gs.rs_K = 1;
+  gs.rs_eps = cfg->rms_eps;
+  InSplit<WT, RS_SSR> in{ga.xo.hi, ga.xo.lo, m * d};
   return launch_gemm<WT, 1>(p.gp, gs, in, EpiRows{g, d}, RowMapStd{}, st);
 }
 
@@ -339,6 +337,8 @@ static int fuse_entry(const spd_config* cfg, const void* hstore, int64_t T_cap, 
   if (a < 0 || a > cfg->n || a > M) return SPD_E_INVALID;
   if (M >= CTR_FINAL) return SPD_E_UNSUPPORTED;  // one arrival counter per row (and per GEMM tile)
   if (cfg->d % 64) return SPD_E_UNSUPPORTED;
+  // the product kernel reduces at most 128 gather blocks' shares per row
+  if ((int64_t)cfg->m * cfg->d > (int64_t)128 * GATHER_COLS) return SPD_E_UNSUPPORTED;
   for (int i = 0; i < (cfg->n + 1) * cfg->m; ++i)
     if (slot_tab[i] < -1 || slot_tab[i] >= S) return SPD_E_INVALID;
   if (!aligned16(hstore) || !aligned16(fc_w) || !aligned16(norm_w) || !aligned16(g) ||

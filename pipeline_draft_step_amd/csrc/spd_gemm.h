@@ -49,7 +49,9 @@ struct GemmShape {
   int x_bytes;         // dynamic LDS: staged X slice (hi + lo), aliased by the
   int ytile_bytes;     // fp32 result tile; the transpose buffers follow both
   // optional per-row scale of the product: 1 / sqrt(sum_p rs_ss[p][row] / rs_K + rs_eps)
-  // (the RMSNorm of an input whose gamma the producer has already applied)
+  // (the RMSNorm of an input whose gamma the producer has already applied); in the
+  // per-row form (RS_SSR) the partials are already divided by the row's own width
+  // and a negative sum marks a row that is not normalised (scale 1)
   const float* rs_ss;  // [rs_P][rs_M] partial sums of squares
   int rs_P, rs_M, rs_K;
   float rs_eps;
@@ -132,8 +134,9 @@ struct TwoPhase<T, std::void_t<decltype(T::kTwoPhase)>> : std::bool_constant<T::
 // (RW = 4 * MT of them); the partial sums are loaded first (load) and reduced
 // into s_rs (finish).
 // Row-scale mode, a compile-time property of the input functor (kRowScale):
-// none, from partial sums of squares (rs_ss), or given per row (rs_inv).
-enum { RS_NONE = 0, RS_SS = 1, RS_INV = 2 };
+// none, from partial sums of squares (rs_ss), from partial mean squares with a
+// per-row width (rs_ss, RS_SSR), or given per row (rs_inv).
+enum { RS_NONE = 0, RS_SS = 1, RS_INV = 2, RS_SSR = 3 };
 template <typename T, typename = void>
 struct RowScaleOf : std::integral_constant<int, RS_NONE> {};
 template <typename T>
@@ -147,7 +150,7 @@ struct RowScale {
     if constexpr (RS == RS_INV) {
 #pragma unroll
       for (int j = 0; j < RW; ++j) p[j][0] = g.rs_inv[m0 + min(wave + GEMM_WAVES * j, Mt - 1)];
-    } else if constexpr (RS == RS_SS) {
+    } else if constexpr (RS == RS_SS || RS == RS_SSR) {
 #pragma unroll
       for (int j = 0; j < RW; ++j) {
         const int mm = wave + GEMM_WAVES * j;
@@ -172,6 +175,11 @@ struct RowScale {
         const float a = (mm < Mt && lane < g.rs_P) ? p[j][0] : 0.f;
         const float b = (mm < Mt && lane + WAVE < g.rs_P) ? p[j][1] : 0.f;
         v = 1.0f / sqrtf(wave_sum(a + b) / (float)g.rs_K + g.rs_eps);
+      } else if constexpr (RS == RS_SSR) {
+        const float a = (mm < Mt && lane < g.rs_P) ? p[j][0] : 0.f;
+        const float b = (mm < Mt && lane + WAVE < g.rs_P) ? p[j][1] : 0.f;
+        const float t = wave_sum(a + b);
+        v = t < 0.f ? 1.f : 1.0f / sqrtf(t + g.rs_eps);
       }
       if (lane == 0) s_rs[mm] = v;
     }
