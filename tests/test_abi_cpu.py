@@ -220,3 +220,45 @@ def test_product_package_never_reaches_the_oracle():
                     names = [node.module or ""]
                 for n in names:
                     assert not n.split(".")[0] == "oracle", (f, n)
+
+
+# ---- property tests: the library's host helpers against the oracle on drawn configurations
+from hypothesis import given, settings, strategies as st  # noqa: E402
+
+
+@st.composite
+def _eligibility_configs(draw):
+    L = draw(st.integers(1, 96))
+    n = draw(st.integers(1, min(32, 4 * L)))
+    m = draw(st.integers(1, min(8, L + 1)))
+    rest = sorted(draw(st.sets(st.integers(1, L), min_size=m - 1, max_size=m - 1))) if m > 1 else []
+    anchors = [0] + rest
+    mode = draw(st.sampled_from([O.ZERO_MASK, O.CLAMP_MIN]))
+    schedule = draw(st.sampled_from([O.PRE_STEP, O.POST_STEP, O.FIRST_STAGE]))
+    return L, n, anchors, mode, schedule
+
+
+@settings(max_examples=300, deadline=None)
+@given(_eligibility_configs())
+def test_slot_table_matches_oracle_on_drawn_configs(c):
+    L, n, anchors, mode, schedule = c
+    cfg = spd.make_config(L=L, n=n, m=len(anchors), d=64, Ls=1, Hq=1, Hkv=1, hd=16, dff=64, V=64,
+                          dtype=0, anchor_mode=mode, feature_schedule=schedule)
+    tab, layers = spd.spd_slot_table(cfg, anchors)
+    assert layers == O.store_layers_for(L, n, anchors, mode)
+    m = len(anchors)
+    for k in range(n + 1):
+        want = O.slot_layers(O.feature_depth(k, n, schedule), L, n, anchors, mode)
+        got = [layers[x] if x >= 0 else -1 for x in tab[k * m:(k + 1) * m]]
+        assert got == want, (k, got, want)
+
+
+@settings(max_examples=300, deadline=None)
+@given(st.integers(1, 32).flatmap(lambda n: st.tuples(st.just(n), st.integers(1, n),
+                                                      st.integers(0, 5000))))
+def test_layout_matches_oracle_on_drawn_cycles(c):
+    n, a, extra = c
+    t = a + 1 + extra
+    pos, dep = spd.spd_layout(t, a, n)
+    pos0, opos, odep = O.cycle_rows(t, a, n)
+    assert pos == opos and dep == odep and pos[0] == pos0
