@@ -719,6 +719,58 @@ def test_verify_streaming_edge_cases():
             assert (int(na[0]), int(nt[0])) == ref
 
 
+def _drawn_row(rng, V):
+    """A float32 probability row of one of several shapes: smooth, sparse (exact
+    zeros), tied (few distinct values), or spanning tiny values."""
+    kind = int(rng.integers(0, 4))
+    if kind == 0:
+        x = rng.normal(0, 3, V)
+    elif kind == 1:
+        x = np.where(rng.random(V) < 0.8, -np.inf, rng.normal(0, 2, V))
+        x[int(rng.integers(0, V))] = 0.0
+    elif kind == 2:
+        x = rng.integers(0, 3, V).astype(np.float64)
+    else:
+        x = rng.normal(0, 30, V)
+    e = np.exp(x - x.max())
+    return (e / e.sum()).astype(np.float32)
+
+
+def test_verify_streaming_drawn_rows_bitexact():
+    """Streaming verify (B = 1, gamma = 1) on 200 drawn small-vocabulary cases: the
+    device's (accepted, next token) equals the oracle's decision on the same fp32 rows
+    and words, bit for bit; the draft token is sometimes one q gives zero mass."""
+    rng = np.random.default_rng(77)
+    say("verify drawn rows")
+    for case in range(200):
+        V = int(rng.integers(1, 3000))
+        p, q = _drawn_row(rng, V), _drawn_row(rng, V)
+        x = int(rng.integers(0, V))
+        words = rng.integers(0, 2 ** 64, size=(1, 2, 2), dtype=np.uint64)
+        na, nt = _verify_gpu(torch.tensor(p, device=DEV).reshape(1, 1, V),
+                             torch.tensor(q, device=DEV).reshape(1, 1, V),
+                             torch.tensor([[x]], dtype=torch.int32, device=DEV), words, 1.0, 0)
+        ref = O.verify([p], [q], [x], words[0], temperature=1.0, bonus=False)
+        assert (int(na[0]), int(nt[0])) == ref, (case, V, x)
+
+
+def test_verify_greedy_drawn_rows_bitexact():
+    """Greedy verify (T = 0) on 100 drawn logit rows with many ties: accepted iff the
+    draft is the lowest-index argmax, the correction that argmax."""
+    rng = np.random.default_rng(78)
+    say("verify greedy drawn rows")
+    for case in range(100):
+        V = int(rng.integers(1, 5000))
+        logits = rng.integers(-3, 3, V).astype(np.float32)
+        am = O.argmax_first(logits)
+        x = am if rng.random() < 0.5 else int(rng.integers(0, V))
+        words = rng.integers(0, 2 ** 64, size=(1, 2, 2), dtype=np.uint64)
+        na, nt = _verify_gpu(torch.tensor(logits, device=DEV).reshape(1, 1, V), None,
+                             torch.tensor([[x]], dtype=torch.int32, device=DEV), words, 0.0, 0)
+        ref = O.verify([logits], None, [x], words[0], temperature=0.0, bonus=False)
+        assert (int(na[0]), int(nt[0])) == ref, (case, V, x)
+
+
 # ------------------------------------------------------------------ rollback
 
 def test_rollback_state_machine():
