@@ -433,6 +433,42 @@ def test_lm_head_top_k_ties_break_by_index(V, top_k):
     assert torch.equal(p2, probs) and torch.equal(t2, tok)
 
 
+def test_lm_head_drawn_shapes():
+    """60 drawn head calls: vocabulary sizes that are ragged against the GEMV's row
+    groups and the 2048-entry sampling chunks, several widths, row counts,
+    temperatures and filters; logits within tolerance, every decision exact."""
+    rng = np.random.default_rng(91)
+    say("lm_head drawn shapes")
+    for case in range(60):
+        V = int(rng.integers(1, 9000))
+        d = int(rng.choice([64, 128, 192]))
+        dtype = int(rng.integers(0, 2))
+        rows = int(rng.integers(1, 7))
+        T = float(rng.choice([0.0, 0.3, 1.0, 3.0]))
+        top_k = int(rng.integers(1, 257)) if (T > 0 and rng.random() < 0.5) else (1 if rng.random() < 0.2 else 0)
+        top_p = float(rng.uniform(0.3, 0.99)) if (top_k > 0 and T > 0 and rng.random() < 0.5) else 1.0
+        W = synth.normal((V, d), 2.0 / np.sqrt(d), device=DEV, seed=100 + case, name="w_lm",
+                         dtype=synth.storage_dtype(dtype))
+        h = synth.normal((rows, d), 1.0, device=DEV, seed=100 + case, name="h")
+        words, logits, probs, tok = _run_lm(W, h, V, d, dtype, rows, T, 100 + case, top_k, top_p)
+        Wh, hh = f64(W), f64(h)
+        for r in range(rows):
+            assert rel_err(f64(logits[r]), O.lm_logits(Wh, hh[r])) < tol_for(dtype), (case, r)
+        if T == 0:
+            toks = tok.cpu().numpy()
+            for r in range(rows):
+                assert toks[r] == O.argmax_first(logits[r].cpu().numpy()), (case, r)
+        elif top_k > 0:
+            _check_filtered(words, logits, probs, tok, T, top_k, top_p)
+        else:
+            toks = tok.cpu().numpy()
+            for r in range(rows):
+                gp = probs[r].cpu().numpy()
+                pref = O.softmax(logits[r].cpu().numpy().astype(np.float64), T)
+                assert np.max(np.abs(gp - pref)) <= 1e-5 * pref.max(), (case, r)
+                assert toks[r] == O.sample_probs(gp, int(words[r]) >> 32), (case, r)
+
+
 # ------------------------------------------------------------------ draft trees
 
 def _width_tree(W, a):
