@@ -237,6 +237,47 @@ def test_pdm_step_with_empty_committed_prefix(shape):
         _check_cache_rows(cyc, cache, 0, M, tol)
 
 
+def test_pdm_drawn_shapes():
+    """16 drawn decoder configurations (fp32 and bf16; head sizes 16..128, GQA ratios
+    1..4, widths, 1-2 layers, 1-40 rows over one or two row tiles, committed prefixes
+    0..300) on a seeded committed cache: last row and the new cache rows within
+    tolerance of the oracle."""
+    rng = np.random.default_rng(123)
+    for case in range(16):
+        dtype = int(rng.integers(0, 2))
+        hd = int(rng.choice([32, 64, 128] if dtype == synth.BF16 else [16, 32, 64, 128]))
+        Hkv = int(rng.integers(1, 4))
+        Hq = Hkv * int(rng.choice([1, 2, 4]))
+        while (Hq * hd) % 32:
+            Hq += Hkv
+        d = 64 * int(rng.integers(1, 5))
+        dff = 64 * int(rng.integers(1, 9))
+        Ls = int(rng.integers(1, 3))
+        M = int(rng.integers(1, 41))
+        pos0 = int(rng.integers(0, 301))
+        T_cap = (pos0 + M + 15) // 8 * 8
+        shape = synth.SpdShape(f"drawn{case}", L=8, n=4, anchors=(0, 4, 7), d=d, Ls=Ls, Hq=Hq, Hkv=Hkv,
+                               hd=hd, dff=dff, V=64, dtype=dtype, ctx=pos0 + M, temperature=0.0,
+                               lm_std=0.02)
+        say("pdm drawn", case, dict(dtype=dtype, d=d, Ls=Ls, Hq=Hq, Hkv=Hkv, hd=hd, dff=dff, M=M,
+                                    pos0=pos0))
+        ci = make_inputs(shape, device=DEV, with_heads=False, T_cap=T_cap, seed=case)
+        model = device_model(ci)
+        cyc = SpdCycle(model, 0.0)
+        om = OC.model_from_inputs(ci, with_heads=False)
+        k, v = synth.kv_cache(shape, model.T_cap, device=DEV, seed=50 + case)
+        cyc.k_cache.copy_(k)
+        cyc.v_cache.copy_(v)
+        g = synth.normal((M, d), 1.0, device=DEV, seed=60 + case, name="rows")
+        cyc.pdm(pos0, M, g=g)
+        torch.cuda.synchronize()
+        cache = _oracle_cache_from(k, v, pos0, shape)
+        last, _ = O.pdm_step(f64(g), pos0, cache, om.layers, om.final_norm, om.pdm)
+        tol = tol_for(dtype)
+        assert rel_err(f64(cyc.h_last), last) < tol, case
+        _check_cache_rows(cyc, cache, pos0, pos0 + M, tol)
+
+
 def test_cycle_calls_are_deterministic():
     """The same feature call and PDM step twice (same inputs, same cache) give the
     same rows, cache entries and last row bit for bit: every cross-block sum runs
