@@ -91,6 +91,42 @@ def test_fuse_features(name, shape, layouts):
         assert err < tol_for(shape.dtype), (t, a, err)
 
 
+def test_fuse_features_drawn_configs():
+    """20 drawn feature configurations (anchor sets, both anchor modes, the three
+    schedules, norm_k0, fp32/bf16, widths, in-flight counts and prefixes, including
+    a sequence's first cycle) against the oracle."""
+    rng = np.random.default_rng(321)
+    for case in range(20):
+        L = int(rng.integers(2, 40))
+        n = int(rng.integers(1, min(16, L) + 1))
+        m = int(rng.integers(1, min(8, L + 1) + 1))
+        anchors = tuple([0] + sorted(rng.choice(np.arange(1, L + 1), size=m - 1, replace=False).tolist()))
+        mode = int(rng.integers(0, 2))
+        sched = int(rng.integers(0, 3))
+        dtype = int(rng.integers(0, 2))
+        d = 64 * int(rng.integers(1, 5))
+        a = int(rng.integers(0, n + 1))
+        t = a + 1 + int(rng.integers(0, 60)) if a > 0 else int(rng.integers(1, 41))
+        shape = synth.SpdShape(f"fdrawn{case}", L=L, n=n, anchors=anchors, d=d, Ls=1, Hq=1, Hkv=1,
+                               hd=16, dff=64, V=64, dtype=dtype, ctx=t, temperature=0.0, lm_std=0.02,
+                               anchor_mode=mode, norm_k0=int(rng.integers(0, 2)), feature_schedule=sched)
+        M = a + 1 if a > 0 else t
+        pos0 = t - 1 - a if a > 0 else 0
+        say("fuse drawn", case, dict(L=L, n=n, anchors=anchors, mode=mode, sched=sched, dtype=dtype, d=d,
+                                     t=t, a=a))
+        ci = make_inputs(shape, device=DEV, with_heads=False, T_cap=(t + 15) // 8 * 8, seed=case)
+        model = device_model(ci)
+        cyc = SpdCycle(model, 0.0)
+        om = OC.model_from_inputs(ci, with_heads=False)
+        out = torch.empty(M, d, device=DEV)
+        cyc.features(pos0, M, a, out=out)
+        torch.cuda.synchronize()
+        ref = O.fuse_features(om.store, om.store_layers, list(range(pos0, pos0 + M)), row_depths(M, a, n),
+                              om.fc_norm, om.w_fc, L=L, n=n, anchors=anchors, mode=mode, eps=shape.eps,
+                              norm_k0=bool(shape.norm_k0), schedule=sched)
+        assert rel_err(f64(out), ref) < tol_for(dtype), case
+
+
 PREFILL_FUSE_CASES = [
     # (name, shape, M, rows checked: None = all)
     ("small_prefill", SMALL_BF16.with_(ctx=320), 300, None),
