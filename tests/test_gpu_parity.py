@@ -637,6 +637,66 @@ def test_tree_features_and_pdm_step(name, shape, W, a, pos0):
     _check_cache_rows(cyc, cache, pos0, pos0 + M, tol)
 
 
+def _random_tree(rng, M, a):
+    """Parents of a random tree of M nodes (topological order, root 0) whose levels
+    stay within a."""
+    parents, level = [-1], [0]
+    for i in range(1, M):
+        cand = [j for j in range(i) if level[j] < a]
+        p = int(rng.choice(cand))
+        parents.append(p)
+        level.append(level[p] + 1)
+    return parents
+
+
+def test_tree_drawn_shapes():
+    """12 random trees (arbitrary branching, 2..64 nodes, levels up to a, committed
+    prefixes from empty upward) on three small workloads: features of every node,
+    the last n_out final rows and every node's cache slot against the oracle."""
+    rng = np.random.default_rng(555)
+    shapes = [synth.TINY, SMALL_BF16, SMALL_BF16_H64]
+    for case in range(12):
+        shape = shapes[case % 3]
+        ci = make_inputs(shape, device=DEV, with_heads=False, T_cap=shape.ctx + 64, seed=case)
+        model = device_model(ci)
+        cyc = SpdCycle(model, shape.temperature)
+        om = OC.model_from_inputs(ci, with_heads=False)
+        a = int(rng.integers(1, shape.n + 1))
+        M = int(rng.integers(2, min(64, model.T_cap) + 1))
+        anc = _masks(_random_tree(rng, M, a))
+        pos0 = int(rng.integers(0, model.T_cap - M + 1))
+        n_out = int(rng.integers(1, min(M, 8) + 1))
+        say("tree drawn", case, shape.name, dict(M=M, a=a, pos0=pos0, n_out=n_out))
+        dev_anc = _anc_tensor(anc)
+        ws = torch.zeros(max(spd.spd_workspace_size(spd.SPD_CALL_FUSE, model.cfg, M),
+                             spd.spd_workspace_size(spd.SPD_CALL_PDM, model.cfg, M, 0, model.T_cap)),
+                         dtype=torch.uint8, device=DEV)
+        g = torch.empty(M, shape.d, device=DEV)
+        spd.spd_fuse_features_tree(model.cfg, model.w.store, model.T_cap, len(model.store_layers),
+                                   model.slot_tab, pos0, M, a, dev_anc, model.w.fc_norm, model.w.w_fc, g,
+                                   ws)
+        torch.cuda.synchronize()
+        rows, depth, _ = O.tree_rows(anc, a, shape.n, pos0)
+        ref = O.fuse_features(om.store, om.store_layers, rows, depth, om.fc_norm, om.w_fc, L=shape.L,
+                              n=shape.n, anchors=shape.anchors, mode=shape.anchor_mode, eps=shape.eps,
+                              norm_k0=bool(shape.norm_k0), schedule=shape.feature_schedule)
+        tol = tol_for(shape.dtype)
+        assert rel_err(f64(g), ref) < tol, case
+        k, v = synth.kv_cache(shape, model.T_cap, device=DEV, seed=80 + case)
+        cyc.k_cache.copy_(k)
+        cyc.v_cache.copy_(v)
+        gin = synth.normal((M, shape.d), 1.0, device=DEV, seed=90 + case, name="tree_rows")
+        h_out = torch.empty(n_out, shape.d, device=DEV)
+        spd.spd_pdm_step_tree(model.cfg, model.layer_arr, model.w.final_norm, cyc.k_cache, cyc.v_cache,
+                              model.T_cap, gin, pos0, M, dev_anc, n_out, h_out, ws)
+        torch.cuda.synchronize()
+        cache = _oracle_cache_from(k, v, pos0, shape)
+        ref_rows, _ = O.pdm_step_tree(f64(gin), pos0, cache, om.layers, om.final_norm, om.pdm, anc)
+        for o in range(n_out):
+            assert rel_err(f64(h_out[o]), ref_rows[M - n_out + o]) < tol, (case, o)
+        _check_cache_rows(cyc, cache, pos0, pos0 + M, tol)
+
+
 def test_tree_pdm_chain_matches_causal_step():
     """A chain given as tree masks is the ordinary step, bit for bit."""
     shape = SMALL_BF16
