@@ -817,6 +817,34 @@ def test_verify_siblings_sampled(B, W, V, top_k):
     assert hist["replaced"] > 0 or B < 8
 
 
+def test_verify_siblings_sampled_drawn_rows():
+    """80 drawn sequences of small vocabularies (smooth, sparse, tied and
+    wide-range rows from _drawn_row), W = 1..8 candidates, some outside q's
+    support, random and forced-reject words: bit-exact against the oracle."""
+    rng = np.random.default_rng(606)
+    say("verify siblings drawn rows")
+    for case in range(80):
+        V = int(rng.integers(1, 3000))
+        W = int(rng.integers(1, 9))
+        p, q = _drawn_row(rng, V), _drawn_row(rng, V)
+        cand = rng.integers(0, V, size=W).astype(np.int32)
+        words = rng.integers(0, 2 ** 64, size=(1, W + 1, 2), dtype=np.uint64)
+        if rng.random() < 0.5:
+            words[0, :, 0] = np.uint64(((1 << 24) - 1) << 40)   # every round's test at its hardest
+        cfg = spd.make_config(L=1, n=1, m=1, d=64, Ls=1, Hq=1, Hkv=1, hd=16, dff=64, V=V, dtype=0)
+        ws = torch.zeros(spd.spd_workspace_size(spd.SPD_CALL_VERIFY, cfg, 1, 0), dtype=torch.uint8,
+                         device=DEV)
+        acc = torch.full((1,), -7, dtype=torch.int32, device=DEV)
+        nxt = torch.full((1,), -7, dtype=torch.int32, device=DEV)
+        spd.spd_verify_siblings(1, W, V, 1.0, torch.tensor(p, device=DEV).reshape(1, V),
+                                torch.tensor(q, device=DEV).reshape(1, V),
+                                torch.tensor(cand, device=DEV).reshape(1, W),
+                                synth.words_tensor(words, DEV), acc, nxt, ws)
+        torch.cuda.synchronize()
+        ref = O.verify_siblings_sampled(p, q, cand, words[0])
+        assert (int(acc[0]), int(nxt[0])) == ref, (case, V, W)
+
+
 # ------------------------------------------------------------------ verify
 
 def _verify_gpu(p, q, draft, words, T, bonus):
