@@ -972,6 +972,38 @@ def test_verify_greedy_drawn_rows_bitexact():
         assert (int(na[0]), int(nt[0])) == ref, (case, V, x)
 
 
+def test_verify_gamma_form_drawn_bitexact():
+    """40 drawn batched verifications (B = 1..12 sequences of gamma = 1..8 drafts,
+    with and without the bonus row, T = 1 on drawn probability rows and T = 0 on
+    tied integer logits): every (accepted count, next token) equals the oracle's."""
+    rng = np.random.default_rng(707)
+    say("verify gamma drawn")
+    for case in range(40):
+        B, G, V = int(rng.integers(1, 13)), int(rng.integers(1, 9)), int(rng.integers(1, 2000))
+        bonus = int(rng.integers(0, 2))
+        T = float(rng.choice([0.0, 1.0]))
+        if T > 0:
+            p = np.stack([np.stack([_drawn_row(rng, V) for _ in range(G + bonus)]) for _ in range(B)])
+            q = np.stack([np.stack([_drawn_row(rng, V) for _ in range(G)]) for _ in range(B)])
+            qd = torch.tensor(q, device=DEV)
+        else:
+            p = rng.integers(-2, 3, size=(B, G + bonus, V)).astype(np.float32)
+            q, qd = None, None
+        draft = rng.integers(0, V, size=(B, G)).astype(np.int32)
+        if T == 0:
+            for b in range(B):                      # long accepted runs as well
+                k = int(rng.integers(0, G + 1))
+                for j in range(k):
+                    draft[b, j] = O.argmax_first(p[b, j])
+        words = rng.integers(0, 2 ** 64, size=(B, G + 1, 2), dtype=np.uint64)
+        na, nt = _verify_gpu(torch.tensor(p, device=DEV), qd, torch.tensor(draft, device=DEV), words, T,
+                             bonus)
+        for b in range(B):
+            ref = O.verify(p[b], None if q is None else q[b], draft[b], words[b], temperature=T,
+                           bonus=bool(bonus))
+            assert (int(na[b]), int(nt[b])) == ref, (case, b)
+
+
 # ------------------------------------------------------------------ rollback
 
 def test_rollback_state_machine():
