@@ -314,6 +314,60 @@ def test_pdm_drawn_shapes():
         _check_cache_rows(cyc, cache, pos0, pos0 + M, tol)
 
 
+def test_large_m_drawn_shapes():
+    """Prefill-sized calls on the large-M MFMA path at drawn, ragged sizes: 4 feature
+    calls (256..700 rows, anchor counts 2..5, widths 64..256) checked on every row,
+    and 4 decoder steps (256..600 rows after a committed prefix of 0..200, head size
+    128, GQA 1..4, 1-2 layers) checked on the last row and every new cache row."""
+    rng = np.random.default_rng(808)
+    for case in range(4):
+        m = int(rng.integers(2, 6))
+        anchors = tuple([0] + sorted(rng.choice(np.arange(1, 33), size=m - 1, replace=False).tolist()))
+        d = 64 * int(rng.integers(1, 5))
+        M = int(rng.integers(256, 701))
+        shape = synth.SpdShape(f"bigf{case}", L=32, n=8, anchors=anchors, d=d, Ls=1, Hq=1, Hkv=1, hd=16,
+                               dff=64, V=64, dtype=synth.BF16, ctx=M, temperature=0.0, lm_std=0.02)
+        say("large-M fuse drawn", case, dict(m=m, d=d, M=M))
+        ci = make_inputs(shape, device=DEV, with_heads=False, T_cap=(M + 15) // 8 * 8, seed=case)
+        model = device_model(ci)
+        cyc = SpdCycle(model, 0.0)
+        om = OC.model_from_inputs(ci, with_heads=False)
+        out = torch.empty(M, d, device=DEV)
+        cyc.features(0, M, 0, out=out)
+        torch.cuda.synchronize()
+        ref = O.fuse_features(om.store, om.store_layers, list(range(M)), [shape.n] * M, om.fc_norm,
+                              om.w_fc, L=shape.L, n=shape.n, anchors=anchors, mode=0, eps=shape.eps,
+                              norm_k0=False, schedule=0)
+        assert rel_err(f64(out), ref) < TOL_BF16, case
+    for case in range(4):
+        Hkv = int(rng.integers(1, 3))
+        Hq = Hkv * int(rng.choice([1, 2, 4]))
+        d = 128 * int(rng.integers(1, 4))
+        dff = 128 * int(rng.integers(1, 5))
+        Ls = int(rng.integers(1, 3))
+        M = int(rng.integers(256, 601))
+        pos0 = int(rng.integers(0, 201))
+        T_cap = (pos0 + M + 15) // 8 * 8
+        shape = synth.SpdShape(f"bigp{case}", L=8, n=4, anchors=(0, 4, 7), d=d, Ls=Ls, Hq=Hq, Hkv=Hkv,
+                               hd=128, dff=dff, V=64, dtype=synth.BF16, ctx=pos0 + M, temperature=0.0,
+                               lm_std=0.02)
+        say("large-M pdm drawn", case, dict(Hq=Hq, Hkv=Hkv, d=d, dff=dff, Ls=Ls, M=M, pos0=pos0))
+        ci = make_inputs(shape, device=DEV, with_heads=False, T_cap=T_cap, seed=10 + case)
+        model = device_model(ci)
+        cyc = SpdCycle(model, 0.0)
+        om = OC.model_from_inputs(ci, with_heads=False)
+        k, v = synth.kv_cache(shape, model.T_cap, device=DEV, seed=20 + case)
+        cyc.k_cache.copy_(k)
+        cyc.v_cache.copy_(v)
+        g = synth.normal((M, d), 1.0, device=DEV, seed=30 + case, name="big_rows")
+        cyc.pdm(pos0, M, g=g)
+        torch.cuda.synchronize()
+        cache = _oracle_cache_from(k, v, pos0, shape)
+        last, _ = O.pdm_step(f64(g), pos0, cache, om.layers, om.final_norm, om.pdm)
+        assert rel_err(f64(cyc.h_last), last) < TOL_BF16, case
+        _check_cache_rows(cyc, cache, pos0, pos0 + M, TOL_BF16)
+
+
 def test_cycle_calls_are_deterministic():
     """The same feature call and PDM step twice (same inputs, same cache) give the
     same rows, cache entries and last row bit for bit: every cross-block sum runs
