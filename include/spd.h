@@ -296,7 +296,10 @@ int spd_pdm_step_tree(const spd_config *cfg, const spd_layer_weights *layers,
  *   s = max(0, bitlength of its sum - 52), the residual max(0, p_i - q) as the next
  *   target.  After W rejections next_token is the inverse-CDF draw from A with
  *   u = words[b][W][1] >> 32 (from floor(p 2^51) if A is empty).  The output token is
- *   distributed as p.  One block per sequence; cost grows with W^2 passes over V.
+ *   distributed as p.  Batches of fewer than 64 sequences spread every pass over the
+ *   vocabulary across many workgroups (one launch per pass, 1 + 2W launches; a sequence
+ *   that is decided makes the remaining launches return at once); larger batches use
+ *   one workgroup per sequence.  The decisions are the same either way.
  * cand DEVICE int32 [B][W] (W <= SPD_TREE_MAX_NODES); accepted, next_token DEVICE int32
  * [B].  ws >= spd_workspace_size(SPD_CALL_VERIFY, cfg with this V, B, 0, 0).  The W
  * candidates of a greedy tree node come from spd_lm_head at T = 0 with cfg.top_k = W. */

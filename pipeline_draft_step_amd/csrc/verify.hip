@@ -429,10 +429,269 @@ __global__ __launch_bounds__(SIB_THREADS) void verify_siblings_sampled_kernel(Ve
   }
 }
 
+// ---------------------------------------------------------------------------
+// The same verification spread over many blocks per sequence, for small batches
+// (one block per sequence would leave the GPU idle).  Each pass over the
+// vocabulary is one launch over (chunk of SIB_CHUNK entries, sequence); the last
+// block of a sequence to arrive adds the chunk partials in chunk order (exact
+// integer sums, so the order does not change them) and does the pass's scalar
+// work: the totals and the first accept test, a round's shift, or the round's new
+// total with the next accept test -- after the last round, the final draw, whose
+// chunk totals are the partials it has just added.  A sequence that has finished
+// makes the later launches return at once.  The decisions are the single-block
+// kernel's, bit for bit.
+constexpr int SIB_CHUNK = 1024;
+constexpr int SIB_MB_THREADS = 256;
+constexpr int SIB_PER = SIB_CHUNK / SIB_MB_THREADS;  // entries per thread (contiguous)
+constexpr int SIB_MULTI_MAX_B = 64;  // batches below this use the multi-block form
+
+struct SibState {
+  uint64_t SA0, SB;
+  uint64_t hSA[SPD_TREE_MAX_NODES + 1];  // total of round i's target weights
+  int32_t hS[SPD_TREE_MAX_NODES];        // shift applied after round i
+  int32_t done;                          // 1: accepted[b] / next_token[b] are final
+  int32_t pad;
+};
+enum { SIB_PASS_TOT = 0, SIB_PASS_D = 1, SIB_PASS_A = 2 };
+
+inline size_t sib_state_bytes(int B) { return align256((size_t)B * sizeof(SibState)); }
+inline size_t sib_part_bytes(int B, int V) {
+  const size_t nch = (size_t)(V + SIB_CHUNK - 1) / SIB_CHUNK;
+  return (size_t)B * 4 * nch * 16;  // sa, sb, d, a partials (128-bit) per chunk
+}
+
+__device__ u128 sib_block_sum256(u128 v, u128* red) {
+  uint64_t lo = (uint64_t)v, hi = (uint64_t)(v >> 64);
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const uint64_t olo = shfl_xor_u64(lo, m), ohi = shfl_xor_u64(hi, m);
+    const uint64_t nlo = lo + olo;
+    hi = hi + ohi + (nlo < lo ? 1ull : 0ull);
+    lo = nlo;
+  }
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ((u128)hi << 64) | lo;
+  __syncthreads();
+  u128 t = 0;
+  for (int w = 0; w < SIB_MB_THREADS / 64; ++w) t += red[w];
+  __syncthreads();
+  return t;
+}
+
+__device__ __forceinline__ void st_coh_u128(u128* p, u128 v) {
+  uint64_t* q = reinterpret_cast<uint64_t*>(p);
+  st_coh_u64(q, (uint64_t)v);
+  st_coh_u64(q + 1, (uint64_t)(v >> 64));
+}
+__device__ __forceinline__ u128 ld_coh_u128(const u128* p) {
+  const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+  return ((u128)ld_coh_u64(q + 1) << 64) | ld_coh_u64(q);
+}
+
+struct SibMulti {
+  SibState* st;      // [B]
+  u128* part;        // [B][4][nch]
+  unsigned* counters;  // [B]
+  int nch;
+};
+
+// accept test of candidate i against round i's target (weights after i rounds)
+__device__ bool sib_accept(const VerArgs& a, const SibState& s, const uint64_t* hSA, const int* hS, int b, int i) {
+  const float* prow = a.p + (size_t)b * a.V;
+  const float* qrow = a.q + (size_t)b * a.V;
+  const uint64_t* wd = a.words + (size_t)b * (a.W + 1) * 2;
+  const int x = a.draft[(size_t)b * a.W + i];
+  if (x < 0 || x >= a.V) return false;
+  const uint64_t bx = sib_weight(qrow[x]);
+  const uint64_t ax = sib_chain(sib_weight(prow[x]), bx, i, hSA, hS, s.SB);
+  const uint64_t R1 = (wd[2 * i] >> 40) + 1;
+  return (u128)R1 * bx * hSA[i] <= ((u128)ax * s.SB) << 24;
+}
+
+__global__ __launch_bounds__(SIB_MB_THREADS) void sib_pass_kernel(VerArgs a, SibMulti m, int pass, int round) {
+  __shared__ u128 s_red[SIB_MB_THREADS / 64];
+  __shared__ uint64_t s_hSA[SPD_TREE_MAX_NODES + 1];
+  __shared__ int s_hS[SPD_TREE_MAX_NODES];
+  __shared__ uint64_t s_scan[SIB_MB_THREADS];
+  __shared__ int s_tok;
+  const int c = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  SibState* st = m.st + b;
+  if (pass != SIB_PASS_TOT && st->done) return;  // written by an earlier launch
+  const uint64_t SB = pass == SIB_PASS_TOT ? 0ull : st->SB;
+  if (pass != SIB_PASS_TOT) {
+    for (int k = t; k <= round + 1 && k <= a.W; k += SIB_MB_THREADS) s_hSA[k] = st->hSA[k];
+    for (int k = t; k <= round && k < a.W; k += SIB_MB_THREADS) s_hS[k] = st->hS[k];
+  }
+  __syncthreads();
+  const float* prow = a.p + (size_t)b * a.V;
+  const float* qrow = a.q + (size_t)b * a.V;
+  const int j0 = c * SIB_CHUNK + t * SIB_PER;
+  u128 v0 = 0, v1 = 0;
+#pragma unroll
+  for (int e = 0; e < SIB_PER; ++e) {
+    const int j = j0 + e;
+    if (j >= a.V) break;
+    const uint64_t aj = sib_weight(prow[j]), bj = sib_weight(qrow[j]);
+    if (pass == SIB_PASS_TOT) {
+      v0 += aj;
+      v1 += bj;
+    } else if (pass == SIB_PASS_D) {
+      v0 += sib_resid(sib_chain(aj, bj, round, s_hSA, s_hS, SB), bj, s_hSA[round], SB);
+    } else {
+      v0 += sib_chain(aj, bj, round + 1, s_hSA, s_hS, SB);
+    }
+  }
+  u128* part = m.part + (size_t)b * 4 * m.nch;
+  const u128 t0 = sib_block_sum256(v0, s_red);
+  const u128 t1 = pass == SIB_PASS_TOT ? sib_block_sum256(v1, s_red) : (u128)0;
+  if (t == 0) {
+    if (pass == SIB_PASS_TOT) {
+      st_coh_u128(part + c, t0);
+      st_coh_u128(part + m.nch + c, t1);
+    } else {
+      st_coh_u128(part + (size_t)(pass == SIB_PASS_D ? 2 : 3) * m.nch + c, t0);
+    }
+  }
+  if (!arrive_last(m.counters + b, (unsigned)m.nch)) return;
+  // last block of this sequence: the pass's scalar work, starting with the sum of
+  // the chunk partials (every thread loads its share)
+  u128 X, Y = 0;
+  {
+    u128 x = 0, y = 0;
+    const u128* src = part + (size_t)(pass == SIB_PASS_TOT ? 0 : (pass == SIB_PASS_D ? 2 : 3)) * m.nch;
+    for (int k = t; k < m.nch; k += SIB_MB_THREADS) {
+      x += ld_coh_u128(src + k);
+      if (pass == SIB_PASS_TOT) y += ld_coh_u128(part + m.nch + k);
+    }
+    X = sib_block_sum256(x, s_red);
+    if (pass == SIB_PASS_TOT) Y = sib_block_sum256(y, s_red);
+  }
+  bool final_draw = false;
+  int rounds = 0;
+  uint64_t S = 0;
+  const u128* fpart = nullptr;
+  if (pass == SIB_PASS_TOT) {
+    if (t == 0) {
+      SibState& s = *st;
+      s.SA0 = (uint64_t)X;
+      s.SB = (uint64_t)Y;
+      s.hSA[0] = s.SA0;
+      s_hSA[0] = s.SA0;
+      const bool acc = sib_accept(a, s, s_hSA, s_hS, b, 0);
+      s.done = acc ? 1 : 0;
+      if (acc) {
+        a.n_accept[b] = 0;
+        a.next_token[b] = -1;
+      }
+    }
+    return;
+  }
+  if (pass == SIB_PASS_D) {
+    if (t == 0) {
+      const uint64_t dhi = (uint64_t)(X >> 64), dlo = (uint64_t)X;
+      const int bits = dhi ? 128 - __builtin_clzll(dhi) : (dlo ? 64 - __builtin_clzll(dlo) : 0);
+      st->hS[round] = bits > 52 ? bits - 52 : 0;
+    }
+    return;
+  }
+  // SIB_PASS_A: total of round (round + 1)'s target
+  const uint64_t SAn = (uint64_t)X;
+  if (round + 1 < a.W) {
+    if (t == 0) {
+      SibState& s = *st;
+      s.hSA[round + 1] = SAn;
+      s_hSA[round + 1] = SAn;
+      const bool acc = sib_accept(a, s, s_hSA, s_hS, b, round + 1);
+      s.done = acc ? 1 : 0;
+      if (acc) {
+        a.n_accept[b] = round + 1;
+        a.next_token[b] = -1;
+      }
+    }
+    return;
+  }
+  // every candidate rejected: inverse-CDF draw from the last residual (from p if empty)
+  final_draw = true;
+  rounds = SAn > 0 ? a.W : 0;
+  S = SAn > 0 ? SAn : st->SA0;
+  fpart = part + (size_t)(SAn > 0 ? 3 : 0) * m.nch;  // chunk totals of that distribution
+  (void)final_draw;
+  const uint64_t* wd = a.words + (size_t)b * (a.W + 1) * 2;
+  const uint64_t tau = scale_u32((uint32_t)(wd[2 * a.W + 1] >> 32), S);
+  // the chunk holding tau: thread t owns chunks [t*cpt, (t+1)*cpt); a block scan of
+  // the threads' totals gives each range's start
+  __shared__ int s_cc;
+  __shared__ uint64_t s_before;
+  if (t == 0) {
+    s_cc = -1;
+    s_tok = -1;
+  }
+  {
+    const int cpt = (m.nch + SIB_MB_THREADS - 1) / SIB_MB_THREADS;
+    uint64_t mine = 0;
+    for (int k = t * cpt; k < min((t + 1) * cpt, m.nch); ++k) mine += (uint64_t)ld_coh_u128(fpart + k);
+    s_scan[t] = mine;
+    __syncthreads();
+    for (int o = 1; o < SIB_MB_THREADS; o <<= 1) {
+      const uint64_t add = t >= o ? s_scan[t - o] : 0ull;
+      __syncthreads();
+      s_scan[t] += add;
+      __syncthreads();
+    }
+    uint64_t before = s_scan[t] - mine;
+    if (mine > 0 && before <= tau && tau < before + mine) {  // exactly one thread
+      for (int k = t * cpt; k < min((t + 1) * cpt, m.nch); ++k) {
+        const uint64_t w = (uint64_t)ld_coh_u128(fpart + k);
+        if (tau < before + w) {
+          s_cc = k;
+          s_before = before;
+          break;
+        }
+        before += w;
+      }
+    }
+  }
+  __syncthreads();
+  const int cc = s_cc;
+  if (cc >= 0) {
+    // the chunk holding tau: this thread's SIB_PER entries, then a block scan
+    uint64_t w[SIB_PER];
+    uint64_t mine = 0;
+    const int jb = cc * SIB_CHUNK + t * SIB_PER;
+#pragma unroll
+    for (int e = 0; e < SIB_PER; ++e) {
+      const int j = jb + e;
+      w[e] = j < a.V ? sib_chain(sib_weight(prow[j]), sib_weight(qrow[j]), rounds, s_hSA, s_hS, SB) : 0ull;
+      mine += w[e];
+    }
+    s_scan[t] = mine;
+    __syncthreads();
+    for (int o = 1; o < SIB_MB_THREADS; o <<= 1) {
+      const uint64_t add = t >= o ? s_scan[t - o] : 0ull;
+      __syncthreads();
+      s_scan[t] += add;
+      __syncthreads();
+    }
+    uint64_t run = s_before + s_scan[t] - mine;  // entries before this thread's first
+#pragma unroll
+    for (int e = 0; e < SIB_PER; ++e) {
+      if (w[e] > 0 && run <= tau && tau < run + w[e]) s_tok = jb + e;  // exactly one entry
+      run += w[e];
+    }
+  }
+  __syncthreads();
+  if (t == 0) {
+    st->done = 1;
+    a.n_accept[b] = -1;
+    a.next_token[b] = s_tok >= 0 ? s_tok : 0;
+  }
+}
+
 size_t verify_workspace(int B, int gamma, int V) {
   const size_t nch = (size_t)(V + VER_CHUNK - 1) / VER_CHUNK;
   const size_t per = std::max((size_t)16, (size_t)(gamma + 1) * sizeof(ArgMax));
-  return SPD_WS_COUNTER_BYTES + align256((size_t)B * nch * per);
+  // also room for the multi-block sibling verification's state and partials
+  return SPD_WS_COUNTER_BYTES + std::max(align256((size_t)B * nch * per),
+                                         sib_state_bytes(B) + align256(sib_part_bytes(B, V)));
 }
 
 }  // namespace spd
@@ -503,8 +762,28 @@ extern "C" int spd_verify_siblings(int32_t B, int32_t W, int32_t V, float temper
   a.W = W;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (temperature > 0.f) {
-    hipLaunchKernelGGL(verify_siblings_sampled_kernel, dim3(B), dim3(SIB_THREADS), 0, st, a);
-    return check_launch();
+    if (B >= SIB_MULTI_MAX_B) {
+      // enough sequences to fill the GPU with one block each
+      hipLaunchKernelGGL(verify_siblings_sampled_kernel, dim3(B), dim3(SIB_THREADS), 0, st, a);
+      return check_launch();
+    }
+    SibMulti mm;
+    char* base = static_cast<char*>(ws) + SPD_WS_COUNTER_BYTES;
+    mm.st = reinterpret_cast<SibState*>(base);
+    mm.part = reinterpret_cast<u128*>(base + sib_state_bytes(B));
+    mm.counters = static_cast<unsigned*>(ws);
+    mm.nch = (V + SIB_CHUNK - 1) / SIB_CHUNK;
+    const dim3 grid(mm.nch, B);
+    hipLaunchKernelGGL(sib_pass_kernel, grid, dim3(SIB_MB_THREADS), 0, st, a, mm, (int)SIB_PASS_TOT, 0);
+    int rc = check_launch();
+    for (int i = 0; i < W && !rc; ++i) {
+      hipLaunchKernelGGL(sib_pass_kernel, grid, dim3(SIB_MB_THREADS), 0, st, a, mm, (int)SIB_PASS_D, i);
+      rc = check_launch();
+      if (rc) break;
+      hipLaunchKernelGGL(sib_pass_kernel, grid, dim3(SIB_MB_THREADS), 0, st, a, mm, (int)SIB_PASS_A, i);
+      rc = check_launch();
+    }
+    return rc;
   }
   hipLaunchKernelGGL(verify_greedy_chunks_kernel, dim3(a.nchunks, B), dim3(VER_THREADS), 0, st, a);
   int rc = check_launch();

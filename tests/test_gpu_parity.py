@@ -832,7 +832,7 @@ def test_verify_siblings_greedy():
 
 
 @pytest.mark.parametrize("B,W,V,top_k", [(6, 4, 151936, 0), (4, 4, 151936, 50), (48, 3, 5000, 0),
-                                         (24, 8, 700, 20)])
+                                         (24, 8, 700, 20), (80, 3, 2100, 0), (1, 1, 151936, 0)])
 def test_verify_siblings_sampled(B, W, V, top_k):
     """T = 1: W independent draws from q per sequence, multi-round rejection; the
     accepted index or the replacement token equal the oracle's on the device's rows
