@@ -511,17 +511,18 @@ def filtered_softmax(logits, temperature, top_k=0, top_p=1.0):
 
     top-k: softmax(logits / T) restricted to top_k_set(logits, top_k) and
     renormalised (top_k = 0: no filter).
-    top-p (nucleus, applied after top-k, only when top_k >= 1 and 0 < top_p < 1):
-    order the kept tokens by probability (descending; probability is increasing
-    in the logit, so this is the logit order, equal logits by ascending index),
-    keep the shortest prefix whose mass reaches top_p, renormalise over it.
+    top-p (nucleus, when 0 < top_p < 1; applied after top-k, or over the whole
+    vocabulary when top_k = 0): order the kept tokens by probability (descending;
+    probability is increasing in the logit, so this is the logit order, equal
+    logits by ascending index), keep the shortest prefix whose mass reaches
+    top_p, renormalise over it.
     """
     x = np.asarray(logits, dtype=np.float64)
     keep = top_k_set(x, top_k)
     z = x[keep] / float(temperature)
     e = np.exp(z - z.max())
     pk = e / e.sum()
-    if top_k >= 1 and 0.0 < top_p < 1.0:
+    if 0.0 < top_p < 1.0:
         order = np.lexsort((keep, -x[keep]))         # logit desc, index asc
         before = np.concatenate(([0.0], np.cumsum(pk[order])[:-1]))
         m = int(np.count_nonzero(before < top_p))    # prefix mass before a kept token < top_p

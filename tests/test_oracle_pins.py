@@ -625,8 +625,10 @@ def test_top_p_worked_example():
     assert np.allclose(got, [0, 4 / 9, 2 / 9, 3 / 9], atol=1e-15)
     assert np.allclose(O.filtered_softmax(x, 1.0, 4, 1.0), [0.1, 0.4, 0.2, 0.3], atol=1e-15)
     assert np.allclose(O.filtered_softmax(x, 1.0, 3, 1e-9), [0, 1, 0, 0], atol=0)
-    # top_k = 0 leaves top_p off
-    assert np.allclose(O.filtered_softmax(x, 1.0, 0, 0.5), [0.1, 0.4, 0.2, 0.3], atol=1e-15)
+    # top_k = 0: the nucleus over the whole vocabulary (0.4 < 0.5 <= 0.7)
+    assert np.allclose(O.filtered_softmax(x, 1.0, 0, 0.5), [0, 4 / 7, 0, 3 / 7], atol=1e-15)
+    assert np.allclose(O.filtered_softmax(x, 1.0, 0, 0.95), [0.1, 0.4, 0.2, 0.3], atol=1e-15)
+    assert np.allclose(O.filtered_softmax(x, 1.0, 0, 0.85), [0, 4 / 9, 2 / 9, 3 / 9], atol=1e-15)
 
 
 def test_top_p_matches_ascending_cumulative_removal():
@@ -636,11 +638,11 @@ def test_top_p_matches_ascending_cumulative_removal():
     for trial in range(30):
         V = 600
         x = rng.standard_normal(V) * 2.5
-        k = int(rng.choice([5, 50, 200, 600]))
+        k = int(rng.choice([0, 5, 50, 200, 600]))
         top_p = float(rng.choice([0.2, 0.5, 0.9, 0.97]))
         T = float(rng.choice([1.0, 0.7]))
         xt = torch.tensor(x) / T
-        if k < V:
+        if 0 < k < V:
             idx = torch.topk(xt, k).indices
             masked = torch.full_like(xt, -math.inf)
             masked[idx] = xt[idx]
