@@ -59,6 +59,7 @@ class CycleOut:
     p: np.ndarray = None
     n_accept: int = -1
     next_token: int = -1
+    q_verified: np.ndarray = None   # the q row the verification used (T > 0)
 
 
 def run_cycle(om: OracleModel, st: O.SeqState, cache: O.PdmCache, ring: dict,
@@ -107,7 +108,10 @@ def run_cycle(om: OracleModel, st: O.SeqState, cache: O.PdmCache, ring: dict,
             if probs_from is not None and "p" in probs_from:
                 p = probs_from["p"]
             out.p = p
+            # the token under verification was drafted n-1 cycles ago, at the cycle
+            # whose length was cand; its draft distribution is the row kept then
             qrow = q_override if q_override is not None else ring[cand]
+            out.q_verified = qrow
             na, nt = O.verify([p], [qrow], [x], vwords, temperature=temperature,
                               bonus=False)
         out.n_accept, out.next_token = na, nt
