@@ -87,8 +87,10 @@ typedef struct spd_config {
   int32_t feature_schedule; /* SPD_SCHEDULE_PRE_STEP (default), _POST_STEP, _FIRST_STAGE */
   int32_t top_k;       /* sampling filter of spd_lm_head at T > 0: 0 = off, else   */
                        /* 1..SPD_TOP_K_MAX (section 4 evaluation setting: 50)      */
-  float top_p;         /* nucleus mass, used when top_k >= 1 and 0 < top_p < 1;   */
-                       /* 0 and 1 = off (section 4 evaluation setting: 1.0)        */
+  float top_p;         /* nucleus mass, used when 0 < top_p < 1 (0 and 1 = off;   */
+                       /* section 4 evaluation setting: 1.0); spd_lm_head applies */
+                       /* it after top-k and returns SPD_E_UNSUPPORTED for        */
+                       /* 0 < top_p < 1 with top_k = 0 at T > 0                    */
   int32_t head_workgroups; /* spd_lm_head's vocabulary GEMV (bf16, one row): 0 = one */
                        /* workgroup per 32 rows; else at most this many, each looping */
                        /* over row groups (a head streaming beside other work)     */
@@ -138,6 +140,25 @@ int spd_slot_table(const spd_config *cfg, const int32_t *anchors, int32_t *slot_
  * in-flight ones have depths a-1 .. 0.  Writes pos[M], depth[M] (HOST) and returns M,
  * or SPD_E_INVALID. */
 int spd_layout(int32_t t, int32_t a, int32_t n, int32_t *pos, int32_t *depth);
+
+/* Everything the host needs to issue one cycle (section 3.1 Eq. (2); section 3.4
+ * streaming verification), from the state (t tokens, a of them in flight) the
+ * cycle starts from; positions are 0-based (position i holds x_{i+1}).
+ *   pos0, M      rows the cycle recomputes, as spd_layout: pos0 = t-1-a, M = a+1
+ *   verifies     1 iff a == n: the pipeline is saturated, the token at `exiting`
+ *                leaves the last stage and its successor `cand` is verified
+ *   exiting      t-n (the target head reads its last-layer state), else -1
+ *   cand         t-n+1, drafted n-1 cycles earlier (x_{t-n+2}), else -1
+ *   draft_pos    t: the position this cycle's draft fills
+ *   ring_draft   t mod n: row of an n-row ring that keeps this cycle's q
+ *   ring_cand    cand mod n: the ring row holding cand's q (the row written when
+ *                cand was drafted; the n-1 drafts since used the other rows), else -1
+ * Returns SPD_OK, SPD_E_INVALID (out NULL, a outside 1..n, t < a+1) or
+ * SPD_E_UNSUPPORTED for n < 2, where cand would be this cycle's own draft. */
+typedef struct spd_cycle_info {
+  int32_t pos0, M, verifies, exiting, cand, draft_pos, ring_draft, ring_cand;
+} spd_cycle_info;
+int spd_cycle_plan(int32_t t, int32_t a, int32_t n, spd_cycle_info *out);
 
 /* Bytes of workspace a call needs.  call: SPD_CALL_*; rows = M for FUSE and PDM, the
  * number of head rows for LM_HEAD, B for VERIFY (then gamma and cfg->V are used);
@@ -205,7 +226,8 @@ int spd_pdm_step(const spd_config *cfg, const spd_layer_weights *layers, const v
  *   ascending index, NaN last) and probs is 0 elsewhere; with 0 < cfg.top_p < 1 it is
  *   further restricted to the shortest run of those, in descending logit order, whose
  *   top-k probability (computed in float64) reaches top_p, and renormalised.  The draw
- *   is the same inverse CDF over the filtered probs.
+ *   is the same inverse CDF over the filtered probs.  A nucleus without top-k
+ *   (cfg.top_k = 0, 0 < cfg.top_p < 1, T > 0) is not offered: SPD_E_UNSUPPORTED.
  * w_lm DEVICE [V][d] (cfg.dtype); h DEVICE float [rows][d]; words DEVICE uint64 [rows];
  * logits, probs DEVICE float [rows][V]; token DEVICE int32 [rows].
  */
@@ -310,7 +332,8 @@ int spd_verify_siblings(int32_t B, int32_t W, int32_t V, float temperature, cons
 
 const char *spd_status_string(int status);
 int spd_last_hip_error(void);
-/* Version of this interface: 2 (spd_config gained top_k, top_p and head_workgroups). */
+/* Version of this interface: 3 (2: spd_config gained top_k, top_p and head_workgroups;
+ * 3: spd_cycle_plan). */
 int spd_version(void);
 
 #ifdef __cplusplus

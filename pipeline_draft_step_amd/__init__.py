@@ -28,7 +28,7 @@ EXPORTED = (
     "spd_slot_table", "spd_layout", "spd_workspace_size", "spd_fuse_features",
     "spd_pdm_step", "spd_lm_head", "spd_verify", "spd_rollback", "spd_status_string",
     "spd_last_hip_error", "spd_version", "spd_fuse_features_tree", "spd_pdm_step_tree",
-    "spd_verify_siblings",
+    "spd_verify_siblings", "spd_cycle_plan",
 )
 
 
@@ -50,6 +50,12 @@ class spd_layer_weights(ctypes.Structure):
 
 class spd_seq_state(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("t", "a", "commits", "cycles")]
+
+
+class spd_cycle_info(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("pos0", "M", "verifies", "exiting", "cand", "draft_pos", "ring_draft",
+                 "ring_cand")]
 
 
 class SpdError(RuntimeError):
@@ -78,6 +84,7 @@ def lib():
         i32p = ctypes.POINTER(_I32)
         L.spd_slot_table.argtypes = [cfgp, i32p, i32p, i32p, i32p]
         L.spd_layout.argtypes = [_I32, _I32, _I32, i32p, i32p]
+        L.spd_cycle_plan.argtypes = [_I32, _I32, _I32, ctypes.POINTER(spd_cycle_info)]
         L.spd_workspace_size.argtypes = [_I32, cfgp, _I32, _I32, _I64]
         L.spd_workspace_size.restype = _SZ
         L.spd_fuse_features.argtypes = [cfgp, _P, _I64, _I32, i32p, _I32, _I32, _I32, _P, _P, _P,
@@ -160,6 +167,12 @@ def spd_layout(t: int, a: int, n: int):
     dep = (_I32 * (a + 1))()
     M = _check("spd_layout", lib().spd_layout(t, a, n, pos, dep))
     return list(pos)[:M], list(dep)[:M]
+
+
+def spd_cycle_plan(t: int, a: int, n: int) -> spd_cycle_info:
+    out = spd_cycle_info()
+    _check("spd_cycle_plan", lib().spd_cycle_plan(t, a, n, ctypes.byref(out)))
+    return out
 
 
 def spd_workspace_size(call: int, cfg: spd_config, rows: int, gamma: int = 0, T_cap: int = 0) -> int:

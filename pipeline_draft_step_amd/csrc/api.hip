@@ -103,6 +103,23 @@ extern "C" int spd_layout(int32_t t, int32_t a, int32_t n, int32_t* pos, int32_t
   return M;
 }
 
+extern "C" int spd_cycle_plan(int32_t t, int32_t a, int32_t n, spd_cycle_info* out) {
+  if (!out || n < 1 || a < 1 || a > n || t < a + 1) return SPD_E_INVALID;
+  // with one stage the token under verification would be this cycle's own draft
+  if (n < 2) return SPD_E_UNSUPPORTED;
+  spd_cycle_info p;
+  p.pos0 = t - 1 - a;
+  p.M = a + 1;
+  p.verifies = a == n ? 1 : 0;
+  p.exiting = p.verifies ? t - n : -1;
+  p.cand = p.verifies ? t - n + 1 : -1;
+  p.draft_pos = t;
+  p.ring_draft = t % n;
+  p.ring_cand = p.verifies ? p.cand % n : -1;
+  *out = p;
+  return SPD_OK;
+}
+
 extern "C" size_t spd_workspace_size(int32_t call, const spd_config* cfg, int32_t rows,
                                      int32_t gamma, int64_t T_cap) {
   if (rows < 1) return 0;
@@ -143,4 +160,4 @@ extern "C" const char* spd_status_string(int status) {
 
 extern "C" int spd_last_hip_error(void) { return last_hip_error_ref(); }
 
-extern "C" int spd_version(void) { return 2; }
+extern "C" int spd_version(void) { return 3; }

@@ -333,7 +333,6 @@ __global__ __launch_bounds__(SMX_THREADS) void softmax_sample_kernel(
   __shared__ int s_cc, s_tok;
   const int c = blockIdx.x, r = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  SPD_MARK(0);
   float M, S;
   if (nstat > 0) {
     stats_max_sum(stat + r, rows, nstat, inv_t, M, S);
@@ -341,7 +340,6 @@ __global__ __launch_bounds__(SMX_THREADS) void softmax_sample_kernel(
     M = gstat[r].mx;
     S = gstat[r].se;
   }
-  SPD_MARK(1);
   const float inv_sum = 1.0f / S;
   const float* lr = logits + (size_t)r * V;
   float* pr = probs + (size_t)r * V;
@@ -368,12 +366,9 @@ __global__ __launch_bounds__(SMX_THREADS) void softmax_sample_kernel(
   __syncthreads();
   if (threadIdx.x == 0)
     st_coh_u64(csum + (size_t)r * nchunks + c, (s_w[0] + s_w[1]) + (s_w[2] + s_w[3]));
-  SPD_MARK(2);
   if (!arrive_last(counters + r, (unsigned)nchunks)) {
-    SPD_MARK(3);
     return;
   }
-  SPD_MARK(3);
   const uint64_t* cs = csum + (size_t)r * nchunks;
   if (wave == 0) {
     // lane l holds chunks 4l .. 4l+3
@@ -452,7 +447,6 @@ __global__ __launch_bounds__(SMX_THREADS) void softmax_sample_kernel(
   }
   __syncthreads();
   if (threadIdx.x == 0) token[r] = s_tok < 0 ? 0 : s_tok;
-  SPD_MARK(4);
 }
 
 // ---------------------------------------------------------------- top-k / top-p sampling
@@ -608,7 +602,6 @@ __global__ __launch_bounds__(SMX_THREADS) void topk_sample_kernel(
   const int base = c * SMX_CHUNK;
   const int n = min(SMX_CHUNK, V - base);
   constexpr int PER = SMX_CHUNK / SMX_THREADS;
-  SPD_MARK(0);
   uint64_t key[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
@@ -616,7 +609,6 @@ __global__ __launch_bounds__(SMX_THREADS) void topk_sample_kernel(
     const float x = lr[j < V ? j : 0];
     key[e] = j < V ? topk_key(x, j) : 0ull;
   }
-  SPD_MARK(1);
   uint64_t th = 1ull;  // every real key is >= 1
   if (n > k)
     th = select_kth(
@@ -625,7 +617,6 @@ __global__ __launch_bounds__(SMX_THREADS) void topk_sample_kernel(
           for (int e = 0; e < PER; ++e) f(key[e]);
         },
         (unsigned)k, s);
-  SPD_MARK(2);
   if (t == 0) s_cnt = 0u;
   __syncthreads();
   const bool list_only = probs == nullptr;  // T = 0: the ordered top-k list, no probabilities
@@ -639,9 +630,7 @@ __global__ __launch_bounds__(SMX_THREADS) void topk_sample_kernel(
       pr[base + t + SMX_THREADS * e] = 0.f;
     }
   }
-  SPD_MARK(3);
   if (!arrive_last(counters + r, (unsigned)nchunks)) return;
-  SPD_MARK(4);
 
   // ---- last block: the k largest of all candidates
   const int ncand = (nchunks - 1) * cs + min(k, V - (nchunks - 1) * SMX_CHUNK);
@@ -661,7 +650,6 @@ __global__ __launch_bounds__(SMX_THREADS) void topk_sample_kernel(
   };
   uint64_t th2 = 1ull;
   if (ncand > kk) th2 = select_kth(visit_cand, (unsigned)kk, s);
-  SPD_MARK(5);
   if (t == 0) s_cnt = 0u;
   __syncthreads();
   visit_cand([&](uint64_t key2) {
@@ -721,7 +709,6 @@ __global__ __launch_bounds__(SMX_THREADS) void topk_sample_kernel(
     s_idx[s_irank[t]] = ix;
   }
   __syncthreads();
-  SPD_MARK(6);
   // inverse CDF in ascending index order
   const uint64_t w = member ? s_w[t] : 0ull;
   const uint64_t winc = wave_scan_u64(w);
@@ -737,7 +724,6 @@ __global__ __launch_bounds__(SMX_THREADS) void topk_sample_kernel(
   } else if (member && lo <= tau && tau < lo + w) {
     token[r] = s_idx[t];
   }
-  SPD_MARK(7);
 }
 
 struct LmPlan {
@@ -850,6 +836,10 @@ extern "C" int spd_lm_head(const spd_config* cfg, const void* w_lm, const float*
   if (rows < 1 || rows > 16) return SPD_E_INVALID;
   if (!(temperature >= 0.f) || temperature == INFINITY) return SPD_E_INVALID;
   if (temperature > 0.f && (!probs || !words)) return SPD_E_INVALID;
+  // the nucleus is cut among the top-k candidates; over the whole vocabulary it
+  // would need a vocabulary-wide ordering, which this library does not offer
+  if (temperature > 0.f && cfg->top_k == 0 && cfg->top_p > 0.f && cfg->top_p < 1.f)
+    return SPD_E_UNSUPPORTED;
   if (cfg->d % 64) return SPD_E_UNSUPPORTED;
   if ((int64_t)cfg->V * cfg->d > ((int64_t)1 << 40)) return SPD_E_UNSUPPORTED;
   if (temperature > 0.f && cfg->V > SMX_MAXCH * SMX_CHUNK) return SPD_E_UNSUPPORTED;

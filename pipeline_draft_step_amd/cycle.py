@@ -14,8 +14,9 @@ from dataclasses import dataclass
 import torch
 
 from . import (SPD_BF16, SPD_CALL_FUSE, SPD_CALL_LM_HEAD, SPD_CALL_PDM, SPD_CALL_VERIFY,
-               layer_weights, make_config, spd_config, spd_fuse_features, spd_lm_head,
-               spd_pdm_step, spd_rollback, spd_slot_table, spd_verify, spd_workspace_size)
+               layer_weights, make_config, spd_config, spd_cycle_plan, spd_fuse_features,
+               spd_lm_head, spd_pdm_step, spd_rollback, spd_slot_table, spd_verify,
+               spd_workspace_size)
 
 PREFILL_BLOCK = 256   # rows per PDM prefill call
 FEATURE_BLOCK = 2048  # rows per prefill feature call (one large-M FC GEMM)
@@ -55,8 +56,11 @@ class SpdCycle:
     """Buffers of one sequence and the calls of one cycle."""
 
     def __init__(self, model: SpdModel, temperature: float, device="cuda"):
-        self.m = model
         c = model.cfg
+        # the library refuses stage counts it cannot cycle (n < 2: the token under
+        # verification would be the cycle's own draft)
+        spd_cycle_plan(c.n + 1, c.n, c.n)
+        self.m = model
         self.T = float(temperature)
         self.device = device
         wdt = torch.bfloat16 if c.dtype == SPD_BF16 else torch.float32
@@ -103,6 +107,7 @@ class SpdCycle:
         self.cfg_bg.head_workgroups = max(1, cus * 3 // 4)
         self.ev_fork = torch.cuda.Event()
         self.ev_join = torch.cuda.Event()
+        self._plans = {}
 
     # ---------------------------------------------------------------- pieces
     def features(self, pos0, M, a, out=None):
@@ -128,30 +133,37 @@ class SpdCycle:
                 M = min(self.pdm_block, Mf - b)
                 self.pdm(s + b, M, g=self.g_pre[b:b + M])
 
-    def draft(self, t, words_block):
-        """Draft head on h_last; at T > 0 the q row goes to ring[t % n]."""
+    def plan(self, t, a):
+        """The library's plan of the cycle that starts at length t with a in flight
+        (rows, verified and exiting positions, ring rows)."""
+        key = (t, a)
+        p = self._plans.get(key)
+        if p is None:
+            p = self._plans[key] = spd_cycle_plan(t, a, self.m.cfg.n)
+        return p
+
+    def draft(self, plan, words_block):
+        """Draft head on h_last; at T > 0 the q row goes to the plan's ring row."""
         m = self.m
-        probs = self.ring[t % m.cfg.n] if self.T > 0 else None
+        probs = self.ring[plan.ring_draft] if self.T > 0 else None
         w = None if words_block is None else words_block.data_ptr() + 2 * 8
         spd_lm_head(m.cfg, m.w.w_dlm, self.h_last, 1, self.T, w, self.dlogits, probs, self.dtoken,
                     self.ws)
 
-    def target_and_verify(self, t, words_block, q_row=None, x_ptr=None, ws=None,
+    def target_and_verify(self, plan, words_block, q_row=None, x_ptr=None, ws=None,
                           background=False):
         """Target head on the exiting token's state and streaming verify of its successor.
         background: the head runs beside the draft chain on a capped grid."""
         m = self.m
         cfg = self.cfg_bg if background else m.cfg
         ws = self.ws if ws is None else ws
-        n, V = m.cfg.n, m.cfg.V
-        exiting = t - n
-        h = m.w.h_final[exiting]
+        V = m.cfg.V
+        h = m.w.h_final[plan.exiting]
         probs = self.p if self.T > 0 else None
         w = None if words_block is None else words_block.data_ptr() + 2 * 8
         spd_lm_head(cfg, m.w.w_tlm, h, 1, self.T, w, self.tlogits, probs, self.ttoken, ws)
-        cand = exiting + 1
-        q = q_row if q_row is not None else self.ring[cand % n]
-        draft = x_ptr if x_ptr is not None else self.tokens.data_ptr() + 4 * cand
+        q = q_row if q_row is not None else self.ring[plan.ring_cand]
+        draft = x_ptr if x_ptr is not None else self.tokens.data_ptr() + 4 * plan.cand
         spd_verify(1, 1, V, self.T, 0, self.p if self.T > 0 else self.tlogits,
                    q if self.T > 0 else None, draft,
                    None if words_block is None else words_block, self.n_accept, self.next_token,
@@ -167,20 +179,19 @@ class SpdCycle:
         """One cycle at sequence length t with a tokens in flight.  In a saturated
         cycle the target head + verify run on the side stream, concurrently with
         the features -> PDM -> draft chain; rollback waits for both."""
-        n = self.m.cfg.n
-        pos0, M = t - 1 - a, a + 1
+        plan = self.plan(t, a)
         main = torch.cuda.current_stream()
-        if a == n:
+        if plan.verifies:
             self.ev_fork.record(main)
             self.side.wait_event(self.ev_fork)
             with torch.cuda.stream(self.side):
-                self.target_and_verify(t, words_block, q_row, x_ptr, ws=self.ws_side,
+                self.target_and_verify(plan, words_block, q_row, x_ptr, ws=self.ws_side,
                                        background=True)
             self.ev_join.record(self.side)
-        self.features(pos0, M, a)
-        self.pdm(pos0, M)
-        self.draft(t, words_block)
-        if a == n:
+        self.features(plan.pos0, plan.M, a)
+        self.pdm(plan.pos0, plan.M)
+        self.draft(plan, words_block)
+        if plan.verifies:
             main.wait_event(self.ev_join)
         self.rollback()
 

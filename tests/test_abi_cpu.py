@@ -21,7 +21,7 @@ def test_header_symbols_are_exported():
     for n in names:                      # the binding uses the C names
         if n not in ("spd_status_string", "spd_last_hip_error"):
             assert hasattr(spd, n), n
-    assert spd.spd_version() == 2
+    assert spd.spd_version() == 3
 
 
 def _cfg(s, **kw):
@@ -97,6 +97,69 @@ def test_layout_matches_oracle(t, a, n):
     pos, dep = spd.spd_layout(t, a, n)
     pos0, opos, odep = O.cycle_rows(t, a, n)
     assert pos == opos and dep == odep and pos[0] == pos0
+
+
+@pytest.mark.parametrize("n", [2, 4, 8, 16])
+def test_cycle_plan_follows_the_pages(n):
+    """The host's cycle plan against the oracle's layout and [SPD] 3.4: a cycle
+    verifies iff the pipeline is saturated; then x_{t-n+1} (0-based t-n) exits and
+    its successor, drafted n-1 cycles earlier at length t-n+1, is verified.  The
+    ring row of a verified token is the row its own draft cycle wrote, and no draft
+    in between (nor this cycle's) reuses it."""
+    for t in range(n + 1, 3 * n + 4):
+        for a in range(1, n + 1):
+            p = spd.spd_cycle_plan(t, a, n)
+            pos0, pos, _ = O.cycle_rows(t, a, n)
+            assert (p.pos0, p.M) == (pos0, len(pos))
+            assert p.draft_pos == t and p.ring_draft == t % n
+            assert p.verifies == (1 if a == n else 0)
+            if a == n:
+                assert (p.exiting, p.cand) == (t - n, t - n + 1)
+                # the candidate was drafted by the cycle at length cand; the drafts of
+                # the n-1 cycles since (lengths cand+1 .. t) wrote other rows
+                assert p.ring_cand == spd.spd_cycle_plan(p.cand, 1, n).ring_draft
+                assert all(spd.spd_cycle_plan(L, 1, n).ring_draft != p.ring_cand
+                           for L in range(p.cand + 1, t + 1))
+            else:
+                assert (p.exiting, p.cand, p.ring_cand) == (-1, -1, -1)
+
+
+def test_cycle_plan_rejects_one_stage_and_bad_arguments():
+    with pytest.raises(spd.SpdError) as e:
+        spd.spd_cycle_plan(5, 1, 1)   # n = 1: the verified token would be this cycle's draft
+    assert e.value.status == spd.SPD_E_UNSUPPORTED
+    for args in ((5, 0, 4), (5, 5, 4), (4, 4, 4)):
+        with pytest.raises(spd.SpdError) as e:
+            spd.spd_cycle_plan(*args)
+        assert e.value.status == spd.SPD_E_INVALID
+
+
+def test_cycle_driver_refuses_one_stage():
+    """SpdCycle asks the library's plan before it allocates anything: n = 1 is
+    refused with a clear error instead of racing the draft against its own
+    verification (features and PDM steps of an n = 1 model stay callable)."""
+    from pipeline_draft_step_amd.cycle import SpdCycle
+    model = type("M", (), {"cfg": _cfg(synth.TINY, n=1)})()
+    with pytest.raises(spd.SpdError, match="spd_cycle_plan"):
+        SpdCycle(model, 0.0, device="cpu")
+
+
+def test_lm_head_refuses_nucleus_without_top_k():
+    """A nucleus over the whole vocabulary (top_k = 0, 0 < top_p < 1, T > 0) is not
+    offered: the call says so instead of sampling from the unfiltered softmax."""
+    lib = spd.lib()
+    s = synth.HEADLINE
+    fake = 1 << 40
+    c = _cfg(s, top_k=0, top_p=0.9)
+    rc = lib.spd_lm_head(ctypes.byref(c), fake, fake, 1, ctypes.c_float(1.0), fake, fake, fake,
+                         fake, fake, 16, None)
+    assert rc == spd.SPD_E_UNSUPPORTED
+    for kw, T in ((dict(top_k=50, top_p=0.9), 1.0), (dict(top_k=0, top_p=1.0), 1.0),
+                  (dict(top_k=0, top_p=0.9), 0.0)):
+        c = _cfg(s, **kw)
+        rc = lib.spd_lm_head(ctypes.byref(c), fake, fake, 1, ctypes.c_float(T), fake, fake, fake,
+                             fake, fake, 16, None)
+        assert rc == spd.SPD_E_WORKSPACE, (kw, T)   # past the filter check, stopped by ws size
 
 
 def test_layout_rejects_bad_arguments():
