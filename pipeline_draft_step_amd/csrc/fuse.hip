@@ -64,7 +64,6 @@ __global__ __launch_bounds__(256) void feature_gather_kernel(GatherArgs<WT> f) {
   __shared__ int8_t s_tab[TABN];
   __shared__ float s_red[4];
   __builtin_amdgcn_s_setprio(3);  // decode chain first on a shared SIMD (as in the GEMMs)
-  SPD_MARK(0);
   if (threadIdx.x == 0) {
     // the table is copied with constant indices: a dynamically indexed kernel
     // argument would be copied to scratch memory
@@ -109,7 +108,6 @@ __global__ __launch_bounds__(256) void feature_gather_kernel(GatherArgs<WT> f) {
     f.xo.put4(r, col, lo4);
     f.xo.put4(r, col + 4, hi4);
   }
-  SPD_MARK(1);
   sq = wave_sum(sq);
   if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = sq;
   __syncthreads();

@@ -161,7 +161,6 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   const int nkeys = a.pos0 + a.M;
   const int r_last = (min(QR, 16 * qt + 16) - 1) / G;
   if (c * ATT_KC > a.pos0 + r_last) return;  // every row of the tile is masked here
-  SPD_MARK(0);
   const int key0 = c * ATT_KC + wave * ATT_SUB;
 
   const WT* K = static_cast<const WT*>(a.kc) + (size_t)h * a.T_cap * HD;
@@ -195,7 +194,6 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     for (int dt = 0; dt < DT; ++dt) vf[kt][dt] = F::load(Vt + (size_t)(dt * 16 + lr) * a.T_cap + kbc);
   }
   __builtin_amdgcn_sched_barrier(0);  // keep V in flight with Q and K
-  SPD_MARK(1);
   // Q fragments (A operand), pre-scaled by 1/sqrt(hd), as hi + lo pairs
   frag qf[DS], ql[DS];
   const float qs = qv ? a.scale : 0.f;  // clamped rows (finite values) become zero
@@ -220,7 +218,6 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
       if constexpr (SPLIT) sc[ks] = F::mma(ql[ds], kf[ks][ds], sc[ks]);
     }
   }
-  SPD_MARK(2);
   // lane holds S[4*lg + i][16*ks + lr] of this wave's keys
   float mx[4], sm[4];
   // draft tree: a row reads the new keys of its own root path only
@@ -290,7 +287,6 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
       for (int dt = 0; dt < DT; ++dt) o[dt] = F::mma(pl, vf[kt][dt], o[dt]);
     }
   }
-  SPD_MARK(3);
   // merge the four waves: rescale to the block maximum of each row
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -329,12 +325,9 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   }
   // the last chunk block of (kv head, query tile) merges the chunk partials of its rows
   const int nchunk_tile = min(a.nch, (a.pos0 + r_last) / ATT_KC + 1);
-  SPD_MARK(4);
   if (!arrive_last(a.counters + h * a.nqt + qt, (unsigned)nchunk_tile)) {
-    SPD_MARK(5);
     return;
   }
-  SPD_MARK(5);
   // chunk weights exp(m_c - max) of each row: 16 threads per row, chunks strided
   __shared__ float s_w[16][ATT_MAXCH];
   __shared__ float s_L[16];
@@ -420,7 +413,6 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     xo.put4(qr / G, (h * G + qr % G) * HD + dimv[ii],
             make_float4(acc[ii].x * il, acc[ii].y * il, acc[ii].z * il, acc[ii].w * il));
   }
-  SPD_MARK(6);
 }
 
 // ---------------------------------------------------------------------------

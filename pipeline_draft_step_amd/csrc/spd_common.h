@@ -7,28 +7,6 @@
 
 #include "../../include/spd.h"
 
-// Optional per-block timeline hook for profiling builds: SPD_MARK(i) stores the
-// device real-time clock (100 MHz) for event i of the calling block into slot
-// [dispatch packet mod 64][block][i] of a buffer that the profiling harness
-// defines, plus the packet address of each dispatch.  Compiles to nothing otherwise.
-#ifdef SPD_TRACE
-extern __device__ unsigned long long spd_trace_buf[];
-extern __device__ unsigned spd_trace_tag[];
-#define SPD_MARK(i)                                                                  \
-  do {                                                                               \
-    if (threadIdx.x == 0) {                                                          \
-      const uintptr_t d_ = (uintptr_t)__builtin_amdgcn_dispatch_ptr();               \
-      const unsigned r_ = (unsigned)(d_ >> 6) & 63u;                                 \
-      const unsigned b_ = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z); \
-      if (b_ < 4096u)                                                                \
-        spd_trace_buf[((size_t)r_ * 4096u + b_) * 8u + (i)] = __builtin_amdgcn_s_memrealtime(); \
-      if (b_ == 0u) spd_trace_tag[r_] = (unsigned)d_ | 1u;                           \
-    }                                                                                \
-  } while (0)
-#else
-#define SPD_MARK(i) ((void)0)
-#endif
-
 namespace spd {
 
 typedef uint16_t bf16;  // bfloat16 bit pattern

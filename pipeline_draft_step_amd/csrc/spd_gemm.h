@@ -222,7 +222,6 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_skinny_kernel(GemmShape g, 
   const int lr = lane & 15;
   const int lg = lane >> 4;
   const int nst = st1 - st0;
-  SPD_MARK(0);
 
   WT* xs = reinterpret_cast<WT*>(smem);
   const int xrows = min(TR, g.M);
@@ -250,7 +249,6 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_skinny_kernel(GemmShape g, 
       }
     const int ksub = lane >> 4;          // k-step of this lane's chunk inside a half group
     const int loff = k0 + 8 * (lane >> 2);  // this lane's element offset in the row
-    SPD_MARK(1);
     // Two register buffers with fixed roles (A: even groups, B: odd groups), so
     // that consuming one never waits for the loads of the other.  Loads are
     // unconditional (a conditional load becomes a branch whose join waits for
@@ -315,9 +313,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_skinny_kernel(GemmShape g, 
       issue(bufA, 0);
     }
     rsc.finish(g, Mt, s_rs);
-    SPD_MARK(7);
     __syncthreads();
-    SPD_MARK(2);
     unsigned char* tb = reinterpret_cast<unsigned char*>(xs_lo + (size_t)xrows * g.ldx) +
                         (size_t)(max(g.ytile_bytes - g.x_bytes, 0)) + wave * TB_WAVE;
     const int rdb = (lr >> 2) * TB_STRIDE + 16 * ((lr & 3) + 4 * lg);
@@ -385,7 +381,6 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_skinny_kernel(GemmShape g, 
     for (int i = 0; i < U; ++i)
 #pragma unroll
       for (int u = 0; u < NT; ++u) cur[i][u] = F::load(wp[u] + (i < nst ? i * F::KSTEP : 0));
-    SPD_MARK(1);
     RowScale<4 * MT, RowScaleOf<In>::value> rsc;
     rsc.load(g, m0, Mt);
     const XStage<WT> xst{xs, xs_lo, g.ldx};
@@ -402,7 +397,6 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_skinny_kernel(GemmShape g, 
     }
     rsc.finish(g, Mt, s_rs);
     __syncthreads();
-    SPD_MARK(2);
     for (int st = 0; st < nst; st += U) {
       const int nxt0 = st + U;
       if (nxt0 < nst) {
@@ -432,7 +426,6 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_skinny_kernel(GemmShape g, 
     }
   }
 
-  SPD_MARK(3);
   // lane holds D[16t + 4*lg + i][16u + lr] of this wave
   float (*ytile)[TC + 1] = reinterpret_cast<float (*)[TC + 1]>(smem);  // aliases the X slice
   if (S == 1) {
@@ -445,9 +438,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_skinny_kernel(GemmShape g, 
         for (int i = 0; i < 4; ++i)
           ytile[16 * t + 4 * lg + i][wave * 16 * NT + 16 * u + lr] = acc[t][u][i] * s_rs[16 * t + 4 * lg + i];
     __syncthreads();
-    SPD_MARK(5);
     epi.template run<MT, NT>(TileY<TC>{ytile}, nb, m0, Mt, rmap);
-    SPD_MARK(6);
     return;
   }
 #pragma unroll
@@ -463,10 +454,8 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_skinny_kernel(GemmShape g, 
       }
     }
   if (!arrive_last(g.counters + mt * g.nblocks + nb, (unsigned)S)) {
-    SPD_MARK(4);
     return;
   }
-  SPD_MARK(4);
   // last block of this tile: sum the S partials (fixed order) into LDS.  Each
   // thread owns 4 consecutive columns of PER4 rows; 16 partial loads of every
   // element are in flight at once.
@@ -515,9 +504,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_skinny_kernel(GemmShape g, 
     ytile[m][c + 3] = sum[j].w * sc;
   }
   __syncthreads();
-  SPD_MARK(5);
   epi.template run<MT, NT>(TileY<TC>{ytile}, nb, m0, Mt, rmap);
-  SPD_MARK(6);
 }
 
 // ---------------------------------------------------------------------------
