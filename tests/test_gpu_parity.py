@@ -66,7 +66,8 @@ FUSE_CASES = [
     ("tiny_post_step", synth.TINY.with_(feature_schedule=1), [(32, 4), (32, 2)]),
     ("headline_post_step", synth.HEADLINE.with_(feature_schedule=1), [(2048, 8), (2048, 3)]),
     ("headline", synth.HEADLINE, [(2048, 8), (2048, 3), (2048, 1), (9, 8), (2, 1)]),
-    ("9b", synth.SHAPES["qwen35_9b_n16_ls4_t1"], [(4096, 16)]),
+    ("4b_n4", synth.SHAPES["qwen35_4b_n4_ls1_greedy"], [(2048, 4), (2048, 3), (2048, 1), (5, 4)]),
+    ("9b", synth.SHAPES["qwen35_9b_n16_ls4_t1"], [(4096, 16), (4096, 7), (4096, 1)]),
 ]
 
 
@@ -1134,55 +1135,68 @@ def test_cycle_trajectory_tiny(schedule):
 def test_cycle_trajectory_tiny_sampled(top_k, top_p):
     """A T = 1 device-state trajectory with rejections and rollbacks: every draft is
     the oracle's draw from the device's (filtered) q row, every verification the
-    oracle's decision on the device's p and ring q rows, the kept sets are the
-    oracle's filters of the device's logits, and the state matches the oracle state
-    machine after every cycle."""
+    oracle's decision with the oracle's own ring of q rows (fed with the device's
+    rows as they are drafted), the kept sets are the oracle's filters of the
+    device's logits, and the state matches the oracle state machine after every
+    cycle.  The q row the device verifies against is, bit for bit, the row it
+    wrote when that token was drafted n-1 cycles earlier ([SPD] 3.3-3.4)."""
     s = synth.TINY.with_(top_k=top_k, top_p=top_p)
+    n = s.n
     ci = make_inputs(s, device=DEV, T_cap=128)
     model = device_model(ci)
     cyc = SpdCycle(model, 1.0)
     om = OC.model_from_inputs(ci)
     t0 = s.ctx
-    ost = O.SeqState(t=t0, a=s.n, tokens=list(range(t0)))
-    cyc.set_state(t0, s.n, ost.tokens)
-    cyc.prefill(t0 - 1 - s.n)
-    cache = OC.prefill(om, t0, s.n)
-    # q rows of the tokens already in flight (drafted before the trajectory starts)
-    seed_logits = synth.normal((s.n, s.V), 3.0, device="cpu", seed=91, name="ring_seed")
-    for r in range(s.n):
-        row = O.filtered_softmax(seed_logits[r].double().numpy(), 1.0, top_k, top_p)
-        cyc.ring[r].copy_(torch.from_numpy(row.astype(np.float32)))
+    ost = O.SeqState(t=t0, a=n, tokens=list(range(t0)))
+    cyc.set_state(t0, n, ost.tokens)
+    cyc.prefill(t0 - 1 - n)
+    cache = OC.prefill(om, t0, n)
+    # q rows of the n-1 tokens in flight at the start (drafted before the trajectory):
+    # the device ring row of position P is P mod n (the library's plan), the oracle's
+    # ring is keyed by position
+    seed_logits = synth.normal((n, s.V), 3.0, device="cpu", seed=91, name="ring_seed")
+    oring, drafted_q = {}, {}
+    for i, P in enumerate(range(t0 - n + 1, t0)):
+        row = O.filtered_softmax(seed_logits[i].double().numpy(), 1.0, top_k, top_p).astype(np.float32)
+        cyc.ring[P % n].copy_(torch.from_numpy(row))
+        oring[P] = drafted_q[P] = row
     wb = synth.cycle_words(40, seed=17)
     wdev = synth.words_tensor(wb, DEV)
     verified = rejected = 0
     for c in range(40):
         t, a = ost.t, ost.a
         say("sampled trajectory cycle", c, t, a)
-        cand = t - s.n + 1
-        q_cand = cyc.ring[cand % s.n].cpu().numpy().copy() if a == s.n else None
+        plan = cyc.plan(t, a)
+        assert (plan.verifies == 1) == (a == n) and plan.draft_pos == t
+        if plan.verifies:
+            assert plan.cand == t - n + 1
+            q_dev = cyc.ring[plan.ring_cand].cpu().numpy().copy()
+            assert np.array_equal(q_dev.view(np.uint32), drafted_q[plan.cand].view(np.uint32))
         cyc.cycle(t, a, wdev[c])
         torch.cuda.synchronize()
-        gq = cyc.ring[t % s.n].cpu().numpy()
-        gp = cyc.p.cpu().numpy() if a == s.n else None
+        gq = cyc.ring[plan.ring_draft].cpu().numpy().copy()
+        gp = cyc.p.cpu().numpy() if plan.verifies else None
         probs_from = {"q": gq} if gp is None else {"q": gq, "p": gp}
-        out = OC.run_cycle(om, O.SeqState(t=t, a=a, tokens=list(ost.tokens)), cache, {}, 1.0, wb[c],
-                           q_override=q_cand, probs_from=probs_from)
+        out = OC.run_cycle(om, O.SeqState(t=t, a=a, tokens=list(ost.tokens)), cache, oring, 1.0,
+                           wb[c], probs_from=probs_from)
+        drafted_q[t] = gq
         assert rel_err(f64(cyc.h_last), out.h_last) < TOL_F32
         dl = cyc.dlogits.cpu().numpy()
         assert rel_err(dl, out.draft_logits) < TOL_F32
         dref = O.filtered_softmax(dl.astype(np.float64), 1.0, top_k, top_p)
         assert np.array_equal(np.flatnonzero(gq), np.flatnonzero(dref))
         assert int(cyc.dtoken.item()) == out.drafted
-        if a == s.n:
+        if plan.verifies:
             verified += 1
             rejected += out.n_accept == 0
+            assert np.array_equal(out.q_verified.view(np.uint32), q_dev.view(np.uint32))
             tl = cyc.tlogits.cpu().numpy()
             assert rel_err(tl, out.target_logits) < TOL_F32
             tref = O.filtered_softmax(tl.astype(np.float64), 1.0, top_k, top_p)
             assert np.array_equal(np.flatnonzero(gp), np.flatnonzero(tref))
             assert (int(cyc.n_accept.item()), int(cyc.next_token.item())) == (out.n_accept,
                                                                              out.next_token)
-        O.transition(ost, s.n, out.drafted, a == s.n, out.n_accept, out.next_token)
+        O.transition(ost, n, out.drafted, a == n, out.n_accept, out.next_token)
         assert cyc.read_state() == (ost.t, ost.a, ost.commits, ost.cycles)
         assert cyc.tokens[:ost.t].tolist() == ost.tokens
         cache.truncate(ost.t - 1 - ost.a)
@@ -1242,3 +1256,232 @@ def test_cycle_full_headline_sampled(top_k, top_p):
             assert (int(cyc.n_accept.item()), int(cyc.next_token.item())) == (out.n_accept,
                                                                              out.next_token)
         assert cyc.read_state() == (st.t, st.a, st.commits, st.cycles)
+
+
+# ------------------------------------------------------------------ whole cycles at full size
+
+def _full_cycle(cyc, om, s, k, v, t, a, tokens, wblock, wdev, qstand):
+    """One independent cycle from the seeded committed cache: device and oracle,
+    with the oracle's decisions taken on the device's fp32 rows."""
+    cyc.k_cache.copy_(k)
+    cyc.v_cache.copy_(v)
+    cyc.set_state(t, a, tokens)
+    cyc.cycle(t, a, wdev, q_row=qstand)
+    torch.cuda.synchronize()
+    plan = cyc.plan(t, a)
+    cache = _oracle_cache_from(k, v, plan.pos0, s)
+    st = O.SeqState(t=t, a=a, tokens=list(tokens))
+    pf = None
+    if s.temperature > 0:
+        pf = {"q": cyc.ring[plan.ring_draft].cpu().numpy()}
+        if plan.verifies:
+            pf["p"] = cyc.p.cpu().numpy()
+    out = OC.run_cycle(om, st, cache, {}, s.temperature, wblock,
+                       q_override=None if qstand is None else qstand.cpu().numpy(), probs_from=pf)
+    assert rel_err(f64(cyc.g[:plan.M]), out.g) < TOL_BF16
+    assert rel_err(f64(cyc.h_last), out.h_last) < TOL_BF16
+    dl = cyc.dlogits.cpu().numpy()
+    assert rel_err(dl, out.draft_logits) < TOL_BF16
+    if s.temperature == 0:
+        assert int(cyc.dtoken.item()) == O.argmax_first(dl)
+    assert int(cyc.dtoken.item()) == out.drafted
+    if plan.verifies:
+        assert rel_err(cyc.tlogits.cpu().numpy(), out.target_logits) < TOL_BF16
+        assert (int(cyc.n_accept.item()), int(cyc.next_token.item())) == (out.n_accept,
+                                                                         out.next_token)
+    assert cyc.read_state() == (st.t, st.a, st.commits, st.cycles)
+    assert cyc.tokens[:st.t].tolist() == st.tokens
+    return out
+
+
+@pytest.mark.parametrize("key", ["qwen35_4b_n4_ls1_greedy", "qwen35_9b_n16_ls4_t1"],
+                         ids=["4b_n4_greedy", "9b_n16_sampled"])
+def test_cycle_full_size(key):
+    """Whole cycles (features -> PDM -> draft head -> target head + verify ->
+    rollback) at the Qwen3.5-4B-shaped n = 4 greedy workload and the 9B-shaped
+    n = 16, L_s = 4, T = 1 workload at context 4096, on a seeded committed cache:
+    a saturated cycle whose verification accepts, one forced to reject (the state
+    rolls back to t-n+1 plus the corrected token), and a partial cycle.  Rows within
+    the bf16 tolerance, decisions and state bit-exact on the device's rows."""
+    s = synth.SHAPES[key]
+    say("full cycle", key)
+    ci = make_inputs(s, device=DEV)
+    model = device_model(ci)
+    cyc = SpdCycle(model, s.temperature)
+    om = OC.model_from_inputs(ci)
+    k, v = synth.kv_cache(s, model.T_cap, device=DEV)
+    t, n = s.ctx, s.n
+    cand = t - n + 1
+    wb = synth.cycle_words(4, seed=29)
+    qstand = None
+    if s.temperature > 0:
+        qstand = torch.softmax(synth.draft_row_logits(s.V, 3.0, device=DEV, seed=8, name="q_standin"), 0)
+        wb[:2, 0] = np.uint64(((1 << 24) - 1) << 40)   # R = 2^24 - 1: accept iff q(x) <= p(x)
+    wdev = synth.words_tensor(wb, DEV)
+    tokens = list(range(t))
+    # probe: the target row of the exiting token does not depend on the token under
+    # verification, so one saturated cycle gives the row the forced cases choose from
+    say("full cycle probe", key)
+    _full_cycle(cyc, om, s, k, v, t, n, tokens, wb[0], wdev[0], qstand)
+    if s.temperature == 0:
+        best = O.argmax_first(cyc.tlogits.cpu().numpy())
+        x_acc, x_rej = best, (best + 1) % s.V
+    else:
+        p = cyc.p.cpu().numpy().astype(np.float64)
+        q = qstand.cpu().numpy().astype(np.float64)
+        x_acc, x_rej = int(np.argmax(p - q)), int(np.argmax(q - p))
+        assert p[x_acc] >= q[x_acc] and q[x_rej] > p[x_rej]
+    for c, (x, want) in enumerate(((x_acc, 1), (x_rej, 0))):
+        say("full cycle", key, "forced", want)
+        toks = list(tokens)
+        toks[cand] = x
+        out = _full_cycle(cyc, om, s, k, v, t, n, toks, wb[c], wdev[c], qstand)
+        assert out.n_accept == want
+        if want == 0:
+            assert cyc.read_state()[:2] == (t - n + 2, 1)
+            assert out.next_token >= 0 and cyc.tokens[cand].item() == out.next_token
+    say("full cycle", key, "partial")
+    _full_cycle(cyc, om, s, k, v, t, 3, tokens, wb[3], wdev[3], qstand)
+
+
+# ------------------------------------------------------------------ graph capture
+
+def test_cycle_graph_replay_matches_eager():
+    """A saturated and a partial headline cycle captured into one HIP graph (two
+    streams, the side head joined by events) and replayed several times, with
+    eager work and synchronisations between the replays: every replay's rows,
+    draft, target decision and q row equal the eager run bit for bit (the
+    library records no memset; its arrival counters return to zero)."""
+    s = synth.HEADLINE
+    ci = make_inputs(s, device=DEV)
+    model = device_model(ci)
+    cyc = SpdCycle(model, s.temperature)
+    k, v = synth.kv_cache(s, model.T_cap, device=DEV)
+    t = s.ctx
+    wdev = synth.words_tensor(synth.cycle_words(2, seed=31), DEV)
+    qstand = torch.softmax(synth.draft_row_logits(s.V, 3.0, device=DEV, seed=8, name="q_standin"), 0)
+    x = torch.full((1,), 17, dtype=torch.int32, device=DEV)
+
+    def run():
+        cyc.k_cache.copy_(k)
+        cyc.v_cache.copy_(v)
+        for c, a in enumerate((s.n, 3)):
+            cyc.cycle(t, a, wdev[c], q_row=qstand, x_ptr=x.data_ptr())
+        return [cyc.g[:4].clone(), cyc.h_last.clone(), cyc.dlogits.clone(), cyc.dtoken.clone(),
+                cyc.tlogits.clone(), cyc.p.clone(), cyc.n_accept.clone(), cyc.next_token.clone(),
+                cyc.ring.clone(), cyc.k_cache.clone()]
+
+    say("graph eager")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ref = run()
+        ref = run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    keep = {}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        outs = run()
+    torch.cuda.synchronize()
+    for r in range(4):
+        say("graph replay", r)
+        g.replay()
+        torch.cuda.synchronize()
+        for a_, b_ in zip(outs, ref):
+            assert torch.equal(a_, b_), r
+        cyc.features(t - 4, 4, 3)        # eager work between replays
+        torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ guard regions
+
+GUARD = 4096  # bytes of sentinel on each side of a buffer
+
+
+class Guarded:
+    """A device buffer with sentinel bytes before and after it: a write outside
+    the buffer changes the sentinel."""
+
+    def __init__(self, shape, dtype, fill=None):
+        n = int(np.prod(shape)) * torch.tensor([], dtype=dtype).element_size()
+        self.raw = torch.empty(n + 2 * GUARD, dtype=torch.uint8, device=DEV)
+        self.pattern = torch.tensor([0xA5, 0x5A, 0xC3, 0x3C], dtype=torch.uint8, device=DEV)
+        self.raw.copy_(self.pattern.repeat((n + 2 * GUARD) // 4 + 1)[:n + 2 * GUARD])
+        self.t = self.raw[GUARD:GUARD + n].view(dtype).view(*shape)
+        if fill is not None:
+            self.t.copy_(fill)
+        self.n = n
+
+    def intact(self):
+        rep = self.pattern.repeat(GUARD // 4)
+        return bool(torch.equal(self.raw[:GUARD], rep) and torch.equal(self.raw[GUARD + self.n:], rep))
+
+
+@pytest.mark.parametrize("shape,M,a,rows", [(synth.HEADLINE, 9, 8, 1), (synth.HEADLINE, 4, 3, 3),
+                                            (synth.HEADLINE, 2048, 0, 1),
+                                            (SMALL_BF16.with_(V=4097), 7, 6, 2),
+                                            (synth.TINY.with_(V=517), 3, 2, 5)],
+                         ids=["headline_sat", "headline_partial", "headline_prefill",
+                              "small_ragged", "tiny_ragged"])
+def test_calls_write_only_their_buffers(shape, M, a, rows):
+    """Every output and the workspace of each call sit between sentinel regions:
+    after the feature call, the PDM step, the LM head (T = 0 and T = 1, top-k on
+    and off), the verify and the rollback, no sentinel byte has changed, at full
+    and ragged sizes."""
+    s = shape
+    say("guard", s.name, M, a, rows)
+    ci = make_inputs(s, device=DEV)
+    model = device_model(ci)
+    c = model.cfg
+    T_cap = model.T_cap
+    pos0 = s.ctx - 1 - a if a > 0 else 0
+    wdt = torch.bfloat16 if s.dtype == synth.BF16 else torch.float32
+    ws = Guarded((max(spd.spd_workspace_size(spd.SPD_CALL_FUSE, c, M),
+                      spd.spd_workspace_size(spd.SPD_CALL_PDM, c, M, 0, T_cap)),), torch.uint8,
+                 fill=torch.zeros(1, dtype=torch.uint8, device=DEV))
+    g = Guarded((M, s.d), torch.float32)
+    spd.spd_fuse_features(c, ci.store, T_cap, len(model.store_layers), model.slot_tab, pos0, M, a,
+                          ci.fc_norm, ci.w_fc, g.t, ws.t)
+    kc = Guarded((s.Ls, s.Hkv, T_cap, s.hd), wdt, fill=torch.zeros(1, dtype=wdt, device=DEV))
+    vc = Guarded((s.Ls, s.Hkv, s.hd, T_cap), wdt, fill=torch.zeros(1, dtype=wdt, device=DEV))
+    h = Guarded((s.d,), torch.float32)
+    spd.spd_pdm_step(c, model.layer_arr, ci.final_norm, kc.t, vc.t, T_cap, g.t, pos0, M, h.t, ws.t)
+    torch.cuda.synchronize()
+    for b in (ws, g, kc, vc, h):
+        assert b.intact()
+    hr = synth.normal((rows, s.d), 1.0, device=DEV, seed=5, name="guard_h")
+    words = synth.words_tensor(synth.cycle_words(rows, seed=6)[:, :1].copy(), DEV)
+    for T, top_k in ((0.0, 0), (1.0, 0), (1.0, min(50, s.V))):
+        cfg = spd.spd_config.from_buffer_copy(c)
+        cfg.top_k = top_k
+        wsh = Guarded((spd.spd_workspace_size(spd.SPD_CALL_LM_HEAD, cfg, rows),), torch.uint8,
+                      fill=torch.zeros(1, dtype=torch.uint8, device=DEV))
+        lg = Guarded((rows, s.V), torch.float32)
+        pr = Guarded((rows, s.V), torch.float32)
+        tok = Guarded((rows,), torch.int32)
+        spd.spd_lm_head(cfg, ci.w_dlm, hr, rows, T, words if T > 0 else None, lg.t,
+                        pr.t if T > 0 else None, tok.t, wsh.t)
+        torch.cuda.synchronize()
+        for b in (wsh, lg, pr, tok):
+            assert b.intact(), (T, top_k)
+    # verify (streaming, T = 1, forced rejection so the residual path runs) and rollback
+    p = torch.softmax(synth.normal((s.V,), 3.0, device=DEV, seed=7, name="gp"), 0).contiguous()
+    q = torch.softmax(synth.normal((s.V,), 3.0, device=DEV, seed=8, name="gq"), 0).contiguous()
+    x = int(torch.argmax(q - p).item())
+    xd = torch.tensor([x], dtype=torch.int32, device=DEV)
+    vw = np.zeros((2, 2), np.uint64)
+    vw[0, 0] = np.uint64(((1 << 24) - 1) << 40)
+    vwd = synth.words_tensor(vw, DEV)
+    wsv = Guarded((spd.spd_workspace_size(spd.SPD_CALL_VERIFY, c, 1, 1),), torch.uint8,
+                  fill=torch.zeros(1, dtype=torch.uint8, device=DEV))
+    na = Guarded((1,), torch.int32)
+    nt = Guarded((1,), torch.int32)
+    spd.spd_verify(1, 1, s.V, 1.0, 0, p, q, xd, vwd, na.t, nt.t, wsv.t)
+    st = Guarded((4,), torch.int32, fill=torch.tensor([s.ctx, s.n, 0, 0], dtype=torch.int32, device=DEV))
+    toks = Guarded((T_cap,), torch.int32, fill=torch.zeros(1, dtype=torch.int32, device=DEV))
+    spd.spd_rollback(st.t, s.n, xd, na.t, nt.t, toks.t, T_cap)
+    torch.cuda.synchronize()
+    assert int(na.t.item()) == 0
+    for b in (wsv, na, nt, st, toks):
+        assert b.intact()
