@@ -26,6 +26,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 HEAD_EVERY = 4      # draft-head calls timed in the loop: every 4th cycle
+REPEATS = 5         # the timed loop runs this many times; value is the median
 
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "spd_lm_head_traffic_headline.md")
@@ -75,9 +76,22 @@ def algorithmic_bytes(s, a: int) -> dict:
     return out
 
 
-def cpu_baseline(s, ci, sched, words, qstand_np, x, budget_s=12.0):
+def cpu_baseline(s, ci, sched, words, qstand_np, x, budget_s=12.0, budget_1t=4.0):
     """The oracle (numpy float64, incremental PDM) on this host, on a time-bounded
-    sample of the same cycles."""
+    sample of the same cycles: with every BLAS thread, then with one."""
+    res = _cpu_run(s, ci, sched, words, qstand_np, x, budget_s)
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            one = _cpu_run(s, ci, sched, words, qstand_np, x, budget_1t)
+        res["one_thread"] = {"value": one["value"], "unit": "cycles/s", "cores": 1,
+                             "sample": one["sample"]}
+    except ImportError:  # pragma: no cover
+        pass
+    return res
+
+
+def _cpu_run(s, ci, sched, words, qstand_np, x, budget_s):
     from oracle import cycle as OC
     from oracle import spd as O
     import synth
@@ -115,12 +129,36 @@ def cpu_baseline(s, ci, sched, words, qstand_np, x, budget_s=12.0):
                       f"on a seeded committed cache), {el:.1f} s"}
 
 
+def _model(spd, synth, s, dev, **kw):
+    """Seeded device weights and an SpdModel of shape s (the anchor store holds the
+    layers the library's slot table reads)."""
+    from pipeline_draft_step_amd.cycle import DeviceWeights, SpdModel
+    cfg0 = spd.make_config(L=s.L, n=s.n, m=s.m, d=s.d, Ls=s.Ls, Hq=s.Hq, Hkv=s.Hkv, hd=s.hd, dff=s.dff,
+                           V=s.V, dtype=s.dtype, anchor_mode=s.anchor_mode, norm_k0=s.norm_k0)
+    ci = synth.cycle_inputs(s, spd.spd_slot_table(cfg0, list(s.anchors))[1], device=dev)
+    w = DeviceWeights(store=ci.store, h_final=ci.h_final, fc_norm=ci.fc_norm, w_fc=ci.w_fc,
+                      layers=ci.layers, final_norm=ci.final_norm, w_dlm=ci.w_dlm, w_tlm=ci.w_tlm)
+    model = SpdModel(L=s.L, n=s.n, anchors=s.anchors, d=s.d, Ls=s.Ls, Hq=s.Hq, Hkv=s.Hkv,
+                     hd=s.hd, dff=s.dff, V=s.V, dtype=s.dtype, weights=w, eps=s.eps,
+                     rope_theta=s.rope_theta, **kw)
+    return ci, w, model
+
+
+def _stats(ms_list):
+    ms = sorted(ms_list)
+    return {"median_ms": round(float(np.median(ms)), 4), "min_ms": round(ms[0], 4),
+            "max_ms": round(ms[-1], 4), "repeats": len(ms)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--repeats", type=int, default=REPEATS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="headline cycles only (no other workloads or per-call breakdowns)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with a plain 256 MiB device-to-device copy, the known-size "
@@ -134,19 +172,12 @@ def main():
     import torch
     import synth
     import pipeline_draft_step_amd as spd
-    from pipeline_draft_step_amd.cycle import DeviceWeights, SpdCycle, SpdModel
+    from pipeline_draft_step_amd.cycle import SpdCycle, SpdModel
 
     spd.lib()
     dev = "cuda"
     s = synth.HEADLINE
-    cfg0 = spd.make_config(L=s.L, n=s.n, m=s.m, d=s.d, Ls=s.Ls, Hq=s.Hq, Hkv=s.Hkv, hd=s.hd, dff=s.dff,
-                           V=s.V, dtype=s.dtype, anchor_mode=s.anchor_mode, norm_k0=s.norm_k0)
-    ci = synth.cycle_inputs(s, spd.spd_slot_table(cfg0, list(s.anchors))[1], device=dev)
-    w = DeviceWeights(store=ci.store, h_final=ci.h_final, fc_norm=ci.fc_norm, w_fc=ci.w_fc,
-                      layers=ci.layers, final_norm=ci.final_norm, w_dlm=ci.w_dlm, w_tlm=ci.w_tlm)
-    model = SpdModel(L=s.L, n=s.n, anchors=s.anchors, d=s.d, Ls=s.Ls, Hq=s.Hq, Hkv=s.Hkv,
-                     hd=s.hd, dff=s.dff, V=s.V, dtype=s.dtype, weights=w, eps=s.eps,
-                     rope_theta=s.rope_theta)
+    ci, w, model = _model(spd, synth, s, dev)
     cyc = SpdCycle(model, s.temperature, device=dev)
     t = s.ctx
     cyc.set_state(t, s.n, list(range(t)))
@@ -163,52 +194,60 @@ def main():
     x = int(x_dev.item())
     torch.cuda.synchronize()
 
-    main = torch.cuda.current_stream()
+    def one_cycle(cyc, t, a, wblock, timed_head=None):
+        """SpdCycle.cycle, with optional events around the draft head."""
+        main = torch.cuda.current_stream()
+        plan = cyc.plan(t, a)
+        if plan.verifies:  # target head + verify on the side stream
+            cyc.ev_fork.record(main)
+            cyc.side.wait_event(cyc.ev_fork)
+            with torch.cuda.stream(cyc.side):
+                cyc.target_and_verify(plan, wblock, q_row=qstand_of[id(cyc)], x_ptr=x_of[id(cyc)],
+                                      ws=cyc.ws_side, background=True)
+            cyc.ev_join.record(cyc.side)
+        cyc.features(plan.pos0, plan.M, a)
+        cyc.pdm(plan.pos0, plan.M)
+        if timed_head is not None:
+            timed_head[0].record()
+        cyc.draft(plan, wblock)
+        if timed_head is not None:
+            timed_head[1].record()
+        if plan.verifies:
+            main.wait_event(cyc.ev_join)
+        cyc.rollback()
 
-    def run_cycles(cyc, steps):
-        """warmup + `steps` timed cycles; returns (ms per cycle, mean draft-head ms, wall s)"""
+    qstand_of = {id(cyc): qstand}
+    x_of = {id(cyc): x_dev.data_ptr()}
+
+    def run_cycles(cyc, t, sched, words, steps, repeats, head_events=True):
+        """warmup, then `repeats` timed loops of `steps` cycles; returns (ms per cycle of
+        each loop, mean draft-head ms, wall s of the last loop)."""
         for c in range(args.warmup):
-            cyc.cycle(t, sched[c], words[c], q_row=qstand, x_ptr=x_dev.data_ptr())
+            one_cycle(cyc, t, sched[c], words[c])
         torch.cuda.synchronize()
-        # timed region: K cycles; events bracket the draft-head call of every HEAD_EVERY-th
-        # cycle (a timing event costs a few us of GPU time; on every cycle they would
-        # slow the loop they measure)
-        head_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(0, steps, HEAD_EVERY)]
-        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        wall0 = time.perf_counter()
-        start.record()
-        for i in range(steps):
-            c = args.warmup + i
-            a = sched[c]
-            pos0, M = t - 1 - a, a + 1
-            sat = a == s.n
-            if sat:  # target head + verify on the side stream (as SpdCycle.cycle does)
-                cyc.ev_fork.record(main)
-                cyc.side.wait_event(cyc.ev_fork)
-                with torch.cuda.stream(cyc.side):
-                    cyc.target_and_verify(t, words[c], q_row=qstand, x_ptr=x_dev.data_ptr(),
-                                          ws=cyc.ws_side, background=True)
-                cyc.ev_join.record(cyc.side)
-            cyc.features(pos0, M, a)
-            cyc.pdm(pos0, M)
-            timed_head = i % HEAD_EVERY == 0
-            if timed_head:
-                head_ev[i // HEAD_EVERY][0].record()
-            cyc.draft(t, words[c])
-            if timed_head:
-                head_ev[i // HEAD_EVERY][1].record()
-            if sat:
-                main.wait_event(cyc.ev_join)
-            cyc.rollback()
-        stop.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - wall0
-        head = float(np.mean([e0.elapsed_time(e1) for e0, e1 in head_ev]))
-        return start.elapsed_time(stop) / steps, head, wall
+        loops, heads, wall = [], [], 0.0
+        for _ in range(repeats):
+            # events bracket the draft-head call of every HEAD_EVERY-th cycle (a timing
+            # event costs a few us of GPU time; on every cycle they would slow the loop)
+            hev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(0, steps, HEAD_EVERY)] if head_events else []
+            start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            wall0 = time.perf_counter()
+            start.record()
+            for i in range(steps):
+                c = args.warmup + i
+                th = hev[i // HEAD_EVERY] if head_events and i % HEAD_EVERY == 0 else None
+                one_cycle(cyc, t, sched[c], words[c], th)
+            stop.record()
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - wall0
+            loops.append(start.elapsed_time(stop) / steps)
+            heads += [e0.elapsed_time(e1) for e0, e1 in hev]
+        return loops, (float(np.mean(heads)) if heads else None), wall
 
-    ms_per_step, head_ms, wall = run_cycles(cyc, args.steps)
+    loops, head_ms, wall = run_cycles(cyc, t, sched, words, args.steps, args.repeats)
+    ms_per_step = float(np.median(loops))
     cycles_per_s = 1000.0 / ms_per_step
 
     timed = sched[args.warmup:]
@@ -217,24 +256,79 @@ def main():
     head_bytes = algorithmic_bytes(s, s.n)["draft_head"]
     achieved = head_bytes / (head_ms * 1e-3) / 1e9
 
+    result = {
+        "metric": "draft+verify cycles/s + achieved HBM GB/s, d=2560 n=8 vocab 151936, 1 GPU",
+        "value": round(cycles_per_s, 2),
+        "unit": "cycles/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "spd_cycle_qwen35_4b_shape_n8_ls2_t1_mix", "d": s.d, "n": s.n,
+                   "L": s.L, "anchors": list(s.anchors), "Ls": s.Ls, "heads": [s.Hq, s.Hkv, s.hd],
+                   "dff": s.dff, "vocab": s.V, "context": s.ctx, "temperature": s.temperature,
+                   "mix": "50% saturated / 50% partial a~U{1..7}", "batch": 1,
+                   "mode": "independent cycles"},
+        "timed_loops": dict(_stats(loops), steps_each=args.steps,
+                            cycles_per_s_each=[round(1000.0 / v, 1) for v in loops]),
+        "achieved_hbm_gbs": round(mean_bytes * cycles_per_s / 1e9, 1),
+        "algorithmic_MB_per_cycle": round(mean_bytes / 1e6, 2),
+        "roofline": {"bound": "hbm", "kernel": "spd_lm_head (vocab GEMV + softmax/sample)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                     "avg_us": round(head_ms * 1000.0, 2),
+                     "algorithmic_bytes_per_launch": int(head_bytes)},
+        "wall_s_timed": round(wall, 3),
+    }
+
+    if not args.no_extra:
+        extra(args, torch, synth, spd, SpdCycle, SpdModel, s, ci, w, model, cyc, t, sched, words,
+              qstand, x_dev, one_cycle, run_cycles, qstand_of, x_of, head_ms, result)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(s, ci, timed[:64],
+                                              words_np[args.warmup:], qstand.cpu().numpy(), x,
+                                              budget_s=args.cpu_budget)
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+    print(json.dumps(result), flush=True)
+
+
+def extra(args, torch, synth, spd, SpdCycle, SpdModel, s, ci, w, model, cyc, t, sched, words,
+          qstand, x_dev, one_cycle, run_cycles, qstand_of, x_of, head_ms, result):
+    """Per-call breakdown, graph-captured cycles, prefill, the sampling filters, the
+    draft tree, and the other workloads (n = 4 greedy, 9B-shaped n = 16, the batched
+    verify)."""
+    dev = "cuda"
+    total = len(sched)
+
     # per-call breakdown (separate instrumented pass over one saturated and one partial cycle)
     calls = {}
     for a in (s.n, 3):
+        plan = cyc.plan(t, a)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
         reps = 20
         acc = np.zeros(6)
         for r in range(reps):
             c = r % total
-            pos0, M = t - 1 - a, a + 1
             ev[0].record()
-            cyc.features(pos0, M, a)
+            cyc.features(plan.pos0, plan.M, a)
             ev[1].record()
-            cyc.pdm(pos0, M)
+            cyc.pdm(plan.pos0, plan.M)
             ev[2].record()
-            cyc.draft(t, words[c])
+            cyc.draft(plan, words[c])
             ev[3].record()
-            if a == s.n:
-                cyc.target_and_verify(t, words[c], q_row=qstand, x_ptr=x_dev.data_ptr())
+            if plan.verifies:
+                cyc.target_and_verify(plan, words[c], q_row=qstand, x_ptr=x_dev.data_ptr())
             ev[4].record()
             cyc.rollback()
             ev[5].record()
@@ -246,6 +340,43 @@ def main():
             "draft_head_us": round(acc[2], 1), "target_head_verify_us": round(acc[3], 1),
             "rollback_us": round(acc[4], 1), "cycle_us": round(acc[5], 1),
             "algorithmic_MB": round(sum(algorithmic_bytes(s, a).values()) / 1e6, 1)}
+    result["calls"] = calls
+
+    # the same timed schedule captured into HIP graphs (GRAPH_CYCLES cycles per graph,
+    # both streams), replayed back to back
+    GRAPH_CYCLES = 8
+    nsteps = max(GRAPH_CYCLES, (args.steps // GRAPH_CYCLES) * GRAPH_CYCLES)
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for c in range(GRAPH_CYCLES):
+            one_cycle(cyc, t, sched[c], words[c])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for g0 in range(0, nsteps, GRAPH_CYCLES):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(g0, g0 + GRAPH_CYCLES):
+                c = args.warmup + (i % args.steps)
+                one_cycle(cyc, t, sched[c], words[c])
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for g in graphs[:2]:
+        g.replay()
+    torch.cuda.synchronize()
+    gl = []
+    for _ in range(args.repeats):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for g in graphs:
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        gl.append(e0.elapsed_time(e1) / nsteps)
+    result["graph_captured"] = dict(_stats(gl), cycles_per_s=round(1000.0 / float(np.median(gl)), 2),
+                                    cycles_per_graph=GRAPH_CYCLES, steps=nsteps)
+    del graphs
 
     # prefill feature call (every row at depth n): the anchor gather plus the
     # MFMA-tiled large-M FC GEMM, timed as a whole on the launch stream
@@ -264,10 +395,11 @@ def main():
     pre_us = pe0.elapsed_time(pe1) / reps * 1000.0
     pre_flops = 2.0 * Mp * s.d * (m_anch * s.d)
     pre_tflops = pre_flops / (pre_us * 1e-6) / 1e12
-    prefill_fc = {"M": Mp, "N": s.d, "K": m_anch * s.d, "call_us": round(pre_us, 2),
-                  "includes": "anchor gather + RMS scale + FC GEMM (one spd_fuse_features call)",
-                  "achieved_tflops": round(pre_tflops, 1), "bound": "mfma",
-                  "peak_tflops": BF16_PEAK_TFLOPS, "frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4)}
+    result["prefill_fc"] = {
+        "M": Mp, "N": s.d, "K": m_anch * s.d, "call_us": round(pre_us, 2),
+        "includes": "anchor gather + RMS scale + FC GEMM (one spd_fuse_features call)",
+        "achieved_tflops": round(pre_tflops, 1), "bound": "mfma", "peak_tflops": BF16_PEAK_TFLOPS,
+        "frac": round(pre_tflops / BF16_PEAK_TFLOPS, 4)}
 
     # whole prefill of the 2039-row prefix (features + PDM over every layer); it
     # rebuilds the same cache from the same inputs
@@ -280,8 +412,8 @@ def main():
         cyc.prefill(P)
     pf1.record()
     torch.cuda.synchronize()
-    prefill = {"rows": P, "us": round(pf0.elapsed_time(pf1) / 3 * 1000.0, 1),
-               "includes": "spd_fuse_features + spd_pdm_step over the prefix, large-M MFMA path"}
+    result["prefill"] = {"rows": P, "us": round(pf0.elapsed_time(pf1) / 3 * 1000.0, 1),
+                         "includes": "spd_fuse_features + spd_pdm_step over the prefix, large-M MFMA path"}
 
     # the pages' sampling setting (T = 1, top-k = 50, top-p = 1.0) on both heads: the
     # same cycles through a second model whose heads filter
@@ -291,15 +423,97 @@ def main():
     cyc_k = SpdCycle(model_k, s.temperature, device=dev)
     cyc_k.set_state(t, s.n, list(range(t)))
     cyc_k.prefill(t - 1 - s.n)
-    ms_k, head_k, _ = run_cycles(cyc_k, max(args.steps // 2, 1))
-    top_k50 = {"top_k": 50, "top_p": 1.0, "cycles_per_s": round(1000.0 / ms_k, 2),
-               "ms_per_step": round(ms_k, 4), "draft_head_us": round(head_k * 1000.0, 2),
-               "draft_head_us_unfiltered": round(head_ms * 1000.0, 2)}
+    qstand_of[id(cyc_k)], x_of[id(cyc_k)] = qstand, x_dev.data_ptr()
+    lk, head_k, _ = run_cycles(cyc_k, t, sched, words, max(args.steps // 2, 1), 3)
+    ms_k = float(np.median(lk))
+    result["sampling_top_k50"] = {
+        "top_k": 50, "top_p": 1.0, "cycles_per_s": round(1000.0 / ms_k, 2),
+        "ms_per_step": round(ms_k, 4), "draft_head_us": round(head_k * 1000.0, 2),
+        "draft_head_us_unfiltered": round(head_ms * 1000.0, 2)}
     del cyc_k, model_k
 
-    # greedy width-4 draft tree at the saturated depth: features and PDM over the
-    # 29 tree nodes (root + 7 levels of 4), the top-4 children of the 4 deepest
-    # nodes, greedy verification of the 4 oldest siblings
+    result["draft_tree_w4"] = tree_step(torch, synth, spd, s, w, model, cyc, t)
+
+    # the other workloads: Qwen3.5-4B-shaped n = 4 (L_s = 1, greedy) and 9B-shaped
+    # n = 16 (L_s = 4, T = 1, context 4096), saturated every cycle, on a seeded
+    # committed cache
+    del cyc
+    torch.cuda.empty_cache()
+    others = {}
+    for key, name in (("qwen35_4b_n4_ls1_greedy", "spd_cycle_qwen35_4b_shape_n4_ls1_t0"),
+                      ("qwen35_9b_n16_ls4_t1", "spd_cycle_qwen35_9b_shape_n16_ls4_t1")):
+        so = synth.SHAPES[key]
+        ci_o, w_o, model_o = _model(spd, synth, so, dev)
+        cyc_o = SpdCycle(model_o, so.temperature, device=dev)
+        k, v = synth.kv_cache(so, model_o.T_cap, device=dev)
+        cyc_o.k_cache.copy_(k)
+        cyc_o.v_cache.copy_(v)
+        del k, v
+        to = so.ctx
+        cyc_o.set_state(to, so.n, list(range(to)))
+        q_o = torch.softmax(synth.draft_row_logits(so.V, 3.0, device=dev, seed=8, name="q_standin"), 0)
+        qstand_of[id(cyc_o)], x_of[id(cyc_o)] = q_o, x_dev.data_ptr()
+        steps_o = max(args.steps // 4, 8)
+        sched_o = [so.n] * (args.warmup + steps_o)
+        words_o = synth.words_tensor(synth.cycle_words(args.warmup + steps_o), dev)
+        lo, _, _ = run_cycles(cyc_o, to, sched_o, words_o, steps_o, 3, head_events=False)
+        ms_o = float(np.median(lo))
+        mb = sum(algorithmic_bytes(so, so.n).values())
+        gbs = mb * (1000.0 / ms_o) / 1e9
+        others[name] = {"d": so.d, "n": so.n, "Ls": so.Ls, "vocab": so.V, "context": so.ctx,
+                        "temperature": so.temperature, "saturated": True,
+                        "cycles_per_s": round(1000.0 / ms_o, 2), "ms_per_step": round(ms_o, 4),
+                        "timed_loops": _stats(lo), "algorithmic_MB_per_cycle": round(mb / 1e6, 1),
+                        "achieved_hbm_gbs": round(gbs, 1),
+                        "frac_of_hbm_ceiling": round(gbs / HBM_PEAK_GBS, 4)}
+        del cyc_o, model_o, w_o, ci_o, q_o
+        torch.cuda.empty_cache()
+
+    # batched verify stress: 64 sequences x gamma = 7 drafts, bonus on full accept,
+    # 100 back-to-back calls.  Algorithmic bytes of one call: the 2 gamma scalars per
+    # sequence it tests, then the rows its outcome needs (residual: p and q of the
+    # rejected position; bonus: p of position gamma) read once
+    vs = synth.VERIFY_STRESS
+    p, q, draft, vwords = synth.verify_stress_inputs(vs, device=dev)
+    vw = synth.words_tensor(vwords, dev)
+    na = torch.zeros(vs.B, dtype=torch.int32, device=dev)
+    nt = torch.zeros(vs.B, dtype=torch.int32, device=dev)
+    cfgv = spd.make_config(L=1, n=2, m=1, d=64, Ls=0, Hq=1, Hkv=1, hd=64, dff=64, V=vs.V, dtype=1)
+    wsv = torch.zeros(spd.spd_workspace_size(spd.SPD_CALL_VERIFY, cfgv, vs.B, vs.gamma),
+                      dtype=torch.uint8, device=dev)
+    for _ in range(5):
+        spd.spd_verify(vs.B, vs.gamma, vs.V, vs.temperature, vs.bonus, p, q, draft, vw, na, nt, wsv)
+    torch.cuda.synchronize()
+    nacc = na.cpu().numpy()
+    rows_read = sum(1 if int(k) == vs.gamma else 2 for k in nacc)
+    scalars = sum(2 * (min(int(k) + 1, vs.gamma)) for k in nacc)
+    vbytes = rows_read * vs.V * 4 + scalars * 4 + vs.B * vs.gamma * 4 + vs.B * 8
+    vl = []
+    for _ in range(args.repeats):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(100):
+            spd.spd_verify(vs.B, vs.gamma, vs.V, vs.temperature, vs.bonus, p, q, draft, vw, na, nt,
+                           wsv)
+        e1.record()
+        torch.cuda.synchronize()
+        vl.append(e0.elapsed_time(e1) / 100)
+    vms = float(np.median(vl))
+    others["verify_stress_b64_g7"] = {
+        "B": vs.B, "gamma": vs.gamma, "vocab": vs.V, "bonus": vs.bonus, "calls": 100,
+        "calls_per_s": round(1000.0 / vms, 1), "us_per_call": round(vms * 1000.0, 2),
+        "timed_loops": _stats(vl), "mean_accepted": round(float(nacc.mean()), 3),
+        "algorithmic_MB_per_call": round(vbytes / 1e6, 2),
+        "achieved_gbs": round(vbytes / (vms * 1e-3) / 1e9, 1),
+        "dense_MB_per_call": round((p.numel() + q.numel()) * 4 / 1e6, 1)}
+    result["other_workloads"] = others
+
+
+def tree_step(torch, synth, spd, s, w, model, cyc, t):
+    """Greedy width-4 draft tree at the saturated depth: features and PDM over the 29
+    tree nodes (root + 7 levels of 4), the top-4 children of the 4 deepest nodes,
+    greedy verification of the 4 oldest siblings."""
+    dev = "cuda"
     W_tree, a_tree = 4, s.n - 1
     parents, prev = [-1], [0]
     for lvl in range(a_tree):
@@ -368,55 +582,12 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     sib_t1_us = e0.elapsed_time(e1) / reps * 1000.0
-    tree = {"width": W_tree, "levels": a_tree, "nodes": Mt, "fuse_us": round(tacc[0], 1),
+    return {"width": W_tree, "levels": a_tree, "nodes": Mt, "fuse_us": round(tacc[0], 1),
             "pdm_us": round(tacc[1], 1), "draft_head_top4_x4rows_us": round(tacc[2], 1),
             "verify_siblings_us": round(tacc[3], 1), "step_us": round(float(tacc.sum()), 1),
             "verify_siblings_t1_all_rejected_us": round(sib_t1_us, 1),
             "note": "calls in sequence, each timed alone (the chain cycle's calls: see calls)"}
 
-    result = {
-        "metric": "draft+verify cycles/s + achieved HBM GB/s, d=2560 n=8 vocab 151936, 1 GPU",
-        "value": round(cycles_per_s, 2),
-        "unit": "cycles/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "spd_cycle_qwen35_4b_shape_n8_ls2_t1_mix", "d": s.d, "n": s.n,
-                   "L": s.L, "anchors": list(s.anchors), "Ls": s.Ls, "heads": [s.Hq, s.Hkv, s.hd],
-                   "dff": s.dff, "vocab": s.V, "context": s.ctx, "temperature": s.temperature,
-                   "mix": "50% saturated / 50% partial a~U{1..7}", "batch": 1,
-                   "mode": "independent cycles"},
-        "achieved_hbm_gbs": round(mean_bytes * cycles_per_s / 1e9, 1),
-        "algorithmic_MB_per_cycle": round(mean_bytes / 1e6, 2),
-        "roofline": {"bound": "hbm", "kernel": "spd_lm_head (vocab GEMV + softmax/sample)",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "avg_us": round(head_ms * 1000.0, 2),
-                     "algorithmic_bytes_per_launch": int(head_bytes)},
-        "calls": calls,
-        "prefill_fc": prefill_fc,
-        "prefill": prefill,
-        "sampling_top_k50": top_k50,
-        "draft_tree_w4": tree,
-        "wall_s_timed": round(wall, 3),
-    }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(s, ci, timed[:64],
-                                              words_np[args.warmup:], qstand.cpu().numpy(), x,
-                                              budget_s=args.cpu_budget)
-    if args.copy_calibration:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-    print(json.dumps(result), flush=True)
 
 
 if __name__ == "__main__":
