@@ -117,10 +117,14 @@ def test_fuse_features_drawn_configs():
                                      t=t, a=a))
         ci = make_inputs(shape, device=DEV, with_heads=False, T_cap=(t + 15) // 8 * 8, seed=case)
         model = device_model(ci)
-        cyc = SpdCycle(model, 0.0)
         om = OC.model_from_inputs(ci, with_heads=False)
         out = torch.empty(M, d, device=DEV)
-        cyc.features(pos0, M, a, out=out)
+        # the feature call alone (n = 1 is drawn too: a valid feature call, though the
+        # cycle driver refuses it)
+        ws = torch.zeros(spd.spd_workspace_size(spd.SPD_CALL_FUSE, model.cfg, M), dtype=torch.uint8,
+                         device=DEV)
+        spd.spd_fuse_features(model.cfg, ci.store, model.T_cap, len(model.store_layers), model.slot_tab,
+                              pos0, M, a, ci.fc_norm, ci.w_fc, out, ws)
         torch.cuda.synchronize()
         ref = O.fuse_features(om.store, om.store_layers, list(range(pos0, pos0 + M)), row_depths(M, a, n),
                               om.fc_norm, om.w_fc, L=L, n=n, anchors=anchors, mode=mode, eps=shape.eps,
