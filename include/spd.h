@@ -330,6 +330,27 @@ int spd_verify_siblings(int32_t B, int32_t W, int32_t V, float temperature, cons
                         int32_t *accepted, int32_t *next_token, void *ws, size_t ws_bytes,
                         void *stream);
 
+/* ---------------------------------------------------------------- no allocation */
+
+/* For callers that cannot allocate device memory or pass a workspace (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same call as spd_lm_head, with its workspace in a device array of
+ * SPD_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends.  It allocates and frees nothing.  The GPU is the one `stream`
+ * belongs to (the current device for NULL).  The first call on a GPU looks up the
+ * array's address with that GPU current and clears its arrival counters with a
+ * kernel on `stream` (make that first call outside graph capture).  Returns
+ * SPD_E_WORKSPACE when spd_workspace_size(SPD_CALL_LM_HEAD, cfg, rows) exceeds
+ * SPD_NOALLOC_SCRATCH_BYTES (64 MiB: up to 16 rows with top_k <= 256 at V = 151936
+ * and d <= 4096 fit; a vocabulary of millions does not), else as spd_lm_head.  Every call on a
+ * GPU shares that GPU's array: calls that may overlap on one GPU (other streams,
+ * other host threads) race and must not be issued; the array keeps the last
+ * call's contents. */
+#define SPD_NOALLOC_SCRATCH_BYTES (64u << 20)
+int spd_lm_head_noalloc(const spd_config *cfg, const void *w_lm, const float *h, int32_t rows,
+                        float temperature, const uint64_t *words, float *logits, float *probs,
+                        int32_t *token, void *stream);
+
 const char *spd_status_string(int status);
 int spd_last_hip_error(void);
 /* Version of this interface: 3 (2: spd_config gained top_k, top_p and head_workgroups;

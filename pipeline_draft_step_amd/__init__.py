@@ -23,12 +23,13 @@ SPD_MAX_ANCHORS = 8
 SPD_MAX_STAGES = 32
 SPD_TOP_K_MAX = 256
 SPD_TREE_MAX_NODES = 64
+SPD_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTED = (
     "spd_slot_table", "spd_layout", "spd_workspace_size", "spd_fuse_features",
     "spd_pdm_step", "spd_lm_head", "spd_verify", "spd_rollback", "spd_status_string",
     "spd_last_hip_error", "spd_version", "spd_fuse_features_tree", "spd_pdm_step_tree",
-    "spd_verify_siblings", "spd_cycle_plan",
+    "spd_verify_siblings", "spd_cycle_plan", "spd_lm_head_noalloc",
 )
 
 
@@ -92,6 +93,7 @@ def lib():
         L.spd_pdm_step.argtypes = [cfgp, ctypes.POINTER(spd_layer_weights), _P, _P, _P, _I64, _P,
                                    _I32, _I32, _P, _P, _SZ, _P]
         L.spd_lm_head.argtypes = [cfgp, _P, _P, _I32, _F, _P, _P, _P, _P, _P, _SZ, _P]
+        L.spd_lm_head_noalloc.argtypes = [cfgp, _P, _P, _I32, _F, _P, _P, _P, _P, _P]
         L.spd_verify.argtypes = [_I32, _I32, _I32, _F, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
         L.spd_rollback.argtypes = [_P, _I32, _P, _P, _P, _P, _I64, _P]
         L.spd_fuse_features_tree.argtypes = [cfgp, _P, _I64, _I32, i32p, _I32, _I32, _I32, _P, _P,
@@ -213,6 +215,13 @@ def spd_lm_head(cfg, w_lm, h, rows, temperature, words, logits, probs, token, ws
         ctypes.byref(cfg), _ptr(w_lm), _ptr(h), rows, float(temperature), _ptr(words),
         _ptr(logits), _ptr(probs), _ptr(token), _ptr(ws), ws.numel() * ws.element_size(),
         _stream(stream)))
+
+
+def spd_lm_head_noalloc(cfg, w_lm, h, rows, temperature, words, logits, probs, token,
+                        stream=None):
+    _check("spd_lm_head_noalloc", lib().spd_lm_head_noalloc(
+        ctypes.byref(cfg), _ptr(w_lm), _ptr(h), rows, float(temperature), _ptr(words),
+        _ptr(logits), _ptr(probs), _ptr(token), _stream(stream)))
 
 
 def spd_verify(B, gamma, V, temperature, bonus, p, q, draft, words, n_accept, next_token, ws,

@@ -17,6 +17,7 @@
 //   of a row scans the chunk sums, finds the chunk holding tau = floor(u*S/2^32)
 //   and the first index inside it whose prefix exceeds tau.
 #include <algorithm>
+#include <mutex>
 
 #include "spd_common.h"
 #include "spd_gemm.h"
@@ -849,4 +850,82 @@ extern "C" int spd_lm_head(const spd_config* cfg, const void* w_lm, const float*
   if (cfg->dtype == SPD_BF16)
     return lm_impl<bf16>(cfg, w_lm, h, rows, temperature, words, logits, probs, token, ws, st);
   return lm_impl<float>(cfg, w_lm, h, rows, temperature, words, logits, probs, token, ws, st);
+}
+
+// ---------------------------------------------------------------------------
+// spd_lm_head_noalloc: spd_lm_head with its workspace in a file-scope device array
+// instead of a caller buffer.  Each GPU the library runs on holds its own copy of
+// the array (allocated with the code object, held until the process ends); host
+// code never passes the array's name to a kernel (in host code it is only a
+// stand-in), but the device address hipGetSymbolAddress returns for the GPU.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)SPD_NOALLOC_SCRATCH_BYTES;
+constexpr int NOALLOC_MAX_DEVICES = 64;
+
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+__global__ void zero_words_kernel(uint32_t* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[NOALLOC_MAX_DEVICES];
+
+// Device address of `scratch` on the stream's GPU.  The first call on a GPU looks
+// it up with that GPU current and clears the arrival counters (a fill kernel on
+// the caller's stream, not a memset); later calls reuse the address.
+int scratch_of(hipStream_t st, void** out) {
+  int dev = -1;
+  hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    last_hip_error_ref() = (int)e;
+    return SPD_E_HIP;
+  }
+  if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return SPD_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    void* ptr = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e == hipSuccess && !ptr) e = hipErrorInvalidSymbol;
+    if (e == hipSuccess) {
+      hipLaunchKernelGGL(zero_words_kernel, dim3(16), dim3(256), 0, st, static_cast<uint32_t*>(ptr),
+                         (int)(SPD_WS_COUNTER_BYTES / 4));
+      e = hipGetLastError();
+    }
+    if (cur >= 0 && cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) {
+      last_hip_error_ref() = (int)e;
+      return SPD_E_HIP;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SPD_OK;
+}
+
+}  // namespace
+
+extern "C" int spd_lm_head_noalloc(const spd_config* cfg, const void* w_lm, const float* h,
+                                   int32_t rows, float temperature, const uint64_t* words,
+                                   float* logits, float* probs, int32_t* token, void* stream) {
+  // the same argument checks as spd_lm_head, then the scratch size
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!w_lm || !h || !logits || !token) return SPD_E_INVALID;
+  if (rows < 1 || rows > 16) return SPD_E_INVALID;
+  if (lm_head_workspace(cfg, rows) > NOALLOC_SCRATCH_BYTES) return SPD_E_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  rc = scratch_of(st, &ws);
+  if (rc) return rc;
+  return spd_lm_head(cfg, w_lm, h, rows, temperature, words, logits, probs, token, ws,
+                     NOALLOC_SCRATCH_BYTES, stream);
 }
