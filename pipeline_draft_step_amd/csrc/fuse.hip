@@ -235,7 +235,9 @@ static FusePlan plan_fuse(const spd_config* cfg, int M) {
   const int es = bf ? 2 : 4;
   const size_t K = (size_t)cfg->m * cfg->d;
   p.big = plan_big(cfg, M);
-  p.gp = plan_gemm(cfg->d, (int)K, M, kstep, es, 1, 256);  // about one block per CU (measured)
+  // about one block per CU: K split six ways at the 2560-wide shape (measured: 320 blocks
+  // of the 62 KB budget ran the cycle 1.6% slower than 240 of the 100 KB budget)
+  p.gp = plan_gemm(cfg->d, (int)K, M, kstep, es, 1, 256, 8, M > 16 ? 0 : 100 * 1024);
   p.ncb = (int)((K + GATHER_COLS - 1) / GATHER_COLS);
   size_t off = SPD_WS_COUNTER_BYTES;
   auto take = [&](size_t b) { size_t r = off; off = align256(off + b); return r; };
