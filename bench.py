@@ -378,6 +378,35 @@ def extra(args, torch, synth, spd, SpdCycle, SpdModel, s, ci, w, model, cyc, t, 
                                     cycles_per_graph=GRAPH_CYCLES, steps=nsteps)
     del graphs
 
+    # a real trajectory: each cycle starts from the state the previous one left on
+    # the device (commit or rollback), read back by the host (one device-to-host
+    # read and synchronisation per cycle), with the q ring of the trajectory itself
+    cyc.set_state(t, s.n, list(range(t)))
+    cyc.prefill(t - 1 - s.n)
+    for r in range(s.n):
+        cyc.ring[r].copy_(qstand)
+    tw = synth.words_tensor(synth.cycle_words(args.warmup + args.steps, seed=41), dev)
+    st = cyc.read_state()
+    for c in range(args.warmup):
+        cyc.cycle(st[0], st[1], tw[c])
+        st = cyc.read_state()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    sat = done = 0
+    for c in range(args.warmup, args.warmup + args.steps):
+        if st[0] + 2 > model.T_cap:   # the sequence would outgrow the cache
+            break
+        sat += st[1] == s.n
+        cyc.cycle(st[0], st[1], tw[c])
+        st = cyc.read_state()
+        done += 1
+    el = time.perf_counter() - t0
+    result["trajectory"] = {
+        "cycles": done, "cycles_per_s": round(done / el, 2),
+        "saturated_fraction": round(sat / max(done, 1), 3), "commits_per_cycle": round(st[2] / max(st[3], 1), 4),
+        "note": "host reads (t, a) after every cycle; random weights reject almost every verification, so "
+                "each rejection is followed by n-1 draft-only refill cycles"}
+
     # prefill feature call (every row at depth n): the anchor gather plus the
     # MFMA-tiled large-M FC GEMM, timed as a whole on the launch stream
     Mp = min(2048, cyc.g_pre.shape[0])
