@@ -93,7 +93,9 @@ typedef struct spd_config {
                        /* 0 < top_p < 1 with top_k = 0 at T > 0                    */
   int32_t head_workgroups; /* spd_lm_head's vocabulary GEMV (bf16, one row): 0 = one */
                        /* workgroup per 32 rows; else at most this many, each looping */
-                       /* over row groups (a head streaming beside other work)     */
+                       /* over row groups with one row's loads in flight per wave (a */
+                       /* head streaming beside latency-bound work); results are   */
+                       /* bit-identical for every value                            */
 } spd_config;
 
 /* One PDM decoder layer (DEVICE pointers, cfg.dtype).  Row-major [rows][cols]. */

@@ -99,12 +99,13 @@ class SpdCycle:
                                        spd_workspace_size(SPD_CALL_VERIFY, c, 1, 1)),
                                    dtype=torch.uint8, device=device)
         self.side = torch.cuda.Stream(device=device)
-        # the side stream's head streams beside the latency-bound feature/PDM chain:
-        # workgroups on three quarters of the compute units leave the chain room
-        # to run (measured: 1/2 to 5/4 of the CU count; 3/4 was fastest)
+        # the side stream's head streams beside the latency-bound feature/PDM chain
+        # on a capped grid (one workgroup per compute unit; measured from 3/4 to 5/4
+        # of the CU count, one was fastest), whose waves keep one row's loads in
+        # flight at a time
         self.cfg_bg = spd_config.from_buffer_copy(c)
         cus = torch.cuda.get_device_properties(device).multi_processor_count
-        self.cfg_bg.head_workgroups = max(1, cus * 3 // 4)
+        self.cfg_bg.head_workgroups = max(1, cus)
         self.ev_fork = torch.cuda.Event()
         self.ev_join = torch.cuda.Event()
         self._plans = {}

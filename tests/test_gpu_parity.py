@@ -486,6 +486,30 @@ def test_lm_head_workgroup_cap_is_bitwise_neutral(workgroups):
     assert torch.equal(l2, logits) and torch.equal(p2, probs) and torch.equal(t2, tok)
 
 
+@pytest.mark.parametrize("V,T", [(3000, 1.0), (3000, 0.0), (300000, 1.0), (530000, 0.0)])
+def test_lm_head_vocabulary_sizes(V, T):
+    """The one-row GEMV finishes the head in its own launch: a ragged second chunk,
+    more chunks than the finish uses workers (300000 entries: 147 chunks), and a
+    greedy vocabulary past the finish's chunk counters (530000: a separate argmax
+    launch).  Logits are checked on sampled rows, the probabilities and the token
+    on the whole row."""
+    say("lm_head vocabulary", V, T)
+    d = 512
+    W, h, words, logits, probs, tok, *_ = _lm_case(V, d, 1, 3.0 / np.sqrt(d), 1, T, seed=14)
+    rng = np.random.default_rng(14)
+    rows = np.unique(np.concatenate([rng.integers(0, V, 2048), [0, V - 1, 2047, 2048]]))
+    ref = O.lm_logits(f64(W[torch.as_tensor(rows, device=DEV)]), f64(h)[0])
+    lg = logits[0].cpu().numpy()
+    assert rel_err(lg[rows].astype(np.float64), ref) < tol_for(1)
+    if T == 0:
+        assert int(tok.item()) == O.argmax_first(lg)
+    else:
+        gp = probs[0].cpu().numpy()
+        pref = O.softmax(lg.astype(np.float64), T)
+        assert np.max(np.abs(gp - pref)) <= 1e-5 * pref.max()
+        assert int(tok.item()) == O.sample_probs(gp, int(words[0]) >> 32)
+
+
 # ------------------------------------------------------------------ top-k / top-p sampling
 
 def _run_lm(W, h, V, d, dtype, rows, T, seed, top_k, top_p):
