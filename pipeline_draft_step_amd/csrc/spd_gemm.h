@@ -743,14 +743,15 @@ struct GemmPlan {
 
 // Choose split-K so that the grid has at most `target` blocks (or one split), each
 // with at least `min_steps` k-steps, and the block's dynamic LDS fits `lds_cap`
-// (0: 62 KB for tiles of 16 rows, two blocks per CU; 140 KB for 32-row tiles,
-// whose staged X slice is twice as tall -- measured on a 29-node draft tree,
-// 388 -> 363 us for its features and PDM step, and on the 17-row 9B-shaped
-// feature call, 70 -> 60 us).
+// (0: 62 KB for tiles of 16 rows, 78 KB for 32-row tiles, whose staged X slice is
+// twice as tall: two blocks per CU either way.  Measured for 32-row tiles against
+// 62, 72, 76, 100 and 140 KB: the 9B-shaped 17-row cycle 1105 us (140 KB: 1137),
+// a 29-node draft tree's PDM step 363-367 us (379-383) and features 46 us (52);
+// 16-row tiles at 70 or 78 KB slow the headline PDM step from 180 to 189 us).
 inline GemmPlan plan_gemm(int N, int K, int M, int kstep, int esize, int NT, int target = 512,
                           int min_steps = 8, size_t lds_cap = 0) {
   GemmPlan p;
-  if (lds_cap == 0) lds_cap = M > 16 ? 140 * 1024 : 62 * 1024;
+  if (lds_cap == 0) lds_cap = M > 16 ? 78 * 1024 : 62 * 1024;
   p.MT = M > 16 ? 2 : 1;
   p.NT = NT;
   p.nblocks = (N + 64 * NT - 1) / (64 * NT);
