@@ -100,12 +100,18 @@ class SpdCycle:
                                    dtype=torch.uint8, device=device)
         self.side = torch.cuda.Stream(device=device)
         # the side stream's head streams beside the latency-bound feature/PDM chain
-        # on a capped grid (one workgroup per compute unit; measured from 3/4 to 5/4
-        # of the CU count, one was fastest), whose waves keep one row's loads in
-        # flight at a time
+        # on a capped grid whose waves keep one row's loads in flight at a time.  Its
+        # rate should end it about when the chain ends: measured on three workloads
+        # (3/4, 1 and 5/4 workgroups per CU), the best cap was 3/4 of the CU count
+        # when the head holds less than 1.2x the chain's weight bytes (9B-shaped,
+        # n = 16, L_s = 4: 0.7x), one per CU up to 2.5x (n = 8, L_s = 2: 1.8x) and
+        # 5/4 above (n = 4, L_s = 1: 3.2x)
         self.cfg_bg = spd_config.from_buffer_copy(c)
         cus = torch.cuda.get_device_properties(device).multi_processor_count
-        self.cfg_bg.head_workgroups = max(1, cus)
+        layer = (c.Hq + 2 * c.Hkv) * c.hd * c.d + c.d * c.Hq * c.hd + 3 * c.dff * c.d
+        ratio = c.V * c.d / (c.d * c.m * c.d + c.Ls * layer)
+        share = 0.75 if ratio < 1.2 else (1.0 if ratio < 2.5 else 1.25)
+        self.cfg_bg.head_workgroups = max(1, int(cus * share))
         self.ev_fork = torch.cuda.Event()
         self.ev_join = torch.cuda.Event()
         self._plans = {}
