@@ -629,25 +629,38 @@ __global__ __launch_bounds__(256) void attn_flash_kernel(FlashArgs a) {
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int key0 = kb * FA_KB;
-    __syncthreads();  // the previous tiles are consumed
+  // The K and V tiles of key block kb + 1 are loaded into registers while block kb
+  // is multiplied (unconditionally: the last block is loaded again at the end).
+  u32x4 kreg[4], vreg[4];  // native vectors: an array of HIP's uint4 structs is kept in memory
+  auto load_tiles = [&](int key0) {
 #pragma unroll
     for (int pass = 0; pass < 4; ++pass) {
       const int idx = pass * 256 + threadIdx.x;
       // K: row = key, 16 chunks of 8 dims; keys past the cache end read its last row
       const int kr = idx >> 4, kc = idx & 15;
       const int key = min(key0 + kr, (int)a.T_cap - 1);
-      *reinterpret_cast<uint4*>(Ks + kr * FA_KSTR + kc * 8) =
-          *reinterpret_cast<const uint4*>(K + (size_t)key * 128 + kc * 8);
+      kreg[pass] = *reinterpret_cast<const u32x4*>(K + (size_t)key * 128 + kc * 8);
       // V: row = dimension, 8 chunks of 8 keys; keys past the last written one are zeroed
       const int vr = idx >> 3, vcn = idx & 7;
       const int kk = key0 + vcn * 8;
-      uint4 v = *reinterpret_cast<const uint4*>(Vt + (size_t)vr * a.T_cap + min(kk, (int)a.T_cap - 8));
-      v = F::mask_from(v, nkeys - kk);
-      *reinterpret_cast<uint4*>(Vs + vr * FA_VSTR + vcn * 8) = v;
+      vreg[pass] = *reinterpret_cast<const u32x4*>(Vt + (size_t)vr * a.T_cap + min(kk, (int)a.T_cap - 8));
+    }
+  };
+  load_tiles(0);
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int key0 = kb * FA_KB;
+    __syncthreads();  // the previous tiles are consumed
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      const int idx = pass * 256 + threadIdx.x;
+      const int kr = idx >> 4, kc = idx & 15;
+      *reinterpret_cast<u32x4*>(Ks + kr * FA_KSTR + kc * 8) = kreg[pass];
+      const int vr = idx >> 3, vcn = idx & 7;
+      *reinterpret_cast<uint4*>(Vs + vr * FA_VSTR + vcn * 8) =
+          F::mask_from(__builtin_bit_cast(uint4, vreg[pass]), nkeys - (key0 + vcn * 8));
     }
     __syncthreads();
+    load_tiles(min(kb + 1, nkb - 1) * FA_KB);
     // S = Q K^T: lane holds S[4 lg + i][16 ks + lr]
     f32x4 sc[4];
 #pragma unroll
