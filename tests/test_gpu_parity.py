@@ -1120,7 +1120,21 @@ def test_cycle_trajectory_tiny(schedule):
     device takes equal the oracle decision functions on the device's rows; the
     state after every cycle matches the oracle state machine.  Run under each
     feature schedule (the prefill and every cycle's features follow it)."""
-    s = synth.TINY.with_(feature_schedule=schedule)
+    _greedy_trajectory(synth.TINY.with_(feature_schedule=schedule), 48)
+
+
+def test_cycle_trajectory_most_stages_and_anchors():
+    """The same greedy trajectory at the most stages and anchors the library takes
+    (n = 32, m = 8): saturated cycles recompute 33 rows, two row tiles of 32 in every
+    product, and each rejection is followed by 31 refill cycles."""
+    s = synth.SpdShape("max_stages_anchors", L=32, n=32, anchors=(0, 4, 8, 12, 16, 20, 24, 31), d=64,
+                       Ls=1, Hq=4, Hkv=2, hd=16, dff=256, V=512, dtype=synth.F32, ctx=48,
+                       temperature=0.0, lm_std=0.02)
+    assert s.n == spd.SPD_MAX_STAGES and s.m == spd.SPD_MAX_ANCHORS
+    _greedy_trajectory(s, 72)
+
+
+def _greedy_trajectory(s, ncycles):
     ci = make_inputs(s, device=DEV, T_cap=128)
     model = device_model(ci)
     cyc = SpdCycle(model, 0.0)
@@ -1130,11 +1144,13 @@ def test_cycle_trajectory_tiny(schedule):
     cyc.set_state(t0, s.n, ost.tokens)
     cyc.prefill(t0 - 1 - s.n)
     cache = OC.prefill(om, t0, s.n)
-    wb = synth.cycle_words(48)
+    wb = synth.cycle_words(ncycles)
     wdev = synth.words_tensor(wb, DEV)
-    for c in range(48):
+    saturated = 0
+    for c in range(ncycles):
         t, a = ost.t, ost.a
-        say("trajectory cycle", c, t, a)
+        saturated += a == s.n
+        say("trajectory cycle", s.name, c, t, a)
         assert cyc.read_state()[:2] == (t, a)
         cyc.cycle(t, a, wdev[c])
         torch.cuda.synchronize()
@@ -1156,6 +1172,7 @@ def test_cycle_trajectory_tiny(schedule):
         assert (tt, aa, cm, cy) == (ost.t, ost.a, ost.commits, ost.cycles)
         assert cyc.tokens[:ost.t].tolist() == ost.tokens
         cache.truncate(ost.t - 1 - ost.a)
+    assert saturated >= 2
 
 
 @pytest.mark.parametrize("top_k,top_p", [(0, 1.0), (50, 1.0), (20, 0.8)],
