@@ -556,10 +556,16 @@ __global__ __launch_bounds__(256) void swiglu_post_kernel(const float* C, int ld
 // owns 64 of a kv head's GQA query rows (query index qi = row * G + head in the
 // group, as in the decode kernel) and walks the keys in blocks of 64 up to its
 // causal limit.  Per key block the K tile (key-major) and the V tile (from the
-// position-minor cache, dimension-major) are staged in LDS; each wave computes
-// S = Q K^T for its 16 rows on MFMA (Q and P as bf16 hi + lo pairs), keeps a
-// running maximum and sum per row, and accumulates O += P V.  The output is
-// written once, as the O projection's [hi | lo] input rows: no partials.
+// position-minor cache, dimension-major) are staged in LDS; the next block's tiles
+// are loaded into registers while the current one is multiplied.  Each wave owns
+// 16 queries and computes S^T = K Q^T on MFMA (Q as bf16 hi + lo pairs, the B
+// operand), keeps a running maximum and sum per query, and accumulates
+// O^T += V^T P^T (P as hi + lo pairs).  The K rows of S^T tile ks are read in the
+// order key(ks, r) = 32 (ks / 2) + 8 (r / 4) + 4 (ks % 2) + r % 4: the lane that
+// holds query c of tile rows 4 g .. 4 g + 3 then holds that query's keys
+// 8 g .. 8 g + 7 (tiles 0, 1) and 32 + 8 g .. + 7 (tiles 2, 3), which is exactly
+// its B operand of the P^T V^T product, so P never leaves the registers.  The
+// output is written once, as the O projection's [hi | lo] input rows.
 constexpr int FA_KB = 64;               // keys per step
 constexpr int FA_ROWS = 64;             // query rows per block (16 per wave)
 constexpr int FA_KSTR = 128 + 8;        // padded LDS row strides (bf16 elements)
@@ -582,7 +588,6 @@ __global__ __launch_bounds__(256) void attn_flash_kernel(FlashArgs a) {
   typedef F::frag frag;
   __shared__ __align__(16) bf16 Ks[FA_KB * FA_KSTR];
   __shared__ __align__(16) bf16 Vs[128 * FA_VSTR];
-  __shared__ __align__(16) bf16 Ps[4][2][16 * FA_VSTR];
   const int h = blockIdx.y;
   const int qt = a.nqt - 1 - blockIdx.x;  // the longest (latest) tiles start first
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
@@ -593,7 +598,7 @@ __global__ __launch_bounds__(256) void attn_flash_kernel(FlashArgs a) {
   const bf16* K = a.kc + (size_t)h * a.T_cap * 128;
   const bf16* Vt = a.vc + (size_t)h * 128 * a.T_cap;
 
-  // Q fragments of this lane's row (A operand), pre-scaled, as hi + lo pairs
+  // Q fragments of this lane's query (B operand), pre-scaled, as hi + lo pairs
   const int qi = FA_ROWS * qt + 16 * wave + lr;
   const bool qv = qi < QR;
   const float* qp = a.q + ((size_t)(qv ? qi / G : 0) * a.Hq + h * G + (qv ? qi % G : 0)) * 128;
@@ -612,20 +617,9 @@ __global__ __launch_bounds__(256) void attn_flash_kernel(FlashArgs a) {
       ql[ds] = F::pack(rem);
     }
   }
-  // causal limit of the 4 rows this lane's accumulators hold (rows 4 lg + i of the wave)
-  int lim[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = FA_ROWS * qt + 16 * wave + 4 * lg + i;
-    lim[i] = a.pos0 + (r < QR ? r / G : 0);
-  }
-  float mrow[4], lrow[4];
-  f32x4 o[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    mrow[i] = -INFINITY;
-    lrow[i] = 0.f;
-  }
+  const int lim = a.pos0 + (qv ? qi / G : 0);  // causal limit of this lane's query
+  float mrow = -INFINITY, lrow = 0.f;
+  f32x4 o[8];  // O^T: lane holds O[query][16 dt + 4 lg + e]
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -661,84 +655,82 @@ __global__ __launch_bounds__(256) void attn_flash_kernel(FlashArgs a) {
     }
     __syncthreads();
     load_tiles(min(kb + 1, nkb - 1) * FA_KB);
-    // S = Q K^T: lane holds S[4 lg + i][16 ks + lr]
+    // S^T = K Q^T: tile ks, lane holds S^T[key(ks, 4 lg + e)][lr]
     f32x4 sc[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
+      const int kr = 32 * (ks >> 1) + 8 * (lr >> 2) + 4 * (ks & 1) + (lr & 3);  // key(ks, lr)
       sc[ks] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ds = 0; ds < 4; ++ds) {
-        const frag kf = *reinterpret_cast<const frag*>(Ks + (16 * ks + lr) * FA_KSTR + ds * 32 + lg * 8);
-        sc[ks] = F::mma(qf[ds], kf, sc[ks]);
-        sc[ks] = F::mma(ql[ds], kf, sc[ks]);
+        const frag kf = *reinterpret_cast<const frag*>(Ks + kr * FA_KSTR + ds * 32 + lg * 8);
+        sc[ks] = F::mma(kf, qf[ds], sc[ks]);
+        sc[ks] = F::mma(kf, ql[ds], sc[ks]);
       }
     }
-    // online softmax per row
-    float scl[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int key = key0 + 16 * ks + lr;
-        if (key > lim[i]) sc[ks][i] = -INFINITY;
-        mx = fmaxf(mx, sc[ks][i]);
-      }
-      mx = row16_max(mx);
-      const float mnew = fmaxf(mrow[i], mx);  // finite: key 0 is inside every row's limit
-      scl[i] = expf(mrow[i] - mnew);
-      float sm = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const float pv = sc[ks][i] == -INFINITY ? 0.f : expf(sc[ks][i] - mnew);
-        sc[ks][i] = pv;
-        sm += pv;
-      }
-      sm = row16_sum(sm);
-      lrow[i] = lrow[i] * scl[i] + sm;
-      mrow[i] = mnew;
-    }
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[dt][i] *= scl[i];
-    // P (16 rows x 64 keys) as hi and lo parts through the wave's LDS buffers
+    // online softmax of this lane's query: its 16 keys, then the 3 other lanes of
+    // the query (lanes lr + 16 j); the butterfly gives all four the same sums
+    float mx = -INFINITY;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bf16 hi = from_f<bf16>(sc[ks][i]);
-        Ps[wave][0][(4 * lg + i) * FA_VSTR + 16 * ks + lr] = hi;
-        Ps[wave][1][(4 * lg + i) * FA_VSTR + 16 * ks + lr] = from_f<bf16>(sc[ks][i] - to_f<bf16>(hi));
+      for (int e = 0; e < 4; ++e) {
+        const int key = key0 + 32 * (ks >> 1) + 8 * lg + 4 * (ks & 1) + e;
+        if (key > lim) sc[ks][e] = -INFINITY;
+        mx = fmaxf(mx, sc[ks][e]);
       }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's P writes are done
-    __builtin_amdgcn_wave_barrier();
-    // O += P V
+    mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+    const float mnew = fmaxf(mrow, mx);  // finite: key 0 is inside every query's limit
+    const float scl = expf(mrow - mnew);
+    float sm = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float pv = sc[ks][e] == -INFINITY ? 0.f : expf(sc[ks][e] - mnew);
+        sc[ks][e] = pv;
+        sm += pv;
+      }
+    sm += __shfl_xor(sm, 16, WAVE);
+    sm += __shfl_xor(sm, 32, WAVE);
+    lrow = lrow * scl + sm;
+    mrow = mnew;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[dt][e] *= scl;
+    // O^T += V^T P^T: the B operand of key step kt is this lane's own P of keys
+    // 32 kt + 8 lg + j (tiles 2 kt and 2 kt + 1), as hi and lo parts
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const frag ph = *reinterpret_cast<const frag*>(&Ps[wave][0][lr * FA_VSTR + kt * 32 + lg * 8]);
-      const frag pl = *reinterpret_cast<const frag*>(&Ps[wave][1][lr * FA_VSTR + kt * 32 + lg * 8]);
+      float ph[8], pl[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        ph[j] = sc[2 * kt + (j >> 2)][j & 3];
+        pl[j] = ph[j] - to_f<bf16>(from_f<bf16>(ph[j]));
+      }
+      const frag bh = F::pack(ph), bl = F::pack(pl);
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const frag vf = *reinterpret_cast<const frag*>(Vs + (16 * dt + lr) * FA_VSTR + kt * 32 + lg * 8);
-        o[dt] = F::mma(ph, vf, o[dt]);
-        o[dt] = F::mma(pl, vf, o[dt]);
+        o[dt] = F::mma(vf, bh, o[dt]);
+        o[dt] = F::mma(vf, bl, o[dt]);
       }
     }
   }
-  // O / l as [hi | lo] parts; lane holds O[4 lg + i][16 dt + lr]
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = FA_ROWS * qt + 16 * wave + 4 * lg + i;
-    if (r >= QR) continue;
-    const float inv = 1.0f / lrow[i];
-    const size_t base = (size_t)(r / G) * a.xld + (size_t)(h * G + r % G) * 128 + lr;
+  // O / l as [hi | lo] parts: this lane's query, dimensions 16 dt + 4 lg .. + 3
+  if (qv) {
+    const float inv = 1.0f / lrow;
+    const size_t base = (size_t)(qi / G) * a.xld + (size_t)(h * G + qi % G) * 128 + 4 * lg;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const float v = o[dt][i] * inv;
-      const bf16 hi = from_f<bf16>(v);
-      a.xh[base + 16 * dt] = hi;
-      a.xl[base + 16 * dt] = from_f<bf16>(v - to_f<bf16>(hi));
+      const float v0 = o[dt][0] * inv, v1 = o[dt][1] * inv, v2 = o[dt][2] * inv, v3 = o[dt][3] * inv;
+      const uint32_t h01 = pack2_bf16(v0, v1), h23 = pack2_bf16(v2, v3);
+      const uint32_t l01 = pack2_bf16(v0 - __uint_as_float(h01 << 16), v1 - __uint_as_float(h01 & 0xffff0000u));
+      const uint32_t l23 = pack2_bf16(v2 - __uint_as_float(h23 << 16), v3 - __uint_as_float(h23 & 0xffff0000u));
+      *reinterpret_cast<uint2*>(a.xh + base + 16 * dt) = make_uint2(h01, h23);
+      *reinterpret_cast<uint2*>(a.xl + base + 16 * dt) = make_uint2(l01, l23);
     }
   }
 }
