@@ -135,10 +135,14 @@ struct AttnArgs {
   float scale;
 };
 
-// One block: kv head h (blockIdx.y), keys [256c, 256c+256) (blockIdx.x), one
-// 16-row tile of the head's GQA query rows (blockIdx.z).  Wave w owns 64 keys:
-// S = Q K^T and O = P V on MFMA (Q and P as bf16 hi + lo pairs), softmax over its
-// keys; the four waves are merged in LDS (log-sum-exp) into one partial per row.
+// One block: kv head h (blockIdx.y), keys [ATT_KC c, ATT_KC (c+1)) (blockIdx.x),
+// one 16-row tile of the head's GQA query rows (blockIdx.z).  Wave w owns ATT_SUB
+// keys: S^T = K Q^T and O^T = V^T P^T on MFMA (Q and P as bf16 hi + lo pairs),
+// softmax over its keys; the four waves are merged in LDS (log-sum-exp) into one
+// partial per query.  The K rows of S^T tile ks are taken in the order
+// key(ks, r) = KSTEP (v / KPL) + KPL (r / 4) + v % KPL with v = 4 ks + r % 4, so
+// that the lane holding query c of tile rows 4 g .. 4 g + 3 holds exactly the
+// keys of its P^T operand (keys KSTEP kt + KPL g + j): P stays in registers.
 template <typename WT, int HD>
 __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   typedef Mfma<WT> F;
@@ -149,9 +153,8 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   constexpr int DT = HD / 16;
   constexpr int KPL = F::KPL;
   constexpr bool SPLIT = sizeof(WT) == 2;
-  constexpr int NP = SPLIT ? 2 : 1;
-  __shared__ __align__(16) WT Ps[ATT_WAVES][NP][16][ATT_SUB + 16];
-  __shared__ float Ob[ATT_WAVES][16][HD + 4];
+  static_assert(KS == 2 && KT * KPL == 4 * KS, "a lane holds 4 KS scores = the KT KPL keys of its P^T");
+  __shared__ __align__(16) float Ob[ATT_WAVES][16][HD + 4];
   __shared__ float2 Ml[ATT_WAVES][16];
 
   __builtin_amdgcn_s_setprio(3);  // decode chain first on a shared SIMD (as in the GEMMs)
@@ -162,12 +165,17 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   const int r_last = (min(QR, 16 * qt + 16) - 1) / G;
   if (c * ATT_KC > a.pos0 + r_last) return;  // every row of the tile is masked here
   const int key0 = c * ATT_KC + wave * ATT_SUB;
+  // key offset (within the wave's keys) of S^T tile ks, row r
+  auto key_of = [](int ks, int r) {
+    const int v = 4 * ks + (r & 3);
+    return F::KSTEP * (v / KPL) + KPL * (r >> 2) + v % KPL;
+  };
 
   const WT* K = static_cast<const WT*>(a.kc) + (size_t)h * a.T_cap * HD;
   const WT* Vt = static_cast<const WT*>(a.vc) + (size_t)h * HD * a.T_cap;
   // All loads are unconditional (a conditional load becomes a branch whose join
   // waits for every outstanding load) and issued in the order they are needed:
-  // Q, K, then V.  Q row = query index 16*qt + lr (clamped; rows past QR are zeroed).
+  // Q, K, then V.  Query = 16*qt + lr (clamped; rows past QR are zeroed).
   const int qi = 16 * qt + lr;
   const bool qv = qi < QR;
   const float* qp = a.q + ((size_t)(qv ? qi / G : 0) * a.Hq + h * G + (qv ? qi % G : 0)) * HD;
@@ -179,12 +187,12 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   frag kf[KS][DS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    const int key = min(key0 + 16 * ks + lr, nkeys - 1);
+    const int key = min(key0 + key_of(ks, lr), nkeys - 1);
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) kf[ks][ds] = F::load(K + (size_t)key * HD + ds * F::KSTEP + lg * KPL);
   }
-  // V: this lane's KPL keys start at kb; kb + KPL <= T_cap whenever kb < nkeys (both
-  // multiples of KPL), so the clamp only moves fully masked fragments
+  // V^T (A operand): this lane's KPL keys start at kb; kb + KPL <= T_cap whenever
+  // kb < nkeys (both multiples of KPL), so the clamp only moves fully masked fragments
   frag vf[KT][DT];
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt) {
@@ -194,7 +202,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     for (int dt = 0; dt < DT; ++dt) vf[kt][dt] = F::load(Vt + (size_t)(dt * 16 + lr) * a.T_cap + kbc);
   }
   __builtin_amdgcn_sched_barrier(0);  // keep V in flight with Q and K
-  // Q fragments (A operand), pre-scaled by 1/sqrt(hd), as hi + lo pairs
+  // Q fragments (B operand), pre-scaled by 1/sqrt(hd), as hi + lo pairs
   frag qf[DS], ql[DS];
   const float qs = qv ? a.scale : 0.f;  // clamped rows (finite values) become zero
 #pragma unroll
@@ -214,57 +222,40 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     sc[ks] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
-      sc[ks] = F::mma(qf[ds], kf[ks][ds], sc[ks]);
-      if constexpr (SPLIT) sc[ks] = F::mma(ql[ds], kf[ks][ds], sc[ks]);
+      sc[ks] = F::mma(kf[ks][ds], qf[ds], sc[ks]);
+      if constexpr (SPLIT) sc[ks] = F::mma(kf[ks][ds], ql[ds], sc[ks]);
     }
   }
-  // lane holds S[4*lg + i][16*ks + lr] of this wave's keys
-  float mx[4], sm[4];
+  // lane holds S^T[key_of(ks, 4 lg + e)][query lr]
+  const int lim = qv ? a.pos0 + qi / G : -1;
   // draft tree: a row reads the new keys of its own root path only
-  uint64_t am[4] = {~0ull, ~0ull, ~0ull, ~0ull};
-  if (a.anc) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) am[i] = a.anc[min(16 * qt + 4 * lg + i, QR - 1) / G];
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int qr = 16 * qt + 4 * lg + i;
-    const int lim = qr < QR ? a.pos0 + qr / G : -1;
-    float m_ = -INFINITY;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int key = key0 + 16 * ks + lr;
-      // key <= lim keeps the shift below the row index (< 64 for tree rows)
-      const bool off_path =
-          a.anc && key >= a.pos0 && key <= lim && !((am[i] >> ((key - a.pos0) & 63)) & 1ull);
-      if (key > lim || key >= nkeys || off_path) sc[ks][i] = -INFINITY;
-      m_ = fmaxf(m_, sc[ks][i]);
-    }
-    m_ = row16_max(m_);
-    float s_ = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const float p = sc[ks][i] == -INFINITY ? 0.f : expf(sc[ks][i] - m_);
-      sc[ks][i] = p;
-      s_ += p;
-    }
-    s_ = row16_sum(s_);
-    mx[i] = m_;
-    sm[i] = s_;
-  }
+  const uint64_t am = a.anc ? a.anc[min(qi, QR - 1) / G] : ~0ull;
+  float mx = -INFINITY;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const WT hi = from_f<WT>(sc[ks][i]);
-      Ps[wave][0][4 * lg + i][16 * ks + lr] = hi;
-      if constexpr (SPLIT) Ps[wave][NP - 1][4 * lg + i][16 * ks + lr] = from_f<WT>(sc[ks][i] - to_f<WT>(hi));
+    for (int e = 0; e < 4; ++e) {
+      const int key = key0 + key_of(ks, 4 * lg + e);
+      // key <= lim keeps the shift below the row index (< 64 for tree rows)
+      const bool off_path = a.anc && key >= a.pos0 && key <= lim && !((am >> ((key - a.pos0) & 63)) & 1ull);
+      if (key > lim || key >= nkeys || off_path) sc[ks][e] = -INFINITY;
+      mx = fmaxf(mx, sc[ks][e]);
     }
-  if (lr == 0) {
+  // the query's other keys sit in lanes lr + 16 j; the butterfly gives all four the same value
+  mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+  float sm = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Ml[wave][4 * lg + i] = make_float2(mx[i], sm[i]);
-  }
-  __syncthreads();
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p = sc[ks][e] == -INFINITY ? 0.f : expf(sc[ks][e] - mx);
+      sc[ks][e] = p;
+      sm += p;
+    }
+  sm += __shfl_xor(sm, 16, WAVE);
+  sm += __shfl_xor(sm, 32, WAVE);
+  if (lg == 0) Ml[wave][lr] = make_float2(mx, sm);
   // zero the V elements of keys >= nkeys (their P is 0, but the cache past the
   // committed rows may hold anything)
 #pragma unroll
@@ -273,30 +264,41 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) vf[kt][dt] = F::mask_from(vf[kt][dt], nkeys - kb);
   }
+  // O^T = V^T P^T: the B operand of key step kt is this lane's own P of keys
+  // KSTEP kt + KPL lg + j, i.e. scores v = KPL kt + j (tile v / 4, row v % 4)
   f32x4 o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt) {
-    const frag pf = F::load(&Ps[wave][0][lr][kt * F::KSTEP + lg * KPL]);
+    float ph[KPL], pl[KPL];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] = F::mma(pf, vf[kt][dt], o[dt]);
+    for (int j = 0; j < KPL; ++j) {
+      const int v = KPL * kt + j;
+      ph[j] = sc[v >> 2][v & 3];
+      pl[j] = ph[j] - to_f<WT>(from_f<WT>(ph[j]));
+    }
+    const frag bh = F::pack(ph);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = F::mma(vf[kt][dt], bh, o[dt]);
     if constexpr (SPLIT) {
-      const frag pl = F::load(&Ps[wave][NP - 1][lr][kt * F::KSTEP + lg * KPL]);
+      const frag bl = F::pack(pl);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt] = F::mma(pl, vf[kt][dt], o[dt]);
+      for (int dt = 0; dt < DT; ++dt) o[dt] = F::mma(vf[kt][dt], bl, o[dt]);
     }
   }
-  // merge the four waves: rescale to the block maximum of each row
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 4 * lg + i;
+  __syncthreads();  // Ml of every wave
+  // merge the four waves: rescale to the block maximum of each query; lane holds
+  // O[query lr][16 dt + 4 lg + e]
+  {
     float mb = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < ATT_WAVES; ++w) mb = fmaxf(mb, Ml[w][row].x);
-    const float f = mx[i] == -INFINITY ? 0.f : expf(mx[i] - mb);
+    for (int w = 0; w < ATT_WAVES; ++w) mb = fmaxf(mb, Ml[w][lr].x);
+    const float f = mx == -INFINITY ? 0.f : expf(mx - mb);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) Ob[wave][row][16 * dt + lr] = o[dt][i] * f;
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<float4*>(&Ob[wave][lr][16 * dt + 4 * lg]) =
+          make_float4(o[dt][0] * f, o[dt][1] * f, o[dt][2] * f, o[dt][3] * f);
   }
   __syncthreads();
   for (int e = threadIdx.x; e < 16 * HD; e += 256) {
