@@ -562,7 +562,7 @@ __global__ __launch_bounds__(256) void swiglu_post_kernel(const float* C, int ld
 // are loaded into registers while the current one is multiplied.  Each wave owns
 // 16 queries and computes S^T = K Q^T on MFMA (Q as bf16 hi + lo pairs, the B
 // operand), keeps a running maximum and sum per query, and accumulates
-// O^T += V^T P^T (P as hi + lo pairs).  The K rows of S^T tile ks are read in the
+// O^T += V^T P^T (P rounded to bf16).  The K rows of S^T tile ks are read in the
 // order key(ks, r) = 32 (ks / 2) + 8 (r / 4) + 4 (ks % 2) + r % 4: the lane that
 // holds query c of tile rows 4 g .. 4 g + 3 then holds that query's keys
 // 8 g .. 8 g + 7 (tiles 0, 1) and 32 + 8 g .. + 7 (tiles 2, 3), which is exactly
@@ -703,21 +703,18 @@ __global__ __launch_bounds__(256) void attn_flash_kernel(FlashArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[dt][e] *= scl;
     // O^T += V^T P^T: the B operand of key step kt is this lane's own P of keys
-    // 32 kt + 8 lg + j (tiles 2 kt and 2 kt + 1), as hi and lo parts
+    // 32 kt + 8 lg + j (tiles 2 kt and 2 kt + 1), rounded to bf16 once (P is in
+    // [0, 1]; a lo part moved no cache row of the headline prefill)
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      float ph[8], pl[8];
+      float ph[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        ph[j] = sc[2 * kt + (j >> 2)][j & 3];
-        pl[j] = ph[j] - to_f<bf16>(from_f<bf16>(ph[j]));
-      }
-      const frag bh = F::pack(ph), bl = F::pack(pl);
+      for (int j = 0; j < 8; ++j) ph[j] = sc[2 * kt + (j >> 2)][j & 3];
+      const frag bh = F::pack(ph);
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const frag vf = *reinterpret_cast<const frag*>(Vs + (16 * dt + lr) * FA_VSTR + kt * 32 + lg * 8);
         o[dt] = F::mma(vf, bh, o[dt]);
-        o[dt] = F::mma(vf, bl, o[dt]);
       }
     }
   }
