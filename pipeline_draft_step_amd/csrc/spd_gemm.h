@@ -36,6 +36,8 @@ constexpr int GEMM_UNROLL = SPD_GEMM_UNROLL;
 constexpr int WG_STEPS = 8;
 constexpr int TB_STRIDE = 1024 + 64;
 constexpr int TB_WAVE = 4 * TB_STRIDE;
+// transpose buffers per wave: one per column group for 16-row tiles, one for 32-row tiles
+constexpr int gemm_tb_buffers(int MT, int NT) { return MT == 1 ? NT : 1; }
 
 struct GemmShape {
   const void* W;
@@ -200,6 +202,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_skinny_kernel(GemmShape g, 
   constexpr int TR = 16 * MT;  // rows per M-tile
   constexpr int TC = 64 * NT;  // columns per N-block
   constexpr bool SPLIT = sizeof(WT) == 2;
+  constexpr int TBN = gemm_tb_buffers(MT, NT);  // transpose buffers per wave
   constexpr int U = GEMM_UNROLL;
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ float s_rs[32];  // row scales of the tile
@@ -315,34 +318,72 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_skinny_kernel(GemmShape g, 
     rsc.finish(g, Mt, s_rs);
     __syncthreads();
     unsigned char* tb = reinterpret_cast<unsigned char*>(xs_lo + (size_t)xrows * g.ldx) +
-                        (size_t)(max(g.ytile_bytes - g.x_bytes, 0)) + wave * TB_WAVE;
+                        (size_t)(max(g.ytile_bytes - g.x_bytes, 0)) + wave * TBN * TB_WAVE;
     const int rdb = (lr >> 2) * TB_STRIDE + 16 * ((lr & 3) + 4 * lg);
-    // multiply one group; FULL: all WG_STEPS k-steps are inside the slice
+    // multiply one group; FULL: all WG_STEPS k-steps are inside the slice.  With
+    // 16-row tiles the NT column groups of a half group pass through TBN = NT
+    // transpose buffers, so each X fragment is read from LDS once per k-step for
+    // all of them (measured: headline PDM step 178.6 -> 171.0 us); 32-row tiles
+    // keep one buffer and read X per column group (their LDS budget goes to the X
+    // slice: sharing cost the 9B-shaped step 685 -> 718 us)
     auto consume = [&](const frag (&c)[NT][WG_STEPS], int st, auto full) {
       constexpr bool FULL = decltype(full)::value;
+      if constexpr (TBN == 1) {
 #pragma unroll
-      for (int u = 0; u < NT; ++u)
+        for (int u = 0; u < NT; ++u)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            if (!FULL && st + 4 * h >= nst) continue;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              *reinterpret_cast<frag*>(tb + j * TB_STRIDE + 16 * lane) = c[u][4 * h + j];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int ks = st + 4 * h + j;
+              if (FULL || ks < nst) {
+                const frag b = *reinterpret_cast<const frag*>(tb + rdb + 256 * j);
+#pragma unroll
+                for (int t = 0; t < MT; ++t) {
+                  const frag af = F::load(xp[t] + ks * F::KSTEP);
+                  const frag al = F::load(xp[t] + lo_off + ks * F::KSTEP);
+                  acc[t][u] = F::mma(af, b, acc[t][u]);
+                  acc[t][u] = F::mma(al, b, acc[t][u]);
+                }
+              }
+            }
+          }
+      } else {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           if (!FULL && st + 4 * h >= nst) continue;
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<frag*>(tb + j * TB_STRIDE + 16 * lane) = c[u][4 * h + j];
+          for (int u = 0; u < NT; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              *reinterpret_cast<frag*>(tb + u * TB_WAVE + j * TB_STRIDE + 16 * lane) = c[u][4 * h + j];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int ks = st + 4 * h + j;
             if (FULL || ks < nst) {
-              const frag b = *reinterpret_cast<const frag*>(tb + rdb + 256 * j);
+              frag af[MT], al[MT];
 #pragma unroll
               for (int t = 0; t < MT; ++t) {
-                const frag af = F::load(xp[t] + ks * F::KSTEP);
-                const frag al = F::load(xp[t] + lo_off + ks * F::KSTEP);
-                acc[t][u] = F::mma(af, b, acc[t][u]);
-                acc[t][u] = F::mma(al, b, acc[t][u]);
+                af[t] = F::load(xp[t] + ks * F::KSTEP);
+                al[t] = F::load(xp[t] + lo_off + ks * F::KSTEP);
+              }
+#pragma unroll
+              for (int u = 0; u < NT; ++u) {
+                const frag b = *reinterpret_cast<const frag*>(tb + u * TB_WAVE + rdb + 256 * j);
+#pragma unroll
+                for (int t = 0; t < MT; ++t) {
+                  acc[t][u] = F::mma(af[t], b, acc[t][u]);
+                  acc[t][u] = F::mma(al[t], b, acc[t][u]);
+                }
               }
             }
           }
         }
+      }
     };
     // Main loop over pairs of full groups with unconditional issues, so that every
     // path into a wait has the same loads outstanding (the wait counts are taken
@@ -764,7 +805,9 @@ inline GemmPlan plan_gemm(int N, int K, int M, int kstep, int esize, int NT, int
   if (S < 1) S = 1;
   const int rows = M < 16 * p.MT ? M : 16 * p.MT;  // rows actually staged
   p.ytile_bytes = 16 * p.MT * (64 * NT + 1) * 4;
-  const size_t tb = esize == 2 ? (size_t)GEMM_WAVES * TB_WAVE : 0;
+  const int tbn = gemm_tb_buffers(p.MT, NT);
+  const size_t tb = esize == 2 ? (size_t)GEMM_WAVES * tbn * TB_WAVE : 0;
+  if (esize == 2) lds_cap += (size_t)(tbn - 1) * GEMM_WAVES * TB_WAVE;  // the X budget stays
   for (;;) {
     const int steps = (p.nsteps + S - 1) / S;
     const int ldx = steps * kstep + 16 / esize * 2;  // +32 bytes of padding
