@@ -235,9 +235,14 @@ static FusePlan plan_fuse(const spd_config* cfg, int M) {
   const int es = bf ? 2 : 4;
   const size_t K = (size_t)cfg->m * cfg->d;
   p.big = plan_big(cfg, M);
-  // about one block per CU: K split six ways at the 2560-wide shape (measured: 320 blocks
-  // of the 62 KB budget ran the cycle 1.6% slower than 240 of the 100 KB budget)
-  p.gp = plan_gemm(cfg->d, (int)K, M, kstep, es, 1, 256, 8, M > 16 ? 0 : 100 * 1024);
+  // about one block per CU.  Tiles of up to 16 rows take 128 columns per block with K
+  // split twelve ways at the 2560-wide shape (measured against 64 columns and six
+  // parts: the feature call alone 1 us slower, the headline cycle 364.4 -> 361.0 us,
+  // the n = 4 cycle unchanged within 0.3%); 32-row tiles keep 64 columns (128 made the
+  // 29-node tree's features faster, 46 -> 35 us, but the 9B-shaped 17-row cycle
+  // slower, 1091 -> 1114 us).  Measured before: 320 blocks of the 62 KB budget ran
+  // the cycle 1.6% slower than 240 of the 100 KB budget.
+  p.gp = plan_gemm(cfg->d, (int)K, M, kstep, es, M > 16 ? 1 : 2, 256, 8, M > 16 ? 0 : 100 * 1024);
   p.ncb = (int)((K + GATHER_COLS - 1) / GATHER_COLS);
   size_t off = SPD_WS_COUNTER_BYTES;
   auto take = [&](size_t b) { size_t r = off; off = align256(off + b); return r; };
@@ -319,6 +324,7 @@ static int fuse_impl(const spd_config* cfg, const void* hstore, int64_t T_cap, i
   gs.rs_K = 1;
   gs.rs_eps = cfg->rms_eps;
   InSplit<WT, RS_SSR> in{ga.xo.hi, ga.xo.lo, m * d};
+  if (p.gp.NT == 2) return launch_gemm<WT, 2>(p.gp, gs, in, EpiRows{g, d}, RowMapStd{}, st);
   return launch_gemm<WT, 1>(p.gp, gs, in, EpiRows{g, d}, RowMapStd{}, st);
 }
 
