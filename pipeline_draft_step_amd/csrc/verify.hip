@@ -6,10 +6,10 @@
 // from p_{gamma+1} when every draft is accepted.)
 //
 // T > 0, launch 1, grid (vocabulary chunks, sequences): every block decides the
-//   sequence's outcome from the 2*gamma scalars p_j(x_j), q_j(x_j) (cheap, exact),
-//   so a fully accepted sequence without bonus reads no rows; otherwise it sums
-//   the exact integer weights of its chunk of the row to sample from (residual
-//   and target weights both, for the empty-residual fallback).
+//   sequence's outcome from the 2*gamma scalars p_j(x_j), q_j(x_j) (cheap, exact;
+//   one lane per draft), so a fully accepted sequence without bonus reads no rows;
+//   otherwise it sums the exact integer weights of its chunk of the row to sample
+//   from (residual and target weights both, for the empty-residual fallback).
 //   Launch 2, one block per sequence: the same decision, the chunk scan and the
 //   search inside the chosen chunk.
 // T == 0, launch 1: per chunk (max, first argmax) of every row; launch 2: merge
@@ -56,44 +56,43 @@ __device__ __forceinline__ uint64_t res_weight(float p, float q) {
   return P > Q ? P - Q : 0ull;
 }
 
-// first rejected position of sequence b (gamma if all accepted); one thread
+// First rejected position of sequence b (gamma if all accepted).  Lane j of wave 0
+// tests draft j (gamma <= 63), all loads issued at once; the lowest rejecting lane
+// wins, which is the position a sequential scan would stop at.  Called by every
+// thread of the block; every thread gets the result.
 __device__ int first_reject(const VerArgs& a, int b) {
-  const int rowsP = a.gamma + a.bonus;
-  int j = 0;
-  for (; j < a.gamma; ++j) {
-    const int x = a.draft[b * a.gamma + j];
-    bool acc = false;
-    if (x >= 0 && x < a.V) {
-      const double px = (double)a.p[((size_t)b * rowsP + j) * a.V + x];
-      const double qx = (double)a.q[((size_t)b * a.gamma + j) * a.V + x];
+  __shared__ int s_first;
+  if (threadIdx.x < WAVE) {
+    const int j = threadIdx.x;
+    bool acc = true;  // lanes past gamma never reject
+    if (j < a.gamma) {
+      const int rowsP = a.gamma + a.bonus;
+      const int x = a.draft[b * a.gamma + j];
       const uint64_t R = a.words[((size_t)b * (a.gamma + 1) + j) * 2] >> 40;
-      acc = (double)(R + 1) * qx <= px * 16777216.0;
+      acc = false;
+      if (x >= 0 && x < a.V) {
+        const double px = (double)a.p[((size_t)b * rowsP + j) * a.V + x];
+        const double qx = (double)a.q[((size_t)b * a.gamma + j) * a.V + x];
+        acc = (double)(R + 1) * qx <= px * 16777216.0;
+      }
     }
-    if (!acc) break;
+    const uint64_t rej = __ballot(!acc);
+    if (threadIdx.x == 0) s_first = rej ? (int)__builtin_ctzll(rej) : a.gamma;
   }
+  __syncthreads();
+  const int j = s_first;
+  __syncthreads();  // s_first is rewritten by the next call
   return j;
 }
 
-__global__ __launch_bounds__(VER_THREADS) void verify_sums_kernel(VerArgs a) {
-  __shared__ int s_j;
-  const int c = blockIdx.x, b = blockIdx.y;
-  if (threadIdx.x == 0) s_j = first_reject(a, b);
-  __syncthreads();
-  const int j = s_j;
-  const bool rejected = j < a.gamma;
-  if (!rejected && !a.bonus) return;
-  const int rowsP = a.gamma + a.bonus;
-  const float* prow = a.p + ((size_t)b * rowsP + j) * a.V;
-  const float* qrow = rejected ? a.q + ((size_t)b * a.gamma + j) * a.V : nullptr;
+// Sums of the exact integer weights (residual, target) of chunk c of the rows that
+// sequence b samples from, once its decision j is known; thread 0 of the block gets
+// them.  pv / qv hold the chunk's probabilities (8 per thread).
+template <int PER>
+__device__ void chunk_weight_sums(const float (&pv)[PER], const float (&qv)[PER], bool rejected,
+                                  uint64_t& tres, uint64_t& tp) {
+  __shared__ uint64_t s_w[2][VER_THREADS / 64];
   uint64_t sres = 0, sp = 0;
-  constexpr int PER = VER_CHUNK / VER_THREADS;
-  float pv[PER], qv[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const int i = c * VER_CHUNK + threadIdx.x + VER_THREADS * e;
-    pv[e] = i < a.V ? prow[i] : 0.f;
-    qv[e] = (rejected && i < a.V) ? qrow[i] : 0.f;
-  }
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     sp += prob_weight(pv[e]);
@@ -101,49 +100,36 @@ __global__ __launch_bounds__(VER_THREADS) void verify_sums_kernel(VerArgs a) {
   }
   sres = wave_sum_u64(sres);
   sp = wave_sum_u64(sp);
-  __shared__ uint64_t s_w[2][VER_THREADS / 64];
   if ((threadIdx.x & 63) == 0) {
     s_w[0][threadIdx.x >> 6] = sres;
     s_w[1][threadIdx.x >> 6] = sp;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint64_t t0 = 0, t1 = 0;
-    for (int w = 0; w < VER_THREADS / 64; ++w) {
-      t0 += s_w[0][w];
-      t1 += s_w[1][w];
-    }
-    uint64_t* part = static_cast<uint64_t*>(a.part) + ((size_t)b * a.nchunks + c) * 2;
-    part[0] = t0;
-    part[1] = t1;
+  tres = 0;
+  tp = 0;
+  for (int w = 0; w < VER_THREADS / 64; ++w) {
+    tres += s_w[0][w];
+    tp += s_w[1][w];
   }
+  __syncthreads();  // s_w is rewritten by the next call
 }
 
-__global__ __launch_bounds__(VER_THREADS) void verify_locate_kernel(VerArgs a) {
+// The draw of sequence b once every chunk's weight sums (residual, target) are in
+// pb[2 c], pb[2 c + 1]: the residual if it has mass, else the target row; the
+// chunk scan, then the search inside the chosen chunk.  Writes n_accept / next_token.
+__device__ void locate_and_write(const VerArgs& a, int b, int j, const uint64_t* pb) {
   __shared__ uint64_t sh[VER_THREADS];
-  __shared__ int s_j;
   __shared__ uint64_t s_tau, s_off;
   __shared__ int s_chunk, s_found;
   __shared__ uint64_t s_t[VER_THREADS / 64];
-  const int b = blockIdx.x;
-  if (threadIdx.x == 0) s_j = first_reject(a, b);
-  __syncthreads();
-  const int j = s_j;
+  auto ld = [&](int i) { return pb[i]; };
   const bool rejected = j < a.gamma;
-  if (!rejected && !a.bonus) {
-    if (threadIdx.x == 0) {
-      a.n_accept[b] = a.gamma;
-      a.next_token[b] = -1;
-    }
-    return;
-  }
   const int rowsP = a.gamma + a.bonus;
   const float* prow = a.p + ((size_t)b * rowsP + j) * a.V;
   const float* qrow = rejected ? a.q + ((size_t)b * a.gamma + j) * a.V : nullptr;
-  const uint64_t* pb = static_cast<const uint64_t*>(a.part) + (size_t)b * a.nchunks * 2;
   // residual if it has mass, else the target row itself
   uint64_t tr = 0;
-  for (int k = threadIdx.x; k < a.nchunks; k += VER_THREADS) tr += pb[2 * k];
+  for (int k = threadIdx.x; k < a.nchunks; k += VER_THREADS) tr += ld(2 * k);
   tr = wave_sum_u64(tr);
   if ((threadIdx.x & 63) == 0) s_t[threadIdx.x >> 6] = tr;
   __syncthreads();
@@ -156,7 +142,7 @@ __global__ __launch_bounds__(VER_THREADS) void verify_locate_kernel(VerArgs a) {
   uint64_t mine = 0;
   for (int e = 0; e < per; ++e) {
     const int k = threadIdx.x * per + e;
-    if (k < a.nchunks) mine += pb[2 * k + which];
+    if (k < a.nchunks) mine += ld(2 * k + which);
   }
   const uint64_t incl = vblock_scan(mine, sh);
   if (threadIdx.x == VER_THREADS - 1) {
@@ -171,7 +157,7 @@ __global__ __launch_bounds__(VER_THREADS) void verify_locate_kernel(VerArgs a) {
     for (int e = 0; e < per; ++e) {
       const int k = threadIdx.x * per + e;
       if (k >= a.nchunks) break;
-      const uint64_t w = pb[2 * k + which];
+      const uint64_t w = ld(2 * k + which);
       if (run + w > tau) {
         s_chunk = k;
         s_off = run;
@@ -212,6 +198,47 @@ __global__ __launch_bounds__(VER_THREADS) void verify_locate_kernel(VerArgs a) {
     a.n_accept[b] = j;
     a.next_token[b] = s_found < 0 ? 0 : s_found;
   }
+}
+
+// T > 0, launch 1: the chunk sums of every (chunk, sequence); launch 2: one block
+// per sequence draws.  (One launch, with the last chunk block of each sequence
+// drawing, was measured slower: 30.5 against 25 us for 64 x 7 sequences.)
+__global__ __launch_bounds__(VER_THREADS) void verify_sums_kernel(VerArgs a) {
+  const int c = blockIdx.x, b = blockIdx.y;
+  const int j = first_reject(a, b);
+  const bool rejected = j < a.gamma;
+  if (!rejected && !a.bonus) return;
+  const int rowsP = a.gamma + a.bonus;
+  const float* prow = a.p + ((size_t)b * rowsP + j) * a.V;
+  const float* qrow = rejected ? a.q + ((size_t)b * a.gamma + j) * a.V : nullptr;
+  constexpr int PER = VER_CHUNK / VER_THREADS;
+  float pv[PER], qv[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int i = c * VER_CHUNK + threadIdx.x + VER_THREADS * e;
+    pv[e] = i < a.V ? prow[i] : 0.f;
+    qv[e] = (rejected && i < a.V) ? qrow[i] : 0.f;
+  }
+  uint64_t tres, tp;
+  chunk_weight_sums(pv, qv, rejected, tres, tp);
+  if (threadIdx.x == 0) {
+    uint64_t* part = static_cast<uint64_t*>(a.part) + ((size_t)b * a.nchunks + c) * 2;
+    part[0] = tres;
+    part[1] = tp;
+  }
+}
+
+__global__ __launch_bounds__(VER_THREADS) void verify_locate_kernel(VerArgs a) {
+  const int b = blockIdx.x;
+  const int j = first_reject(a, b);
+  if (j == a.gamma && !a.bonus) {
+    if (threadIdx.x == 0) {
+      a.n_accept[b] = a.gamma;
+      a.next_token[b] = -1;
+    }
+    return;
+  }
+  locate_and_write(a, b, j, static_cast<const uint64_t*>(a.part) + (size_t)b * a.nchunks * 2);
 }
 
 __global__ __launch_bounds__(VER_THREADS) void verify_greedy_chunks_kernel(VerArgs a) {

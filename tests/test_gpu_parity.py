@@ -958,6 +958,27 @@ def test_verify_batched_stress_bitexact():
     assert hist[0] < v.B      # the correlated drafts are accepted at times
 
 
+def test_verify_sampled_large_batch():
+    """16400 sampled sequences (gamma = 2, bonus) in one call: every checked
+    sequence's outcome is the oracle's."""
+    B, G, V = 16400, 2, 256
+    say("verify two-launch", B, G, V)
+    pl = synth.normal((B, G + 1, V), 2.0, device=DEV, seed=41, name="big_p")
+    p = torch.softmax(pl, -1)
+    q = torch.softmax(pl[:, :G] + synth.normal((B, G, V), 1.0, device=DEV, seed=42, name="big_q"), -1)
+    draft = torch.multinomial(q.reshape(-1, V), 1, generator=torch.Generator(device=DEV).manual_seed(43))
+    draft = draft.reshape(B, G).to(torch.int32).contiguous()
+    words = synth.rand_words(44, 3, B * (G + 1) * 2).reshape(B, G + 1, 2)
+    na, nt = _verify_gpu(p, q.contiguous(), draft, words, 1.0, 1)
+    pc, qc, dc = p.cpu().numpy(), q.cpu().numpy(), draft.cpu().numpy()
+    for b in range(0, B, 7):
+        ref = O.verify(pc[b], qc[b], list(dc[b]), words[b], temperature=1.0, bonus=True)
+        assert (int(na[b]), int(nt[b])) == ref, b
+    for b in range(B - 40, B):
+        ref = O.verify(pc[b], qc[b], list(dc[b]), words[b], temperature=1.0, bonus=True)
+        assert (int(na[b]), int(nt[b])) == ref, b
+
+
 def test_verify_greedy_gamma_form():
     say("verify greedy")
     B, G, V = 16, 7, 151936
