@@ -131,6 +131,7 @@ struct AttnArgs {
   unsigned* counters;  // [Hkv][nqt]
   const uint64_t* anc;  // draft-tree ancestor masks [M], or null for causal rows
   int M, Hq, Hkv, pos0, nch, nqt;
+  int r0;  // query rows r0 .. M-1 (local rows 0 .. M-1-r0 of the output); keys of all M rows
   int64_t T_cap;
   float scale;
 };
@@ -160,10 +161,11 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   __builtin_amdgcn_s_setprio(3);  // decode chain first on a shared SIMD (as in the GEMMs)
   const int c = blockIdx.x, h = blockIdx.y, qt = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
-  const int G = a.Hq / a.Hkv, QR = a.M * G;
+  const int G = a.Hq / a.Hkv, QR = (a.M - a.r0) * G;
   const int nkeys = a.pos0 + a.M;
+  const int qpos0 = a.pos0 + a.r0;  // position of local query row 0
   const int r_last = (min(QR, 16 * qt + 16) - 1) / G;
-  if (c * ATT_KC > a.pos0 + r_last) return;  // every row of the tile is masked here
+  if (c * ATT_KC > qpos0 + r_last) return;  // every row of the tile is masked here
   const int key0 = c * ATT_KC + wave * ATT_SUB;
   // key offset (within the wave's keys) of S^T tile ks, row r
   auto key_of = [](int ks, int r) {
@@ -178,7 +180,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   // Q, K, then V.  Query = 16*qt + lr (clamped; rows past QR are zeroed).
   const int qi = 16 * qt + lr;
   const bool qv = qi < QR;
-  const float* qp = a.q + ((size_t)(qv ? qi / G : 0) * a.Hq + h * G + (qv ? qi % G : 0)) * HD;
+  const float* qp = a.q + ((size_t)(a.r0 + (qv ? qi / G : 0)) * a.Hq + h * G + (qv ? qi % G : 0)) * HD;
   float qraw[DS][KPL];
 #pragma unroll
   for (int ds = 0; ds < DS; ++ds)
@@ -227,9 +229,9 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     }
   }
   // lane holds S^T[key_of(ks, 4 lg + e)][query lr]
-  const int lim = qv ? a.pos0 + qi / G : -1;
+  const int lim = qv ? qpos0 + qi / G : -1;
   // draft tree: a row reads the new keys of its own root path only
-  const uint64_t am = a.anc ? a.anc[min(qi, QR - 1) / G] : ~0ull;
+  const uint64_t am = a.anc ? a.anc[a.r0 + min(qi, QR - 1) / G] : ~0ull;
   float mx = -INFINITY;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
@@ -326,7 +328,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     }
   }
   // the last chunk block of (kv head, query tile) merges the chunk partials of its rows
-  const int nchunk_tile = min(a.nch, (a.pos0 + r_last) / ATT_KC + 1);
+  const int nchunk_tile = min(a.nch, (qpos0 + r_last) / ATT_KC + 1);
   if (!arrive_last(a.counters + h * a.nqt + qt, (unsigned)nchunk_tile)) {
     return;
   }
@@ -337,7 +339,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     constexpr int CPT = ATT_MAXCH / 16;  // chunks per thread at most
     const int row = threadIdx.x >> 4, j = threadIdx.x & 15;
     const int qr = 16 * qt + row;
-    const int nv = qr < QR ? (a.pos0 + qr / G) / ATT_KC + 1 : 0;
+    const int nv = qr < QR ? (qpos0 + qr / G) / ATT_KC + 1 : 0;
     const uint64_t* ml = reinterpret_cast<const uint64_t*>(a.pml + ((size_t)h * QR + (qr < QR ? qr : 0)) * a.nch);
     float2 v[CPT];
 #pragma unroll
@@ -381,7 +383,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     rowv[ii] = ok ? row : 0;
     dimv[ii] = ok ? dim : 0;
     qrv[ii] = ok ? qr : -1;
-    nvv[ii] = ok ? (a.pos0 + qr / G) / ATT_KC + 1 : 0;
+    nvv[ii] = ok ? (qpos0 + qr / G) / ATT_KC + 1 : 0;
     basev[ii] = (uint32_t)(((((size_t)h * QR + qc) * a.nch) * HD + (ok ? dim : 0)) * 4);
     nvmax = max(nvmax, nvv[ii]);
   }
@@ -419,8 +421,8 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------------------
 // Prefill-sized steps (bf16, M >= 256, hd = 128): the four products of a layer
-// run on the large-M MFMA GEMM with bf16-rounded activations and write fp32
-// rows; the row kernels below apply what the decode path's GEMM epilogues do.
+// run on the large-M MFMA GEMM and write fp32 rows; the row kernels below apply
+// what the decode path's GEMM epilogues do.
 // ---------------------------------------------------------------------------
 constexpr int PDM_BIG_MIN_M = 256;
 
@@ -510,12 +512,10 @@ __global__ __launch_bounds__(256) void v_post_kernel(const float* C, int ldc, WT
   for (int dim = threadIdx.x >> 6; dim < 128; dim += 4) vp[(size_t)dim * T_cap] = from_f<WT>(y[dim]);
 }
 
-// h += y, the row's 1/rms, the next GEMM's input h * gnext as a [hi | lo] row
-// when gnext is given; with final_norm, the final-normed last row into h_last
+// h += y, the row's 1/rms and the next GEMM's input h * gnext as a [hi | lo] row
 template <typename WT>
 __global__ __launch_bounds__(256) void resid_post_kernel(const float* C, int ldc, float* h, float* rs, WT* xa,
-                                                         const WT* gnext, int d, float eps, const WT* final_norm,
-                                                         float* h_last, int M) {
+                                                         const WT* gnext, int d, float eps) {
   const int r = blockIdx.x;
   float sq = 0.f;
   for (int c = 4 * threadIdx.x; c < d; c += 4 * 256) {
@@ -528,17 +528,12 @@ __global__ __launch_bounds__(256) void resid_post_kernel(const float* C, int ldc
     v.w += y.w;
     *reinterpret_cast<float4*>(h + i) = v;
     sq += (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
-    if (gnext)
-      put4_hilo(xa + (size_t)r * 2 * d + c, d,
-                make_float4(v.x * to_f<WT>(gnext[c]), v.y * to_f<WT>(gnext[c + 1]), v.z * to_f<WT>(gnext[c + 2]),
-                            v.w * to_f<WT>(gnext[c + 3])));
+    put4_hilo(xa + (size_t)r * 2 * d + c, d,
+              make_float4(v.x * to_f<WT>(gnext[c]), v.y * to_f<WT>(gnext[c + 1]), v.z * to_f<WT>(gnext[c + 2]),
+                          v.w * to_f<WT>(gnext[c + 3])));
   }
   const float t = block_sum256(sq);
-  const float inv = 1.0f / sqrtf(t / (float)d + eps);
-  if (threadIdx.x == 0) rs[r] = inv;
-  if (final_norm && r == M - 1) {
-    for (int c = threadIdx.x; c < d; c += 256) h_last[c] = h[(size_t)r * d + c] * inv * to_f<WT>(final_norm[c]);
-  }
+  if (threadIdx.x == 0) rs[r] = 1.0f / sqrtf(t / (float)d + eps);
 }
 
 // act[r][j] = silu(gate_j) * up_j (gate columns first, then up) as a [hi | lo]
@@ -739,6 +734,7 @@ struct PdmPlan {
   int nch, QR;
   size_t off_h, off_ss, off_q, off_rope, off_po, off_pml, off_x0h, off_x0l, off_x1h, off_x1l, off_part, total;
   int ld1;  // row stride of the second XSplit buffer
+  size_t part_bytes;  // split-K partials of the decode-shaped products
   // large-M path
   bool big;
   BigPlan bqkv, bo, bgu, bdown;
@@ -754,17 +750,44 @@ struct PdmPlan {
 constexpr int PDM_BIG_LO = 0xD;
 static inline int big_k(int prod, int K) { return ((PDM_BIG_LO >> prod) & 1) ? 2 * K : K; }
 
-static PdmPlan plan_pdm(const spd_config* c, int M, int64_t T_cap) {
-  PdmPlan p;
+// The decode-shaped products for M rows.  Grid targets measured at the 2560-wide
+// shape: about one block per CU for the products over the hidden size, two for the
+// down projection (rows of dff).
+struct RowPlans {
+  GemmPlan qkv, o, gu, down;
+};
+static RowPlans plan_rows(const spd_config* c, int M) {
   const bool bf = c->dtype == SPD_BF16;
   const int ks = bf ? Mfma<bf16>::KSTEP : Mfma<float>::KSTEP;
   const int es = bf ? 2 : 4;
-  // grid targets measured at the 2560-wide shape: about one block per CU for the
-  // products over the hidden size, two for the down projection (rows of dff)
-  p.qkv = plan_gemm((c->Hq + 2 * c->Hkv) * c->hd, c->d, M, ks, es, 2, 256);
-  p.o = plan_gemm(c->d, c->Hq * c->hd, M, ks, es, 1, 256);
-  p.gu = plan_gemm(2 * c->dff, c->d, M, ks, es, 2, 256);
-  p.down = plan_gemm(c->d, c->dff, M, ks, es, 1, 512);
+  RowPlans r;
+  r.qkv = plan_gemm((c->Hq + 2 * c->Hkv) * c->hd, c->d, M, ks, es, 2, 256);
+  r.o = plan_gemm(c->d, c->Hq * c->hd, M, ks, es, 1, 256);
+  r.gu = plan_gemm(2 * c->dff, c->d, M, ks, es, 2, 256);
+  r.down = plan_gemm(c->d, c->dff, M, ks, es, 1, 512);
+  return r;
+}
+
+// split-K partial floats of the O, gate/up and down products over M rows
+static size_t tail_part_bytes(const spd_config* c, const RowPlans& r, int M) {
+  size_t b = 0;
+  if (r.o.S > 1) b = std::max(b, (size_t)r.o.S * M * c->d * 4);
+  if (r.gu.S > 1) b = std::max(b, (size_t)r.gu.S * M * 2 * c->dff * 4);
+  if (r.down.S > 1) b = std::max(b, (size_t)r.down.S * M * c->d * 4);
+  return b;
+}
+
+static PdmPlan plan_pdm(const spd_config* c, int M, int64_t T_cap) {
+  PdmPlan p;
+  const bool bf = c->dtype == SPD_BF16;
+  const int es = bf ? 2 : 4;
+  {
+    const RowPlans r = plan_rows(c, M);
+    p.qkv = r.qkv;
+    p.o = r.o;
+    p.gu = r.gu;
+    p.down = r.down;
+  }
   p.nch = (int)((T_cap + ATT_KC - 1) / ATT_KC);
   p.QR = M * (c->Hq / c->Hkv);
   size_t off = SPD_WS_COUNTER_BYTES;
@@ -787,6 +810,9 @@ static PdmPlan plan_pdm(const spd_config* c, int M, int64_t T_cap) {
                         (size_t)c->d};
   for (int i = 0; i < 4; ++i)
     if (gps[i]->S > 1) part = std::max(part, (size_t)gps[i]->S * M * Ns[i] * 4);
+  // the one-row tail of the last layer (the chain's h_last)
+  part = std::max(part, tail_part_bytes(c, plan_rows(c, 1), 1));
+  p.part_bytes = part;
   p.off_part = take(part);
   p.big = bf && M >= PDM_BIG_MIN_M && c->hd == 128;
   if (p.big) {
@@ -848,9 +874,86 @@ static int launch_attention(const AttnArgs& aa, hipStream_t st) {
   }
 }
 
-// Large-M step.  Buffers: x0 hi = bf16 input of QKV and gate/up (d wide), x1 hi/lo =
-// attention output (the GEMM reads the hi part) and SwiGLU activations, C = one
-// GEMM's fp32 output, rs = the row scales 1/rms(h).
+// Attention, O projection, gate/up and down of one layer for the query rows
+// r0 .. M-1, once the layer's QKV product has put the keys and values of all M
+// rows in the cache and their queries in the attention buffer.  Rows r0 .. M-1 of
+// h are updated in place; x0, x1 and the row statistics hold them from local row
+// 0.  The last layer (next == null) final-norms local rows Mq - n_out .. Mq - 1
+// into h_last, Mq = M - r0.  P returns the partial count of the row statistics
+// the down projection leaves for the next layer's QKV product.
+template <typename WT>
+static int layer_rows(const spd_config* c, const PdmPlan& p, const spd_layer_weights& lw,
+                      const spd_layer_weights* next, const void* final_norm, int M, int r0, int n_out,
+                      float* h_last, char* w, AttnArgs aa, int& P, hipStream_t st) {
+  const int d = c->d, hd = c->hd, Hq = c->Hq, dff = c->dff;
+  const int Mq = M - r0;
+  const RowPlans rp = r0 == 0 ? RowPlans{p.qkv, p.o, p.gu, p.down} : plan_rows(c, Mq);
+  float* h = reinterpret_cast<float*>(w + p.off_h) + (size_t)r0 * d;
+  float* ss = reinterpret_cast<float*>(w + p.off_ss);
+  float* part = reinterpret_cast<float*>(w + p.off_part);
+  unsigned* ctr = reinterpret_cast<unsigned*>(w);
+  const XSplit<WT> x0{reinterpret_cast<WT*>(w + p.off_x0h), reinterpret_cast<WT*>(w + p.off_x0l), d};
+  const XSplit<WT> x1{reinterpret_cast<WT*>(w + p.off_x1h), reinterpret_cast<WT*>(w + p.off_x1l), p.ld1};
+  const XSplit<WT> none{nullptr, nullptr, 0};
+  int rc;
+  // attention -> x1
+  aa.r0 = r0;
+  aa.nqt = (Mq * (Hq / c->Hkv) + 15) / 16;
+  switch (hd) {
+    case 16: rc = launch_attention<WT, 16>(aa, st); break;
+    case 32: rc = launch_attention<WT, 32>(aa, st); break;
+    case 64: rc = launch_attention<WT, 64>(aa, st); break;
+    default: rc = launch_attention<WT, 128>(aa, st); break;
+  }
+  if (rc) return rc;
+  // O projection + residual; x0 = h * mlp_norm
+  {
+    InSplit<WT> in{x1.hi, x1.lo, p.ld1};
+    EpiResid<WT> epi{h, ss, d, Mq, 0, nullptr, nullptr, ctr + CTR_FINAL, rp.o.nblocks, c->rms_eps,
+                     x0, static_cast<const WT*>(lw.mlp_norm)};
+    rc = launch_gemm<WT, 1>(rp.o, shape_of(rp.o, lw.wo, d, Hq * hd, Mq, part, ctr), in, epi,
+                            RowMapStd{}, st);
+    if (rc) return rc;
+  }
+  // gate/up + silu*mul -> x1; row scale = 1 / rms(h)
+  {
+    InSplit<WT, RS_SS> in{x0.hi, x0.lo, d};
+    EpiSilu<WT> epi{x1, dff};
+    rc = launch_gemm<WT, 2>(rp.gu, shape_of(rp.gu, lw.w_gate_up, 2 * dff, d, Mq, part, ctr, ss,
+                                            rp.o.nblocks, c->rms_eps),
+                            in, epi, RowMapGateUp{dff}, st);
+    if (rc) return rc;
+  }
+  // down + residual; x0 = h * next attn_norm; after the last layer h_last
+  {
+    InSplit<WT> in{x1.hi, x1.lo, p.ld1};
+    const bool last = next == nullptr;
+    EpiResid<WT> epi{h, ss, d, Mq, last ? 1 : 0, static_cast<const WT*>(final_norm), h_last,
+                     ctr + CTR_FINAL, rp.down.nblocks, c->rms_eps, last ? none : x0,
+                     last ? nullptr : static_cast<const WT*>(next->attn_norm), n_out};
+    rc = launch_gemm<WT, 1>(rp.down, shape_of(rp.down, lw.w_down, d, dff, Mq, part, ctr), in, epi,
+                            RowMapStd{}, st);
+    if (rc) return rc;
+    P = rp.down.nblocks;
+  }
+  return SPD_OK;
+}
+
+// First query row of the last layer: only the rows that are final-normed into the
+// output need that layer's attention, O projection and MLP (the others' outputs
+// feed nothing; their keys and values come from the QKV product).  Falls back to
+// every row when the tail's split-K partials would not fit the workspace.
+static int last_layer_r0(const spd_config* c, const PdmPlan& p, int M, int n_out) {
+  const int r0 = M - n_out;
+  if (r0 <= 0) return 0;
+  return tail_part_bytes(c, plan_rows(c, n_out), n_out) <= p.part_bytes ? r0 : 0;
+}
+
+// Large-M step.  Buffers: xa = [hi | lo] input of QKV and gate/up (2d wide), xb =
+// attention output and SwiGLU activations, C = one GEMM's fp32 output, rs = the
+// row scales 1/rms(h).  The last layer runs its QKV product over every row (the
+// cache needs all keys and values) and the rest for the output row only, on the
+// decode-shaped kernels.
 static int pdm_big(const spd_config* c, const spd_layer_weights* layers, const void* final_norm, void* k_cache,
                    void* v_cache, int64_t T_cap, const float* g, int pos0, int M, float* h_last, char* w,
                    const PdmPlan& p, AttnArgs aa, hipStream_t st) {
@@ -884,6 +987,15 @@ static int pdm_big(const spd_config* c, const spd_layer_weights* layers, const v
                        (Hq + Hkv) * hd, pos0, T_cap, M);
     rc = check_launch();
     if (rc) return rc;
+    if (l == c->Ls - 1) {
+      // the last layer's attention, O and MLP for the output row only, on the
+      // decode-shaped kernels (the other rows' outputs of this layer feed nothing)
+      aa.kc = kc;
+      aa.vc = vc;
+      int P = 0;
+      return layer_rows<WT>(c, p, lw, nullptr, final_norm, M, last_layer_r0(c, p, M, 1), 1, h_last, w, aa, P,
+                            st);
+    }
     {
       FlashArgs fa;
       fa.q = qb;
@@ -906,22 +1018,19 @@ static int pdm_big(const spd_config* c, const spd_layer_weights* layers, const v
     launch_big_gemm(p.bo, xb, 2 * ko, static_cast<const WT*>(lw.wo), C, d, nullptr, M, d, big_k(1, ko), bpart, ctr,
                     st, ko);
     hipLaunchKernelGGL((resid_post_kernel<WT>), dim3(M), dim3(256), 0, st, C, d, h, rs, xa,
-                       static_cast<const WT*>(lw.mlp_norm), d, c->rms_eps, static_cast<const WT*>(nullptr),
-                       static_cast<float*>(nullptr), M);
+                       static_cast<const WT*>(lw.mlp_norm), d, c->rms_eps);
     launch_big_gemm(p.bgu, xa, 2 * d, static_cast<const WT*>(lw.w_gate_up), C, 2 * dff, rs, M, 2 * dff,
                     big_k(2, d), bpart, ctr, st, d);
     hipLaunchKernelGGL((swiglu_post_kernel<WT>), dim3((dff / 4 + 255) / 256, M), dim3(256), 0, st, C, 2 * dff,
                        xb, dff);
     launch_big_gemm(p.bdown, xb, 2 * dff, static_cast<const WT*>(lw.w_down), C, d, nullptr, M, d, big_k(3, dff),
                     bpart, ctr, st, dff);
-    const bool last = l == c->Ls - 1;
-    hipLaunchKernelGGL((resid_post_kernel<WT>), dim3(M), dim3(256), 0, st, C, d, h, rs, last ? nullptr : xa,
-                       last ? nullptr : static_cast<const WT*>(layers[l + 1].attn_norm), d, c->rms_eps,
-                       last ? static_cast<const WT*>(final_norm) : nullptr, h_last, M);
+    hipLaunchKernelGGL((resid_post_kernel<WT>), dim3(M), dim3(256), 0, st, C, d, h, rs, xa,
+                       static_cast<const WT*>(layers[l + 1].attn_norm), d, c->rms_eps);
     rc = check_launch();
     if (rc) return rc;
   }
-  return SPD_OK;
+  return SPD_E_UNSUPPORTED;  // Ls == 0 (rejected by the caller)
 }
 
 template <typename WT>
@@ -961,6 +1070,7 @@ static int pdm_impl(const spd_config* c, const spd_layer_weights* layers, const 
   aa.T_cap = T_cap;
   aa.scale = 1.0f / sqrtf((float)hd);
   aa.anc = anc;
+  aa.r0 = 0;
 
   if constexpr (sizeof(WT) == 2) {
     if (p.big && !anc) return pdm_big(c, layers, final_norm, k_cache, v_cache, T_cap, g, pos0, M, h_last, w, p, aa, st);
@@ -983,47 +1093,13 @@ static int pdm_impl(const spd_config* c, const spd_layer_weights* layers, const 
                               in, epi, RowMapStd{}, st);
       if (rc) return rc;
     }
-    // attention -> x1
+    // attention, O, MLP; the last layer only for the output rows
     aa.kc = kc;
     aa.vc = vc;
-    switch (hd) {
-      case 16: rc = launch_attention<WT, 16>(aa, st); break;
-      case 32: rc = launch_attention<WT, 32>(aa, st); break;
-      case 64: rc = launch_attention<WT, 64>(aa, st); break;
-      default: rc = launch_attention<WT, 128>(aa, st); break;
-    }
+    const bool last = l == c->Ls - 1;
+    rc = layer_rows<WT>(c, p, lw, last ? nullptr : &layers[l + 1], final_norm, M,
+                        last ? last_layer_r0(c, p, M, n_out) : 0, n_out, h_last, w, aa, P, st);
     if (rc) return rc;
-    // O projection + residual; x0 = h * mlp_norm
-    {
-      InSplit<WT> in{x1.hi, x1.lo, p.ld1};
-      EpiResid<WT> epi{h, ss, d, M, 0, nullptr, nullptr, ctr + CTR_FINAL, p.o.nblocks, c->rms_eps,
-                       x0, static_cast<const WT*>(lw.mlp_norm)};
-      rc = launch_gemm<WT, 1>(p.o, shape_of(p.o, lw.wo, d, Hq * hd, M, part, ctr), in, epi,
-                              RowMapStd{}, st);
-      if (rc) return rc;
-      P = p.o.nblocks;
-    }
-    // gate/up + silu*mul -> x1; row scale = 1 / rms(h)
-    {
-      InSplit<WT, RS_SS> in{x0.hi, x0.lo, d};
-      EpiSilu<WT> epi{x1, dff};
-      rc = launch_gemm<WT, 2>(p.gu, shape_of(p.gu, lw.w_gate_up, 2 * dff, d, M, part, ctr, ss, P,
-                                             c->rms_eps),
-                              in, epi, RowMapGateUp{dff}, st);
-      if (rc) return rc;
-    }
-    // down + residual; x0 = h * next attn_norm; after the last layer h_last
-    {
-      InSplit<WT> in{x1.hi, x1.lo, p.ld1};
-      const bool last = l == c->Ls - 1;
-      EpiResid<WT> epi{h, ss, d, M, last ? 1 : 0, static_cast<const WT*>(final_norm), h_last,
-                       ctr + CTR_FINAL, p.down.nblocks, c->rms_eps, last ? none : x0,
-                       last ? nullptr : static_cast<const WT*>(layers[l + 1].attn_norm), n_out};
-      rc = launch_gemm<WT, 1>(p.down, shape_of(p.down, lw.w_down, d, dff, M, part, ctr), in, epi,
-                              RowMapStd{}, st);
-      if (rc) return rc;
-      P = p.down.nblocks;
-    }
   }
   if (c->Ls == 0) return SPD_E_UNSUPPORTED;
   return SPD_OK;
