@@ -737,7 +737,7 @@ struct PdmPlan {
   size_t part_bytes;  // split-K partials of the decode-shaped products
   // large-M path
   bool big;
-  BigPlan bqkv, bo, bgu, bdown;
+  BigPlan bqkv, bkv, bo, bgu, bdown;  // bkv: the key/value columns of W_qkv only
   size_t off_C, off_rs, off_bpart, off_xa, off_xb;
 };
 
@@ -766,6 +766,12 @@ static RowPlans plan_rows(const spd_config* c, int M) {
   r.gu = plan_gemm(2 * c->dff, c->d, M, ks, es, 2, 256);
   r.down = plan_gemm(c->d, c->dff, M, ks, es, 1, 512);
   return r;
+}
+
+// the query heads of one row (the first Hq hd rows of W_qkv)
+static GemmPlan plan_q_row(const spd_config* c) {
+  const bool bf = c->dtype == SPD_BF16;
+  return plan_gemm(c->Hq * c->hd, c->d, 1, bf ? Mfma<bf16>::KSTEP : Mfma<float>::KSTEP, bf ? 2 : 4, 2, 256);
 }
 
 // split-K partial floats of the O, gate/up and down products over M rows
@@ -810,8 +816,13 @@ static PdmPlan plan_pdm(const spd_config* c, int M, int64_t T_cap) {
                         (size_t)c->d};
   for (int i = 0; i < 4; ++i)
     if (gps[i]->S > 1) part = std::max(part, (size_t)gps[i]->S * M * Ns[i] * 4);
-  // the one-row tail of the last layer (the chain's h_last)
+  // the one-row tail of the last layer (the chain's h_last) and, on the large-M
+  // path, the output row's query product
   part = std::max(part, tail_part_bytes(c, plan_rows(c, 1), 1));
+  {
+    const GemmPlan q1 = plan_q_row(c);
+    if (q1.S > 1) part = std::max(part, (size_t)q1.S * c->Hq * c->hd * 4);
+  }
   p.part_bytes = part;
   p.off_part = take(part);
   p.big = bf && M >= PDM_BIG_MIN_M && c->hd == 128;
@@ -820,10 +831,11 @@ static PdmPlan plan_pdm(const spd_config* c, int M, int64_t T_cap) {
     // columns, the others over the K hi columns only
     const int nq = (c->Hq + 2 * c->Hkv) * c->hd;
     p.bqkv = plan_big_gemm(M, nq, big_k(0, c->d));
+    p.bkv = plan_big_gemm(M, 2 * c->Hkv * c->hd, big_k(0, c->d));
     p.bo = plan_big_gemm(M, c->d, big_k(1, c->Hq * c->hd));
     p.bgu = plan_big_gemm(M, 2 * c->dff, big_k(2, c->d));
     p.bdown = plan_big_gemm(M, c->d, big_k(3, c->dff));
-    p.big = p.bqkv.use && p.bo.use && p.bgu.use && p.bdown.use;
+    p.big = p.bqkv.use && p.bkv.use && p.bo.use && p.bgu.use && p.bdown.use;
   }
   if (p.big) {
     const int nq = (c->Hq + 2 * c->Hkv) * c->hd;
@@ -831,7 +843,7 @@ static PdmPlan plan_pdm(const spd_config* c, int M, int64_t T_cap) {
     p.off_rs = take((size_t)M * 4);
     p.off_xa = take((size_t)M * 2 * c->d * 2);
     p.off_xb = take((size_t)M * 2 * p.ld1 * 2);
-    p.off_bpart = take(std::max(std::max(p.bqkv.part_bytes, p.bo.part_bytes),
+    p.off_bpart = take(std::max(std::max(std::max(p.bqkv.part_bytes, p.bkv.part_bytes), p.bo.part_bytes),
                                 std::max(p.bgu.part_bytes, p.bdown.part_bytes)));
   }
   p.total = off;
@@ -978,6 +990,41 @@ static int pdm_big(const spd_config* c, const spd_layer_weights* layers, const v
     const spd_layer_weights& lw = layers[l];
     WT* kc = static_cast<WT*>(k_cache) + (size_t)l * Hkv * T_cap * hd;
     WT* vc = static_cast<WT*>(v_cache) + (size_t)l * Hkv * hd * T_cap;
+    if (l == c->Ls - 1) {
+      // Last layer: every row's keys and values (the key/value columns of W_qkv on
+      // the large-M GEMM), then the output row alone on the decode-shaped kernels:
+      // its queries, attention, O and MLP (the other rows' outputs of this layer
+      // feed nothing).
+      const int nkv = 2 * Hkv * hd;
+      launch_big_gemm(p.bkv, xa, 2 * d, static_cast<const WT*>(lw.wqkv) + (size_t)Hq * hd * d, C, nkv, rs, M, nkv,
+                      big_k(0, d), bpart, ctr, st, d);
+      // C holds key heads then value heads: no query heads in front of the keys
+      hipLaunchKernelGGL((qk_post_kernel<WT>), dim3(Hkv, M), dim3(64), 0, st, C, nkv, qb, kc,
+                         static_cast<const WT*>(lw.q_norm), static_cast<const WT*>(lw.k_norm), rope, 0, pos0,
+                         T_cap, c->rms_eps);
+      hipLaunchKernelGGL((v_post_kernel<WT>), dim3(Hkv, (M + 63) / 64), dim3(256), 0, st, C, nkv, vc, Hkv * hd,
+                         pos0, T_cap, M);
+      rc = check_launch();
+      if (rc) return rc;
+      const int r = M - 1;
+      {
+        const GemmPlan qp = plan_q_row(c);
+        GemmShape gs = shape_of(qp, lw.wqkv, Hq * hd, d, 1, reinterpret_cast<float*>(w + p.off_part), ctr);
+        gs.rs_inv = rs + r;
+        const WT* xr = xa + (size_t)r * 2 * d;
+        InSplit<WT, RS_INV> in{xr, xr + d, 2 * d};
+        EpiQKV<WT> epi{qb + (size_t)r * Hq * hd, kc, vc, static_cast<const WT*>(lw.q_norm),
+                       static_cast<const WT*>(lw.k_norm), rope + (size_t)r * (hd / 2), Hq, Hkv, hd, pos0 + r,
+                       T_cap, c->rms_eps};
+        rc = launch_gemm<WT, 2>(qp, gs, in, epi, RowMapStd{}, st);
+        if (rc) return rc;
+      }
+      // (the workspace always holds the one-row tail's partials: r0 = M - 1)
+      aa.kc = kc;
+      aa.vc = vc;
+      int P = 0;
+      return layer_rows<WT>(c, p, lw, nullptr, final_norm, M, r, 1, h_last, w, aa, P, st);
+    }
     launch_big_gemm(p.bqkv, xa, 2 * d, static_cast<const WT*>(lw.wqkv), C, nq, rs, M, nq, big_k(0, d), bpart, ctr,
                     st, d);
     hipLaunchKernelGGL((qk_post_kernel<WT>), dim3(Hq + Hkv, M), dim3(64), 0, st, C, nq, qb, kc,
@@ -987,15 +1034,6 @@ static int pdm_big(const spd_config* c, const spd_layer_weights* layers, const v
                        (Hq + Hkv) * hd, pos0, T_cap, M);
     rc = check_launch();
     if (rc) return rc;
-    if (l == c->Ls - 1) {
-      // the last layer's attention, O and MLP for the output row only, on the
-      // decode-shaped kernels (the other rows' outputs of this layer feed nothing)
-      aa.kc = kc;
-      aa.vc = vc;
-      int P = 0;
-      return layer_rows<WT>(c, p, lw, nullptr, final_norm, M, last_layer_r0(c, p, M, 1), 1, h_last, w, aa, P,
-                            st);
-    }
     {
       FlashArgs fa;
       fa.q = qb;
