@@ -2,17 +2,19 @@
 // ("Speculative Pipeline Decoding", arXiv 2605.30852, section 3.1) run over the
 // M rows a cycle recomputes, attending to the committed key/value cache.
 //
-// Per layer (5 launches + attention combine):
+// Per layer (5 launches):
 //   QKV GEMM  : X = RMSNorm(h)*attn_norm staged in LDS (bf16 hi+lo pairs); per head:
 //               q/k RMSNorm, rotate-half RoPE, k/v written to the cache, q kept.
-//   attention : MFMA flash-decode, one block per (256-key chunk, kv head, 16-row
+//   attention : MFMA flash-decode, one block per (128-key chunk, kv head, 16-row
 //               query tile), GQA rows of a kv head together, waves merged in LDS;
 //               the last chunk block of a (kv head, tile) merges the chunk partials.
 //   O GEMM    : h += W_o attn                (epilogue keeps row sums of squares)
 //   gate/up   : X = RMSNorm(h)*mlp_norm; epilogue silu(gate)*up
 //   down GEMM : h += W_down act.
-// GEMMs split over K reduce their partial tiles in the last block of each tile;
-// after the last layer the down epilogue also writes h_last = RMSNorm(h[M-1]) * final_norm.
+// GEMMs split over K reduce their partial tiles in the last block of each tile.
+// The last layer runs its QKV GEMM over every row (the cache needs all keys and
+// values) and the other four launches over the output rows only; its down
+// epilogue writes h_last = RMSNorm(h[M-1]) * final_norm.
 #include <math.h>
 
 #include <algorithm>
