@@ -192,6 +192,27 @@ int spd_fuse_features(const spd_config *cfg, const void *hstore, int64_t T_cap, 
                       const void *norm_w, const void *fc_w, float *g,
                       void *ws, size_t ws_bytes, void *stream);
 
+/* FC weights with the norm folded in, for spd_fuse_features_scaled (section 3.2 Eq. (3):
+ * W_fc (norm_w * x) / rms = (W_fc diag(norm_w)) x / rms).  Writes
+ *   fc_w_scaled[c][j] = bf16(fc_w[c][j] * norm_w[j])   (the product is exact in fp32,
+ *                                                         rounded once)
+ * norm_w DEVICE bf16 [m*d]; fc_w, fc_w_scaled DEVICE bf16 [d][m*d] (caller-owned, 16-byte
+ * aligned, not overlapping).  bf16 only (SPD_E_UNSUPPORTED otherwise); d % 64 == 0. */
+int spd_fc_prepare(const spd_config *cfg, const void *norm_w, const void *fc_w, void *fc_w_scaled,
+                   void *stream);
+
+/* spd_fuse_features with the prepared weights of spd_fc_prepare.  A bf16 call with
+ * M >= 256, a == 0 and every anchor j in store slot j at depth n (each row's
+ * concatenation is then the first m*d values of its store row) runs one launch: the
+ * product reads the anchor store directly, multiplies by fc_w_scaled and scales each
+ * row by 1/rms of its store values; any other call is spd_fuse_features (fc_w_scaled is
+ * not read).  Same arguments and workspace as spd_fuse_features, plus fc_w_scaled
+ * DEVICE bf16 [d][m*d] (required). */
+int spd_fuse_features_scaled(const spd_config *cfg, const void *hstore, int64_t T_cap, int32_t S,
+                             const int32_t *slot_tab, int32_t pos0, int32_t M, int32_t a,
+                             const void *norm_w, const void *fc_w, const void *fc_w_scaled,
+                             float *g, void *ws, size_t ws_bytes, void *stream);
+
 /* PDM step (section 3.1: f_theta is an Ls-layer decoder with Qwen3-style attention; the
  * draft reads its last-position output).  Each layer (pre-norm):
  *   h += W_o . Attn(RoPE(qnorm(W_q n1)), RoPE(knorm(W_k n1)), W_v n1),  n1 = RMSNorm(h)

@@ -29,7 +29,8 @@ EXPORTED = (
     "spd_slot_table", "spd_layout", "spd_workspace_size", "spd_fuse_features",
     "spd_pdm_step", "spd_lm_head", "spd_verify", "spd_rollback", "spd_status_string",
     "spd_last_hip_error", "spd_version", "spd_fuse_features_tree", "spd_pdm_step_tree",
-    "spd_verify_siblings", "spd_cycle_plan", "spd_lm_head_noalloc",
+    "spd_verify_siblings", "spd_cycle_plan", "spd_lm_head_noalloc", "spd_fuse_features_scaled",
+    "spd_fc_prepare",
 )
 
 
@@ -90,6 +91,9 @@ def lib():
         L.spd_workspace_size.restype = _SZ
         L.spd_fuse_features.argtypes = [cfgp, _P, _I64, _I32, i32p, _I32, _I32, _I32, _P, _P, _P,
                                         _P, _SZ, _P]
+        L.spd_fuse_features_scaled.argtypes = [cfgp, _P, _I64, _I32, i32p, _I32, _I32, _I32, _P, _P,
+                                               _P, _P, _P, _SZ, _P]
+        L.spd_fc_prepare.argtypes = [cfgp, _P, _P, _P, _P]
         L.spd_pdm_step.argtypes = [cfgp, ctypes.POINTER(spd_layer_weights), _P, _P, _P, _I64, _P,
                                    _I32, _I32, _P, _P, _SZ, _P]
         L.spd_lm_head.argtypes = [cfgp, _P, _P, _I32, _F, _P, _P, _P, _P, _P, _SZ, _P]
@@ -190,6 +194,19 @@ def spd_fuse_features(cfg, hstore, T_cap, S, slot_tab, pos0, M, a, norm_w, fc_w,
         ctypes.byref(cfg), _ptr(hstore), T_cap, S, _i32_array(slot_tab), pos0, M, a,
         _ptr(norm_w), _ptr(fc_w), _ptr(g), _ptr(ws), ws.numel() * ws.element_size(),
         _stream(stream)))
+
+
+def spd_fuse_features_scaled(cfg, hstore, T_cap, S, slot_tab, pos0, M, a, norm_w, fc_w, fc_w_scaled,
+                             g, ws, stream=None):
+    _check("spd_fuse_features_scaled", lib().spd_fuse_features_scaled(
+        ctypes.byref(cfg), _ptr(hstore), T_cap, S, _i32_array(slot_tab), pos0, M, a,
+        _ptr(norm_w), _ptr(fc_w), _ptr(fc_w_scaled), _ptr(g), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def spd_fc_prepare(cfg, norm_w, fc_w, fc_w_scaled, stream=None):
+    _check("spd_fc_prepare", lib().spd_fc_prepare(
+        ctypes.byref(cfg), _ptr(norm_w), _ptr(fc_w), _ptr(fc_w_scaled), _stream(stream)))
 
 
 def layer_weights(layers) -> ctypes.Array:

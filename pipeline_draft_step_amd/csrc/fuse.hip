@@ -225,7 +225,7 @@ struct FusePlan {
   GemmPlan gp;
   BigPlan big;
   int ncb;
-  size_t off_part, off_inv, off_xh, off_xl, off_gpart, total;
+  size_t off_part, off_inv, off_xh, off_xl, off_gpart, off_gsq, total;
 };
 
 static FusePlan plan_fuse(const spd_config* cfg, int M) {
@@ -252,9 +252,11 @@ static FusePlan plan_fuse(const spd_config* cfg, int M) {
   if (p.big.use) {
     p.off_xl = take(0);
     p.off_gpart = take(p.big.part_bytes);
+    p.off_gsq = take(p.big.sq_bytes);
   } else {
     p.off_xl = take(bf ? (size_t)M * K * es : 0);
     p.off_gpart = take(p.gp.S > 1 ? (size_t)p.gp.S * M * cfg->d * 4 : 0);
+    p.off_gsq = take(0);
   }
   p.total = off;
   return p;
@@ -262,14 +264,38 @@ static FusePlan plan_fuse(const spd_config* cfg, int M) {
 
 size_t fuse_workspace(const spd_config* cfg, int M) { return plan_fuse(cfg, M).total; }
 
+// Prefill-sized calls whose rows all sit at depth n, with every anchor j in store
+// slot j at that depth: each row's concatenation is the first m d values of its
+// store row, so with the weights' columns already scaled by norm_w (spd_fc_prepare)
+// the product reads the store directly and forms the rows' 1/rms from the staged
+// tiles (no gather launch, no staged copy of the input).
+static bool direct_rows(const spd_config* cfg, const int32_t* slot_tab, int M, int a, const uint64_t* anc,
+                        const void* fc_w_scaled, const BigPlan& big) {
+  if (!fc_w_scaled || !big.use || anc || a != 0 || cfg->dtype != SPD_BF16) return false;
+  for (int j = 0; j < cfg->m; ++j)
+    if (slot_tab[cfg->n * cfg->m + j] != j) return false;
+  (void)M;
+  return true;
+}
+
 template <typename WT>
 static int fuse_impl(const spd_config* cfg, const void* hstore, int64_t T_cap, int S_store,
                      const int32_t* slot_tab, int pos0, int M, int a, const uint64_t* anc,
-                     const void* norm_w, const void* fc_w, float* g, void* ws, hipStream_t st) {
+                     const void* norm_w, const void* fc_w, const void* fc_w_scaled, float* g, void* ws,
+                     hipStream_t st) {
   (void)T_cap;
   FusePlan p = plan_fuse(cfg, M);
   const int d = cfg->d, m = cfg->m, n = cfg->n;
   char* w = static_cast<char*>(ws);
+  if constexpr (sizeof(WT) == 2) {
+    if (direct_rows(cfg, slot_tab, M, a, anc, fc_w_scaled, p.big)) {
+      const bf16* A = static_cast<const bf16*>(hstore) + (size_t)pos0 * S_store * d;
+      launch_big_gemm(p.big, A, S_store * d, static_cast<const bf16*>(fc_w_scaled), g, d, nullptr, M, d, m * d,
+                      reinterpret_cast<float*>(w + p.off_gpart), reinterpret_cast<unsigned*>(w), st, 0,
+                      reinterpret_cast<float*>(w + p.off_gsq), m * d, cfg->rms_eps);
+      return check_launch();
+    }
+  }
   GatherArgs<WT> ga;
   for (int i = 0; i < TABN; ++i) ga.tab.v[i] = -1;
   for (int k = 0; k <= n; ++k)
@@ -334,8 +360,8 @@ using namespace spd;
 
 static int fuse_entry(const spd_config* cfg, const void* hstore, int64_t T_cap, int32_t S,
                       const int32_t* slot_tab, int32_t pos0, int32_t M, int32_t a,
-                      const uint64_t* anc, const void* norm_w, const void* fc_w, float* g,
-                      void* ws, size_t ws_bytes, void* stream) {
+                      const uint64_t* anc, const void* norm_w, const void* fc_w, const void* fc_w_scaled,
+                      float* g, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_config(cfg);
   if (rc) return rc;
   if (!hstore || !slot_tab || !norm_w || !fc_w || !g || !ws) return SPD_E_INVALID;
@@ -348,21 +374,74 @@ static int fuse_entry(const spd_config* cfg, const void* hstore, int64_t T_cap, 
   for (int i = 0; i < (cfg->n + 1) * cfg->m; ++i)
     if (slot_tab[i] < -1 || slot_tab[i] >= S) return SPD_E_INVALID;
   if (!aligned16(hstore) || !aligned16(fc_w) || !aligned16(norm_w) || !aligned16(g) ||
-      !aligned16(ws))
+      !aligned16(ws) || !aligned16(fc_w_scaled))
     return SPD_E_INVALID;
   if (ws_bytes < fuse_workspace(cfg, M)) return SPD_E_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (cfg->dtype == SPD_BF16)
-    return fuse_impl<bf16>(cfg, hstore, T_cap, S, slot_tab, pos0, M, a, anc, norm_w, fc_w, g, ws, st);
-  return fuse_impl<float>(cfg, hstore, T_cap, S, slot_tab, pos0, M, a, anc, norm_w, fc_w, g, ws, st);
+    return fuse_impl<bf16>(cfg, hstore, T_cap, S, slot_tab, pos0, M, a, anc, norm_w, fc_w, fc_w_scaled, g, ws,
+                           st);
+  return fuse_impl<float>(cfg, hstore, T_cap, S, slot_tab, pos0, M, a, anc, norm_w, fc_w, fc_w_scaled, g, ws,
+                          st);
 }
 
 extern "C" int spd_fuse_features(const spd_config* cfg, const void* hstore, int64_t T_cap,
                                  int32_t S, const int32_t* slot_tab, int32_t pos0, int32_t M,
                                  int32_t a, const void* norm_w, const void* fc_w, float* g,
                                  void* ws, size_t ws_bytes, void* stream) {
-  return fuse_entry(cfg, hstore, T_cap, S, slot_tab, pos0, M, a, nullptr, norm_w, fc_w, g, ws,
+  return fuse_entry(cfg, hstore, T_cap, S, slot_tab, pos0, M, a, nullptr, norm_w, fc_w, nullptr, g, ws,
                     ws_bytes, stream);
+}
+
+extern "C" int spd_fuse_features_scaled(const spd_config* cfg, const void* hstore, int64_t T_cap,
+                                        int32_t S, const int32_t* slot_tab, int32_t pos0, int32_t M,
+                                        int32_t a, const void* norm_w, const void* fc_w,
+                                        const void* fc_w_scaled, float* g, void* ws, size_t ws_bytes,
+                                        void* stream) {
+  if (!fc_w_scaled) return SPD_E_INVALID;
+  return fuse_entry(cfg, hstore, T_cap, S, slot_tab, pos0, M, a, nullptr, norm_w, fc_w, fc_w_scaled, g, ws,
+                    ws_bytes, stream);
+}
+
+namespace {
+
+// out[c][k] = bf16(fc_w[c][k] * norm_w[k]); the product of two bf16 values is exact
+// in fp32, so the result is rounded once
+__global__ __launch_bounds__(256) void fc_scale_kernel(const bf16* fc_w, const bf16* norm_w, bf16* out, int K,
+                                                       int64_t n8) {
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n8; e += (int64_t)gridDim.x * 256) {
+    const int64_t i = e * 8;
+    const int k = (int)(i % K);
+    const uint4 wv = *reinterpret_cast<const uint4*>(fc_w + i);
+    const uint4 gv = *reinterpret_cast<const uint4*>(norm_w + k);
+    const uint32_t* wa = reinterpret_cast<const uint32_t*>(&wv);
+    const uint32_t* ga = reinterpret_cast<const uint32_t*>(&gv);
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      o[q] = pack2_bf16(bf2f((bf16)(wa[q] & 0xffff)) * bf2f((bf16)(ga[q] & 0xffff)),
+                        bf2f((bf16)(wa[q] >> 16)) * bf2f((bf16)(ga[q] >> 16)));
+    *reinterpret_cast<uint4*>(out + i) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+}  // namespace
+
+extern "C" int spd_fc_prepare(const spd_config* cfg, const void* norm_w, const void* fc_w, void* fc_w_scaled,
+                              void* stream) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!norm_w || !fc_w || !fc_w_scaled) return SPD_E_INVALID;
+  if (cfg->dtype != SPD_BF16) return SPD_E_UNSUPPORTED;
+  if (!aligned16(norm_w) || !aligned16(fc_w) || !aligned16(fc_w_scaled)) return SPD_E_INVALID;
+  const int K = cfg->m * cfg->d;  // d % 64 == 0: whole 8-element groups
+  if (cfg->d % 64) return SPD_E_UNSUPPORTED;
+  const int64_t n8 = (int64_t)cfg->d * K / 8;
+  const int blocks = (int)std::min<int64_t>((n8 + 255) / 256, 4096);
+  hipLaunchKernelGGL(fc_scale_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const bf16*>(fc_w), static_cast<const bf16*>(norm_w), static_cast<bf16*>(fc_w_scaled),
+                     K, n8);
+  return check_launch();
 }
 
 extern "C" int spd_fuse_features_tree(const spd_config* cfg, const void* hstore, int64_t T_cap,
@@ -371,6 +450,6 @@ extern "C" int spd_fuse_features_tree(const spd_config* cfg, const void* hstore,
                                       const void* fc_w, float* g, void* ws, size_t ws_bytes,
                                       void* stream) {
   if (!anc || ((uintptr_t)anc & 7) || M > SPD_TREE_MAX_NODES || a < 1) return SPD_E_INVALID;
-  return fuse_entry(cfg, hstore, T_cap, S, slot_tab, pos0, M, a, anc, norm_w, fc_w, g, ws,
+  return fuse_entry(cfg, hstore, T_cap, S, slot_tab, pos0, M, a, anc, norm_w, fc_w, nullptr, g, ws,
                     ws_bytes, stream);
 }

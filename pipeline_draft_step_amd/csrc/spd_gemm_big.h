@@ -53,6 +53,10 @@ struct BigGemm {
   int kb;  // B's K: for K = 2 kb, A's row is [hi | lo] and B's columns repeat
   int mtiles, ntiles, KS;
   int kstages;  // 64-wide K stages per block (K / (64 KS))
+  // row statistics of A (RSQ kernels): C rows scaled by 1 / sqrt(sum_k A^2 / rs_k + rs_eps)
+  float* sqp;  // [tiles][KS][BG_BM] partial sums of squares when KS > 1
+  int rs_k;
+  float rs_eps;
 };
 
 typedef f32x4 BgAccT;
@@ -93,8 +97,9 @@ __device__ __forceinline__ void bg_wait_vm() {
 // The MFMAs of one stage for wave (wm, wn).  16x16x32 operand layout: lane l
 // supplies row l % 16 and k = 8 (l / 16) .. +7 of the 32-wide k step; the B
 // tile is stored [n][k], so both operands are read the same way.
-__device__ __forceinline__ void bg_compute(const unsigned char* sa, BgAccT (&acc)[BG_FRAGS], int wm, int wn,
-                                           int lane) {
+template <bool RSQ>
+__device__ __forceinline__ void bg_compute(const unsigned char* sa, BgAccT (&acc)[BG_FRAGS], BgAccT (&sq)[2],
+                                           int wm, int wn, int lane) {
   const unsigned char* sb = sa + BG_A_BYTES;
   const int lr = lane & 15, lq = lane >> 4;
 #pragma unroll
@@ -118,6 +123,16 @@ __device__ __forceinline__ void bg_compute(const unsigned char* sa, BgAccT (&acc
         acc[i * 5 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, af[i]),
                                                                  __builtin_bit_cast(bf16x8_v, bfr[j]),
                                                                  acc[i * 5 + j], 0, 0, 0);
+    if constexpr (RSQ) {
+      // A A^T of two of the wave's four 16-row tiles (wn picks which): its diagonal
+      // holds the rows' sums of squares over this k step
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const u32x4 a = wn ? af[2 + ii] : af[ii];
+        sq[ii] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, a),
+                                                         __builtin_bit_cast(bf16x8_v, a), sq[ii], 0, 0, 0);
+      }
+    }
   }
 }
 
@@ -131,18 +146,21 @@ __device__ __forceinline__ void bg_compute(const unsigned char* sa, BgAccT (&acc
     bg_wait_vm<BG_LOADS>();                                                         \
     __builtin_amdgcn_s_barrier();                                                   \
     bg_issue(g, nxt, kbeg + min(s + BG_SLOTS - 1, ns - 1), m0, n0, wave, lane);     \
-    bg_compute(cur, acc, wm, wn, lane);                                             \
+    bg_compute<RSQ>(cur, acc, sq, wm, wn, lane);                                    \
     _Pragma("unroll") for (int r_ = 0; r_ < BG_LOADS - 1; ++r_) {                   \
       __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);                            \
       __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                            \
     }                                                                               \
-    __builtin_amdgcn_sched_group_barrier(0x008, BG_MFMAS - 6 * (BG_LOADS - 1), 0);  \
+    __builtin_amdgcn_sched_group_barrier(0x008, MF - 6 * (BG_LOADS - 1), 0);       \
     __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                              \
     ++s;                                                                            \
   } while (0)
 
-// internal linkage: every translation unit that launches it holds its own copy
+// internal linkage: every translation unit that launches it holds its own copy.
+// RSQ: the row scale comes from A itself (rs_k, rs_eps) instead of g.rs.
+template <bool RSQ>
 static __global__ __launch_bounds__(BG_THREADS) void gemm_big_kernel(BigGemm g) {
+  constexpr int MF = BG_MFMAS + (RSQ ? 4 : 0);  // MFMAs per wave and stage
   // one array per ring slot: separate objects let the compiler tell the
   // direct-to-LDS writes of later stages from the reads of the current one
   __shared__ __align__(1024) unsigned char s0[BG_STAGE_BYTES];
@@ -170,6 +188,7 @@ static __global__ __launch_bounds__(BG_THREADS) void gemm_big_kernel(BigGemm g) 
   BgAccT acc[BG_FRAGS];
 #pragma unroll
   for (int f = 0; f < BG_FRAGS; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+  BgAccT sq[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 
   int s = 0;
   while (s + BG_SLOTS <= ns) {
@@ -185,6 +204,18 @@ static __global__ __launch_bounds__(BG_THREADS) void gemm_big_kernel(BigGemm g) 
   // accumulator register e of tile (i, j): row 64 wm + 16 i + 4 (lane / 16) + e,
   // column 80 wn + 16 j + lane % 16
   const int lr = lane & 15, lq = lane >> 4;
+  __shared__ float s_sq[RSQ ? BG_BM : 1];
+  if constexpr (RSQ) {
+    // the Gram diagonal: register e of lane (lq, lr) is entry (4 lq + e, lr)
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (4 * lq + e == lr) s_sq[wm * 64 + 16 * (2 * wn + ii) + lr] = sq[ii][e];
+    __syncthreads();
+    if (KS > 1 && threadIdx.x < BG_BM)
+      st_coh(g.sqp + ((size_t)u * KS + kh) * BG_BM + threadIdx.x, s_sq[threadIdx.x]);
+  }
   if (KS > 1) {
     // partial tile as [wave][f][lane][e]: every store is 1 KB contiguous
     float* mine = g.part + ((size_t)u * KS + kh) * BG_PART_FLOATS + (size_t)wave * (BG_FRAGS * 256);
@@ -215,6 +246,16 @@ static __global__ __launch_bounds__(BG_THREADS) void gemm_big_kernel(BigGemm g) 
       }
     }
   }
+  if constexpr (RSQ) {
+    // the parts' sums in the order 0 .. KS-1 whichever block finishes
+    if (threadIdx.x < BG_BM) {
+      float t = 0.f;
+      for (int p = 0; p < KS; ++p)
+        t += p == kh ? s_sq[threadIdx.x] : ld_coh(g.sqp + ((size_t)u * KS + p) * BG_BM + threadIdx.x);
+      s_sq[threadIdx.x] = 1.0f / sqrtf(t / (float)g.rs_k + g.rs_eps);
+    }
+    __syncthreads();
+  }
   // the 16 row scales of this lane, loaded together before any store
   float rsv[4][4];
 #pragma unroll
@@ -222,7 +263,10 @@ static __global__ __launch_bounds__(BG_THREADS) void gemm_big_kernel(BigGemm g) 
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int row = m0 + wm * 64 + 16 * i + 4 * lq + e;
-      rsv[i][e] = g.rs ? g.rs[min(row, g.M - 1)] : 1.f;
+      if constexpr (RSQ)
+        rsv[i][e] = s_sq[wm * 64 + 16 * i + 4 * lq + e];
+      else
+        rsv[i][e] = g.rs ? g.rs[min(row, g.M - 1)] : 1.f;
     }
   const bool full = m0 + BG_BM <= g.M && n0 + BG_BN <= g.N;
   if (full) {
@@ -264,6 +308,7 @@ struct BigPlan {
   bool use;
   int mtiles, ntiles, KS, kstages;
   size_t part_bytes;  // partial tiles when KS > 1
+  size_t sq_bytes;    // partial row sums of squares of the row-statistics form when KS > 1
 };
 
 inline BigPlan plan_big_gemm(int M, int N, int K) {
@@ -279,6 +324,7 @@ inline BigPlan plan_big_gemm(int M, int N, int K) {
     b.KS *= 2;
   b.kstages = stages / b.KS;
   b.part_bytes = b.KS > 1 ? (size_t)b.mtiles * b.ntiles * b.KS * BG_PART_FLOATS * 4 : 0;
+  b.sq_bytes = b.KS > 1 ? (size_t)b.mtiles * b.ntiles * b.KS * BG_BM * 4 : 0;
   b.use = true;
   return b;
 }
@@ -286,10 +332,12 @@ inline BigPlan plan_big_gemm(int M, int N, int K) {
 // C[M][ldc] = rs[m] * (A[M][lda] . B[N][kb]^T) over K columns of A; K = kb, or
 // K = 2 kb with A's rows holding [hi | lo] bf16 parts of an fp32 activation (the
 // product then carries the activation to about fp32 accuracy).  counters: at
-// least mtiles * ntiles zero words, left zero.
+// least mtiles * ntiles zero words, left zero.  With rs_k > 0 (K = kb) the row
+// scale is taken from A itself: rs[m] = 1 / sqrt(sum_k A[m][k]^2 / rs_k + rs_eps),
+// the sums formed on the MFMA from the staged A tiles (sqp: p.sq_bytes).
 inline void launch_big_gemm(const BigPlan& p, const bf16* A, int lda, const bf16* B, float* C, int ldc,
                             const float* rs, int M, int N, int K, float* part, unsigned* counters,
-                            hipStream_t st, int kb = 0) {
+                            hipStream_t st, int kb = 0, float* sqp = nullptr, int rs_k = 0, float rs_eps = 0.f) {
   BigGemm g{};
   g.A = A;
   g.B = B;
@@ -308,7 +356,13 @@ inline void launch_big_gemm(const BigPlan& p, const bf16* A, int lda, const bf16
   g.ntiles = p.ntiles;
   g.KS = p.KS;
   g.kstages = p.kstages;
-  hipLaunchKernelGGL(gemm_big_kernel, dim3(p.mtiles * p.ntiles * p.KS), dim3(BG_THREADS), 0, st, g);
+  g.sqp = sqp;
+  g.rs_k = rs_k;
+  g.rs_eps = rs_eps;
+  if (rs_k > 0)
+    hipLaunchKernelGGL(gemm_big_kernel<true>, dim3(p.mtiles * p.ntiles * p.KS), dim3(BG_THREADS), 0, st, g);
+  else
+    hipLaunchKernelGGL(gemm_big_kernel<false>, dim3(p.mtiles * p.ntiles * p.KS), dim3(BG_THREADS), 0, st, g);
 }
 
 }  // namespace spd

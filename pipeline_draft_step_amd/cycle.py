@@ -14,7 +14,8 @@ from dataclasses import dataclass
 import torch
 
 from . import (SPD_BF16, SPD_CALL_FUSE, SPD_CALL_LM_HEAD, SPD_CALL_PDM, SPD_CALL_VERIFY,
-               layer_weights, make_config, spd_config, spd_cycle_plan, spd_fuse_features,
+               layer_weights, make_config, spd_config, spd_cycle_plan, spd_fc_prepare,
+               spd_fuse_features, spd_fuse_features_scaled,
                spd_lm_head, spd_pdm_step, spd_rollback, spd_slot_table, spd_verify,
                spd_workspace_size)
 
@@ -50,6 +51,17 @@ class SpdModel:
         self.T_cap = weights.store.shape[0]
         if weights.store.shape[1] != len(self.store_layers):
             raise ValueError("anchor store does not hold the layers the slot table reads")
+        self._fc_scaled = None
+
+    def fc_scaled(self):
+        """W_fc with norm_w folded into its columns (bf16; prepared on first use on the
+        current stream), or None for fp32 models."""
+        if self.cfg.dtype != SPD_BF16:
+            return None
+        if self._fc_scaled is None:
+            self._fc_scaled = torch.empty_like(self.w.w_fc)
+            spd_fc_prepare(self.cfg, self.w.fc_norm, self.w.w_fc, self._fc_scaled)
+        return self._fc_scaled
 
 
 class SpdCycle:
@@ -118,10 +130,18 @@ class SpdCycle:
 
     # ---------------------------------------------------------------- pieces
     def features(self, pos0, M, a, out=None):
+        """Features of rows pos0 .. pos0+M-1 (the last a in flight).  bf16 models pass
+        the prepared weights, which prefill-sized calls use to read the anchor store
+        directly."""
         m = self.m
         g = self.g if out is None else out
-        spd_fuse_features(m.cfg, m.w.store, m.T_cap, len(m.store_layers), m.slot_tab, pos0, M, a,
-                          m.w.fc_norm, m.w.w_fc, g, self.ws)
+        ws_ = m.fc_scaled()
+        if ws_ is None:
+            spd_fuse_features(m.cfg, m.w.store, m.T_cap, len(m.store_layers), m.slot_tab, pos0, M, a,
+                              m.w.fc_norm, m.w.w_fc, g, self.ws)
+        else:
+            spd_fuse_features_scaled(m.cfg, m.w.store, m.T_cap, len(m.store_layers), m.slot_tab, pos0,
+                                     M, a, m.w.fc_norm, m.w.w_fc, ws_, g, self.ws)
         return g
 
     def pdm(self, pos0, M, g=None):

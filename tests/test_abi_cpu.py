@@ -162,6 +162,30 @@ def test_lm_head_refuses_nucleus_without_top_k():
         assert rc == spd.SPD_E_WORKSPACE, (kw, T)   # past the filter check, stopped by ws size
 
 
+def test_prepared_feature_calls_check_their_arguments():
+    """spd_fc_prepare is bf16 only and needs all three buffers; the prepared feature
+    call needs its extra weights and otherwise checks what spd_fuse_features checks
+    (every case returns on the host)."""
+    lib = spd.lib()
+    fake = 1 << 40
+    c16 = _cfg(synth.HEADLINE)
+    assert lib.spd_fc_prepare(ctypes.byref(c16), fake, None, fake, None) == spd.SPD_E_INVALID
+    assert lib.spd_fc_prepare(ctypes.byref(c16), fake, fake, fake + 8, None) == spd.SPD_E_INVALID
+    c32 = _cfg(synth.TINY)
+    assert lib.spd_fc_prepare(ctypes.byref(c32), fake, fake, fake, None) == spd.SPD_E_UNSUPPORTED
+    s = synth.TINY
+    tab = (ctypes.c_int32 * ((s.n + 1) * s.m))(*([0] * ((s.n + 1) * s.m)))
+    rc = lib.spd_fuse_features_scaled(ctypes.byref(c32), fake, 64, 3, tab, 0, 5, 4, fake, fake, None,
+                                      fake, fake, 1 << 30, None)
+    assert rc == spd.SPD_E_INVALID        # no prepared weights
+    rc = lib.spd_fuse_features_scaled(ctypes.byref(c32), fake, 64, 3, tab, 0, 5, 4, fake, fake, fake,
+                                      fake, fake, 16, None)
+    assert rc == spd.SPD_E_WORKSPACE
+    rc = lib.spd_fuse_features_scaled(ctypes.byref(c32), fake, 64, 3, tab, 62, 5, 4, fake, fake, fake,
+                                      fake, fake, 1 << 30, None)
+    assert rc == spd.SPD_E_INVALID        # pos0 + M > T_cap
+
+
 def test_layout_rejects_bad_arguments():
     for args in ((5, 0, 4), (5, 5, 4), (4, 4, 4)):
         with pytest.raises(spd.SpdError):

@@ -141,21 +141,29 @@ PREFILL_FUSE_CASES = [
 ]
 
 
+@pytest.mark.parametrize("prepared", [False, True], ids=["gather", "prepared"])
 @pytest.mark.parametrize("name,shape,M,nsample", PREFILL_FUSE_CASES,
                          ids=[c[0] for c in PREFILL_FUSE_CASES])
-def test_fuse_features_prefill(name, shape, M, nsample):
+def test_fuse_features_prefill(name, shape, M, nsample, prepared):
     """Prefill-sized calls (every row at depth n) take the MFMA-tiled large-M GEMM:
-    split-K partial tiles, ragged M and N tiles.  The full headline product is
-    checked on sampled rows (tile edges included), which the oracle computes one
-    by one."""
+    split-K partial tiles, ragged M and N tiles; either after the gather launch
+    (spd_fuse_features) or, with the prepared weights (spd_fuse_features_scaled),
+    straight from the anchor store with the row statistics formed in the product.
+    The full headline product is checked on sampled rows (tile edges included),
+    which the oracle computes one by one."""
     ci = make_inputs(shape, device=DEV, with_heads=False)
     model = device_model(ci)
     cyc = SpdCycle(model, shape.temperature)
     om = OC.model_from_inputs(ci, with_heads=False)
-    say(name, "prefill fuse", M)
+    say(name, "prefill fuse", M, "prepared" if prepared else "gather")
     out = torch.full((M, shape.d), float("nan"), device=DEV)
+    pos0 = 3 if M < 2048 else 0   # the store rows from pos0 (ctx leaves room for it)
     for rep in range(2):  # the second call reuses the arrival counters the first left at zero
-        cyc.features(0, M, 0, out=out)
+        if prepared:
+            cyc.features(pos0, M, 0, out=out)
+        else:
+            spd.spd_fuse_features(model.cfg, model.w.store, model.T_cap, len(model.store_layers),
+                                  model.slot_tab, pos0, M, 0, model.w.fc_norm, model.w.w_fc, out, cyc.ws)
     torch.cuda.synchronize()
     if nsample is None:
         rows = list(range(M))
@@ -163,13 +171,45 @@ def test_fuse_features_prefill(name, shape, M, nsample):
         rng = np.random.default_rng(5)
         edges = [0, 1, 255, 256, 511, 512, M // 2, M - 2, M - 1]
         rows = sorted(set(edges) | set(int(x) for x in rng.choice(M, nsample, replace=False)))
-    ref = O.fuse_features(om.store, om.store_layers, rows, [shape.n] * len(rows), om.fc_norm,
-                          om.w_fc, L=shape.L, n=shape.n, anchors=shape.anchors,
+    ref = O.fuse_features(om.store, om.store_layers, [pos0 + r for r in rows], [shape.n] * len(rows),
+                          om.fc_norm, om.w_fc, L=shape.L, n=shape.n, anchors=shape.anchors,
                           mode=shape.anchor_mode, eps=shape.eps, norm_k0=bool(shape.norm_k0))
     got = f64(out)[rows]
     assert np.isfinite(got).all()
     err = rel_err(got, ref)
     assert err < tol_for(shape.dtype), (M, err)
+
+
+def test_fc_prepare_folds_the_norm_into_the_weights():
+    """spd_fc_prepare: every weight times its column's norm weight, rounded to bf16
+    once (the fp32 product of two bf16 values is exact), bit for bit."""
+    s = synth.HEADLINE
+    ci = make_inputs(s, device=DEV, with_heads=False)
+    model = device_model(ci)
+    say("fc_prepare", tuple(ci.w_fc.shape))
+    out = torch.empty_like(ci.w_fc)
+    spd.spd_fc_prepare(model.cfg, ci.fc_norm, ci.w_fc, out)
+    ref = (ci.w_fc.float() * ci.fc_norm.float()[None, :]).to(torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+def test_prepared_features_fall_back_where_rows_are_not_all_full_depth():
+    """With prepared weights, calls that do not qualify for the one-launch form
+    (rows in flight, decode sizes) are the gather path exactly."""
+    s = synth.HEADLINE
+    ci = make_inputs(s, device=DEV, with_heads=False)
+    model = device_model(ci)
+    cyc = SpdCycle(model, s.temperature)
+    for pos0, M, a in ((100, 300, 8), (s.ctx - 9, 9, 8), (s.ctx - 4, 4, 3)):
+        say("prepared fallback", pos0, M, a)
+        x = torch.empty(M, s.d, device=DEV)
+        y = torch.empty(M, s.d, device=DEV)
+        cyc.features(pos0, M, a, out=x)
+        spd.spd_fuse_features(model.cfg, model.w.store, model.T_cap, len(model.store_layers), model.slot_tab,
+                              pos0, M, a, model.w.fc_norm, model.w.w_fc, y, cyc.ws)
+        torch.cuda.synchronize()
+        assert torch.equal(x, y), (pos0, M, a)
 
 
 # ------------------------------------------------------------------ PDM step
