@@ -538,18 +538,6 @@ __global__ __launch_bounds__(256) void resid_post_kernel(const float* C, int ldc
   if (threadIdx.x == 0) rs[r] = 1.0f / sqrtf(t / (float)d + eps);
 }
 
-// act[r][j] = silu(gate_j) * up_j (gate columns first, then up) as a [hi | lo]
-// row of 2 dff bf16 values
-template <typename WT>
-__global__ __launch_bounds__(256) void swiglu_post_kernel(const float* C, int ldc, WT* xb, int dff) {
-  const int r = blockIdx.y, j = 4 * (blockIdx.x * 256 + threadIdx.x);
-  if (j >= dff) return;
-  const float4 gt = *reinterpret_cast<const float4*>(C + (size_t)r * ldc + j);
-  const float4 up = *reinterpret_cast<const float4*>(C + (size_t)r * ldc + dff + j);
-  auto act = [](float gv, float uv) { return gv / (1.0f + expf(-gv)) * uv; };
-  put4_hilo(xb + (size_t)r * 2 * dff + j, dff,
-            make_float4(act(gt.x, up.x), act(gt.y, up.y), act(gt.z, up.z), act(gt.w, up.w)));
-}
 
 // Causal attention for prefill-sized steps (bf16, hd = 128), flash style: a block
 // owns 64 of a kv head's GQA query rows (query index qi = row * G + head in the
@@ -835,13 +823,13 @@ static PdmPlan plan_pdm(const spd_config* c, int M, int64_t T_cap) {
     p.bqkv = plan_big_gemm(M, nq, big_k(0, c->d));
     p.bkv = plan_big_gemm(M, 2 * c->Hkv * c->hd, big_k(0, c->d));
     p.bo = plan_big_gemm(M, c->d, big_k(1, c->Hq * c->hd));
-    p.bgu = plan_big_gemm(M, 2 * c->dff, big_k(2, c->d));
+    p.bgu = plan_big_swiglu(M, c->dff, big_k(2, c->d));
     p.bdown = plan_big_gemm(M, c->d, big_k(3, c->dff));
     p.big = p.bqkv.use && p.bkv.use && p.bo.use && p.bgu.use && p.bdown.use;
   }
   if (p.big) {
     const int nq = (c->Hq + 2 * c->Hkv) * c->hd;
-    p.off_C = take((size_t)M * std::max(std::max(nq, c->d), 2 * c->dff) * 4);
+    p.off_C = take((size_t)M * std::max(nq, c->d) * 4);  // gate/up writes its activations directly
     p.off_rs = take((size_t)M * 4);
     p.off_xa = take((size_t)M * 2 * c->d * 2);
     p.off_xb = take((size_t)M * 2 * p.ld1 * 2);
@@ -1059,10 +1047,8 @@ static int pdm_big(const spd_config* c, const spd_layer_weights* layers, const v
                     st, ko);
     hipLaunchKernelGGL((resid_post_kernel<WT>), dim3(M), dim3(256), 0, st, C, d, h, rs, xa,
                        static_cast<const WT*>(lw.mlp_norm), d, c->rms_eps);
-    launch_big_gemm(p.bgu, xa, 2 * d, static_cast<const WT*>(lw.w_gate_up), C, 2 * dff, rs, M, 2 * dff,
-                    big_k(2, d), bpart, ctr, st, d);
-    hipLaunchKernelGGL((swiglu_post_kernel<WT>), dim3((dff / 4 + 255) / 256, M), dim3(256), 0, st, C, 2 * dff,
-                       xb, dff);
+    launch_big_swiglu(p.bgu, xa, 2 * d, static_cast<const WT*>(lw.w_gate_up), xb, 2 * dff, dff, rs, M,
+                      big_k(2, d), bpart, ctr, st, d);
     launch_big_gemm(p.bdown, xb, 2 * dff, static_cast<const WT*>(lw.w_down), C, d, nullptr, M, d, big_k(3, dff),
                     bpart, ctr, st, dff);
     hipLaunchKernelGGL((resid_post_kernel<WT>), dim3(M), dim3(256), 0, st, C, d, h, rs, xa,

@@ -57,7 +57,14 @@ struct BigGemm {
   float* sqp;  // [tiles][KS][BG_BM] partial sums of squares when KS > 1
   int rs_k;
   float rs_eps;
+  // gate/up with SwiGLU (BG_EPI_SWIGLU): B = [gate; up] with `half` rows each; a tile
+  // takes 80 gate rows and the matching 80 up rows and writes silu(gate) * up as
+  // [hi | lo] bf16 rows of act (row stride act_ld) instead of C
+  bf16* act;
+  int act_ld, half;
 };
+
+enum { BG_EPI_PLAIN = 0, BG_EPI_RSQ = 1, BG_EPI_SWIGLU = 2 };
 
 typedef f32x4 BgAccT;
 
@@ -69,6 +76,7 @@ __device__ __forceinline__ int bg_swz(int r) { return r & 7; }
 // `base`: 1 KB groups (8 tile rows) v, v + 8, ...; the 52 groups do not split
 // evenly, so waves 4 .. 7 repeat one of their own groups (same bytes to the
 // same place) instead of taking a branch.
+template <bool GU>
 __device__ __forceinline__ void bg_issue(const BigGemm& g, unsigned char* base, int st, int m0, int n0,
                                          int v, int lane) {
   const int k0 = st * BG_BK;
@@ -81,8 +89,15 @@ __device__ __forceinline__ void bg_issue(const BigGemm& g, unsigned char* base, 
     const bool isA = q < BG_A_GROUPS;
     const int r = 8 * (isA ? q : q - BG_A_GROUPS) + rin;  // tile row
     const int c = pc ^ bg_swz(r);
-    const bf16* src = isA ? g.A + (size_t)min(m0 + r, g.M - 1) * g.lda + k0
-                          : g.B + (size_t)min(n0 + r, g.N - 1) * g.ldb + kB;
+    int brow;
+    if constexpr (GU) {
+      // rows 0..79: gate rows n0 .., rows 80..159: the matching up rows
+      const int rr = r < 80 ? r : r - 80;
+      brow = min(n0 + rr, g.half - 1) + (r < 80 ? 0 : g.half);
+    } else {
+      brow = min(n0 + r, g.N - 1);
+    }
+    const bf16* src = isA ? g.A + (size_t)min(m0 + r, g.M - 1) * g.lda + k0 : g.B + (size_t)brow * g.ldb + kB;
     __builtin_amdgcn_global_load_lds((const void*)(src + 8 * c), (lds_ptr_t)(base + q * 1024), 16, 0, 0);
   }
 }
@@ -145,7 +160,7 @@ __device__ __forceinline__ void bg_compute(const unsigned char* sa, BgAccT (&acc
   do {                                                                              \
     bg_wait_vm<BG_LOADS>();                                                         \
     __builtin_amdgcn_s_barrier();                                                   \
-    bg_issue(g, nxt, kbeg + min(s + BG_SLOTS - 1, ns - 1), m0, n0, wave, lane);     \
+    bg_issue<GU>(g, nxt, kbeg + min(s + BG_SLOTS - 1, ns - 1), m0, n0, wave, lane); \
     bg_compute<RSQ>(cur, acc, sq, wm, wn, lane);                                    \
     _Pragma("unroll") for (int r_ = 0; r_ < BG_LOADS - 1; ++r_) {                   \
       __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);                            \
@@ -157,9 +172,11 @@ __device__ __forceinline__ void bg_compute(const unsigned char* sa, BgAccT (&acc
   } while (0)
 
 // internal linkage: every translation unit that launches it holds its own copy.
-// RSQ: the row scale comes from A itself (rs_k, rs_eps) instead of g.rs.
-template <bool RSQ>
+// EPI: BG_EPI_PLAIN writes rs[m] * (A B^T); BG_EPI_RSQ takes the row scale from A
+// itself (rs_k, rs_eps) instead of g.rs; BG_EPI_SWIGLU writes silu(gate) * up.
+template <int EPI>
 static __global__ __launch_bounds__(BG_THREADS) void gemm_big_kernel(BigGemm g) {
+  constexpr bool RSQ = EPI == BG_EPI_RSQ, GU = EPI == BG_EPI_SWIGLU;
   constexpr int MF = BG_MFMAS + (RSQ ? 4 : 0);  // MFMAs per wave and stage
   // one array per ring slot: separate objects let the compiler tell the
   // direct-to-LDS writes of later stages from the reads of the current one
@@ -179,11 +196,11 @@ static __global__ __launch_bounds__(BG_THREADS) void gemm_big_kernel(BigGemm g) 
   const int gsz = min(g.mtiles - first_m, GM);
   const int tin = u - grp * GM * g.ntiles;
   const int mt = first_m + tin % gsz, nt = tin / gsz;
-  const int m0 = mt * BG_BM, n0 = nt * BG_BN;
+  const int m0 = mt * BG_BM, n0 = nt * (GU ? BG_BN / 2 : BG_BN);
   const int ns = g.kstages, kbeg = kh * ns;  // the host guarantees ns >= BG_SLOTS
 
-  bg_issue(g, s0, kbeg, m0, n0, wave, lane);
-  bg_issue(g, s1, kbeg + 1, m0, n0, wave, lane);
+  bg_issue<GU>(g, s0, kbeg, m0, n0, wave, lane);
+  bg_issue<GU>(g, s1, kbeg + 1, m0, n0, wave, lane);
 
   BgAccT acc[BG_FRAGS];
 #pragma unroll
@@ -268,6 +285,46 @@ static __global__ __launch_bounds__(BG_THREADS) void gemm_big_kernel(BigGemm g) 
       else
         rsv[i][e] = g.rs ? g.rs[min(row, g.M - 1)] : 1.f;
     }
+  if constexpr (GU) {
+    // the up half (wn = 1) hands its scaled values to the gate half through the
+    // stage buffers (every wave is past its last read of them), which writes
+    // silu(gate) * up for its 80 columns
+    __syncthreads();
+    float* xch = reinterpret_cast<float*>(wm < 2 ? s0 : s1) + (size_t)(wm & 1) * (BG_FRAGS * 4 * 64);
+    if (wn == 1) {
+#pragma unroll
+      for (int f = 0; f < BG_FRAGS; ++f)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xch[(f * 4 + e) * 64 + lane] = acc[f][e] * rsv[f / 5][e];
+    }
+    __syncthreads();
+    if (wn == 0) {
+      // columns 16 j + lr and + 1 sit in neighbouring lanes: the even lane of each
+      // pair writes both (4-byte stores); half is even, so a pair never straddles it
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = m0 + wm * 64 + 16 * i + 4 * lq + e;
+#pragma unroll
+          for (int j = 0; j < 5; ++j) {
+            const int col = n0 + 16 * j + lr;
+            const float gt = acc[i * 5 + j][e] * rsv[i][e];
+            const float up = xch[((i * 5 + j) * 4 + e) * 64 + lane];
+            const float a = gt / (1.0f + expf(-gt)) * up;
+            const bf16 hi = f2bf(a), lo = f2bf(a - bf2f(hi));
+            const uint32_t hl = (uint32_t)hi | ((uint32_t)lo << 16);
+            const uint32_t nb = (uint32_t)__shfl_xor((int)hl, 1, 64);
+            if ((lr & 1) == 0 && row < g.M && col < g.half) {
+              bf16* out = g.act + (size_t)row * g.act_ld + col;
+              *reinterpret_cast<uint32_t*>(out) = (hl & 0xffffu) | (nb << 16);
+              *reinterpret_cast<uint32_t*>(out + g.half) = (hl >> 16) | (nb & 0xffff0000u);
+            }
+          }
+        }
+    }
+    return;
+  }
   const bool full = m0 + BG_BM <= g.M && n0 + BG_BN <= g.N;
   if (full) {
     // no bounds checks: one straight run of stores
@@ -360,9 +417,42 @@ inline void launch_big_gemm(const BigPlan& p, const bf16* A, int lda, const bf16
   g.rs_k = rs_k;
   g.rs_eps = rs_eps;
   if (rs_k > 0)
-    hipLaunchKernelGGL(gemm_big_kernel<true>, dim3(p.mtiles * p.ntiles * p.KS), dim3(BG_THREADS), 0, st, g);
+    hipLaunchKernelGGL(gemm_big_kernel<BG_EPI_RSQ>, dim3(p.mtiles * p.ntiles * p.KS), dim3(BG_THREADS), 0, st, g);
   else
-    hipLaunchKernelGGL(gemm_big_kernel<false>, dim3(p.mtiles * p.ntiles * p.KS), dim3(BG_THREADS), 0, st, g);
+    hipLaunchKernelGGL(gemm_big_kernel<BG_EPI_PLAIN>, dim3(p.mtiles * p.ntiles * p.KS), dim3(BG_THREADS), 0, st,
+                       g);
+}
+
+// Gate/up product with the SwiGLU epilogue: W = [gate; up] ([2 half][kb] bf16), A as in
+// launch_big_gemm; act[m][j] = silu(g_j) * u_j with g, u = rs[m] * (A W^T), written as
+// bf16 hi at act + m act_ld + j and lo at + half.  Plan: plan_big_swiglu.
+inline BigPlan plan_big_swiglu(int M, int half, int K) {
+  return plan_big_gemm(M, BG_BN * ((half + BG_BN / 2 - 1) / (BG_BN / 2)), K);
+}
+inline void launch_big_swiglu(const BigPlan& p, const bf16* A, int lda, const bf16* W, bf16* act, int act_ld,
+                              int half, const float* rs, int M, int K, float* part, unsigned* counters,
+                              hipStream_t st, int kb) {
+  BigGemm g{};
+  g.A = A;
+  g.B = W;
+  g.rs = rs;
+  g.part = part;
+  g.counters = counters;
+  g.M = M;
+  g.N = 2 * half;
+  g.K = K;
+  g.lda = lda;
+  g.kb = kb > 0 ? kb : K;
+  g.ldb = g.kb;
+  g.mtiles = p.mtiles;
+  g.ntiles = p.ntiles;
+  g.KS = p.KS;
+  g.kstages = p.kstages;
+  g.act = act;
+  g.act_ld = act_ld;
+  g.half = half;
+  hipLaunchKernelGGL(gemm_big_kernel<BG_EPI_SWIGLU>, dim3(p.mtiles * p.ntiles * p.KS), dim3(BG_THREADS), 0, st,
+                     g);
 }
 
 }  // namespace spd
