@@ -87,7 +87,7 @@ __device__ __forceinline__ BlockStat ld_stat(const BlockStat* p) {
 template <bool COH>
 __device__ BlockStat merge_stats(const BlockStat* st, int stride, int n, float inv_t) {
   __shared__ BlockStat s_ws[SMX_THREADS / 64];
-  constexpr int PB = 8;
+  constexpr int PB = 20;  // one round of loads for up to 5120 statistics
   BlockStat a{-INFINITY, ARG_NONE, 0.f};
   for (int b0 = 0; b0 < n; b0 += PB * SMX_THREADS) {
     BlockStat v[PB];
