@@ -14,6 +14,11 @@
 // which takes the input pre-split into bf16 hi/lo parts (fp32-accurate
 // activations); prefill-sized calls in bf16 run the MFMA-tiled large-M GEMM,
 // which takes the bf16-rounded input as a plain bf16 operand.
+//
+// One launch (spd_fuse_features_scaled): with W_fc diag(gamma) prepared once
+// (spd_fc_prepare), a prefill-sized call whose rows all sit at depth n, with anchor j
+// in store slot j, runs only the large-M GEMM: A is the anchor store itself and the
+// row scale comes from the sums of squares the product forms from its A tiles.
 #include "spd_common.h"
 #include "spd_gemm.h"
 #include "spd_gemm_big.h"
@@ -269,12 +274,11 @@ size_t fuse_workspace(const spd_config* cfg, int M) { return plan_fuse(cfg, M).t
 // store row, so with the weights' columns already scaled by norm_w (spd_fc_prepare)
 // the product reads the store directly and forms the rows' 1/rms from the staged
 // tiles (no gather launch, no staged copy of the input).
-static bool direct_rows(const spd_config* cfg, const int32_t* slot_tab, int M, int a, const uint64_t* anc,
+static bool direct_rows(const spd_config* cfg, const int32_t* slot_tab, int a, const uint64_t* anc,
                         const void* fc_w_scaled, const BigPlan& big) {
   if (!fc_w_scaled || !big.use || anc || a != 0 || cfg->dtype != SPD_BF16) return false;
   for (int j = 0; j < cfg->m; ++j)
     if (slot_tab[cfg->n * cfg->m + j] != j) return false;
-  (void)M;
   return true;
 }
 
@@ -288,7 +292,7 @@ static int fuse_impl(const spd_config* cfg, const void* hstore, int64_t T_cap, i
   const int d = cfg->d, m = cfg->m, n = cfg->n;
   char* w = static_cast<char*>(ws);
   if constexpr (sizeof(WT) == 2) {
-    if (direct_rows(cfg, slot_tab, M, a, anc, fc_w_scaled, p.big)) {
+    if (direct_rows(cfg, slot_tab, a, anc, fc_w_scaled, p.big)) {
       const bf16* A = static_cast<const bf16*>(hstore) + (size_t)pos0 * S_store * d;
       launch_big_gemm(p.big, A, S_store * d, static_cast<const bf16*>(fc_w_scaled), g, d, nullptr, M, d, m * d,
                       reinterpret_cast<float*>(w + p.off_gpart), reinterpret_cast<unsigned*>(w), st, 0,
