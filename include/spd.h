@@ -233,6 +233,31 @@ int spd_pdm_step(const spd_config *cfg, const spd_layer_weights *layers, const v
                  void *k_cache, void *v_cache, int64_t T_cap, const float *g, int32_t pos0,
                  int32_t M, float *h_last, void *ws, size_t ws_bytes, void *stream);
 
+/* Prepared weights for prefill-sized PDM steps (the same decoder as spd_pdm_step, section
+ * 3.1).  Those steps carry each activation feeding the QKV, gate/up and down products as
+ * a bf16 part plus its residual; with prepared weights the residual's product runs on the
+ * block-scaled e4m3 MFMA instead of a second bf16 pass (about 2^-12 of the activation
+ * against 2^-9 for the bf16 part alone).  spd_pdm_prepare writes, per layer, e4m3 copies
+ * of W_qkv, W_gate_up and W_down with one power-of-two factor per row (the row's largest
+ * magnitude scaled into [128, 256)) and that row's E8M0 scale byte.
+ * spd_pdm_prepared_bytes: the buffer size, 0 when the configuration takes no prepared
+ *   weights (they need bf16, hd == 128, d % 128 == 0 and dff % 128 == 0).
+ * spd_pdm_prepare: prep DEVICE, 16-byte aligned, prep_bytes >= that size; layers as in
+ *   spd_pdm_step (the three matrices are read).  SPD_E_UNSUPPORTED for other
+ *   configurations, SPD_E_WORKSPACE if prep_bytes is short.  Run it again whenever the
+ *   weights change.
+ * spd_pdm_step_prepared: spd_pdm_step with prep (written by spd_pdm_prepare for these
+ *   weights, prep_bytes its size), used by steps with M >= 256; prep == NULL is
+ *   spd_pdm_step.  SPD_E_INVALID when prep is given for a configuration that takes none.
+ *   Same workspace as spd_pdm_step. */
+size_t spd_pdm_prepared_bytes(const spd_config *cfg);
+int spd_pdm_prepare(const spd_config *cfg, const spd_layer_weights *layers, void *prep,
+                    size_t prep_bytes, void *stream);
+int spd_pdm_step_prepared(const spd_config *cfg, const spd_layer_weights *layers, const void *prep,
+                          size_t prep_bytes, const void *final_norm, void *k_cache, void *v_cache,
+                          int64_t T_cap, const float *g, int32_t pos0, int32_t M, float *h_last,
+                          void *ws, size_t ws_bytes, void *stream);
+
 /* LM head and next-token choice (section 3.1 Eq. (1); section 3.4 target head).
  * logits[r] = W_lm . h[r] for r < rows (rows <= 16).
  * temperature == 0: token[r] = lowest index of the maximum logit (NaN never wins);

@@ -30,7 +30,7 @@ EXPORTED = (
     "spd_pdm_step", "spd_lm_head", "spd_verify", "spd_rollback", "spd_status_string",
     "spd_last_hip_error", "spd_version", "spd_fuse_features_tree", "spd_pdm_step_tree",
     "spd_verify_siblings", "spd_cycle_plan", "spd_lm_head_noalloc", "spd_fuse_features_scaled",
-    "spd_fc_prepare",
+    "spd_fc_prepare", "spd_pdm_prepared_bytes", "spd_pdm_prepare", "spd_pdm_step_prepared",
 )
 
 
@@ -96,6 +96,11 @@ def lib():
         L.spd_fc_prepare.argtypes = [cfgp, _P, _P, _P, _P]
         L.spd_pdm_step.argtypes = [cfgp, ctypes.POINTER(spd_layer_weights), _P, _P, _P, _I64, _P,
                                    _I32, _I32, _P, _P, _SZ, _P]
+        L.spd_pdm_prepared_bytes.argtypes = [cfgp]
+        L.spd_pdm_prepared_bytes.restype = _SZ
+        L.spd_pdm_prepare.argtypes = [cfgp, ctypes.POINTER(spd_layer_weights), _P, _SZ, _P]
+        L.spd_pdm_step_prepared.argtypes = [cfgp, ctypes.POINTER(spd_layer_weights), _P, _SZ, _P, _P, _P,
+                                            _I64, _P, _I32, _I32, _P, _P, _SZ, _P]
         L.spd_lm_head.argtypes = [cfgp, _P, _P, _I32, _F, _P, _P, _P, _P, _P, _SZ, _P]
         L.spd_lm_head_noalloc.argtypes = [cfgp, _P, _P, _I32, _F, _P, _P, _P, _P, _P]
         L.spd_verify.argtypes = [_I32, _I32, _I32, _F, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
@@ -216,6 +221,27 @@ def layer_weights(layers) -> ctypes.Array:
         for k, _ in spd_layer_weights._fields_:
             setattr(arr[i], k, _ptr(lw[k]))
     return arr
+
+
+def spd_pdm_prepared_bytes(cfg) -> int:
+    """Bytes of the prepared e4m3 weight copies spd_pdm_prepare writes (0: the
+    configuration takes none)."""
+    return int(lib().spd_pdm_prepared_bytes(ctypes.byref(cfg)))
+
+
+def spd_pdm_prepare(cfg, layers, prep, stream=None):
+    arr = layers if isinstance(layers, ctypes.Array) else layer_weights(layers)
+    _check("spd_pdm_prepare", lib().spd_pdm_prepare(
+        ctypes.byref(cfg), arr, _ptr(prep), prep.numel() * prep.element_size(), _stream(stream)))
+
+
+def spd_pdm_step_prepared(cfg, layers, prep, final_norm, k_cache, v_cache, T_cap, g, pos0, M, h_last,
+                          ws, stream=None):
+    arr = layers if isinstance(layers, ctypes.Array) else layer_weights(layers)
+    _check("spd_pdm_step_prepared", lib().spd_pdm_step_prepared(
+        ctypes.byref(cfg), arr, _ptr(prep), 0 if prep is None else prep.numel() * prep.element_size(),
+        _ptr(final_norm), _ptr(k_cache), _ptr(v_cache), T_cap, _ptr(g), pos0, M, _ptr(h_last), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def spd_pdm_step(cfg, layers, final_norm, k_cache, v_cache, T_cap, g, pos0, M, h_last, ws,

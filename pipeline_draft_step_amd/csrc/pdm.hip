@@ -447,13 +447,36 @@ __device__ __forceinline__ void put4_hilo(bf16* p, int K, float4 v) {
   *reinterpret_cast<uint2*>(p + K) = make_uint2(l0, l1);
 }
 
-// h = g, the row's 1/rms, the first QKV input g * attn_norm as a [hi | lo] row
-// of 2d bf16 values, and the rotate-half RoPE table of the row's position
+// four values as bf16 hi parts at p and their lo8 bytes (e4m3 of 256 (v - hi)) at q
+__device__ __forceinline__ void put4_hilo8(bf16* p, unsigned char* q, float4 v) {
+  const uint32_t h0 = pack2_bf16(v.x, v.y), h1 = pack2_bf16(v.z, v.w);
+  *reinterpret_cast<uint2*>(p) = make_uint2(h0, h1);
+  *reinterpret_cast<uint32_t*>(q) =
+      lo8_word(v.x - __uint_as_float(h0 << 16), v.y - __uint_as_float(h0 & 0xffff0000u),
+               v.z - __uint_as_float(h1 << 16), v.w - __uint_as_float(h1 & 0xffff0000u));
+}
+
+// A row of the next large-M product's input: [hi | lo] (2d bf16), or with LO8
+// [hi | lo8] (d bf16 hi parts, then d lo8 bytes: 3d bytes); with LO8 row M - 1 also
+// goes to xlast as [hi | lo] (the output row's query product on the decode kernels).
+template <bool LO8>
+__device__ __forceinline__ void put4_row(bf16* xa, bf16* xlast, int r, int M, int d, int c, float4 v) {
+  if constexpr (LO8) {
+    bf16* row = xa + (size_t)r * (3 * d / 2);
+    put4_hilo8(row + c, reinterpret_cast<unsigned char*>(row + d) + c, v);
+    if (r == M - 1) put4_hilo(xlast + c, d, v);
+  } else {
+    put4_hilo(xa + (size_t)r * 2 * d + c, d, v);
+  }
+}
+
+// h = g, the row's 1/rms, the first QKV input g * attn_norm as a row of the next
+// product's input (put4_row), and the rotate-half RoPE table of the row's position
 // (fp64 angles)
-template <typename WT>
+template <typename WT, bool LO8>
 __global__ __launch_bounds__(256) void big_rows_init_kernel(const float* g, float* h, float* rs, WT* xa,
                                                             const WT* gamma, float2* rope, int d, int pos0,
-                                                            int hd, float theta, float eps) {
+                                                            int hd, float theta, float eps, WT* xlast, int M) {
   const int r = blockIdx.x;
   if (threadIdx.x < hd / 2) {
     double sn, cs;
@@ -466,9 +489,9 @@ __global__ __launch_bounds__(256) void big_rows_init_kernel(const float* g, floa
     const float4 v = *reinterpret_cast<const float4*>(g + i);
     *reinterpret_cast<float4*>(h + i) = v;
     sq += (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
-    put4_hilo(xa + (size_t)r * 2 * d + c, d,
-              make_float4(v.x * to_f<WT>(gamma[c]), v.y * to_f<WT>(gamma[c + 1]), v.z * to_f<WT>(gamma[c + 2]),
-                          v.w * to_f<WT>(gamma[c + 3])));
+    put4_row<LO8>(xa, xlast, r, M, d, c,
+                  make_float4(v.x * to_f<WT>(gamma[c]), v.y * to_f<WT>(gamma[c + 1]), v.z * to_f<WT>(gamma[c + 2]),
+                              v.w * to_f<WT>(gamma[c + 3])));
   }
   const float t = block_sum256(sq);
   if (threadIdx.x == 0) rs[r] = 1.0f / sqrtf(t / (float)d + eps);
@@ -514,10 +537,10 @@ __global__ __launch_bounds__(256) void v_post_kernel(const float* C, int ldc, WT
   for (int dim = threadIdx.x >> 6; dim < 128; dim += 4) vp[(size_t)dim * T_cap] = from_f<WT>(y[dim]);
 }
 
-// h += y, the row's 1/rms and the next GEMM's input h * gnext as a [hi | lo] row
-template <typename WT>
+// h += y, the row's 1/rms and the next GEMM's input h * gnext (put4_row)
+template <typename WT, bool LO8>
 __global__ __launch_bounds__(256) void resid_post_kernel(const float* C, int ldc, float* h, float* rs, WT* xa,
-                                                         const WT* gnext, int d, float eps) {
+                                                         const WT* gnext, int d, float eps, WT* xlast, int M) {
   const int r = blockIdx.x;
   float sq = 0.f;
   for (int c = 4 * threadIdx.x; c < d; c += 4 * 256) {
@@ -530,9 +553,9 @@ __global__ __launch_bounds__(256) void resid_post_kernel(const float* C, int ldc
     v.w += y.w;
     *reinterpret_cast<float4*>(h + i) = v;
     sq += (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
-    put4_hilo(xa + (size_t)r * 2 * d + c, d,
-              make_float4(v.x * to_f<WT>(gnext[c]), v.y * to_f<WT>(gnext[c + 1]), v.z * to_f<WT>(gnext[c + 2]),
-                          v.w * to_f<WT>(gnext[c + 3])));
+    put4_row<LO8>(xa, xlast, r, M, d, c,
+                  make_float4(v.x * to_f<WT>(gnext[c]), v.y * to_f<WT>(gnext[c + 1]), v.z * to_f<WT>(gnext[c + 2]),
+                              v.w * to_f<WT>(gnext[c + 3])));
   }
   const float t = block_sum256(sq);
   if (threadIdx.x == 0) rs[r] = 1.0f / sqrtf(t / (float)d + eps);
@@ -729,7 +752,38 @@ struct PdmPlan {
   bool big;
   BigPlan bqkv, bkv, bo, bgu, bdown;  // bkv: the key/value columns of W_qkv only
   size_t off_C, off_rs, off_bpart, off_xa, off_xb;
+  // the same products with [hi | lo8] inputs (prepared e4m3 weights), and the output
+  // row's [hi | lo] copy for its query product
+  bool big8;
+  BigPlan b8qkv, b8kv, b8gu, b8down;
+  size_t off_xlast;
 };
+
+// Prepared e4m3 copies (spd_pdm_prepare) of the weights of the products that take
+// [hi | lo] inputs on the large-M path: per layer W_qkv, W_gate_up and W_down as
+// [rows][K] bytes, then their per-row E8M0 scale bytes, each 256-byte aligned.
+struct PrepLayout {
+  size_t qkv8, gu8, dn8, qkv_s, gu_s, dn_s, layer_bytes, total;
+};
+static PrepLayout prep_layout(const spd_config* c) {
+  PrepLayout L{};
+  const size_t nq = (size_t)(c->Hq + 2 * c->Hkv) * c->hd, d = c->d, dff = c->dff;
+  size_t off = 0;
+  auto take = [&](size_t b) { size_t r = off; off = align256(off + b); return r; };
+  L.qkv8 = take(nq * d);
+  L.gu8 = take(2 * dff * d);
+  L.dn8 = take(d * dff);
+  L.qkv_s = take(nq);
+  L.gu_s = take(2 * dff);
+  L.dn_s = take(d);
+  L.layer_bytes = off;
+  L.total = off * (size_t)c->Ls;
+  return L;
+}
+// the configurations whose large-M products take prepared weights
+static bool prep_supported(const spd_config* c) {
+  return c->dtype == SPD_BF16 && c->hd == 128 && c->d % 128 == 0 && c->dff % 128 == 0;
+}
 
 // Products of the large-M step that take the activations as bf16 hi + lo pairs
 // (bit i: QKV, O, gate/up, down); the others take the bf16-rounded activations.
@@ -739,6 +793,8 @@ struct PdmPlan {
 // to 0.0157; the O projection's lo half moves no tensor by more than 0.0004.
 constexpr int PDM_BIG_LO = 0xD;
 static inline int big_k(int prod, int K) { return ((PDM_BIG_LO >> prod) & 1) ? 2 * K : K; }
+// With prepared weights exactly these products (QKV, gate/up, down) take [hi | lo8] rows.
+static_assert(PDM_BIG_LO == 0xD, "the lo8 form covers QKV, gate/up and down");
 
 // The decode-shaped products for M rows.  Grid targets measured at the 2560-wide
 // shape: about one block per CU for the products over the hidden size, two for the
@@ -816,6 +872,8 @@ static PdmPlan plan_pdm(const spd_config* c, int M, int64_t T_cap) {
   p.part_bytes = part;
   p.off_part = take(part);
   p.big = bf && M >= PDM_BIG_MIN_M && c->hd == 128;
+  p.big8 = false;
+  p.off_xlast = 0;
   if (p.big) {
     // activations enter as [hi | lo] rows; a product in PDM_BIG_LO runs over all 2K
     // columns, the others over the K hi columns only
@@ -833,8 +891,21 @@ static PdmPlan plan_pdm(const spd_config* c, int M, int64_t T_cap) {
     p.off_rs = take((size_t)M * 4);
     p.off_xa = take((size_t)M * 2 * c->d * 2);
     p.off_xb = take((size_t)M * 2 * p.ld1 * 2);
-    p.off_bpart = take(std::max(std::max(std::max(p.bqkv.part_bytes, p.bkv.part_bytes), p.bo.part_bytes),
-                                std::max(p.bgu.part_bytes, p.bdown.part_bytes)));
+    p.big8 = prep_supported(c);
+    if (p.big8) {
+      p.b8qkv = plan_big_lo8(M, nq, c->d);
+      p.b8kv = plan_big_lo8(M, 2 * c->Hkv * c->hd, c->d);
+      p.b8gu = plan_big_swiglu_lo8(M, c->dff, c->d);
+      p.b8down = plan_big_lo8(M, c->d, c->dff);
+      p.big8 = p.b8qkv.use && p.b8kv.use && p.b8gu.use && p.b8down.use;
+    }
+    size_t bp = std::max(std::max(std::max(p.bqkv.part_bytes, p.bkv.part_bytes), p.bo.part_bytes),
+                         std::max(p.bgu.part_bytes, p.bdown.part_bytes));
+    if (p.big8)
+      bp = std::max(bp, std::max(std::max(p.b8qkv.part_bytes, p.b8kv.part_bytes),
+                                 std::max(p.b8gu.part_bytes, p.b8down.part_bytes)));
+    p.off_bpart = take(bp);
+    p.off_xlast = take((size_t)2 * c->d * 2);
   }
   p.total = off;
   return p;
@@ -956,9 +1027,12 @@ static int last_layer_r0(const spd_config* c, const PdmPlan& p, int M, int n_out
 // row scales 1/rms(h).  The last layer runs its QKV product over every row (the
 // cache needs all keys and values) and the rest for the output row only, on the
 // decode-shaped kernels.
+// With prepared weights (prep, lo8) the QKV, gate/up and down products take their
+// inputs as [hi | lo8] rows and multiply the lo8 parts on the block-scaled fp8 MFMA.
+template <bool LO8>
 static int pdm_big(const spd_config* c, const spd_layer_weights* layers, const void* final_norm, void* k_cache,
                    void* v_cache, int64_t T_cap, const float* g, int pos0, int M, float* h_last, char* w,
-                   const PdmPlan& p, AttnArgs aa, hipStream_t st) {
+                   const PdmPlan& p, AttnArgs aa, const unsigned char* prep, hipStream_t st) {
   typedef bf16 WT;
   const int d = c->d, hd = c->hd, Hq = c->Hq, Hkv = c->Hkv, dff = c->dff;
   const int nq = (Hq + 2 * Hkv) * hd;
@@ -972,22 +1046,33 @@ static int pdm_big(const spd_config* c, const spd_layer_weights* layers, const v
   WT* xb = reinterpret_cast<WT*>(w + p.off_xb);  // [M][2 K]: O (K = Hq hd) and down (K = dff) input
   const int ko = Hq * hd;
   float2* rope = reinterpret_cast<float2*>(w + p.off_rope);
-  hipLaunchKernelGGL((big_rows_init_kernel<WT>), dim3(M), dim3(256), 0, st, g, h, rs, xa,
-                     static_cast<const WT*>(layers[0].attn_norm), rope, d, pos0, hd, c->rope_theta, c->rms_eps);
+  WT* xlast = reinterpret_cast<WT*>(w + p.off_xlast);  // [hi | lo] copy of row M - 1 (LO8)
+  const int lda = LO8 ? 3 * d / 2 : 2 * d;              // xa row stride (bf16 elements)
+  const int ldact = LO8 ? 3 * dff / 2 : 2 * dff;        // row stride of the SwiGLU output in xb
+  const PrepLayout PL = prep_layout(c);
+  hipLaunchKernelGGL((big_rows_init_kernel<WT, LO8>), dim3(M), dim3(256), 0, st, g, h, rs, xa,
+                     static_cast<const WT*>(layers[0].attn_norm), rope, d, pos0, hd, c->rope_theta, c->rms_eps,
+                     xlast, M);
   int rc = check_launch();
   if (rc) return rc;
   for (int l = 0; l < c->Ls; ++l) {
     const spd_layer_weights& lw = layers[l];
     WT* kc = static_cast<WT*>(k_cache) + (size_t)l * Hkv * T_cap * hd;
     WT* vc = static_cast<WT*>(v_cache) + (size_t)l * Hkv * hd * T_cap;
+    const unsigned char* pl = LO8 ? prep + (size_t)l * PL.layer_bytes : nullptr;
     if (l == c->Ls - 1) {
       // Last layer: every row's keys and values (the key/value columns of W_qkv on
       // the large-M GEMM), then the output row alone on the decode-shaped kernels:
       // its queries, attention, O and MLP (the other rows' outputs of this layer
       // feed nothing).
       const int nkv = 2 * Hkv * hd;
-      launch_big_gemm(p.bkv, xa, 2 * d, static_cast<const WT*>(lw.wqkv) + (size_t)Hq * hd * d, C, nkv, rs, M, nkv,
-                      big_k(0, d), bpart, ctr, st, d);
+      if constexpr (LO8)
+        launch_big_gemm_lo8(p.b8kv, xa, lda, static_cast<const WT*>(lw.wqkv) + (size_t)Hq * hd * d,
+                            pl + PL.qkv8 + (size_t)Hq * hd * d, pl + PL.qkv_s + (size_t)Hq * hd, C, nkv, rs, M,
+                            nkv, d, bpart, ctr, st);
+      else
+        launch_big_gemm(p.bkv, xa, 2 * d, static_cast<const WT*>(lw.wqkv) + (size_t)Hq * hd * d, C, nkv, rs, M,
+                        nkv, big_k(0, d), bpart, ctr, st, d);
       // C holds key heads then value heads: no query heads in front of the keys
       hipLaunchKernelGGL((qk_post_kernel<WT>), dim3(Hkv, M), dim3(64), 0, st, C, nkv, qb, kc,
                          static_cast<const WT*>(lw.q_norm), static_cast<const WT*>(lw.k_norm), rope, 0, pos0,
@@ -1001,7 +1086,7 @@ static int pdm_big(const spd_config* c, const spd_layer_weights* layers, const v
         const GemmPlan qp = plan_q_row(c);
         GemmShape gs = shape_of(qp, lw.wqkv, Hq * hd, d, 1, reinterpret_cast<float*>(w + p.off_part), ctr);
         gs.rs_inv = rs + r;
-        const WT* xr = xa + (size_t)r * 2 * d;
+        const WT* xr = LO8 ? xlast : xa + (size_t)r * 2 * d;
         InSplit<WT, RS_INV> in{xr, xr + d, 2 * d};
         EpiQKV<WT> epi{qb + (size_t)r * Hq * hd, kc, vc, static_cast<const WT*>(lw.q_norm),
                        static_cast<const WT*>(lw.k_norm), rope + (size_t)r * (hd / 2), Hq, Hkv, hd, pos0 + r,
@@ -1015,8 +1100,12 @@ static int pdm_big(const spd_config* c, const spd_layer_weights* layers, const v
       int P = 0;
       return layer_rows<WT>(c, p, lw, nullptr, final_norm, M, r, 1, h_last, w, aa, P, st);
     }
-    launch_big_gemm(p.bqkv, xa, 2 * d, static_cast<const WT*>(lw.wqkv), C, nq, rs, M, nq, big_k(0, d), bpart, ctr,
-                    st, d);
+    if constexpr (LO8)
+      launch_big_gemm_lo8(p.b8qkv, xa, lda, static_cast<const WT*>(lw.wqkv), pl + PL.qkv8, pl + PL.qkv_s, C, nq,
+                          rs, M, nq, d, bpart, ctr, st);
+    else
+      launch_big_gemm(p.bqkv, xa, 2 * d, static_cast<const WT*>(lw.wqkv), C, nq, rs, M, nq, big_k(0, d), bpart,
+                      ctr, st, d);
     hipLaunchKernelGGL((qk_post_kernel<WT>), dim3(Hq + Hkv, M), dim3(64), 0, st, C, nq, qb, kc,
                        static_cast<const WT*>(lw.q_norm), static_cast<const WT*>(lw.k_norm), rope, Hq, pos0,
                        T_cap, c->rms_eps);
@@ -1045,14 +1134,21 @@ static int pdm_big(const spd_config* c, const spd_layer_weights* layers, const v
     }
     launch_big_gemm(p.bo, xb, 2 * ko, static_cast<const WT*>(lw.wo), C, d, nullptr, M, d, big_k(1, ko), bpart, ctr,
                     st, ko);
-    hipLaunchKernelGGL((resid_post_kernel<WT>), dim3(M), dim3(256), 0, st, C, d, h, rs, xa,
-                       static_cast<const WT*>(lw.mlp_norm), d, c->rms_eps);
-    launch_big_swiglu(p.bgu, xa, 2 * d, static_cast<const WT*>(lw.w_gate_up), xb, 2 * dff, dff, rs, M,
-                      big_k(2, d), bpart, ctr, st, d);
-    launch_big_gemm(p.bdown, xb, 2 * dff, static_cast<const WT*>(lw.w_down), C, d, nullptr, M, d, big_k(3, dff),
-                    bpart, ctr, st, dff);
-    hipLaunchKernelGGL((resid_post_kernel<WT>), dim3(M), dim3(256), 0, st, C, d, h, rs, xa,
-                       static_cast<const WT*>(layers[l + 1].attn_norm), d, c->rms_eps);
+    hipLaunchKernelGGL((resid_post_kernel<WT, LO8>), dim3(M), dim3(256), 0, st, C, d, h, rs, xa,
+                       static_cast<const WT*>(lw.mlp_norm), d, c->rms_eps, xlast, M);
+    if constexpr (LO8) {
+      launch_big_swiglu_lo8(p.b8gu, xa, lda, static_cast<const WT*>(lw.w_gate_up), pl + PL.gu8, pl + PL.gu_s, xb,
+                            ldact, dff, rs, M, d, bpart, ctr, st);
+      launch_big_gemm_lo8(p.b8down, xb, ldact, static_cast<const WT*>(lw.w_down), pl + PL.dn8, pl + PL.dn_s, C, d,
+                          nullptr, M, d, dff, bpart, ctr, st);
+    } else {
+      launch_big_swiglu(p.bgu, xa, 2 * d, static_cast<const WT*>(lw.w_gate_up), xb, 2 * dff, dff, rs, M,
+                        big_k(2, d), bpart, ctr, st, d);
+      launch_big_gemm(p.bdown, xb, 2 * dff, static_cast<const WT*>(lw.w_down), C, d, nullptr, M, d, big_k(3, dff),
+                      bpart, ctr, st, dff);
+    }
+    hipLaunchKernelGGL((resid_post_kernel<WT, LO8>), dim3(M), dim3(256), 0, st, C, d, h, rs, xa,
+                       static_cast<const WT*>(layers[l + 1].attn_norm), d, c->rms_eps, xlast, M);
     rc = check_launch();
     if (rc) return rc;
   }
@@ -1062,7 +1158,8 @@ static int pdm_big(const spd_config* c, const spd_layer_weights* layers, const v
 template <typename WT>
 static int pdm_impl(const spd_config* c, const spd_layer_weights* layers, const void* final_norm,
                     void* k_cache, void* v_cache, int64_t T_cap, const float* g, int pos0, int M,
-                    const uint64_t* anc, int n_out, float* h_last, void* ws, hipStream_t st) {
+                    const uint64_t* anc, int n_out, float* h_last, void* ws, const void* prep,
+                    hipStream_t st) {
   const PdmPlan p = plan_pdm(c, M, T_cap);
   char* w = static_cast<char*>(ws);
   float* h = reinterpret_cast<float*>(w + p.off_h);
@@ -1099,7 +1196,13 @@ static int pdm_impl(const spd_config* c, const spd_layer_weights* layers, const 
   aa.r0 = 0;
 
   if constexpr (sizeof(WT) == 2) {
-    if (p.big && !anc) return pdm_big(c, layers, final_norm, k_cache, v_cache, T_cap, g, pos0, M, h_last, w, p, aa, st);
+    if (p.big && !anc) {
+      if (prep && p.big8)
+        return pdm_big<true>(c, layers, final_norm, k_cache, v_cache, T_cap, g, pos0, M, h_last, w, p, aa,
+                             static_cast<const unsigned char*>(prep), st);
+      return pdm_big<false>(c, layers, final_norm, k_cache, v_cache, T_cap, g, pos0, M, h_last, w, p, aa, nullptr,
+                            st);
+    }
   }
   hipLaunchKernelGGL((rows_init_kernel<WT>), dim3(d / 64, M), dim3(64), 0, st, g, h, ss, M, d, x0,
                      static_cast<const WT*>(layers[0].attn_norm), rope, pos0, hd, c->rope_theta, anc);
@@ -1138,7 +1241,7 @@ using namespace spd;
 static int pdm_entry(const spd_config* cfg, const spd_layer_weights* layers, const void* final_norm,
                      void* k_cache, void* v_cache, int64_t T_cap, const float* g, int32_t pos0,
                      int32_t M, const uint64_t* anc, int32_t n_out, float* h_last, void* ws,
-                     size_t ws_bytes, void* stream) {
+                     size_t ws_bytes, void* stream, const void* prep = nullptr) {
   int rc = check_config(cfg);
   if (rc) return rc;
   if (!layers || !final_norm || !k_cache || !v_cache || !g || !h_last || !ws) return SPD_E_INVALID;
@@ -1170,11 +1273,12 @@ static int pdm_entry(const spd_config* cfg, const spd_layer_weights* layers, con
     return SPD_E_INVALID;
   if (ws_bytes < pdm_workspace(cfg, M, T_cap)) return SPD_E_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (prep && (!prep_supported(cfg) || !aligned16(prep))) return SPD_E_INVALID;
   if (cfg->dtype == SPD_BF16)
     return pdm_impl<bf16>(cfg, layers, final_norm, k_cache, v_cache, T_cap, g, pos0, M, anc, n_out,
-                          h_last, ws, st);
+                          h_last, ws, prep, st);
   return pdm_impl<float>(cfg, layers, final_norm, k_cache, v_cache, T_cap, g, pos0, M, anc, n_out,
-                         h_last, ws, st);
+                         h_last, ws, nullptr, st);
 }
 
 extern "C" int spd_pdm_step(const spd_config* cfg, const spd_layer_weights* layers,
@@ -1194,4 +1298,98 @@ extern "C" int spd_pdm_step_tree(const spd_config* cfg, const spd_layer_weights*
     return SPD_E_INVALID;
   return pdm_entry(cfg, layers, final_norm, k_cache, v_cache, T_cap, g, pos0, M, anc, n_out, h_out,
                    ws, ws_bytes, stream);
+}
+
+// e4m3 copy of weight rows with a per-row power-of-two factor: row n's largest
+// magnitude m = f 2^E (0.5 <= f < 1) becomes f 2^8 in [128, 256) by 2^e, e = 8 - E
+// (e = 0 for a row of zeros); s8[n] = 127 - e is the E8M0 scale that undoes the
+// factor in the block-scaled MFMA.  Rows with non-finite values keep them (NaN).
+__global__ __launch_bounds__(256) void fp8_rows_kernel(const bf16* W, int K, unsigned char* W8, unsigned char* s8) {
+  const int n = blockIdx.x;
+  const bf16* row = W + (size_t)n * K;
+  float m = 0.f;
+  for (int k = 8 * threadIdx.x; k < K; k += 8 * 256) {
+    const uint4 v = *reinterpret_cast<const uint4*>(row + k);
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      m = fmaxf(m, fmaxf(fabsf(__uint_as_float(u[i] << 16)), fabsf(__uint_as_float(u[i] & 0xffff0000u))));
+  }
+  __shared__ float s_m[4];
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) s_m[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+  int e = 0;
+  if (m > 0.f && m <= 3.402823466e38f) {
+    int E;
+    frexpf(m, &E);
+    e = 8 - E;
+  }
+  if (threadIdx.x == 0) s8[n] = (unsigned char)(127 - e);
+  for (int k = 8 * threadIdx.x; k < K; k += 8 * 256) {
+    const uint4 v = *reinterpret_cast<const uint4*>(row + k);
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float a0 = ldexpf(__uint_as_float(u[2 * i] << 16), e), a1 = ldexpf(__uint_as_float(u[2 * i] & 0xffff0000u), e);
+      const float a2 = ldexpf(__uint_as_float(u[2 * i + 1] << 16), e),
+                  a3 = ldexpf(__uint_as_float(u[2 * i + 1] & 0xffff0000u), e);
+      int x = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+      x = __builtin_amdgcn_cvt_pk_fp8_f32(a2, a3, x, true);
+      o[i] = (uint32_t)x;
+    }
+    *reinterpret_cast<uint2*>(W8 + (size_t)n * K + k) = make_uint2(o[0], o[1]);
+  }
+}
+
+extern "C" size_t spd_pdm_prepared_bytes(const spd_config* cfg) {
+  if (check_config(cfg) || cfg->Ls < 1 || cfg->Hq < 1 || cfg->Hkv < 1 || !prep_supported(cfg)) return 0;
+  return prep_layout(cfg).total;
+}
+
+extern "C" int spd_pdm_prepare(const spd_config* cfg, const spd_layer_weights* layers, void* prep,
+                               size_t prep_bytes, void* stream) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!layers || !prep) return SPD_E_INVALID;
+  if (cfg->Ls < 1 || cfg->Hq < 1 || cfg->Hkv < 1 || cfg->hd < 1 || cfg->dff < 1) return SPD_E_INVALID;
+  if (!prep_supported(cfg)) return SPD_E_UNSUPPORTED;
+  if (!aligned16(prep)) return SPD_E_INVALID;
+  const PrepLayout L = prep_layout(cfg);
+  if (prep_bytes < L.total) return SPD_E_WORKSPACE;
+  for (int l = 0; l < cfg->Ls; ++l)
+    if (!layers[l].wqkv || !layers[l].w_gate_up || !layers[l].w_down || !aligned16(layers[l].wqkv) ||
+        !aligned16(layers[l].w_gate_up) || !aligned16(layers[l].w_down))
+      return SPD_E_INVALID;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int d = cfg->d, dff = cfg->dff, nq = (cfg->Hq + 2 * cfg->Hkv) * cfg->hd;
+  for (int l = 0; l < cfg->Ls; ++l) {
+    unsigned char* base = static_cast<unsigned char*>(prep) + (size_t)l * L.layer_bytes;
+    hipLaunchKernelGGL(fp8_rows_kernel, dim3(nq), dim3(256), 0, st, static_cast<const bf16*>(layers[l].wqkv), d,
+                       base + L.qkv8, base + L.qkv_s);
+    hipLaunchKernelGGL(fp8_rows_kernel, dim3(2 * dff), dim3(256), 0, st,
+                       static_cast<const bf16*>(layers[l].w_gate_up), d, base + L.gu8, base + L.gu_s);
+    hipLaunchKernelGGL(fp8_rows_kernel, dim3(d), dim3(256), 0, st, static_cast<const bf16*>(layers[l].w_down), dff,
+                       base + L.dn8, base + L.dn_s);
+    rc = check_launch();
+    if (rc) return rc;
+  }
+  return SPD_OK;
+}
+
+extern "C" int spd_pdm_step_prepared(const spd_config* cfg, const spd_layer_weights* layers, const void* prep,
+                                     size_t prep_bytes, const void* final_norm, void* k_cache, void* v_cache,
+                                     int64_t T_cap, const float* g, int32_t pos0, int32_t M, float* h_last,
+                                     void* ws, size_t ws_bytes, void* stream) {
+  if (prep) {
+    const int rc = check_config(cfg);
+    if (rc) return rc;
+    if (cfg->Ls < 1 || cfg->Hq < 1 || cfg->Hkv < 1 || cfg->hd < 1 || cfg->dff < 1) return SPD_E_INVALID;
+    if (!prep_supported(cfg)) return SPD_E_INVALID;
+    if (prep_bytes < prep_layout(cfg).total) return SPD_E_WORKSPACE;
+  }
+  return pdm_entry(cfg, layers, final_norm, k_cache, v_cache, T_cap, g, pos0, M, nullptr, 1, h_last, ws,
+                   ws_bytes, stream, prep);
 }

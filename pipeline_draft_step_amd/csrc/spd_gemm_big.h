@@ -62,7 +62,31 @@ struct BigGemm {
   // [hi | lo] bf16 rows of act (row stride act_ld) instead of C
   bf16* act;
   int act_ld, half;
+  // [hi | lo8] activation rows (LO8 kernels): A's row holds kb bf16 hi parts, then at
+  // byte 2 kb the kb bytes lo8 = e4m3(256 (x - hi)).  Each 128 columns take two bf16
+  // stages (hi parts times B) and one fp8 stage (the same 128 bytes per tile row: lo8
+  // times B8 = e4m3(W_n 2^e_n), [N][kb] bytes) on the block-scaled fp8 MFMA, whose
+  // scales (2^-8 for A, b8s[n] = 127 - e_n for row n of B, E8M0) undo both factors
+  // exactly.
+  const unsigned char* B8;
+  const unsigned char* b8s;
 };
+
+// E8M0 scale of the lo8 operand: 2^(119 - 127) undoes its factor 256
+constexpr int BG_LO8_ASCALE = 119;
+
+// lo8 parts: e4m3 (round to nearest even) of 256 r, saturated to +-448; |r| is at
+// most 2^-8 |x| for the residual r = x - bf16(x), so only |x| > 448 saturates.
+__device__ __forceinline__ float lo8_arg(float r) { return fminf(fmaxf(256.f * r, -448.f), 448.f); }
+__device__ __forceinline__ uint32_t lo8_byte(float r) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(lo8_arg(r), 0.f, 0, false) & 0xffu;
+}
+// four residuals as four bytes, r0 lowest
+__device__ __forceinline__ uint32_t lo8_word(float r0, float r1, float r2, float r3) {
+  int v = __builtin_amdgcn_cvt_pk_fp8_f32(lo8_arg(r0), lo8_arg(r1), 0, false);
+  v = __builtin_amdgcn_cvt_pk_fp8_f32(lo8_arg(r2), lo8_arg(r3), v, true);
+  return (uint32_t)v;
+}
 
 enum { BG_EPI_PLAIN = 0, BG_EPI_RSQ = 1, BG_EPI_SWIGLU = 2 };
 
@@ -76,6 +100,18 @@ __device__ __forceinline__ int bg_swz(int r) { return r & 7; }
 // `base`: 1 KB groups (8 tile rows) v, v + 8, ...; the 52 groups do not split
 // evenly, so waves 4 .. 7 repeat one of their own groups (same bytes to the
 // same place) instead of taking a branch.
+// B row of tile row r (0 .. 159) of the block whose first column is n0
+template <bool GU>
+__device__ __forceinline__ int bg_brow(const BigGemm& g, int n0, int r) {
+  if constexpr (GU) {
+    // rows 0..79: gate rows n0 .., rows 80..159: the matching up rows
+    const int rr = r < 80 ? r : r - 80;
+    return min(n0 + rr, g.half - 1) + (r < 80 ? 0 : g.half);
+  } else {
+    return min(n0 + r, g.N - 1);
+  }
+}
+
 template <bool GU>
 __device__ __forceinline__ void bg_issue(const BigGemm& g, unsigned char* base, int st, int m0, int n0,
                                          int v, int lane) {
@@ -89,16 +125,54 @@ __device__ __forceinline__ void bg_issue(const BigGemm& g, unsigned char* base, 
     const bool isA = q < BG_A_GROUPS;
     const int r = 8 * (isA ? q : q - BG_A_GROUPS) + rin;  // tile row
     const int c = pc ^ bg_swz(r);
-    int brow;
-    if constexpr (GU) {
-      // rows 0..79: gate rows n0 .., rows 80..159: the matching up rows
-      const int rr = r < 80 ? r : r - 80;
-      brow = min(n0 + rr, g.half - 1) + (r < 80 ? 0 : g.half);
-    } else {
-      brow = min(n0 + r, g.N - 1);
-    }
+    const int brow = bg_brow<GU>(g, n0, r);
     const bf16* src = isA ? g.A + (size_t)min(m0 + r, g.M - 1) * g.lda + k0 : g.B + (size_t)brow * g.ldb + kB;
     __builtin_amdgcn_global_load_lds((const void*)(src + 8 * c), (lds_ptr_t)(base + q * 1024), 16, 0, 0);
+  }
+}
+
+// The same loads for the [hi | lo8] kernels, from 32-bit byte offsets (the host keeps
+// every operand below 4 GB).  Per load only its row's offset unit is kept: A row m at
+// m (2 lda) bytes, B row n at n kb (fp8) or 2 n kb (bf16) bytes; a stage adds a
+// uniform column offset.  The lane's 16-byte chunk (pc ^ (row & 7)) is the same for
+// all of its loads (every group starts at a multiple of 8 rows).
+struct BgLo8Rows {
+  uint32_t unit[BG_LOADS];
+  uint32_t c16;
+};
+template <bool GU>
+__device__ __forceinline__ BgLo8Rows bg_lo8_rows(const BigGemm& g, int m0, int n0, int v, int lane) {
+  BgLo8Rows R;
+  const int rin = lane >> 3, pc = lane & 7;
+  R.c16 = 16u * (uint32_t)(pc ^ rin);
+#pragma unroll
+  for (int i = 0; i < BG_LOADS; ++i) {
+    int q = v + BG_WAVES * i;
+    if (i == BG_LOADS - 1) q = q < BG_GROUPS ? q : v;
+    const bool isA = q < BG_A_GROUPS;
+    const int r = 8 * (isA ? q : q - BG_A_GROUPS) + rin;
+    R.unit[i] = isA ? (uint32_t)min(m0 + r, g.M - 1) * (uint32_t)(2 * g.lda) : (uint32_t)bg_brow<GU>(g, n0, r) * (uint32_t)g.kb;
+  }
+  return R;
+}
+// Stage st of a [hi | lo8] product: round t = st / 3 covers columns 128 t .. 128 t + 127
+// as two bf16 stages (st % 3 = 0, 1: the hi parts times B) and one fp8 stage
+// (st % 3 = 2: the lo8 bytes times B8), so the kinds follow the three ring slots.
+__device__ __forceinline__ void bg_issue_lo8(const BigGemm& g, const BgLo8Rows& R, unsigned char* base, int st,
+                                             int v) {
+  const int t = st / 3, k = st - 3 * t;
+  const bool f8 = k == 2;
+  const uint32_t aoff = f8 ? (uint32_t)(2 * g.kb + 128 * t) : (uint32_t)(256 * t + 128 * k);
+  const uint32_t boff = f8 ? (uint32_t)(128 * t) : (uint32_t)(256 * t + 128 * k);
+  const unsigned char* bbase = f8 ? g.B8 : reinterpret_cast<const unsigned char*>(g.B);
+#pragma unroll
+  for (int i = 0; i < BG_LOADS; ++i) {
+    int q = v + BG_WAVES * i;
+    if (i == BG_LOADS - 1) q = q < BG_GROUPS ? q : v;
+    const bool isA = q < BG_A_GROUPS;
+    const unsigned char* src = isA ? reinterpret_cast<const unsigned char*>(g.A) + (R.unit[i] + aoff + R.c16)
+                                   : bbase + ((R.unit[i] << (f8 ? 0 : 1)) + boff + R.c16);
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr_t)(base + q * 1024), 16, 0, 0);
   }
 }
 
@@ -151,32 +225,103 @@ __device__ __forceinline__ void bg_compute(const unsigned char* sa, BgAccT (&acc
   }
 }
 
+// The MFMAs of one fp8 stage (128 columns) for wave (wm, wn): 16x16x128 block-scaled
+// e4m3 MFMA, lane l supplying row l % 16 and columns 32 (l / 16) .. +31 (16-byte
+// chunks 2 (l / 16) and 2 (l / 16) + 1 of the tile row) of both operands; byte j % 4
+// of bs[j / 4] is the E8M0 scale of the B row this lane supplies to fragment j.
+typedef int bg_i32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ void bg_compute_f8(const unsigned char* sa, BgAccT (&acc)[BG_FRAGS], const int (&bs)[2],
+                                              int wm, int wn, int lane) {
+  const unsigned char* sb = sa + BG_A_BYTES;
+  const int lr = lane & 15, lq = lane >> 4;
+  auto frag8 = [&](const unsigned char* t, int r) {
+    const u32x4 x0 = *reinterpret_cast<const u32x4*>(t + r * BG_ROW + 16 * ((2 * lq) ^ bg_swz(r)));
+    const u32x4 x1 = *reinterpret_cast<const u32x4*>(t + r * BG_ROW + 16 * ((2 * lq + 1) ^ bg_swz(r)));
+    return bg_i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+  };
+  // the five B fragments stay in registers; the A fragments are read one at a time
+  // (all nine at once would not fit two waves' registers beside the accumulators)
+  bg_i32x8 bfr[5];
+#pragma unroll
+  for (int j = 0; j < 5; ++j) bfr[j] = frag8(sb, wn * 80 + j * 16 + lr);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bg_i32x8 af = frag8(sa, wm * 64 + i * 16 + lr);
+    acc[i * 5 + 0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bfr[0], acc[i * 5 + 0], 0, 0, 0,
+                                                                      BG_LO8_ASCALE, 0, bs[0]);
+    acc[i * 5 + 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bfr[1], acc[i * 5 + 1], 0, 0, 0,
+                                                                      BG_LO8_ASCALE, 1, bs[0]);
+    acc[i * 5 + 2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bfr[2], acc[i * 5 + 2], 0, 0, 0,
+                                                                      BG_LO8_ASCALE, 2, bs[0]);
+    acc[i * 5 + 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bfr[3], acc[i * 5 + 3], 0, 0, 0,
+                                                                      BG_LO8_ASCALE, 3, bs[0]);
+    acc[i * 5 + 4] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bfr[4], acc[i * 5 + 4], 0, 0, 0,
+                                                                      BG_LO8_ASCALE, 0, bs[1]);
+  }
+}
+
+#define BG_ISSUE(slot, st)                        \
+  do {                                            \
+    if constexpr (LO8)                            \
+      bg_issue_lo8(g, lrows, slot, st, wave);     \
+    else                                          \
+      bg_issue<GU>(g, slot, st, m0, n0, wave, lane); \
+  } while (0)
+
 // One K stage held in ring slot `cur`; `nxt` (the slot of stage s - 1, free
 // once every wave has passed the barrier) receives stage s + 2.  The loads are
 // unconditional (past the end they re-read the last stage into the free slot),
 // so the whole step is one scheduling region and the wait counts never change;
 // the group barriers spread the wave's loads through its MFMAs.
-#define BG_STEP(cur, nxt)                                                           \
-  do {                                                                              \
-    bg_wait_vm<BG_LOADS>();                                                         \
-    __builtin_amdgcn_s_barrier();                                                   \
-    bg_issue<GU>(g, nxt, kbeg + min(s + BG_SLOTS - 1, ns - 1), m0, n0, wave, lane); \
-    bg_compute<RSQ>(cur, acc, sq, wm, wn, lane);                                    \
-    _Pragma("unroll") for (int r_ = 0; r_ < BG_LOADS - 1; ++r_) {                   \
-      __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);                            \
-      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                            \
-    }                                                                               \
-    __builtin_amdgcn_sched_group_barrier(0x008, MF - 6 * (BG_LOADS - 1), 0);       \
-    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                              \
-    ++s;                                                                            \
+#define BG_STEP_BF16(cur, nxt)                                                           \
+  do {                                                                                   \
+    bg_wait_vm<BG_LOADS>();                                                              \
+    __builtin_amdgcn_s_barrier();                                                        \
+    BG_ISSUE(nxt, kbeg + min(s + BG_SLOTS - 1, ns - 1));                                 \
+    bg_compute<RSQ>(cur, acc, sq, wm, wn, lane);                                         \
+    _Pragma("unroll") for (int r_ = 0; r_ < BG_LOADS - 1; ++r_) {                        \
+      __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);                                 \
+      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                                 \
+    }                                                                                    \
+    __builtin_amdgcn_sched_group_barrier(0x008, MF - 6 * (BG_LOADS - 1), 0);            \
+    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                                   \
+    ++s;                                                                                 \
+  } while (0)
+// an fp8 stage: 20 MFMAs of twice the length, a load after every third
+#define BG_STEP_F8(cur, nxt)                                                             \
+  do {                                                                                   \
+    bg_wait_vm<BG_LOADS>();                                                              \
+    __builtin_amdgcn_s_barrier();                                                        \
+    BG_ISSUE(nxt, kbeg + min(s + BG_SLOTS - 1, ns - 1));                                 \
+    bg_compute_f8(cur, acc, bs, wm, wn, lane);                                           \
+    _Pragma("unroll") for (int r_ = 0; r_ < BG_LOADS - 1; ++r_) {                        \
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);                                 \
+      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                                 \
+    }                                                                                    \
+    __builtin_amdgcn_sched_group_barrier(0x008, 20 - 3 * (BG_LOADS - 1), 0);            \
+    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);                                   \
+    ++s;                                                                                 \
+  } while (0)
+// Steps s .. e - 1 of one kind, the ring slot of step s being slot (s mod 3) and the
+// current phase P = s mod 3 known: whole rounds of three, then up to two steps.
+#define BG_RUN(STEP, e, a, b, c) \
+  do {                           \
+    while (s + 3 <= (e)) {       \
+      STEP(a, c);                \
+      STEP(b, a);                \
+      STEP(c, b);                \
+    }                            \
+    if (s < (e)) STEP(a, c);     \
+    if (s < (e)) STEP(b, a);     \
   } while (0)
 
 // internal linkage: every translation unit that launches it holds its own copy.
 // EPI: BG_EPI_PLAIN writes rs[m] * (A B^T); BG_EPI_RSQ takes the row scale from A
 // itself (rs_k, rs_eps) instead of g.rs; BG_EPI_SWIGLU writes silu(gate) * up.
-template <int EPI>
+template <int EPI, bool LO8 = false>
 static __global__ __launch_bounds__(BG_THREADS) void gemm_big_kernel(BigGemm g) {
   constexpr bool RSQ = EPI == BG_EPI_RSQ, GU = EPI == BG_EPI_SWIGLU;
+  static_assert(!(RSQ && LO8), "the row-statistics form takes plain bf16 rows");
   constexpr int MF = BG_MFMAS + (RSQ ? 4 : 0);  // MFMAs per wave and stage
   // one array per ring slot: separate objects let the compiler tell the
   // direct-to-LDS writes of later stages from the reads of the current one
@@ -199,8 +344,17 @@ static __global__ __launch_bounds__(BG_THREADS) void gemm_big_kernel(BigGemm g) 
   const int m0 = mt * BG_BM, n0 = nt * (GU ? BG_BN / 2 : BG_BN);
   const int ns = g.kstages, kbeg = kh * ns;  // the host guarantees ns >= BG_SLOTS
 
-  bg_issue<GU>(g, s0, kbeg, m0, n0, wave, lane);
-  bg_issue<GU>(g, s1, kbeg + 1, m0, n0, wave, lane);
+  // E8M0 scales of the B rows this lane supplies to its fp8 fragments
+  int bs[2] = {0, 0};
+  if constexpr (LO8) {
+#pragma unroll
+    for (int j = 0; j < 5; ++j)
+      bs[j / 4] |= (int)g.b8s[bg_brow<GU>(g, n0, wn * 80 + j * 16 + (lane & 15))] << (8 * (j % 4));
+  }
+  BgLo8Rows lrows{};
+  if constexpr (LO8) lrows = bg_lo8_rows<GU>(g, m0, n0, wave, lane);
+  BG_ISSUE(s0, kbeg);
+  BG_ISSUE(s1, kbeg + 1);
 
   BgAccT acc[BG_FRAGS];
 #pragma unroll
@@ -208,13 +362,17 @@ static __global__ __launch_bounds__(BG_THREADS) void gemm_big_kernel(BigGemm g) 
   BgAccT sq[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 
   int s = 0;
-  while (s + BG_SLOTS <= ns) {
-    BG_STEP(s0, s2);
-    BG_STEP(s1, s0);
-    BG_STEP(s2, s1);
+  if constexpr (LO8) {
+    // whole rounds (the host makes ns a multiple of 3): slots s0, s1 hold the bf16
+    // stages of a round, s2 its fp8 stage
+    while (s + 3 <= ns) {
+      BG_STEP_BF16(s0, s2);
+      BG_STEP_BF16(s1, s0);
+      BG_STEP_F8(s2, s1);
+    }
+  } else {
+    BG_RUN(BG_STEP_BF16, ns, s0, s1, s2);
   }
-  if (s < ns) BG_STEP(s0, s2);
-  if (s < ns) BG_STEP(s1, s0);
   // the surplus loads of the last steps must land before the block's LDS is released
   bg_wait_vm<0>();
 
@@ -312,13 +470,26 @@ static __global__ __launch_bounds__(BG_THREADS) void gemm_big_kernel(BigGemm g) 
             const float gt = acc[i * 5 + j][e] * rsv[i][e];
             const float up = xch[((i * 5 + j) * 4 + e) * 64 + lane];
             const float a = gt / (1.0f + expf(-gt)) * up;
-            const bf16 hi = f2bf(a), lo = f2bf(a - bf2f(hi));
-            const uint32_t hl = (uint32_t)hi | ((uint32_t)lo << 16);
-            const uint32_t nb = (uint32_t)__shfl_xor((int)hl, 1, 64);
-            if ((lr & 1) == 0 && row < g.M && col < g.half) {
-              bf16* out = g.act + (size_t)row * g.act_ld + col;
-              *reinterpret_cast<uint32_t*>(out) = (hl & 0xffffu) | (nb << 16);
-              *reinterpret_cast<uint32_t*>(out + g.half) = (hl >> 16) | (nb & 0xffff0000u);
+            const bf16 hi = f2bf(a);
+            if constexpr (LO8) {
+              // [hi | lo8] rows: hi pairs at act + row act_ld + col, lo8 pairs at byte 2 half + col
+              const uint32_t hl = (uint32_t)hi | (lo8_byte(a - bf2f(hi)) << 16);
+              const uint32_t nb = (uint32_t)__shfl_xor((int)hl, 1, 64);
+              if ((lr & 1) == 0 && row < g.M && col < g.half) {
+                bf16* out = g.act + (size_t)row * g.act_ld;
+                *reinterpret_cast<uint32_t*>(out + col) = (hl & 0xffffu) | (nb << 16);
+                *reinterpret_cast<uint16_t*>(reinterpret_cast<unsigned char*>(out + g.half) + col) =
+                    (uint16_t)((hl >> 16) | ((nb >> 8) & 0xff00u));
+              }
+            } else {
+              const bf16 lo = f2bf(a - bf2f(hi));
+              const uint32_t hl = (uint32_t)hi | ((uint32_t)lo << 16);
+              const uint32_t nb = (uint32_t)__shfl_xor((int)hl, 1, 64);
+              if ((lr & 1) == 0 && row < g.M && col < g.half) {
+                bf16* out = g.act + (size_t)row * g.act_ld + col;
+                *reinterpret_cast<uint32_t*>(out) = (hl & 0xffffu) | (nb << 16);
+                *reinterpret_cast<uint32_t*>(out + g.half) = (hl >> 16) | (nb & 0xffff0000u);
+              }
             }
           }
         }
@@ -353,7 +524,10 @@ static __global__ __launch_bounds__(BG_THREADS) void gemm_big_kernel(BigGemm g) 
   }
 }
 
-#undef BG_STEP
+#undef BG_RUN
+#undef BG_ISSUE
+#undef BG_STEP_BF16
+#undef BG_STEP_F8
 
 // ---------------------------------------------------------------------------
 // Host-side planning: KS splits K so that the tiles times KS fill the GPU
@@ -384,6 +558,33 @@ inline BigPlan plan_big_gemm(int M, int N, int K) {
   b.sq_bytes = b.KS > 1 ? (size_t)b.mtiles * b.ntiles * b.KS * BG_BM * 4 : 0;
   b.use = true;
   return b;
+}
+
+// The [hi | lo8] form of a product over kb columns: kb / 64 bf16 stages and kb / 128
+// fp8 stages (kb % 128 == 0), planned as one run of equal stages.
+// (the kernel addresses its operands with 32-bit byte offsets: A's M rows of 3 kb bytes
+// and B's N rows of 2 kb bytes stay below 4 GB)
+inline bool lo8_fits(int M, int N, int kb) {
+  return kb % 128 == 0 && (uint64_t)M * 3 * kb < (1ull << 32) && (uint64_t)N * 2 * kb < (1ull << 32);
+}
+// K parts of whole rounds (three stages: 128 columns of hi and of lo8)
+inline BigPlan plan_lo8_rounds(int M, int N, int kb) {
+  BigPlan b{};
+  if (!lo8_fits(M, N, kb) || M < 1 || N < 1) return b;
+  b.mtiles = (M + BG_BM - 1) / BG_BM;
+  b.ntiles = (N + BG_BN - 1) / BG_BN;
+  const int rounds = kb / 128;
+  b.KS = 1;
+  while (b.KS < BG_MAX_KS && b.mtiles * b.ntiles * b.KS * 2 <= BG_TARGET_BLOCKS && rounds % (b.KS * 2) == 0)
+    b.KS *= 2;
+  b.kstages = 3 * (rounds / b.KS);
+  b.part_bytes = b.KS > 1 ? (size_t)b.mtiles * b.ntiles * b.KS * BG_PART_FLOATS * 4 : 0;
+  b.use = true;
+  return b;
+}
+inline BigPlan plan_big_lo8(int M, int N, int kb) { return plan_lo8_rounds(M, N, kb); }
+inline BigPlan plan_big_swiglu_lo8(int M, int half, int kb) {
+  return plan_lo8_rounds(M, BG_BN * ((half + BG_BN / 2 - 1) / (BG_BN / 2)), kb);
 }
 
 // C[M][ldc] = rs[m] * (A[M][lda] . B[N][kb]^T) over K columns of A; K = kb, or
@@ -423,6 +624,37 @@ inline void launch_big_gemm(const BigPlan& p, const bf16* A, int lda, const bf16
                        g);
 }
 
+// The same product with A's rows in the [hi | lo8] form (lda in bf16 elements, at
+// least 3 kb / 2): the hi parts times B plus the lo8 parts times B8 (e4m3 rows of B
+// scaled by 2^e_n, b8s[n] = 127 - e_n).  Plan: plan_big_lo8.
+inline void launch_big_gemm_lo8(const BigPlan& p, const bf16* A, int lda, const bf16* B,
+                                const unsigned char* B8, const unsigned char* b8s, float* C, int ldc,
+                                const float* rs, int M, int N, int kb, float* part, unsigned* counters,
+                                hipStream_t st) {
+  BigGemm g{};
+  g.A = A;
+  g.B = B;
+  g.B8 = B8;
+  g.b8s = b8s;
+  g.C = C;
+  g.rs = rs;
+  g.part = part;
+  g.counters = counters;
+  g.M = M;
+  g.N = N;
+  g.K = kb + kb / 2;
+  g.lda = lda;
+  g.kb = kb;
+  g.ldb = kb;
+  g.ldc = ldc;
+  g.mtiles = p.mtiles;
+  g.ntiles = p.ntiles;
+  g.KS = p.KS;
+  g.kstages = p.kstages;
+  hipLaunchKernelGGL((gemm_big_kernel<BG_EPI_PLAIN, true>), dim3(p.mtiles * p.ntiles * p.KS), dim3(BG_THREADS), 0,
+                     st, g);
+}
+
 // Gate/up product with the SwiGLU epilogue: W = [gate; up] ([2 half][kb] bf16), A as in
 // launch_big_gemm; act[m][j] = silu(g_j) * u_j with g, u = rs[m] * (A W^T), written as
 // bf16 hi at act + m act_ld + j and lo at + half.  Plan: plan_big_swiglu.
@@ -453,6 +685,39 @@ inline void launch_big_swiglu(const BigPlan& p, const bf16* A, int lda, const bf
   g.half = half;
   hipLaunchKernelGGL(gemm_big_kernel<BG_EPI_SWIGLU>, dim3(p.mtiles * p.ntiles * p.KS), dim3(BG_THREADS), 0, st,
                      g);
+}
+
+// The gate/up product with A in the [hi | lo8] form (as launch_big_gemm_lo8, B8 and
+// b8s over the 2 half rows of W) writing act as [hi | lo8] rows: hi at act + m act_ld + j,
+// lo8 at byte 2 half + j of the row (act_ld >= 3 half / 2, half % 4 == 0).
+// Plan: plan_big_swiglu_lo8.
+inline void launch_big_swiglu_lo8(const BigPlan& p, const bf16* A, int lda, const bf16* W,
+                                  const unsigned char* W8, const unsigned char* w8s, bf16* act, int act_ld,
+                                  int half, const float* rs, int M, int kb, float* part, unsigned* counters,
+                                  hipStream_t st) {
+  BigGemm g{};
+  g.A = A;
+  g.B = W;
+  g.B8 = W8;
+  g.b8s = w8s;
+  g.rs = rs;
+  g.part = part;
+  g.counters = counters;
+  g.M = M;
+  g.N = 2 * half;
+  g.K = kb + kb / 2;
+  g.lda = lda;
+  g.kb = kb;
+  g.ldb = kb;
+  g.mtiles = p.mtiles;
+  g.ntiles = p.ntiles;
+  g.KS = p.KS;
+  g.kstages = p.kstages;
+  g.act = act;
+  g.act_ld = act_ld;
+  g.half = half;
+  hipLaunchKernelGGL((gemm_big_kernel<BG_EPI_SWIGLU, true>), dim3(p.mtiles * p.ntiles * p.KS), dim3(BG_THREADS),
+                     0, st, g);
 }
 
 }  // namespace spd

@@ -16,8 +16,8 @@ import torch
 from . import (SPD_BF16, SPD_CALL_FUSE, SPD_CALL_LM_HEAD, SPD_CALL_PDM, SPD_CALL_VERIFY,
                layer_weights, make_config, spd_config, spd_cycle_plan, spd_fc_prepare,
                spd_fuse_features, spd_fuse_features_scaled,
-               spd_lm_head, spd_pdm_step, spd_rollback, spd_slot_table, spd_verify,
-               spd_workspace_size)
+               spd_lm_head, spd_pdm_prepare, spd_pdm_prepared_bytes, spd_pdm_step_prepared,
+               spd_rollback, spd_slot_table, spd_verify, spd_workspace_size)
 
 PREFILL_BLOCK = 256   # rows per PDM prefill call
 FEATURE_BLOCK = 2048  # rows per prefill feature call (one large-M FC GEMM)
@@ -52,6 +52,21 @@ class SpdModel:
         if weights.store.shape[1] != len(self.store_layers):
             raise ValueError("anchor store does not hold the layers the slot table reads")
         self._fc_scaled = None
+        self._pdm_prep = None
+        self.use_pdm_prep = True
+
+    def pdm_prep(self):
+        """The e4m3 weight copies prefill-sized PDM steps use (prepared on first use on the
+        current stream), or None where the configuration takes none or use_pdm_prep is off."""
+        if not self.use_pdm_prep:
+            return None
+        if self._pdm_prep is None:
+            nbytes = spd_pdm_prepared_bytes(self.cfg)
+            if nbytes == 0:
+                return None
+            self._pdm_prep = torch.empty(nbytes, dtype=torch.uint8, device=self.w.final_norm.device)
+            spd_pdm_prepare(self.cfg, self.layer_arr, self._pdm_prep)
+        return self._pdm_prep
 
     def fc_scaled(self):
         """W_fc with norm_w folded into its columns (bf16; prepared on first use on the
@@ -145,9 +160,12 @@ class SpdCycle:
         return g
 
     def pdm(self, pos0, M, g=None):
+        """PDM step over rows pos0 .. pos0+M-1; prefill-sized steps use the model's
+        prepared weights where it has them."""
         m = self.m
-        spd_pdm_step(m.cfg, m.layer_arr, m.w.final_norm, self.k_cache, self.v_cache, m.T_cap,
-                     self.g if g is None else g, pos0, M, self.h_last, self.ws)
+        spd_pdm_step_prepared(m.cfg, m.layer_arr, m.pdm_prep() if M >= PREFILL_BLOCK else None,
+                              m.w.final_norm, self.k_cache, self.v_cache, m.T_cap,
+                              self.g if g is None else g, pos0, M, self.h_last, self.ws)
         return self.h_last
 
     def prefill(self, P: int):

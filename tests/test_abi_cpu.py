@@ -186,6 +186,54 @@ def test_prepared_feature_calls_check_their_arguments():
     assert rc == spd.SPD_E_INVALID        # pos0 + M > T_cap
 
 
+def test_prepared_pdm_calls_check_their_arguments():
+    """The prepared e4m3 weights exist for bf16, hd = 128, d and dff multiples of 128:
+    their size (per layer: W_qkv, W_gate_up and W_down bytes plus one scale byte per
+    row), and the host-side checks of spd_pdm_prepare and spd_pdm_step_prepared (every
+    case returns before anything is enqueued)."""
+    lib = spd.lib()
+    fake = 1 << 40
+    s = synth.HEADLINE
+    c16 = _cfg(s)
+    nq = (s.Hq + 2 * s.Hkv) * s.hd
+    rows = nq + 2 * s.dff + s.d
+    nbytes = spd.spd_pdm_prepared_bytes(c16)
+    per_layer = nq * s.d + 2 * s.dff * s.d + s.d * s.dff + rows
+    assert per_layer * s.Ls <= nbytes <= (per_layer + 6 * 256) * s.Ls
+    c32 = _cfg(synth.TINY)
+    assert spd.spd_pdm_prepared_bytes(c32) == 0
+    lw = (spd.spd_layer_weights * s.Ls)()
+    for i in range(s.Ls):
+        for k, _ in spd.spd_layer_weights._fields_:
+            setattr(lw[i], k, fake)
+    assert lib.spd_pdm_prepare(ctypes.byref(c16), lw, None, nbytes, None) == spd.SPD_E_INVALID
+    assert lib.spd_pdm_prepare(ctypes.byref(c16), lw, fake, nbytes - 1, None) == spd.SPD_E_WORKSPACE
+    assert lib.spd_pdm_prepare(ctypes.byref(c16), lw, fake + 8, nbytes, None) == spd.SPD_E_INVALID
+    assert lib.spd_pdm_prepare(ctypes.byref(c32), lw, fake, nbytes, None) == spd.SPD_E_UNSUPPORTED
+    lw[0].w_down = None
+    assert lib.spd_pdm_prepare(ctypes.byref(c16), lw, fake, nbytes, None) == spd.SPD_E_INVALID
+    lw[0].w_down = fake
+    T_cap = 2112
+    ws = spd.spd_workspace_size(spd.SPD_CALL_PDM, c16, 2048, 0, T_cap)
+    step = lib.spd_pdm_step_prepared
+    assert step(ctypes.byref(c16), lw, fake, nbytes - 1, fake, fake, fake, T_cap, fake, 0, 2048, fake, fake, ws,
+                None) == spd.SPD_E_WORKSPACE
+    assert step(ctypes.byref(c16), lw, fake + 8, nbytes, fake, fake, fake, T_cap, fake, 0, 2048, fake, fake, ws,
+                None) == spd.SPD_E_INVALID
+    assert step(ctypes.byref(c16), lw, fake, nbytes, fake, fake, fake, T_cap, fake, 100, 2048, fake, fake, ws,
+                None) == spd.SPD_E_INVALID  # pos0 + M > T_cap
+    assert step(ctypes.byref(c16), lw, fake, nbytes, fake, fake, fake, T_cap, fake, 0, 2048, fake, fake, 16,
+                None) == spd.SPD_E_WORKSPACE
+    s32 = synth.TINY
+    lw32 = (spd.spd_layer_weights * s32.Ls)()
+    for i in range(s32.Ls):
+        for k, _ in spd.spd_layer_weights._fields_:
+            setattr(lw32[i], k, fake)
+    ws32 = spd.spd_workspace_size(spd.SPD_CALL_PDM, c32, 5, 0, 64)
+    assert step(ctypes.byref(c32), lw32, fake, 1 << 30, fake, fake, fake, 64, fake, 0, 5, fake, fake, ws32,
+                None) == spd.SPD_E_INVALID  # fp32 takes no prepared weights
+
+
 def test_layout_rejects_bad_arguments():
     for args in ((5, 0, 4), (5, 5, 4), (4, 4, 4)):
         with pytest.raises(spd.SpdError):

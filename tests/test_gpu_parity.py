@@ -242,9 +242,64 @@ def test_pdm_prefill_then_cycle(shape):
     Prefills of 256 rows or more in bf16 with head size 128 take the large-M
     path (MFMA-tiled GEMMs with bf16 activations, row kernels for the
     epilogues): 311 rows at d = 256 and the headline's 2039 rows at d = 2560,
-    every cache row and the final row checked."""
+    every cache row and the final row checked.  bf16 models with d and dff
+    multiples of 128 run it with prepared e4m3 weights (the activation residuals'
+    products on the fp8 MFMA)."""
+    _prefill_then_cycle(shape, prepared=True)
+
+
+def _excess_over_bf16(dev, ref):
+    """max |dev - ref| beyond half a bf16 unit in the last place of ref, over rms(ref):
+    the error a computation adds on top of storing its result in bf16."""
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+    return float(np.maximum(np.abs(dev - ref) - ulp / 2, 0).max() / np.sqrt((ref ** 2).mean()))
+
+
+@pytest.mark.parametrize("prepared", [True, False], ids=["prepared", "plain"])
+def test_pdm_prefill_9b_shape(prepared):
+    """A 2048-row prefill of the 9B-shaped PDM (d = 4096, 4 layers, GQA 32/8): the
+    output row within 2e-2; every cache row within 3e-2 beyond its own bf16 storage
+    rounding (half a unit in the last place of the exact value; the largest keys sit
+    near 6.5 rms, where storage alone costs 0.015 of rms).  The cache is bf16 by
+    design and the fp64 oracle's is exact: each layer's attention reads the earlier
+    rows' rounded keys and values (every score moves by about 2^-9 of its size), so
+    the deeper layers' entries drift further from the exact ones (measured 0.012,
+    0.015 and 0.021 beyond storage in layers 1-3, both forms), while the output row
+    stays near 0.002."""
+    shape = synth.SHAPES["qwen35_9b_n16_ls4_t1"]
     ci = make_inputs(shape, device=DEV, with_heads=False)
     model = device_model(ci)
+    model.use_pdm_prep = prepared
+    cyc = SpdCycle(model, shape.temperature)
+    om = OC.model_from_inputs(ci, with_heads=False)
+    P = 2048
+    G = synth.normal((P, shape.d), 1.0, device=DEV, seed=9, name="pdm_rows")
+    say("9b prefill", prepared)
+    cyc.pdm(0, P, g=G)
+    torch.cuda.synchronize()
+    cache = O.PdmCache(shape.Ls, om.pdm)
+    last, _ = O.pdm_step(f64(G), 0, cache, om.layers, om.final_norm, om.pdm)
+    assert rel_err(f64(cyc.h_last), last) < TOL_BF16
+    for l in range(shape.Ls):
+        gk = f64(cyc.k_cache[l]).transpose(1, 0, 2)[:P]
+        gv = f64(cyc.v_cache[l]).transpose(2, 0, 1)[:P]
+        ek, ev = _excess_over_bf16(gk, cache.k[l][:P]), _excess_over_bf16(gv, cache.v[l][:P])
+        say("layer", l, "excess", round(ek, 4), round(ev, 4))
+        assert ek < 3e-2 and ev < 3e-2, (l, ek, ev)
+
+
+@pytest.mark.parametrize("shape", [SMALL_BF16.with_(ctx=320), synth.HEADLINE],
+                         ids=["small_bf16_large_m", "headline_large_m"])
+def test_pdm_prefill_then_cycle_plain_form(shape):
+    """The same prefill and cycles without prepared weights (the residuals' products
+    as a second bf16 pass)."""
+    _prefill_then_cycle(shape, prepared=False)
+
+
+def _prefill_then_cycle(shape, prepared):
+    ci = make_inputs(shape, device=DEV, with_heads=False)
+    model = device_model(ci)
+    model.use_pdm_prep = prepared
     cyc = SpdCycle(model, shape.temperature)
     om = OC.model_from_inputs(ci, with_heads=False)
     tol = tol_for(shape.dtype)
@@ -357,6 +412,45 @@ def test_pdm_drawn_shapes():
         tol = tol_for(dtype)
         assert rel_err(f64(cyc.h_last), last) < tol, case
         _check_cache_rows(cyc, cache, pos0, pos0 + M, tol)
+
+
+def _prep_layout(s):
+    """Byte offsets of the prepared weights of one layer (spd_pdm_prepare's layout:
+    W_qkv, W_gate_up, W_down e4m3 rows, then their scale bytes, each 256-aligned)."""
+    nq = (s.Hq + 2 * s.Hkv) * s.hd
+    off, out = 0, {}
+    for key, n in (("qkv8", nq * s.d), ("gu8", 2 * s.dff * s.d), ("dn8", s.d * s.dff), ("qkv_s", nq),
+                   ("gu_s", 2 * s.dff), ("dn_s", s.d)):
+        out[key] = off
+        off = (off + n + 255) // 256 * 256
+    out["layer"] = off
+    return out
+
+
+@pytest.mark.parametrize("shape", [synth.HEADLINE, synth.SHAPES["qwen35_9b_n16_ls4_t1"]],
+                         ids=["headline", "9b_n16"])
+def test_pdm_prepare_writes_scaled_e4m3_rows(shape):
+    """spd_pdm_prepare: row n of W_qkv, W_gate_up and W_down becomes the e4m3 value
+    (round to nearest even: torch's float8_e4m3fn) of W_n 2^e_n, e_n = 8 - E_n for the
+    row's largest magnitude f 2^E_n (0.5 <= f < 1), and its scale byte is 127 - e_n;
+    checked bit for bit on every row of every layer."""
+    ci = make_inputs(shape, device=DEV, with_heads=False)
+    model = device_model(ci)
+    prep = model.pdm_prep().cpu()
+    L = _prep_layout(shape)
+    assert prep.numel() >= L["layer"] * shape.Ls
+    for l, lw in enumerate(ci.layers):
+        base = l * L["layer"]
+        for wkey, k8, ks in (("wqkv", "qkv8", "qkv_s"), ("w_gate_up", "gu8", "gu_s"), ("w_down", "dn8", "dn_s")):
+            W = lw[wkey].float().cpu()
+            N, K = W.shape
+            say("prepare", shape.name, l, wkey)
+            m = W.abs().amax(dim=1)
+            e = torch.where(m > 0, 8 - torch.frexp(m)[1], torch.zeros_like(m, dtype=torch.int32))
+            want = torch.ldexp(W, e[:, None].float()).to(torch.float8_e4m3fn).view(torch.uint8)
+            got = prep[base + L[k8]: base + L[k8] + N * K].view(N, K)
+            assert torch.equal(got, want), (l, wkey, int((got != want).sum()))
+            assert torch.equal(prep[base + L[ks]: base + L[ks] + N].to(torch.int32), (127 - e).to(torch.int32))
 
 
 def test_large_m_drawn_shapes():
