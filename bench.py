@@ -144,6 +144,18 @@ def _model(spd, synth, s, dev, **kw):
     return ci, w, model
 
 
+def prefill_flops(s, P):
+    """Multiply-add flops a P-row prefix needs: the feature FC of every row, every
+    layer but the last in full (QKV, causal attention, O, gate/up, down), and the last
+    layer's keys and values (its other outputs feed only the output row, which is
+    negligible)."""
+    d, hd, Hq, Hkv, dff = s.d, s.hd, s.Hq, s.Hkv, s.dff
+    f = 2.0 * P * d * (s.m * d)
+    layer = (2.0 * P * d * (Hq + 2 * Hkv) * hd + 2.0 * 2 * (P * P / 2.0) * hd * Hq
+             + 2.0 * P * Hq * hd * d + 2.0 * P * d * 2 * dff + 2.0 * P * dff * d)
+    return f + (s.Ls - 1) * layer + 2.0 * P * d * 2 * Hkv * hd
+
+
 def _stats(ms_list):
     ms = sorted(ms_list)
     return {"median_ms": round(float(np.median(ms)), 4), "min_ms": round(ms[0], 4),
@@ -442,17 +454,31 @@ def extra(args, torch, synth, spd, SpdCycle, SpdModel, s, ci, w, model, cyc, t, 
 
     # whole prefill of the 2039-row prefix (features + PDM over every layer); it
     # rebuilds the same cache from the same inputs
-    pf0, pf1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     P = t - 1 - s.n
-    cyc.prefill(P)
-    torch.cuda.synchronize()
-    pf0.record()
-    for _ in range(3):
+
+    def time_prefill():
+        pf0, pf1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         cyc.prefill(P)
-    pf1.record()
-    torch.cuda.synchronize()
-    result["prefill"] = {"rows": P, "us": round(pf0.elapsed_time(pf1) / 3 * 1000.0, 1),
-                         "includes": "spd_fuse_features + spd_pdm_step over the prefix, large-M MFMA path"}
+        torch.cuda.synchronize()
+        pf0.record()
+        for _ in range(3):
+            cyc.prefill(P)
+        pf1.record()
+        torch.cuda.synchronize()
+        return pf0.elapsed_time(pf1) / 3 * 1000.0
+
+    model.use_pdm_prep = False
+    plain_us = time_prefill()
+    model.use_pdm_prep = True
+    prep_us = time_prefill()
+    pf_flops = prefill_flops(s, P)
+    result["prefill"] = {"rows": P, "us": round(prep_us, 1),
+                         "includes": "spd_fuse_features + spd_pdm_step_prepared over the prefix, large-M "
+                                     "MFMA path (activation residuals on the block-scaled fp8 MFMA)",
+                         "algorithmic_gflop": round(pf_flops / 1e9, 1),
+                         "achieved_tflops": round(pf_flops / (prep_us * 1e-6) / 1e12, 1),
+                         "frac_of_bf16_peak": round(pf_flops / (prep_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                         "plain_form_us": round(plain_us, 1)}
 
     # the pages' sampling setting (T = 1, top-k = 50, top-p = 1.0) on both heads: the
     # same cycles through a second model whose heads filter
