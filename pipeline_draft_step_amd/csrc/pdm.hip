@@ -15,6 +15,12 @@
 // The last layer runs its QKV GEMM over every row (the cache needs all keys and
 // values) and the other four launches over the output rows only; its down
 // epilogue writes h_last = RMSNorm(h[M-1]) * final_norm.
+//
+// Prefill-sized steps (bf16, M >= 256, hd = 128) run the products on the large-M
+// MFMA GEMM with row kernels for the epilogues and causal flash attention (pdm_big).
+// With weights prepared by spd_pdm_prepare (e4m3 rows with per-row power-of-two
+// factors) the QKV, gate/up and down inputs are [hi | lo8] rows and the residuals'
+// products run on the block-scaled fp8 MFMA (spd_pdm_step_prepared).
 #include <math.h>
 
 #include <algorithm>

@@ -19,6 +19,11 @@
 // robin (block b runs on XCD b mod 8); block ids are remapped so that each XCD
 // holds all KS parts of its tiles and a compact patch of tiles, which keeps the
 // partials and the shared operand rows in that XCD's L2.
+//
+// LO8 kernels take A as [hi | lo8] rows (bf16 parts, then e4m3 residuals) and B
+// twice (bf16 W and its e4m3 copy B8 with per-row E8M0 scales): every 128 columns
+// are two bf16 stages and one fp8 stage of the same 52 KB, the fp8 stage on the
+// 16x16x128 block-scaled MFMA, with the kinds tied to the three ring slots.
 #pragma once
 
 #include "spd_common.h"
