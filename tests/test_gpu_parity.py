@@ -530,6 +530,38 @@ def test_cycle_calls_are_deterministic():
         assert torch.equal(x, y)
 
 
+def test_pdm_step_prepared_contract():
+    """spd_pdm_step_prepared: a decode-sized step (M < 256) does not read the prepared
+    weights, and prep == NULL is spd_pdm_step, on a prefill-sized step too -- rows,
+    cache entries and last row bit for bit."""
+    s = synth.HEADLINE
+    ci = make_inputs(s, device=DEV, with_heads=False)
+    model = device_model(ci)
+    cyc = SpdCycle(model, s.temperature)
+    prep = model.pdm_prep()
+    assert prep is not None
+    k, v = synth.kv_cache(s, model.T_cap, device=DEV)
+    m = model
+    for pos0, M in ((s.ctx - 1 - s.n, s.n + 1), (0, 300)):
+        g = synth.normal((M, s.d), 1.0, device=DEV, seed=40 + M, name="rows")
+        outs = []
+        for mode in ("plain", "prepared" if M < 256 else "null"):
+            cyc.k_cache.copy_(k)
+            cyc.v_cache.copy_(v)
+            say("prepared contract", M, mode)
+            if mode == "plain":
+                spd.spd_pdm_step(m.cfg, m.layer_arr, m.w.final_norm, cyc.k_cache, cyc.v_cache, m.T_cap, g,
+                                 pos0, M, cyc.h_last, cyc.ws)
+            else:
+                spd.spd_pdm_step_prepared(m.cfg, m.layer_arr, prep if mode == "prepared" else None,
+                                          m.w.final_norm, cyc.k_cache, cyc.v_cache, m.T_cap, g, pos0, M,
+                                          cyc.h_last, cyc.ws)
+            torch.cuda.synchronize()
+            outs.append((cyc.h_last.clone(), cyc.k_cache.clone(), cyc.v_cache.clone()))
+        for x, y in zip(*outs):
+            assert torch.equal(x, y), (pos0, M)
+
+
 # ------------------------------------------------------------------ LM head
 
 def _lm_case(V, d, dtype, std, rows, T, seed):
