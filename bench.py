@@ -144,6 +144,35 @@ def _model(spd, synth, s, dev, **kw):
     return ci, w, model
 
 
+def time_prefills(torch, s, model, cyc, P, reps=3):
+    """Whole prefills of the P-row prefix (features + PDM over every layer, rebuilding
+    the same cache from the same inputs): reps in the plain form, then reps with
+    prepared weights."""
+    def time_prefill():
+        pf0, pf1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        cyc.prefill(P)
+        torch.cuda.synchronize()
+        pf0.record()
+        for _ in range(reps):
+            cyc.prefill(P)
+        pf1.record()
+        torch.cuda.synchronize()
+        return pf0.elapsed_time(pf1) / reps * 1000.0
+
+    model.use_pdm_prep = False
+    plain_us = time_prefill()
+    model.use_pdm_prep = True
+    prep_us = time_prefill()
+    pf_flops = prefill_flops(s, P)
+    return {"rows": P, "us": round(prep_us, 1),
+            "includes": "spd_fuse_features + spd_pdm_step_prepared over the prefix, large-M "
+                        "MFMA path (activation residuals on the block-scaled fp8 MFMA)",
+            "algorithmic_gflop": round(pf_flops / 1e9, 1),
+            "achieved_tflops": round(pf_flops / (prep_us * 1e-6) / 1e12, 1),
+            "frac_of_bf16_peak": round(pf_flops / (prep_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "plain_form_us": round(plain_us, 1)}
+
+
 def prefill_flops(s, P):
     """Multiply-add flops a P-row prefix needs: the feature FC of every row, every
     layer but the last in full (QKV, causal attention, O, gate/up, down), and the last
@@ -172,6 +201,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="headline cycles only (no other workloads or per-call breakdowns)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only whole prefills of the headline prefix (plain form and "
+                         "prepared weights, 10 each) and print their JSON; for counter runs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with a plain 256 MiB device-to-device copy, the known-size "
                          "reference that scales the FETCH_SIZE / WRITE_SIZE counters")
@@ -193,6 +225,9 @@ def main():
     cyc = SpdCycle(model, s.temperature, device=dev)
     t = s.ctx
     cyc.set_state(t, s.n, list(range(t)))
+    if args.prefill_only:
+        print(json.dumps({"prefill": time_prefills(torch, s, model, cyc, t - 1 - s.n, reps=10)}))
+        return
     cyc.prefill(t - 1 - s.n)
 
     total = args.warmup + args.steps
@@ -454,31 +489,7 @@ def extra(args, torch, synth, spd, SpdCycle, SpdModel, s, ci, w, model, cyc, t, 
 
     # whole prefill of the 2039-row prefix (features + PDM over every layer); it
     # rebuilds the same cache from the same inputs
-    P = t - 1 - s.n
-
-    def time_prefill():
-        pf0, pf1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        cyc.prefill(P)
-        torch.cuda.synchronize()
-        pf0.record()
-        for _ in range(3):
-            cyc.prefill(P)
-        pf1.record()
-        torch.cuda.synchronize()
-        return pf0.elapsed_time(pf1) / 3 * 1000.0
-
-    model.use_pdm_prep = False
-    plain_us = time_prefill()
-    model.use_pdm_prep = True
-    prep_us = time_prefill()
-    pf_flops = prefill_flops(s, P)
-    result["prefill"] = {"rows": P, "us": round(prep_us, 1),
-                         "includes": "spd_fuse_features + spd_pdm_step_prepared over the prefix, large-M "
-                                     "MFMA path (activation residuals on the block-scaled fp8 MFMA)",
-                         "algorithmic_gflop": round(pf_flops / 1e9, 1),
-                         "achieved_tflops": round(pf_flops / (prep_us * 1e-6) / 1e12, 1),
-                         "frac_of_bf16_peak": round(pf_flops / (prep_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                         "plain_form_us": round(plain_us, 1)}
+    result["prefill"] = time_prefills(torch, s, model, cyc, t - 1 - s.n)
 
     # the pages' sampling setting (T = 1, top-k = 50, top-p = 1.0) on both heads: the
     # same cycles through a second model whose heads filter
