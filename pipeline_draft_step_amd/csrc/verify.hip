@@ -33,6 +33,7 @@ struct VerArgs {
   int32_t* n_accept;
   int32_t* next_token;
   void* part;
+  int32_t* jrej;  // [B] first rejected position (T > 0: the sums pass leaves it for the draw)
   int B, gamma, V, bonus, nchunks;
   int W;  // sibling candidates per sequence (greedy sibling verification)
 };
@@ -206,6 +207,7 @@ __device__ void locate_and_write(const VerArgs& a, int b, int j, const uint64_t*
 __global__ __launch_bounds__(VER_THREADS) void verify_sums_kernel(VerArgs a) {
   const int c = blockIdx.x, b = blockIdx.y;
   const int j = first_reject(a, b);
+  if (c == 0 && threadIdx.x == 0) a.jrej[b] = j;
   const bool rejected = j < a.gamma;
   if (!rejected && !a.bonus) return;
   const int rowsP = a.gamma + a.bonus;
@@ -228,9 +230,11 @@ __global__ __launch_bounds__(VER_THREADS) void verify_sums_kernel(VerArgs a) {
   }
 }
 
+// (the decision of sequence b comes from the sums pass: one load instead of the
+// draft and probability loads one after the other)
 __global__ __launch_bounds__(VER_THREADS) void verify_locate_kernel(VerArgs a) {
   const int b = blockIdx.x;
-  const int j = first_reject(a, b);
+  const int j = a.jrej[b];
   if (j == a.gamma && !a.bonus) {
     if (threadIdx.x == 0) {
       a.n_accept[b] = a.gamma;
@@ -713,11 +717,15 @@ __global__ __launch_bounds__(SIB_MB_THREADS) void sib_pass_kernel(VerArgs a, Sib
   }
 }
 
-size_t verify_workspace(int B, int gamma, int V) {
+// chunk partials of every (chunk, sequence), then the sequences' first rejections
+static size_t verify_part_bytes(int B, int gamma, int V) {
   const size_t nch = (size_t)(V + VER_CHUNK - 1) / VER_CHUNK;
   const size_t per = std::max((size_t)16, (size_t)(gamma + 1) * sizeof(ArgMax));
+  return align256((size_t)B * nch * per);
+}
+size_t verify_workspace(int B, int gamma, int V) {
   // also room for the multi-block sibling verification's state and partials
-  return SPD_WS_COUNTER_BYTES + std::max(align256((size_t)B * nch * per),
+  return SPD_WS_COUNTER_BYTES + std::max(verify_part_bytes(B, gamma, V) + align256((size_t)B * 4),
                                          sib_state_bytes(B) + align256(sib_part_bytes(B, V)));
 }
 
@@ -744,6 +752,7 @@ extern "C" int spd_verify(int32_t B, int32_t gamma, int32_t V, float temperature
   a.n_accept = n_accept;
   a.next_token = next_token;
   a.part = static_cast<char*>(ws) + SPD_WS_COUNTER_BYTES;
+  a.jrej = reinterpret_cast<int32_t*>(static_cast<char*>(a.part) + verify_part_bytes(B, gamma, V));
   a.B = B;
   a.gamma = gamma;
   a.V = V;
